@@ -1,0 +1,133 @@
+"""KDA oracle: plain fp64 CPU reference for parity tests.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product
+package ``kda_gated_delta_chunk_amd`` never imports it, and the two share no
+code: the only thing both sides use is the seeded input generator
+(``kda_gated_delta_chunk_amd.synth``), which holds none of the method's
+arithmetic.
+
+The arithmetic lives in ``kda_oracle.c`` (per-token recurrence, see the
+citations there). This module compiles it with gcc and calls it via ctypes.
+Every array is widened to float64 before the call, so the oracle sees exactly
+the values the GPU received (bf16 or fp32), just held in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "kda_oracle.c"
+_LIB = _HERE / "libkda_oracle.so"
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile the C oracle with gcc (-O2, no fast-math)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp%d" % os.getpid())
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+               str(_SRC), "-o", str(tmp), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+            build(force=True)
+        lib = ctypes.CDLL(str(_LIB))
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.kda_oracle_chunk_fwd.argtypes = [dp, dp, dp, dp, dp, dp, ip,
+                                             i64, i64, i64, i64, i64, i64, dp, dp, ctypes.c_int]
+        lib.kda_oracle_chunk_fwd.restype = ctypes.c_int
+        lib.kda_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                          i64, i64, i64, i64, ctypes.c_int]
+        lib.kda_oracle_decode.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Widen to a C-contiguous float64 copy (exact for bf16/fp16/fp32 inputs)."""
+    if hasattr(x, "detach"):  # a torch tensor: copy to host, widen exactly
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0):
+    """Run the fp64 recurrence over whole sequences.
+
+    q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H];
+    S0: [N, H, K, V] or None (zeros); cu_seqlens: [N+1] or None.
+    Returns (o [B, T, H, V], S_final [N, H, K, V]) as float64 arrays.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent input shapes")
+    cu = None
+    if cu_seqlens is not None:
+        if hasattr(cu_seqlens, "detach"):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+    else:
+        N = B
+    s0 = None if S0 is None else _f64(S0)
+    if s0 is not None and s0.shape != (N, H, K, V):
+        raise ValueError("S0 shape %s != %s" % (s0.shape, (N, H, K, V)))
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    sf = np.zeros((N, H, K, V), dtype=np.float64)
+    cu_ptr = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = _load().kda_oracle_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), cu_ptr,
+                                      B, T, H, K, V, N, _ptr(o), _ptr(sf), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, sf
+
+
+def decode_step(q, k, v, g, beta, S, threads: int = 0):
+    """One decode step. q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H]; S: [N, H, K, V].
+
+    Returns (o [N, H, V], S_new [N, H, K, V]); the input S is not modified.
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    S_new = _f64(S).copy()
+    N, H, K = q.shape
+    V = v.shape[-1]
+    if S_new.shape != (N, H, K, V):
+        raise ValueError("state shape mismatch")
+    o = np.zeros((N, H, V), dtype=np.float64)
+    rc = _load().kda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S_new), _ptr(o),
+                                   N, H, K, V, int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, S_new
+
+
+def parity_error(x, ref) -> float:
+    """max|x - ref| / rms(ref), the comparison metric used by every parity test."""
+    x = _f64(x)
+    ref = _f64(ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    diff = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    if rms == 0.0:
+        return diff
+    return diff / rms

@@ -1,0 +1,157 @@
+"""CPU tests: the fp64 oracle against its pins (closed forms, independent
+formulations, invariants), plus planted mistakes that the pins must catch."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import kda_pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def run_oracle(q, k, v, g, beta, S0, cu):
+    return oracle.chunk_fwd(q, k, v, g, beta, S0=S0, cu_seqlens=cu, threads=2)
+
+
+@pytest.mark.parametrize("pin", kda_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(run_oracle, np.random.default_rng(1234))
+
+
+def test_exact_bruteforce():
+    kda_pins.pin_exact_bruteforce(run_oracle, seeds=(1, 2, 3, 4))
+
+
+def test_decode_equals_prefill():
+    """n decode steps from S equal one prefill of those n tokens started at S."""
+    rng = np.random.default_rng(7)
+    N, H, K, V, n = 3, 2, 5, 4, 6
+    q, k, v, g, beta = kda_pins._rand_problem(rng, N, n, H, K, V)
+    S0 = rng.standard_normal((N, H, K, V))
+    o_ref, S_ref = oracle.chunk_fwd(q, k, v, g, beta, S0=S0)
+    S = S0.copy()
+    for t in range(n):
+        o_t, S = oracle.decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
+        assert kda_pins.rel_err(o_t, o_ref[:, t]) < 1e-13
+    assert kda_pins.rel_err(S, S_ref) < 1e-13
+
+
+def test_golden_exact_fixture():
+    """Stored exact-rational result of a hand-sized problem (tests/golden)."""
+    with open(os.path.join(HERE, "golden", "tiny_exact.json")) as f:
+        fx = json.load(f)
+    to = lambda m: np.array([[float(Fraction(x)) for x in row] for row in m])
+    q, k, v = to(fx["q"]), to(fx["k"]), to(fx["v"])
+    alpha = to(fx["alpha"])
+    beta = np.array([float(Fraction(x)) for x in fx["beta"]])
+    S0 = to(fx["S0"])
+    o, Sf = oracle.chunk_fwd(q[None, :, None], k[None, :, None], v[None, :, None], np.log(alpha)[None, :, None],
+                             beta[None, :, None], S0=S0[None, None])
+    assert kda_pins.rel_err(o[0, :, 0], to(fx["o"])) < 1e-13
+    assert kda_pins.rel_err(Sf[0, 0], to(fx["S_final"])) < 1e-13
+
+
+def test_threads_do_not_change_results():
+    rng = np.random.default_rng(11)
+    q, k, v, g, beta = kda_pins._rand_problem(rng, 2, 17, 5, 6, 4)
+    a = oracle.chunk_fwd(q, k, v, g, beta, threads=1)
+    b = oracle.chunk_fwd(q, k, v, g, beta, threads=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rejects_bad_arguments():
+    z = np.zeros((1, 4, 1, 2))
+    with pytest.raises(ValueError):
+        oracle.chunk_fwd(z, z, z, z, np.zeros((1, 4, 1)), cu_seqlens=np.array([0, 3]))  # cu[-1] != T
+    with pytest.raises(ValueError):
+        oracle.chunk_fwd(z, z, z[..., :1], z, np.zeros((1, 5, 1)))
+
+
+# ------------------------------------------------------------ planted mistakes
+#
+# A small numpy re-implementation with switches for plausible mistakes. The
+# correct switch setting must pass every pin; each mistake must fail at least
+# one pin. This shows the pins constrain the oracle's arithmetic.
+
+def make_runner(mistake=None):
+    def run(q, k, v, g, beta, S0, cu):
+        q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+        B, T, H, K = q.shape
+        V = v.shape[-1]
+        if cu is None:
+            seqs = [(n, n * T, (n + 1) * T) for n in range(B)]
+        else:
+            seqs = [(n, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)]
+        qf, kf, gf = (x.reshape(B * T, H, K) for x in (q, k, g))
+        vf = v.reshape(B * T, H, V)
+        bf = beta.reshape(B * T, H)
+        o = np.zeros((B * T, H, V))
+        Sf = np.zeros((len(seqs), H, K, V))
+        carry = None
+        for n, t0, t1 in seqs:
+            for h in range(H):
+                S = np.zeros((K, V)) if S0 is None else np.array(S0[n, h], dtype=np.float64)
+                if mistake == "no_reset" and carry is not None and h == 0:
+                    S = carry.copy()
+                for t in range(t0, t1):
+                    kt, vt, qt, bt = kf[t, h], vf[t, h], qf[t, h], bf[t, h]
+                    gt = gf[t - 1, h] if (mistake == "gate_index" and t > t0) else gf[t, h]
+                    a = gt if mistake == "alpha_is_g" else np.exp(gt)
+                    if mistake == "read_before_decay":
+                        u = S.T @ kt
+                        S = a[:, None] * S
+                    elif mistake == "decay_after_write":
+                        u = S.T @ kt
+                    else:
+                        S = (a[:V][None, :] * S) if mistake == "decay_columns" else a[:, None] * S
+                        u = S.T @ (qt if mistake == "query_reads" else kt)
+                    if mistake == "transposed_read":
+                        u = S @ kt[:V]
+                    if mistake == "sign_flip":
+                        S_new = S + bt * np.outer(kt, vt + u)
+                    elif mistake == "beta_on_value_only":
+                        S_new = S + np.outer(kt, bt * vt - u)
+                    elif mistake == "beta_squared":
+                        S_new = S + bt * bt * np.outer(kt, vt - u)
+                    else:
+                        S_new = S + bt * np.outer(kt, vt - u)
+                    if mistake == "decay_after_write":
+                        S_new = a[:, None] * S_new
+                    o[t, h] = (S if mistake == "read_old_state" else S_new).T @ qt
+                    S = S_new
+                Sf[n, h] = S
+                if h == 0:
+                    carry = S
+        return o.reshape(B, T, H, V), Sf
+    return run
+
+
+MISTAKES = ["read_before_decay", "decay_after_write", "read_old_state", "sign_flip", "beta_on_value_only",
+            "beta_squared", "decay_columns", "alpha_is_g", "query_reads", "transposed_read", "gate_index",
+            "no_reset"]
+
+
+def _fails_some_pin(run):
+    for pin in kda_pins.ALL_PINS:
+        try:
+            pin(run, np.random.default_rng(99))
+        except Exception:
+            return pin.__name__
+    try:
+        kda_pins.pin_exact_bruteforce(run, seeds=(1,))
+    except Exception:
+        return "pin_exact_bruteforce"
+    return None
+
+
+def test_correct_reimplementation_passes_pins():
+    assert _fails_some_pin(make_runner(None)) is None
+
+
+@pytest.mark.parametrize("mistake", MISTAKES)
+def test_planted_mistake_is_caught(mistake):
+    assert _fails_some_pin(make_runner(mistake)) is not None, mistake
