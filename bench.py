@@ -1,0 +1,191 @@
+"""Benchmark of the MI355X KDA hot path on one GPU; prints ONE JSON line.
+
+A step is one chunked prefill (kda_chunk_prep + kda_chunk_state, i.e. one
+kda_chunk_fwd) of the K3-shaped workload: B=1, T=4096, H=96, K=V=128, bf16
+q/k/v/g/beta, chunk 16, zero initial state, returning o and S_final. Inputs
+are seeded synthetic tensors already resident in HBM. `value` is prefill
+tokens/s. The decode half of the metric (N=512 streams, H=96, fp32 state of
+~3.2 GB updated in place, 100 consecutive steps) is timed after the prefill
+steps and reported under "decode".
+
+Kernel durations come from HIP events recorded on the stream the kernels run
+on, around each phase of every timed step. Roofline figures use algorithmic
+bytes (the tensors the operation must read and write once) divided by those
+durations, against MI355X's published 8 TB/s HBM3E bandwidth.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+from kda_gated_delta_chunk_amd import _lib, decode_step, synth
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix, TFLOP/s
+
+
+def prefill_algorithmic_bytes(T, H, K, V, N, es=2, with_S0=False):
+    """Bytes the prefill must move once: q, k, g, v, beta in, o out, S_final out (S0 in)."""
+    per_tok = H * (3 * K * es + V * es + es + V * es)
+    states = N * H * K * V * 4 * (2 if with_S0 else 1)
+    return T * per_tok + states, {"prep": T * H * (3 * K * es + es),
+                                  "state": T * H * 2 * V * es + states}
+
+
+def prefill_flops(T, H, K, V, C=16):
+    """Algorithmic flops of the chunk form per token-head: 6dK (W, state update, Q*S) plus the
+    intra-chunk products and the solve (triangles counted as triangles)."""
+    d = K
+    per = 6 * d * V + (5 * C + 3) * d + d * d / C + C * C / 3
+    return T * H * per
+
+
+def time_prefill(w, steps, warmup, dev):
+    lib = _lib.load()
+    inp = synth.workload_prefill_inputs(w, device=dev)
+    B, T, H, K = inp["q"].shape
+    V = inp["v"].shape[-1]
+    N = B
+    o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, 16, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
+
+    def prep():
+        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, 16, 1,
+                                      ws.data_ptr(), wsb, sh), "kda_chunk_prep")
+
+    def state():
+        _lib.check(lib.kda_chunk_state(p["v"], None, None, B, T, H, K, V, N, 16, 1, 1, o.data_ptr(),
+                                       Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
+
+    for _ in range(warmup):
+        prep()
+        state()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        prep()
+        ev[i][1].record(stream)
+        state()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    state_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return {"B": B, "T": T, "H": H, "K": K, "V": V, "N": N, "wall_s": wall, "prep_ms": prep_ms,
+            "state_ms": state_ms, "ws_bytes": wsb}
+
+
+def time_decode(w, steps, dev):
+    N, H, K, V = w.N, w.H, w.K, w.V
+    S = synth.decode_state(N, H, K, V, seed=w.seed, device=dev)
+    inputs = [synth.decode_inputs(N, H, K, V, w.io, seed=w.seed, step=s, device=dev) for s in range(steps)]
+    o = torch.empty((N, H, V), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for s in range(2):  # warm-up on the same state (its values only drift)
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for s in range(steps):
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+    bytes_step = N * H * (2 * K * V * 4 + (3 * K + V + 1) * 2 + V * 2)
+    return {"steps": steps, "total_ms": total, "ms_per_step": total / steps, "median_ms": per[len(per) // 2],
+            "bytes_per_step": bytes_step, "N": N, "H": H}
+
+
+def cpu_baseline(w):
+    """The fp64 oracle on the host, on the full prefill workload (generation excluded)."""
+    import oracle  # test infrastructure: only this baseline leg uses it
+    inp = synth.workload_prefill_inputs(w, device="cpu")
+    args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    t0 = time.perf_counter()
+    oracle.chunk_fwd(*args, threads=threads)
+    dt = time.perf_counter() - t0
+    B, T, H, _ = args[0].shape
+    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "full workload: B=1 T=%d H=%d K=V=128 bf16 inputs, fp64 per-token recurrence, %.1f s" %
+                      (T, H, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (heads and sequences would "
+              "shard without communication; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["prefill_4k"]
+    print("[bench] prefill %s: warmup %d, steps %d" % (w.name, args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    r = time_prefill(w, args.steps, args.warmup, dev)
+    ms = r["wall_s"] * 1e3 / args.steps
+    tok_s = r["B"] * r["T"] / (ms * 1e-3)
+    path_bytes, kb = prefill_algorithmic_bytes(r["T"] * r["B"], r["H"], r["K"], r["V"], r["N"])
+    kern_ms = {"kda_chunk_prep (+chunk table)": r["prep_ms"], "kda_state_pass": r["state_ms"]}
+    dom = "state" if r["state_ms"] >= r["prep_ms"] else "prep"
+    dom_ms = r["state_ms"] if dom == "state" else r["prep_ms"]
+    dom_gbs = kb[dom] / (dom_ms * 1e-3) / 1e9
+    path_ms = r["prep_ms"] + r["state_ms"]
+    path_gbs = path_bytes / (path_ms * 1e-3) / 1e9
+    flops = prefill_flops(r["T"] * r["B"], r["H"], r["K"], r["V"])
+    out = {
+        "metric": "KDA prefill tokens/s (H=96,d=128,bf16) + decode state GB/s, % of roofline",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,v~N(0,1), k L2-normalised, g=-5*sigmoid(N(0,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 16, zero S0", "global_batch": 1,
+                   "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
+                     "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms},
+        "roofline_path": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes": path_bytes,
+                          "event_ms": path_ms, "mfma_tflops_algorithmic": flops / (path_ms * 1e-3) / 1e12,
+                          "mfma_frac_algorithmic": flops / (path_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "kernels_ms": kern_ms,
+        "workspace_bytes": r["ws_bytes"],
+    }
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode_512"]
+        print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)
+        d = time_decode(wd, args.decode_steps, dev)
+        gbs = d["bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9
+        out["decode"] = {"workload": "decode N=512 H=96 K=V=128 bf16 in, fp32 state in place, %d steps" %
+                                     d["steps"],
+                         "ms_per_step": d["ms_per_step"], "median_ms": d["median_ms"],
+                         "tokens_per_s": d["N"] / (d["ms_per_step"] * 1e-3),
+                         "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                      "traffic": None, "algorithmic_bytes_per_launch": d["bytes_per_step"]}}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention hot path.
+ *
+ * The operation (per sequence n and head h, state S in R^{K x V}, rows = key
+ * channels, columns = value channels):
+ *
+ *   S   <- diag(exp(g_t)) S                 decay every key channel
+ *   u   <- S^T k_t                          what the key reads now
+ *   S   <- S + beta_t k_t (v_t - u)^T       write back only the error
+ *   o_t <- S^T q_t                          read the updated state
+ *
+ * Sources (page titles as published):
+ *   "Kimi K3 发布核实与 Moonshot AI 主干架构演变", section 3, paragraph
+ *     "KDA 为什么不同于 MLA": one state matrix per head; a token first decays
+ *     the state channel by channel with alpha_t, then corrects it with beta_t,
+ *     k_t and v_t; the query reads the updated state; training runs recurrent
+ *     across chunks and parallel inside a chunk.
+ *   same page, paragraph "K3 对 Kimi Linear 的进一步修改": the log-decay is a
+ *     scaled sigmoid bounded below by -5, which keeps the reciprocal decay
+ *     scaling inside a 16-token tile within BF16 range.
+ *   "Kimi K3 模型架构解析：KDA、AttnRes 与 Stable LatentMoE", section 二.2
+ *     (S_t = Update(S_{t-1}, k_t, v_t), o_t = Read(S_t, q_t)) and section 二.3
+ *     (the delta rule; 96 heads with 128-dim state channels).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *     on the current HIP device, 16-byte aligned, contiguous row-major.
+ *   - The caller owns every buffer. kda_chunk_fwd and kda_decode_step
+ *     allocate nothing; kda_chunk_fwd uses only the caller's workspace.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronising. Arguments are validated
+ *     before anything is enqueued: on any error status nothing is launched
+ *     and no output is written. A fault inside a kernel surfaces at the
+ *     caller's next synchronisation of the stream.
+ *   - Supported sizes: K, V in {32, 64, 128}; chunk = 16.
+ *   - The functions keep no state between calls and may be called from
+ *     several host threads on different streams (calls that share output
+ *     buffers or a workspace race).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,      /* null/misaligned pointer, bad size, overflow   */
+    KDA_ERROR_NOT_SUPPORTED = 2,      /* valid request this build does not implement   */
+    KDA_ERROR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERROR_NO_DEVICE = 4,          /* no HIP device visible                         */
+    KDA_ERROR_HIP = 5                 /* a HIP runtime call or a launch failed         */
+} kda_status_t;
+
+typedef enum {
+    KDA_DTYPE_FP32 = 0,
+    KDA_DTYPE_BF16 = 1
+} kda_dtype_t;
+
+/* Version of this ABI (bumped on any signature change). */
+int kda_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Bytes of device workspace that kda_chunk_fwd needs for these sizes.
+ *   B, T        batch rows and tokens per row (packed: B = 1, T = total tokens)
+ *   num_seqs    number of sequences: B without cu_seqlens, else len(cu_seqlens)-1
+ *   chunk, io   as for kda_chunk_fwd
+ * Returns 0 if the sizes are invalid or unsupported.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                                     int32_t num_seqs, int32_t chunk, kda_dtype_t io);
+
+/*
+ * Chunked prefill over whole sequences: the recurrence above for every
+ * token, computed chunk-parallel ("recurrent across chunks, parallel inside a
+ * chunk", first page cited above).
+ *
+ * Inputs (dtype `io`):
+ *   q, k, g   [B, T, H, K]   g is the post-activation log-decay; the chunk
+ *                            form assumes -5 <= g <= 0 (the bounded gate);
+ *                            outside that range results are unspecified
+ *   v         [B, T, H, V]
+ *   beta      [B, T, H]      write strength, used as given
+ *   S0        [num_seqs, H, K, V] fp32, or NULL for a zero initial state
+ *   cu_seqlens int32 [num_seqs + 1] or NULL. With it, B must be 1 and
+ *              sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of
+ *              the packed row; every sequence restarts from S0[n] (or 0).
+ *              Without it, num_seqs must equal B and row n is sequence n.
+ *              Entries are clamped into [0, T] and made non-decreasing on
+ *              the device, so a corrupt table gives wrong numbers but never
+ *              an out-of-bounds access. Empty sequences are allowed.
+ * Outputs:
+ *   o         [B, T, H, V] in `o_dtype` (bf16: round-to-nearest-even of the
+ *             fp32 result). Rows of tokens outside every sequence are not
+ *             written.
+ *   S_final   [num_seqs, H, K, V] fp32, or NULL to skip. May not alias S0.
+ *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes().
+ * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
+ *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow),
+ *   NOT_SUPPORTED (K, V or chunk outside the supported set),
+ *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens,
+                           int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                           int32_t chunk, kda_dtype_t io, kda_dtype_t o_dtype,
+                           void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * The two halves of kda_chunk_fwd, for callers that overlap or time them
+ * separately (kda_chunk_fwd is exactly kda_chunk_prep followed by
+ * kda_chunk_state on one stream).
+ *
+ * kda_chunk_prep: everything that does not depend on the state. Numbers the
+ *   chunks (cu_seqlens as for kda_chunk_fwd, read on the device) and, per
+ *   (chunk, head), forms the cumulative log-decay, the beta-weighted
+ *   decay-scaled key products, solves the chunk's unit lower-triangular
+ *   system and stores the resulting factors in `workspace` (layout private to
+ *   the library). Reads q, k, g, beta; V only sizes the workspace check.
+ * kda_chunk_state: the sequential pass over the chunks of each (sequence,
+ *   head): carries S from S0 (or 0), writes o and S_final. Reads v, S0 and a
+ *   workspace that kda_chunk_prep filled with the same sizes and the same
+ *   cu_seqlens pointer (used here only to tell packed from batched input;
+ *   not dereferenced). The workspace may not be modified in between.
+ * Errors as for kda_chunk_fwd.
+ */
+kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, void *workspace,
+                            size_t workspace_bytes, void *stream);
+kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
+                             int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
+                             kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for N independent sequences, one new token each: the four
+ * steps above applied once, with the fixed-size state updated in place
+ * ("S_t = Update(S_{t-1}, k_t, v_t)", second page cited above).
+ *   q, k, g [N, H, K]; v [N, H, V]; beta [N, H]      dtype `io`
+ *   S       [N, H, K, V] fp32, read and overwritten in place
+ *   o       [N, H, V] in `o_dtype`
+ * Any finite g is accepted (no chunk-range assumption). S may not alias any
+ * other argument. Errors as for kda_chunk_fwd.
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
+                             kda_dtype_t io, kda_dtype_t o_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

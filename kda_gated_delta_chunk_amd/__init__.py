@@ -1,0 +1,129 @@
+"""MI355X (gfx950) Kimi Delta Attention hot path: chunked prefill and decode.
+
+The compute lives in libkda.so (hand-written HIP kernels behind the C ABI of
+include/kda.h). This module marshals torch tensors into that ABI: it checks
+shapes, dtypes and devices, allocates the outputs and the workspace with
+torch, and passes raw device pointers plus torch's current HIP stream. It
+performs no arithmetic of the method itself.
+
+Shapes (contiguous): q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H];
+states [num_seqs, H, K, V] fp32. With cu_seqlens (int32 [num_seqs+1], on the
+device), B must be 1 and sequences are packed along T.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import KDAError, KDA_DTYPE_BF16, KDA_DTYPE_FP32
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "KDAError", "abi_version"]
+
+_DT = {torch.bfloat16: KDA_DTYPE_BF16, torch.float32: KDA_DTYPE_FP32}
+_NAME = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def abi_version() -> int:
+    return _lib.load().kda_abi_version()
+
+
+def _io_code(dtype) -> int:
+    if isinstance(dtype, str):
+        dtype = _NAME[dtype]
+    if dtype not in _DT:
+        raise TypeError("unsupported dtype %s (bf16 or fp32)" % dtype)
+    return _DT[dtype]
+
+
+def workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16") -> int:
+    """Device workspace bytes kda_chunk_fwd needs (0 = unsupported sizes)."""
+    return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io)))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t, name, shape, dtype, dev):
+    if t.device != dev:
+        raise ValueError("%s must be on %s" % (name, dev))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
+              output_final_state: bool = True, workspace=None, out=None):
+    """Chunked KDA prefill. Returns (o, S_final or None).
+
+    o is in ``o_dtype`` (default: the input dtype); S_final is fp32
+    [num_seqs, H, K, V]. ``workspace`` (uint8 CUDA tensor) and ``out`` may be
+    passed to avoid allocations.
+    """
+    lib = _lib.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be CUDA (HIP) tensors")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    io = _io_code(dt)
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
+                         ("beta", beta, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _need(q, "q", (B, T, H, K), dt, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, K, V), torch.float32, dev)
+    odt = dt if o_dtype is None else (_NAME[o_dtype] if isinstance(o_dtype, str) else o_dtype)
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=odt, device=dev)
+    else:
+        _need(out, "out", (B, T, H, V), odt, dev)
+    S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io)
+    if need == 0:
+        raise KDAError(2, "kda_chunk_fwd_workspace_bytes(B=%d,T=%d,H=%d,K=%d,V=%d,N=%d,chunk=%d)"
+                       % (B, T, H, K, V, N, chunk))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+                               B, T, H, K, V, N, chunk, io, _io_code(odt), _ptr(out), _ptr(S_final),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(status, "kda_chunk_fwd")
+    return out, S_final
+
+
+def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None):
+    """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V]."""
+    lib = _lib.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be CUDA (HIP) tensors")
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    io = _io_code(dt)
+    for name, t, shp in (("k", k, (N, H, K)), ("g", g, (N, H, K)), ("v", v, (N, H, V)), ("beta", beta, (N, H))):
+        _need(t, name, shp, dt, dev)
+    _need(S, "S", (N, H, K, V), torch.float32, dev)
+    odt = dt if o_dtype is None else (_NAME[o_dtype] if isinstance(o_dtype, str) else o_dtype)
+    if out is None:
+        out = torch.empty((N, H, V), dtype=odt, device=dev)
+    else:
+        _need(out, "out", (N, H, V), odt, dev)
+    status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
+                                 N, H, K, V, io, _io_code(odt), _stream(dev))
+    _lib.check(status, "kda_decode_step")
+    return out

@@ -1,0 +1,182 @@
+// C ABI of the KDA library (declared in include/kda.h): argument validation,
+// workspace sizing and dispatch to the kernel launchers. Validation runs
+// entirely on the host before any HIP call, so every error status leaves the
+// device untouched (and works on a host with no GPU).
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+constexpr int kChunk = 16;
+constexpr int64_t kMaxElems = (int64_t)1 << 60;
+
+bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; }
+
+// Upper bound on chunks over all sequences: every sequence starts a chunk, so
+// packed input has at most ceil(T/C) full-or-partial chunks plus one partial
+// chunk per sequence boundary.
+int64_t max_chunks(int64_t B, int64_t T, int32_t num_seqs, bool packed) {
+    if (packed) return (T + kChunk - 1) / kChunk + num_seqs;
+    return B * ((T + kChunk - 1) / kChunk);
+}
+
+// Shared size checks. Returns KDA_SUCCESS or the error to report.
+kda_status_t check_prefill_sizes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                 int32_t chunk, bool packed) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 1 || K < 1 || V < 1) return KDA_ERROR_INVALID_VALUE;
+    if (packed ? (B != 1) : (num_seqs != B)) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_dim(K) || !supported_dim(V) || chunk != kChunk) return KDA_ERROR_NOT_SUPPORTED;
+    // overflow: element counts, chunk indices (int32 in the kernels), grid sizes
+    if (T > kMaxElems / B) return KDA_ERROR_INVALID_VALUE;
+    const int64_t BT = B * T;
+    if (BT > kMaxElems / H / 128) return KDA_ERROR_INVALID_VALUE;
+    const int64_t nc = max_chunks(B, T, num_seqs, packed);
+    if (nc >= ((int64_t)1 << 31) || nc * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
+    if ((int64_t)num_seqs * H >= ((int64_t)1 << 28)) return KDA_ERROR_INVALID_VALUE;
+    return KDA_SUCCESS;
+}
+
+kda_status_t check_device() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return KDA_ERROR_NO_DEVICE;
+    }
+    return KDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return 1; }
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_SUCCESS: return "KDA_SUCCESS";
+        case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+        case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+        case KDA_ERROR_WORKSPACE_TOO_SMALL: return "KDA_ERROR_WORKSPACE_TOO_SMALL";
+        case KDA_ERROR_NO_DEVICE: return "KDA_ERROR_NO_DEVICE";
+        case KDA_ERROR_HIP: return "KDA_ERROR_HIP";
+    }
+    return "KDA_ERROR_UNKNOWN";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     int32_t chunk, kda_dtype_t io) {
+    if (!valid_dtype(io)) return 0;
+    // B == 1 may be packed (cu_seqlens) or not; the packed bound is the larger and covers both
+    const bool packed = (B == 1);
+    if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
+    const int64_t nc = max_chunks(B, T, num_seqs, packed);
+    return kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16);
+}
+
+namespace {
+// Validation shared by the prefill entry points. `need_*` select which
+// pointers the entry point reads or writes.
+kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                          const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
+                          int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_dtype_t o_dtype, void *o,
+                          float *S_final, const void *workspace, size_t workspace_bytes, bool need_prep,
+                          bool need_state, kda::PrefillArgs &a) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    const bool packed = cu_seqlens != nullptr;
+    kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed);
+    if (st != KDA_SUCCESS) return st;
+    if (T > 0 && need_prep && (!q || !k || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
+    if (T > 0 && need_state && (!v || !o)) return KDA_ERROR_INVALID_VALUE;
+    const void *ptrs[] = {q, k, v, g, beta, S0, o, S_final, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
+    if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
+    const int64_t nc = max_chunks(B, T, num_seqs, packed);
+    const size_t need = kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16);
+    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    st = check_device();
+    if (st != KDA_SUCCESS) return st;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.S0 = S0; a.cu_seqlens = cu_seqlens;
+    a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
+    a.io_bf16 = io == KDA_DTYPE_BF16;
+    a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
+    a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
+    a.n_chunks_max = nc;
+    return KDA_SUCCESS;
+}
+}  // namespace
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
+                           int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
+                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_args(q, k, v, g, beta, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, o_dtype,
+                                   o, S_final, workspace, workspace_bytes, true, true, a);
+    if (st != KDA_SUCCESS) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (kda::launch_prep(a, s) != hipSuccess) return KDA_ERROR_HIP;
+    if (kda::launch_state(a, s) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
+                            const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
+                                   io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
+    if (st != KDA_SUCCESS) return st;
+    if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
+                             int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
+                             kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, S0, cu_seqlens, B, T, H, K, V, num_seqs,
+                                   chunk, io, o_dtype, o, S_final, workspace, workspace_bytes, false, true, a);
+    if (st != KDA_SUCCESS) return st;
+    if (kda::launch_state(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta, float *S,
+                             void *o, int32_t N, int32_t H, int32_t K, int32_t V, kda_dtype_t io,
+                             kda_dtype_t o_dtype, void *stream) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if (N < 0 || H < 1) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_dim(K) || !supported_dim(V)) return KDA_ERROR_NOT_SUPPORTED;
+    if ((int64_t)N * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
+    if (N == 0) return KDA_SUCCESS;
+    if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERROR_INVALID_VALUE;
+    const void *ptrs[] = {q, k, v, g, beta, S, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if ((const void *)S == q || (const void *)S == k || (const void *)S == v || (const void *)S == g ||
+        (const void *)S == beta || (const void *)S == o)
+        return KDA_ERROR_INVALID_VALUE;
+    kda_status_t st = check_device();
+    if (st != KDA_SUCCESS) return st;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.S = S; a.o = o;
+    a.N = N; a.H = H; a.K = K; a.V = V;
+    a.io_bf16 = io == KDA_DTYPE_BF16;
+    a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
+    if (kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+}  // extern "C"

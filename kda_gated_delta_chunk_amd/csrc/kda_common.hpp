@@ -1,0 +1,118 @@
+// Shared device helpers for the gfx950 KDA kernels: bf16 packing, MFMA
+// fragment types and the two matrix-core products every kernel uses.
+//
+// Matrix-core layout used throughout (one 64-lane wavefront, 16x16 output):
+//   accumulator / D tile : lane l holds D[4*(l/16) + i][l%16], i = 0..3
+//   mma16 operands       : lane l holds A[l%16][4*(l/16) + i] and
+//                          B[4*(l/16) + i][l%16], i = 0..3 (16-deep product)
+//   mma32 operands       : lane l holds 8 reduction slots, slot j <-> reduction
+//                          index 8*(l/16) + j, the same map for A and B
+//                          (32-deep product). Any bijection between slots and
+//                          reduction indices gives the same sum as long as A
+//                          and B agree; the kernels pick the map that lets an
+//                          accumulator tile pair feed a product directly.
+// A 16-deep accumulator tile therefore IS a valid B operand of mma16, which is
+// what lets the inter-chunk state and the corrected values stay in registers.
+//
+// Two element types share one code path:
+//   bf16 I/O : operands are bf16 (bit patterns in uint32 pairs), products run
+//              on v_mfma_f32_16x16x16_bf16 / v_mfma_f32_16x16x32_bf16 with fp32
+//              accumulation;
+//   fp32 I/O : operands are fp32, every product runs as a sum of
+//              v_mfma_f32_16x16x4_f32 steps (step i takes slot i of each lane,
+//              which realises the same slot map as above).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round two floats to bf16 (round-to-nearest-even, one v_cvt_pk_bf16_f32) and pack (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2 p;
+    p[0] = (__bf16)a;
+    p[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Split x into hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits in two bf16s.
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16(a, b);
+    lo = pack_bf16(a - bf_lo(hi), b - bf_hi(hi));
+}
+
+// ------------------------------------------------------------ fragment types
+// Frag4: 4 reduction slots per lane (mma16 operand). Frag8: 8 slots (mma32 operand).
+template <bool BF> struct Frag4;
+template <> struct Frag4<true> { uint32_t p[2]; };   // 4 bf16
+template <> struct Frag4<false> { float f[4]; };     // 4 fp32
+template <bool BF> struct Frag8;
+template <> struct Frag8<true> { uint32_t p[4]; };   // 8 bf16
+template <> struct Frag8<false> { float f[8]; };     // 8 fp32
+
+// Build operands from fp32 values (bf16: rounded to nearest even).
+__device__ __forceinline__ void set4(Frag4<true> &a, float x0, float x1, float x2, float x3) {
+    a.p[0] = pack_bf16(x0, x1);
+    a.p[1] = pack_bf16(x2, x3);
+}
+__device__ __forceinline__ void set4(Frag4<false> &a, float x0, float x1, float x2, float x3) {
+    a.f[0] = x0; a.f[1] = x1; a.f[2] = x2; a.f[3] = x3;
+}
+
+// D += A * B, 16 x 16 x 16.
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag4<true> &a, const Frag4<true> &b) {
+    s16x4 av = __builtin_bit_cast(s16x4, make_uint2(a.p[0], a.p[1]));
+    s16x4 bv = __builtin_bit_cast(s16x4, make_uint2(b.p[0], b.p[1]));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag4<false> &a, const Frag4<false> &b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[i], b.f[i], acc, 0, 0, 0);
+    return acc;
+}
+// D += A * B, 16 x 16 x 32.
+__device__ __forceinline__ f32x4 mma32(f32x4 acc, const Frag8<true> &a, const Frag8<true> &b) {
+    bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(a.p[0], a.p[1], a.p[2], a.p[3]));
+    bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(b.p[0], b.p[1], b.p[2], b.p[3]));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(f32x4 acc, const Frag8<false> &a, const Frag8<false> &b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[i], b.f[i], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// e^x through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// I/O element access by dtype.
+template <bool BF> struct IO;
+template <> struct IO<true> {
+    using T = uint16_t;
+    static __device__ __forceinline__ float ld(const T *p, int64_t i) { return bf2f(p[i]); }
+    static __device__ __forceinline__ void st(T *p, int64_t i, float x) {
+        bf16x2 v;
+        v[0] = (__bf16)x;
+        p[i] = __builtin_bit_cast(uint16_t, v[0]);
+    }
+};
+template <> struct IO<false> {
+    using T = float;
+    static __device__ __forceinline__ float ld(const T *p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(T *p, int64_t i, float x) { p[i] = x; }
+};
+
+}  // namespace kda

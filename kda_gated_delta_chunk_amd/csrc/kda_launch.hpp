@@ -1,0 +1,40 @@
+// Host-side launch interface between the C ABI (kda_api.hip) and the kernel
+// translation units. Internal to the library; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float *S0;
+    const int32_t *cu_seqlens;
+    int64_t B, T;
+    int32_t H, K, V, num_seqs;
+    bool io_bf16, o_bf16;
+    void *o;
+    float *S_final;
+    void *workspace;
+    int64_t n_chunks_max;  // upper bound on chunks over all sequences
+};
+
+// Workspace bytes for a prefill with at most n_chunks_max chunks.
+size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16);
+// Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
+hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
+// Enqueue the state pass over a workspace that launch_prep filled with the same sizes.
+hipError_t launch_state(const PrefillArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *S;
+    void *o;
+    int32_t N, H, K, V;
+    bool io_bf16, o_bf16;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kda

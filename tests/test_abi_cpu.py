@@ -1,0 +1,138 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every function
+include/kda.h declares, and rejects bad arguments with the documented status
+before touching the device. No kernel is launched here: every call below fails
+validation (or, on a host without a GPU, the device check)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from kda_gated_delta_chunk_amd import _lib
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "kda.h"
+
+A = 1 << 20  # a 16-byte aligned fake address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kda_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code, name in _lib.STATUS.items():
+        assert lib.kda_status_string(code).decode() == name
+    assert lib.kda_status_string(99).decode() == "KDA_ERROR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    ws = lib.kda_chunk_fwd_workspace_bytes
+    n1 = ws(1, 4096, 96, 128, 128, 1, 16, 1)
+    assert n1 > 0
+    # grows with tokens and heads; bf16 blocks are smaller than fp32 blocks
+    assert ws(1, 8192, 96, 128, 128, 1, 16, 1) > n1
+    assert ws(1, 4096, 48, 128, 128, 1, 16, 1) < n1
+    assert ws(1, 4096, 96, 128, 128, 1, 16, 0) > n1
+    # packed batches need room for one extra partial chunk per sequence
+    assert ws(1, 4096, 96, 128, 128, 16, 16, 1) > n1
+    # unsupported sizes report 0
+    assert ws(1, 4096, 96, 96, 128, 1, 16, 1) == 0
+    assert ws(1, 4096, 96, 128, 128, 1, 32, 1) == 0
+    assert ws(2, 4096, 96, 128, 128, 3, 16, 1) == 0
+    assert ws(1, 4096, 0, 128, 128, 1, 16, 1) == 0
+
+
+def _fwd(**kw):
+    lib = _lib.load()
+    a = dict(q=A, k=A, v=A, g=A, beta=A, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
+             odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"], a["T"], a["H"],
+                             a["K"], a["V"], a["N"], a["chunk"], a["io"], a["odt"], a["o"], a["Sf"], a["ws"],
+                             a["wsb"], a["stream"])
+
+
+INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(k=A + 8), INVALID),            # misaligned
+    (dict(S0=A + 4), INVALID),
+    (dict(cu=A + 2), INVALID),
+    (dict(B=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(H=0), INVALID),
+    (dict(N=2), INVALID),                # num_seqs != B without cu_seqlens
+    (dict(B=2, N=2, cu=A), INVALID),     # cu_seqlens needs B == 1
+    (dict(io=7), INVALID),
+    (dict(odt=-1), INVALID),
+    (dict(S0=A, Sf=A), INVALID),         # S0 aliases S_final
+    (dict(T=1 << 40, H=96), INVALID),    # size overflow
+    (dict(K=48), UNSUP),
+    (dict(V=256), UNSUP),
+    (dict(chunk=64), UNSUP),
+    (dict(chunk=8), UNSUP),
+    (dict(wsb=10), WS_SMALL),
+    (dict(ws=None), WS_SMALL),
+])
+def test_chunk_fwd_rejects(kw, expect):
+    assert _fwd(**kw) == expect
+
+
+def _dec(**kw):
+    lib = _lib.load()
+    a = dict(q=A, k=A, v=A, g=A, beta=A, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, odt=1, stream=None)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["o"], a["N"], a["H"], a["K"],
+                               a["V"], a["io"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(S=None), INVALID),
+    (dict(beta=None), INVALID),
+    (dict(v=A + 2), INVALID),
+    (dict(S=A), INVALID),                 # S aliases q
+    (dict(N=-1), INVALID),
+    (dict(H=0), INVALID),
+    (dict(io=3), INVALID),
+    (dict(K=16), UNSUP),
+    (dict(V=96), UNSUP),
+])
+def test_decode_rejects(kw, expect):
+    assert _dec(**kw) == expect
+
+
+def test_decode_empty_batch_is_a_no_op():
+    assert _dec(N=0, q=None, S=None) == 0
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid arguments would launch kernels on fake pointers")
+def test_valid_arguments_without_a_device_report_no_device():
+    assert _fwd() == NO_DEV
+    assert _dec() == NO_DEV

@@ -1,0 +1,74 @@
+"""GPU parity of kda_decode_step (through the C ABI) against the fp64 oracle."""
+import pytest
+import torch
+
+import oracle
+from kda_gated_delta_chunk_amd import chunk_fwd, decode_step
+from kda_gated_delta_chunk_amd import synth
+from tests.parity import TOL_BF16, TOL_FP32, err, err_stored
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _announce(name, **kw):
+    print("\n[case] %s %s" % (name, " ".join("%s=%s" % kv for kv in kw.items())), flush=True)
+
+
+def _steps(N, H, K, V, io, steps, seed):
+    S = synth.decode_state(N, H, K, V, seed=seed, device=DEV)
+    S_ref = S.double().cpu().numpy()
+    worst = {"o": 0.0, "S": 0.0}
+    for step in range(steps):
+        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV)
+        args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+        S32 = S.clone()
+        o = decode_step(*args, S)
+        o32 = decode_step(*args, S32, o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(S32, S)
+        o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref)
+        if io == "fp32":
+            worst["o"] = max(worst["o"], err(o.cpu(), o_ref))
+        else:
+            assert torch.equal(o32.to(torch.bfloat16), o)
+            worst["o"] = max(worst["o"], err(o32.cpu(), o_ref), err_stored(o.cpu(), o_ref))
+        worst["S"] = max(worst["S"], err(S.cpu(), S_ref))
+    print("  errors", worst, flush=True)
+    tol = TOL_FP32 if io == "fp32" else TOL_BF16
+    assert worst["o"] <= tol and worst["S"] <= tol, worst
+
+
+@pytest.mark.parametrize("N,H,K,V", [(3, 2, 32, 32), (2, 3, 128, 128), (5, 1, 64, 32), (1, 2, 32, 128),
+                                     (2, 2, 128, 64)])
+def test_decode_fp32(N, H, K, V):
+    _announce("decode_fp32", N=N, H=H, K=K, V=V)
+    _steps(N, H, K, V, "fp32", steps=4, seed=31)
+
+
+@pytest.mark.parametrize("N,H,K,V", [(4, 3, 128, 128), (7, 2, 64, 64)])
+def test_decode_bf16(N, H, K, V):
+    _announce("decode_bf16", N=N, H=H, K=K, V=V)
+    _steps(N, H, K, V, "bf16", steps=4, seed=32)
+
+
+def test_decode_512_streams():
+    """N=512, H=96, K=V=128, bf16 inputs, fp32 state (~3.2 GB), 3 consecutive steps, all heads."""
+    w = synth.WORKLOADS["decode_512"]
+    _announce("decode_512", seed=w.seed)
+    _steps(w.N, w.H, w.K, w.V, "bf16", steps=3, seed=w.seed)
+
+
+def test_decode_steps_equal_prefill():
+    """n decode steps from S equal one chunked prefill over the same n tokens from S."""
+    _announce("decode_vs_prefill", n=21)
+    N, H, K, V, n = 2, 2, 64, 64, 21
+    inp = synth.prefill_inputs(N, n, H, K, V, "fp32", seed=33, device=DEV, with_S0=True)
+    o_p, S_p = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"])
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(n):
+        outs.append(decode_step(*(inp[x][:, t].contiguous() for x in ("q", "k", "v", "g", "beta")), S))
+    torch.cuda.synchronize()
+    assert err(torch.stack(outs, 1).cpu(), o_p.cpu()) <= TOL_FP32
+    assert err(S.cpu(), S_p.cpu()) <= TOL_FP32
