@@ -24,7 +24,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
- *     on the current HIP device, 16-byte aligned, contiguous row-major.
+ *     on the current HIP device, contiguous row-major, 16-byte aligned
+ *     (beta: aligned to its element size; cu_seqlens: 4 bytes).
  *   - The caller owns every buffer. kda_chunk_fwd and kda_decode_step
  *     allocate nothing; kda_chunk_fwd uses only the caller's workspace.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default

@@ -16,6 +16,8 @@ constexpr int64_t kMaxElems = (int64_t)1 << 60;
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; }
+// beta is read one element at a time: natural alignment of its dtype suffices
+bool aligned_elem(const void *p, kda_dtype_t t) { return ((uintptr_t)p & (t == KDA_DTYPE_BF16 ? 1u : 3u)) == 0; }
 
 // Upper bound on chunks over all sequences: every sequence starts a chunk, so
 // packed input has at most ceil(T/C) full-or-partial chunks plus one partial
@@ -92,9 +94,10 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (st != KDA_SUCCESS) return st;
     if (T > 0 && need_prep && (!q || !k || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
     if (T > 0 && need_state && (!v || !o)) return KDA_ERROR_INVALID_VALUE;
-    const void *ptrs[] = {q, k, v, g, beta, S0, o, S_final, workspace};
+    const void *ptrs[] = {q, k, v, g, S0, o, S_final, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
     const int64_t nc = max_chunks(B, T, num_seqs, packed);
@@ -161,9 +164,10 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     if ((int64_t)N * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     if (N == 0) return KDA_SUCCESS;
     if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERROR_INVALID_VALUE;
-    const void *ptrs[] = {q, k, v, g, beta, S, o};
+    const void *ptrs[] = {q, k, v, g, S, o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if ((const void *)S == q || (const void *)S == k || (const void *)S == v || (const void *)S == g ||
         (const void *)S == beta || (const void *)S == o)
         return KDA_ERROR_INVALID_VALUE;

@@ -95,6 +95,30 @@ __device__ __forceinline__ f32x4 mma32(f32x4 acc, const Frag8<false> &a, const F
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Keep matrix-core accumulators in AGPRs. With a VGPR budget of at most 256
+// per lane (workgroups above 512 threads) the compiler otherwise selects the
+// VGPR-destination MFMA form, and in that form it has been observed to let a
+// VALU instruction overwrite a register that an in-flight dependent
+// v_mfma_f32_16x16x32_bf16 still reads as its accumulator input (wrong results
+// in the rows held by that register). Declaring a possible AGPR use makes the
+// compiler keep the AGPR form, where accumulators are not VALU-writable.
+// Extra wait states between the last matrix-core instruction of a chain and a
+// memory instruction (LDS or global store) that reads its result. The
+// compiler's own padding before such a store (8 wait states after a bf16
+// 16x16x16 / 16x16x32 product) has been observed to let the store read stale
+// accumulator values for the first elements stored, intermittently. The
+// scheduling barriers keep the stores from being hoisted above the padding.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void use_agpr_accumulators() {
+    float z = 0.f;
+    asm volatile("; agpr accumulators %0" : "+a"(z));
+}
+
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 

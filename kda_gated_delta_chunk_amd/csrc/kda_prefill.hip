@@ -67,7 +67,8 @@ struct PrepLayout {
     static constexpr int PL = PH + F4;                 // P lo part (bf16 only)
     static constexpr int TT = PL + (BF ? F4 : 0);      // T [64][4]
     static constexpr int GC = TT + F4;                 // Gamma_C [K] fp32
-    static constexpr int BYTES = GC + K * 4;
+    static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
+    static constexpr int BYTES = UNITS * 1024;
 };
 
 // --------------------------------------------------------- chunk table (K0)
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
     constexpr int CPL = K / 16;
     constexpr int KS = K / 32;
     extern __shared__ __align__(16) char smem[];
+    use_agpr_accumulators();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tg = lane >> 4, n16 = lane & 15;
     const int64_t item = (int64_t)blockIdx.x * WPB + wave;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
     for (int i = 0; i < 4; ++i) frag8_scatter_row<BF, K>(blk + L::WK, 4 * tg + i, n16 * CPL, kg[i]);
 }
 
-// ------------------------------------------------------ state pass (K3+K4)
+// Operand loads (global or LDS): 8 or 4 reduction slots per lane.
 template <bool BF>
 __device__ __forceinline__ Frag8<BF> gload8(const char *p) {
     Frag8<BF> f;
@@ -515,9 +517,33 @@ __device__ __forceinline__ Frag4<BF> gload4(const char *p) {
     return f;
 }
 
+// ------------------------------------------------------ state pass (K3+K4)
+// Asynchronous global -> LDS copy of 16 bytes per lane (64 lanes = 1 KiB, lane
+// l lands at lds + 16*l). Issued from inline assembly so that the compiler
+// does not put a full vmcnt(0) wait in front of every later LDS access of the
+// issuing wavefront: completion is awaited by hand (wait_copies). M0 holds the
+// LDS byte address.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds, const void *g) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Completion of these copies is NOT ordered: a partial vmcnt(N) wait does not
+// imply that the oldest copies have landed. Every copy is therefore awaited
+// with vmcnt(0), by a wavefront that has exactly one chunk in flight.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
 // blockIdx -> (sequence*H + head, column tile), keeping all column tiles of a
 // head on one XCD (workgroups are dealt to the 8 XCDs round-robin by index),
-// so the K-side fragments every tile of that head reads come from one L2.
+// so the fragments every tile of that head reads come from one L2.
 __device__ __forceinline__ bool state_item(int NH, int NT, int &head, int &tile) {
     const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
     head = (slot / NT) * 8 + xcd;
@@ -525,116 +551,218 @@ __device__ __forceinline__ bool state_item(int NH, int NT, int &head, int &tile)
     return head < NH;
 }
 
-template <bool BF, int K, int V, int VT>
-__global__ __launch_bounds__(VT / 16 * 64) void kda_state_pass(
+// Tiling of the state pass for value width V. A workgroup has NW compute
+// wavefronts (16 value columns each) and NL = D-1 loader wavefronts, and a
+// ring of D chunk slots in LDS (each slot = the chunk's fragment block plus
+// its v tile). Loader k copies chunks k, k+NL, k+2NL, ... so it never has more
+// than one chunk in flight, and a chunk is copied NL iterations before use.
+template <bool BF, int K, int V>
+struct StateCfg {
+    using L = PrepLayout<BF, K>;
+    static constexpr int NW = V >= 64 ? 4 : V / 16;
+    static constexpr int VT = 16 * NW;
+    static constexpr int ES = L::ES;
+    static constexpr int KU = L::UNITS;
+    static constexpr int VB = 16 * VT * ES;        // v tile bytes (16 tokens x VT columns)
+    static constexpr int VU = (VB + 1023) / 1024;
+    static constexpr int U = KU + VU;              // 1 KiB copies per chunk
+    static constexpr int SLOT = U * 1024;
+    static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
+    static constexpr int OBUF = 2 * 16 * OPITCH * 4;
+    static constexpr int DFIT = (150 * 1024 - OBUF) / SLOT;
+    static constexpr int D = DFIT > 6 ? 6 : DFIT;
+    static constexpr int NL = D - 1;
+    static constexpr int THREADS = (NW + NL) * 64;
+    static constexpr int LDS = D * SLOT + OBUF;
+    static_assert(D >= 3, "ring too shallow");
+};
+
+template <bool BF, int K, int V>
+__global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
     const void *__restrict__ vp, const float *__restrict__ S0, void *__restrict__ op, int o_bf16,
     float *__restrict__ Sfin, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
     const int32_t *__restrict__ chunk_off, const char *__restrict__ frags) {
+    using C = StateCfg<BF, K, V>;
     using L = PrepLayout<BF, K>;
-    constexpr int KS = K / 32, KT = K / 16, NT = V / VT;
-    constexpr int ES = L::ES;
+    constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, VT = C::VT, NT = V / VT, D = C::D;
+    constexpr int NL = C::NL;
+    use_agpr_accumulators();
+    extern __shared__ __align__(1024) char smem[];
+    float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
+
     int head, tile;
-    if (!state_item(N * H, NT, head, tile)) return;
+    if (!state_item(N * H, NT, head, tile)) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tg = lane >> 4, cl = lane & 15;
-    const int col = tile * VT + wave * 16 + cl;
-
-    // state columns of this wave in accumulator layout: S[rt][i] = S[16rt + 4tg + i][col]
-    f32x4 S[KT];
-    const size_t sbase = ((size_t)n * H + h) * K * V;
-#pragma unroll
-    for (int rt = 0; rt < KT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][i] = S0 ? S0[sbase + (size_t)(16 * rt + 4 * tg + i) * V + col] : 0.f;
-
-    const int c0 = chunk_off[n], c1 = chunk_off[n + 1];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int c0 = chunk_off[n], nc = chunk_off[n + 1] - c0;
     const int64_t s0 = seq_tok[n], s1 = seq_tok[n + 1];
-    for (int gc = c0; gc < c1; ++gc) {
-        const int64_t tok0 = s0 + (int64_t)(gc - c0) * CH;
-        const int nvalid = (int)((s1 - tok0) < CH ? (s1 - tok0) : CH);
-        const char *blk = frags + ((size_t)gc * H + h) * L::BYTES;
 
-        // U = T V (16 x 16 columns)
-        Frag4<BF> vf;
-        {
-            float x[4];
+    if (w >= NW) {
+        // ---------------- loader wavefront k: copies chunks k (mod NL) into the ring
+        const int k = w - NW;
+        const uint32_t lds0 = lds_u32(smem);
+        const char *vbase = reinterpret_cast<const char *>(vp);
+        auto issue = [&](int c) {
+            const char *blk = frags + ((size_t)(c0 + c) * H + h) * L::BYTES;
+            const int64_t tok0 = s0 + (int64_t)c * CH;
+            const int64_t nval = (s1 - tok0) < CH ? (s1 - tok0) : CH;
+            const uint32_t slot = lds0 + (uint32_t)((c % D) * C::SLOT);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * tg + j;
-                x[j] = (r < nvalid) ? IO<BF>::ld(reinterpret_cast<const typename IO<BF>::T *>(vp),
-                                                  ((tok0 + r) * H + h) * V + col) : 0.f;
+            for (int u = 0; u < C::KU; ++u) dma16(slot + (uint32_t)(u * 1024), blk + u * 1024 + lane * 16);
+#pragma unroll
+            for (int u = 0; u < C::VU; ++u) {
+                const int off = u * 1024 + lane * 16;
+                int64_t row = off / (VT * ES);
+                const int within = off % (VT * ES);
+                row = row < nval ? row : nval - 1;  // padding and masked rows re-read a valid row
+                const char *src = vbase + (((tok0 + row) * H + h) * V + (int64_t)tile * VT) * ES + within;
+                dma16(slot + (uint32_t)((C::KU + u) * 1024), src);
             }
-            set4(vf, x[0], x[1], x[2], x[3]);
+        };
+        if (nc > 0) {
+            for (int c = k; c < nc && c < D - 1; c += NL) issue(c);
+            for (int c = 0; c < nc; ++c) {
+                const bool mine = (c % NL) == k;
+                if (mine) wait_copies();        // chunk c (this loader's only chunk in flight) landed
+                wg_barrier();                   // B_c: chunk c visible; slot of chunk c-1 free
+                if (mine && c + NL < nc) issue(c + NL);
+            }
+            wg_barrier();                       // B_nc
         }
-        const Frag4<BF> tf = gload4<BF>(blk + L::TT + lane * 4 * ES);
-        const f32x4 U = mma16(zero4(), tf, vf);
+        return;
+    }
 
-        // state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
-        Frag8<BF> sb[KS];
+    // ---------------- compute wavefronts: 16 value columns each
+    const int tg = lane >> 4, cl = lane & 15;
+    const int lcol = w * 16 + cl, col = tile * VT + lcol;
+    f32x4 S[KT];  // S[rt][i] = S[16rt + 4tg + i][col]
+    const size_t sbase = ((size_t)n * H + h) * K * V;
+    if (S0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if constexpr (BF) {
-                sb[s].p[0] = pack_bf16(S[2 * s][0], S[2 * s][1]);
-                sb[s].p[1] = pack_bf16(S[2 * s][2], S[2 * s][3]);
-                sb[s].p[2] = pack_bf16(S[2 * s + 1][0], S[2 * s + 1][1]);
-                sb[s].p[3] = pack_bf16(S[2 * s + 1][2], S[2 * s + 1][3]);
-            } else {
+        for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sb[s].f[i] = S[2 * s][i];
-                    sb[s].f[4 + i] = S[2 * s + 1][i];
+            for (int i = 0; i < 4; ++i) S[rt][i] = S0[sbase + (size_t)(16 * rt + 4 * tg + i) * V + col];
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) S[rt] = zero4();
+    }
+
+    // write chunk c's staged o rows (fp32 in obuf[c & 1]) to global memory, 16 bytes per lane
+    auto store_o = [&](int c) {
+        const int64_t tok0 = s0 + (int64_t)c * CH;
+        const int64_t nval = (s1 - tok0) < CH ? (s1 - tok0) : CH;
+        const float *ob = obuf + (c & 1) * 16 * C::OPITCH;
+        if (o_bf16) {
+            constexpr int UPR = VT / 8;
+            for (int idx = threadIdx.x; idx < 16 * UPR; idx += NW * 64) {
+                const int row = idx / UPR, c8 = (idx % UPR) * 8;
+                if (row < nval) {
+                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
+                    const float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c8;
+                    *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w),
+                                                                 pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+                }
+            }
+        } else {
+            constexpr int UPR = VT / 4;
+            for (int idx = threadIdx.x; idx < 16 * UPR; idx += NW * 64) {
+                const int row = idx / UPR, c4 = (idx % UPR) * 4;
+                if (row < nval) {
+                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
+                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c4;
+                    *reinterpret_cast<float4 *>(dst) = a;
                 }
             }
         }
-        // W = U - Wk S
-        f32x4 X = zero4();
+    };
+
+    if (nc > 0) {
+        for (int c = 0; c < nc; ++c) {
+            lds_done_barrier();  // B_c
+            if (c > 0) store_o(c - 1);
+            const char *sl = smem + (c % D) * C::SLOT;
+
+            // U = T V (16 tokens x this wave's 16 columns)
+            Frag4<BF> vf;
+            {
+                const char *vt = sl + C::KU * 1024;
+                float x[4];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) X = mma32(X, gload8<BF>(blk + L::WK + (s * 64 + lane) * 8 * ES), sb[s]);
-        f32x4 W = U - X;
-        Frag4<BF> wh, wl;
-        if constexpr (BF) {
-            split_bf16(W[0], W[1], wh.p[0], wl.p[0]);
-            split_bf16(W[2], W[3], wh.p[1], wl.p[1]);
-        } else {
-            set4(wh, W[0], W[1], W[2], W[3]);
-        }
-        // O = (Q*Gamma) S + P W
-        f32x4 O = zero4();
+                for (int j = 0; j < 4; ++j) {
+                    const int off = ((4 * tg + j) * VT + lcol) * ES;
+                    if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
+                    else x[j] = *reinterpret_cast<const float *>(vt + off);
+                }
+                set4(vf, x[0], x[1], x[2], x[3]);
+            }
+            const f32x4 U = mma16(zero4(), gload4<BF>(sl + L::TT + lane * 4 * ES), vf);
+
+            // state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
+            Frag8<BF> sb[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            O = mma32(O, gload8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES), sb[s]);
-            if constexpr (BF) O = mma32(O, gload8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES), sb[s]);
-        }
-        {
-            const Frag4<BF> ph = gload4<BF>(blk + L::PH + lane * 4 * ES);
-            O = mma16(O, ph, wh);
+            for (int s = 0; s < KS; ++s) {
+                if constexpr (BF) {
+                    sb[s].p[0] = pack_bf16(S[2 * s][0], S[2 * s][1]);
+                    sb[s].p[1] = pack_bf16(S[2 * s][2], S[2 * s][3]);
+                    sb[s].p[2] = pack_bf16(S[2 * s + 1][0], S[2 * s + 1][1]);
+                    sb[s].p[3] = pack_bf16(S[2 * s + 1][2], S[2 * s + 1][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sb[s].f[i] = S[2 * s][i];
+                        sb[s].f[4 + i] = S[2 * s + 1][i];
+                    }
+                }
+            }
+            // W = U - Wk S
+            f32x4 X = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) X = mma32(X, gload8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES), sb[s]);
+            const f32x4 W = U - X;
+            Frag4<BF> wh, wl;
             if constexpr (BF) {
-                const Frag4<BF> pl = gload4<BF>(blk + L::PL + lane * 4 * ES);
-                O = mma16(O, ph, wl);
-                O = mma16(O, pl, wh);
+                split_bf16(W[0], W[1], wh.p[0], wl.p[0]);
+                split_bf16(W[2], W[3], wh.p[1], wl.p[1]);
+            } else {
+                set4(wh, W[0], W[1], W[2], W[3]);
+            }
+            // O = (Q*Gamma) S + P W
+            f32x4 O = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                O = mma32(O, gload8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES), sb[s]);
+                if constexpr (BF) O = mma32(O, gload8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES), sb[s]);
+            }
+            {
+                const Frag4<BF> ph = gload4<BF>(sl + L::PH + lane * 4 * ES);
+                O = mma16(O, ph, wh);
+                if constexpr (BF) {
+                    O = mma16(O, ph, wl);
+                    O = mma16(O, gload4<BF>(sl + L::PL + lane * 4 * ES), wh);
+                }
+            }
+            mfma_drain();
+            {
+                float *ob = obuf + (c & 1) * 16 * C::OPITCH;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
+            }
+            // S <- diag(Gamma_C) S + (K exp(b_C - b))^T W
+            const float *gcp = reinterpret_cast<const float *>(sl + L::GC);
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
+                S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
+                const Frag4<BF> kf = gload4<BF>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
+                S[rt] = mma16(S[rt], kf, wh);
+                if constexpr (BF) S[rt] = mma16(S[rt], kf, wl);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * tg + i;
-            if (r < nvalid) {
-                const int64_t oi = ((tok0 + r) * H + h) * V + col;
-                if (o_bf16) IO<true>::st(reinterpret_cast<uint16_t *>(op), oi, O[i]);
-                else IO<false>::st(reinterpret_cast<float *>(op), oi, O[i]);
-            }
-        }
-        // S <- diag(Gamma_C) S + (K exp(b_C - b))^T W
-        const float *gcp = reinterpret_cast<const float *>(blk + L::GC);
-#pragma unroll
-        for (int rt = 0; rt < KT; ++rt) {
-            const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
-            S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
-            const Frag4<BF> kf = gload4<BF>(blk + L::KP + (rt * 64 + lane) * 4 * ES);
-            S[rt] = mma16(S[rt], kf, wh);
-            if constexpr (BF) S[rt] = mma16(S[rt], kf, wl);
-        }
+        lds_done_barrier();  // B_nc
+        store_o(nc - 1);
     }
+    mfma_drain();
     if (Sfin) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
@@ -667,8 +795,6 @@ size_t block_bytes_rt(bool bf, int K) {
     return K == 32 ? block_bytes<false, 32>() : K == 64 ? block_bytes<false, 64>() : block_bytes<false, 128>();
 }
 
-// Value columns per state-pass workgroup (one wavefront per 16 columns).
-constexpr int state_vt(int /*V*/) { return 16; }
 
 struct WsPtrs {
     int64_t *seq_tok;
@@ -701,12 +827,19 @@ hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
 
 template <bool BF, int K, int V>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
+    using C = StateCfg<BF, K, V>;
     const WsPtrs w = ws_ptrs(a);
-    constexpr int VT = state_vt(V);
-    constexpr int NT = V / VT;
+    constexpr int NT = V / C::VT;
+    static bool lds_set = false;  // idempotent attribute; a race only repeats the call
+    if (!lds_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+        lds_set = true;
+    }
     const int64_t NH = (int64_t)a.num_seqs * a.H;
     const unsigned grid = (unsigned)(8 * ((NH + 7) / 8) * NT);
-    hipLaunchKernelGGL((kda_state_pass<BF, K, V, VT>), dim3(grid), dim3(VT / 16 * 64), 0, st, a.v, a.S0, a.o,
+    hipLaunchKernelGGL((kda_state_pass<BF, K, V>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
                        (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     return hipGetLastError();
 }

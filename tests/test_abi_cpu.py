@@ -77,6 +77,8 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(k=A + 8), INVALID),            # misaligned
     (dict(S0=A + 4), INVALID),
     (dict(cu=A + 2), INVALID),
+    (dict(beta=A + 1), INVALID),         # bf16 beta needs 2-byte alignment
+    (dict(beta=A + 2, io=0, odt=0), INVALID),  # fp32 beta needs 4-byte alignment
     (dict(B=0), INVALID),
     (dict(T=-1), INVALID),
     (dict(H=0), INVALID),
