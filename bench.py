@@ -132,12 +132,22 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short pass for hardware-counter runs: a 1 GiB device copy (calibration of the byte "
+                         "counters), then the prefill and decode steps, no CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (heads and sequences would "
               "shard without communication; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.counters:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        args.no_cpu_baseline = True
     w = synth.WORKLOADS["prefill_4k"]
     print("[bench] prefill %s: warmup %d, steps %d" % (w.name, args.warmup, args.steps), file=sys.stderr,
           flush=True)

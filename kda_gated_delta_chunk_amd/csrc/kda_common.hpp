@@ -95,25 +95,43 @@ __device__ __forceinline__ f32x4 mma32(f32x4 acc, const Frag8<false> &a, const F
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Keep matrix-core accumulators in AGPRs. With a VGPR budget of at most 256
-// per lane (workgroups above 512 threads) the compiler otherwise selects the
-// VGPR-destination MFMA form, and in that form it has been observed to let a
-// VALU instruction overwrite a register that an in-flight dependent
-// v_mfma_f32_16x16x32_bf16 still reads as its accumulator input (wrong results
-// in the rows held by that register). Declaring a possible AGPR use makes the
-// compiler keep the AGPR form, where accumulators are not VALU-writable.
-// Extra wait states between the last matrix-core instruction of a chain and a
-// memory instruction (LDS or global store) that reads its result. The
-// compiler's own padding before such a store (8 wait states after a bf16
-// 16x16x16 / 16x16x32 product) has been observed to let the store read stale
-// accumulator values for the first elements stored, intermittently. The
-// scheduling barriers keep the stores from being hoisted above the padding.
-__device__ __forceinline__ void mfma_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+// Explicit wait states between matrix-core products and the first
+// non-matrix-core instruction that reads their results (VALU, accumulator
+// read, LDS or global store). On gfx950 the compiler's own padding after a
+// bf16 16x16x16 product (8 wait states) has been observed to be too short: the
+// first elements read back (rows 4g and 4g+1 of the tile) came out stale. The
+// padding is an asm statement that takes the results as read-write
+// accumulator operands ("+a", as every product here writes AGPRs), so every
+// consumer depends on it, every producing product precedes it, and no copy
+// of the results is placed in front of the padding. (A scheduling barrier
+// alone does not stop the compiler from sinking a pure product below it.)
+__device__ __forceinline__ void mfma_fence(f32x4 &a) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a));
+}
+__device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
+}
+__device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b), "+a"(c));
+}
+// The same for a whole register tile of the state (2, 4 or 8 accumulators),
+// in one asm statement so that the padding sits between every product and its
+// readers.
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2]) { mfma_fence(x[0], x[1]); }
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[4]) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
+}
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[8]) {
+    asm volatile("s_nop 7\n\ts_nop 7"
+                 : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(x[6]), "+a"(x[7]));
 }
 
+// Keep matrix-core accumulators in AGPRs. When a kernel's VGPR budget is at
+// most 256 per lane the compiler selects the VGPR-destination MFMA form; in
+// that form on gfx950 it has been observed to reuse the accumulator-input
+// registers of a just-issued product for other values before the product read
+// them (wrong rows in the result tile). Declaring a possible AGPR use keeps the
+// AGPR form, in which only matrix-core instructions write accumulators.
 __device__ __forceinline__ void use_agpr_accumulators() {
     float z = 0.f;
     asm volatile("; agpr accumulators %0" : "+a"(z));

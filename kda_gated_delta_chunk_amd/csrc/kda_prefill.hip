@@ -344,6 +344,7 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
         Frag4<BF> gf;
         set4(gf, g[0][t], g[1][t], g[2][t], g[3][t]);
         f32x4 acc = mma16(zero4(), ltri, gf);
+        mfma_fence(acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) b[i][t] = acc[i];
         bc[t] = __shfl(acc[3], 48 + n16);  // b at the chunk's last row (masked rows add 0)
@@ -427,6 +428,7 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
             P = mma32(P, fql, fih);
         }
     }
+    mfma_fence(A, P);
     float *sA = reinterpret_cast<float *>(lds + D::A_OFF);  // [16][17]
     float *sP = reinterpret_cast<float *>(lds + D::P_OFF);
     float *sT = reinterpret_cast<float *>(lds + D::T_OFF);
@@ -482,6 +484,7 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
         Frag4<BF> kb;
         set4(kb, kg[0][t], kg[1][t], kg[2][t], kg[3][t]);
         f32x4 w = mma16(zero4(), tf, kb);
+        mfma_fence(w);
 #pragma unroll
         for (int i = 0; i < 4; ++i) kg[i][t] = w[i];  // reuse: kg now holds Wk rows 4tg+i
     }
@@ -696,7 +699,7 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
                 }
                 set4(vf, x[0], x[1], x[2], x[3]);
             }
-            const f32x4 U = mma16(zero4(), gload4<BF>(sl + L::TT + lane * 4 * ES), vf);
+            f32x4 U = mma16(zero4(), gload4<BF>(sl + L::TT + lane * 4 * ES), vf);
 
             // state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
             Frag8<BF> sb[KS];
@@ -715,54 +718,83 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
                     }
                 }
             }
-            // W = U - Wk S
-            f32x4 X = zero4();
+            // W = U - Wk S (two independent accumulation chains)
+            f32x4 X0 = zero4(), X1 = zero4();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) X = mma32(X, gload8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES), sb[s]);
-            const f32x4 W = U - X;
-            Frag4<BF> wh, wl;
-            if constexpr (BF) {
-                split_bf16(W[0], W[1], wh.p[0], wl.p[0]);
-                split_bf16(W[2], W[3], wh.p[1], wl.p[1]);
-            } else {
-                set4(wh, W[0], W[1], W[2], W[3]);
+            for (int s = 0; s < KS; s += 2) {
+                X0 = mma32(X0, gload8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES), sb[s]);
+                if (s + 1 < KS) X1 = mma32(X1, gload8<BF>(sl + L::WK + ((s + 1) * 64 + lane) * 8 * ES), sb[s + 1]);
             }
-            // O = (Q*Gamma) S + P W
-            f32x4 O = zero4();
+            mfma_fence(U, X0, X1);
+            const f32x4 W = U - (X0 + X1);
+            // O = (Q*Gamma) S + P W: the hi part, the lo part and the intra-chunk term accumulate
+            // independently and are summed at the end.
+            f32x4 Oh = zero4(), Ol = zero4(), Op = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                O = mma32(O, gload8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES), sb[s]);
-                if constexpr (BF) O = mma32(O, gload8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES), sb[s]);
+                Oh = mma32(Oh, gload8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES), sb[s]);
+                if constexpr (BF) Ol = mma32(Ol, gload8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES), sb[s]);
             }
-            {
-                const Frag4<BF> ph = gload4<BF>(sl + L::PH + lane * 4 * ES);
-                O = mma16(O, ph, wh);
-                if constexpr (BF) {
-                    O = mma16(O, ph, wl);
-                    O = mma16(O, gload4<BF>(sl + L::PL + lane * 4 * ES), wh);
-                }
-            }
-            mfma_drain();
-            {
-                float *ob = obuf + (c & 1) * 16 * C::OPITCH;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
-            }
-            // S <- diag(Gamma_C) S + (K exp(b_C - b))^T W
             const float *gcp = reinterpret_cast<const float *>(sl + L::GC);
+            if constexpr (BF) {
+                // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
+                // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
+                uint32_t wh0, wl0, wh1, wl1;
+                split_bf16(W[0], W[1], wh0, wl0);
+                split_bf16(W[2], W[3], wh1, wl1);
+                Frag8<true> whl;  // [Wh | Wl]
+                whl.p[0] = wh0; whl.p[1] = wh1; whl.p[2] = wl0; whl.p[3] = wl1;
+                const Frag4<true> ph = gload4<true>(sl + L::PH + lane * 4 * ES);
+                const Frag4<true> pl = gload4<true>(sl + L::PL + lane * 4 * ES);
+                // [Ph | Ph] x [Wh | Wl]  +  [Pl | 0] x [Wh | Wl]: every product of one
+                // accumulation chain has the same shape (a chain that mixes 16-deep and
+                // 32-deep products read a stale accumulator on gfx950).
+                Frag8<true> pp, pz;
+                pp.p[0] = ph.p[0]; pp.p[1] = ph.p[1]; pp.p[2] = ph.p[0]; pp.p[3] = ph.p[1];
+                pz.p[0] = pl.p[0]; pz.p[1] = pl.p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
+                Op = mma32(Op, pp, whl);
+                Op = mma32(Op, pz, whl);
+                mfma_fence(Oh, Ol, Op);
+                const f32x4 O = (Oh + Ol) + Op;
+                {
+                    float *ob = obuf + (c & 1) * 16 * C::OPITCH;
 #pragma unroll
-            for (int rt = 0; rt < KT; ++rt) {
-                const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
-                S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
-                const Frag4<BF> kf = gload4<BF>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
-                S[rt] = mma16(S[rt], kf, wh);
-                if constexpr (BF) S[rt] = mma16(S[rt], kf, wl);
+                    for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
+                }
+                // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]
+#pragma unroll
+                for (int rt = 0; rt < KT; ++rt) {
+                    const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
+                    S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
+                    const Frag4<true> kf = gload4<true>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
+                    Frag8<true> kk;
+                    kk.p[0] = kf.p[0]; kk.p[1] = kf.p[1]; kk.p[2] = kf.p[0]; kk.p[3] = kf.p[1];
+                    S[rt] = mma32(S[rt], kk, whl);
+                }
+                mfma_fence_all(S);
+            } else {
+                Frag4<false> wf;
+                set4(wf, W[0], W[1], W[2], W[3]);
+                Op = mma16(Op, gload4<false>(sl + L::PH + lane * 4 * ES), wf);
+                mfma_fence(Oh, Op);
+                const f32x4 O = Oh + Op;
+                {
+                    float *ob = obuf + (c & 1) * 16 * C::OPITCH;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
+                }
+#pragma unroll
+                for (int rt = 0; rt < KT; ++rt) {
+                    const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
+                    S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
+                    S[rt] = mma16(S[rt], gload4<false>(sl + L::KP + (rt * 64 + lane) * 4 * ES), wf);
+                }
+                mfma_fence_all(S);
             }
         }
         lds_done_barrier();  // B_nc
         store_o(nc - 1);
     }
-    mfma_drain();
     if (Sfin) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
