@@ -100,41 +100,30 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // read, LDS or global store). On gfx950 the compiler's own padding after a
 // bf16 16x16x16 product (8 wait states) has been observed to be too short: the
 // first elements read back (rows 4g and 4g+1 of the tile) came out stale. The
-// padding is an asm statement that takes the results as read-write
-// accumulator operands ("+a", as every product here writes AGPRs), so every
-// consumer depends on it, every producing product precedes it, and no copy
-// of the results is placed in front of the padding. (A scheduling barrier
+// padding is an asm statement that takes the results as read-write VGPR
+// operands (the kernels keep accumulators in VGPRs: their register budget is at
+// most 256 per lane), so every consumer depends on it, every producing product
+// precedes it, and no copy of the results is placed in front of the padding. (A scheduling barrier
 // alone does not stop the compiler from sinking a pure product below it.)
 __device__ __forceinline__ void mfma_fence(f32x4 &a) {
-    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a));
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a));
 }
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b) {
-    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b));
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
 }
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c) {
-    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a), "+a"(b), "+a"(c));
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c));
 }
 // The same for a whole register tile of the state (2, 4 or 8 accumulators),
 // in one asm statement so that the padding sits between every product and its
 // readers.
 __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2]) { mfma_fence(x[0], x[1]); }
 __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[4]) {
-    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
 __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[8]) {
     asm volatile("s_nop 7\n\ts_nop 7"
-                 : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(x[6]), "+a"(x[7]));
-}
-
-// Keep matrix-core accumulators in AGPRs. When a kernel's VGPR budget is at
-// most 256 per lane the compiler selects the VGPR-destination MFMA form; in
-// that form on gfx950 it has been observed to reuse the accumulator-input
-// registers of a just-issued product for other values before the product read
-// them (wrong rows in the result tile). Declaring a possible AGPR use keeps the
-// AGPR form, in which only matrix-core instructions write accumulators.
-__device__ __forceinline__ void use_agpr_accumulators() {
-    float z = 0.f;
-    asm volatile("; agpr accumulators %0" : "+a"(z));
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
 }
 
 // e^x through the hardware base-2 exponential.

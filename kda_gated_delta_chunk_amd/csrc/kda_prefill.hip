@@ -291,8 +291,10 @@ __device__ __forceinline__ void frag8_scatter_row(char *dst, int r, int kappa0, 
     }
 }
 
+// At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
+// the matrix-core accumulators in VGPRs, as mfma_fence expects.
 template <bool BF, int K, int WPB>
-__global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
+__global__ __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ gp,
     const void *__restrict__ bp, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
     const int32_t *__restrict__ chunk_off, char *__restrict__ frags) {
@@ -301,7 +303,6 @@ __global__ __launch_bounds__(WPB * 64) void kda_chunk_prep(
     constexpr int CPL = K / 16;
     constexpr int KS = K / 32;
     extern __shared__ __align__(16) char smem[];
-    use_agpr_accumulators();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tg = lane >> 4, n16 = lane & 15;
     const int64_t item = (int64_t)blockIdx.x * WPB + wave;
@@ -589,7 +590,6 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
     using L = PrepLayout<BF, K>;
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, VT = C::VT, NT = V / VT, D = C::D;
     constexpr int NL = C::NL;
-    use_agpr_accumulators();
     extern __shared__ __align__(1024) char smem[];
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
