@@ -24,6 +24,7 @@ import time
 import torch
 
 from kda_gated_delta_chunk_amd import _lib, decode_step, synth
+from kda_gated_delta_chunk_amd.source_hash import csrc_hash
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix, TFLOP/s
@@ -109,6 +110,23 @@ def time_decode(w, steps, dev):
             "bytes_per_step": bytes_step, "N": N, "H": H}
 
 
+def measured_traffic(kernel_prefix):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (profiles/traffic.json), or None if the kernels changed since it was taken."""
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("csrc_hash") != csrc_hash():
+        return None
+    for name, v in t["kernels"].items():
+        if name.startswith(kernel_prefix):
+            return v["traffic_bytes"]
+    return None
+
+
 def cpu_baseline(w):
     """The fp64 oracle on the host, on the full prefill workload (generation excluded)."""
     import oracle  # test infrastructure: only this baseline leg uses it
@@ -171,7 +189,9 @@ def main():
                    "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
                      "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms},
+                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128>" if dom == "state"
+                                                 else "kda::kda_chunk_prep<true, 128"),
+                     "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms},
         "roofline_path": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes": path_bytes,
                           "event_ms": path_ms, "mfma_tflops_algorithmic": flops / (path_ms * 1e-3) / 1e12,
@@ -190,7 +210,8 @@ def main():
                          "tokens_per_s": d["N"] / (d["ms_per_step"] * 1e-3),
                          "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                      "traffic": None, "algorithmic_bytes_per_launch": d["bytes_per_step"]}}
+                                      "traffic": measured_traffic("kda::kda_decode_kernel<true, 128, 128>"),
+                                      "algorithmic_bytes_per_launch": d["bytes_per_step"]}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -179,14 +179,11 @@ struct PrepLds {
     static constexpr int BYTES = B_OFF + 16 * 4;
 };
 
+// Load CPL consecutive values of one token row (always a valid row: callers
+// clamp the index, so no branch separates the loads and they all stay in flight).
 template <bool BF, int K>
-__device__ __forceinline__ void load_row(const void *base, int64_t idx, bool valid, float *out) {
+__device__ __forceinline__ void load_row(const void *base, int64_t idx, float *out) {
     constexpr int CPL = K / 16;
-    if (!valid) {
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) out[t] = 0.f;
-        return;
-    }
     if constexpr (BF) {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + idx;
         if constexpr (CPL == 8) {
@@ -303,7 +300,7 @@ __global__ __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int CPL = K / 16;
     constexpr int KS = K / 32;
     extern __shared__ __align__(16) char smem[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int tg = lane >> 4, n16 = lane & 15;
     const int64_t item = (int64_t)blockIdx.x * WPB + wave;
     const int total = chunk_off[N];
@@ -316,18 +313,27 @@ __global__ __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t tend = seq_tok[n + 1];
     const int nvalid = (int)((tend - tok0) < CH ? (tend - tok0) : CH);
 
-    // ---- load this lane's 4 tokens x CPL channels of q, k, g and its betas
+    // ---- load this lane's 4 tokens x CPL channels of q, k, g and its betas. Rows past the
+    // sequence end (only in its last chunk) re-read the last valid row and then act as
+    // identity tokens: g = 0 (no decay) and beta = 0 (no write); their q and k only reach
+    // outputs that are masked or multiplied by zero.
     float q[4][CPL], k[4][CPL], g[4][CPL], beta[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * tg + i;
-        const bool valid = r < nvalid;
-        const int64_t row = (tok0 + r) * H + h;
-        load_row<BF, K>(qp, row * K + n16 * CPL, valid, q[i]);
-        load_row<BF, K>(kp, row * K + n16 * CPL, valid, k[i]);
-        load_row<BF, K>(gp, row * K + n16 * CPL, valid, g[i]);
-        if constexpr (BF) beta[i] = valid ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : 0.f;
-        else beta[i] = valid ? reinterpret_cast<const float *>(bp)[row] : 0.f;
+        const int64_t row = (tok0 + (r < nvalid ? r : nvalid - 1)) * H + h;
+        load_row<BF, K>(qp, row * K + n16 * CPL, q[i]);
+        load_row<BF, K>(kp, row * K + n16 * CPL, k[i]);
+        load_row<BF, K>(gp, row * K + n16 * CPL, g[i]);
+        if constexpr (BF) beta[i] = bf2f(reinterpret_cast<const uint16_t *>(bp)[row]);
+        else beta[i] = reinterpret_cast<const float *>(bp)[row];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool valid = 4 * tg + i < nvalid;
+        beta[i] = valid ? beta[i] : 0.f;
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) g[i][t] = valid ? g[i][t] : 0.f;
     }
     float *betas = reinterpret_cast<float *>(lds + D::B_OFF);
     if (n16 == 0) {
