@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kChunk = 16;
+bool supported_chunk(int32_t c) { return c == 16; }
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
@@ -22,9 +22,9 @@ bool aligned_elem(const void *p, kda_dtype_t t) { return ((uintptr_t)p & (t == K
 // Upper bound on chunks over all sequences: every sequence starts a chunk, so
 // packed input has at most ceil(T/C) full-or-partial chunks plus one partial
 // chunk per sequence boundary.
-int64_t max_chunks(int64_t B, int64_t T, int32_t num_seqs, bool packed) {
-    if (packed) return (T + kChunk - 1) / kChunk + num_seqs;
-    return B * ((T + kChunk - 1) / kChunk);
+int64_t max_chunks(int64_t B, int64_t T, int32_t num_seqs, bool packed, int32_t chunk) {
+    if (packed) return (T + chunk - 1) / chunk + num_seqs;
+    return B * ((T + chunk - 1) / chunk);
 }
 
 // Shared size checks. Returns KDA_SUCCESS or the error to report.
@@ -32,13 +32,13 @@ kda_status_t check_prefill_sizes(int64_t B, int64_t T, int32_t H, int32_t K, int
                                  int32_t chunk, bool packed) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1 || K < 1 || V < 1) return KDA_ERROR_INVALID_VALUE;
     if (packed ? (B != 1) : (num_seqs != B)) return KDA_ERROR_INVALID_VALUE;
-    if (!supported_dim(K) || !supported_dim(V) || chunk != kChunk) return KDA_ERROR_NOT_SUPPORTED;
+    if (!supported_dim(K) || !supported_dim(V) || !supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
     // overflow: element counts, chunk indices (int32 in the kernels), grid sizes
     if (T > kMaxElems / B) return KDA_ERROR_INVALID_VALUE;
     const int64_t BT = B * T;
     if (BT > kMaxElems / H / 128) return KDA_ERROR_INVALID_VALUE;
-    const int64_t nc = max_chunks(B, T, num_seqs, packed);
-    if (nc >= ((int64_t)1 << 31) || nc * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
+    const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
+    if (nc >= ((int64_t)1 << 31) || nc * H * (chunk / 16) >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     if ((int64_t)num_seqs * H >= ((int64_t)1 << 28)) return KDA_ERROR_INVALID_VALUE;
     return KDA_SUCCESS;
 }
@@ -76,8 +76,8 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
     // B == 1 may be packed (cu_seqlens) or not; the packed bound is the larger and covers both
     const bool packed = (B == 1);
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
-    const int64_t nc = max_chunks(B, T, num_seqs, packed);
-    return kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16);
+    const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
+    return kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16, chunk);
 }
 
 namespace {
@@ -100,8 +100,8 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
-    const int64_t nc = max_chunks(B, T, num_seqs, packed);
-    const size_t need = kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16);
+    const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
+    const size_t need = kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16, chunk);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
@@ -111,6 +111,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
     a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
+    a.chunk = chunk;
     a.n_chunks_max = nc;
     return KDA_SUCCESS;
 }

@@ -114,6 +114,9 @@ __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b) {
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c) {
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c));
 }
+__device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d, f32x4 &e) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e));
+}
 // The same for a whole register tile of the state (2, 4 or 8 accumulators),
 // in one asm statement so that the padding sits between every product and its
 // readers.
@@ -125,6 +128,23 @@ __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[8]) {
     asm volatile("s_nop 7\n\ts_nop 7"
                  : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
 }
+
+// Cross-lane moves inside a 16-lane row (DPP). row_scan16 is the inclusive
+// prefix sum over the 16 lanes of each row; row_last broadcasts lane 15 of each
+// row to the whole row.
+template <int CTRL, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
+                                                                 BOUND_ZERO));
+}
+__device__ __forceinline__ float row_scan16(float x) {
+    x += dpp_f<0x111, true>(x);  // row_shr:1, lanes without a source add 0
+    x += dpp_f<0x112, true>(x);  // row_shr:2
+    x += dpp_f<0x114, true>(x);  // row_shr:4
+    x += dpp_f<0x118, true>(x);  // row_shr:8
+    return x;
+}
+__device__ __forceinline__ float row_last(float x) { return dpp_f<0x15f, false>(x); }  // row_newbcast:15
 
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }

@@ -18,11 +18,13 @@ struct PrefillArgs {
     void *o;
     float *S_final;
     void *workspace;
+    int32_t chunk;         // tokens per chunk (16 or 64)
     int64_t n_chunks_max;  // upper bound on chunks over all sequences
 };
 
 // Workspace bytes for a prefill with at most n_chunks_max chunks.
-size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16);
+size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16,
+                               int32_t chunk);
 // Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
 // Enqueue the state pass over a workspace that launch_prep filled with the same sizes.

@@ -1,7 +1,7 @@
 // Chunked KDA prefill for gfx950: chunk table, chunk-prep and state-pass kernels.
 //
-// Chunk form of the recurrence (per sequence and head; C = 16 tokens per
-// chunk, r and i index tokens inside a chunk, kappa indexes key channels):
+// Chunk form of the recurrence (per sequence and head; C tokens per chunk,
+// r and i index tokens inside a chunk, kappa indexes key channels):
 //   b_r     = g_1 + ... + g_r                     cumulative log-decay (per channel)
 //   Gamma_r = exp(b_r)
 //   A[r,i]  = beta_r sum_kappa k_r k_i exp(b_r - b_i)      for i < r, else 0
@@ -19,22 +19,25 @@
 // exp(-b_r) of a 16-token tile stay inside BF16 range (at most e^80), which is
 // what lets A and P run as dense bf16 products.
 //
+// Chunks are processed in 16-token sub-tiles (one matrix-core tile row).
+//
 // Kernels (one call of kda_chunk_fwd launches all three on one stream):
 //   kda_chunk_table  one workgroup: clamps cu_seqlens, numbers the chunks
 //                    (each sequence starts a new chunk; its last chunk may be
 //                    partial) and writes the per-sequence chunk offsets.
-//   kda_chunk_prep   one wavefront per (chunk, head): everything that does not
-//                    depend on the state — cumulative decay (a 16x16 lower
-//                    triangle of ones times g on the matrix cores), the decay
-//                    scaled operands, A and P (bf16 products, fp32 accumulate),
-//                    the 16x16 solve for T (fp32, in LDS), Wk = T (K*Gamma) —
-//                    written to the workspace already in matrix-core fragment
-//                    order so the state pass reads them with 16-byte loads.
+//   kda_chunk_prep   one wavefront per (sub-tile, head), lane = token row:
+//                    everything that does not depend on the state. Cumulative
+//                    decay (a prefix sum across the 16 lanes of a row), the
+//                    decay-scaled operands, A and P (bf16 products, fp32
+//                    accumulate, operands straight from registers), the
+//                    solve for T (fp32), Wk = T (K*Gamma); written to the
+//                    workspace in matrix-core fragment order, every lane
+//                    storing whole 8- or 16-byte runs.
 //   kda_state_pass   one workgroup per (sequence, head, tile of VT value
-//                    columns), one wavefront per 16 columns; walks the chunks
-//                    in order with its 16 columns of the fp32 state held in
-//                    accumulator registers, computes W, O and the state update
-//                    on the matrix cores, writes o and S_final. Value columns
+//                    columns), one wavefront per 16 columns; walks the
+//                    sub-tiles in order with its 16 columns of the fp32 state
+//                    held in registers, computes W, O and the state update on
+//                    the matrix cores, writes o and S_final. Value columns
 //                    never interact (decay scales rows only), so the column
 //                    split is exact.
 //
@@ -48,25 +51,41 @@
 
 namespace kda {
 
-constexpr int CH = 16;  // tokens per chunk
+constexpr int SUB = 16;  // tokens per sub-tile
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ------------------------------------------------------------ channel order
+// The state pass keeps key channel state_row_channel(rho) in state row rho:
+// for rho = 32 s + 16 h + 4 a + j (h < 2, a < 4, j < 4) that channel is
+// 32 s + 8 a + 4 h + j. A 32-deep product over state rows 32s .. 32s+31 then
+// gives lane group a the eight consecutive key channels 32s + 8a .. 32s + 8a + 7,
+// so every operand indexed by key channel is a plain 16-byte run of a token row.
+__host__ __device__ constexpr int state_row_channel(int rho) {
+    return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
 
 // ------------------------------------------------------------------ layout
-// Per (chunk, head) block of the workspace, in bytes (ES = element size).
-template <bool BF, int K>
-struct PrepLayout {
+// Workspace block per (chunk, head, sub-tile), in bytes (ES = element size).
+// Fragment orders (lane = 16 * a + m):
+//   [KS][64][8]: lane (a, m) holds token m, key channels 32s + 8a .. +7
+//   [KT][64][4]: state update, tile rt: lane (a, m) holds tokens 4a .. 4a+3 of
+//                key channel state_row_channel(16 rt + m)
+//   [CS][64][4]: 16x16 tile I of a row block: lane (a, m) holds row m, columns 4a .. 4a+3
+template <bool BF, int K, int CS>
+struct SubLayout {
     static constexpr int ES = BF ? 2 : 4;
     static constexpr int KS = K / 32;  // 32-deep reduction steps over key channels
     static constexpr int KT = K / 16;  // 16-row tiles of the state
-    static constexpr int F8 = 64 * 8 * ES;  // one mma32 operand, whole wave
-    static constexpr int F4 = 64 * 4 * ES;  // one mma16 operand, whole wave
-    static constexpr int WK = 0;                       // Wk      [KS][64][8]
-    static constexpr int QH = WK + KS * F8;            // Q*Gamma [KS][64][8] (hi)
-    static constexpr int QL = QH + KS * F8;            // Q*Gamma lo part (bf16 only)
-    static constexpr int KP = QL + (BF ? KS * F8 : 0); // K*exp(b_C-b) [KT][64][4]
-    static constexpr int PH = KP + KT * F4;            // P [64][4] (hi)
-    static constexpr int PL = PH + F4;                 // P lo part (bf16 only)
-    static constexpr int TT = PL + (BF ? F4 : 0);      // T [64][4]
-    static constexpr int GC = TT + F4;                 // Gamma_C [K] fp32
+    static constexpr int F8 = 64 * 8 * ES;
+    static constexpr int F4 = 64 * 4 * ES;
+    static constexpr int WK = 0;                        // Wk rows [KS][64][8]
+    static constexpr int QH = WK + KS * F8;             // Q*Gamma [KS][64][8] (hi)
+    static constexpr int QL = QH + KS * F8;             // Q*Gamma lo part (bf16 only)
+    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b) [KT][64][4]
+    static constexpr int PH = KP + KT * F4;             // P tiles [CS][64][4] (hi)
+    static constexpr int PL = PH + CS * F4;             // P lo part (bf16 only)
+    static constexpr int TT = PL + (BF ? CS * F4 : 0);  // T tiles [CS][64][4]
+    static constexpr int GC = TT + CS * F4;             // Gamma_C [K] fp32 in state-row order (sub-tile 0)
     static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
     static constexpr int BYTES = UNITS * 1024;
 };
@@ -104,7 +123,7 @@ __device__ __forceinline__ int64_t block_scan_excl_sum(int64_t x, int64_t *sh) {
 }
 
 __global__ __launch_bounds__(1024) void kda_chunk_table(const int32_t *__restrict__ cu, int32_t N,
-                                                         int64_t T_row, int64_t total_tokens,
+                                                         int64_t T_row, int64_t total_tokens, int32_t C,
                                                          int64_t *__restrict__ seq_tok,
                                                          int32_t *__restrict__ chunk_off) {
     __shared__ int64_t sh[1024];
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(1024) void kda_chunk_table(const int32_t *__restric
         if (m < N) {
             int64_t s2 = start_of(m + 1);
             int64_t nxt = s2 > cur ? s2 : cur;
-            cnt += (nxt - cur + CH - 1) / CH;
+            cnt += (nxt - cur + C - 1) / C;
         }
     }
     const int64_t cbase = block_scan_excl_sum(cnt, sh);
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(1024) void kda_chunk_table(const int32_t *__restric
             int64_t s = seq_tok[m];  // written by this thread above
             int64_t s2 = start_of(m + 1);
             int64_t nxt = s2 > s ? s2 : s;
-            c += (nxt - s + CH - 1) / CH;
+            c += (nxt - s + C - 1) / C;
         }
     }
 }
@@ -164,367 +183,329 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int gc)
 // (waits for outstanding LDS operations; also a compiler reordering barrier).
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); }
 
-// LDS per wavefront: five [16][K+pad] operand tiles, A, P, T (fp32 16x16), beta.
+// LDS of the prep kernel, per wavefront: a transposed [K][16] operand tile
+// (K*Gamma for Wk, then K*exp(b_C-b)), A^T and T of the 16x16 tile, P and the
+// sub-tile's betas.
 template <bool BF, int K>
 struct PrepLds {
-    static constexpr int PITCH = BF ? (K + 8) : (K + 4);  // elements; 16-byte pad
     static constexpr int ES = BF ? 2 : 4;
-    static constexpr int TILE = 16 * PITCH * ES;
-    static constexpr int NT = BF ? 5 : 3;  // KG, KIGh, (KIGl), QGh, (QGl)
-    static constexpr int MAT = NT * TILE;
-    static constexpr int A_OFF = MAT;
-    static constexpr int P_OFF = A_OFF + 16 * 17 * 4;
-    static constexpr int T_OFF = P_OFF + 16 * 17 * 4;
-    static constexpr int B_OFF = T_OFF + 16 * 17 * 4;
-    static constexpr int BYTES = B_OFF + 16 * 4;
+    static constexpr int MP = 20;                  // pitch (floats) of 16x16 matrices
+    static constexpr int M16 = 16 * MP * 4;
+    static constexpr int XT = 0;                   // [K][16 tokens]
+    static constexpr int SA = XT + K * 16 * ES;    // A^T
+    static constexpr int ST = SA + M16;            // T
+    static constexpr int SP = ST + M16;            // P
+    static constexpr int SB = SP + M16;            // beta [16]
+    static constexpr int WAVE = SB + 64;
 };
 
-// Load CPL consecutive values of one token row (always a valid row: callers
-// clamp the index, so no branch separates the loads and they all stay in flight).
-template <bool BF, int K>
-__device__ __forceinline__ void load_row(const void *base, int64_t idx, float *out) {
-    constexpr int CPL = K / 16;
+// Eight consecutive values of one token row (one 16-byte bf16 / two fp32 loads).
+template <bool BF>
+__device__ __forceinline__ void load8(const void *base, int64_t idx, float (&x)[8]) {
     if constexpr (BF) {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + idx;
-        if constexpr (CPL == 8) {
-            uint4 w = *reinterpret_cast<const uint4 *>(p);
-            out[0] = bf_lo(w.x); out[1] = bf_hi(w.x); out[2] = bf_lo(w.y); out[3] = bf_hi(w.y);
-            out[4] = bf_lo(w.z); out[5] = bf_hi(w.z); out[6] = bf_lo(w.w); out[7] = bf_hi(w.w);
-        } else if constexpr (CPL == 4) {
-            uint2 w = *reinterpret_cast<const uint2 *>(p);
-            out[0] = bf_lo(w.x); out[1] = bf_hi(w.x); out[2] = bf_lo(w.y); out[3] = bf_hi(w.y);
-        } else {
-            uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-            out[0] = bf_lo(w); out[1] = bf_hi(w);
-        }
+        const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + idx);
+        x[0] = bf_lo(w.x); x[1] = bf_hi(w.x); x[2] = bf_lo(w.y); x[3] = bf_hi(w.y);
+        x[4] = bf_lo(w.z); x[5] = bf_hi(w.z); x[6] = bf_lo(w.w); x[7] = bf_hi(w.w);
     } else {
         const float *p = reinterpret_cast<const float *>(base) + idx;
-#pragma unroll
-        for (int t = 0; t < CPL; t += 2) {
-            float2 w = *reinterpret_cast<const float2 *>(p + t);
-            out[t] = w.x; out[t + 1] = w.y;
-        }
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }
 }
 
-// Store CPL consecutive values of one token row into an LDS operand tile.
-template <bool BF, int K>
-__device__ __forceinline__ void lds_row_store(char *tile, int row, int col0, const float *x) {
-    constexpr int CPL = K / 16;
-    constexpr int PITCH = PrepLds<BF, K>::PITCH;
-    if constexpr (BF) {
-        uint32_t w[CPL / 2];
+// mma32 operands from eight fp32 values: rounded (single) or split into hi + lo.
+__device__ __forceinline__ Frag8<true> frag8_of(const float (&x)[8], Frag8<true>) {
+    Frag8<true> f;
 #pragma unroll
-        for (int t = 0; t < CPL / 2; ++t) w[t] = pack_bf16(x[2 * t], x[2 * t + 1]);
-        uint16_t *p = reinterpret_cast<uint16_t *>(tile) + row * PITCH + col0;
-        if constexpr (CPL == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-        else if constexpr (CPL == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
-        else *reinterpret_cast<uint32_t *>(p) = w[0];
+    for (int t = 0; t < 4; ++t) f.p[t] = pack_bf16(x[2 * t], x[2 * t + 1]);
+    return f;
+}
+__device__ __forceinline__ Frag8<false> frag8_of(const float (&x)[8], Frag8<false>) {
+    Frag8<false> f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.f[t] = x[t];
+    return f;
+}
+__device__ __forceinline__ void split8(const float (&x)[8], Frag8<true> &hi, Frag8<true> &lo) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) split_bf16(x[2 * t], x[2 * t + 1], hi.p[t], lo.p[t]);
+}
+__device__ __forceinline__ void split8(const float (&x)[8], Frag8<false> &hi, Frag8<false> &) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) hi.f[t] = x[t];
+}
+__device__ __forceinline__ void split4(const float4 &x, Frag4<true> &hi, Frag4<true> &lo) {
+    split_bf16(x.x, x.y, hi.p[0], lo.p[0]);
+    split_bf16(x.z, x.w, hi.p[1], lo.p[1]);
+}
+__device__ __forceinline__ void split4(const float4 &x, Frag4<false> &hi, Frag4<false> &) {
+    set4(hi, x.x, x.y, x.z, x.w);
+}
+
+// Operand fragments to / from memory (global or LDS; 8- or 16-byte aligned runs).
+template <bool BF>
+__device__ __forceinline__ void st_frag8(char *dst, const Frag8<BF> &f) {
+    if constexpr (BF) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(f.p[0], f.p[1], f.p[2], f.p[3]);
     } else {
-        float *p = reinterpret_cast<float *>(tile) + row * PITCH + col0;
-#pragma unroll
-        for (int t = 0; t < CPL; t += 2) *reinterpret_cast<float2 *>(p + t) = make_float2(x[t], x[t + 1]);
+        *reinterpret_cast<float4 *>(dst) = make_float4(f.f[0], f.f[1], f.f[2], f.f[3]);
+        *reinterpret_cast<float4 *>(dst + 16) = make_float4(f.f[4], f.f[5], f.f[6], f.f[7]);
     }
 }
-
-// mma32 operand from an LDS tile: row `row`, key channels 32*s + 8*(lane/16) + j.
-template <bool BF, int K>
-__device__ __forceinline__ Frag8<BF> lds_frag8(const char *tile, int row, int s, int grp) {
-    constexpr int PITCH = PrepLds<BF, K>::PITCH;
-    Frag8<BF> f;
-    const int col = 32 * s + 8 * grp;
+template <bool BF>
+__device__ __forceinline__ void st_frag4(char *dst, const Frag4<BF> &f) {
+    if constexpr (BF) *reinterpret_cast<uint2 *>(dst) = make_uint2(f.p[0], f.p[1]);
+    else *reinterpret_cast<float4 *>(dst) = make_float4(f.f[0], f.f[1], f.f[2], f.f[3]);
+}
+template <bool BF>
+__device__ __forceinline__ Frag4<BF> ld_frag4(const char *p) {
+    Frag4<BF> f;
     if constexpr (BF) {
-        uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(tile) + row * PITCH + col);
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        f.p[0] = w.x; f.p[1] = w.y;
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        f.f[0] = a.x; f.f[1] = a.y; f.f[2] = a.z; f.f[3] = a.w;
+    }
+    return f;
+}
+template <bool BF>
+__device__ __forceinline__ Frag8<BF> ld_frag8(const char *p) {
+    Frag8<BF> f;
+    if constexpr (BF) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(p);
         f.p[0] = w.x; f.p[1] = w.y; f.p[2] = w.z; f.p[3] = w.w;
     } else {
-        const float *p = reinterpret_cast<const float *>(tile) + row * PITCH + col;
-        float4 a = *reinterpret_cast<const float4 *>(p);
-        float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 16);
         f.f[0] = a.x; f.f[1] = a.y; f.f[2] = a.z; f.f[3] = a.w;
         f.f[4] = b.x; f.f[5] = b.y; f.f[6] = b.z; f.f[7] = b.w;
     }
     return f;
 }
-
-// Write `n` (1, 2 or 4) consecutive operand values to global memory.
+// One element of an operand tile in LDS (bf16: rounded to nearest even).
 template <bool BF>
-__device__ __forceinline__ void gstore_run(char *dst, const float *x, int n) {
+__device__ __forceinline__ void st_elem(char *base, int idx, float x) {
     if constexpr (BF) {
-        if (n == 4) *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
-        else if (n == 2) *reinterpret_cast<uint32_t *>(dst) = pack_bf16(x[0], x[1]);
-        else {
-            bf16x2 v;
-            v[0] = (__bf16)x[0];
-            *reinterpret_cast<uint16_t *>(dst) = __builtin_bit_cast(uint16_t, v[0]);
-        }
+        bf16x2 v;
+        v[0] = (__bf16)x;
+        reinterpret_cast<uint16_t *>(base)[idx] = __builtin_bit_cast(uint16_t, v[0]);
     } else {
-        if (n == 4) *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-        else if (n == 2) *reinterpret_cast<float2 *>(dst) = make_float2(x[0], x[1]);
-        else *reinterpret_cast<float *>(dst) = x[0];
+        reinterpret_cast<float *>(base)[idx] = x;
     }
 }
+// Four consecutive values (bf16 packed or fp32).
+template <bool BF>
+__device__ __forceinline__ void st_run4(char *dst, float a, float b, float c, float d) {
+    if constexpr (BF) *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
+    else *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
+}
 
-// Scatter one token row (channels kappa0 .. kappa0+CPL-1 of token r) of a
-// [16][K] operand into mma32 fragment order for the state pass:
-//   step s = kappa/32, o = kappa%32;
-//   o < 16 : lane group g = o/4,      slot j = o%4
-//   o >= 16: lane group g = (o-16)/4, slot j = 4 + o%4
-//   lane = 16*g + r, element ((s*64 + lane)*8 + j).
-// Slots 0..3 / 4..7 then match state rows 32s+4g+j and 32s+16+4g+(j-4), the
-// rows a lane holds in its accumulator tiles 2s and 2s+1.
-template <bool BF, int K>
-__device__ __forceinline__ void frag8_scatter_row(char *dst, int r, int kappa0, const float *x) {
-    constexpr int CPL = K / 16;
-    constexpr int RUN = CPL < 4 ? CPL : 4;
-    constexpr int ES = BF ? 2 : 4;
+// x[4g + i] for a lane-group index g known only at run time (no register indexing).
+__device__ __forceinline__ float pick16(const float (&x)[16], int g, int i) {
+    const float a = x[i], b = x[4 + i], c = x[8 + i], d = x[12 + i];
+    return g == 0 ? a : g == 1 ? b : g == 2 ? c : d;
+}
+
+// Forward substitution for X = (I + A)^{-1}, A strictly lower 16x16, stored
+// transposed in LDS (row j = column j of A, pitch MP floats). The lane owning
+// column n ends with column n of X in x[0..15] (right-looking: once x[j] is
+// final, every later row subtracts its multiple, so the updates of one step
+// are independent of each other).
+template <int MP>
+__device__ __forceinline__ void solve16(const float *sAT, int n, float (&x)[16]) {
 #pragma unroll
-    for (int t = 0; t < CPL; t += RUN) {
-        const int kappa = kappa0 + t;
-        const int s = kappa >> 5, o = kappa & 31;
-        const int g = (o < 16) ? (o >> 2) : ((o - 16) >> 2);
-        const int j = (o < 16) ? (o & 3) : (4 + (o & 3));
-        const int lane = 16 * g + r;
-        gstore_run<BF>(dst + (size_t)((s * 64 + lane) * 8 + j) * ES, x + t, RUN);
+    for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == n) ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+        float col[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 c = *reinterpret_cast<const float4 *>(sAT + j * MP + 4 * q4);
+            col[4 * q4] = c.x; col[4 * q4 + 1] = c.y; col[4 * q4 + 2] = c.z; col[4 * q4 + 3] = c.w;
+        }
+#pragma unroll
+        for (int rr = j + 1; rr < 16; ++rr) x[rr] = __builtin_fmaf(-col[rr], x[j], x[rr]);
     }
 }
 
 // At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
 // the matrix-core accumulators in VGPRs, as mfma_fence expects.
-template <bool BF, int K, int WPB>
-__global__ __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(
+template <bool BF, int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ gp,
     const void *__restrict__ bp, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
     const int32_t *__restrict__ chunk_off, char *__restrict__ frags) {
-    using L = PrepLayout<BF, K>;
+    using L = SubLayout<BF, K, 1>;
     using D = PrepLds<BF, K>;
-    constexpr int CPL = K / 16;
-    constexpr int KS = K / 32;
+    constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP;
     extern __shared__ __align__(16) char smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int tg = lane >> 4, n16 = lane & 15;
-    const int64_t item = (int64_t)blockIdx.x * WPB + wave;
+    const int ag = lane >> 4, r = lane & 15;  // lane group; token (row) or column in a tile
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
     const int total = chunk_off[N];
     const int gc = (int)(item / H), h = (int)(item % H);
-    if (gc >= total) return;  // wave-uniform; no block-level barriers in this kernel
-    char *lds = smem + wave * D::BYTES;
+    if (gc >= total) return;  // wave-uniform; no workgroup barriers in this kernel
+    char *lds = smem + wave * D::WAVE;
+    char *xt = lds + D::XT;
+    float *sAT = reinterpret_cast<float *>(lds + D::SA);
+    float *sT = reinterpret_cast<float *>(lds + D::ST);
+    float *sP = reinterpret_cast<float *>(lds + D::SP);
+    float *sB = reinterpret_cast<float *>(lds + D::SB);
 
     const int n = find_seq(chunk_off, N, gc);
-    const int64_t tok0 = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * CH;
+    const int64_t tok0 = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * SUB;
     const int64_t tend = seq_tok[n + 1];
-    const int nvalid = (int)((tend - tok0) < CH ? (tend - tok0) : CH);
+    const int nvalid = (int)((tend - tok0) < SUB ? (tend - tok0) : SUB);  // >= 1
 
-    // ---- load this lane's 4 tokens x CPL channels of q, k, g and its betas. Rows past the
-    // sequence end (only in its last chunk) re-read the last valid row and then act as
-    // identity tokens: g = 0 (no decay) and beta = 0 (no write); their q and k only reach
-    // outputs that are masked or multiplied by zero.
-    float q[4][CPL], k[4][CPL], g[4][CPL], beta[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * tg + i;
-        const int64_t row = (tok0 + (r < nvalid ? r : nvalid - 1)) * H + h;
-        load_row<BF, K>(qp, row * K + n16 * CPL, q[i]);
-        load_row<BF, K>(kp, row * K + n16 * CPL, k[i]);
-        load_row<BF, K>(gp, row * K + n16 * CPL, g[i]);
-        if constexpr (BF) beta[i] = bf2f(reinterpret_cast<const uint16_t *>(bp)[row]);
-        else beta[i] = reinterpret_cast<const float *>(bp)[row];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool valid = 4 * tg + i < nvalid;
-        beta[i] = valid ? beta[i] : 0.f;
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) g[i][t] = valid ? g[i][t] : 0.f;
-    }
-    float *betas = reinterpret_cast<float *>(lds + D::B_OFF);
-    if (n16 == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) betas[4 * tg + i] = beta[i];
-    }
-
-    // ---- cumulative log-decay: b = Ltri * g on the matrix cores (exact inputs, fp32 sums)
-    Frag4<BF> ltri;
-    set4(ltri, (4 * tg + 0 <= n16) ? 1.f : 0.f, (4 * tg + 1 <= n16) ? 1.f : 0.f,
-         (4 * tg + 2 <= n16) ? 1.f : 0.f, (4 * tg + 3 <= n16) ? 1.f : 0.f);
-    float b[4][CPL], bc[CPL];
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-        Frag4<BF> gf;
-        set4(gf, g[0][t], g[1][t], g[2][t], g[3][t]);
-        f32x4 acc = mma16(zero4(), ltri, gf);
-        mfma_fence(acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) b[i][t] = acc[i];
-        bc[t] = __shfl(acc[3], 48 + n16);  // b at the chunk's last row (masked rows add 0)
-    }
-
-    // ---- decay-scaled operands (fp32), staged to LDS for A and P, scattered to the workspace
-    char *blk = frags + ((size_t)gc * H + h) * L::BYTES;
-    char *tKG = lds, *tKIh = lds + D::TILE, *tQh = lds + 2 * D::TILE;
-    char *tKIl = lds + 3 * D::TILE, *tQl = lds + 4 * D::TILE;  // bf16 only
-    float kg[4][CPL];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * tg + i;
-        float kig[CPL], qg[CPL];
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) {
-            const float gam = exp_e(b[i][t]);
-            kg[i][t] = k[i][t] * gam;
-            kig[t] = k[i][t] * exp_e(-b[i][t]);
-            qg[t] = q[i][t] * gam;
-        }
-        lds_row_store<BF, K>(tKG, r, n16 * CPL, kg[i]);
-        if constexpr (BF) {
-            float hi[CPL], lo[CPL];
-#pragma unroll
-            for (int t = 0; t < CPL; ++t) {
-                hi[t] = __uint_as_float(pack_bf16(kig[t], 0.f) << 16);
-                lo[t] = kig[t] - hi[t];
-            }
-            lds_row_store<BF, K>(tKIh, r, n16 * CPL, hi);
-            lds_row_store<BF, K>(tKIl, r, n16 * CPL, lo);
-#pragma unroll
-            for (int t = 0; t < CPL; ++t) {
-                hi[t] = __uint_as_float(pack_bf16(qg[t], 0.f) << 16);
-                lo[t] = qg[t] - hi[t];
-            }
-            lds_row_store<BF, K>(tQh, r, n16 * CPL, hi);
-            lds_row_store<BF, K>(tQl, r, n16 * CPL, lo);
-            frag8_scatter_row<BF, K>(blk + L::QH, r, n16 * CPL, hi);
-            frag8_scatter_row<BF, K>(blk + L::QL, r, n16 * CPL, lo);
-        } else {
-            lds_row_store<BF, K>(tKIh, r, n16 * CPL, kig);
-            lds_row_store<BF, K>(tQh, r, n16 * CPL, qg);
-            frag8_scatter_row<BF, K>(blk + L::QH, r, n16 * CPL, qg);
-        }
-    }
-    // K * exp(b_C - b) as mma16 A operands of the state update: tile kappa/16, lane 16*tg + kappa%16
-    {
-        constexpr int ES = L::ES;
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) {
-            const int kappa = n16 * CPL + t;
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = k[i][t] * exp_e(bc[t] - b[i][t]);
-            const int rt = kappa >> 4, ln = 16 * tg + (kappa & 15);
-            gstore_run<BF>(blk + L::KP + (size_t)((rt * 64 + ln) * 4) * ES, x, 4);
-        }
-    }
-    if (tg == 3) {  // Gamma_C, fp32
-        float *gcp = reinterpret_cast<float *>(blk + L::GC);
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) gcp[n16 * CPL + t] = exp_e(bc[t]);
-    }
-    lds_sync();
-
-    // ---- A = tril_strict(diag(beta) KG KIG^T), P = tril(QG KIG^T) (reduction over key channels)
-    f32x4 A = zero4(), P = zero4();
+    // ---- this lane's token row: key channels 32s + 8ag .. +7 of q, k, g, and beta. Rows
+    // past the sequence end re-read the last valid row and act as identity tokens (g = 0:
+    // no decay, beta = 0: no write); their q and k only reach masked or zero-weighted terms.
+    const bool valid = r < nvalid;
+    const int64_t row = (tok0 + (valid ? r : nvalid - 1)) * H + h;
+    float qv[KS][8], kv[KS][8], bl[KS][8];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        Frag8<BF> fk = lds_frag8<BF, K>(tKG, n16, s, tg);
-        Frag8<BF> fih = lds_frag8<BF, K>(tKIh, n16, s, tg);
-        Frag8<BF> fqh = lds_frag8<BF, K>(tQh, n16, s, tg);
-        A = mma32(A, fk, fih);
-        P = mma32(P, fqh, fih);
+        load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+        load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+        load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    }
+    float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
+    beta = valid ? beta : 0.f;
+
+    // ---- cumulative log-decay in base 2 (prefix over the 16 token lanes) and the chunk total
+    float bt[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bl[s][j] = row_scan16(valid ? bl[s][j] * LOG2E : 0.f);
+            bt[s][j] = row_last(bl[s][j]);
+        }
+    if (ag == 0) sB[r] = beta;
+
+    // ---- decay-scaled operands. Q*Gamma goes straight to the workspace (its fragment order
+    // is this lane's row layout); K*Gamma is transposed through LDS for Wk.
+    char *blk = frags + ((size_t)gc * H + h) * L::BYTES;
+    Frag8<BF> qh[KS], ql[KS], kgf[KS], kih[KS], kil[KS];
+    float kpv[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        float qg[8], kg[8], ki[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(bl[s][j]);
+            const float ei = __builtin_amdgcn_exp2f(-bl[s][j]);
+            qg[j] = qv[s][j] * e;
+            kg[j] = kv[s][j] * e;
+            ki[j] = kv[s][j] * ei;
+            kpv[s][j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
+            st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
+        }
+        split8(qg, qh[s], ql[s]);
+        kgf[s] = frag8_of(kg, Frag8<BF>{});
+        split8(ki, kih[s], kil[s]);
+        st_frag8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES, qh[s]);
+        if constexpr (BF) st_frag8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES, ql[s]);
+    }
+
+    // ---- A = K*Gamma (K/Gamma)^T and P = Q*Gamma (K/Gamma)^T over key channels: both
+    // operands are lane registers (token r, eight channels per step).
+    f32x4 A0 = zero4(), A1 = zero4(), P0 = zero4(), P1 = zero4(), P2 = zero4();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        A0 = mma32(A0, kgf[s], kih[s]);
+        P0 = mma32(P0, qh[s], kih[s]);
         if constexpr (BF) {
-            Frag8<BF> fil = lds_frag8<BF, K>(tKIl, n16, s, tg);
-            Frag8<BF> fql = lds_frag8<BF, K>(tQl, n16, s, tg);
-            A = mma32(A, fk, fil);
-            P = mma32(P, fqh, fil);
-            P = mma32(P, fql, fih);
+            A1 = mma32(A1, kgf[s], kil[s]);
+            P1 = mma32(P1, qh[s], kil[s]);
+            P2 = mma32(P2, ql[s], kih[s]);
         }
     }
-    mfma_fence(A, P);
-    float *sA = reinterpret_cast<float *>(lds + D::A_OFF);  // [16][17]
-    float *sP = reinterpret_cast<float *>(lds + D::P_OFF);
-    float *sT = reinterpret_cast<float *>(lds + D::T_OFF);
+    mfma_fence(A0, A1, P0, P1, P2);
+    lds_sync();  // betas visible
+    {
+        // lane (ag, r) holds rows 4ag+i, column r; A^T goes to LDS for the solve, P row-major
+        const float4 bet = *reinterpret_cast<const float4 *>(sB + 4 * ag);
+        const float bv[4] = {bet.x, bet.y, bet.z, bet.w};
+        float at[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * tg + i;  // row; column = n16
-        sA[r * 17 + n16] = (n16 < r) ? beta[i] * A[i] : 0.f;
-        sP[r * 17 + n16] = (n16 <= r) ? P[i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int ri = 4 * ag + i;
+            at[i] = (r < ri) ? bv[i] * (A0[i] + A1[i]) : 0.f;
+            sP[ri * MP + r] = (r <= ri) ? (P0[i] + P1[i]) + P2[i] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(sAT + r * MP + 4 * ag) = make_float4(at[0], at[1], at[2], at[3]);
     }
     lds_sync();
 
-    // ---- T = (I + A)^{-1} diag(beta): forward substitution, lane n16 owns column n16 (fp32)
+    // ---- T = (I + A)^{-1} diag(beta): this lane's column r, scaled by its own beta;
+    // lane group ag writes rows 4ag..4ag+3
     {
         float x[16];
+        solve16<MP>(sAT, r, x);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == n16) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < r; ++j) acc -= sA[r * 17 + j] * x[j];
-            x[r] = acc;
-        }
-        const float bn = betas[n16];
-        if (tg == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sT[r * 17 + n16] = x[r] * bn;
-        }
+        for (int i = 0; i < 4; ++i) sT[(4 * ag + i) * MP + r] = pick16(x, ag, i) * beta;
     }
     lds_sync();
 
-    // ---- fragments of T and P for mma16 A operands: lane holds row n16, columns 4*tg..4*tg+3
+    // ---- T and P fragments (lane (ag, m=r): row r, columns 4ag..4ag+3) to the workspace
     Frag4<BF> tf;
     {
-        const float *tr = sT + n16 * 17 + 4 * tg;
-        set4(tf, tr[0], tr[1], tr[2], tr[3]);
-        const float *pr = sP + n16 * 17 + 4 * tg;
-        constexpr int ES = L::ES;
-        if constexpr (BF) {
-            uint32_t h0, l0, h1, l1;
-            split_bf16(pr[0], pr[1], h0, l0);
-            split_bf16(pr[2], pr[3], h1, l1);
-            *reinterpret_cast<uint2 *>(blk + L::PH + lane * 4 * ES) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2 *>(blk + L::PL + lane * 4 * ES) = make_uint2(l0, l1);
-            *reinterpret_cast<uint2 *>(blk + L::TT + lane * 4 * ES) = make_uint2(tf.p[0], tf.p[1]);
-        } else {
-            *reinterpret_cast<float4 *>(blk + L::PH + lane * 16) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-            *reinterpret_cast<float4 *>(blk + L::TT + lane * 16) = make_float4(tf.f[0], tf.f[1], tf.f[2], tf.f[3]);
+        const float4 tv = *reinterpret_cast<const float4 *>(sT + r * MP + 4 * ag);
+        const float4 pv = *reinterpret_cast<const float4 *>(sP + r * MP + 4 * ag);
+        set4(tf, tv.x, tv.y, tv.z, tv.w);
+        Frag4<BF> ph, pl;
+        split4(pv, ph, pl);
+        st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
+        st_frag4<BF>(blk + L::PH + lane * 4 * ES, ph);
+        if constexpr (BF) st_frag4<BF>(blk + L::PL + lane * 4 * ES, pl);
+    }
+
+    // ---- Wk^T = (K*Gamma)^T T^T, one 16-channel tile t at a time: A operand from the
+    // transposed tile (lane (ag, m): channel 16t+m, tokens 4ag..4ag+3), B operand = the T
+    // fragment. Result lane (ag, r): Wk[r][16t + 4ag + i], which are slots 4(ag%2)..+3 of
+    // the [KS][64][8] fragment of lane 16(2(t%2) + ag/2) + r in step t/2.
+    {
+        f32x4 w[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            w[t] = mma16(zero4(), ld_frag4<BF>(xt + ((16 * t + r) * 16 + 4 * ag) * ES), tf);
+        mfma_fence_all(w);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int dl = 16 * (2 * (t & 1) + (ag >> 1)) + r;
+            st_run4<BF>(blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES, w[t][0], w[t][1], w[t][2],
+                        w[t][3]);
         }
     }
+    lds_sync();  // the Wk reads of the tile are done before it is overwritten
 
-    // ---- Wk = T (K * Gamma): B operand = this lane's own KG values (tokens 4tg+i, one channel)
+    // ---- K*exp(b_C - b): transposed through the same tile, then out in state-row order
 #pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-        Frag4<BF> kb;
-        set4(kb, kg[0][t], kg[1][t], kg[2][t], kg[3][t]);
-        f32x4 w = mma16(zero4(), tf, kb);
-        mfma_fence(w);
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kg[i][t] = w[i];  // reuse: kg now holds Wk rows 4tg+i
+        for (int j = 0; j < 8; ++j) st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kpv[s][j]);
+    lds_sync();
+#pragma unroll
+    for (int rt = 0; rt < KT; ++rt) {
+        const int kappa = state_row_channel(16 * rt + r);
+        st_frag4<BF>(blk + L::KP + (rt * 64 + lane) * 4 * ES, ld_frag4<BF>(xt + (kappa * 16 + 4 * ag) * ES));
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) frag8_scatter_row<BF, K>(blk + L::WK, 4 * tg + i, n16 * CPL, kg[i]);
-}
 
-// Operand loads (global or LDS): 8 or 4 reduction slots per lane.
-template <bool BF>
-__device__ __forceinline__ Frag8<BF> gload8(const char *p) {
-    Frag8<BF> f;
-    if constexpr (BF) {
-        uint4 w = *reinterpret_cast<const uint4 *>(p);
-        f.p[0] = w.x; f.p[1] = w.y; f.p[2] = w.z; f.p[3] = w.w;
-    } else {
-        float4 a = *reinterpret_cast<const float4 *>(p);
-        float4 b = *reinterpret_cast<const float4 *>(p + 16);
-        f.f[0] = a.x; f.f[1] = a.y; f.f[2] = a.z; f.f[3] = a.w;
-        f.f[4] = b.x; f.f[5] = b.y; f.f[6] = b.z; f.f[7] = b.w;
+    // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
+    if (r == 0) {
+        float *gcp = reinterpret_cast<float *>(blk + L::GC);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(bt[s][j]);
+            *reinterpret_cast<float4 *>(gcp + 32 * s + 4 * ag) = make_float4(e[0], e[1], e[2], e[3]);
+            *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
+        }
     }
-    return f;
-}
-template <bool BF>
-__device__ __forceinline__ Frag4<BF> gload4(const char *p) {
-    Frag4<BF> f;
-    if constexpr (BF) {
-        uint2 w = *reinterpret_cast<const uint2 *>(p);
-        f.p[0] = w.x; f.p[1] = w.y;
-    } else {
-        float4 a = *reinterpret_cast<const float4 *>(p);
-        f.f[0] = a.x; f.f[1] = a.y; f.f[2] = a.z; f.f[3] = a.w;
-    }
-    return f;
 }
 
 // ------------------------------------------------------ state pass (K3+K4)
@@ -542,7 +523,7 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void *g) {
 
 // Completion of these copies is NOT ordered: a partial vmcnt(N) wait does not
 // imply that the oldest copies have landed. Every copy is therefore awaited
-// with vmcnt(0), by a wavefront that has exactly one chunk in flight.
+// with vmcnt(0), by a wavefront that has exactly one sub-tile in flight.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -563,19 +544,19 @@ __device__ __forceinline__ bool state_item(int NH, int NT, int &head, int &tile)
 
 // Tiling of the state pass for value width V. A workgroup has NW compute
 // wavefronts (16 value columns each) and NL = D-1 loader wavefronts, and a
-// ring of D chunk slots in LDS (each slot = the chunk's fragment block plus
-// its v tile). Loader k copies chunks k, k+NL, k+2NL, ... so it never has more
-// than one chunk in flight, and a chunk is copied NL iterations before use.
-template <bool BF, int K, int V>
+// ring of D sub-tile slots in LDS (each slot = the sub-tile's workspace block
+// plus its v tile). Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never
+// has more than one in flight, and a sub-tile is copied NL steps before use.
+template <bool BF, int K, int V, int CS>
 struct StateCfg {
-    using L = PrepLayout<BF, K>;
+    using L = SubLayout<BF, K, CS>;
     static constexpr int NW = V >= 64 ? 4 : V / 16;
     static constexpr int VT = 16 * NW;
     static constexpr int ES = L::ES;
     static constexpr int KU = L::UNITS;
     static constexpr int VB = 16 * VT * ES;        // v tile bytes (16 tokens x VT columns)
     static constexpr int VU = (VB + 1023) / 1024;
-    static constexpr int U = KU + VU;              // 1 KiB copies per chunk
+    static constexpr int U = KU + VU;              // 1 KiB copies per sub-tile
     static constexpr int SLOT = U * 1024;
     static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
     static constexpr int OBUF = 2 * 16 * OPITCH * 4;
@@ -587,13 +568,13 @@ struct StateCfg {
     static_assert(D >= 3, "ring too shallow");
 };
 
-template <bool BF, int K, int V>
-__global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
+template <bool BF, int K, int V, int CS>
+__global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_pass(
     const void *__restrict__ vp, const float *__restrict__ S0, void *__restrict__ op, int o_bf16,
     float *__restrict__ Sfin, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
     const int32_t *__restrict__ chunk_off, const char *__restrict__ frags) {
-    using C = StateCfg<BF, K, V>;
-    using L = PrepLayout<BF, K>;
+    using C = StateCfg<BF, K, V, CS>;
+    using L = SubLayout<BF, K, CS>;
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, VT = C::VT, NT = V / VT, D = C::D;
     constexpr int NL = C::NL;
     extern __shared__ __align__(1024) char smem[];
@@ -603,40 +584,41 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
     if (!state_item(N * H, NT, head, tile)) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c0 = chunk_off[n], nc = chunk_off[n + 1] - c0;
+    const int c0 = chunk_off[n], nu = (chunk_off[n + 1] - c0) * CS;  // sub-tile steps
     const int64_t s0 = seq_tok[n], s1 = seq_tok[n + 1];
 
     if (w >= NW) {
-        // ---------------- loader wavefront k: copies chunks k (mod NL) into the ring
+        // ---------------- loader wavefront k: copies sub-tiles k (mod NL) into the ring
         const int k = w - NW;
         const uint32_t lds0 = lds_u32(smem);
         const char *vbase = reinterpret_cast<const char *>(vp);
-        auto issue = [&](int c) {
-            const char *blk = frags + ((size_t)(c0 + c) * H + h) * L::BYTES;
-            const int64_t tok0 = s0 + (int64_t)c * CH;
-            const int64_t nval = (s1 - tok0) < CH ? (s1 - tok0) : CH;
-            const uint32_t slot = lds0 + (uint32_t)((c % D) * C::SLOT);
+        auto issue = [&](int u) {
+            const char *blk = frags + (((size_t)(c0 + u / CS) * H + h) * CS + u % CS) * L::BYTES;
+            const int64_t tok0 = s0 + (int64_t)u * SUB;
+            const int64_t nval = s1 - tok0;  // <= 0 for the empty tail sub-tiles of a 64-token chunk
+            const uint32_t slot = lds0 + (uint32_t)((u % D) * C::SLOT);
 #pragma unroll
-            for (int u = 0; u < C::KU; ++u) dma16(slot + (uint32_t)(u * 1024), blk + u * 1024 + lane * 16);
+            for (int q = 0; q < C::KU; ++q) dma16(slot + (uint32_t)(q * 1024), blk + q * 1024 + lane * 16);
 #pragma unroll
-            for (int u = 0; u < C::VU; ++u) {
-                const int off = u * 1024 + lane * 16;
-                int64_t row = off / (VT * ES);
+            for (int q = 0; q < C::VU; ++q) {
+                const int off = q * 1024 + lane * 16;
+                const int64_t rw = off / (VT * ES);
                 const int within = off % (VT * ES);
-                row = row < nval ? row : nval - 1;  // padding and masked rows re-read a valid row
-                const char *src = vbase + (((tok0 + row) * H + h) * V + (int64_t)tile * VT) * ES + within;
-                dma16(slot + (uint32_t)((C::KU + u) * 1024), src);
+                // padding and masked rows re-read a valid token of the sequence
+                const int64_t tok = (rw < nval) ? tok0 + rw : s1 - 1;
+                const char *src = vbase + ((tok * H + h) * V + (int64_t)tile * VT) * ES + within;
+                dma16(slot + (uint32_t)((C::KU + q) * 1024), src);
             }
         };
-        if (nc > 0) {
-            for (int c = k; c < nc && c < D - 1; c += NL) issue(c);
-            for (int c = 0; c < nc; ++c) {
-                const bool mine = (c % NL) == k;
-                if (mine) wait_copies();        // chunk c (this loader's only chunk in flight) landed
-                wg_barrier();                   // B_c: chunk c visible; slot of chunk c-1 free
-                if (mine && c + NL < nc) issue(c + NL);
+        if (nu > 0) {
+            for (int u = k; u < nu && u < D - 1; u += NL) issue(u);
+            for (int u = 0; u < nu; ++u) {
+                const bool mine = (u % NL) == k;
+                if (mine) wait_copies();        // sub-tile u (this loader's only copy in flight) landed
+                wg_barrier();                   // B_u: sub-tile u visible; slot of sub-tile u-1 free
+                if (mine && u + NL < nu) issue(u + NL);
             }
-            wg_barrier();                       // B_nc
+            wg_barrier();                       // B_nu
         }
         return;
     }
@@ -644,23 +626,44 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
     // ---------------- compute wavefronts: 16 value columns each
     const int tg = lane >> 4, cl = lane & 15;
     const int lcol = w * 16 + cl, col = tile * VT + lcol;
-    f32x4 S[KT];  // S[rt][i] = S[16rt + 4tg + i][col]
+    f32x4 S[KT];  // S[rt][i] = S[key channel state_row_channel(16rt + 4tg + i)][col]
     const size_t sbase = ((size_t)n * H + h) * K * V;
     if (S0) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[rt][i] = S0[sbase + (size_t)(16 * rt + 4 * tg + i) * V + col];
+            for (int i = 0; i < 4; ++i)
+                S[rt][i] = S0[sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + col];
     } else {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt) S[rt] = zero4();
     }
+    // the state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
+    Frag8<BF> sb[KS];
+    auto pack_state = [&]() {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if constexpr (BF) {
+                sb[s].p[0] = pack_bf16(S[2 * s][0], S[2 * s][1]);
+                sb[s].p[1] = pack_bf16(S[2 * s][2], S[2 * s][3]);
+                sb[s].p[2] = pack_bf16(S[2 * s + 1][0], S[2 * s + 1][1]);
+                sb[s].p[3] = pack_bf16(S[2 * s + 1][2], S[2 * s + 1][3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sb[s].f[i] = S[2 * s][i];
+                    sb[s].f[4 + i] = S[2 * s + 1][i];
+                }
+            }
+        }
+    };
+    pack_state();
 
-    // write chunk c's staged o rows (fp32 in obuf[c & 1]) to global memory, 16 bytes per lane
-    auto store_o = [&](int c) {
-        const int64_t tok0 = s0 + (int64_t)c * CH;
-        const int64_t nval = (s1 - tok0) < CH ? (s1 - tok0) : CH;
-        const float *ob = obuf + (c & 1) * 16 * C::OPITCH;
+    // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
+    auto store_o = [&](int u) {
+        const int64_t tok0 = s0 + (int64_t)u * SUB;
+        const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
+        const float *ob = obuf + (u & 1) * 16 * C::OPITCH;
         if (o_bf16) {
             constexpr int UPR = VT / 8;
             for (int idx = threadIdx.x; idx < 16 * UPR; idx += NW * 64) {
@@ -686,126 +689,116 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
         }
     };
 
-    if (nc > 0) {
-        for (int c = 0; c < nc; ++c) {
-            lds_done_barrier();  // B_c
-            if (c > 0) store_o(c - 1);
-            const char *sl = smem + (c % D) * C::SLOT;
+    for (int u = 0; u < nu; ++u) {
+        lds_done_barrier();  // B_u
+        if (u > 0) store_o(u - 1);
+        const char *sl = smem + (u % D) * C::SLOT;
 
-            // U = T V (16 tokens x this wave's 16 columns)
-            Frag4<BF> vf;
-            {
-                const char *vt = sl + C::KU * 1024;
-                float x[4];
+        // ---- every LDS operand of this step, read up front in order of use
+        const Frag4<BF> tt = ld_frag4<BF>(sl + L::TT + lane * 4 * ES);
+        Frag4<BF> vf;
+        {
+            const char *vt = sl + C::KU * 1024;
+            float x[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int off = ((4 * tg + j) * VT + lcol) * ES;
-                    if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
-                    else x[j] = *reinterpret_cast<const float *>(vt + off);
-                }
-                set4(vf, x[0], x[1], x[2], x[3]);
+            for (int j = 0; j < 4; ++j) {
+                const int off = ((4 * tg + j) * VT + lcol) * ES;
+                if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
+                else x[j] = *reinterpret_cast<const float *>(vt + off);
             }
-            f32x4 U = mma16(zero4(), gload4<BF>(sl + L::TT + lane * 4 * ES), vf);
+            set4(vf, x[0], x[1], x[2], x[3]);
+        }
+        Frag8<BF> wk[KS], qh[KS], ql[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
+            if constexpr (BF) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
+        }
+        const Frag4<BF> ph = ld_frag4<BF>(sl + L::PH + lane * 4 * ES);
+        Frag4<BF> pl;
+        if constexpr (BF) pl = ld_frag4<BF>(sl + L::PL + lane * 4 * ES);
+        Frag4<BF> kpf[KT];
+        float4 gm[KT];
+        const float *gcp = reinterpret_cast<const float *>(sl + L::GC);
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) {
+            kpf[rt] = ld_frag4<BF>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
+            gm[rt] = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
+        }
 
-            // state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
-            Frag8<BF> sb[KS];
+        // ---- W = T V - Wk S (the state product in two independent accumulation chains)
+        f32x4 U = mma16(zero4(), tt, vf);
+        f32x4 X0 = zero4(), X1 = zero4();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if constexpr (BF) {
-                    sb[s].p[0] = pack_bf16(S[2 * s][0], S[2 * s][1]);
-                    sb[s].p[1] = pack_bf16(S[2 * s][2], S[2 * s][3]);
-                    sb[s].p[2] = pack_bf16(S[2 * s + 1][0], S[2 * s + 1][1]);
-                    sb[s].p[3] = pack_bf16(S[2 * s + 1][2], S[2 * s + 1][3]);
-                } else {
+        for (int s = 0; s < KS; s += 2) {
+            X0 = mma32(X0, wk[s], sb[s]);
+            if (s + 1 < KS) X1 = mma32(X1, wk[s + 1], sb[s + 1]);
+        }
+        mfma_fence(U, X0, X1);
+        const f32x4 W = U - (X0 + X1);
+        // ---- O = (Q*Gamma) S + P W: hi part, lo part and intra-chunk term accumulate apart
+        f32x4 Oh = zero4(), Ol = zero4(), Op = zero4();
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sb[s].f[i] = S[2 * s][i];
-                        sb[s].f[4 + i] = S[2 * s + 1][i];
-                    }
-                }
+        for (int s = 0; s < KS; ++s) {
+            Oh = mma32(Oh, qh[s], sb[s]);
+            if constexpr (BF) Ol = mma32(Ol, ql[s], sb[s]);
+        }
+        if constexpr (BF) {
+            // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
+            // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
+            uint32_t wh0, wl0, wh1, wl1;
+            split_bf16(W[0], W[1], wh0, wl0);
+            split_bf16(W[2], W[3], wh1, wl1);
+            Frag8<true> whl;  // [Wh | Wl]
+            whl.p[0] = wh0; whl.p[1] = wh1; whl.p[2] = wl0; whl.p[3] = wl1;
+            // [Ph | Ph] x [Wh | Wl]  +  [Pl | 0] x [Wh | Wl]: every product of one
+            // accumulation chain has the same shape (a chain that mixes 16-deep and
+            // 32-deep products read a stale accumulator on gfx950).
+            Frag8<true> pp, pz;
+            pp.p[0] = ph.p[0]; pp.p[1] = ph.p[1]; pp.p[2] = ph.p[0]; pp.p[3] = ph.p[1];
+            pz.p[0] = pl.p[0]; pz.p[1] = pl.p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
+            Op = mma32(Op, pp, whl);
+            Op = mma32(Op, pz, whl);
+            // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                S[rt][0] *= gm[rt].x; S[rt][1] *= gm[rt].y; S[rt][2] *= gm[rt].z; S[rt][3] *= gm[rt].w;
+                Frag8<true> kk;
+                kk.p[0] = kpf[rt].p[0]; kk.p[1] = kpf[rt].p[1]; kk.p[2] = kpf[rt].p[0]; kk.p[3] = kpf[rt].p[1];
+                S[rt] = mma32(S[rt], kk, whl);
             }
-            // W = U - Wk S (two independent accumulation chains)
-            f32x4 X0 = zero4(), X1 = zero4();
+        } else {
+            Frag4<false> wf;
+            set4(wf, W[0], W[1], W[2], W[3]);
+            Op = mma16(Op, ph, wf);
 #pragma unroll
-            for (int s = 0; s < KS; s += 2) {
-                X0 = mma32(X0, gload8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES), sb[s]);
-                if (s + 1 < KS) X1 = mma32(X1, gload8<BF>(sl + L::WK + ((s + 1) * 64 + lane) * 8 * ES), sb[s + 1]);
-            }
-            mfma_fence(U, X0, X1);
-            const f32x4 W = U - (X0 + X1);
-            // O = (Q*Gamma) S + P W: the hi part, the lo part and the intra-chunk term accumulate
-            // independently and are summed at the end.
-            f32x4 Oh = zero4(), Ol = zero4(), Op = zero4();
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                Oh = mma32(Oh, gload8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES), sb[s]);
-                if constexpr (BF) Ol = mma32(Ol, gload8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES), sb[s]);
-            }
-            const float *gcp = reinterpret_cast<const float *>(sl + L::GC);
-            if constexpr (BF) {
-                // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
-                // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
-                uint32_t wh0, wl0, wh1, wl1;
-                split_bf16(W[0], W[1], wh0, wl0);
-                split_bf16(W[2], W[3], wh1, wl1);
-                Frag8<true> whl;  // [Wh | Wl]
-                whl.p[0] = wh0; whl.p[1] = wh1; whl.p[2] = wl0; whl.p[3] = wl1;
-                const Frag4<true> ph = gload4<true>(sl + L::PH + lane * 4 * ES);
-                const Frag4<true> pl = gload4<true>(sl + L::PL + lane * 4 * ES);
-                // [Ph | Ph] x [Wh | Wl]  +  [Pl | 0] x [Wh | Wl]: every product of one
-                // accumulation chain has the same shape (a chain that mixes 16-deep and
-                // 32-deep products read a stale accumulator on gfx950).
-                Frag8<true> pp, pz;
-                pp.p[0] = ph.p[0]; pp.p[1] = ph.p[1]; pp.p[2] = ph.p[0]; pp.p[3] = ph.p[1];
-                pz.p[0] = pl.p[0]; pz.p[1] = pl.p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
-                Op = mma32(Op, pp, whl);
-                Op = mma32(Op, pz, whl);
-                mfma_fence(Oh, Ol, Op);
-                const f32x4 O = (Oh + Ol) + Op;
-                {
-                    float *ob = obuf + (c & 1) * 16 * C::OPITCH;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
-                }
-                // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]
-#pragma unroll
-                for (int rt = 0; rt < KT; ++rt) {
-                    const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
-                    S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
-                    const Frag4<true> kf = gload4<true>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
-                    Frag8<true> kk;
-                    kk.p[0] = kf.p[0]; kk.p[1] = kf.p[1]; kk.p[2] = kf.p[0]; kk.p[3] = kf.p[1];
-                    S[rt] = mma32(S[rt], kk, whl);
-                }
-                mfma_fence_all(S);
-            } else {
-                Frag4<false> wf;
-                set4(wf, W[0], W[1], W[2], W[3]);
-                Op = mma16(Op, gload4<false>(sl + L::PH + lane * 4 * ES), wf);
-                mfma_fence(Oh, Op);
-                const f32x4 O = Oh + Op;
-                {
-                    float *ob = obuf + (c & 1) * 16 * C::OPITCH;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
-                }
-#pragma unroll
-                for (int rt = 0; rt < KT; ++rt) {
-                    const float4 gm = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
-                    S[rt][0] *= gm.x; S[rt][1] *= gm.y; S[rt][2] *= gm.z; S[rt][3] *= gm.w;
-                    S[rt] = mma16(S[rt], gload4<false>(sl + L::KP + (rt * 64 + lane) * 4 * ES), wf);
-                }
-                mfma_fence_all(S);
+            for (int rt = 0; rt < KT; ++rt) {
+                S[rt][0] *= gm[rt].x; S[rt][1] *= gm[rt].y; S[rt][2] *= gm[rt].z; S[rt][3] *= gm[rt].w;
+                S[rt] = mma16(S[rt], kpf[rt], wf);
             }
         }
-        lds_done_barrier();  // B_nc
-        store_o(nc - 1);
+        mfma_fence(Oh, Ol, Op);
+        {
+            const f32x4 O = (Oh + Ol) + Op;
+            float *ob = obuf + (u & 1) * 16 * C::OPITCH;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
+        }
+        mfma_fence_all(S);
+        pack_state();  // operand for the next step
+    }
+    if (nu > 0) {
+        lds_done_barrier();  // B_nu
+        store_o(nu - 1);
     }
     if (Sfin) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Sfin[sbase + (size_t)(16 * rt + 4 * tg + i) * V + col] = S[rt][i];
+            for (int i = 0; i < 4; ++i)
+                Sfin[sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + col] = S[rt][i];
     }
 }
 
@@ -817,7 +810,6 @@ __global__ __launch_bounds__((StateCfg<BF, K, V>::THREADS)) void kda_state_pass(
 namespace kda {
 namespace {
 
-constexpr int PREP_WPB = 2;  // wavefronts (= (chunk, head) items) per prep workgroup
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -825,14 +817,13 @@ size_t table_bytes(int32_t num_seqs) {
     return align_up((size_t)(num_seqs + 1) * sizeof(int64_t)) + align_up((size_t)(num_seqs + 1) * sizeof(int32_t));
 }
 
-template <bool BF, int K>
-size_t block_bytes() { return (size_t)PrepLayout<BF, K>::BYTES; }
+template <bool BF, int K, int CS>
+size_t chunk_bytes() { return (size_t)CS * SubLayout<BF, K, CS>::BYTES; }
 
-size_t block_bytes_rt(bool bf, int K) {
-    if (bf) return K == 32 ? block_bytes<true, 32>() : K == 64 ? block_bytes<true, 64>() : block_bytes<true, 128>();
-    return K == 32 ? block_bytes<false, 32>() : K == 64 ? block_bytes<false, 64>() : block_bytes<false, 128>();
+size_t chunk_bytes_rt(bool bf, int K) {
+    if (bf) return K == 32 ? chunk_bytes<true, 32, 1>() : K == 64 ? chunk_bytes<true, 64, 1>() : chunk_bytes<true, 128, 1>();
+    return K == 32 ? chunk_bytes<false, 32, 1>() : K == 64 ? chunk_bytes<false, 64, 1>() : chunk_bytes<false, 128, 1>();
 }
-
 
 struct WsPtrs {
     int64_t *seq_tok;
@@ -852,32 +843,33 @@ template <bool BF, int K>
 hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
     hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
-                       w.seq_tok, w.chunk_off);
+                       (int32_t)SUB, w.seq_tok, w.chunk_off);
     if (a.n_chunks_max > 0) {
         const int64_t items = a.n_chunks_max * a.H;
-        const unsigned grid = (unsigned)((items + PREP_WPB - 1) / PREP_WPB);
-        const size_t lds = (size_t)PREP_WPB * PrepLds<BF, K>::BYTES;
-        hipLaunchKernelGGL((kda_chunk_prep<BF, K, PREP_WPB>), dim3(grid), dim3(PREP_WPB * 64), lds, st, a.q, a.k,
-                           a.g, a.beta, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
+        const unsigned grid = (unsigned)((items + 3) / 4);
+        const size_t lds = 4 * (size_t)PrepLds<BF, K>::WAVE;
+        hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3(grid), dim3(256), lds, st, a.q, a.k, a.g, a.beta, a.H,
+                           a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     }
     return hipGetLastError();
 }
 
 template <bool BF, int K, int V>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
-    using C = StateCfg<BF, K, V>;
+    constexpr int CS = 1;
+    using C = StateCfg<BF, K, V, CS>;
     const WsPtrs w = ws_ptrs(a);
     constexpr int NT = V / C::VT;
     static bool lds_set = false;  // idempotent attribute; a race only repeats the call
     if (!lds_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
         if (e != hipSuccess) return e;
         lds_set = true;
     }
     const int64_t NH = (int64_t)a.num_seqs * a.H;
     const unsigned grid = (unsigned)(8 * ((NH + 7) / 8) * NT);
-    hipLaunchKernelGGL((kda_state_pass<BF, K, V>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
+    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
                        (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     return hipGetLastError();
 }
@@ -893,8 +885,10 @@ hipError_t state_k(const PrefillArgs &a, hipStream_t st) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16) {
-    return table_bytes(num_seqs) + (size_t)n_chunks_max * (size_t)H * block_bytes_rt(io_bf16, K);
+size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16,
+                               int32_t chunk) {
+    (void)chunk;
+    return table_bytes(num_seqs) + (size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K);
 }
 
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t st) {
