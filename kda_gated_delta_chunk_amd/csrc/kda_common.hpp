@@ -117,6 +117,9 @@ __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c) {
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d, f32x4 &e) {
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e));
 }
+__device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d, f32x4 &e, f32x4 &f) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f));
+}
 // The same for a whole register tile of the state (2, 4 or 8 accumulators),
 // in one asm statement so that the padding sits between every product and its
 // readers.
@@ -145,6 +148,43 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 __device__ __forceinline__ float row_last(float x) { return dpp_f<0x15f, false>(x); }  // row_newbcast:15
+// Lane k of each 16-lane row, broadcast to the row (row_newbcast:k); k must be a compile-time constant.
+__device__ __forceinline__ float row_bcast(float x, int k) {
+    switch (k) {
+        case 0: return dpp_f<0x150, false>(x);
+        case 1: return dpp_f<0x151, false>(x);
+        case 2: return dpp_f<0x152, false>(x);
+        case 3: return dpp_f<0x153, false>(x);
+        case 4: return dpp_f<0x154, false>(x);
+        case 5: return dpp_f<0x155, false>(x);
+        case 6: return dpp_f<0x156, false>(x);
+        case 7: return dpp_f<0x157, false>(x);
+        case 8: return dpp_f<0x158, false>(x);
+        case 9: return dpp_f<0x159, false>(x);
+        case 10: return dpp_f<0x15a, false>(x);
+        case 11: return dpp_f<0x15b, false>(x);
+        case 12: return dpp_f<0x15c, false>(x);
+        case 13: return dpp_f<0x15d, false>(x);
+        case 14: return dpp_f<0x15e, false>(x);
+        default: return dpp_f<0x15f, false>(x);
+    }
+}
+
+// Two column tiles of the state (2 x 2, 2 x 4 or 2 x 8 accumulators), one asm statement.
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2][2]) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[1][0]), "+v"(x[1][1]));
+}
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2][4]) {
+    asm volatile("s_nop 7\n\ts_nop 7"
+                 : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]), "+v"(x[1][1]),
+                   "+v"(x[1][2]), "+v"(x[1][3]));
+}
+__device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2][8]) {
+    asm volatile("s_nop 7\n\ts_nop 7"
+                 : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[0][4]), "+v"(x[0][5]),
+                   "+v"(x[0][6]), "+v"(x[0][7]), "+v"(x[1][0]), "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]),
+                   "+v"(x[1][4]), "+v"(x[1][5]), "+v"(x[1][6]), "+v"(x[1][7]));
+}
 
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }

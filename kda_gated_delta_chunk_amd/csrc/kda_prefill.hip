@@ -67,10 +67,13 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 // ------------------------------------------------------------------ layout
 // Workspace block per (chunk, head, sub-tile), in bytes (ES = element size).
 // Fragment orders (lane = 16 * a + m):
-//   [KS][64][8]: lane (a, m) holds token m, key channels 32s + 8a .. +7
-//   [KT][64][4]: state update, tile rt: lane (a, m) holds tokens 4a .. 4a+3 of
-//                key channel state_row_channel(16 rt + m)
-//   [CS][64][4]: 16x16 tile I of a row block: lane (a, m) holds row m, columns 4a .. 4a+3
+//   [KS][64][8]  : lane (a, m) holds token m, key channels 32s + 8a .. +7
+//   [KT/2][64][8]: state update, tiles rt = 2p (slots 0..3) and 2p+1 (slots 4..7):
+//                  lane (a, m) holds tokens 4a .. 4a+3 of key channel
+//                  state_row_channel(16 rt + m)
+//   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
+//                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
+//                  columns 4a .. 4a+3
 template <bool BF, int K, int CS>
 struct SubLayout {
     static constexpr int ES = BF ? 2 : 4;
@@ -78,13 +81,12 @@ struct SubLayout {
     static constexpr int KT = K / 16;  // 16-row tiles of the state
     static constexpr int F8 = 64 * 8 * ES;
     static constexpr int F4 = 64 * 4 * ES;
-    static constexpr int WK = 0;                        // Wk rows [KS][64][8]
+    static constexpr int WK = 0;                        // -Wk rows [KS][64][8]
     static constexpr int QH = WK + KS * F8;             // Q*Gamma [KS][64][8] (hi)
     static constexpr int QL = QH + KS * F8;             // Q*Gamma lo part (bf16 only)
-    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b) [KT][64][4]
-    static constexpr int PH = KP + KT * F4;             // P tiles [CS][64][4] (hi)
-    static constexpr int PL = PH + CS * F4;             // P lo part (bf16 only)
-    static constexpr int TT = PL + (BF ? CS * F4 : 0);  // T tiles [CS][64][4]
+    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b) [KT/2][64][8]
+    static constexpr int PP = KP + (KT / 2) * F8;       // P tiles [CS][64][8] (hi | lo)
+    static constexpr int TT = PP + CS * (BF ? F8 : F4); // T tiles [CS][64][4]
     static constexpr int GC = TT + CS * F4;             // Gamma_C [K] fp32 in state-row order (sub-tile 0)
     static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
     static constexpr int BYTES = UNITS * 1024;
@@ -459,8 +461,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         Frag4<BF> ph, pl;
         split4(pv, ph, pl);
         st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
-        st_frag4<BF>(blk + L::PH + lane * 4 * ES, ph);
-        if constexpr (BF) st_frag4<BF>(blk + L::PL + lane * 4 * ES, pl);
+        if constexpr (BF) *reinterpret_cast<uint4 *>(blk + L::PP + lane * 16) = make_uint4(ph.p[0], ph.p[1], pl.p[0], pl.p[1]);
+        else st_frag4<BF>(blk + L::PP + lane * 16, ph);
     }
 
     // ---- Wk^T = (K*Gamma)^T T^T, one 16-channel tile t at a time: A operand from the
@@ -476,8 +478,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
             const int dl = 16 * (2 * (t & 1) + (ag >> 1)) + r;
-            st_run4<BF>(blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES, w[t][0], w[t][1], w[t][2],
-                        w[t][3]);
+            st_run4<BF>(blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES, -w[t][0], -w[t][1], -w[t][2],
+                        -w[t][3]);
         }
     }
     lds_sync();  // the Wk reads of the tile are done before it is overwritten
@@ -489,9 +491,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int j = 0; j < 8; ++j) st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kpv[s][j]);
     lds_sync();
 #pragma unroll
-    for (int rt = 0; rt < KT; ++rt) {
-        const int kappa = state_row_channel(16 * rt + r);
-        st_frag4<BF>(blk + L::KP + (rt * 64 + lane) * 4 * ES, ld_frag4<BF>(xt + (kappa * 16 + 4 * ag) * ES));
+    for (int p2 = 0; p2 < KT / 2; ++p2) {
+        const Frag4<BF> f0 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + r) * 16 + 4 * ag) * ES);
+        const Frag4<BF> f1 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag) * ES);
+        char *dst = blk + L::KP + (p2 * 64 + lane) * 8 * ES;
+        st_frag4<BF>(dst, f0);
+        st_frag4<BF>(dst + 4 * ES, f1);
     }
 
     // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
@@ -532,36 +537,30 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// blockIdx -> (sequence*H + head, column tile), keeping all column tiles of a
-// head on one XCD (workgroups are dealt to the 8 XCDs round-robin by index),
-// so the fragments every tile of that head reads come from one L2.
-__device__ __forceinline__ bool state_item(int NH, int NT, int &head, int &tile) {
-    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-    head = (slot / NT) * 8 + xcd;
-    tile = slot % NT;
-    return head < NH;
-}
-
-// Tiling of the state pass for value width V. A workgroup has NW compute
-// wavefronts (16 value columns each) and NL = D-1 loader wavefronts, and a
-// ring of D sub-tile slots in LDS (each slot = the sub-tile's workspace block
-// plus its v tile). Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never
-// has more than one in flight, and a sub-tile is copied NL steps before use.
+// Tiling of the state pass for value width V. A workgroup owns one (sequence,
+// head) and has NW = V/32 compute wavefronts and NL = D-1 loader wavefronts,
+// and a ring of D sub-tile slots in LDS (each slot = the sub-tile's workspace
+// block plus its v tile). A compute wavefront owns 32 value columns as two
+// 16-column matrix-core tiles, so every operand it reads from LDS serves two
+// products (LDS read throughput per wavefront is what bounds a step). Loader k
+// copies sub-tiles k, k+NL, k+2NL, ... so it never has more than one in
+// flight, and a sub-tile is copied NL steps before use.
 template <bool BF, int K, int V, int CS>
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
-    static constexpr int NW = V >= 64 ? 4 : V / 16;
-    static constexpr int VT = 16 * NW;
+    static constexpr int NW = V / 32;
     static constexpr int ES = L::ES;
     static constexpr int KU = L::UNITS;
-    static constexpr int VB = 16 * VT * ES;        // v tile bytes (16 tokens x VT columns)
+    static constexpr int VB = 16 * V * ES;         // v tile bytes (16 tokens x V columns)
     static constexpr int VU = (VB + 1023) / 1024;
     static constexpr int U = KU + VU;              // 1 KiB copies per sub-tile
     static constexpr int SLOT = U * 1024;
-    static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
+    static constexpr int OPITCH = V + 4;           // fp32 o staging row pitch (bank spread)
     static constexpr int OBUF = 2 * 16 * OPITCH * 4;
-    static constexpr int DFIT = (150 * 1024 - OBUF) / SLOT;
-    static constexpr int D = DFIT > 6 ? 6 : DFIT;
+    static constexpr int DFIT = (152 * 1024 - OBUF) / SLOT;
+    // at most 8 wavefronts (two per SIMD) keeps 256 registers per lane
+    static constexpr int DMAX = 9 - NW < 6 ? 9 - NW : 6;
+    static constexpr int D = DFIT > DMAX ? DMAX : DFIT;
     static constexpr int NL = D - 1;
     static constexpr int THREADS = (NW + NL) * 64;
     static constexpr int LDS = D * SLOT + OBUF;
@@ -575,17 +574,48 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     const int32_t *__restrict__ chunk_off, const char *__restrict__ frags) {
     using C = StateCfg<BF, K, V, CS>;
     using L = SubLayout<BF, K, CS>;
-    constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, VT = C::VT, NT = V / VT, D = C::D;
-    constexpr int NL = C::NL;
+    constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, D = C::D, NL = C::NL;
     extern __shared__ __align__(1024) char smem[];
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
-    int head, tile;
-    if (!state_item(N * H, NT, head, tile)) return;  // whole workgroup: uniform
+    const int head = blockIdx.x;  // sequence * H + head
+    if (head >= N * H) return;    // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int c0 = chunk_off[n], nu = (chunk_off[n + 1] - c0) * CS;  // sub-tile steps
     const int64_t s0 = seq_tok[n], s1 = seq_tok[n + 1];
+
+    // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
+    // (done by the loader wavefronts one step later: obuf[u & 1] is complete at B_{u+1} and next
+    // overwritten after B_{u+2})
+    auto store_o = [&](int u, int t0, int nthreads) {
+        const int64_t tok0 = s0 + (int64_t)u * SUB;
+        const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
+        const float *ob = obuf + (u & 1) * 16 * C::OPITCH;
+        if (o_bf16) {
+            constexpr int UPR = V / 8;
+            for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
+                const int row = idx / UPR, c8 = (idx % UPR) * 8;
+                if (row < nval) {
+                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
+                    const float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + c8;
+                    *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w),
+                                                                 pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+                }
+            }
+        } else {
+            constexpr int UPR = V / 4;
+            for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
+                const int row = idx / UPR, c4 = (idx % UPR) * 4;
+                if (row < nval) {
+                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
+                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + c4;
+                    *reinterpret_cast<float4 *>(dst) = a;
+                }
+            }
+        }
+    };
 
     if (w >= NW) {
         // ---------------- loader wavefront k: copies sub-tiles k (mod NL) into the ring
@@ -602,203 +632,244 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
 #pragma unroll
             for (int q = 0; q < C::VU; ++q) {
                 const int off = q * 1024 + lane * 16;
-                const int64_t rw = off / (VT * ES);
-                const int within = off % (VT * ES);
+                const int64_t rw = off / (V * ES);
+                const int within = off % (V * ES);
                 // padding and masked rows re-read a valid token of the sequence
                 const int64_t tok = (rw < nval) ? tok0 + rw : s1 - 1;
-                const char *src = vbase + ((tok * H + h) * V + (int64_t)tile * VT) * ES + within;
+                const char *src = vbase + ((tok * H + h) * V) * ES + within;
                 dma16(slot + (uint32_t)((C::KU + q) * 1024), src);
             }
         };
+        // Barrier B_u certifies sub-tiles u and u+1 (the compute wavefronts read u+1's first
+        // operands during step u) and frees the slot of sub-tile u-1.
         if (nu > 0) {
             for (int u = k; u < nu && u < D - 1; u += NL) issue(u);
+            const int lt = threadIdx.x - NW * 64;
             for (int u = 0; u < nu; ++u) {
-                const bool mine = (u % NL) == k;
-                if (mine) wait_copies();        // sub-tile u (this loader's only copy in flight) landed
-                wg_barrier();                   // B_u: sub-tile u visible; slot of sub-tile u-1 free
-                if (mine && u + NL < nu) issue(u + NL);
+                if ((u == 0 && k == 0) || (u + 1 < nu && (u + 1) % NL == k))
+                    wait_copies();              // sub-tile u+1 (or 0): this loader's only copy in flight
+                lds_done_barrier();             // B_u (the o rows read before it are done)
+                if ((u % NL) == k && u + NL < nu) issue(u + NL);
+                if (u > 0) store_o(u - 1, lt, NL * 64);
             }
-            wg_barrier();                       // B_nu
+            lds_done_barrier();                 // B_nu
+            store_o(nu - 1, lt, NL * 64);
         }
         return;
     }
 
-    // ---------------- compute wavefronts: 16 value columns each
+    // ---------------- compute wavefronts: lane (tg, cl) owns value columns c2 (tile 0) and c2+1 (tile 1)
     const int tg = lane >> 4, cl = lane & 15;
-    const int lcol = w * 16 + cl, col = tile * VT + lcol;
-    f32x4 S[KT];  // S[rt][i] = S[key channel state_row_channel(16rt + 4tg + i)][col]
+    const int c2 = w * 32 + 2 * cl;
+    f32x4 S[2][KT];  // S[ct][rt][i] = S[key channel state_row_channel(16rt + 4tg + i)][c2 + ct]
     const size_t sbase = ((size_t)n * H + h) * K * V;
     if (S0) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[rt][i] = S0[sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + col];
+            for (int i = 0; i < 4; ++i) {
+                const float2 x =
+                    *reinterpret_cast<const float2 *>(S0 + sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + c2);
+                S[0][rt][i] = x.x;
+                S[1][rt][i] = x.y;
+            }
     } else {
 #pragma unroll
-        for (int rt = 0; rt < KT; ++rt) S[rt] = zero4();
+        for (int rt = 0; rt < KT; ++rt) S[0][rt] = S[1][rt] = zero4();
     }
     // the state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
-    Frag8<BF> sb[KS];
+    Frag8<BF> sb[2][KS];
     auto pack_state = [&]() {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if constexpr (BF) {
-                sb[s].p[0] = pack_bf16(S[2 * s][0], S[2 * s][1]);
-                sb[s].p[1] = pack_bf16(S[2 * s][2], S[2 * s][3]);
-                sb[s].p[2] = pack_bf16(S[2 * s + 1][0], S[2 * s + 1][1]);
-                sb[s].p[3] = pack_bf16(S[2 * s + 1][2], S[2 * s + 1][3]);
-            } else {
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sb[s].f[i] = S[2 * s][i];
-                    sb[s].f[4 + i] = S[2 * s + 1][i];
+            for (int s = 0; s < KS; ++s) {
+                if constexpr (BF) {
+                    sb[ct][s].p[0] = pack_bf16(S[ct][2 * s][0], S[ct][2 * s][1]);
+                    sb[ct][s].p[1] = pack_bf16(S[ct][2 * s][2], S[ct][2 * s][3]);
+                    sb[ct][s].p[2] = pack_bf16(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
+                    sb[ct][s].p[3] = pack_bf16(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sb[ct][s].f[i] = S[ct][2 * s][i];
+                        sb[ct][s].f[4 + i] = S[ct][2 * s + 1][i];
+                    }
                 }
             }
-        }
     };
     pack_state();
 
-    // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
-    auto store_o = [&](int u) {
-        const int64_t tok0 = s0 + (int64_t)u * SUB;
-        const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
-        const float *ob = obuf + (u & 1) * 16 * C::OPITCH;
-        if (o_bf16) {
-            constexpr int UPR = VT / 8;
-            for (int idx = threadIdx.x; idx < 16 * UPR; idx += NW * 64) {
-                const int row = idx / UPR, c8 = (idx % UPR) * 8;
-                if (row < nval) {
-                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
-                    const float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c8;
-                    *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w),
-                                                                 pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
-                }
-            }
-        } else {
-            constexpr int UPR = VT / 4;
-            for (int idx = threadIdx.x; idx < 16 * UPR; idx += NW * 64) {
-                const int row = idx / UPR, c4 = (idx % UPR) * 4;
-                if (row < nval) {
-                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
-                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c4;
-                    *reinterpret_cast<float4 *>(dst) = a;
-                }
+    // operands of a step's first product chain (T, the v tile, -Wk); read one step ahead
+    Frag4<BF> tt, vf[2];
+    Frag8<BF> wk[KS];
+    auto read_first = [&](const char *sl) {
+        tt = ld_frag4<BF>(sl + L::TT + lane * 4 * ES);
+        {
+            const char *vt = sl + C::KU * 1024;
+            if constexpr (BF) {
+                uint32_t x[4];  // columns (c2, c2+1) of tokens 4tg+j
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint32_t *>(vt + ((4 * tg + j) * V + c2) * 2);
+                vf[0].p[0] = (x[0] & 0xffffu) | (x[1] << 16);
+                vf[0].p[1] = (x[2] & 0xffffu) | (x[3] << 16);
+                vf[1].p[0] = (x[0] >> 16) | (x[1] & 0xffff0000u);
+                vf[1].p[1] = (x[2] >> 16) | (x[3] & 0xffff0000u);
+            } else {
+                float2 x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float2 *>(vt + ((4 * tg + j) * V + c2) * 4);
+                set4(vf[0], x[0].x, x[1].x, x[2].x, x[3].x);
+                set4(vf[1], x[0].y, x[1].y, x[2].y, x[3].y);
             }
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
     };
 
     for (int u = 0; u < nu; ++u) {
         lds_done_barrier();  // B_u
-        if (u > 0) store_o(u - 1);
         const char *sl = smem + (u % D) * C::SLOT;
-
-        // ---- every LDS operand of this step, read up front in order of use
-        const Frag4<BF> tt = ld_frag4<BF>(sl + L::TT + lane * 4 * ES);
-        Frag4<BF> vf;
-        {
-            const char *vt = sl + C::KU * 1024;
-            float x[4];
+        if (u == 0) read_first(sl);
+        // ---- the step's other LDS operands, issued before any product so they land while the
+        // first chain runs (LDS read throughput per wavefront bounds a step)
+        Frag8<BF> kp2[KT / 2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int off = ((4 * tg + j) * VT + lcol) * ES;
-                if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
-                else x[j] = *reinterpret_cast<const float *>(vt + off);
-            }
-            set4(vf, x[0], x[1], x[2], x[3]);
-        }
-        Frag8<BF> wk[KS], qh[KS], ql[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
+        for (int p2 = 0; p2 < KT / 2; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
+        // Gamma_C: lane (tg, cl) reads state rows 16(cl/2) + 4tg + 2(cl%2) + {0, 1}; row rt, entry i of
+        // lane group tg then comes from lane 2rt + i/2 of the same row (DPP row broadcast)
+        const float2 g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
+        Frag8<BF> qh[KS], ql[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
             if constexpr (BF) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
         }
-        const Frag4<BF> ph = ld_frag4<BF>(sl + L::PH + lane * 4 * ES);
-        Frag4<BF> pl;
-        if constexpr (BF) pl = ld_frag4<BF>(sl + L::PL + lane * 4 * ES);
-        Frag4<BF> kpf[KT];
-        float4 gm[KT];
-        const float *gcp = reinterpret_cast<const float *>(sl + L::GC);
-#pragma unroll
-        for (int rt = 0; rt < KT; ++rt) {
-            kpf[rt] = ld_frag4<BF>(sl + L::KP + (rt * 64 + lane) * 4 * ES);
-            gm[rt] = *reinterpret_cast<const float4 *>(gcp + 16 * rt + 4 * tg);
+        Frag4<BF> ph, pl;
+        if constexpr (BF) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(sl + L::PP + lane * 16);
+            ph.p[0] = x.x; ph.p[1] = x.y; pl.p[0] = x.z; pl.p[1] = x.w;
+        } else {
+            ph = ld_frag4<BF>(sl + L::PP + lane * 16);
         }
+        __builtin_amdgcn_sched_barrier(0);
 
-        // ---- W = T V - Wk S (the state product in two independent accumulation chains)
-        f32x4 U = mma16(zero4(), tt, vf);
-        f32x4 X0 = zero4(), X1 = zero4();
+        // ---- W = T V + (-Wk) S: one accumulation chain per tile, every product 32 deep (T V
+        // as [T | 0] x [V | 0]; a chain that mixes 16-deep and 32-deep products read a stale
+        // accumulator on gfx950)
+        f32x4 W[2], O[2];
+        {
+            Frag8<BF> t8;
+            if constexpr (BF) {
+                t8.p[0] = tt.p[0]; t8.p[1] = tt.p[1]; t8.p[2] = 0u; t8.p[3] = 0u;
+            } else {
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            X0 = mma32(X0, wk[s], sb[s]);
-            if (s + 1 < KS) X1 = mma32(X1, wk[s + 1], sb[s + 1]);
-        }
-        mfma_fence(U, X0, X1);
-        const f32x4 W = U - (X0 + X1);
-        // ---- O = (Q*Gamma) S + P W: hi part, lo part and intra-chunk term accumulate apart
-        f32x4 Oh = zero4(), Ol = zero4(), Op = zero4();
+                for (int i = 0; i < 4; ++i) { t8.f[i] = tt.f[i]; t8.f[4 + i] = 0.f; }
+            }
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            Oh = mma32(Oh, qh[s], sb[s]);
-            if constexpr (BF) Ol = mma32(Ol, ql[s], sb[s]);
+            for (int ct = 0; ct < 2; ++ct) {
+                Frag8<BF> v8;
+                if constexpr (BF) {
+                    v8.p[0] = vf[ct].p[0]; v8.p[1] = vf[ct].p[1]; v8.p[2] = 0u; v8.p[3] = 0u;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { v8.f[i] = vf[ct].f[i]; v8.f[4 + i] = 0.f; }
+                }
+                W[ct] = mma32(zero4(), t8, v8);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
+            }
         }
+        mfma_fence(W[0], W[1]);
         if constexpr (BF) {
             // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
             // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
-            uint32_t wh0, wl0, wh1, wl1;
-            split_bf16(W[0], W[1], wh0, wl0);
-            split_bf16(W[2], W[3], wh1, wl1);
-            Frag8<true> whl;  // [Wh | Wl]
-            whl.p[0] = wh0; whl.p[1] = wh1; whl.p[2] = wl0; whl.p[3] = wl1;
-            // [Ph | Ph] x [Wh | Wl]  +  [Pl | 0] x [Wh | Wl]: every product of one
-            // accumulation chain has the same shape (a chain that mixes 16-deep and
-            // 32-deep products read a stale accumulator on gfx950).
+            Frag8<true> whl[2];  // [Wh | Wl]
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                uint32_t wh0, wl0, wh1, wl1;
+                split_bf16(W[ct][0], W[ct][1], wh0, wl0);
+                split_bf16(W[ct][2], W[ct][3], wh1, wl1);
+                whl[ct].p[0] = wh0; whl[ct].p[1] = wh1; whl[ct].p[2] = wl0; whl[ct].p[3] = wl1;
+            }
+            // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]   (first: the next step waits on it)
+#pragma unroll
+            for (int rt = 0; rt < KT; ++rt) {
+                float gm[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gm[i] = row_bcast(i & 1 ? g2.y : g2.x, 2 * rt + (i >> 1));
+                const Frag8<true> &kq = kp2[rt >> 1];
+                Frag8<true> kk;
+                kk.p[0] = kq.p[2 * (rt & 1)]; kk.p[1] = kq.p[2 * (rt & 1) + 1];
+                kk.p[2] = kk.p[0]; kk.p[3] = kk.p[1];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
+                    S[ct][rt] = mma32(S[ct][rt], kk, whl[ct]);
+                }
+            }
+            // O = (Q*Gamma)_hi S + (Q*Gamma)_lo S + [Ph | Ph] x [Wh | Wl] + [Pl | 0] x [Wh | Wl]
             Frag8<true> pp, pz;
             pp.p[0] = ph.p[0]; pp.p[1] = ph.p[1]; pp.p[2] = ph.p[0]; pp.p[3] = ph.p[1];
             pz.p[0] = pl.p[0]; pz.p[1] = pl.p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
-            Op = mma32(Op, pp, whl);
-            Op = mma32(Op, pz, whl);
-            // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]
 #pragma unroll
-            for (int rt = 0; rt < KT; ++rt) {
-                S[rt][0] *= gm[rt].x; S[rt][1] *= gm[rt].y; S[rt][2] *= gm[rt].z; S[rt][3] *= gm[rt].w;
-                Frag8<true> kk;
-                kk.p[0] = kpf[rt].p[0]; kk.p[1] = kpf[rt].p[1]; kk.p[2] = kpf[rt].p[0]; kk.p[3] = kpf[rt].p[1];
-                S[rt] = mma32(S[rt], kk, whl);
+            for (int ct = 0; ct < 2; ++ct) {
+                O[ct] = mma32(zero4(), pp, whl[ct]);
+                O[ct] = mma32(O[ct], pz, whl[ct]);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
+                    O[ct] = mma32(O[ct], ql[s], sb[ct][s]);
+                }
             }
         } else {
-            Frag4<false> wf;
-            set4(wf, W[0], W[1], W[2], W[3]);
-            Op = mma16(Op, ph, wf);
+            Frag4<false> wf[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) set4(wf[ct], W[ct][0], W[ct][1], W[ct][2], W[ct][3]);
 #pragma unroll
             for (int rt = 0; rt < KT; ++rt) {
-                S[rt][0] *= gm[rt].x; S[rt][1] *= gm[rt].y; S[rt][2] *= gm[rt].z; S[rt][3] *= gm[rt].w;
-                S[rt] = mma16(S[rt], kpf[rt], wf);
+                float gm[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gm[i] = row_bcast(i & 1 ? g2.y : g2.x, 2 * rt + (i >> 1));
+                const Frag8<false> &kq = kp2[rt >> 1];
+                Frag4<false> kf;
+                set4(kf, kq.f[4 * (rt & 1)], kq.f[4 * (rt & 1) + 1], kq.f[4 * (rt & 1) + 2], kq.f[4 * (rt & 1) + 3]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
+                    S[ct][rt] = mma16(S[ct][rt], kf, wf[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                O[ct] = mma16(zero4(), ph, wf[ct]);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
             }
         }
-        mfma_fence(Oh, Ol, Op);
-        {
-            const f32x4 O = (Oh + Ol) + Op;
-            float *ob = obuf + (u & 1) * 16 * C::OPITCH;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ob[(4 * tg + i) * C::OPITCH + lcol] = O[i];
-        }
+        // next step's first operands (certified at B_u), read while the products run
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < nu) read_first(smem + ((u + 1) % D) * C::SLOT);
+        __builtin_amdgcn_sched_barrier(0);
+        // the state products were issued first: packing the next operand overlaps the output products
         mfma_fence_all(S);
         pack_state();  // operand for the next step
+        mfma_fence(O[0], O[1]);
+        {
+            float *ob = obuf + (u & 1) * 16 * C::OPITCH;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + c2) = make_float2(O[0][i], O[1][i]);
+        }
     }
-    if (nu > 0) {
-        lds_done_barrier();  // B_nu
-        store_o(nu - 1);
-    }
+    if (nu > 0) lds_done_barrier();  // B_nu: the loader wavefronts store the last o rows
     if (Sfin) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                Sfin[sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + col] = S[rt][i];
+                *reinterpret_cast<float2 *>(Sfin + sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + c2) =
+                    make_float2(S[0][rt][i], S[1][rt][i]);
     }
 }
 
@@ -859,7 +930,6 @@ hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
     constexpr int CS = 1;
     using C = StateCfg<BF, K, V, CS>;
     const WsPtrs w = ws_ptrs(a);
-    constexpr int NT = V / C::VT;
     static bool lds_set = false;  // idempotent attribute; a race only repeats the call
     if (!lds_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>),
@@ -867,8 +937,7 @@ hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
         lds_set = true;
     }
-    const int64_t NH = (int64_t)a.num_seqs * a.H;
-    const unsigned grid = (unsigned)(8 * ((NH + 7) / 8) * NT);
+    const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.H);
     hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
                        (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     return hipGetLastError();
