@@ -10,7 +10,7 @@
 
 namespace {
 
-bool supported_chunk(int32_t c) { return c == 16; }
+bool supported_chunk(int32_t c) { return c == 16 || c == 64; }
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }

@@ -186,6 +186,8 @@ __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[2][8]) {
                    "+v"(x[1][4]), "+v"(x[1][5]), "+v"(x[1][6]), "+v"(x[1][7]));
 }
 
+template <int N> __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[1][N]) { mfma_fence_all(x[0]); }
+
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 

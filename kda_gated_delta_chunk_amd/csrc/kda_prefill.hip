@@ -229,13 +229,21 @@ __device__ __forceinline__ Frag8<false> frag8_of(const float (&x)[8], Frag8<fals
     for (int t = 0; t < 8; ++t) f.f[t] = x[t];
     return f;
 }
+// Slot j of an 8-slot operand as fp32 (bf16: exact widening).
+__device__ __forceinline__ float frag8_get(const Frag8<true> &f, int j) {
+    return (j & 1) ? bf_hi(f.p[j >> 1]) : bf_lo(f.p[j >> 1]);
+}
+__device__ __forceinline__ float frag8_get(const Frag8<false> &f, int j) { return f.f[j]; }
 __device__ __forceinline__ void split8(const float (&x)[8], Frag8<true> &hi, Frag8<true> &lo) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) split_bf16(x[2 * t], x[2 * t + 1], hi.p[t], lo.p[t]);
 }
-__device__ __forceinline__ void split8(const float (&x)[8], Frag8<false> &hi, Frag8<false> &) {
+__device__ __forceinline__ void split8(const float (&x)[8], Frag8<false> &hi, Frag8<false> &lo) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) hi.f[t] = x[t];
+    for (int t = 0; t < 8; ++t) {
+        hi.f[t] = x[t];
+        lo.f[t] = 0.f;  // fp32 operands are whole: the lo part is zero
+    }
 }
 __device__ __forceinline__ void split4(const float4 &x, Frag4<true> &hi, Frag4<true> &lo) {
     split_bf16(x.x, x.y, hi.p[0], lo.p[0]);
@@ -513,6 +521,368 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
+// ------------------------------------------------- chunk prep, 64 tokens
+// One workgroup per (64-token chunk, head); wavefront R handles sub-tile R
+// (tokens 16R .. 16R+15). Per sub-tile the work is that of the 16-token prep
+// with chunk-relative decay (b = B_R + local prefix, B_R = sum of the earlier
+// sub-tiles' totals); on top of it:
+//   off-diagonal tiles I < R of A and P: exp(b_r - b_i) = exp(bl_r) *
+//     exp(B_R - B_{I+1}) * exp(bt_I - bl_i) with bl the sub-tile prefix and bt
+//     its total, every factor at most 1 (the left operand is this wavefront's
+//     K or Q scaled by the first two, the right one the keys of sub-tile I
+//     scaled to its end, shared through LDS);
+//   X = (I + A)^{-1} by blocks: each wavefront solves its diagonal 16x16 block,
+//     then wavefront R forms column block R, X_JR = -X_JJ sum_{R<=M<J} A_JM X_MR
+//     for J > R, on the fp32 matrix cores; T = X diag(beta);
+//   Wk rows of sub-tile R = sum_{I<=R} T_RI (K*Gamma)_I.
+template <bool BF, int K>
+struct Prep64Lds {
+    static constexpr int ES = BF ? 2 : 4;
+    static constexpr int KS = K / 32;
+    static constexpr int MP = 20;                               // pitch (floats), 16x16 matrices
+    static constexpr int BP = 68;                               // pitch (floats), 64-wide matrices
+    static constexpr int XT_B = K * 16 * ES;                    // one transposed [K][16] tile
+    static constexpr int KE_B = (BF ? 2 : 1) * KS * 64 * 8 * ES;  // scaled keys of a sub-tile, hi | lo
+    static constexpr int XT = 0;                                // [4] transposed K*Gamma, then K*exp(b_C-b)
+    static constexpr int LB = XT + 4 * XT_B;                    // [4][K] sub-tile decay totals (base 2)
+    static constexpr int B64 = LB + 4 * K * 4;                  // betas of the chunk [64]
+    static constexpr int SP = B64 + 64 * 4;                     // [4] P row blocks [16][BP]
+    static constexpr int X64 = SP + 4 * 16 * BP * 4;            // X = (I + A)^{-1} [64][BP]
+    static constexpr int U1 = X64 + 64 * BP * 4;                // union: KE (off-diagonal phase), then A64 + SA
+    static constexpr int KE = U1;                               // [3] sub-tiles 0..2
+    static constexpr int A64 = U1;                              // A [64][BP] (blocks below the diagonal)
+    static constexpr int SA = A64 + 64 * BP * 4;                // [4] A^T of the diagonal blocks [16][MP]
+    static constexpr int U1_B = (3 * KE_B > 64 * BP * 4 + 4 * 16 * MP * 4) ? 3 * KE_B : 64 * BP * 4 + 4 * 16 * MP * 4;
+    static constexpr int BYTES = U1 + U1_B;
+};
+
+// v x f elementwise for the eight values of one step (f: per channel, same for all tokens).
+__device__ __forceinline__ void scale8(const float (&x)[8], const float (&f)[8], float (&y)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = x[j] * f[j];
+}
+
+template <bool BF, int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep64(
+    const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ gp,
+    const void *__restrict__ bp, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
+    const int32_t *__restrict__ chunk_off, char *__restrict__ frags) {
+    constexpr int CS = 4;
+    using L = SubLayout<BF, K, CS>;
+    using D = Prep64Lds<BF, K>;
+    constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP, BP = D::BP;
+    extern __shared__ __align__(16) char smem[];
+    const int R = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int ag = lane >> 4, r = lane & 15;
+    const int total = chunk_off[N];
+    const int gc = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
+    if (gc >= total) return;  // whole workgroup (uniform)
+    char *xt = smem + D::XT + R * D::XT_B;
+    float *lb = reinterpret_cast<float *>(smem + D::LB);
+    float *b64 = reinterpret_cast<float *>(smem + D::B64);
+    float *sP = reinterpret_cast<float *>(smem + D::SP) + R * 16 * BP;
+    float *x64 = reinterpret_cast<float *>(smem + D::X64);
+    float *a64 = reinterpret_cast<float *>(smem + D::A64);
+    float *sAT = reinterpret_cast<float *>(smem + D::SA) + R * 16 * MP;
+
+    const int n = find_seq(chunk_off, N, gc);
+    const int64_t t0c = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * (CS * SUB);
+    const int64_t tend = seq_tok[n + 1];
+    const int nvc = (int)((tend - t0c) < CS * SUB ? (tend - t0c) : CS * SUB);  // >= 1
+
+    // ---- token row 16R + r of the chunk (rows past the sequence end act as identity tokens)
+    const bool valid = SUB * R + r < nvc;
+    const int64_t row = (t0c + (valid ? SUB * R + r : nvc - 1)) * H + h;
+    float qv[KS][8], kv[KS][8], bl[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+        load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+        load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    }
+    float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
+    beta = valid ? beta : 0.f;
+    // ---- sub-tile prefix of the log-decay (base 2) and its total; totals to LDS
+    float bt[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bl[s][j] = row_scan16(valid ? bl[s][j] * LOG2E : 0.f);
+            bt[s][j] = row_last(bl[s][j]);
+        }
+    if (r == 0) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag) = make_float4(bt[s][0], bt[s][1], bt[s][2], bt[s][3]);
+            *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag + 4) = make_float4(bt[s][4], bt[s][5], bt[s][6], bt[s][7]);
+        }
+    }
+    if (ag == 0) b64[SUB * R + r] = beta;
+    // keys scaled to the sub-tile end (right operands of the later sub-tiles' off-diagonal tiles)
+    if (R < 3) {
+        char *kep = smem + D::KE + R * D::KE_B;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float ke[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ke[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
+            Frag8<BF> eh, el;
+            split8(ke, eh, el);
+            st_frag8<BF>(kep + (s * 64 + lane) * 8 * ES, eh);
+            if constexpr (BF) st_frag8<BF>(kep + ((KS + s) * 64 + lane) * 8 * ES, el);
+        }
+    }
+    __syncthreads();
+
+    // ---- decay-scaled operands of this sub-tile. br = B_R (sum of the earlier sub-tiles' totals),
+    // bc = B_4 (chunk total), for this lane's channels.
+    char *blk = frags + (((size_t)gc * H + h) * CS + R) * L::BYTES;
+    Frag8<BF> kgf[KS], kih[KS], kil[KS], qlh[KS], qll[KS], kpp[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        float br[8], bc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { br[j] = 0.f; bc[j] = 0.f; }
+#pragma unroll
+        for (int I = 0; I < CS; ++I) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(lb + I * K + 32 * s + 8 * ag);
+            const float4 x1 = *reinterpret_cast<const float4 *>(lb + I * K + 32 * s + 8 * ag + 4);
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (I < R) br[j] += x[j];
+                bc[j] += x[j];
+            }
+        }
+        float kg[8], ki[8], qg[8], qgc[8], kpv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(bl[s][j]);
+            const float gam = __builtin_amdgcn_exp2f(bl[s][j] + br[j]);  // chunk-relative Gamma
+            kg[j] = kv[s][j] * e;
+            qg[j] = qv[s][j] * e;
+            ki[j] = kv[s][j] * __builtin_amdgcn_exp2f(-bl[s][j]);
+            qgc[j] = qv[s][j] * gam;
+            kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bc[j] - br[j] - bl[s][j]);
+            st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kv[s][j] * gam);
+        }
+        // Q*Gamma (chunk-relative) straight to the workspace
+        Frag8<BF> qh, ql;
+        split8(qgc, qh, ql);
+        st_frag8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES, qh);
+        if constexpr (BF) st_frag8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES, ql);
+        // operands of the diagonal tile (sub-tile-relative scaling); K*exp(b_C-b) kept for the end
+        kgf[s] = frag8_of(kg, Frag8<BF>{});
+        split8(ki, kih[s], kil[s]);
+        split8(qg, qlh[s], qll[s]);
+        kpp[s] = frag8_of(kpv, Frag8<BF>{});
+    }
+    // ---- diagonal tile: A_RR, P_RR from registers
+    f32x4 A0 = zero4(), A1 = zero4(), P0 = zero4(), P1 = zero4(), P2 = zero4();
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        A0 = mma32(A0, kgf[s], kih[s]);
+        P0 = mma32(P0, qlh[s], kih[s]);
+        if constexpr (BF) {
+            A1 = mma32(A1, kgf[s], kil[s]);
+            P1 = mma32(P1, qlh[s], kil[s]);
+            P2 = mma32(P2, qll[s], kih[s]);
+        }
+    }
+    mfma_fence(A0, A1, P0, P1, P2);
+    __syncthreads();  // scaled keys and K*Gamma tiles of every sub-tile visible
+
+    // ---- off-diagonal tiles I < R: A_RI = diag(beta_R) (K e^{bl} f)(KE_I)^T, P_RI = (Q e^{bl} f)(KE_I)^T,
+    // f = exp2(B_R - B_{I+1}) = exp2(sum of the totals of sub-tiles I+1 .. R-1) (1 for I = R-1). The
+    // left operands are rebuilt from this sub-tile's packed diagonal operands.
+    f32x4 Ao[3], Po[3];
+#pragma unroll
+    for (int I = 0; I < 3; ++I) {
+        Ao[I] = zero4();
+        Po[I] = zero4();
+        if (I < R) {
+            const char *kep = smem + D::KE + I * D::KE_B;
+            f32x4 a1 = zero4(), p1 = zero4(), p2 = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                Frag8<BF> ka = kgf[s], qa = qlh[s], qb = qll[s];
+                if (I < R - 1) {
+                    float f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) f[j] = 0.f;
+#pragma unroll
+                    for (int M = 1; M < 3; ++M) {
+                        if (M <= I || M >= R) continue;
+                        const float4 x0 = *reinterpret_cast<const float4 *>(lb + M * K + 32 * s + 8 * ag);
+                        const float4 x1 = *reinterpret_cast<const float4 *>(lb + M * K + 32 * s + 8 * ag + 4);
+                        f[0] += x0.x; f[1] += x0.y; f[2] += x0.z; f[3] += x0.w;
+                        f[4] += x1.x; f[5] += x1.y; f[6] += x1.z; f[7] += x1.w;
+                    }
+                    float kf[8], qf[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float e = __builtin_amdgcn_exp2f(f[j]);
+                        kf[j] = frag8_get(kgf[s], j) * e;
+                        qf[j] = (frag8_get(qlh[s], j) + frag8_get(qll[s], j)) * e;
+                    }
+                    ka = frag8_of(kf, Frag8<BF>{});
+                    split8(qf, qa, qb);
+                }
+                const Frag8<BF> eh = ld_frag8<BF>(kep + (s * 64 + lane) * 8 * ES);
+                Ao[I] = mma32(Ao[I], ka, eh);
+                Po[I] = mma32(Po[I], qa, eh);
+                if constexpr (BF) {
+                    const Frag8<BF> el = ld_frag8<BF>(kep + ((KS + s) * 64 + lane) * 8 * ES);
+                    a1 = mma32(a1, ka, el);
+                    p1 = mma32(p1, qa, el);
+                    p2 = mma32(p2, qb, eh);
+                }
+            }
+            mfma_fence(Ao[I], Po[I], a1, p1, p2);
+            Ao[I] = Ao[I] + a1;
+            Po[I] = (Po[I] + p1) + p2;
+        }
+    }
+    __syncthreads();  // every off-diagonal read of the scaled keys is done (A64 reuses their space)
+
+    // ---- A row block R to LDS (beta_r scaled; diagonal strictly lower), its diagonal block also
+    // transposed for the 16x16 solve; P row block row-major (diagonal tile lower incl.)
+    {
+        const float4 bet = *reinterpret_cast<const float4 *>(b64 + SUB * R + 4 * ag);
+        const float bv[4] = {bet.x, bet.y, bet.z, bet.w};
+        float at[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ri = 4 * ag + i;
+            at[i] = (r < ri) ? bv[i] * (A0[i] + A1[i]) : 0.f;
+            sP[ri * BP + SUB * R + r] = (r <= ri) ? (P0[i] + P1[i]) + P2[i] : 0.f;
+#pragma unroll
+            for (int I = 0; I < 3; ++I)
+                if (I < R) {
+                    a64[(SUB * R + ri) * BP + SUB * I + r] = bv[i] * Ao[I][i];
+                    sP[ri * BP + SUB * I + r] = Po[I][i];
+                }
+        }
+        *reinterpret_cast<float4 *>(sAT + r * MP + 4 * ag) = make_float4(at[0], at[1], at[2], at[3]);
+    }
+    lds_sync();
+    // ---- diagonal block X_RR = (I + A_RR)^{-1}: column r of this lane to X64 (rows 4ag..4ag+3)
+    {
+        float x[16];
+        solve16<MP>(sAT, r, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x64[(SUB * R + 4 * ag + i) * BP + SUB * R + r] = pick16(x, ag, i);
+    }
+    __syncthreads();  // A64 and the diagonal blocks of X complete
+
+    // ---- column block R of X: X_JR = -X_JJ sum_{R<=M<J} A_JM X_MR, J = R+1 .. 3 (fp32 products)
+    if (R < 3) {
+        f32x4 xm[4];  // X_MR in the accumulator layout (lane (ag, n): rows 4ag+i, column n)
+        f32x4 xr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[i] = x64[(SUB * R + 4 * ag + i) * BP + SUB * R + r];
+#pragma unroll
+        for (int M = 0; M < 4; ++M) xm[M] = (M == R) ? xr : zero4();
+#pragma unroll
+        for (int J = 1; J < 4; ++J) {
+            if (J <= R) continue;
+            f32x4 y = zero4();
+#pragma unroll
+            for (int M = 0; M < 3; ++M) {
+                if (M < R || M >= J) continue;
+                const float4 av = *reinterpret_cast<const float4 *>(a64 + (SUB * J + r) * BP + SUB * M + 4 * ag);
+                Frag4<false> fa, fb;
+                set4(fa, av.x, av.y, av.z, av.w);
+                set4(fb, xm[M][0], xm[M][1], xm[M][2], xm[M][3]);
+                y = mma16(y, fa, fb);
+            }
+            mfma_fence(y);
+            const float4 xv = *reinterpret_cast<const float4 *>(x64 + (SUB * J + r) * BP + SUB * J + 4 * ag);
+            Frag4<false> fa, fb;
+            set4(fa, -xv.x, -xv.y, -xv.z, -xv.w);
+            set4(fb, y[0], y[1], y[2], y[3]);
+            f32x4 xj = mma16(zero4(), fa, fb);
+            mfma_fence(xj);
+            xm[J] = xj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x64[(SUB * J + 4 * ag + i) * BP + SUB * R + r] = xj[i];
+        }
+    }
+    __syncthreads();  // X complete
+
+    // ---- T row block R (T_RI = X_RI diag(beta_I)) and P row block R to the workspace; T fragments
+    // feed Wk
+    Frag4<BF> tf[CS];
+#pragma unroll
+    for (int I = 0; I < CS; ++I) {
+        if (I > R) continue;
+        const float4 xv = *reinterpret_cast<const float4 *>(x64 + (SUB * R + r) * BP + SUB * I + 4 * ag);
+        const float4 bv = *reinterpret_cast<const float4 *>(b64 + SUB * I + 4 * ag);
+        set4(tf[I], xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
+        st_frag4<BF>(blk + L::TT + (I * 64 + lane) * 4 * ES, tf[I]);
+        const float4 pv = *reinterpret_cast<const float4 *>(sP + r * BP + SUB * I + 4 * ag);
+        Frag4<BF> ph, pl;
+        split4(pv, ph, pl);
+        if constexpr (BF)
+            *reinterpret_cast<uint4 *>(blk + L::PP + (I * 64 + lane) * 16) = make_uint4(ph.p[0], ph.p[1], pl.p[0], pl.p[1]);
+        else st_frag4<BF>(blk + L::PP + (I * 64 + lane) * 16, ph);
+    }
+    // ---- Wk^T tile t = sum_{I<=R} (K*Gamma)_I^T T_RI^T (negated on store, as in the 16-token prep)
+    {
+        f32x4 w[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            w[t] = zero4();
+#pragma unroll
+            for (int I = 0; I < CS; ++I)
+                if (I <= R)
+                    w[t] = mma16(w[t], ld_frag4<BF>(smem + D::XT + I * D::XT_B + ((16 * t + r) * 16 + 4 * ag) * ES), tf[I]);
+        }
+        mfma_fence_all(w);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int dl = 16 * (2 * (t & 1) + (ag >> 1)) + r;
+            st_run4<BF>(blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES, -w[t][0], -w[t][1], -w[t][2],
+                        -w[t][3]);
+        }
+    }
+    __syncthreads();  // every wavefront's reads of the K*Gamma tiles are done
+
+    // ---- K*exp(b_C - b) in state-row order, through this sub-tile's transposed tile
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, frag8_get(kpp[s], j));
+    lds_sync();
+#pragma unroll
+    for (int p2 = 0; p2 < KT / 2; ++p2) {
+        const Frag4<BF> f0 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + r) * 16 + 4 * ag) * ES);
+        const Frag4<BF> f1 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag) * ES);
+        char *dst = blk + L::KP + (p2 * 64 + lane) * 8 * ES;
+        st_frag4<BF>(dst, f0);
+        st_frag4<BF>(dst + 4 * ES, f1);
+    }
+    // ---- Gamma_C (chunk total) in state-row order, in sub-tile 0's block
+    if (R == 0 && r == 0) {
+        float *gcp = reinterpret_cast<float *>(blk + L::GC);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = 0.f;
+#pragma unroll
+            for (int I = 0; I < CS; ++I)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[j] += lb[I * K + 32 * s + 8 * ag + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(e[j]);
+            *reinterpret_cast<float4 *>(gcp + 32 * s + 4 * ag) = make_float4(e[0], e[1], e[2], e[3]);
+            *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
+        }
+    }
+}
+
 // ------------------------------------------------------ state pass (K3+K4)
 // Asynchronous global -> LDS copy of 16 bytes per lane (64 lanes = 1 KiB, lane
 // l lands at lds + 16*l). Issued from inline assembly so that the compiler
@@ -537,25 +907,29 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// Tiling of the state pass for value width V. A workgroup owns one (sequence,
-// head) and has NW = V/32 compute wavefronts and NL = D-1 loader wavefronts,
-// and a ring of D sub-tile slots in LDS (each slot = the sub-tile's workspace
-// block plus its v tile). A compute wavefront owns 32 value columns as two
-// 16-column matrix-core tiles, so every operand it reads from LDS serves two
-// products (LDS read throughput per wavefront is what bounds a step). Loader k
-// copies sub-tiles k, k+NL, k+2NL, ... so it never has more than one in
-// flight, and a sub-tile is copied NL steps before use.
+// Tiling of the state pass for value width V. A workgroup owns VT value
+// columns of one (sequence, head): NW compute wavefronts of CT 16-column tiles
+// each, NL = D-1 loader wavefronts and a ring of D sub-tile slots in LDS (each
+// slot = the sub-tile's workspace block plus its v tile). Every operand a
+// compute wavefront reads from LDS serves its CT products (LDS read
+// throughput per wavefront is what bounds a step); 64-token chunks carry the
+// chunk's earlier corrected values in registers and use one tile per
+// wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never has
+// more than one in flight; a sub-tile is copied NL steps before use.
 template <bool BF, int K, int V, int CS>
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
-    static constexpr int NW = V / 32;
+    static constexpr int CT = CS == 1 ? 2 : 1;
+    static constexpr int NW = V / (16 * CT) < 4 ? V / (16 * CT) : 4;
+    static constexpr int VT = 16 * CT * NW;        // columns per workgroup
+    static constexpr int NT = V / VT;              // workgroups per (sequence, head)
     static constexpr int ES = L::ES;
     static constexpr int KU = L::UNITS;
-    static constexpr int VB = 16 * V * ES;         // v tile bytes (16 tokens x V columns)
+    static constexpr int VB = 16 * VT * ES;        // v tile bytes (16 tokens x VT columns)
     static constexpr int VU = (VB + 1023) / 1024;
     static constexpr int U = KU + VU;              // 1 KiB copies per sub-tile
     static constexpr int SLOT = U * 1024;
-    static constexpr int OPITCH = V + 4;           // fp32 o staging row pitch (bank spread)
+    static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
     static constexpr int OBUF = 2 * 16 * OPITCH * 4;
     static constexpr int DFIT = (152 * 1024 - OBUF) / SLOT;
     // at most 8 wavefronts (two per SIMD) keeps 256 registers per lane
@@ -567,6 +941,24 @@ struct StateCfg {
     static_assert(D >= 3, "ring too shallow");
 };
 
+// [A | B] stacking of two 4-slot operands into one 8-slot operand.
+__device__ __forceinline__ Frag8<true> cat4(const Frag4<true> &a, const Frag4<true> &b) {
+    Frag8<true> f;
+    f.p[0] = a.p[0]; f.p[1] = a.p[1]; f.p[2] = b.p[0]; f.p[3] = b.p[1];
+    return f;
+}
+__device__ __forceinline__ Frag8<false> cat4(const Frag4<false> &a, const Frag4<false> &b) {
+    Frag8<false> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f.f[i] = a.f[i]; f.f[4 + i] = b.f[i]; }
+    return f;
+}
+template <bool BF> __device__ __forceinline__ Frag4<BF> zero_frag4() {
+    Frag4<BF> f;
+    if constexpr (BF) { f.p[0] = 0u; f.p[1] = 0u; } else { set4(f, 0.f, 0.f, 0.f, 0.f); }
+    return f;
+}
+
 template <bool BF, int K, int V, int CS>
 __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_pass(
     const void *__restrict__ vp, const float *__restrict__ S0, void *__restrict__ op, int o_bf16,
@@ -575,11 +967,12 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     using C = StateCfg<BF, K, V, CS>;
     using L = SubLayout<BF, K, CS>;
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, D = C::D, NL = C::NL;
+    constexpr int CT = C::CT, VT = C::VT, NT = C::NT;
     extern __shared__ __align__(1024) char smem[];
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
-    const int head = blockIdx.x;  // sequence * H + head
-    if (head >= N * H) return;    // whole workgroup: uniform
+    const int head = blockIdx.x / NT, tile = blockIdx.x % NT;  // head = sequence * H + head
+    if (head >= N * H) return;                                  // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int c0 = chunk_off[n], nu = (chunk_off[n + 1] - c0) * CS;  // sub-tile steps
@@ -593,24 +986,24 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
         const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
         const float *ob = obuf + (u & 1) * 16 * C::OPITCH;
         if (o_bf16) {
-            constexpr int UPR = V / 8;
+            constexpr int UPR = VT / 8;
             for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
                 const int row = idx / UPR, c8 = (idx % UPR) * 8;
                 if (row < nval) {
                     const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
                     const float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + c8;
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c8;
                     *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w),
                                                                  pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
                 }
             }
         } else {
-            constexpr int UPR = V / 4;
+            constexpr int UPR = VT / 4;
             for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
                 const int row = idx / UPR, c4 = (idx % UPR) * 4;
                 if (row < nval) {
                     const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
-                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + c4;
+                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c4;
                     *reinterpret_cast<float4 *>(dst) = a;
                 }
             }
@@ -632,11 +1025,11 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
 #pragma unroll
             for (int q = 0; q < C::VU; ++q) {
                 const int off = q * 1024 + lane * 16;
-                const int64_t rw = off / (V * ES);
-                const int within = off % (V * ES);
+                const int64_t rw = off / (VT * ES);
+                const int within = off % (VT * ES);
                 // padding and masked rows re-read a valid token of the sequence
                 const int64_t tok = (rw < nval) ? tok0 + rw : s1 - 1;
-                const char *src = vbase + ((tok * H + h) * V) * ES + within;
+                const char *src = vbase + ((tok * H + h) * V + (int64_t)tile * VT) * ES + within;
                 dma16(slot + (uint32_t)((C::KU + q) * 1024), src);
             }
         };
@@ -658,30 +1051,30 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
         return;
     }
 
-    // ---------------- compute wavefronts: lane (tg, cl) owns value columns c2 (tile 0) and c2+1 (tile 1)
+    // ---------------- compute wavefronts: lane (tg, cl) owns value columns cc .. cc+CT-1 (one per tile)
     const int tg = lane >> 4, cl = lane & 15;
-    const int c2 = w * 32 + 2 * cl;
-    f32x4 S[2][KT];  // S[ct][rt][i] = S[key channel state_row_channel(16rt + 4tg + i)][c2 + ct]
+    const int lc = w * 16 * CT + CT * cl;   // first column within the workgroup's tile
+    const int cc = tile * VT + lc;          // first column of the head
+    f32x4 S[CT][KT];  // S[ct][rt][i] = S[key channel state_row_channel(16rt + 4tg + i)][cc + ct]
     const size_t sbase = ((size_t)n * H + h) * K * V;
-    if (S0) {
 #pragma unroll
-        for (int rt = 0; rt < KT; ++rt)
+    for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float2 x =
-                    *reinterpret_cast<const float2 *>(S0 + sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + c2);
+        for (int i = 0; i < 4; ++i) {
+            const size_t e = sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + cc;
+            if constexpr (CT == 2) {
+                const float2 x = S0 ? *reinterpret_cast<const float2 *>(S0 + e) : make_float2(0.f, 0.f);
                 S[0][rt][i] = x.x;
                 S[1][rt][i] = x.y;
+            } else {
+                S[0][rt][i] = S0 ? S0[e] : 0.f;
             }
-    } else {
-#pragma unroll
-        for (int rt = 0; rt < KT; ++rt) S[0][rt] = S[1][rt] = zero4();
-    }
+        }
     // the state as the B operand of 32-deep products (slots 0..3: tile 2s, 4..7: tile 2s+1)
-    Frag8<BF> sb[2][KS];
+    Frag8<BF> sb[CT][KS];
     auto pack_state = [&]() {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 if constexpr (BF) {
@@ -700,34 +1093,46 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     };
     pack_state();
 
-    // operands of a step's first product chain (T, the v tile, -Wk); read one step ahead
-    Frag4<BF> tt, vf[2];
+    // operands of a step's first product chain (T tiles, the v tile, -Wk); read one step ahead
+    Frag4<BF> tt[CS], vf[CT];
     Frag8<BF> wk[KS];
     auto read_first = [&](const char *sl) {
-        tt = ld_frag4<BF>(sl + L::TT + lane * 4 * ES);
-        {
-            const char *vt = sl + C::KU * 1024;
-            if constexpr (BF) {
-                uint32_t x[4];  // columns (c2, c2+1) of tokens 4tg+j
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint32_t *>(vt + ((4 * tg + j) * V + c2) * 2);
-                vf[0].p[0] = (x[0] & 0xffffu) | (x[1] << 16);
-                vf[0].p[1] = (x[2] & 0xffffu) | (x[3] << 16);
-                vf[1].p[0] = (x[0] >> 16) | (x[1] & 0xffff0000u);
-                vf[1].p[1] = (x[2] >> 16) | (x[3] & 0xffff0000u);
-            } else {
-                float2 x[4];
+        for (int I = 0; I < CS; ++I) tt[I] = ld_frag4<BF>(sl + L::TT + (I * 64 + lane) * 4 * ES);
+        const char *vt = sl + C::KU * 1024;
+        if constexpr (CT == 2 && BF) {
+            uint32_t x[4];  // columns (lc, lc+1) of tokens 4tg+j
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float2 *>(vt + ((4 * tg + j) * V + c2) * 4);
-                set4(vf[0], x[0].x, x[1].x, x[2].x, x[3].x);
-                set4(vf[1], x[0].y, x[1].y, x[2].y, x[3].y);
+            for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint32_t *>(vt + ((4 * tg + j) * VT + lc) * 2);
+            vf[0].p[0] = (x[0] & 0xffffu) | (x[1] << 16);
+            vf[0].p[1] = (x[2] & 0xffffu) | (x[3] << 16);
+            vf[CT - 1].p[0] = (x[0] >> 16) | (x[1] & 0xffff0000u);
+            vf[CT - 1].p[1] = (x[2] >> 16) | (x[3] & 0xffff0000u);
+        } else if constexpr (CT == 2) {
+            float2 x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float2 *>(vt + ((4 * tg + j) * VT + lc) * 4);
+            set4(vf[0], x[0].x, x[1].x, x[2].x, x[3].x);
+            set4(vf[CT - 1], x[0].y, x[1].y, x[2].y, x[3].y);
+        } else {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int off = ((4 * tg + j) * VT + lc) * ES;
+                if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
+                else x[j] = *reinterpret_cast<const float *>(vt + off);
             }
+            set4(vf[0], x[0], x[1], x[2], x[3]);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
     };
 
+    // 64-token chunks: v fragments and corrected values [Wh | Wl] of the chunk's earlier sub-tiles
+    Frag4<BF> vhist[CS][CT];
+    Frag8<BF> whist[CS][CT];
     for (int u = 0; u < nu; ++u) {
+        const int R = CS == 1 ? 0 : (u & (CS - 1));
         lds_done_barrier();  // B_u
         const char *sl = smem + (u % D) * C::SLOT;
         if (u == 0) read_first(sl);
@@ -736,63 +1141,73 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
         Frag8<BF> kp2[KT / 2];
 #pragma unroll
         for (int p2 = 0; p2 < KT / 2; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
-        // Gamma_C: lane (tg, cl) reads state rows 16(cl/2) + 4tg + 2(cl%2) + {0, 1}; row rt, entry i of
-        // lane group tg then comes from lane 2rt + i/2 of the same row (DPP row broadcast)
-        const float2 g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
+        // Gamma_C (first sub-tile of a chunk): lane (tg, cl) reads state rows 16(cl/2) + 4tg +
+        // 2(cl%2) + {0, 1}; row rt, entry i of lane group tg then comes from lane 2rt + i/2 of the
+        // same row (DPP row broadcast)
+        float2 g2 = make_float2(1.f, 1.f);
+        if (R == 0) g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
         Frag8<BF> qh[KS], ql[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
             if constexpr (BF) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
         }
-        Frag4<BF> ph, pl;
-        if constexpr (BF) {
-            const uint4 x = *reinterpret_cast<const uint4 *>(sl + L::PP + lane * 16);
-            ph.p[0] = x.x; ph.p[1] = x.y; pl.p[0] = x.z; pl.p[1] = x.w;
-        } else {
-            ph = ld_frag4<BF>(sl + L::PP + lane * 16);
+        Frag4<BF> ph[CS], pl[CS];
+#pragma unroll
+        for (int I = 0; I < CS; ++I) {
+            if (I > R) continue;
+            if constexpr (BF) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(sl + L::PP + (I * 64 + lane) * 16);
+                ph[I].p[0] = x.x; ph[I].p[1] = x.y; pl[I].p[0] = x.z; pl[I].p[1] = x.w;
+            } else {
+                ph[I] = ld_frag4<BF>(sl + L::PP + (I * 64 + lane) * 16);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int I = 0; I < CS; ++I)
+            if (I == R)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) vhist[I][ct] = vf[ct];
 
-        // ---- W = T V + (-Wk) S: one accumulation chain per tile, every product 32 deep (T V
-        // as [T | 0] x [V | 0]; a chain that mixes 16-deep and 32-deep products read a stale
-        // accumulator on gfx950)
-        f32x4 W[2], O[2];
-        {
-            Frag8<BF> t8;
-            if constexpr (BF) {
-                t8.p[0] = tt.p[0]; t8.p[1] = tt.p[1]; t8.p[2] = 0u; t8.p[3] = 0u;
-            } else {
+        // ---- W = sum_{I<=R} T_RI V_I + (-Wk) S: one accumulation chain per tile, every product
+        // 32 deep (T V pairs stacked as [T_RI | T_RI'] x [V_I | V_I']; a chain that mixes
+        // 16-deep and 32-deep products read a stale accumulator on gfx950)
+        f32x4 W[CT], O[CT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { t8.f[i] = tt.f[i]; t8.f[4 + i] = 0.f; }
+        for (int ct = 0; ct < CT; ++ct) {
+            W[ct] = zero4();
+#pragma unroll
+            for (int I = 0; I < CS; I += 2) {
+                if (I > R) continue;
+                const bool two = I + 1 <= R;
+                const Frag4<BF> z = zero_frag4<BF>();
+                W[ct] = mma32(W[ct], cat4(tt[I], two ? tt[I + 1 < CS ? I + 1 : I] : z),
+                              cat4(vhist[I][ct], two ? vhist[I + 1 < CS ? I + 1 : I][ct] : z));
             }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                Frag8<BF> v8;
-                if constexpr (BF) {
-                    v8.p[0] = vf[ct].p[0]; v8.p[1] = vf[ct].p[1]; v8.p[2] = 0u; v8.p[3] = 0u;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) { v8.f[i] = vf[ct].f[i]; v8.f[4 + i] = 0.f; }
-                }
-                W[ct] = mma32(zero4(), t8, v8);
-#pragma unroll
-                for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
-            }
+            for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
         }
-        mfma_fence(W[0], W[1]);
+        if constexpr (CT == 2) mfma_fence(W[0], W[CT - 1]);
+        else mfma_fence(W[0]);
         if constexpr (BF) {
             // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
             // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
-            Frag8<true> whl[2];  // [Wh | Wl]
+            Frag8<true> whl[CT];  // [Wh | Wl]
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 uint32_t wh0, wl0, wh1, wl1;
                 split_bf16(W[ct][0], W[ct][1], wh0, wl0);
                 split_bf16(W[ct][2], W[ct][3], wh1, wl1);
                 whl[ct].p[0] = wh0; whl[ct].p[1] = wh1; whl[ct].p[2] = wl0; whl[ct].p[3] = wl1;
             }
-            // S <- diag(Gamma_C) S + [Kp | Kp]^T [Wh | Wl]   (first: the next step waits on it)
+#pragma unroll
+            for (int I = 0; I < CS; ++I)
+                if (I == R)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) whist[I][ct] = whl[ct];
+            // S <- diag(Gamma_C) S (at a chunk's first sub-tile) + [Kp | Kp]^T [Wh | Wl]
+            // (first: the next step waits on it)
 #pragma unroll
             for (int rt = 0; rt < KT; ++rt) {
                 float gm[4];
@@ -803,19 +1218,24 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
                 kk.p[0] = kq.p[2 * (rt & 1)]; kk.p[1] = kq.p[2 * (rt & 1) + 1];
                 kk.p[2] = kk.p[0]; kk.p[3] = kk.p[1];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < CT; ++ct) {
                     S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
                     S[ct][rt] = mma32(S[ct][rt], kk, whl[ct]);
                 }
             }
-            // O = (Q*Gamma)_hi S + (Q*Gamma)_lo S + [Ph | Ph] x [Wh | Wl] + [Pl | 0] x [Wh | Wl]
-            Frag8<true> pp, pz;
-            pp.p[0] = ph.p[0]; pp.p[1] = ph.p[1]; pp.p[2] = ph.p[0]; pp.p[3] = ph.p[1];
-            pz.p[0] = pl.p[0]; pz.p[1] = pl.p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
+            // O = sum_{I<=R} ([Ph | Ph] + [Pl | 0]) x [Wh | Wl]_I + (Q*Gamma)_hi S + (Q*Gamma)_lo S
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                O[ct] = mma32(zero4(), pp, whl[ct]);
-                O[ct] = mma32(O[ct], pz, whl[ct]);
+            for (int ct = 0; ct < CT; ++ct) {
+                O[ct] = zero4();
+#pragma unroll
+                for (int I = 0; I < CS; ++I) {
+                    if (I > R) continue;
+                    Frag8<true> pp, pz;
+                    pp.p[0] = ph[I].p[0]; pp.p[1] = ph[I].p[1]; pp.p[2] = ph[I].p[0]; pp.p[3] = ph[I].p[1];
+                    pz.p[0] = pl[I].p[0]; pz.p[1] = pl[I].p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
+                    O[ct] = mma32(O[ct], pp, whist[I][ct]);
+                    O[ct] = mma32(O[ct], pz, whist[I][ct]);
+                }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
@@ -823,9 +1243,15 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
                 }
             }
         } else {
-            Frag4<false> wf[2];
+            // fp32: W kept whole (slots 0..3 of the history; 4..7 zero)
+            Frag4<false> wf[CT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) set4(wf[ct], W[ct][0], W[ct][1], W[ct][2], W[ct][3]);
+            for (int ct = 0; ct < CT; ++ct) {
+                set4(wf[ct], W[ct][0], W[ct][1], W[ct][2], W[ct][3]);
+#pragma unroll
+                for (int I = 0; I < CS; ++I)
+                    if (I == R) whist[I][ct] = cat4(wf[ct], zero_frag4<false>());
+            }
 #pragma unroll
             for (int rt = 0; rt < KT; ++rt) {
                 float gm[4];
@@ -835,14 +1261,21 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
                 Frag4<false> kf;
                 set4(kf, kq.f[4 * (rt & 1)], kq.f[4 * (rt & 1) + 1], kq.f[4 * (rt & 1) + 2], kq.f[4 * (rt & 1) + 3]);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < CT; ++ct) {
                     S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
                     S[ct][rt] = mma16(S[ct][rt], kf, wf[ct]);
                 }
             }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                O[ct] = mma16(zero4(), ph, wf[ct]);
+            for (int ct = 0; ct < CT; ++ct) {
+                O[ct] = zero4();
+#pragma unroll
+                for (int I = 0; I < CS; ++I) {
+                    if (I > R) continue;
+                    Frag4<false> wi;
+                    set4(wi, whist[I][ct].f[0], whist[I][ct].f[1], whist[I][ct].f[2], whist[I][ct].f[3]);
+                    O[ct] = mma16(O[ct], ph[I], wi);
+                }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
             }
@@ -853,13 +1286,17 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
         __builtin_amdgcn_sched_barrier(0);
         // the state products were issued first: packing the next operand overlaps the output products
         mfma_fence_all(S);
-        pack_state();  // operand for the next step
-        mfma_fence(O[0], O[1]);
+        if (R == CS - 1) pack_state();  // operand for the next chunk
+        if constexpr (CT == 2) mfma_fence(O[0], O[CT - 1]);
+        else mfma_fence(O[0]);
         {
             float *ob = obuf + (u & 1) * 16 * C::OPITCH;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + c2) = make_float2(O[0][i], O[1][i]);
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (CT == 2)
+                    *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + lc) = make_float2(O[0][i], O[CT - 1][i]);
+                else ob[(4 * tg + i) * C::OPITCH + lc] = O[0][i];
+            }
         }
     }
     if (nu > 0) lds_done_barrier();  // B_nu: the loader wavefronts store the last o rows
@@ -867,9 +1304,11 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<float2 *>(Sfin + sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + c2) =
-                    make_float2(S[0][rt][i], S[1][rt][i]);
+            for (int i = 0; i < 4; ++i) {
+                const size_t e = sbase + (size_t)state_row_channel(16 * rt + 4 * tg + i) * V + cc;
+                if constexpr (CT == 2) *reinterpret_cast<float2 *>(Sfin + e) = make_float2(S[0][rt][i], S[1][rt][i]);
+                else Sfin[e] = S[0][rt][i];
+            }
     }
 }
 
@@ -891,9 +1330,13 @@ size_t table_bytes(int32_t num_seqs) {
 template <bool BF, int K, int CS>
 size_t chunk_bytes() { return (size_t)CS * SubLayout<BF, K, CS>::BYTES; }
 
-size_t chunk_bytes_rt(bool bf, int K) {
-    if (bf) return K == 32 ? chunk_bytes<true, 32, 1>() : K == 64 ? chunk_bytes<true, 64, 1>() : chunk_bytes<true, 128, 1>();
-    return K == 32 ? chunk_bytes<false, 32, 1>() : K == 64 ? chunk_bytes<false, 64, 1>() : chunk_bytes<false, 128, 1>();
+template <bool BF, int CS>
+size_t chunk_bytes_k(int K) {
+    return K == 32 ? chunk_bytes<BF, 32, CS>() : K == 64 ? chunk_bytes<BF, 64, CS>() : chunk_bytes<BF, 128, CS>();
+}
+size_t chunk_bytes_rt(bool bf, int K, int chunk) {
+    if (chunk == 64) return bf ? chunk_bytes_k<true, 4>(K) : chunk_bytes_k<false, 4>(K);
+    return bf ? chunk_bytes_k<true, 1>(K) : chunk_bytes_k<false, 1>(K);
 }
 
 struct WsPtrs {
@@ -910,54 +1353,70 @@ WsPtrs ws_ptrs(const PrefillArgs &a) {
     return w;
 }
 
+// Dynamic LDS above the default limit needs a one-time attribute per kernel (idempotent; a
+// race between threads only repeats the call).
+hipError_t allow_lds(const void *kernel, bool &done, int bytes) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
 template <bool BF, int K>
 hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
     hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
-                       (int32_t)SUB, w.seq_tok, w.chunk_off);
+                       (int32_t)a.chunk, w.seq_tok, w.chunk_off);
     if (a.n_chunks_max > 0) {
         const int64_t items = a.n_chunks_max * a.H;
-        const unsigned grid = (unsigned)((items + 3) / 4);
-        const size_t lds = 4 * (size_t)PrepLds<BF, K>::WAVE;
-        hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3(grid), dim3(256), lds, st, a.q, a.k, a.g, a.beta, a.H,
-                           a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
+        if (a.chunk == 64) {
+            static bool lds_set = false;
+            constexpr int LDS = Prep64Lds<BF, K>::BYTES;
+            hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K>), lds_set, LDS);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((kda_chunk_prep64<BF, K>), dim3((unsigned)items), dim3(256), LDS, st, a.q, a.k, a.g,
+                               a.beta, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
+        } else {
+            const unsigned grid = (unsigned)((items + 3) / 4);
+            const size_t lds = 4 * (size_t)PrepLds<BF, K>::WAVE;
+            hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3(grid), dim3(256), lds, st, a.q, a.k, a.g, a.beta, a.H,
+                               a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
+        }
     }
     return hipGetLastError();
 }
 
-template <bool BF, int K, int V>
+template <bool BF, int K, int V, int CS>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
-    constexpr int CS = 1;
     using C = StateCfg<BF, K, V, CS>;
     const WsPtrs w = ws_ptrs(a);
-    static bool lds_set = false;  // idempotent attribute; a race only repeats the call
-    if (!lds_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-        if (e != hipSuccess) return e;
-        lds_set = true;
-    }
-    const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.H);
+    static bool lds_set = false;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.H * C::NT);
     hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
                        (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     return hipGetLastError();
 }
 
+template <bool BF, int K, int CS>
+hipError_t state_v(const PrefillArgs &a, hipStream_t st) {
+    switch (a.V) {
+        case 32: return state_typed<BF, K, 32, CS>(a, st);
+        case 64: return state_typed<BF, K, 64, CS>(a, st);
+        default: return state_typed<BF, K, 128, CS>(a, st);
+    }
+}
 template <bool BF, int K>
 hipError_t state_k(const PrefillArgs &a, hipStream_t st) {
-    switch (a.V) {
-        case 32: return state_typed<BF, K, 32>(a, st);
-        case 64: return state_typed<BF, K, 64>(a, st);
-        default: return state_typed<BF, K, 128>(a, st);
-    }
+    return a.chunk == 64 ? state_v<BF, K, 4>(a, st) : state_v<BF, K, 1>(a, st);
 }
 
 }  // namespace
 
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16,
                                int32_t chunk) {
-    (void)chunk;
-    return table_bytes(num_seqs) + (size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K);
+    return table_bytes(num_seqs) + (size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk);
 }
 
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t st) {

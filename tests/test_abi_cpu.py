@@ -51,6 +51,9 @@ def test_workspace_bytes():
     assert ws(1, 4096, 96, 128, 128, 1, 16, 0) > n1
     # packed batches need room for one extra partial chunk per sequence
     assert ws(1, 4096, 96, 128, 128, 16, 16, 1) > n1
+    # 64-token chunks: one block of four 16-token sub-tiles per chunk
+    n64 = ws(1, 4096, 96, 128, 128, 1, 64, 1)
+    assert n64 > 0 and ws(1, 4096 + 64, 96, 128, 128, 1, 64, 1) > n64
     # unsupported sizes report 0
     assert ws(1, 4096, 96, 96, 128, 1, 16, 1) == 0
     assert ws(1, 4096, 96, 128, 128, 1, 32, 1) == 0
@@ -90,8 +93,8 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(T=1 << 40, H=96), INVALID),    # size overflow
     (dict(K=48), UNSUP),
     (dict(V=256), UNSUP),
-    (dict(chunk=64), UNSUP),
     (dict(chunk=8), UNSUP),
+    (dict(chunk=32), UNSUP),
     (dict(wsb=10), WS_SMALL),
     (dict(ws=None), WS_SMALL),
 ])

@@ -31,17 +31,17 @@ def _oracle(inp, heads=None):
                             None if cu is None else cu.cpu())
 
 
-def _run(inp, o_dtype=None):
+def _run(inp, o_dtype=None, chunk=16):
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
-                      cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype)
+                      cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk)
     torch.cuda.synchronize()
     return o, Sf
 
 
-def _check(inp, heads=None, io="bf16", written=None):
+def _check(inp, heads=None, io="bf16", written=None, chunk=16):
     """Run the GPU path (and for bf16 also with fp32 o) and compare with the oracle."""
     o_ref, S_ref = _oracle(inp, heads)
-    o, Sf = _run(inp)
+    o, Sf = _run(inp, chunk=chunk)
     sel = (lambda x: x[:, :, list(heads)]) if heads is not None else (lambda x: x)
     selS = (lambda x: x[:, list(heads)]) if heads is not None else (lambda x: x)
     o_c = sel(o).cpu()
@@ -53,7 +53,7 @@ def _check(inp, heads=None, io="bf16", written=None):
         print("  errors", res, flush=True)
         assert res["o"] <= TOL_FP32 and res["S"] <= TOL_FP32, res
         return o, Sf
-    o32, Sf32 = _run(inp, o_dtype=torch.float32)
+    o32, Sf32 = _run(inp, o_dtype=torch.float32, chunk=chunk)
     o32_c = sel(o32).cpu()
     if written is not None:
         o32_c = o32_c[:, written]
@@ -81,91 +81,116 @@ def test_tiny_fp32_workload():
     _check(inp, io="fp32")
 
 
+CHUNKS = pytest.mark.parametrize("chunk", [16, 64])
+
+
+@CHUNKS
 @pytest.mark.parametrize("B,T,H,K,V", [(2, 77, 3, 128, 128), (1, 50, 2, 64, 32), (1, 33, 2, 32, 128),
-                                       (1, 16, 1, 128, 64), (3, 5, 2, 32, 32)])
-def test_fp32_shapes_with_state(B, T, H, K, V):
-    _announce("fp32_shapes", B=B, T=T, H=H, K=K, V=V, seed=11)
+                                       (1, 16, 1, 128, 64), (3, 5, 2, 32, 32), (1, 130, 2, 64, 128)])
+def test_fp32_shapes_with_state(B, T, H, K, V, chunk):
+    _announce("fp32_shapes", B=B, T=T, H=H, K=K, V=V, chunk=chunk, seed=11)
     inp = synth.prefill_inputs(B, T, H, K, V, "fp32", seed=11, device=DEV, with_S0=True)
-    _check(inp, io="fp32")
+    _check(inp, io="fp32", chunk=chunk)
 
 
+@CHUNKS
 @pytest.mark.parametrize("B,T,H,K,V", [(2, 200, 3, 128, 128), (1, 97, 2, 64, 64), (1, 48, 4, 32, 128),
-                                       (2, 31, 2, 128, 32)])
-def test_bf16_shapes_with_state(B, T, H, K, V):
-    _announce("bf16_shapes", B=B, T=T, H=H, K=K, V=V, seed=12)
+                                       (2, 31, 2, 128, 32), (1, 129, 2, 128, 64)])
+def test_bf16_shapes_with_state(B, T, H, K, V, chunk):
+    _announce("bf16_shapes", B=B, T=T, H=H, K=K, V=V, chunk=chunk, seed=12)
     inp = synth.prefill_inputs(B, T, H, K, V, "bf16", seed=12, device=DEV, with_S0=True)
-    _check(inp)
+    _check(inp, chunk=chunk)
 
 
-def test_bf16_varlen_with_empty_and_ragged_sequences():
-    lengths = [37, 0, 16, 1, 150, 64, 0]
+@CHUNKS
+def test_bf16_varlen_with_empty_and_ragged_sequences(chunk):
+    lengths = [37, 0, 16, 1, 150, 64, 0, 65]
     cu = synth.cu_from_lengths(lengths)
-    _announce("bf16_varlen", lengths=lengths, seed=13)
+    _announce("bf16_varlen", lengths=lengths, chunk=chunk, seed=13)
     inp = synth.prefill_inputs(1, cu[-1], 4, 64, 64, "bf16", seed=13, device=DEV, cu_seqlens=cu, with_S0=True)
-    o, Sf = _check(inp)
+    o, Sf = _check(inp, chunk=chunk)
     S0 = inp["S0"]
     assert torch.equal(Sf[1], S0[1]) and torch.equal(Sf[6], S0[6]), "empty sequences return S0 exactly"
 
 
-def test_fp32_varlen():
-    lengths = [5, 0, 17, 32, 3]
+@CHUNKS
+def test_fp32_varlen(chunk):
+    lengths = [5, 0, 17, 32, 3, 70]
     cu = synth.cu_from_lengths(lengths)
-    _announce("fp32_varlen", lengths=lengths, seed=14)
+    _announce("fp32_varlen", lengths=lengths, chunk=chunk, seed=14)
     inp = synth.prefill_inputs(1, cu[-1], 3, 32, 64, "fp32", seed=14, device=DEV, cu_seqlens=cu, with_S0=True)
-    _check(inp, io="fp32")
+    _check(inp, io="fp32", chunk=chunk)
 
 
-def test_bf16_mild_decay_long_carry():
+@CHUNKS
+def test_bf16_mild_decay_long_carry(chunk):
     """g = -5 sigmoid(x - 6): alpha ~ 0.988, state carried across many chunks."""
-    _announce("bf16_mild_decay", T=1024, H=2, seed=15)
+    _announce("bf16_mild_decay", T=1024, H=2, chunk=chunk, seed=15)
     inp = synth.prefill_inputs(1, 1024, 2, 128, 128, "bf16", seed=15, device=DEV, with_S0=True, g_shift=-6.0)
-    _check(inp)
+    _check(inp, chunk=chunk)
 
 
-def test_range_edge_and_dense_recall():
-    """g = -5 exactly on every channel (e^-80 factors inside a chunk), beta = 1."""
-    _announce("range_edge", T=64, H=2, seed=16)
-    inp = synth.prefill_inputs(1, 64, 2, 128, 128, "bf16", seed=16, device=DEV, with_S0=True, g_const=-5.0,
+@CHUNKS
+def test_range_edge_and_dense_recall(chunk):
+    """g = -5 exactly on every channel (e^-80 factors inside a 16-token tile, e^-320 across a
+    64-token chunk), beta = 1."""
+    _announce("range_edge", T=160, H=2, chunk=chunk, seed=16)
+    inp = synth.prefill_inputs(1, 160, 2, 128, 128, "bf16", seed=16, device=DEV, with_S0=True, g_const=-5.0,
                                beta_const=1.0)
-    _check(inp)
+    _check(inp, chunk=chunk)
 
 
+@CHUNKS
 @pytest.mark.parametrize("io,K,V", [("fp32", 64, 64), ("bf16", 32, 128), ("bf16", 64, 32), ("bf16", 128, 128),
                                      ("fp32", 32, 32)])
-def test_passthrough_is_exact(io, K, V):
+def test_passthrough_is_exact(io, K, V, chunk):
     """beta = 0, g = 0: S_final is S0 bit for bit and o_t = S0^T q_t in every chunk
     (the state carried into chunks after the first is checked row by row)."""
-    _announce("passthrough", io=io, K=K, V=V, T=72, H=2, seed=17)
-    inp = synth.prefill_inputs(1, 72, 2, K, V, io, seed=17, device=DEV, with_S0=True, g_const=0.0, beta_const=0.0)
-    o, Sf = _run(inp, o_dtype=torch.float32)
+    _announce("passthrough", io=io, K=K, V=V, T=150, H=2, chunk=chunk, seed=17)
+    inp = synth.prefill_inputs(1, 150, 2, K, V, io, seed=17, device=DEV, with_S0=True, g_const=0.0, beta_const=0.0)
+    o, Sf = _run(inp, o_dtype=torch.float32, chunk=chunk)
     assert torch.equal(Sf, inp["S0"])
     o_ref = torch.einsum("bthk,bhkv->bthv", inp["q"].double().cpu(), inp["S0"].double().cpu())
     assert err(o.cpu(), o_ref) <= (TOL_FP32 if io == "fp32" else TOL_BF16)
 
 
-def test_zero_and_one_token():
+@CHUNKS
+def test_zero_and_one_token(chunk):
     for T in (0, 1):
-        _announce("short", T=T, seed=18)
+        _announce("short", T=T, chunk=chunk, seed=18)
         inp = synth.prefill_inputs(1, T, 2, 32, 32, "fp32", seed=18, device=DEV, with_S0=True)
-        o, Sf = _run(inp)
+        o, Sf = _run(inp, chunk=chunk)
         if T == 0:
             assert torch.equal(Sf, inp["S0"])
         else:
-            _check(inp, io="fp32")
+            _check(inp, io="fp32", chunk=chunk)
 
 
-def test_split_resume_matches_one_call():
-    _announce("split_resume", T=300, seed=19)
+@CHUNKS
+def test_split_resume_matches_one_call(chunk):
+    _announce("split_resume", T=300, chunk=chunk, seed=19)
     inp = synth.prefill_inputs(1, 300, 2, 128, 128, "fp32", seed=19, device=DEV, with_S0=True)
-    o, Sf = _run(inp)
+    o, Sf = _run(inp, chunk=chunk)
     s = 123
     a = {n: (x[:, :s].contiguous() if n in ("q", "k", "v", "g", "beta") else x) for n, x in inp.items()}
-    oa, Sa = _run(a)
+    oa, Sa = _run(a, chunk=chunk)
     b = {n: (x[:, s:].contiguous() if n in ("q", "k", "v", "g", "beta") else x) for n, x in inp.items()}
     b["S0"] = Sa
-    ob, Sb = _run(b)
+    ob, Sb = _run(b, chunk=chunk)
     assert err(torch.cat([oa, ob], 1).cpu(), o.cpu()) <= TOL_FP32
     assert err(Sb.cpu(), Sf.cpu()) <= TOL_FP32
+
+
+def test_chunk16_and_chunk64_agree():
+    """The chunk size is a reformulation: 16- and 64-token chunks give the same result within the
+    tolerance, on the benchmark distribution and with mild decay (long carry)."""
+    for gs, io in ((0.0, "bf16"), (-6.0, "bf16"), (0.0, "fp32")):
+        _announce("chunk16_vs_64", g_shift=gs, io=io, T=777, seed=21)
+        inp = synth.prefill_inputs(1, 777, 3, 128, 128, io, seed=21, device=DEV, with_S0=True, g_shift=gs)
+        o16, S16 = _run(inp, o_dtype=torch.float32, chunk=16)
+        o64, S64 = _run(inp, o_dtype=torch.float32, chunk=64)
+        tol = TOL_FP32 if io == "fp32" else TOL_BF16
+        assert err(o64.cpu(), o16.cpu()) <= tol and err(S64.cpu(), S16.cpu()) <= tol
 
 
 @pytest.mark.parametrize("io", ["bf16", "fp32"])
@@ -173,27 +198,30 @@ def test_split_resume_matches_one_call():
 @pytest.mark.parametrize("V", [32, 64, 128])
 def test_deterministic(io, K, V):
     """Bitwise run-to-run reproducibility (no atomics, no order-dependent reductions),
-    over every kernel variant; four repeats so an intermittent race shows up."""
+    over every kernel variant and both chunk sizes; repeats so an intermittent race shows up."""
     _announce("deterministic", io=io, K=K, V=V, seed=20)
     inp = synth.prefill_inputs(1, 500, 4, K, V, io, seed=20, device=DEV, with_S0=True)
-    o1, S1 = _run(inp, o_dtype=torch.float32)
-    for _ in range(3):
-        o2, S2 = _run(inp, o_dtype=torch.float32)
-        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for chunk in (16, 64):
+        o1, S1 = _run(inp, o_dtype=torch.float32, chunk=chunk)
+        for _ in range(3):
+            o2, S2 = _run(inp, o_dtype=torch.float32, chunk=chunk)
+            assert torch.equal(o1, o2) and torch.equal(S1, S2), chunk
 
 
-def test_k3_prefill_4k_all_heads():
-    """H=96, T=4096, K=V=128, bf16, chunk 16 (the benchmarked workload), every head."""
+@CHUNKS
+def test_k3_prefill_4k_all_heads(chunk):
+    """H=96, T=4096, K=V=128, bf16 (the benchmarked workload, chunk 16 and chunk 64), every head."""
     w = synth.WORKLOADS["prefill_4k"]
-    _announce("prefill_4k", seed=w.seed)
+    _announce("prefill_4k", chunk=chunk, seed=w.seed)
     inp = synth.workload_prefill_inputs(w, device=DEV)
-    _check(inp)
+    _check(inp, chunk=chunk)
 
 
-def test_k3_varlen_16_sampled_heads():
+@CHUNKS
+def test_k3_varlen_16_sampled_heads(chunk):
     """16 packed sequences (lengths 256..16384, ~130K tokens), H=96, per-sequence S0;
     the oracle runs on 3 heads, compared with the same heads of the full GPU call."""
     w = synth.WORKLOADS["varlen_16"]
-    _announce("varlen_16", seed=w.seed)
+    _announce("varlen_16", chunk=chunk, seed=w.seed)
     inp = synth.workload_prefill_inputs(w, device=DEV)
-    _check(inp, heads=(0, 41, 95))
+    _check(inp, heads=(0, 41, 95), chunk=chunk)
