@@ -4,9 +4,10 @@ A step is one chunked prefill (kda_chunk_prep + kda_chunk_state, i.e. one
 kda_chunk_fwd) of the K3-shaped workload: B=1, T=4096, H=96, K=V=128, bf16
 q/k/v/g/beta, chunk 16, zero initial state, returning o and S_final. Inputs
 are seeded synthetic tensors already resident in HBM. `value` is prefill
-tokens/s. The decode half of the metric (N=512 streams, H=96, fp32 state of
-~3.2 GB updated in place, 100 consecutive steps) is timed after the prefill
-steps and reported under "decode".
+tokens/s at chunk 16; the same workload is also timed at chunk 64 and
+reported under "chunk64". The decode half of the metric (N=512 streams,
+H=96, fp32 state of ~3.2 GB updated in place, 100 consecutive steps) is
+timed after the prefill steps and reported under "decode".
 
 Kernel durations come from HIP events recorded on the stream the kernels run
 on, around each phase of every timed step. Roofline figures use algorithmic
@@ -46,7 +47,7 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev):
+def time_prefill(w, steps, warmup, dev, chunk=16):
     lib = _lib.load()
     inp = synth.workload_prefill_inputs(w, device=dev)
     B, T, H, K = inp["q"].shape
@@ -54,18 +55,18 @@ def time_prefill(w, steps, warmup, dev):
     N = B
     o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
     Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, 16, 1)
+    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def prep():
-        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, 16, 1,
+        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1,
                                       ws.data_ptr(), wsb, sh), "kda_chunk_prep")
 
     def state():
-        _lib.check(lib.kda_chunk_state(p["v"], None, None, B, T, H, K, V, N, 16, 1, 1, o.data_ptr(),
+        _lib.check(lib.kda_chunk_state(p["v"], None, None, B, T, H, K, V, N, chunk, 1, 1, o.data_ptr(),
                                        Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
 
     for _ in range(warmup):
@@ -177,9 +178,15 @@ def main():
     dom = "state" if r["state_ms"] >= r["prep_ms"] else "prep"
     dom_ms = r["state_ms"] if dom == "state" else r["prep_ms"]
     dom_gbs = kb[dom] / (dom_ms * 1e-3) / 1e9
-    path_ms = r["prep_ms"] + r["state_ms"]
-    path_gbs = path_bytes / (path_ms * 1e-3) / 1e9
-    flops = prefill_flops(r["T"] * r["B"], r["H"], r["K"], r["V"])
+
+    def path_roofline(rr, C):
+        pm = rr["prep_ms"] + rr["state_ms"]
+        gbs = path_bytes / (pm * 1e-3) / 1e9
+        tf = prefill_flops(rr["T"] * rr["B"], rr["H"], rr["K"], rr["V"], C) / (pm * 1e-3) / 1e12
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "algorithmic_bytes": path_bytes, "event_ms": pm, "mfma_tflops_algorithmic": tf,
+                "mfma_frac_algorithmic": tf / BF16_PEAK_TFLOPS}
+
     out = {
         "metric": "KDA prefill tokens/s (H=96,d=128,bf16) + decode state GB/s, % of roofline",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -189,16 +196,22 @@ def main():
                    "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
                      "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128>" if dom == "state"
-                                                 else "kda::kda_chunk_prep<true, 128"),
+                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1>" if dom == "state"
+                                                 else "kda::kda_chunk_prep<true, 128>"),
                      "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms},
-        "roofline_path": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes": path_bytes,
-                          "event_ms": path_ms, "mfma_tflops_algorithmic": flops / (path_ms * 1e-3) / 1e12,
-                          "mfma_frac_algorithmic": flops / (path_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "roofline_path": path_roofline(r, 16),
         "kernels_ms": kern_ms,
         "workspace_bytes": r["ws_bytes"],
     }
+    print("[bench] prefill %s at chunk 64: warmup %d, steps %d" % (w.name, args.warmup, args.steps),
+          file=sys.stderr, flush=True)
+    r64 = time_prefill(w, args.steps, args.warmup, dev, chunk=64)
+    ms64 = r64["wall_s"] * 1e3 / args.steps
+    out["chunk64"] = {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 64, zero S0",
+                      "tokens_per_s": r64["B"] * r64["T"] / (ms64 * 1e-3), "ms_per_step": ms64,
+                      "kernels_ms": {"kda_chunk_prep64 (+chunk table)": r64["prep_ms"],
+                                     "kda_state_pass": r64["state_ms"]},
+                      "roofline_path": path_roofline(r64, 64), "workspace_bytes": r64["ws_bytes"]}
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
         print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)
