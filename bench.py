@@ -128,6 +128,39 @@ def measured_traffic(kernel_prefix):
     return None
 
 
+def traffic_from_counters(fetch_csv, write_csv, out_path):
+    """Per-launch HBM bytes of each kda kernel from two rocprofv3 counter runs of
+    `bench.py --counters` (FETCH_SIZE, then WRITE_SIZE; values in KiB per dispatch), each
+    scaled by what the same counter reads for the run's 1 GiB device copy; written as JSON
+    together with the hash of the kernel sources it was measured on."""
+    import csv
+    from collections import defaultdict
+    copy_bytes = 1 << 30
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        vals = defaultdict(list)
+        for r in rows:
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if "kda" in name:
+                vals[name].append(float(r["Counter_Value"]))
+        return copy, {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fcopy, f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wcopy, w = per_kernel(write_csv, "WRITE_SIZE")
+    fscale = copy_bytes / (fcopy * 1024.0)  # the copy reads and writes 1 GiB
+    wscale = copy_bytes / (wcopy * 1024.0)
+    out = {"csrc_hash": csrc_hash(), "fetch_scale": fscale, "write_scale": wscale, "kernels": {}}
+    for k in sorted(set(f) | set(w)):
+        fb = f.get(k, 0.0) * 1024.0 * fscale
+        wb = w.get(k, 0.0) * 1024.0 * wscale
+        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb}
+    with open(out_path, "w") as fh:
+        fh.write(json.dumps(out, indent=1) + "\n")
+    return out
+
+
 def cpu_baseline(w):
     """The fp64 oracle on the host, on the full prefill workload (generation excluded)."""
     import oracle  # test infrastructure: only this baseline leg uses it
@@ -154,7 +187,15 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="short pass for hardware-counter runs: a 1 GiB device copy (calibration of the byte "
                          "counters), then the prefill and decode steps, no CPU baseline")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two counter runs of --counters (FETCH_SIZE, WRITE_SIZE "
+                         "run_counter_collection.csv) into per-kernel HBM bytes (profiles/traffic.json)")
+    ap.add_argument("--traffic-out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                          "traffic.json"))
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from_counters(*args.traffic_from, args.traffic_out)))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (heads and sequences would "
               "shard without communication; see the design notes). Use --gpus 1.", file=sys.stderr)

@@ -971,8 +971,12 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     extern __shared__ __align__(1024) char smem[];
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
-    const int head = blockIdx.x / NT, tile = blockIdx.x % NT;  // head = sequence * H + head
-    if (head >= N * H) return;                                  // whole workgroup: uniform
+    // blockIdx -> (sequence * H + head, column tile). Workgroups are dealt to the 8 XCDs round-robin
+    // by index; the NT tiles of one head share an XCD (blocks 8 apart), so the workspace blocks
+    // every tile of that head reads come from one L2.
+    const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
+    const int head = (slot8 / NT) * 8 + xcd, tile = slot8 % NT;
+    if (head >= N * H) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int c0 = chunk_off[n], nu = (chunk_off[n + 1] - c0) * CS;  // sub-tile steps
@@ -1393,7 +1397,7 @@ hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
     static bool lds_set = false;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>), lds_set, C::LDS);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)((int64_t)a.num_seqs * a.H * C::NT);
+    const unsigned grid = (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * C::NT);
     hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
                        (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
     return hipGetLastError();
