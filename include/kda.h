@@ -33,7 +33,7 @@
  *     before anything is enqueued: on any error status nothing is launched
  *     and no output is written. A fault inside a kernel surfaces at the
  *     caller's next synchronisation of the stream.
- *   - Supported sizes: K, V in {32, 64, 128}; chunk = 16.
+ *   - Supported sizes: K, V in {32, 64, 128}; chunk in {16, 64}.
  *   - The functions keep no state between calls and may be called from
  *     several host threads on different streams (calls that share output
  *     buffers or a workspace race).
@@ -117,8 +117,13 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 
 /*
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
- * separately (kda_chunk_fwd is exactly kda_chunk_prep followed by
- * kda_chunk_state on one stream).
+ * separately. kda_chunk_fwd returns bitwise the results of kda_chunk_prep
+ * followed by kda_chunk_state on one stream; where the state pass leaves most
+ * of the GPU idle (16-token chunks, num_seqs * H <= 128, at least 128 chunks)
+ * it splits the chunks into ranges and runs the prep of each range beside the
+ * state pass of the previous one. The environment variable
+ * KDA_PIPELINE_RANGES (1 .. 16, read at each call) sets the number of ranges;
+ * 1 turns this off.
  *
  * kda_chunk_prep: everything that does not depend on the state. Numbers the
  *   chunks (cu_seqlens as for kda_chunk_fwd, read on the device) and, per

@@ -77,7 +77,7 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
     const bool packed = (B == 1);
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
-    return kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16, chunk);
+    return kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk);
 }
 
 namespace {
@@ -101,7 +101,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
-    const size_t need = kda::prefill_workspace_bytes(nc, H, K, num_seqs, io == KDA_DTYPE_BF16, chunk);
+    const size_t need = kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
@@ -126,9 +126,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     kda_status_t st = prefill_args(q, k, v, g, beta, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, o_dtype,
                                    o, S_final, workspace, workspace_bytes, true, true, a);
     if (st != KDA_SUCCESS) return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (kda::launch_prep(a, s) != hipSuccess) return KDA_ERROR_HIP;
-    if (kda::launch_state(a, s) != hipSuccess) return KDA_ERROR_HIP;
+    if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }
 

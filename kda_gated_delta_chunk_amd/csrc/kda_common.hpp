@@ -114,6 +114,9 @@ __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b) {
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c) {
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c));
 }
+__device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 __device__ __forceinline__ void mfma_fence(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d, f32x4 &e) {
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e));
 }

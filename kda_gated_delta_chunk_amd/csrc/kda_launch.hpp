@@ -23,12 +23,16 @@ struct PrefillArgs {
 };
 
 // Workspace bytes for a prefill with at most n_chunks_max chunks.
-size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16,
-                               int32_t chunk);
+size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                               bool io_bf16, int32_t chunk);
 // Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
 // Enqueue the state pass over a workspace that launch_prep filled with the same sizes.
 hipError_t launch_state(const PrefillArgs &a, hipStream_t stream);
+// The whole prefill: launch_prep then launch_state, or, where the state pass leaves most CUs
+// free, the same work over consecutive chunk ranges with the prep of each range running beside
+// the state pass of the one before.
+hipError_t launch_fwd(const PrefillArgs &a, hipStream_t stream);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;

@@ -68,9 +68,11 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 // Workspace block per (chunk, head, sub-tile), in bytes (ES = element size).
 // Fragment orders (lane = 16 * a + m):
 //   [KS][64][8]  : lane (a, m) holds token m, key channels 32s + 8a .. +7
-//   [KT/2][64][8]: state update, tiles rt = 2p (slots 0..3) and 2p+1 (slots 4..7):
-//                  lane (a, m) holds tokens 4a .. 4a+3 of key channel
-//                  state_row_channel(16 rt + m)
+//   KP, bf16 [KT][64][8]: state update, tile rt: lane (a, m) holds tokens
+//                  4a .. 4a+3 of key channel state_row_channel(16 rt + m), hi
+//                  parts in slots 0..3, lo parts in 4..7
+//   KP, fp32 [KT/2][64][8]: tiles rt = 2p (slots 0..3) and 2p+1 (slots 4..7),
+//                  same tokens and channels, one part
 //   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
 //                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
 //                  columns 4a .. 4a+3
@@ -84,8 +86,8 @@ struct SubLayout {
     static constexpr int WK = 0;                        // -Wk rows [KS][64][8]
     static constexpr int QH = WK + KS * F8;             // Q*Gamma [KS][64][8] (hi)
     static constexpr int QL = QH + KS * F8;             // Q*Gamma lo part (bf16 only)
-    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b) [KT/2][64][8]
-    static constexpr int PP = KP + (KT / 2) * F8;       // P tiles [CS][64][8] (hi | lo)
+    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b), bf16 [KT][64][8], fp32 [KT/2][64][8]
+    static constexpr int PP = KP + (BF ? KT : KT / 2) * F8;  // P tiles [CS][64][8] (hi | lo)
     static constexpr int TT = PP + CS * (BF ? F8 : F4); // T tiles [CS][64][4]
     static constexpr int GC = TT + CS * F4;             // Gamma_C [K] fp32 in state-row order (sub-tile 0)
     static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
@@ -186,15 +188,16 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int gc)
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); }
 
 // LDS of the prep kernel, per wavefront: a transposed [K][16] operand tile
-// (K*Gamma for Wk, then K*exp(b_C-b)), A^T and T of the 16x16 tile, P and the
-// sub-tile's betas.
+// (K*Gamma, for Wk), the staged K*exp(b_C-b), A^T and T of the 16x16 tile, P
+// and the sub-tile's betas.
 template <bool BF, int K>
 struct PrepLds {
     static constexpr int ES = BF ? 2 : 4;
     static constexpr int MP = 20;                  // pitch (floats) of 16x16 matrices
     static constexpr int M16 = 16 * MP * 4;
     static constexpr int XT = 0;                   // [K][16 tokens]
-    static constexpr int SA = XT + K * 16 * ES;    // A^T
+    static constexpr int KX = XT + K * 16 * ES;    // K*exp(b_C-b) [K][16 tokens] (bf16: hi tile, then lo tile)
+    static constexpr int SA = KX + K * 16 * 4;     // A^T
     static constexpr int ST = SA + M16;            // T
     static constexpr int SP = ST + M16;            // P
     static constexpr int SB = SP + M16;            // beta [16]
@@ -312,6 +315,54 @@ __device__ __forceinline__ void st_run4(char *dst, float a, float b, float c, fl
     else *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
 }
 
+// K*exp(b_C - b) staging: a per-wavefront LDS tile of one sub-tile, [K][16 tokens], channel-major.
+// bf16: hi parts [K][16], then lo parts [K][16] (hi + lo carries about 16 significant bits: the
+// state update is the one product whose rounding reaches S_final undamped); fp32: one [K][16] tile.
+template <bool BF, int K>
+__device__ __forceinline__ void put_kp8(char *tile, int c0, int r, const float (&x)[8]) {
+    if constexpr (BF) {
+        uint16_t *hi = reinterpret_cast<uint16_t *>(tile), *lo = hi + K * 16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t h, l;
+            split_bf16(x[2 * t], x[2 * t + 1], h, l);
+            hi[(c0 + 2 * t) * 16 + r] = (uint16_t)h;
+            hi[(c0 + 2 * t + 1) * 16 + r] = (uint16_t)(h >> 16);
+            lo[(c0 + 2 * t) * 16 + r] = (uint16_t)l;
+            lo[(c0 + 2 * t + 1) * 16 + r] = (uint16_t)(l >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) reinterpret_cast<float *>(tile)[(c0 + j) * 16 + r] = x[j];
+    }
+}
+// The staged tile to the workspace in the state update's fragment order (state row 16 rt + m
+// holds key channel state_row_channel(16 rt + m)).
+template <bool BF, int K>
+__device__ __forceinline__ void store_kp(const char *tile, char *dst, int lane) {
+    constexpr int KT = K / 16;
+    const int ag = lane >> 4, r = lane & 15;
+    if constexpr (BF) {
+        const uint16_t *hi = reinterpret_cast<const uint16_t *>(tile), *lo = hi + K * 16;
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) {
+            const int e = state_row_channel(16 * rt + r) * 16 + 4 * ag;
+            const uint2 h = *reinterpret_cast<const uint2 *>(hi + e);
+            const uint2 l = *reinterpret_cast<const uint2 *>(lo + e);
+            *reinterpret_cast<uint4 *>(dst + (rt * 64 + lane) * 16) = make_uint4(h.x, h.y, l.x, l.y);
+        }
+    } else {
+        const float *x = reinterpret_cast<const float *>(tile);
+#pragma unroll
+        for (int p2 = 0; p2 < KT / 2; ++p2) {
+            const float4 f0 = *reinterpret_cast<const float4 *>(x + state_row_channel(32 * p2 + r) * 16 + 4 * ag);
+            const float4 f1 = *reinterpret_cast<const float4 *>(x + state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag);
+            *reinterpret_cast<float4 *>(dst + (p2 * 64 + lane) * 32) = f0;
+            *reinterpret_cast<float4 *>(dst + (p2 * 64 + lane) * 32 + 16) = f1;
+        }
+    }
+}
+
 // x[4g + i] for a lane-group index g known only at run time (no register indexing).
 __device__ __forceinline__ float pick16(const float (&x)[16], int g, int i) {
     const float a = x[i], b = x[4 + i], c = x[8 + i], d = x[12 + i];
@@ -340,25 +391,37 @@ __device__ __forceinline__ void solve16(const float *sAT, int n, float (&x)[16])
     }
 }
 
-// At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
-// the matrix-core accumulators in VGPRs, as mfma_fence expects.
+// Arguments shared by the prep kernels: inputs, the chunk table and the
+// workspace, and the range [g0, g1) of global chunk indices to prepare.
+struct PrepParams {
+    const void *q, *k, *g, *beta;
+    int32_t H, N;
+    const int64_t *seq_tok;
+    const int32_t *chunk_off;
+    char *frags;
+    int32_t g0, g1;
+};
+
+// The 16-token prep of item (chunk g0 + item / H, head item % H) by one
+// wavefront, with D::WAVE bytes of LDS of its own at `lds`. No workgroup
+// barriers: wavefronts of a workgroup are independent.
 template <bool BF, int K>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(
-    const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ gp,
-    const void *__restrict__ bp, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
-    const int32_t *__restrict__ chunk_off, char *__restrict__ frags) {
+__device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, char *lds) {
     using L = SubLayout<BF, K, 1>;
     using D = PrepLds<BF, K>;
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP;
-    extern __shared__ __align__(16) char smem[];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
+    const int32_t H = pa.H, N = pa.N;
+    const int64_t *__restrict__ seq_tok = pa.seq_tok;
+    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    char *__restrict__ frags = pa.frags;
+    const int lane = threadIdx.x & 63;
     const int ag = lane >> 4, r = lane & 15;  // lane group; token (row) or column in a tile
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    const int total = chunk_off[N];
-    const int gc = (int)(item / H), h = (int)(item % H);
-    if (gc >= total) return;  // wave-uniform; no workgroup barriers in this kernel
-    char *lds = smem + wave * D::WAVE;
+    const int total = chunk_off[N] < pa.g1 ? chunk_off[N] : pa.g1;
+    const int gc = pa.g0 + (int)(item / H), h = (int)(item % H);
+    if (gc >= total) return;  // wave-uniform
     char *xt = lds + D::XT;
+    char *kx = lds + D::KX;
     float *sAT = reinterpret_cast<float *>(lds + D::SA);
     float *sT = reinterpret_cast<float *>(lds + D::ST);
     float *sP = reinterpret_cast<float *>(lds + D::SP);
@@ -399,10 +462,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // is this lane's row layout); K*Gamma is transposed through LDS for Wk.
     char *blk = frags + ((size_t)gc * H + h) * L::BYTES;
     Frag8<BF> qh[KS], ql[KS], kgf[KS], kih[KS], kil[KS];
-    float kpv[KS][8];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        float qg[8], kg[8], ki[8];
+        float qg[8], kg[8], ki[8], kpv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float e = __builtin_amdgcn_exp2f(bl[s][j]);
@@ -410,9 +472,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             qg[j] = qv[s][j] * e;
             kg[j] = kv[s][j] * e;
             ki[j] = kv[s][j] * ei;
-            kpv[s][j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
+            kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
             st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
         }
+        put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
         split8(qg, qh[s], ql[s]);
         kgf[s] = frag8_of(kg, Frag8<BF>{});
         split8(ki, kih[s], kil[s]);
@@ -490,22 +553,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                         -w[t][3]);
         }
     }
-    lds_sync();  // the Wk reads of the tile are done before it is overwritten
 
-    // ---- K*exp(b_C - b): transposed through the same tile, then out in state-row order
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kpv[s][j]);
-    lds_sync();
-#pragma unroll
-    for (int p2 = 0; p2 < KT / 2; ++p2) {
-        const Frag4<BF> f0 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + r) * 16 + 4 * ag) * ES);
-        const Frag4<BF> f1 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag) * ES);
-        char *dst = blk + L::KP + (p2 * 64 + lane) * 8 * ES;
-        st_frag4<BF>(dst, f0);
-        st_frag4<BF>(dst + 4 * ES, f1);
-    }
+    // ---- K*exp(b_C - b) (staged in LDS since the start) out in state-row order
+    store_kp<BF, K>(kx, blk + L::KP, lane);
 
     // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
     if (r == 0) {
@@ -519,6 +569,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
         }
     }
+}
+
+// At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
+// the matrix-core accumulators in VGPRs, as mfma_fence expects.
+template <bool BF, int K>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(PrepParams pa) {
+    extern __shared__ __align__(16) char smem[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    prep16_item<BF, K>(pa, (int64_t)blockIdx.x * 4 + wave, smem + wave * PrepLds<BF, K>::WAVE);
 }
 
 // ------------------------------------------------- chunk prep, 64 tokens
@@ -543,7 +602,7 @@ struct Prep64Lds {
     static constexpr int BP = 68;                               // pitch (floats), 64-wide matrices
     static constexpr int XT_B = K * 16 * ES;                    // one transposed [K][16] tile
     static constexpr int KE_B = (BF ? 2 : 1) * KS * 64 * 8 * ES;  // scaled keys of a sub-tile, hi | lo
-    static constexpr int XT = 0;                                // [4] transposed K*Gamma, then K*exp(b_C-b)
+    static constexpr int XT = 0;                                // [4] transposed K*Gamma
     static constexpr int LB = XT + 4 * XT_B;                    // [4][K] sub-tile decay totals (base 2)
     static constexpr int B64 = LB + 4 * K * 4;                  // betas of the chunk [64]
     static constexpr int SP = B64 + 64 * 4;                     // [4] P row blocks [16][BP]
@@ -554,6 +613,11 @@ struct Prep64Lds {
     static constexpr int SA = A64 + 64 * BP * 4;                // [4] A^T of the diagonal blocks [16][MP]
     static constexpr int U1_B = (3 * KE_B > 64 * BP * 4 + 4 * 16 * MP * 4) ? 3 * KE_B : 64 * BP * 4 + 4 * 16 * MP * 4;
     static constexpr int BYTES = U1 + U1_B;
+    // staging of K*exp(b_C-b) ([K][16], 4 bytes per element) per wavefront, over SP and X64
+    // (free until the first workgroup barrier after the diagonal tiles)
+    static constexpr int KX = SP;
+    static constexpr int KX_B = K * 16 * 4;
+    static_assert(KX + 4 * KX_B <= U1, "K*exp(b_C-b) staging overlaps the union area");
 };
 
 // v x f elementwise for the eight values of one step (f: per channel, same for all tokens).
@@ -563,19 +627,21 @@ __device__ __forceinline__ void scale8(const float (&x)[8], const float (&f)[8],
 }
 
 template <bool BF, int K>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep64(
-    const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ gp,
-    const void *__restrict__ bp, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
-    const int32_t *__restrict__ chunk_off, char *__restrict__ frags) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep64(PrepParams pa) {
     constexpr int CS = 4;
     using L = SubLayout<BF, K, CS>;
     using D = Prep64Lds<BF, K>;
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP, BP = D::BP;
+    const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
+    const int32_t H = pa.H, N = pa.N;
+    const int64_t *__restrict__ seq_tok = pa.seq_tok;
+    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    char *__restrict__ frags = pa.frags;
     extern __shared__ __align__(16) char smem[];
     const int R = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ag = lane >> 4, r = lane & 15;
-    const int total = chunk_off[N];
-    const int gc = (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
+    const int total = chunk_off[N] < pa.g1 ? chunk_off[N] : pa.g1;
+    const int gc = pa.g0 + (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
     if (gc >= total) return;  // whole workgroup (uniform)
     char *xt = smem + D::XT + R * D::XT_B;
     float *lb = reinterpret_cast<float *>(smem + D::LB);
@@ -584,6 +650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     float *x64 = reinterpret_cast<float *>(smem + D::X64);
     float *a64 = reinterpret_cast<float *>(smem + D::A64);
     float *sAT = reinterpret_cast<float *>(smem + D::SA) + R * 16 * MP;
+    char *kx = smem + D::KX + R * D::KX_B;
 
     const int n = find_seq(chunk_off, N, gc);
     const int64_t t0c = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * (CS * SUB);
@@ -638,7 +705,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // ---- decay-scaled operands of this sub-tile. br = B_R (sum of the earlier sub-tiles' totals),
     // bc = B_4 (chunk total), for this lane's channels.
     char *blk = frags + (((size_t)gc * H + h) * CS + R) * L::BYTES;
-    Frag8<BF> kgf[KS], kih[KS], kil[KS], qlh[KS], qll[KS], kpp[KS];
+    Frag8<BF> kgf[KS], kih[KS], kil[KS], qlh[KS], qll[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         float br[8], bc[8];
@@ -672,12 +739,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         split8(qgc, qh, ql);
         st_frag8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES, qh);
         if constexpr (BF) st_frag8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES, ql);
-        // operands of the diagonal tile (sub-tile-relative scaling); K*exp(b_C-b) kept for the end
+        // operands of the diagonal tile (sub-tile-relative scaling)
         kgf[s] = frag8_of(kg, Frag8<BF>{});
         split8(ki, kih[s], kil[s]);
         split8(qg, qlh[s], qll[s]);
-        kpp[s] = frag8_of(kpv, Frag8<BF>{});
+        put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
     }
+    // ---- K*exp(b_C - b) out in state-row order (its staging tile lies in the P and X areas,
+    // which are first written after the next workgroup barrier)
+    lds_sync();
+    store_kp<BF, K>(kx, blk + L::KP, lane);
     // ---- diagonal tile: A_RR, P_RR from registers
     f32x4 A0 = zero4(), A1 = zero4(), P0 = zero4(), P1 = zero4(), P2 = zero4();
 #pragma unroll
@@ -847,22 +918,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                         -w[t][3]);
         }
     }
-    __syncthreads();  // every wavefront's reads of the K*Gamma tiles are done
 
-    // ---- K*exp(b_C - b) in state-row order, through this sub-tile's transposed tile
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, frag8_get(kpp[s], j));
-    lds_sync();
-#pragma unroll
-    for (int p2 = 0; p2 < KT / 2; ++p2) {
-        const Frag4<BF> f0 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + r) * 16 + 4 * ag) * ES);
-        const Frag4<BF> f1 = ld_frag4<BF>(xt + (state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag) * ES);
-        char *dst = blk + L::KP + (p2 * 64 + lane) * 8 * ES;
-        st_frag4<BF>(dst, f0);
-        st_frag4<BF>(dst + 4 * ES, f1);
-    }
     // ---- Gamma_C (chunk total) in state-row order, in sub-tile 0's block
     if (R == 0 && r == 0) {
         float *gcp = reinterpret_cast<float *>(blk + L::GC);
@@ -917,9 +973,12 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never has
 // more than one in flight; a sub-tile is copied NL steps before use.
 template <bool BF, int K, int V, int CS>
+#ifndef KDA_STATE_CT
+#define KDA_STATE_CT (CS == 1 ? 2 : 1)
+#endif
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
-    static constexpr int CT = CS == 1 ? 2 : 1;
+    static constexpr int CT = KDA_STATE_CT;
     static constexpr int NW = V / (16 * CT) < 4 ? V / (16 * CT) : 4;
     static constexpr int VT = 16 * CT * NW;        // columns per workgroup
     static constexpr int NT = V / VT;              // workgroups per (sequence, head)
@@ -959,32 +1018,63 @@ template <bool BF> __device__ __forceinline__ Frag4<BF> zero_frag4() {
     return f;
 }
 
+// Arguments of the state pass. One launch covers the global chunk range
+// [g0, g1): each (sequence, head) runs over its chunks inside the range. A
+// sequence that starts inside the range starts from S0 (or 0), one that ends
+// inside it writes S_final; in between, the state is carried to the next range
+// through Scarry ([N][H][K][V] fp32). Empty sequences are finished by the
+// launch that covers range 0 (`first`).
+struct StateParams {
+    const void *v;
+    const float *S0;
+    void *o;
+    int32_t o_bf16;
+    float *Sfin;
+    int32_t H, N;
+    const int64_t *seq_tok;
+    const int32_t *chunk_off;
+    const char *frags;
+    int32_t g0, g1;
+    float *Scarry;
+    int32_t first;
+};
+
+// The state pass of workgroup `bid` (C::LDS bytes of LDS at smem).
 template <bool BF, int K, int V, int CS>
-__global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_pass(
-    const void *__restrict__ vp, const float *__restrict__ S0, void *__restrict__ op, int o_bf16,
-    float *__restrict__ Sfin, int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
-    const int32_t *__restrict__ chunk_off, const char *__restrict__ frags) {
+__device__ __forceinline__ void state_body(const StateParams &pa, int bid, char *smem) {
     using C = StateCfg<BF, K, V, CS>;
     using L = SubLayout<BF, K, CS>;
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, D = C::D, NL = C::NL;
     constexpr int CT = C::CT, VT = C::VT, NT = C::NT;
-    extern __shared__ __align__(1024) char smem[];
+    const void *__restrict__ vp = pa.v;
+    void *__restrict__ op = pa.o;
+    const int o_bf16 = pa.o_bf16;
+    const int32_t H = pa.H, N = pa.N;
+    const int64_t *__restrict__ seq_tok = pa.seq_tok;
+    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    const char *__restrict__ frags = pa.frags;
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
-    // blockIdx -> (sequence * H + head, column tile). Workgroups are dealt to the 8 XCDs round-robin
+    // bid -> (sequence * H + head, column tile). Workgroups are dealt to the 8 XCDs round-robin
     // by index; the NT tiles of one head share an XCD (blocks 8 apart), so the workspace blocks
     // every tile of that head reads come from one L2.
-    const int xcd = blockIdx.x & 7, slot8 = blockIdx.x >> 3;
+    const int xcd = bid & 7, slot8 = bid >> 3;
     const int head = (slot8 / NT) * 8 + xcd, tile = slot8 % NT;
     if (head >= N * H) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c0 = chunk_off[n], nu = (chunk_off[n + 1] - c0) * CS;  // sub-tile steps
-    const int64_t s0 = seq_tok[n], s1 = seq_tok[n + 1];
+    const int c0n = chunk_off[n], c1n = chunk_off[n + 1];
+    const int c0 = c0n > pa.g0 ? c0n : pa.g0, c1 = c1n < pa.g1 ? c1n : pa.g1;  // chunks in the range
+    const int nu = c1 > c0 ? (c1 - c0) * CS : 0;                              // sub-tile steps
+    const bool empty = c0n == c1n;
+    if (nu == 0 && !(empty && pa.first)) return;  // nothing of this sequence here (uniform)
+    const float *__restrict__ S0 = (empty || c0 == c0n) ? pa.S0 : pa.Scarry;
+    float *__restrict__ Sfin = (empty || c1 == c1n) ? pa.Sfin : pa.Scarry;
+    const int64_t s0 = seq_tok[n] + (int64_t)(c0 - c0n) * (CS * SUB), s1 = seq_tok[n + 1];
 
     // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
-    // (done by the loader wavefronts one step later: obuf[u & 1] is complete at B_{u+1} and next
-    // overwritten after B_{u+2})
+    // (done by the loader wavefronts between B_{u+2} and B_{u+3}: the compute wavefronts stage
+    // them after B_{u+1} and next overwrite obuf[u & 1] after B_{u+3})
     auto store_o = [&](int u, int t0, int nthreads) {
         const int64_t tok0 = s0 + (int64_t)u * SUB;
         const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
@@ -1047,9 +1137,11 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
                     wait_copies();              // sub-tile u+1 (or 0): this loader's only copy in flight
                 lds_done_barrier();             // B_u (the o rows read before it are done)
                 if ((u % NL) == k && u + NL < nu) issue(u + NL);
-                if (u > 0) store_o(u - 1, lt, NL * 64);
+                if (u > 1) store_o(u - 2, lt, NL * 64);
             }
             lds_done_barrier();                 // B_nu
+            if (nu > 1) store_o(nu - 2, lt, NL * 64);
+            lds_done_barrier();                 // B_{nu+1}
             store_o(nu - 1, lt, NL * 64);
         }
         return;
@@ -1097,87 +1189,141 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     };
     pack_state();
 
-    // operands of a step's first product chain (T tiles, the v tile, -Wk); read one step ahead
+    // operands read one step ahead, during the previous step's state update (a wavefront reads
+    // LDS at about 23 bytes per clock, so a step's 22 KiB of operands must stream in while
+    // products run): T tiles, the v tile (raw row words, assembled into fragments when used),
+    // -Wk, Q*Gamma (hi, lo). Part p of read_ahead covers a quarter of them.
     Frag4<BF> tt[CS], vf[CT];
-    Frag8<BF> wk[KS];
-    auto read_first = [&](const char *sl) {
+    Frag8<BF> wk[KS], qh[KS], ql[KS];
+    uint32_t vraw[4 * CT];
+    auto read_ahead = [&](const char *sl, int part) {
+        if (part == 0) {
 #pragma unroll
-        for (int I = 0; I < CS; ++I) tt[I] = ld_frag4<BF>(sl + L::TT + (I * 64 + lane) * 4 * ES);
-        const char *vt = sl + C::KU * 1024;
-        if constexpr (CT == 2 && BF) {
-            uint32_t x[4];  // columns (lc, lc+1) of tokens 4tg+j
+            for (int s = 0; s < KS; ++s) qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
+        } else if (part == 1) {
+            if constexpr (BF) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint32_t *>(vt + ((4 * tg + j) * VT + lc) * 2);
-            vf[0].p[0] = (x[0] & 0xffffu) | (x[1] << 16);
-            vf[0].p[1] = (x[2] & 0xffffu) | (x[3] << 16);
-            vf[CT - 1].p[0] = (x[0] >> 16) | (x[1] & 0xffff0000u);
-            vf[CT - 1].p[1] = (x[2] >> 16) | (x[3] & 0xffff0000u);
-        } else if constexpr (CT == 2) {
-            float2 x[4];
+                for (int s = 0; s < KS; ++s) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
+            }
+        } else if (part == 2) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float2 *>(vt + ((4 * tg + j) * VT + lc) * 4);
-            set4(vf[0], x[0].x, x[1].x, x[2].x, x[3].x);
-            set4(vf[CT - 1], x[0].y, x[1].y, x[2].y, x[3].y);
+            for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
         } else {
-            float x[4];
+#pragma unroll
+            for (int I = 0; I < CS; ++I) tt[I] = ld_frag4<BF>(sl + L::TT + (I * 64 + lane) * 4 * ES);
+            const char *vt = sl + C::KU * 1024;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int off = ((4 * tg + j) * VT + lc) * ES;
-                if constexpr (BF) x[j] = bf2f(*reinterpret_cast<const uint16_t *>(vt + off));
-                else x[j] = *reinterpret_cast<const float *>(vt + off);
+                const char *row = vt + ((4 * tg + j) * VT + lc) * ES;  // token 4tg+j, columns lc ..
+                if constexpr (BF && CT == 2) vraw[j] = *reinterpret_cast<const uint32_t *>(row);
+                else if constexpr (BF) vraw[j] = *reinterpret_cast<const uint16_t *>(row);
+                else if constexpr (CT == 2) {
+                    const uint2 x = *reinterpret_cast<const uint2 *>(row);
+                    vraw[2 * j] = x.x;
+                    vraw[2 * j + 1] = x.y;
+                } else vraw[j] = *reinterpret_cast<const uint32_t *>(row);
             }
-            set4(vf[0], x[0], x[1], x[2], x[3]);
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) wk[s] = ld_frag8<BF>(sl + L::WK + (s * 64 + lane) * 8 * ES);
+    };
+    auto make_vf = [&]() {
+        if constexpr (BF && CT == 2) {  // word j = columns (lc, lc+1) of token 4tg+j
+            vf[0].p[0] = (vraw[0] & 0xffffu) | (vraw[1] << 16);
+            vf[0].p[1] = (vraw[2] & 0xffffu) | (vraw[3] << 16);
+            vf[CT - 1].p[0] = (vraw[0] >> 16) | (vraw[1] & 0xffff0000u);
+            vf[CT - 1].p[1] = (vraw[2] >> 16) | (vraw[3] & 0xffff0000u);
+        } else if constexpr (BF) {
+            vf[0].p[0] = vraw[0] | (vraw[1] << 16);
+            vf[0].p[1] = vraw[2] | (vraw[3] << 16);
+        } else if constexpr (CT == 2) {
+            set4(vf[0], __uint_as_float(vraw[0]), __uint_as_float(vraw[2]), __uint_as_float(vraw[4]),
+                 __uint_as_float(vraw[6]));
+            set4(vf[CT - 1], __uint_as_float(vraw[1]), __uint_as_float(vraw[3]), __uint_as_float(vraw[5]),
+                 __uint_as_float(vraw[7]));
+        } else {
+            set4(vf[0], __uint_as_float(vraw[0]), __uint_as_float(vraw[1]), __uint_as_float(vraw[2]),
+                 __uint_as_float(vraw[3]));
+        }
     };
 
-    // 64-token chunks: v fragments and corrected values [Wh | Wl] of the chunk's earlier sub-tiles
+    // 64-token chunks: v fragments and corrected values of the chunk's earlier sub-tiles
+    // (bf16: [Wh | Wh] and [Wl | Wl]; fp32: [W | 0] in whist)
     Frag4<BF> vhist[CS][CT];
-    Frag8<BF> whist[CS][CT];
-    for (int u = 0; u < nu; ++u) {
-        const int R = CS == 1 ? 0 : (u & (CS - 1));
-        lds_done_barrier();  // B_u
-        const char *sl = smem + (u % D) * C::SLOT;
-        if (u == 0) read_first(sl);
-        // ---- the step's other LDS operands, issued before any product so they land while the
-        // first chain runs (LDS read throughput per wavefront bounds a step)
-        Frag8<BF> kp2[KT / 2];
-#pragma unroll
-        for (int p2 = 0; p2 < KT / 2; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
-        // Gamma_C (first sub-tile of a chunk): lane (tg, cl) reads state rows 16(cl/2) + 4tg +
-        // 2(cl%2) + {0, 1}; row rt, entry i of lane group tg then comes from lane 2rt + i/2 of the
-        // same row (DPP row broadcast)
-        float2 g2 = make_float2(1.f, 1.f);
-        if (R == 0) g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
-        Frag8<BF> qh[KS], ql[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
-            if constexpr (BF) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
+    Frag8<BF> whist[CS][CT], wlist[CS][CT];
+    // o rows of a step: computed in step u, staged to obuf[u & 1] right after barrier B_{u+1},
+    // stored to global memory by the loader wavefronts after B_{u+2}
+    f32x4 O[CT];
+    auto write_o = [&](int uu) {
+        if constexpr (!BF) {
+            if constexpr (CT == 2) mfma_fence(O[0], O[CT - 1]);
+            else mfma_fence(O[0]);
         }
-        Frag4<BF> ph[CS], pl[CS];
+        float *ob = obuf + (uu & 1) * 16 * C::OPITCH;
 #pragma unroll
-        for (int I = 0; I < CS; ++I) {
-            if (I > R) continue;
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (CT == 2)
+                *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + lc) = make_float2(O[0][i], O[CT - 1][i]);
+            else ob[(4 * tg + i) * C::OPITCH + lc] = O[0][i];
+        }
+    };
+    // pack state rows 32s .. 32s+31 (tiles 2s, 2s+1) of every column tile into the bf16 operand
+    auto pack_pair = [&](int s) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
             if constexpr (BF) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(sl + L::PP + (I * 64 + lane) * 16);
-                ph[I].p[0] = x.x; ph[I].p[1] = x.y; pl[I].p[0] = x.z; pl[I].p[1] = x.w;
+                sb[ct][s].p[0] = pack_bf16(S[ct][2 * s][0], S[ct][2 * s][1]);
+                sb[ct][s].p[1] = pack_bf16(S[ct][2 * s][2], S[ct][2 * s][3]);
+                sb[ct][s].p[2] = pack_bf16(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
+                sb[ct][s].p[3] = pack_bf16(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
             } else {
-                ph[I] = ld_frag4<BF>(sl + L::PP + (I * 64 + lane) * 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sb[ct][s].f[i] = S[ct][2 * s][i];
+                    sb[ct][s].f[4 + i] = S[ct][2 * s + 1][i];
+                }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // keeps the packing of a pair where it is written (the compiler would otherwise sink it to
+    // the end of the step, after the last product)
+    auto pin_pair = [&](int s) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            if constexpr (BF)
+                asm volatile("" : "+v"(sb[ct][s].p[0]), "+v"(sb[ct][s].p[1]), "+v"(sb[ct][s].p[2]), "+v"(sb[ct][s].p[3]));
+        }
+    };
+    // Padding between the products of a pair and its readers (fp32 path). The bf16 path needs
+    // none of its own: its 16x16x32 products are read only after several further products have
+    // been issued (each takes the matrix core 16 cycles), far beyond their latency, and the
+    // compiler pads these products itself.
+    auto fence_pair = [&](int s) {
+        if constexpr (BF) return;
+        if constexpr (CT == 2) mfma_fence(S[0][2 * s], S[0][2 * s + 1], S[1][2 * s], S[1][2 * s + 1]);
+        else mfma_fence(S[0][2 * s], S[0][2 * s + 1]);
+    };
+    if (nu > 0) {
+        wg_barrier();  // B_0
+#pragma unroll
+        for (int part = 0; part < 4; ++part) read_ahead(smem, part);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) O[ct] = zero4();
+    for (int u = 0; u < nu; ++u) {
+        const int R = CS == 1 ? 0 : (u & (CS - 1));
+        const bool repack = R == CS - 1;  // the state operand is renewed after a chunk's last sub-tile
+        const char *sl = smem + (u % D) * C::SLOT;
+        make_vf();
 #pragma unroll
         for (int I = 0; I < CS; ++I)
             if (I == R)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) vhist[I][ct] = vf[ct];
 
-        // ---- W = sum_{I<=R} T_RI V_I + (-Wk) S: one accumulation chain per tile, every product
+        // ---- phase A: W = sum_{I<=R} T_RI V_I + (-Wk) S (operands read one step ahead), while
+        // this step's other operands are read. One accumulation chain per tile, every product
         // 32 deep (T V pairs stacked as [T_RI | T_RI'] x [V_I | V_I']; a chain that mixes
-        // 16-deep and 32-deep products read a stale accumulator on gfx950)
-        f32x4 W[CT], O[CT];
+        // 16-deep and 32-deep products read a stale accumulator on gfx950).
+        f32x4 W[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             W[ct] = zero4();
@@ -1192,118 +1338,150 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
 #pragma unroll
             for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
         }
-        if constexpr (CT == 2) mfma_fence(W[0], W[CT - 1]);
-        else mfma_fence(W[0]);
-        if constexpr (BF) {
-            // W = Wh + Wl; one 32-deep product stacks the two halves: slots 0..3 carry
-            // (token 4tg+j, hi), slots 4..7 (token 4tg+j, lo), for A and B alike.
-            Frag8<true> whl[CT];  // [Wh | Wl]
+        // the previous step's o rows, staged ahead of this step's reads (which the step consumes,
+        // so the rows are in LDS by the next barrier). At u = 0 this stages zeros into obuf[1],
+        // which step 1 overwrites before any loader reads it.
+        write_o(u - 1);
+        constexpr int NKP = BF ? KT : KT / 2;  // bf16: [hi | lo] of tile rt; fp32: tiles 2p, 2p+1
+        Frag8<BF> kp2[NKP];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
+        for (int p2 = 0; p2 < NKP; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
+        // Gamma_C (first sub-tile of a chunk): lane (tg, cl) reads state rows 16(cl/2) + 4tg +
+        // 2(cl%2) + {0, 1}; row rt, entry i of lane group tg then comes from lane 2rt + i/2 of the
+        // same row (DPP row broadcast)
+        float2 g2 = make_float2(1.f, 1.f);
+        if (R == 0) g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
+        Frag8<true> pp[CS];  // bf16: [Ph | Pl] of tile I
+        Frag4<BF> ph[CS];    // fp32: P tile I
+#pragma unroll
+        for (int I = 0; I < CS; ++I) {
+            if (I > R) continue;
+            if constexpr (BF) pp[I] = ld_frag8<true>(sl + L::PP + (I * 64 + lane) * 16);
+            else ph[I] = ld_frag4<BF>(sl + L::PP + (I * 64 + lane) * 16);
+        }
+        // one product (per tile), then two reads, while the chain runs
+#pragma unroll
+        for (int i = 0; i < (CS + 1) / 2 + KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, CT, 0);  // matrix products
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- phase B: O = (Q*Gamma) S (hi and lo parts), independent of W: it keeps the matrix
+        // cores busy while W is split
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            O[ct] = zero4();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
+                if constexpr (BF) O[ct] = mma32(O[ct], ql[s], sb[ct][s]);
+            }
+        }
+        if constexpr (!BF) {
+            if constexpr (CT == 2) mfma_fence(W[0], W[CT - 1]);
+            else mfma_fence(W[0]);
+        }
+        // W = Wh + Wl. The bf16 operands of the state update ([Kh | Kl] per tile) and of the
+        // output ([Ph | Pl]) carry hi and lo parts of the same tokens in slots 0..3 and 4..7;
+        // multiplied by [Wh | Wh] and then by [Wl | Wl], the two products sum all four cross
+        // terms. fp32: W kept whole ([W | 0]).
+        Frag8<BF> whh[CT], wll[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            if constexpr (BF) {
                 uint32_t wh0, wl0, wh1, wl1;
                 split_bf16(W[ct][0], W[ct][1], wh0, wl0);
                 split_bf16(W[ct][2], W[ct][3], wh1, wl1);
-                whl[ct].p[0] = wh0; whl[ct].p[1] = wh1; whl[ct].p[2] = wl0; whl[ct].p[3] = wl1;
+                whh[ct].p[0] = wh0; whh[ct].p[1] = wh1; whh[ct].p[2] = wh0; whh[ct].p[3] = wh1;
+                wll[ct].p[0] = wl0; wll[ct].p[1] = wl1; wll[ct].p[2] = wl0; wll[ct].p[3] = wl1;
+            } else {
+                Frag4<false> wf;
+                set4(wf, W[ct][0], W[ct][1], W[ct][2], W[ct][3]);
+                whh[ct] = cat4(wf, zero_frag4<false>());
             }
+        }
 #pragma unroll
-            for (int I = 0; I < CS; ++I)
-                if (I == R)
+        for (int I = 0; I < CS; ++I)
+            if (I == R)
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) whist[I][ct] = whl[ct];
-            // S <- diag(Gamma_C) S (at a chunk's first sub-tile) + [Kp | Kp]^T [Wh | Wl]
-            // (first: the next step waits on it)
+                for (int ct = 0; ct < CT; ++ct) {
+                    whist[I][ct] = whh[ct];
+                    if constexpr (BF) wlist[I][ct] = wll[ct];
+                }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- phase C: S <- diag(Gamma_C) S (a chunk's first sub-tile) + Kp^T W, one pair of state
+        // row tiles at a time; the bf16 operand of a pair is renewed while the next pair's
+        // products run, and the next step's first operands are read (slot of sub-tile u+1,
+        // certified at B_u; after the last step the reads are of a stale slot and unused)
+        const char *sl_next = smem + ((u + 1) % D) * C::SLOT;
 #pragma unroll
-            for (int rt = 0; rt < KT; ++rt) {
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int part = 0; part < 4; ++part)
+                if (part * KS / 4 == s) read_ahead(sl_next, part);
+#pragma unroll
+            for (int rt = 2 * s; rt < 2 * s + 2; ++rt) {
                 float gm[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) gm[i] = row_bcast(i & 1 ? g2.y : g2.x, 2 * rt + (i >> 1));
-                const Frag8<true> &kq = kp2[rt >> 1];
-                Frag8<true> kk;
-                kk.p[0] = kq.p[2 * (rt & 1)]; kk.p[1] = kq.p[2 * (rt & 1) + 1];
-                kk.p[2] = kk.p[0]; kk.p[3] = kk.p[1];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
-                    S[ct][rt] = mma32(S[ct][rt], kk, whl[ct]);
+                    if (CS == 1 || R == 0) {
+                        S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
+                    }
+                    if constexpr (BF) {
+                        S[ct][rt] = mma32(S[ct][rt], kp2[rt], whh[ct]);
+                        S[ct][rt] = mma32(S[ct][rt], kp2[rt], wll[ct]);
+                    } else {
+                        const Frag8<false> &kq = kp2[rt >> 1];
+                        Frag4<false> kf, wf;
+                        set4(kf, kq.f[4 * (rt & 1)], kq.f[4 * (rt & 1) + 1], kq.f[4 * (rt & 1) + 2], kq.f[4 * (rt & 1) + 3]);
+                        set4(wf, whh[ct].f[0], whh[ct].f[1], whh[ct].f[2], whh[ct].f[3]);
+                        S[ct][rt] = mma16(S[ct][rt], kf, wf);
+                    }
                 }
             }
-            // O = sum_{I<=R} ([Ph | Ph] + [Pl | 0]) x [Wh | Wl]_I + (Q*Gamma)_hi S + (Q*Gamma)_lo S
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                O[ct] = zero4();
-#pragma unroll
-                for (int I = 0; I < CS; ++I) {
-                    if (I > R) continue;
-                    Frag8<true> pp, pz;
-                    pp.p[0] = ph[I].p[0]; pp.p[1] = ph[I].p[1]; pp.p[2] = ph[I].p[0]; pp.p[3] = ph[I].p[1];
-                    pz.p[0] = pl[I].p[0]; pz.p[1] = pl[I].p[1]; pz.p[2] = 0u; pz.p[3] = 0u;
-                    O[ct] = mma32(O[ct], pp, whist[I][ct]);
-                    O[ct] = mma32(O[ct], pz, whist[I][ct]);
-                }
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
-                    O[ct] = mma32(O[ct], ql[s], sb[ct][s]);
-                }
+            if (s > 0 && repack) {
+                fence_pair(s - 1);
+                pack_pair(s - 1);
+                pin_pair(s - 1);
             }
-        } else {
-            // fp32: W kept whole (slots 0..3 of the history; 4..7 zero)
-            Frag4<false> wf[CT];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- phase D: O += sum_{I<=R} P_RI W_I; the last pair of the state operand
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                set4(wf[ct], W[ct][0], W[ct][1], W[ct][2], W[ct][3]);
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int I = 0; I < CS; ++I)
-                    if (I == R) whist[I][ct] = cat4(wf[ct], zero_frag4<false>());
-            }
-#pragma unroll
-            for (int rt = 0; rt < KT; ++rt) {
-                float gm[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gm[i] = row_bcast(i & 1 ? g2.y : g2.x, 2 * rt + (i >> 1));
-                const Frag8<false> &kq = kp2[rt >> 1];
-                Frag4<false> kf;
-                set4(kf, kq.f[4 * (rt & 1)], kq.f[4 * (rt & 1) + 1], kq.f[4 * (rt & 1) + 2], kq.f[4 * (rt & 1) + 3]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
-                    S[ct][rt] = mma16(S[ct][rt], kf, wf[ct]);
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                O[ct] = zero4();
-#pragma unroll
-                for (int I = 0; I < CS; ++I) {
-                    if (I > R) continue;
+            for (int I = 0; I < CS; ++I) {
+                if (I > R) continue;
+                if constexpr (BF) {
+                    O[ct] = mma32(O[ct], pp[I], whist[I][ct]);
+                    O[ct] = mma32(O[ct], pp[I], wlist[I][ct]);
+                } else {
                     Frag4<false> wi;
                     set4(wi, whist[I][ct].f[0], whist[I][ct].f[1], whist[I][ct].f[2], whist[I][ct].f[3]);
                     O[ct] = mma16(O[ct], ph[I], wi);
                 }
-#pragma unroll
-                for (int s = 0; s < KS; ++s) O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
             }
+        if (repack) {
+            fence_pair(KS - 1);
+            pack_pair(KS - 1);
+            pin_pair(KS - 1);
         }
-        // next step's first operands (certified at B_u), read while the products run
         __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < nu) read_first(smem + ((u + 1) % D) * C::SLOT);
-        __builtin_amdgcn_sched_barrier(0);
-        // the state products were issued first: packing the next operand overlaps the output products
-        mfma_fence_all(S);
-        if (R == CS - 1) pack_state();  // operand for the next chunk
-        if constexpr (CT == 2) mfma_fence(O[0], O[CT - 1]);
-        else mfma_fence(O[0]);
-        {
-            float *ob = obuf + (u & 1) * 16 * C::OPITCH;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (CT == 2)
-                    *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + lc) = make_float2(O[0][i], O[CT - 1][i]);
-                else ob[(4 * tg + i) * C::OPITCH + lc] = O[0][i];
-            }
-        }
+        // B_{u+1}. No LDS wait is needed before it: every read of the slot it frees (sub-tile u)
+        // was consumed by an instruction of this step, and the o rows staged in this step were
+        // followed by reads the step consumed (a wavefront's LDS operations complete in order).
+        // Only the next step's first operands may still be in flight.
+        wg_barrier();
     }
-    if (nu > 0) lds_done_barrier();  // B_nu: the loader wavefronts store the last o rows
+    if (nu > 0) {
+        write_o(nu - 1);
+        lds_done_barrier();       // B_{nu+1}: the loader wavefronts store the last o rows
+    }
     if (Sfin) {
 #pragma unroll
         for (int rt = 0; rt < KT; ++rt)
@@ -1316,10 +1494,45 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_p
     }
 }
 
+template <bool BF, int K, int V, int CS>
+__global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_pass(StateParams pa) {
+    extern __shared__ __align__(1024) char smem[];
+    state_body<BF, K, V, CS>(pa, blockIdx.x, smem);
+}
+
+// Prep wavefronts per workgroup of the combined kernel below (each owns PrepLds::WAVE bytes of
+// the state pass's LDS).
+template <bool BF, int K, int V>
+constexpr int combined_prep_waves() {
+    using C = StateCfg<BF, K, V, 1>;
+    constexpr int byl = C::LDS / PrepLds<BF, K>::WAVE, byw = C::THREADS / 64;
+    return byl < byw ? byl : byw;
+}
+
+// One launch that runs the state pass over one chunk range (workgroups 0 .. nstate-1, dispatched
+// first) and the 16-token prep of the next range (the remaining workgroups, on the CUs the state
+// pass leaves free). The state pass of H heads occupies H workgroups, one per CU; the prep of
+// the following chunks then runs beside it instead of after it.
+template <bool BF, int K, int V>
+__global__ __launch_bounds__((StateCfg<BF, K, V, 1>::THREADS)) void kda_state_prep(StateParams sa, PrepParams pa,
+                                                                                   int32_t nstate) {
+    extern __shared__ __align__(1024) char smem[];
+    if ((int)blockIdx.x < nstate) {
+        state_body<BF, K, V, 1>(sa, blockIdx.x, smem);
+        return;
+    }
+    constexpr int PW = combined_prep_waves<BF, K, V>();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave >= PW) return;
+    prep16_item<BF, K>(pa, (int64_t)(blockIdx.x - nstate) * PW + wave, smem + wave * PrepLds<BF, K>::WAVE);
+}
+
 }  // namespace kda
 
 // ------------------------------------------------------------------ host side
 #include "kda_launch.hpp"
+
+#include <stdlib.h>
 
 namespace kda {
 namespace {
@@ -1347,13 +1560,17 @@ struct WsPtrs {
     int64_t *seq_tok;
     int32_t *chunk_off;
     char *frags;
+    float *carry;  // state between chunk ranges (pipelined calls only)
 };
 WsPtrs ws_ptrs(const PrefillArgs &a) {
     WsPtrs w;
-    w.seq_tok = reinterpret_cast<int64_t *>(a.workspace);
-    w.chunk_off = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(a.workspace) +
-                                              align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
-    w.frags = reinterpret_cast<char *>(a.workspace) + table_bytes(a.num_seqs);
+    char *base = reinterpret_cast<char *>(a.workspace);
+    w.seq_tok = reinterpret_cast<int64_t *>(base);
+    w.chunk_off = reinterpret_cast<int32_t *>(base + align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
+    w.frags = base + table_bytes(a.num_seqs);
+    w.carry = reinterpret_cast<float *>(
+        base + table_bytes(a.num_seqs) +
+        align_up((size_t)a.n_chunks_max * (size_t)a.H * chunk_bytes_rt(a.io_bf16, a.K, a.chunk)));
     return w;
 }
 
@@ -1366,41 +1583,122 @@ hipError_t allow_lds(const void *kernel, bool &done, int bytes) {
     return e;
 }
 
+constexpr int32_t ALL_CHUNKS = 0x7fffffff;
+
+PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1) {
+    PrepParams p;
+    p.q = a.q; p.k = a.k; p.g = a.g; p.beta = a.beta;
+    p.H = a.H; p.N = a.num_seqs;
+    p.seq_tok = w.seq_tok; p.chunk_off = w.chunk_off; p.frags = w.frags;
+    p.g0 = g0; p.g1 = g1;
+    return p;
+}
+
+StateParams state_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first) {
+    StateParams p;
+    p.v = a.v; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
+    p.H = a.H; p.N = a.num_seqs;
+    p.seq_tok = w.seq_tok; p.chunk_off = w.chunk_off; p.frags = w.frags;
+    p.g0 = g0; p.g1 = g1;
+    p.Scarry = w.carry;
+    p.first = first ? 1 : 0;
+    return p;
+}
+
+hipError_t launch_table(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
+                       (int32_t)a.chunk, w.seq_tok, w.chunk_off);
+    return hipGetLastError();
+}
+
+// Prep of the chunk range [g0, g1) (g1 - g0 <= n_chunks_max).
+template <bool BF, int K>
+hipError_t prep_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, hipStream_t st) {
+    const int64_t n = (int64_t)(g1 < a.n_chunks_max ? g1 : a.n_chunks_max) - g0;
+    if (n <= 0) return hipSuccess;
+    const int64_t items = n * a.H;
+    const PrepParams pp = prep_params(a, w, g0, g1);
+    if (a.chunk == 64) {
+        static bool lds_set = false;
+        constexpr int LDS = Prep64Lds<BF, K>::BYTES;
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K>), lds_set, LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kda_chunk_prep64<BF, K>), dim3((unsigned)items), dim3(256), LDS, st, pp);
+    } else {
+        static bool lds_set = false;
+        constexpr int LDS = 4 * PrepLds<BF, K>::WAVE;
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep<BF, K>), lds_set, LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3((unsigned)((items + 3) / 4)), dim3(256), LDS, st, pp);
+    }
+    return hipGetLastError();
+}
+
 template <bool BF, int K>
 hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
-    hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
-                       (int32_t)a.chunk, w.seq_tok, w.chunk_off);
-    if (a.n_chunks_max > 0) {
-        const int64_t items = a.n_chunks_max * a.H;
-        if (a.chunk == 64) {
-            static bool lds_set = false;
-            constexpr int LDS = Prep64Lds<BF, K>::BYTES;
-            hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K>), lds_set, LDS);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((kda_chunk_prep64<BF, K>), dim3((unsigned)items), dim3(256), LDS, st, a.q, a.k, a.g,
-                               a.beta, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
-        } else {
-            const unsigned grid = (unsigned)((items + 3) / 4);
-            const size_t lds = 4 * (size_t)PrepLds<BF, K>::WAVE;
-            hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3(grid), dim3(256), lds, st, a.q, a.k, a.g, a.beta, a.H,
-                               a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
-        }
-    }
+    hipError_t e = launch_table(a, w, st);
+    if (e != hipSuccess) return e;
+    return prep_range<BF, K>(a, w, 0, ALL_CHUNKS, st);
+}
+
+template <bool BF, int K, int V, int CS>
+unsigned state_grid(const PrefillArgs &a) {
+    return (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * StateCfg<BF, K, V, CS>::NT);
+}
+
+template <bool BF, int K, int V, int CS>
+hipError_t state_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
+    using C = StateCfg<BF, K, V, CS>;
+    static bool lds_set = false;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS), C::LDS,
+                       st, state_params(a, w, g0, g1, first));
     return hipGetLastError();
 }
 
 template <bool BF, int K, int V, int CS>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
-    using C = StateCfg<BF, K, V, CS>;
+    return state_range<BF, K, V, CS>(a, ws_ptrs(a), 0, ALL_CHUNKS, true, st);
+}
+
+// Pipelined forward over nseg chunk ranges (16-token chunks): prep(0); then per range s the
+// combined kernel {state(s), prep(s+1)}; then state(last).
+template <bool BF, int K, int V>
+hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
+    using C = StateCfg<BF, K, V, 1>;
+    constexpr int PW = combined_prep_waves<BF, K, V>();
+    static_assert(PW >= 1, "no room for prep wavefronts");
     const WsPtrs w = ws_ptrs(a);
-    static bool lds_set = false;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>), lds_set, C::LDS);
+    const int64_t per = (a.n_chunks_max + nseg - 1) / nseg;
+    auto g = [&](int s) { return (int32_t)(per * s < a.n_chunks_max ? per * s : a.n_chunks_max); };
+    hipError_t e = launch_table(a, w, st);
+    if (e == hipSuccess) e = prep_range<BF, K>(a, w, g(0), g(1), st);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * C::NT);
-    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(grid), dim3(C::THREADS), C::LDS, st, a.v, a.S0, a.o,
-                       (int)a.o_bf16, a.S_final, a.H, a.num_seqs, w.seq_tok, w.chunk_off, w.frags);
-    return hipGetLastError();
+    static bool lds_set = false;
+    e = allow_lds(reinterpret_cast<const void *>(&kda_state_prep<BF, K, V>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    const unsigned nstate = state_grid<BF, K, V, 1>(a);
+    for (int s = 0; s + 1 < nseg; ++s) {
+        const int64_t items = (int64_t)(g(s + 2) - g(s + 1)) * a.H;
+        const unsigned grid = nstate + (unsigned)((items + PW - 1) / PW);
+        hipLaunchKernelGGL((kda_state_prep<BF, K, V>), dim3(grid), dim3(C::THREADS), C::LDS, st,
+                           state_params(a, w, g(s), g(s + 1), s == 0), prep_params(a, w, g(s + 1), g(s + 2)),
+                           (int32_t)nstate);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return state_range<BF, K, V, 1>(a, w, g(nseg - 1), ALL_CHUNKS, nseg == 1, st);
+}
+
+template <bool BF, int K>
+hipError_t fwd_pipelined_v(const PrefillArgs &a, int nseg, hipStream_t st) {
+    switch (a.V) {
+        case 32: return fwd_pipelined<BF, K, 32>(a, nseg, st);
+        case 64: return fwd_pipelined<BF, K, 64>(a, nseg, st);
+        default: return fwd_pipelined<BF, K, 128>(a, nseg, st);
+    }
 }
 
 template <bool BF, int K, int CS>
@@ -1416,11 +1714,51 @@ hipError_t state_k(const PrefillArgs &a, hipStream_t st) {
     return a.chunk == 64 ? state_v<BF, K, 4>(a, st) : state_v<BF, K, 1>(a, st);
 }
 
+// Pipelining over chunk ranges pays when the state pass leaves most of the 256 CUs free (at
+// 16-token chunks it runs one workgroup per (sequence, head), one per CU) and there are enough
+// chunks to split. The decision depends on sizes only, so the workspace query agrees with it.
+bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk) {
+    return chunk == 16 && (int64_t)num_seqs * H <= 128 && n_chunks_max >= 128;
+}
+
+// Chunk ranges of a pipelined call: 4 (at least 64 chunks each). KDA_PIPELINE_RANGES (1 .. 16)
+// overrides the count; 1 turns pipelining off.
+int pipeline_ranges(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk) {
+    if (!can_pipeline(n_chunks_max, num_seqs, H, chunk)) return 1;
+    const char *e = getenv("KDA_PIPELINE_RANGES");
+    const int env = e ? atoi(e) : 0;
+    if (env >= 1 && env <= 16) return env;
+    const int64_t n = n_chunks_max / 64;
+    return (int)(n < 4 ? n : 4);
+}
+
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t num_seqs, bool io_bf16,
-                               int32_t chunk) {
-    return table_bytes(num_seqs) + (size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk);
+size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                               bool io_bf16, int32_t chunk) {
+    size_t b = table_bytes(num_seqs) + align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk));
+    if (can_pipeline(n_chunks_max, num_seqs, H, chunk)) b += align_up((size_t)num_seqs * H * K * V * sizeof(float));
+    return b;
+}
+
+hipError_t launch_fwd(const PrefillArgs &a, hipStream_t st) {
+    const int nseg = pipeline_ranges(a.n_chunks_max, a.num_seqs, a.H, a.chunk);
+    if (nseg > 1) {
+        if (a.io_bf16) {
+            switch (a.K) {
+                case 32: return fwd_pipelined_v<true, 32>(a, nseg, st);
+                case 64: return fwd_pipelined_v<true, 64>(a, nseg, st);
+                default: return fwd_pipelined_v<true, 128>(a, nseg, st);
+            }
+        }
+        switch (a.K) {
+            case 32: return fwd_pipelined_v<false, 32>(a, nseg, st);
+            case 64: return fwd_pipelined_v<false, 64>(a, nseg, st);
+            default: return fwd_pipelined_v<false, 128>(a, nseg, st);
+        }
+    }
+    hipError_t e = launch_prep(a, st);
+    return e != hipSuccess ? e : launch_state(a, st);
 }
 
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t st) {

@@ -4,6 +4,8 @@ Every case prints its name, seed and shape before touching the GPU. Inputs
 come from the seeded generator; the oracle sees exactly the values the GPU
 received (bf16 or fp32), widened to fp64.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -225,3 +227,67 @@ def test_k3_varlen_16_sampled_heads(chunk):
     _announce("varlen_16", chunk=chunk, seed=w.seed)
     inp = synth.workload_prefill_inputs(w, device=DEV)
     _check(inp, heads=(0, 41, 95), chunk=chunk)
+
+
+class _Ranges:
+    """Sets KDA_PIPELINE_RANGES (read by the library on every call) for the duration of a block."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        self.old = os.environ.get("KDA_PIPELINE_RANGES")
+        os.environ["KDA_PIPELINE_RANGES"] = str(self.n)
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            del os.environ["KDA_PIPELINE_RANGES"]
+        else:
+            os.environ["KDA_PIPELINE_RANGES"] = self.old
+
+
+PIPE_CASES = {
+    # name: (B, T or lengths, H, K, V, io)
+    "single_ragged": (1, 2500, 4, 128, 128, "bf16"),
+    "varlen_range_edges": (1, [0, 700, 1, 1200, 0, 617, 33], 8, 64, 64, "bf16"),
+    "batched_fp32": (2, 1100, 3, 32, 128, "fp32"),
+}
+
+
+@pytest.mark.parametrize("name", list(PIPE_CASES))
+def test_pipelined_ranges_are_bit_identical(name):
+    """Where the state pass leaves CUs free, kda_chunk_fwd splits the chunks into ranges and runs
+    the prep of range s+1 beside the state pass of range s, carrying the fp32 state between
+    ranges. Per chunk the arithmetic is unchanged, so o and S_final are bitwise those of one prep
+    and one state pass, for any range count: ranges that cut sequences, hold no chunk of a
+    sequence, or start at an empty one."""
+    B, TL, H, K, V, io = PIPE_CASES[name]
+    cu = None
+    if isinstance(TL, list):
+        cu = synth.cu_from_lengths(TL)
+        T = cu[-1]
+    else:
+        T = TL
+    _announce("pipelined_ranges", case=name, B=B, T=T, H=H, K=K, V=V, io=io, seed=22)
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=22, device=DEV, cu_seqlens=cu, with_S0=True)
+    with _Ranges(1):
+        o1, S1 = _run(inp)
+    for n in (2, 3, 4, 7, 16):
+        with _Ranges(n):
+            on, Sn = _run(inp)
+        assert torch.equal(o1, on) and torch.equal(S1, Sn), n
+    with _Ranges(4):  # without S_final the carry still flows between ranges
+        o4, _ = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
+                          cu_seqlens=inp["cu_seqlens"], output_final_state=False)
+        torch.cuda.synchronize()
+    assert torch.equal(o1, o4)
+
+
+def test_pipelined_varlen_against_oracle():
+    """The default pipelined call on packed sequences of mixed lengths (with an empty one and
+    range boundaries inside sequences) against the oracle."""
+    lengths = [900, 0, 1500, 31, 1100]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("pipelined_varlen", lengths=lengths, H=16, seed=23)
+    inp = synth.prefill_inputs(1, cu[-1], 16, 128, 128, "bf16", seed=23, device=DEV, cu_seqlens=cu, with_S0=True)
+    _check(inp, heads=(0, 7, 15))

@@ -1,7 +1,7 @@
 """Million-token prefill (B=1, T=1,048,576, H=96, K=V=128, bf16, chunk 16) against the oracle.
 
 One kda_chunk_fwd call over the whole sequence (about 129 GB of q/k/v/g/o plus a
-113 GB workspace in HBM). The oracle cannot redo all 96 heads end to end in a
+142 GB workspace in HBM). The oracle cannot redo all 96 heads end to end in a
 test's time, so the check has two parts:
 
 * four seeded heads end to end: the fp64 recurrence is streamed over blocks of
@@ -48,7 +48,7 @@ def test_k3_prefill_1m():
     free, total = torch.cuda.mem_get_info()
     _say("  device memory: %.1f GB free of %.1f GB" % (free / 1e9, total / 1e9))
     need = 4 * w.T * w.H * w.K * 2 + w.T * w.H * 2 + w.T * w.H * w.V * 2
-    need += w.T // 16 * w.H * 18 * 1024
+    need += w.T // 16 * w.H * 22 * 1024
     if free < need + (8 << 30):
         pytest.skip("needs %.0f GB of free device memory, %.0f GB free" % (need / 1e9, free / 1e9))
     inp = synth.workload_prefill_inputs(w, device=DEV, block_tokens=BLOCK)
