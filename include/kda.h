@@ -119,7 +119,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
  * separately. kda_chunk_fwd returns bitwise the results of kda_chunk_prep
  * followed by kda_chunk_state on one stream; where the state pass leaves most
- * of the GPU idle (16-token chunks, num_seqs * H <= 128, at least 128 chunks)
+ * of the GPU idle (16-token chunks, num_seqs * H <= 64, at least 128 chunks)
  * it splits the chunks into ranges and runs the prep of each range beside the
  * state pass of the previous one. The environment variable
  * KDA_PIPELINE_RANGES (1 .. 16, read at each call) sets the number of ranges;

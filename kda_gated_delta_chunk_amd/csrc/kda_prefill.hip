@@ -973,12 +973,13 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never has
 // more than one in flight; a sub-tile is copied NL steps before use.
 template <bool BF, int K, int V, int CS>
-#ifndef KDA_STATE_CT
-#define KDA_STATE_CT (CS == 1 ? 2 : 1)
-#endif
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
-    static constexpr int CT = KDA_STATE_CT;
+    // One 16-column tile per compute wavefront, four compute wavefronts per workgroup: at V = 128 a
+    // head takes two workgroups (on one XCD). Measured at 4096 tokens, 96 heads: 224 us, against
+    // 262 us for one workgroup per head with two tiles per wavefront (the per-step latency of a
+    // wavefront, not HBM, bounds the pass) and 310 us for eight one-tile wavefronts per workgroup.
+    static constexpr int CT = 1;
     static constexpr int NW = V / (16 * CT) < 4 ? V / (16 * CT) : 4;
     static constexpr int VT = 16 * CT * NW;        // columns per workgroup
     static constexpr int NT = V / VT;              // workgroups per (sequence, head)
@@ -1511,8 +1512,8 @@ constexpr int combined_prep_waves() {
 
 // One launch that runs the state pass over one chunk range (workgroups 0 .. nstate-1, dispatched
 // first) and the 16-token prep of the next range (the remaining workgroups, on the CUs the state
-// pass leaves free). The state pass of H heads occupies H workgroups, one per CU; the prep of
-// the following chunks then runs beside it instead of after it.
+// pass leaves free). The state pass of H heads occupies 2H workgroups (V = 128), one per CU; the
+// prep of the following chunks then runs beside it instead of after it.
 template <bool BF, int K, int V>
 __global__ __launch_bounds__((StateCfg<BF, K, V, 1>::THREADS)) void kda_state_prep(StateParams sa, PrepParams pa,
                                                                                    int32_t nstate) {
@@ -1715,10 +1716,11 @@ hipError_t state_k(const PrefillArgs &a, hipStream_t st) {
 }
 
 // Pipelining over chunk ranges pays when the state pass leaves most of the 256 CUs free (at
-// 16-token chunks it runs one workgroup per (sequence, head), one per CU) and there are enough
-// chunks to split. The decision depends on sizes only, so the workspace query agrees with it.
+// 16-token chunks and V = 128 it runs two workgroups per (sequence, head), one per CU) and there
+// are enough chunks to split. The decision depends on sizes only, so the workspace query agrees
+// with it.
 bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk) {
-    return chunk == 16 && (int64_t)num_seqs * H <= 128 && n_chunks_max >= 128;
+    return chunk == 16 && (int64_t)num_seqs * H <= 64 && n_chunks_max >= 128;
 }
 
 // Chunk ranges of a pipelined call: 4 (at least 64 chunks each). KDA_PIPELINE_RANGES (1 .. 16)
