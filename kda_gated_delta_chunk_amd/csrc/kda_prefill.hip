@@ -991,11 +991,15 @@ struct StateCfg {
     static constexpr int SLOT = U * 1024;
     static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
     static constexpr int OBUF = 2 * 16 * OPITCH * 4;
-    static constexpr int DFIT = (152 * 1024 - OBUF) / SLOT;
-    // at most 8 wavefronts (two per SIMD) keeps 256 registers per lane
-    static constexpr int DMAX = 9 - NW < 6 ? 9 - NW : 6;
+    static constexpr int DFIT = (160 * 1024 - OBUF) / SLOT;
+    // at most 8 wavefronts (two per SIMD) keeps 256 registers per lane. A loader has one
+    // sub-tile in flight, issued after barrier B_{v-D+1} and awaited before B_{v-1}; its next
+    // one is issued after B_{v-D+1+NL}, so the ring may be one slot deeper than there are
+    // loaders.
+    static constexpr int NLMAX = 8 - NW;
+    static constexpr int DMAX = NLMAX + 2 < 6 ? NLMAX + 2 : 6;
     static constexpr int D = DFIT > DMAX ? DMAX : DFIT;
-    static constexpr int NL = D - 1;
+    static constexpr int NL = D - 1 < NLMAX ? D - 1 : NLMAX;
     static constexpr int THREADS = (NW + NL) * 64;
     static constexpr int LDS = D * SLOT + OBUF;
     static_assert(D >= 3, "ring too shallow");
@@ -1131,13 +1135,15 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // Barrier B_u certifies sub-tiles u and u+1 (the compute wavefronts read u+1's first
         // operands during step u) and frees the slot of sub-tile u-1.
         if (nu > 0) {
+            // sub-tiles 0 .. D-2 before the loop (a loader may start with two in flight: its first
+            // wait covers both)
             for (int u = k; u < nu && u < D - 1; u += NL) issue(u);
             const int lt = threadIdx.x - NW * 64;
             for (int u = 0; u < nu; ++u) {
                 if ((u == 0 && k == 0) || (u + 1 < nu && (u + 1) % NL == k))
-                    wait_copies();              // sub-tile u+1 (or 0): this loader's only copy in flight
+                    wait_copies();              // sub-tile u+1 (or 0)
                 lds_done_barrier();             // B_u (the o rows read before it are done)
-                if ((u % NL) == k && u + NL < nu) issue(u + NL);
+                if (((u + D - 1) % NL) == k && u + D - 1 < nu) issue(u + D - 1);
                 if (u > 1) store_o(u - 2, lt, NL * 64);
             }
             lds_done_barrier();                 // B_nu
