@@ -182,6 +182,22 @@ __device__ __forceinline__ int find_seq(const int32_t *chunk_off, int N, int gc)
     return lo;
 }
 
+// The chunk table as the kernels read it. Batched input (no cu_seqlens) has N sequences of
+// T_row tokens each, so the table is arithmetic and is neither built nor read.
+struct ChunkTab {
+    const int64_t *seq_tok;   // null: batched
+    const int32_t *chunk_off;
+    int64_t T_row;
+    int32_t cpr;              // chunks per row (batched)
+    __device__ __forceinline__ int64_t tok(int n) const { return seq_tok ? seq_tok[n] : (int64_t)n * T_row; }
+    __device__ __forceinline__ int off(int n) const { return chunk_off ? chunk_off[n] : n * cpr; }
+    __device__ __forceinline__ int find(int N, int gc) const {
+        if (chunk_off) return find_seq(chunk_off, N, gc);
+        const int n = gc / cpr;  // only called for gc < off(N), so cpr >= 1
+        return n < N - 1 ? n : N - 1;
+    }
+};
+
 // ------------------------------------------------------ chunk prep (K1+K2)
 // Order this wavefront's LDS writes before its later LDS reads by other lanes
 // (waits for outstanding LDS operations; also a compiler reordering barrier).
@@ -396,8 +412,7 @@ __device__ __forceinline__ void solve16(const float *sAT, int n, float (&x)[16])
 struct PrepParams {
     const void *q, *k, *g, *beta;
     int32_t H, N;
-    const int64_t *seq_tok;
-    const int32_t *chunk_off;
+    ChunkTab tab;
     char *frags;
     int32_t g0, g1;
 };
@@ -412,12 +427,11 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP;
     const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
     const int32_t H = pa.H, N = pa.N;
-    const int64_t *__restrict__ seq_tok = pa.seq_tok;
-    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    const ChunkTab &tab = pa.tab;
     char *__restrict__ frags = pa.frags;
     const int lane = threadIdx.x & 63;
     const int ag = lane >> 4, r = lane & 15;  // lane group; token (row) or column in a tile
-    const int total = chunk_off[N] < pa.g1 ? chunk_off[N] : pa.g1;
+    const int total = tab.off(N) < pa.g1 ? tab.off(N) : pa.g1;
     const int gc = pa.g0 + (int)(item / H), h = (int)(item % H);
     if (gc >= total) return;  // wave-uniform
     char *xt = lds + D::XT;
@@ -427,9 +441,9 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     float *sP = reinterpret_cast<float *>(lds + D::SP);
     float *sB = reinterpret_cast<float *>(lds + D::SB);
 
-    const int n = find_seq(chunk_off, N, gc);
-    const int64_t tok0 = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * SUB;
-    const int64_t tend = seq_tok[n + 1];
+    const int n = tab.find(N, gc);
+    const int64_t tok0 = tab.tok(n) + (int64_t)(gc - tab.off(n)) * SUB;
+    const int64_t tend = tab.tok(n + 1);
     const int nvalid = (int)((tend - tok0) < SUB ? (tend - tok0) : SUB);  // >= 1
 
     // ---- this lane's token row: key channels 32s + 8ag .. +7 of q, k, g, and beta. Rows
@@ -634,13 +648,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP, BP = D::BP;
     const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
     const int32_t H = pa.H, N = pa.N;
-    const int64_t *__restrict__ seq_tok = pa.seq_tok;
-    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    const ChunkTab &tab = pa.tab;
     char *__restrict__ frags = pa.frags;
     extern __shared__ __align__(16) char smem[];
     const int R = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ag = lane >> 4, r = lane & 15;
-    const int total = chunk_off[N] < pa.g1 ? chunk_off[N] : pa.g1;
+    const int total = tab.off(N) < pa.g1 ? tab.off(N) : pa.g1;
     const int gc = pa.g0 + (int)(blockIdx.x / H), h = (int)(blockIdx.x % H);
     if (gc >= total) return;  // whole workgroup (uniform)
     char *xt = smem + D::XT + R * D::XT_B;
@@ -652,9 +665,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     float *sAT = reinterpret_cast<float *>(smem + D::SA) + R * 16 * MP;
     char *kx = smem + D::KX + R * D::KX_B;
 
-    const int n = find_seq(chunk_off, N, gc);
-    const int64_t t0c = seq_tok[n] + (int64_t)(gc - chunk_off[n]) * (CS * SUB);
-    const int64_t tend = seq_tok[n + 1];
+    const int n = tab.find(N, gc);
+    const int64_t t0c = tab.tok(n) + (int64_t)(gc - tab.off(n)) * (CS * SUB);
+    const int64_t tend = tab.tok(n + 1);
     const int nvc = (int)((tend - t0c) < CS * SUB ? (tend - t0c) : CS * SUB);  // >= 1
 
     // ---- token row 16R + r of the chunk (rows past the sequence end act as identity tokens)
@@ -1036,8 +1049,7 @@ struct StateParams {
     int32_t o_bf16;
     float *Sfin;
     int32_t H, N;
-    const int64_t *seq_tok;
-    const int32_t *chunk_off;
+    ChunkTab tab;
     const char *frags;
     int32_t g0, g1;
     float *Scarry;
@@ -1055,8 +1067,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     void *__restrict__ op = pa.o;
     const int o_bf16 = pa.o_bf16;
     const int32_t H = pa.H, N = pa.N;
-    const int64_t *__restrict__ seq_tok = pa.seq_tok;
-    const int32_t *__restrict__ chunk_off = pa.chunk_off;
+    const ChunkTab &tab = pa.tab;
     const char *__restrict__ frags = pa.frags;
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
@@ -1068,14 +1079,14 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     if (head >= N * H) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c0n = chunk_off[n], c1n = chunk_off[n + 1];
+    const int c0n = tab.off(n), c1n = tab.off(n + 1);
     const int c0 = c0n > pa.g0 ? c0n : pa.g0, c1 = c1n < pa.g1 ? c1n : pa.g1;  // chunks in the range
     const int nu = c1 > c0 ? (c1 - c0) * CS : 0;                              // sub-tile steps
     const bool empty = c0n == c1n;
     if (nu == 0 && !(empty && pa.first)) return;  // nothing of this sequence here (uniform)
     const float *__restrict__ S0 = (empty || c0 == c0n) ? pa.S0 : pa.Scarry;
     float *__restrict__ Sfin = (empty || c1 == c1n) ? pa.Sfin : pa.Scarry;
-    const int64_t s0 = seq_tok[n] + (int64_t)(c0 - c0n) * (CS * SUB), s1 = seq_tok[n + 1];
+    const int64_t s0 = tab.tok(n) + (int64_t)(c0 - c0n) * (CS * SUB), s1 = tab.tok(n + 1);
 
     // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
     // (done by the loader wavefronts between B_{u+2} and B_{u+3}: the compute wavefronts stage
@@ -1592,11 +1603,21 @@ hipError_t allow_lds(const void *kernel, bool &done, int bytes) {
 
 constexpr int32_t ALL_CHUNKS = 0x7fffffff;
 
+ChunkTab chunk_tab(const PrefillArgs &a, const WsPtrs &w) {
+    ChunkTab t;
+    const bool batched = a.cu_seqlens == nullptr;
+    t.seq_tok = batched ? nullptr : w.seq_tok;
+    t.chunk_off = batched ? nullptr : w.chunk_off;
+    t.T_row = a.T;
+    t.cpr = (int32_t)((a.T + a.chunk - 1) / a.chunk);
+    return t;
+}
+
 PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1) {
     PrepParams p;
     p.q = a.q; p.k = a.k; p.g = a.g; p.beta = a.beta;
     p.H = a.H; p.N = a.num_seqs;
-    p.seq_tok = w.seq_tok; p.chunk_off = w.chunk_off; p.frags = w.frags;
+    p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     return p;
 }
@@ -1605,14 +1626,16 @@ StateParams state_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int3
     StateParams p;
     p.v = a.v; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
     p.H = a.H; p.N = a.num_seqs;
-    p.seq_tok = w.seq_tok; p.chunk_off = w.chunk_off; p.frags = w.frags;
+    p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     p.Scarry = w.carry;
     p.first = first ? 1 : 0;
     return p;
 }
 
+// Packed input only: batched input reads no table (ChunkTab).
 hipError_t launch_table(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    if (a.cu_seqlens == nullptr) return hipSuccess;
     hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
                        (int32_t)a.chunk, w.seq_tok, w.chunk_off);
     return hipGetLastError();
