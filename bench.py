@@ -47,9 +47,10 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev, chunk=16):
+def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay"):
     lib = _lib.load()
-    inp = synth.workload_prefill_inputs(w, device=dev)
+    gc = _lib.GATES[gate]
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"))
     B, T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
     N = B
@@ -62,7 +63,7 @@ def time_prefill(w, steps, warmup, dev, chunk=16):
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def prep():
-        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1,
+        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1, gc,
                                       ws.data_ptr(), wsb, sh), "kda_chunk_prep")
 
     def state():
@@ -71,7 +72,7 @@ def time_prefill(w, steps, warmup, dev, chunk=16):
 
     def fwd():
         _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, B, T, H, K, V, N, chunk,
-                                     1, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
+                                     1, gc, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
 
     # the step: one kda_chunk_fwd call (where the state pass leaves CUs free, the library runs the
     # prep of later chunks beside the state pass of earlier ones)
@@ -106,19 +107,20 @@ def time_prefill(w, steps, warmup, dev, chunk=16):
             "state_ms": state_ms, "ws_bytes": wsb}
 
 
-def time_decode(w, steps, dev):
+def time_decode(w, steps, dev, gate="log_decay"):
     N, H, K, V = w.N, w.H, w.K, w.V
     S = synth.decode_state(N, H, K, V, seed=w.seed, device=dev)
-    inputs = [synth.decode_inputs(N, H, K, V, w.io, seed=w.seed, step=s, device=dev) for s in range(steps)]
+    inputs = [synth.decode_inputs(N, H, K, V, w.io, seed=w.seed, step=s, device=dev,
+                                  gate_preact=(gate == "scaled_sigmoid")) for s in range(steps)]
     o = torch.empty((N, H, V), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     for s in range(2):  # warm-up on the same state (its values only drift)
-        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o)
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for s in range(steps):
-        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o)
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate)
         ev[s + 1].record(stream)
     torch.cuda.synchronize()
     per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
@@ -273,6 +275,16 @@ def main():
                                      "kda_state_pass": r64["state_ms"]},
                       "split_calls_ms": r64["prep_ms"] + r64["state_ms"],
                       "roofline_path": path_roofline(r64, 64), "workspace_bytes": r64["ws_bytes"]}
+    print("[bench] prefill %s with the gate formed in-kernel: warmup %d, steps %d" % (w.name, args.warmup,
+                                                                                    args.steps),
+          file=sys.stderr, flush=True)
+    rg = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid")
+    msg = rg["wall_s"] * 1e3 / args.steps
+    out["gate_fused"] = {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 16, zero S0; g holds the gate "
+                                     "pre-activation x, log-decay -5*sigmoid(x) formed in kda_chunk_prep",
+                         "tokens_per_s": rg["B"] * rg["T"] / (msg * 1e-3), "ms_per_step": msg,
+                         "kernels_ms": {"kda_chunk_prep (+chunk table)": rg["prep_ms"],
+                                        "kda_state_pass": rg["state_ms"]}}
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
         print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)
@@ -286,6 +298,8 @@ def main():
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                       "traffic": measured_traffic("kda::kda_decode_kernel<true, 128, 128>"),
                                       "algorithmic_bytes_per_launch": d["bytes_per_step"]}}
+        dg = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid")
+        out["decode"]["gate_fused_ms_per_step"] = dg["ms_per_step"]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

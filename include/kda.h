@@ -62,6 +62,21 @@ typedef enum {
     KDA_DTYPE_BF16 = 1
 } kda_dtype_t;
 
+/*
+ * What the g argument holds.
+ *   KDA_GATE_LOG_DECAY      the log-decay itself (alpha = exp(g)).
+ *   KDA_GATE_SCALED_SIGMOID the gate pre-activation x; the kernels form the
+ *                           log-decay -5 / (1 + exp(-x)) in fp32 as they read
+ *                           it (the scaled sigmoid bounded below by -5 that
+ *                           the first page above describes in its paragraph
+ *                           "K3 对 Kimi Linear 的进一步修改"), so the activation
+ *                           costs no pass and no bytes of its own.
+ */
+typedef enum {
+    KDA_GATE_LOG_DECAY = 0,
+    KDA_GATE_SCALED_SIGMOID = 1
+} kda_gate_t;
+
 /* Version of this ABI (bumped on any signature change). */
 int kda_abi_version(void);
 
@@ -84,9 +99,11 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  * chunk", first page cited above).
  *
  * Inputs (dtype `io`):
- *   q, k, g   [B, T, H, K]   g is the post-activation log-decay; the chunk
- *                            form assumes -5 <= g <= 0 (the bounded gate);
- *                            outside that range results are unspecified
+ *   q, k, g   [B, T, H, K]   g as `gate` says. With KDA_GATE_LOG_DECAY the
+ *                            chunk form assumes -5 <= g <= 0 (the bounded
+ *                            gate); outside that range results are
+ *                            unspecified. With KDA_GATE_SCALED_SIGMOID any
+ *                            finite g is valid.
  *   v         [B, T, H, V]
  *   beta      [B, T, H]      write strength, used as given
  *   S0        [num_seqs, H, K, V] fp32, or NULL for a zero initial state
@@ -104,14 +121,15 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *   S_final   [num_seqs, H, K, V] fp32, or NULL to skip. May not alias S0.
  *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes().
  * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
- *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow),
+ *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow,
+ *   unknown dtype or gate),
  *   NOT_SUPPORTED (K, V or chunk outside the supported set),
  *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const float *S0, const int32_t *cu_seqlens,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                           int32_t chunk, kda_dtype_t io, kda_dtype_t o_dtype,
+                           int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype,
                            void *o, float *S_final, void *workspace, size_t workspace_bytes,
                            void *stream);
 
@@ -130,7 +148,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  *   (chunk, head), forms the cumulative log-decay, the beta-weighted
  *   decay-scaled key products, solves the chunk's unit lower-triangular
  *   system and stores the resulting factors in `workspace` (layout private to
- *   the library). Reads q, k, g, beta; V only sizes the workspace check.
+ *   the library). Reads q, k, g (as `gate` says), beta; V only sizes the
+ *   workspace check.
  * kda_chunk_state: the sequential pass over the chunks of each (sequence,
  *   head): carries S from S0 (or 0), writes o and S_final. Reads v, S0 and a
  *   workspace that kda_chunk_prep filled with the same sizes and the same
@@ -140,7 +159,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  */
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, void *workspace,
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
                             size_t workspace_bytes, void *stream);
 kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
@@ -152,6 +171,7 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
  * steps above applied once, with the fixed-size state updated in place
  * ("S_t = Update(S_{t-1}, k_t, v_t)", second page cited above).
  *   q, k, g [N, H, K]; v [N, H, V]; beta [N, H]      dtype `io`
+ *   g       as `gate` says
  *   S       [N, H, K, V] fp32, read and overwritten in place
  *   o       [N, H, V] in `o_dtype`
  * Any finite g is accepted (no chunk-range assumption). S may not alias any
@@ -159,7 +179,7 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
                              float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
-                             kda_dtype_t io, kda_dtype_t o_dtype, void *stream);
+                             kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype, void *stream);
 
 #ifdef __cplusplus
 }

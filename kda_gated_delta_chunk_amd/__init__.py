@@ -59,13 +59,21 @@ def _need(t, name, shape, dtype, dev):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _gate_code(gate: str) -> int:
+    if gate not in _lib.GATES:
+        raise ValueError("gate must be one of %s" % sorted(_lib.GATES))
+    return _lib.GATES[gate]
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
-              output_final_state: bool = True, workspace=None, out=None):
+              output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay"):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
     [num_seqs, H, K, V]. ``workspace`` (uint8 CUDA tensor) and ``out`` may be
-    passed to avoid allocations.
+    passed to avoid allocations. ``gate`` says what ``g`` holds: "log_decay"
+    (the log-decay itself) or "scaled_sigmoid" (the gate pre-activation,
+    mapped to -5*sigmoid(g) inside the kernels).
     """
     lib = _lib.load()
     dev = q.device
@@ -75,6 +83,7 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     V = v.shape[-1]
     dt = q.dtype
     io = _io_code(dt)
+    gc = _gate_code(gate)
     for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
                          ("beta", beta, (B, T, H))):
         _need(t, name, shp, dt, dev)
@@ -99,14 +108,17 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
-                               B, T, H, K, V, N, chunk, io, _io_code(odt), _ptr(out), _ptr(S_final),
+                               B, T, H, K, V, N, chunk, io, gc, _io_code(odt), _ptr(out), _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(status, "kda_chunk_fwd")
     return out, S_final
 
 
-def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None):
-    """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V]."""
+def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay"):
+    """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V].
+
+    ``gate`` as for :func:`chunk_fwd`.
+    """
     lib = _lib.load()
     dev = q.device
     if dev.type != "cuda":
@@ -115,6 +127,7 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None):
     V = v.shape[-1]
     dt = q.dtype
     io = _io_code(dt)
+    gc = _gate_code(gate)
     for name, t, shp in (("k", k, (N, H, K)), ("g", g, (N, H, K)), ("v", v, (N, H, V)), ("beta", beta, (N, H))):
         _need(t, name, shp, dt, dev)
     _need(S, "S", (N, H, K, V), torch.float32, dev)
@@ -124,6 +137,6 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None):
     else:
         _need(out, "out", (N, H, V), odt, dev)
     status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
-                                 N, H, K, V, io, _io_code(odt), _stream(dev))
+                                 N, H, K, V, io, gc, _io_code(odt), _stream(dev))
     _lib.check(status, "kda_decode_step")
     return out

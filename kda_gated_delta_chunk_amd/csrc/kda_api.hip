@@ -16,6 +16,7 @@ constexpr int64_t kMaxElems = (int64_t)1 << 60;
 bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; }
+bool valid_gate(kda_gate_t g) { return g == KDA_GATE_LOG_DECAY || g == KDA_GATE_SCALED_SIGMOID; }
 // beta is read one element at a time: natural alignment of its dtype suffices
 bool aligned_elem(const void *p, kda_dtype_t t) { return ((uintptr_t)p & (t == KDA_DTYPE_BF16 ? 1u : 3u)) == 0; }
 
@@ -56,7 +57,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 1; }
+int kda_abi_version(void) { return 2; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -85,10 +86,10 @@ namespace {
 // pointers the entry point reads or writes.
 kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
                           const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
-                          int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_dtype_t o_dtype, void *o,
-                          float *S_final, const void *workspace, size_t workspace_bytes, bool need_prep,
-                          bool need_state, kda::PrefillArgs &a) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+                          int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
+                          kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
+                          size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed);
     if (st != KDA_SUCCESS) return st;
@@ -110,6 +111,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
+    a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
     a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
     a.chunk = chunk;
     a.n_chunks_max = nc;
@@ -120,11 +122,11 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
                            int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
-                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           kda_gate_t gate, kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
-    kda_status_t st = prefill_args(q, k, v, g, beta, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, o_dtype,
-                                   o, S_final, workspace, workspace_bytes, true, true, a);
+    kda_status_t st = prefill_args(q, k, v, g, beta, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
+                                   o_dtype, o, S_final, workspace, workspace_bytes, true, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -132,11 +134,11 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, void *workspace,
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
                             size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
-                                   io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
+                                   gate, io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -148,7 +150,8 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
                              size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, S0, cu_seqlens, B, T, H, K, V, num_seqs,
-                                   chunk, io, o_dtype, o, S_final, workspace, workspace_bytes, false, true, a);
+                                   chunk, io, KDA_GATE_LOG_DECAY, o_dtype, o, S_final, workspace, workspace_bytes,
+                                   false, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_state(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -156,8 +159,8 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta, float *S,
                              void *o, int32_t N, int32_t H, int32_t K, int32_t V, kda_dtype_t io,
-                             kda_dtype_t o_dtype, void *stream) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype)) return KDA_ERROR_INVALID_VALUE;
+                             kda_gate_t gate, kda_dtype_t o_dtype, void *stream) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
     if (N < 0 || H < 1) return KDA_ERROR_INVALID_VALUE;
     if (!supported_dim(K) || !supported_dim(V)) return KDA_ERROR_NOT_SUPPORTED;
     if ((int64_t)N * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
@@ -178,6 +181,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     a.N = N; a.H = H; a.K = K; a.V = V;
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
+    a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
     if (kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }

@@ -194,6 +194,17 @@ template <int N> __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[1][N]
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// The bounded log-decay gate of "Kimi K3 发布核实与 Moonshot AI 主干架构演变" (section 3,
+// paragraph "K3 对 Kimi Linear 的进一步修改"): a sigmoid of the pre-activation x scaled so the
+// log-decay lies in (-5, 0), returned in base 2 (log2 of the retention):
+//   -5 log2(e) / (1 + e^-x).
+// For x below about -88 the exponential overflows to +inf and the result is -0 (no decay); for
+// large x it tends to -5 log2(e). v_exp_f32 and v_rcp_f32 are each within 1 ulp.
+__device__ __forceinline__ float gate_log2_decay(float x) {
+    constexpr float L2E = 1.4426950408889634f;
+    return (-5.f * L2E) * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * L2E));
+}
+
 // I/O element access by dtype.
 template <bool BF> struct IO;
 template <> struct IO<true> {

@@ -10,7 +10,9 @@
 //   S  = S' + beta k delta^T,          o = S^T q = y + beta (k.q) delta
 // Everything is one read and one write of S: both reductions (u and y) are
 // taken in the same pass over S', so the state makes exactly one round trip
-// through HBM and o needs no second pass.
+// through HBM and o needs no second pass. g is either the log-decay itself or
+// the gate pre-activation, mapped here through the bounded scaled sigmoid of
+// the first page's paragraph "K3 对 Kimi Linear 的进一步修改".
 //
 // One 256-thread workgroup per (n, h). Thread t owns 4 adjacent value columns
 // (one 16-byte vector) of K*V/1024 rows; the rows of a wavefront's load
@@ -27,7 +29,7 @@ template <bool BF, int K, int V>
 __global__ __launch_bounds__(256) void kda_decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
     const void *__restrict__ gp, const void *__restrict__ bp, float *__restrict__ S,
-    void *__restrict__ op, int o_bf16, int32_t NH) {
+    void *__restrict__ op, int o_bf16, int gate, int32_t NH) {
     constexpr int CG = V / 4;          // column groups (float4) per row
     constexpr int RG = 256 / CG;       // row groups
     constexpr int RPT = K / RG;        // rows per thread
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     for (int j = 0; j < RPT; ++j)
         s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (size_t)(rg + RG * j) * V) + cg);
 
-    // 2. token vectors to LDS; alpha = exp(g)
+    // 2. token vectors to LDS; alpha = exp(log-decay)
     using E = typename IO<BF>::T;
     const E *q = reinterpret_cast<const E *>(qp) + (size_t)nh * K;
     const E *k = reinterpret_cast<const E *>(kp) + (size_t)nh * K;
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     float kq = 0.f;
     if (t < K) {
         const float kt = IO<BF>::ld(k, t), qt = IO<BF>::ld(q, t);
-        s_alpha[t] = exp_e(IO<BF>::ld(g, t));
+        const float gt = IO<BF>::ld(g, t);
+        s_alpha[t] = __builtin_amdgcn_exp2f(gate ? gate_log2_decay(gt) : gt * 1.4426950408889634f);
         s_k[t] = kt;
         s_q[t] = qt;
         kq = kt * qt;
@@ -139,9 +142,9 @@ hipError_t launch_dk(const DecodeArgs &a, hipStream_t st) {
     const int32_t NH = a.N * a.H;
     const dim3 grid(NH), block(256);
     switch (a.V) {
-        case 32: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 32>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, NH); break;
-        case 64: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 64>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, NH); break;
-        default: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 128>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, NH); break;
+        case 32: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 32>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
+        case 64: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 64>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
+        default: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 128>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
     }
     return hipGetLastError();
 }

@@ -15,6 +15,7 @@ struct PrefillArgs {
     int64_t B, T;
     int32_t H, K, V, num_seqs;
     bool io_bf16, o_bf16;
+    bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
     void *o;
     float *S_final;
     void *workspace;
@@ -40,6 +41,7 @@ struct DecodeArgs {
     void *o;
     int32_t N, H, K, V;
     bool io_bf16, o_bf16;
+    bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -412,6 +412,7 @@ __device__ __forceinline__ void solve16(const float *sAT, int n, float (&x)[16])
 struct PrepParams {
     const void *q, *k, *g, *beta;
     int32_t H, N;
+    int32_t gate;  // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
     ChunkTab tab;
     char *frags;
     int32_t g0, g1;
@@ -467,7 +468,7 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bl[s][j] = row_scan16(valid ? bl[s][j] * LOG2E : 0.f);
+            bl[s][j] = row_scan16(valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f);
             bt[s][j] = row_last(bl[s][j]);
         }
     if (ag == 0) sB[r] = beta;
@@ -688,7 +689,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bl[s][j] = row_scan16(valid ? bl[s][j] * LOG2E : 0.f);
+            bl[s][j] = row_scan16(valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f);
             bt[s][j] = row_last(bl[s][j]);
         }
     if (r == 0) {
@@ -1617,6 +1618,7 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
     PrepParams p;
     p.q = a.q; p.k = a.k; p.g = a.g; p.beta = a.beta;
     p.H = a.H; p.N = a.num_seqs;
+    p.gate = a.gate_sigmoid ? 1 : 0;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     return p;

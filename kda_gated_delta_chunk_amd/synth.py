@@ -9,7 +9,9 @@ Distributions (the workloads of the spec configurations):
   k     ~ N(0, 1), then L2-normalised over the key dimension per (token, head)
           in fp32 before the cast to the I/O dtype
   g     = -5 * sigmoid(x), x ~ N(0, 1) per (token, head, key channel): the
-          bounded log-retention of the K3 gate (lower bound -5)
+          bounded log-retention of the K3 gate (lower bound -5); with
+          ``gate_preact=True`` g is the draw x itself (times ``g_scale``), for
+          calls that form the log-decay from the pre-activation
   beta  = sigmoid(x), x ~ N(0, 1) per (token, head)
   S0    ~ N(0, 0.02^2) (standard deviation 0.02), fp32
 All draws are fp32 and then rounded to the I/O dtype with round-to-nearest-
@@ -95,13 +97,15 @@ def cu_from_lengths(lengths) -> list[int]:
 
 def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0,
                    device="cpu", cu_seqlens=None, with_S0: bool = False, block_tokens: int = 65536,
-                   g_shift: float = 0.0, g_const: float | None = None, beta_const: float | None = None):
+                   g_shift: float = 0.0, g_const: float | None = None, beta_const: float | None = None,
+                   gate_preact: bool = False, g_scale: float = 1.0):
     """Inputs of one prefill call.
 
     Returns a dict with q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H] in the I/O
     dtype, S0 [N,H,K,V] fp32 (or None) and cu_seqlens int32 [N+1] (or None).
     ``g_shift`` moves the pre-sigmoid draw of g (e.g. -6 for mild decay);
-    ``g_const``/``beta_const`` replace the draw by a constant (stress cases).
+    ``g_const``/``beta_const`` replace the draw by a constant (stress cases);
+    ``gate_preact`` stores the pre-sigmoid draw g_scale * x + g_shift itself.
     """
     dt = DTYPES[io]
     dev = torch.device(device)
@@ -125,6 +129,8 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
         vf[a:b] = _randn((n, H, V), seed, "v", blk, dev).to(dt)
         if g_const is not None:
             gf[a:b] = torch.full((n, H, K), float(g_const), device=dev).to(dt)
+        elif gate_preact:
+            gf[a:b] = (g_scale * _randn((n, H, K), seed, "g", blk, dev) + g_shift).to(dt)
         else:
             gf[a:b] = (-5.0 * torch.sigmoid(_randn((n, H, K), seed, "g", blk, dev) + g_shift)).to(dt)
         if beta_const is not None:
@@ -153,15 +159,17 @@ def workload_prefill_inputs(w: Workload, device="cpu", **kw):
 
 
 def decode_inputs(N: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0, step: int = 0,
-                  device="cpu"):
-    """Per-step decode inputs q, k, g [N,H,K], v [N,H,V], beta [N,H] (step = block id)."""
+                  device="cpu", gate_preact: bool = False, g_scale: float = 1.0):
+    """Per-step decode inputs q, k, g [N,H,K], v [N,H,V], beta [N,H] (step = block id).
+    ``gate_preact``: g is the pre-sigmoid draw g_scale * x itself."""
     dt = DTYPES[io]
     dev = torch.device(device)
     q = _randn((N, H, K), seed, "q", step, dev).to(dt)
     kr = _randn((N, H, K), seed, "k", step, dev)
     k = (kr / torch.sqrt(torch.sum(kr * kr, dim=-1, keepdim=True))).to(dt)
     v = _randn((N, H, V), seed, "v", step, dev).to(dt)
-    g = (-5.0 * torch.sigmoid(_randn((N, H, K), seed, "g", step, dev))).to(dt)
+    x = _randn((N, H, K), seed, "g", step, dev)
+    g = (g_scale * x if gate_preact else -5.0 * torch.sigmoid(x)).to(dt)
     beta = torch.sigmoid(_randn((N, H), seed, "beta", step, dev)).to(dt)
     return {"q": q, "k": k, "v": v, "g": g, "beta": beta}
 

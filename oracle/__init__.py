@@ -70,13 +70,39 @@ def _ptr(a: np.ndarray | None):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0):
+GATES = ("log_decay", "scaled_sigmoid")
+
+
+def scaled_sigmoid_gate(x) -> np.ndarray:
+    """Log-decay from the gate pre-activation x, in fp64: -5 * sigmoid(x) = -5 / (1 + e^(-x)).
+
+    "Kimi K3 发布核实与 Moonshot AI 主干架构演变", section 3, paragraph
+    "K3 对 Kimi Linear 的进一步修改": K3's log-decay is a sigmoid scaled to a
+    lower bound of -5 (in place of Kimi Linear's unbounded negative softplus).
+    The plainest reading of "scaled sigmoid bounded below by -5" for a
+    log-decay (which must be <= 0) is -5 * sigmoid(x), range (-5, 0).
+    """
+    x = _f64(x)
+    with np.errstate(over="ignore"):  # e^(-x) = inf for x < -709: the result is -0 (no decay)
+        return -5.0 / (1.0 + np.exp(-x))
+
+
+def _log_decay(g, gate: str) -> np.ndarray:
+    if gate not in GATES:
+        raise ValueError("gate must be one of %s" % (GATES,))
+    return scaled_sigmoid_gate(g) if gate == "scaled_sigmoid" else _f64(g)
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate: str = "log_decay"):
     """Run the fp64 recurrence over whole sequences.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H];
     S0: [N, H, K, V] or None (zeros); cu_seqlens: [N+1] or None.
+    gate: "log_decay" (g is the log-decay) or "scaled_sigmoid" (g is the gate
+    pre-activation; the log-decay is scaled_sigmoid_gate(g)).
     Returns (o [B, T, H, V], S_final [N, H, K, V]) as float64 arrays.
     """
+    g = _log_decay(g, gate)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -103,11 +129,13 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0):
     return o, sf
 
 
-def decode_step(q, k, v, g, beta, S, threads: int = 0):
+def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay"):
     """One decode step. q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H]; S: [N, H, K, V].
 
-    Returns (o [N, H, V], S_new [N, H, K, V]); the input S is not modified.
+    gate as for chunk_fwd. Returns (o [N, H, V], S_new [N, H, K, V]); the
+    input S is not modified.
     """
+    g = _log_decay(g, gate)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     S_new = _f64(S).copy()
     N, H, K = q.shape

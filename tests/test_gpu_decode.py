@@ -15,19 +15,20 @@ def _announce(name, **kw):
     print("\n[case] %s %s" % (name, " ".join("%s=%s" % kv for kv in kw.items())), flush=True)
 
 
-def _steps(N, H, K, V, io, steps, seed):
+def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0):
     S = synth.decode_state(N, H, K, V, seed=seed, device=DEV)
     S_ref = S.double().cpu().numpy()
     worst = {"o": 0.0, "S": 0.0}
+    pre = gate == "scaled_sigmoid"
     for step in range(steps):
-        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV)
+        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV, gate_preact=pre, g_scale=g_scale)
         args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
         S32 = S.clone()
-        o = decode_step(*args, S)
-        o32 = decode_step(*args, S32, o_dtype=torch.float32)
+        o = decode_step(*args, S, gate=gate)
+        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate)
         torch.cuda.synchronize()
         assert torch.equal(S32, S)
-        o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref)
+        o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate=gate)
         if io == "fp32":
             worst["o"] = max(worst["o"], err(o.cpu(), o_ref))
         else:
@@ -50,6 +51,14 @@ def test_decode_fp32(N, H, K, V):
 def test_decode_bf16(N, H, K, V):
     _announce("decode_bf16", N=N, H=H, K=K, V=V)
     _steps(N, H, K, V, "bf16", steps=4, seed=32)
+
+
+@pytest.mark.parametrize("io,g_scale", [("fp32", 1.0), ("fp32", 30.0), ("bf16", 1.0), ("bf16", 30.0)])
+def test_decode_gate_fused(io, g_scale):
+    """g holds the gate pre-activation x (scale 30: most channels saturated at either end); the
+    kernel forms -5*sigmoid(x) in fp32, the oracle in fp64."""
+    _announce("decode_gate", io=io, g_scale=g_scale)
+    _steps(3, 2, 128, 128, io, steps=4, seed=34, gate="scaled_sigmoid", g_scale=g_scale)
 
 
 def test_decode_512_streams():

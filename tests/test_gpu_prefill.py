@@ -30,12 +30,13 @@ def _oracle(inp, heads=None):
         q, k, v, g, beta = (x[:, :, hs].contiguous() for x in (q, k, v, g, beta))
         S0 = None if S0 is None else S0[:, hs].contiguous()
     return oracle.chunk_fwd(q.cpu(), k.cpu(), v.cpu(), g.cpu(), beta.cpu(), None if S0 is None else S0.cpu(),
-                            None if cu is None else cu.cpu())
+                            None if cu is None else cu.cpu(), gate=inp.get("gate", "log_decay"))
 
 
 def _run(inp, o_dtype=None, chunk=16):
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
-                      cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk)
+                      cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk,
+                      gate=inp.get("gate", "log_decay"))
     torch.cuda.synchronize()
     return o, Sf
 
@@ -291,3 +292,65 @@ def test_pipelined_varlen_against_oracle():
     _announce("pipelined_varlen", lengths=lengths, H=12, seed=23)
     inp = synth.prefill_inputs(1, cu[-1], 12, 128, 128, "bf16", seed=23, device=DEV, cu_seqlens=cu, with_S0=True)
     _check(inp, heads=(0, 7, 11))
+
+
+# ------------------------------------------------------------ gate formed in-kernel
+#
+# With gate="scaled_sigmoid", g holds the gate pre-activation x and kda_chunk_prep forms the
+# log-decay -5*sigmoid(x) in fp32 as it reads it; the oracle forms it in fp64 from the same x.
+
+def _gate_inputs(B, T, H, K, V, io, seed, g_scale=1.0, **kw):
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=seed, device=DEV, gate_preact=True, g_scale=g_scale, **kw)
+    inp["gate"] = "scaled_sigmoid"
+    return inp
+
+
+@CHUNKS
+@pytest.mark.parametrize("io,B,T,H,K,V", [("fp32", 2, 77, 3, 128, 128), ("fp32", 1, 130, 2, 32, 64),
+                                          ("bf16", 2, 200, 3, 128, 128), ("bf16", 1, 97, 2, 64, 32)])
+def test_gate_fused_shapes(io, B, T, H, K, V, chunk):
+    _announce("gate_fused", io=io, B=B, T=T, H=H, K=K, V=V, chunk=chunk, seed=40)
+    _check(_gate_inputs(B, T, H, K, V, io, 40, with_S0=True), io=io, chunk=chunk)
+
+
+@CHUNKS
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_gate_fused_saturating(io, chunk):
+    """x ~ N(0, 30^2): most channels sit at one end of the gate, log-decay ~-5 (the dense-path
+    bound) or ~0 (x below about -88, where e^-x overflows fp32 and the gate gives exactly 0)."""
+    _announce("gate_saturating", io=io, chunk=chunk, seed=41)
+    _check(_gate_inputs(1, 150, 3, 128, 128, io, 41, g_scale=30.0, with_S0=True), io=io, chunk=chunk)
+
+
+@CHUNKS
+def test_gate_fused_varlen(chunk):
+    lengths = [37, 0, 16, 1, 150, 64, 0, 65]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("gate_varlen", lengths=lengths, chunk=chunk, seed=42)
+    inp = _gate_inputs(1, cu[-1], 4, 128, 128, "bf16", 42, cu_seqlens=cu, with_S0=True)
+    _check(inp, chunk=chunk)
+
+
+def test_gate_fused_matches_given_log_decay():
+    """fp32 I/O: the kernel's in-kernel gate and a log-decay given as input (the oracle's fp64
+    gate rounded to fp32) lead to the same outputs, to the fp32 parity bound: the two log-decays
+    differ by an ulp or so, which the cumulative sums carry into every decay factor."""
+    _announce("gate_vs_given", seed=43)
+    inp = _gate_inputs(1, 300, 4, 64, 64, "fp32", 43, with_S0=True)
+    o_a, S_a = _run(inp, chunk=16)
+    given = dict(inp, g=torch.from_numpy(oracle.scaled_sigmoid_gate(inp["g"].cpu())).float().to(DEV),
+                 gate="log_decay")
+    o_b, S_b = _run(given, chunk=16)
+    res = {"o": err(o_a.cpu(), o_b.cpu()), "S": err(S_a.cpu(), S_b.cpu())}
+    print("  differences", res, flush=True)
+    assert res["o"] <= TOL_FP32 and res["S"] <= TOL_FP32, res
+
+
+def test_gate_fused_k3_prefill_4k_sampled_heads():
+    """The gate-fused leg of the benchmark: H=96, T=4096, K=V=128, bf16, chunk 16, g = x ~ N(0,1)
+    pre-activations; the oracle runs on 4 heads of the full GPU call."""
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("gate_prefill_4k", seed=w.seed)
+    inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True)
+    inp["gate"] = "scaled_sigmoid"
+    _check(inp, heads=(0, 31, 64, 95))

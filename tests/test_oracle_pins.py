@@ -71,6 +71,56 @@ def test_rejects_bad_arguments():
         oracle.chunk_fwd(z, z, z[..., :1], z, np.zeros((1, 5, 1)))
 
 
+# ------------------------------------------------------------ the scaled-sigmoid gate
+
+def test_gate_closed_forms():
+    """-5 * sigmoid(x) at points where the sigmoid has exact values: 1/2 at 0, 3/4 at ln 3, 1/4 at
+    -ln 3, 1/(1+e) at -1; saturation at both ends without NaN."""
+    g = oracle.scaled_sigmoid_gate
+    assert g(np.array([0.0]))[0] == -2.5
+    assert abs(g(np.array([np.log(3.0)]))[0] + 3.75) < 1e-15
+    assert abs(g(np.array([-np.log(3.0)]))[0] + 1.25) < 1e-15
+    assert abs(g(np.array([-1.0]))[0] + 5.0 / (1.0 + np.e)) < 1e-15
+    hi, lo = g(np.array([800.0, 40.0])), g(np.array([-800.0, -40.0]))
+    assert hi[0] == -5.0 and abs(hi[1] + 5.0) < 1e-16
+    assert lo[0] == 0.0 and -5e-17 < lo[1] < 0.0
+    assert not np.isnan(g(np.array([-1e308, 1e308]))).any()
+
+
+def test_gate_symmetry_range_and_order():
+    """sigmoid(x) + sigmoid(-x) = 1, so g(x) + g(-x) = -5; g is strictly decreasing with range (-5, 0)."""
+    x = np.sort(np.random.default_rng(5).standard_normal(2001) * 6.0)
+    g = oracle.scaled_sigmoid_gate(x)
+    assert np.max(np.abs(g + oracle.scaled_sigmoid_gate(-x) + 5.0)) < 1e-14
+    assert np.all(np.diff(g) < 0.0)
+    assert np.all((g > -5.0) & (g < 0.0))
+
+
+def test_gate_drives_the_decay():
+    """Through the recurrence: with beta = 0 nothing is written, so S_final = diag(prod_t e^(g_t)) S0
+    and o_t = (decayed S)^T q_t. At x = 0 every token retains e^(-2.5) of each row; at x = ln 3
+    e^(-3.75); a row whose x is very negative keeps S0 unchanged (the gate's upper end)."""
+    T, K, V = 5, 3, 2
+    rng = np.random.default_rng(17)
+    x = np.zeros((1, T, 1, K))
+    x[..., 1] = np.log(3.0)
+    x[..., 2] = -800.0
+    q = rng.standard_normal((1, T, 1, K))
+    k = rng.standard_normal((1, T, 1, K))
+    v = rng.standard_normal((1, T, 1, V))
+    S0 = rng.standard_normal((1, 1, K, V))
+    o, Sf = oracle.chunk_fwd(q, k, v, x, np.zeros((1, T, 1)), S0=S0, gate="scaled_sigmoid")
+    rate = np.array([-2.5, -3.75, 0.0])
+    for t in range(T):
+        St = np.exp(rate * (t + 1))[:, None] * S0[0, 0]
+        assert kda_pins.rel_err(o[0, t, 0], St.T @ q[0, t, 0]) < 1e-13
+    assert kda_pins.rel_err(Sf[0, 0], np.exp(rate * T)[:, None] * S0[0, 0]) < 1e-13
+    o_d, S_d = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], x[:, 0], np.zeros((1, 1)), S0, gate="scaled_sigmoid")
+    assert kda_pins.rel_err(S_d[0, 0], np.exp(rate)[:, None] * S0[0, 0]) < 1e-13
+    with pytest.raises(ValueError):
+        oracle.chunk_fwd(q, k, v, x, np.zeros((1, T, 1)), gate="softplus")
+
+
 # ------------------------------------------------------------ planted mistakes
 #
 # A small numpy re-implementation with switches for plausible mistakes. The
