@@ -970,8 +970,55 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void *g) {
 // imply that the oldest copies have landed. Every copy is therefore awaited
 // with vmcnt(0), by a wavefront that has exactly one sub-tile in flight.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Progress flags in LDS (monotonic counters, one writer each). A flag is written after every LDS
+// operation it vouches for has been issued; a wavefront's LDS operations are carried out in
+// order, so a reader that sees the new value also sees what came before it.
+__device__ __forceinline__ void flag_put(uint32_t addr, int v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ int flag_get(uint32_t addr) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+}
+// A flag read issued without waiting; flag_ready() completes it (and every LDS operation issued
+// before it) and returns the value. Used to fetch a flag along with a step's operand reads.
+__device__ __forceinline__ int flag_issue(uint32_t addr) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ int flag_ready(int v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v)::"memory");
+    return __builtin_amdgcn_readfirstlane(v);
+}
+// The smallest of n consecutive flags (n = 2 or 4, 8- or 16-byte aligned).
+template <int n> __device__ __forceinline__ int flag_min(uint32_t addr) {
+    static_assert(n == 2 || n == 4, "flag_min: 2 or 4 flags");
+    typedef __attribute__((ext_vector_type(n))) int vec;
+    vec x;
+    if constexpr (n == 4)
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+    else
+        asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+    int m = x[0] < x[1] ? x[0] : x[1];
+    if constexpr (n == 4) {
+        const int m2 = x[2] < x[3] ? x[2] : x[3];
+        m = m < m2 ? m : m2;
+    }
+    return __builtin_amdgcn_readfirstlane(m);
+}
+// Every wait on a flag is bounded: after FLAG_SPINS polls (~0.1 s of sleeping) it gives up, so a
+// protocol error can only give wrong numbers, never a wavefront that does not finish.
+constexpr int FLAG_SPINS = 1 << 21;
+__device__ __forceinline__ void flag_wait(uint32_t addr, int target) {
+    for (int it = 0; it < FLAG_SPINS && flag_get(addr) < target; ++it) __builtin_amdgcn_s_sleep(1);
+}
+template <int n> __device__ __forceinline__ void flag_wait_min(uint32_t addr, int target) {
+    for (int it = 0; it < FLAG_SPINS && flag_min<n>(addr) < target; ++it) __builtin_amdgcn_s_sleep(1);
+}
 
 __device__ __forceinline__ uint32_t lds_u32(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
@@ -979,13 +1026,13 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 
 // Tiling of the state pass for value width V. A workgroup owns VT value
 // columns of one (sequence, head): NW compute wavefronts of CT 16-column tiles
-// each, NL = D-1 loader wavefronts and a ring of D sub-tile slots in LDS (each
-// slot = the sub-tile's workspace block plus its v tile). Every operand a
-// compute wavefront reads from LDS serves its CT products (LDS read
-// throughput per wavefront is what bounds a step); 64-token chunks carry the
-// chunk's earlier corrected values in registers and use one tile per
-// wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ... so it never has
-// more than one in flight; a sub-tile is copied NL steps before use.
+// each, NL loader wavefronts and a ring of D sub-tile slots in LDS (each slot =
+// the sub-tile's workspace block plus its v tile), followed by the progress
+// flags. Every operand a compute wavefront reads from LDS serves its CT
+// products (LDS read throughput per wavefront is what bounds a step); 64-token
+// chunks carry the chunk's earlier corrected values in registers and use one
+// tile per wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ..., one at a
+// time, each as soon as its slot is free.
 template <bool BF, int K, int V, int CS>
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
@@ -1004,19 +1051,29 @@ struct StateCfg {
     static constexpr int U = KU + VU;              // 1 KiB copies per sub-tile
     static constexpr int SLOT = U * 1024;
     static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
-    static constexpr int OBUF = 2 * 16 * OPITCH * 4;
-    static constexpr int DFIT = (160 * 1024 - OBUF) / SLOT;
+    static constexpr int OROWS = 16 * OPITCH * 4;  // one sub-tile's o rows
+    // flags: ready[8] (loader k: 1 + the last sub-tile it landed), done[8] (compute wavefront w:
+    // steps finished), ostored[8] (loader k: 1 + the last sub-tile whose o rows it wrote out)
+    static constexpr int FLAGS = 96;
+    static constexpr int DFIT = (160 * 1024 - FLAGS - 2 * OROWS) / SLOT;
     // at most 8 wavefronts (two per SIMD) keeps 256 registers per lane. A loader has one
-    // sub-tile in flight, issued after barrier B_{v-D+1} and awaited before B_{v-1}; its next
-    // one is issued after B_{v-D+1+NL}, so the ring may be one slot deeper than there are
-    // loaders.
+    // sub-tile in flight; the ring holds the slot being computed on, the next one (read a step
+    // ahead) and the loaders' copies.
     static constexpr int NLMAX = 8 - NW;
     static constexpr int DMAX = NLMAX + 2 < 6 ? NLMAX + 2 : 6;
     static constexpr int D = DFIT > DMAX ? DMAX : DFIT;
     static constexpr int NL = D - 1 < NLMAX ? D - 1 : NLMAX;
     static constexpr int THREADS = (NW + NL) * 64;
-    static constexpr int LDS = D * SLOT + OBUF;
+    // o staging buffers: sub-tile v's rows go to buffer v % NB (2 or 3, as LDS allows); a compute
+    // wavefront may run NB - 1 steps ahead of the slowest one
+    static constexpr int NBFIT = (160 * 1024 - FLAGS - D * SLOT) / OROWS;
+    static constexpr int NB = NBFIT > 3 ? 3 : NBFIT;
+    static constexpr int OBUF = NB * OROWS;
+    static constexpr int LDS = D * SLOT + OBUF + FLAGS;
+    static_assert(NB >= 2, "two o buffers at least");
     static_assert(D >= 3, "ring too shallow");
+    static_assert(NW == 2 || NW == 4, "flag_min reads 2 or 4 done flags");
+    static_assert(NL <= 8, "eight ready flags");
 };
 
 // [A | B] stacking of two 4-slot operands into one 8-slot operand.
@@ -1070,7 +1127,6 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     const int32_t H = pa.H, N = pa.N;
     const ChunkTab &tab = pa.tab;
     const char *__restrict__ frags = pa.frags;
-    float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
 
     // bid -> (sequence * H + head, column tile). Workgroups are dealt to the 8 XCDs round-robin
     // by index; the NT tiles of one head share an XCD (blocks 8 apart), so the workspace blocks
@@ -1089,13 +1145,13 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     float *__restrict__ Sfin = (empty || c1 == c1n) ? pa.Sfin : pa.Scarry;
     const int64_t s0 = tab.tok(n) + (int64_t)(c0 - c0n) * (CS * SUB), s1 = tab.tok(n + 1);
 
-    // write sub-tile u's staged o rows (fp32 in obuf[u & 1]) to global memory, 16 bytes per lane
-    // (done by the loader wavefronts between B_{u+2} and B_{u+3}: the compute wavefronts stage
-    // them after B_{u+1} and next overwrite obuf[u & 1] after B_{u+3})
+    // o rows of sub-tile v: staged (fp32) to obuf[v % NB] by the compute wavefronts during step
+    // v+1, written out by loader v % NL
+    float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
     auto store_o = [&](int u, int t0, int nthreads) {
         const int64_t tok0 = s0 + (int64_t)u * SUB;
         const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
-        const float *ob = obuf + (u & 1) * 16 * C::OPITCH;
+        const float *ob = obuf + (u % C::NB) * 16 * C::OPITCH;
         if (o_bf16) {
             constexpr int UPR = VT / 8;
             for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
@@ -1121,6 +1177,15 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         }
     };
 
+    // Progress flags (no workgroup barrier after this point): ready[k] = 1 + the last sub-tile
+    // loader k has landed in the ring; done[w] = steps compute wavefront w has finished (its
+    // reads of those slots are done and their o rows staged, up to one step back); ostored[k] =
+    // 1 + the last sub-tile whose staged o rows loader k has read out.
+    const uint32_t fl = lds_u32(smem) + (uint32_t)(D * C::SLOT + C::OBUF);
+    const uint32_t ready0 = fl, done0 = fl + 32, ostored0 = fl + 64;
+    if (w == 0 && lane < 24) flag_put(fl + 4 * lane, 0);
+    lds_done_barrier();  // the only workgroup barrier
+
     if (w >= NW) {
         // ---------------- loader wavefront k: copies sub-tiles k (mod NL) into the ring
         const int k = w - NW;
@@ -1144,24 +1209,33 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                 dma16(slot + (uint32_t)((C::KU + q) * 1024), src);
             }
         };
-        // Barrier B_u certifies sub-tiles u and u+1 (the compute wavefronts read u+1's first
-        // operands during step u) and frees the slot of sub-tile u-1.
-        if (nu > 0) {
-            // sub-tiles 0 .. D-2 before the loop (a loader may start with two in flight: its first
-            // wait covers both)
-            for (int u = k; u < nu && u < D - 1; u += NL) issue(u);
-            const int lt = threadIdx.x - NW * 64;
-            for (int u = 0; u < nu; ++u) {
-                if ((u == 0 && k == 0) || (u + 1 < nu && (u + 1) % NL == k))
-                    wait_copies();              // sub-tile u+1 (or 0)
-                lds_done_barrier();             // B_u (the o rows read before it are done)
-                if (((u + D - 1) % NL) == k && u + D - 1 < nu) issue(u + D - 1);
-                if (u > 1) store_o(u - 2, lt, NL * 64);
+        // Loader k copies sub-tiles x = k, k+NL, ... (x to slot x % D once every compute
+        // wavefront has finished sub-tile x - D, the slot's previous tenant; one copy in flight)
+        // and writes out the o rows of sub-tiles v = k, k+NL, ... (once every compute wavefront
+        // has staged them), whichever is possible first. Neither kind of work waits on the
+        // other, so no wait closes a cycle; every wait is bounded.
+        int x = k, v = k, idle = 0;
+        while ((x < nu || v < nu) && idle < FLAG_SPINS) {
+            const int md = flag_min<NW>(done0);
+            bool did = false;
+            if (v < nu && md >= v + 2) {
+                store_o(v, lane, 64);
+                flag_put(ostored0 + 4 * k, v + 1);  // after the staged rows were read (in order)
+                v += NL;
+                did = true;
             }
-            lds_done_barrier();                 // B_nu
-            if (nu > 1) store_o(nu - 2, lt, NL * 64);
-            lds_done_barrier();                 // B_{nu+1}
-            store_o(nu - 1, lt, NL * 64);
+            if (x < nu && (x < D || md >= x - D + 1)) {
+                issue(x);
+                wait_copies();
+                flag_put(ready0 + 4 * k, x + 1);
+                x += NL;
+                did = true;
+            }
+            if (did) idle = 0;
+            else {
+                ++idle;
+                __builtin_amdgcn_s_sleep(1);
+            }
         }
         return;
     }
@@ -1268,21 +1342,28 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     // (bf16: [Wh | Wh] and [Wl | Wl]; fp32: [W | 0] in whist)
     Frag4<BF> vhist[CS][CT];
     Frag8<BF> whist[CS][CT], wlist[CS][CT];
-    // o rows of a step: computed in step u, staged to obuf[u & 1] right after barrier B_{u+1},
-    // stored to global memory by the loader wavefronts after B_{u+2}
+    // o rows of a step: computed in step u, staged to obuf[u % NB] during step u+1 (once the
+    // loader has read out sub-tile u - NB from that buffer)
     f32x4 O[CT];
     auto write_o = [&](int uu) {
         if constexpr (!BF) {
             if constexpr (CT == 2) mfma_fence(O[0], O[CT - 1]);
             else mfma_fence(O[0]);
         }
-        float *ob = obuf + (uu & 1) * 16 * C::OPITCH;
+        float *ob = obuf + (uu % C::NB) * 16 * C::OPITCH;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (CT == 2)
                 *reinterpret_cast<float2 *>(ob + (4 * tg + i) * C::OPITCH + lc) = make_float2(O[0][i], O[CT - 1][i]);
             else ob[(4 * tg + i) * C::OPITCH + lc] = O[0][i];
         }
+    };
+    // The flags a step needs are fetched with the previous step's operand reads and checked when
+    // those are waited for; only if one is not yet set does the wavefront poll.
+    auto ready_addr = [&](int x) { return ready0 + 4 * (uint32_t)(x % NL); };
+    auto ostored_addr = [&](int vv) { return ostored0 + 4 * (uint32_t)(vv % NL); };
+    auto need = [&](int fetched, uint32_t addr, int target) {
+        if (flag_ready(fetched) < target) flag_wait(addr, target);
     };
     // pack state rows 32s .. 32s+31 (tiles 2s, 2s+1) of every column tile into the bf16 operand
     auto pack_pair = [&](int s) {
@@ -1320,10 +1401,12 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         if constexpr (CT == 2) mfma_fence(S[0][2 * s], S[0][2 * s + 1], S[1][2 * s], S[1][2 * s + 1]);
         else mfma_fence(S[0][2 * s], S[0][2 * s + 1]);
     };
+    int f_ready = 0, f_ost = 0;  // flags fetched for the coming step
     if (nu > 0) {
-        wg_barrier();  // B_0
+        flag_wait(ready0, 1);  // sub-tile 0 (loader 0)
 #pragma unroll
         for (int part = 0; part < 4; ++part) read_ahead(smem, part);
+        f_ready = flag_issue(ready_addr(1));
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) O[ct] = zero4();
@@ -1331,6 +1414,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         const int R = CS == 1 ? 0 : (u & (CS - 1));
         const bool repack = R == CS - 1;  // the state operand is renewed after a chunk's last sub-tile
         const char *sl = smem + (u % D) * C::SLOT;
+        // sub-tile u+1 (read ahead in phase C) has landed; the o buffer of sub-tile u-1 is free
+        if (u + 1 < nu) need(f_ready, ready_addr(u + 1), u + 2);
+        if (u - 1 - C::NB >= 0) need(f_ost, ostored_addr(u - 1 - C::NB), u - C::NB);
         make_vf();
 #pragma unroll
         for (int I = 0; I < CS; ++I)
@@ -1357,10 +1443,8 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
         }
-        // the previous step's o rows, staged ahead of this step's reads (which the step consumes,
-        // so the rows are in LDS by the next barrier). At u = 0 this stages zeros into obuf[1],
-        // which step 1 overwrites before any loader reads it.
-        write_o(u - 1);
+        // the previous step's o rows (in LDS before this step's done flag)
+        if (u > 0) write_o(u - 1);
         constexpr int NKP = BF ? KT : KT / 2;  // bf16: [hi | lo] of tile rt; fp32: tiles 2p, 2p+1
         Frag8<BF> kp2[NKP];
 #pragma unroll
@@ -1432,8 +1516,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 
         // ---- phase C: S <- diag(Gamma_C) S (a chunk's first sub-tile) + Kp^T W, one pair of state
         // row tiles at a time; the bf16 operand of a pair is renewed while the next pair's
-        // products run, and the next step's first operands are read (slot of sub-tile u+1,
-        // certified at B_u; after the last step the reads are of a stale slot and unused)
+        // products run, and the next step's first operands are read (slot of sub-tile u+1, once
+        // its loader has published it; after the last step the reads are of a stale slot and
+        // unused)
         const char *sl_next = smem + ((u + 1) % D) * C::SLOT;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -1470,6 +1555,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        // the flags of step u+1, queued behind its operand reads
+        f_ready = flag_issue(ready_addr(u + 2));
+        f_ost = flag_issue(ostored_addr(u >= C::NB ? u - C::NB : 0));
+
         // ---- phase D: O += sum_{I<=R} P_RI W_I; the last pair of the state operand
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -1491,15 +1580,14 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             pin_pair(KS - 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // B_{u+1}. No LDS wait is needed before it: every read of the slot it frees (sub-tile u)
-        // was consumed by an instruction of this step, and the o rows staged in this step were
-        // followed by reads the step consumed (a wavefront's LDS operations complete in order).
-        // Only the next step's first operands may still be in flight.
-        wg_barrier();
+        // step u done: every read of slot u was issued before this (and consumed by a product of
+        // this step); only the next step's first operands may still be in flight
+        flag_put(done0 + 4 * w, u + 1);
     }
     if (nu > 0) {
+        if (nu - 1 - C::NB >= 0) flag_wait(ostored_addr(nu - 1 - C::NB), nu - C::NB);
         write_o(nu - 1);
-        lds_done_barrier();       // B_{nu+1}: the loader wavefronts store the last o rows
+        flag_put(done0 + 4 * w, nu + 1);  // the last o rows are staged
     }
     if (Sfin) {
 #pragma unroll
