@@ -47,10 +47,11 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay"):
+def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False):
     lib = _lib.load()
     gc = _lib.GATES[gate]
-    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"))
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"), with_o_gate=o_gate)
+    og = inp["o_gate"].data_ptr() if o_gate else None
     B, T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
     N = B
@@ -67,11 +68,11 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay"):
                                       ws.data_ptr(), wsb, sh), "kda_chunk_prep")
 
     def state():
-        _lib.check(lib.kda_chunk_state(p["v"], None, None, B, T, H, K, V, N, chunk, 1, 1, o.data_ptr(),
+        _lib.check(lib.kda_chunk_state(p["v"], og, None, None, B, T, H, K, V, N, chunk, 1, 1, o.data_ptr(),
                                        Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
 
     def fwd():
-        _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, B, T, H, K, V, N, chunk,
+        _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, None, None, B, T, H, K, V, N, chunk,
                                      1, gc, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
 
     # the step: one kda_chunk_fwd call (where the state pass leaves CUs free, the library runs the
@@ -285,6 +286,16 @@ def main():
                          "tokens_per_s": rg["B"] * rg["T"] / (msg * 1e-3), "ms_per_step": msg,
                          "kernels_ms": {"kda_chunk_prep (+chunk table)": rg["prep_ms"],
                                         "kda_state_pass": rg["state_ms"]}}
+    print("[bench] prefill %s with both gates formed in-kernel: warmup %d, steps %d" % (w.name, args.warmup,
+                                                                                      args.steps),
+          file=sys.stderr, flush=True)
+    ro = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True)
+    mso = ro["wall_s"] * 1e3 / args.steps
+    out["gates_fused"] = {"workload": "as gate_fused, plus an output gate: o * sigmoid(z), z [B,T,H,V] bf16 read "
+                                      "and applied where kda_state_pass stores o",
+                          "tokens_per_s": ro["B"] * ro["T"] / (mso * 1e-3), "ms_per_step": mso,
+                          "kernels_ms": {"kda_chunk_prep (+chunk table)": ro["prep_ms"],
+                                         "kda_state_pass": ro["state_ms"]}}
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
         print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)

@@ -106,6 +106,13 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *                            finite g is valid.
  *   v         [B, T, H, V]
  *   beta      [B, T, H]      write strength, used as given
+ *   o_gate    [B, T, H, V] or NULL: the output gate's pre-activation z. When
+ *             given, each output is scaled channel by channel,
+ *             o_t = (S_t^T q_t) * sigmoid(z_t), computed in fp32 before the
+ *             store (the input-dependent, full-rank channel gate of the first
+ *             page's paragraph "K3 对 Kimi Linear 的进一步修改"; the pages do not
+ *             name its activation, and sigmoid is read as the gate's plain
+ *             form). S_final does not depend on it.
  *   S0        [num_seqs, H, K, V] fp32, or NULL for a zero initial state
  *   cu_seqlens int32 [num_seqs + 1] or NULL. With it, B must be 1 and
  *              sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of
@@ -127,7 +134,7 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                           const float *S0, const int32_t *cu_seqlens,
+                           const void *o_gate, const float *S0, const int32_t *cu_seqlens,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                            int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype,
                            void *o, float *S_final, void *workspace, size_t workspace_bytes,
@@ -151,7 +158,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  *   the library). Reads q, k, g (as `gate` says), beta; V only sizes the
  *   workspace check.
  * kda_chunk_state: the sequential pass over the chunks of each (sequence,
- *   head): carries S from S0 (or 0), writes o and S_final. Reads v, S0 and a
+ *   head): carries S from S0 (or 0), writes o (gated by o_gate, if given) and
+ *   S_final. Reads v, o_gate, S0 and a
  *   workspace that kda_chunk_prep filled with the same sizes and the same
  *   cu_seqlens pointer (used here only to tell packed from batched input;
  *   not dereferenced). The workspace may not be modified in between.
@@ -161,7 +169,7 @@ kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const v
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
                             size_t workspace_bytes, void *stream);
-kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
+kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                              kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
                              size_t workspace_bytes, void *stream);
@@ -172,13 +180,14 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
  * ("S_t = Update(S_{t-1}, k_t, v_t)", second page cited above).
  *   q, k, g [N, H, K]; v [N, H, V]; beta [N, H]      dtype `io`
  *   g       as `gate` says
+ *   o_gate  [N, H, V] or NULL: output gate pre-activation, as for kda_chunk_fwd
  *   S       [N, H, K, V] fp32, read and overwritten in place
  *   o       [N, H, V] in `o_dtype`
  * Any finite g is accepted (no chunk-range assumption). S may not alias any
  * other argument. Errors as for kda_chunk_fwd.
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                             float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
+                             const void *o_gate, float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
                              kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype, void *stream);
 
 #ifdef __cplusplus

@@ -66,14 +66,15 @@ def _gate_code(gate: str) -> int:
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
-              output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay"):
+              output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
     [num_seqs, H, K, V]. ``workspace`` (uint8 CUDA tensor) and ``out`` may be
     passed to avoid allocations. ``gate`` says what ``g`` holds: "log_decay"
     (the log-decay itself) or "scaled_sigmoid" (the gate pre-activation,
-    mapped to -5*sigmoid(g) inside the kernels).
+    mapped to -5*sigmoid(g) inside the kernels). ``o_gate`` [B, T, H, V] (input
+    dtype), if given, scales the output channel by channel: o * sigmoid(o_gate).
     """
     lib = _lib.load()
     dev = q.device
@@ -87,6 +88,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("v", v, (B, T, H, V)),
                          ("beta", beta, (B, T, H))):
         _need(t, name, shp, dt, dev)
+    if o_gate is not None:
+        _need(o_gate, "o_gate", (B, T, H, V), dt, dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
         N = cu_seqlens.numel() - 1
@@ -107,17 +110,18 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
                        % (B, T, H, K, V, N, chunk))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+    status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0),
+                               _ptr(cu_seqlens),
                                B, T, H, K, V, N, chunk, io, gc, _io_code(odt), _ptr(out), _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(status, "kda_chunk_fwd")
     return out, S_final
 
 
-def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay"):
+def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay", o_gate=None):
     """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V].
 
-    ``gate`` as for :func:`chunk_fwd`.
+    ``gate`` and ``o_gate`` ([N, H, V]) as for :func:`chunk_fwd`.
     """
     lib = _lib.load()
     dev = q.device
@@ -131,12 +135,14 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
     for name, t, shp in (("k", k, (N, H, K)), ("g", g, (N, H, K)), ("v", v, (N, H, V)), ("beta", beta, (N, H))):
         _need(t, name, shp, dt, dev)
     _need(S, "S", (N, H, K, V), torch.float32, dev)
+    if o_gate is not None:
+        _need(o_gate, "o_gate", (N, H, V), dt, dev)
     odt = dt if o_dtype is None else (_NAME[o_dtype] if isinstance(o_dtype, str) else o_dtype)
     if out is None:
         out = torch.empty((N, H, V), dtype=odt, device=dev)
     else:
         _need(out, "out", (N, H, V), odt, dev)
-    status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(out),
+    status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S), _ptr(out),
                                  N, H, K, V, io, gc, _io_code(odt), _stream(dev))
     _lib.check(status, "kda_decode_step")
     return out

@@ -21,7 +21,7 @@ STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPP
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_prep", "kda_chunk_state", "kda_decode_step")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 _lib = None
 
 
@@ -51,16 +51,16 @@ def load() -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
-    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int,
                                    ctypes.c_int, vp, sz, vp]
     lib.kda_chunk_prep.restype = ctypes.c_int
-    lib.kda_chunk_state.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
+    lib.kda_chunk_state.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                     vp, vp, vp, sz, vp]
     lib.kda_chunk_state.restype = ctypes.c_int
-    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     _lib = lib

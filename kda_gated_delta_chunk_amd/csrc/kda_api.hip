@@ -57,7 +57,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 2; }
+int kda_abi_version(void) { return 3; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -85,7 +85,7 @@ namespace {
 // Validation shared by the prefill entry points. `need_*` select which
 // pointers the entry point reads or writes.
 kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                          const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
+                          const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
                           int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
                           kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
                           size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
@@ -95,7 +95,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (st != KDA_SUCCESS) return st;
     if (T > 0 && need_prep && (!q || !k || !g || !beta)) return KDA_ERROR_INVALID_VALUE;
     if (T > 0 && need_state && (!v || !o)) return KDA_ERROR_INVALID_VALUE;
-    const void *ptrs[] = {q, k, v, g, S0, o, S_final, workspace};
+    const void *ptrs[] = {q, k, v, g, o_gate, S0, o, S_final, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
     if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
@@ -106,7 +106,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o_gate = o_gate;
     a.S0 = S0; a.cu_seqlens = cu_seqlens;
     a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
     a.io_bf16 = io == KDA_DTYPE_BF16;
@@ -120,12 +120,12 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
 }  // namespace
 
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                           const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
+                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
                            int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                            kda_gate_t gate, kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
                            size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
-    kda_status_t st = prefill_args(q, k, v, g, beta, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
+    kda_status_t st = prefill_args(q, k, v, g, beta, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
                                    o_dtype, o, S_final, workspace, workspace_bytes, true, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
@@ -137,19 +137,20 @@ kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const v
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
                             size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
-    kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
+    kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
                                    gate, io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }
 
-kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
+kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens,
+                             int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                              kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
                              size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
-    kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, S0, cu_seqlens, B, T, H, K, V, num_seqs,
+    kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs,
                                    chunk, io, KDA_GATE_LOG_DECAY, o_dtype, o, S_final, workspace, workspace_bytes,
                                    false, true, a);
     if (st != KDA_SUCCESS) return st;
@@ -157,7 +158,8 @@ kda_status_t kda_chunk_state(const void *v, const float *S0, const int32_t *cu_s
     return KDA_SUCCESS;
 }
 
-kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta, float *S,
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             const void *o_gate, float *S,
                              void *o, int32_t N, int32_t H, int32_t K, int32_t V, kda_dtype_t io,
                              kda_gate_t gate, kda_dtype_t o_dtype, void *stream) {
     if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
@@ -169,14 +171,15 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     const void *ptrs[] = {q, k, v, g, S, o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (o_gate && !aligned16(o_gate)) return KDA_ERROR_INVALID_VALUE;
     if (!aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if ((const void *)S == q || (const void *)S == k || (const void *)S == v || (const void *)S == g ||
-        (const void *)S == beta || (const void *)S == o)
+        (const void *)S == beta || (const void *)S == o || (const void *)S == o_gate)
         return KDA_ERROR_INVALID_VALUE;
     kda_status_t st = check_device();
     if (st != KDA_SUCCESS) return st;
     kda::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o_gate = o_gate;
     a.S = S; a.o = o;
     a.N = N; a.H = H; a.K = K; a.V = V;
     a.io_bf16 = io == KDA_DTYPE_BF16;

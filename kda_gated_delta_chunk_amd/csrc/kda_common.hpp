@@ -205,6 +205,11 @@ __device__ __forceinline__ float gate_log2_decay(float x) {
     return (-5.f * L2E) * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * L2E));
 }
 
+// 1 / (1 + e^-x) in fp32 (the output gate's activation); exactly 0 below about -88, 1 for large x.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 // I/O element access by dtype.
 template <bool BF> struct IO;
 template <> struct IO<true> {

@@ -10,9 +10,13 @@
 //   S  = S' + beta k delta^T,          o = S^T q = y + beta (k.q) delta
 // Everything is one read and one write of S: both reductions (u and y) are
 // taken in the same pass over S', so the state makes exactly one round trip
-// through HBM and o needs no second pass. g is either the log-decay itself or
-// the gate pre-activation, mapped here through the bounded scaled sigmoid of
-// the first page's paragraph "K3 对 Kimi Linear 的进一步修改".
+// through HBM and o needs no second pass.
+//
+// Two gates of the first page's paragraph "K3 对 Kimi Linear 的进一步修改" can be
+// formed here: g is either the log-decay itself or the decay gate's
+// pre-activation, mapped through the scaled sigmoid bounded below by -5; and
+// an optional output gate z (the input-dependent, full-rank channel gate)
+// scales o channel by channel as o * sigmoid(z).
 //
 // One 256-thread workgroup per (n, h). Thread t owns 4 adjacent value columns
 // (one 16-byte vector) of K*V/1024 rows; the rows of a wavefront's load
@@ -28,7 +32,7 @@ namespace kda {
 template <bool BF, int K, int V>
 __global__ __launch_bounds__(256) void kda_decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
-    const void *__restrict__ gp, const void *__restrict__ bp, float *__restrict__ S,
+    const void *__restrict__ gp, const void *__restrict__ bp, const void *__restrict__ zp, float *__restrict__ S,
     void *__restrict__ op, int o_bf16, int gate, int32_t NH) {
     constexpr int CG = V / 4;          // column groups (float4) per row
     constexpr int RG = 256 / CG;       // row groups
@@ -121,6 +125,11 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     }
     if (rg == 0) {
         const size_t ob = (size_t)nh * V + 4 * cg;
+        if (zp) {  // output gate: o * sigmoid(z)
+            const E *z = reinterpret_cast<const E *>(zp) + ob;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] *= sigmoid_f(IO<BF>::ld(z, c));
+        }
         if (o_bf16) {
             uint16_t *ot = reinterpret_cast<uint16_t *>(op) + ob;
             *reinterpret_cast<uint2 *>(ot) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
@@ -142,9 +151,9 @@ hipError_t launch_dk(const DecodeArgs &a, hipStream_t st) {
     const int32_t NH = a.N * a.H;
     const dim3 grid(NH), block(256);
     switch (a.V) {
-        case 32: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 32>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
-        case 64: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 64>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
-        default: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 128>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
+        case 32: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 32>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
+        case 64: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 64>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
+        default: hipLaunchKernelGGL((kda_decode_kernel<BF, K, 128>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta, a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH); break;
     }
     return hipGetLastError();
 }

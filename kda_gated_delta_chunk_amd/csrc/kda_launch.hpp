@@ -10,6 +10,7 @@ namespace kda {
 
 struct PrefillArgs {
     const void *q, *k, *v, *g, *beta;
+    const void *o_gate;    // [B,T,H,V] output-gate pre-activation in the I/O dtype, or null
     const float *S0;
     const int32_t *cu_seqlens;
     int64_t B, T;
@@ -37,6 +38,7 @@ hipError_t launch_fwd(const PrefillArgs &a, hipStream_t stream);
 
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
+    const void *o_gate;    // [N,H,V] output-gate pre-activation in the I/O dtype, or null
     float *S;
     void *o;
     int32_t N, H, K, V;

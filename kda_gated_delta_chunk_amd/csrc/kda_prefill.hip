@@ -48,6 +48,7 @@
 // fp32 I/O runs the same code with fp32 operands on v_mfma_f32_16x16x4_f32.
 
 #include "kda_common.hpp"
+#include <type_traits>
 
 namespace kda {
 
@@ -1102,6 +1103,7 @@ template <bool BF> __device__ __forceinline__ Frag4<BF> zero_frag4() {
 // launch that covers range 0 (`first`).
 struct StateParams {
     const void *v;
+    const void *ogate;  // output-gate pre-activation [tokens][H][V] (I/O dtype), or null
     const float *S0;
     void *o;
     int32_t o_bf16;
@@ -1146,36 +1148,80 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     const int64_t s0 = tab.tok(n) + (int64_t)(c0 - c0n) * (CS * SUB), s1 = tab.tok(n + 1);
 
     // o rows of sub-tile v: staged (fp32) to obuf[v % NB] by the compute wavefronts during step
-    // v+1, written out by loader v % NL
+    // v+1, written out by loader v % NL (times sigmoid of the output gate, where one is given)
     float *obuf = reinterpret_cast<float *>(smem + D * C::SLOT);
-    auto store_o = [&](int u, int t0, int nthreads) {
+    const void *__restrict__ ogp = pa.ogate;
+    // Output gate: the pre-activations of the o values a loader lane writes out for sub-tile v,
+    // loaded one write-out ahead. A lane's write-out items are idx = lane + 64 j: runs of RUN
+    // columns (8 with a bf16 o, 4 with fp32), 16 gate values per lane in either case.
+    float gz[16];
+    using Run8 = std::integral_constant<int, 8>;
+    using Run4 = std::integral_constant<int, 4>;
+    auto load_gate_run = [&](int u, auto run_c) {
+        constexpr int RUN = decltype(run_c)::value, UPR = VT / RUN, J = 16 * UPR / 64;
+        static_assert(J * 64 == 16 * UPR && J * RUN <= 16, "write-out items per lane");
+        const int64_t tok0 = s0 + (int64_t)u * SUB;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int idx = lane + 64 * j, row = idx / UPR, c = (idx % UPR) * RUN;
+            const int64_t tok = tok0 + row < s1 ? tok0 + row : s1 - 1;  // rows past the end re-read a valid one
+            const int64_t e = (tok * H + h) * V + tile * VT + c;
+#pragma unroll
+            for (int q4 = 0; q4 < RUN; q4 += 4) {
+                if constexpr (BF) {
+                    const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(ogp) + e + q4);
+                    gz[RUN * j + q4] = bf_lo(r.x); gz[RUN * j + q4 + 1] = bf_hi(r.x);
+                    gz[RUN * j + q4 + 2] = bf_lo(r.y); gz[RUN * j + q4 + 3] = bf_hi(r.y);
+                } else {
+                    const float4 z = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(ogp) + e + q4);
+                    gz[RUN * j + q4] = z.x; gz[RUN * j + q4 + 1] = z.y; gz[RUN * j + q4 + 2] = z.z; gz[RUN * j + q4 + 3] = z.w;
+                }
+            }
+        }
+    };
+    auto load_gate = [&](int u) {
+        if (!ogp || u >= nu) return;
+        if (o_bf16) load_gate_run(u, Run8{});
+        else load_gate_run(u, Run4{});
+    };
+    auto gate_mul = [&](float4 &a, int i) {
+        a.x *= sigmoid_f(gz[i]); a.y *= sigmoid_f(gz[i + 1]); a.z *= sigmoid_f(gz[i + 2]); a.w *= sigmoid_f(gz[i + 3]);
+    };
+    auto store_o = [&](int u) {
         const int64_t tok0 = s0 + (int64_t)u * SUB;
         const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
         const float *ob = obuf + (u % C::NB) * 16 * C::OPITCH;
         if (o_bf16) {
-            constexpr int UPR = VT / 8;
-            for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
-                const int row = idx / UPR, c8 = (idx % UPR) * 8;
+            constexpr int UPR = VT / 8, J = 16 * UPR / 64;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int idx = lane + 64 * j, row = idx / UPR, c8 = (idx % UPR) * 8;
                 if (row < nval) {
-                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
-                    const float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
+                    float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8);
+                    float4 b = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c8 + 4);
+                    if (ogp) {
+                        gate_mul(a, 8 * j);
+                        gate_mul(b, 8 * j + 4);
+                    }
                     uint16_t *dst = reinterpret_cast<uint16_t *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c8;
                     *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w),
                                                                  pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
                 }
             }
         } else {
-            constexpr int UPR = VT / 4;
-            for (int idx = t0; idx < 16 * UPR; idx += nthreads) {
-                const int row = idx / UPR, c4 = (idx % UPR) * 4;
+            constexpr int UPR = VT / 4, J = 16 * UPR / 64;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int idx = lane + 64 * j, row = idx / UPR, c4 = (idx % UPR) * 4;
                 if (row < nval) {
-                    const float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
-                    float *dst = reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c4;
-                    *reinterpret_cast<float4 *>(dst) = a;
+                    float4 a = *reinterpret_cast<const float4 *>(ob + row * C::OPITCH + c4);
+                    if (ogp) gate_mul(a, 4 * j);
+                    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(op) + ((tok0 + row) * H + h) * V + tile * VT + c4) = a;
                 }
             }
         }
     };
+
 
     // Progress flags (no workgroup barrier after this point): ready[k] = 1 + the last sub-tile
     // loader k has landed in the ring; done[w] = steps compute wavefront w has finished (its
@@ -1214,14 +1260,18 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // and writes out the o rows of sub-tiles v = k, k+NL, ... (once every compute wavefront
         // has staged them), whichever is possible first. Neither kind of work waits on the
         // other, so no wait closes a cycle; every wait is bounded.
+        // The output-gate loads of the next write-out are issued right after a write-out, so they
+        // are in flight together with the next copy and its vmcnt(0) wait covers both.
         int x = k, v = k, idle = 0;
+        load_gate(v);
         while ((x < nu || v < nu) && idle < FLAG_SPINS) {
             const int md = flag_min<NW>(done0);
             bool did = false;
             if (v < nu && md >= v + 2) {
-                store_o(v, lane, 64);
+                store_o(v);
                 flag_put(ostored0 + 4 * k, v + 1);  // after the staged rows were read (in order)
                 v += NL;
+                load_gate(v);
                 did = true;
             }
             if (x < nu && (x < D || md >= x - D + 1)) {
@@ -1714,7 +1764,7 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
 
 StateParams state_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first) {
     StateParams p;
-    p.v = a.v; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
+    p.v = a.v; p.ogate = a.o_gate; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
     p.H = a.H; p.N = a.num_seqs;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;

@@ -14,6 +14,8 @@ Distributions (the workloads of the spec configurations):
           calls that form the log-decay from the pre-activation
   beta  = sigmoid(x), x ~ N(0, 1) per (token, head)
   S0    ~ N(0, 0.02^2) (standard deviation 0.02), fp32
+  o_gate ~ N(0, 1) per (token, head, value channel), where asked for: the
+          output gate's pre-activation
 All draws are fp32 and then rounded to the I/O dtype with round-to-nearest-
 even (torch ``.to``). Generation is block-seeded over tokens so a
 million-token batch never needs more than one block of fp32 temporaries; a
@@ -27,7 +29,7 @@ import numpy as np
 import torch
 
 # tensor ids used in the block seeds
-_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "lengths": 6}
+_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "lengths": 6, "o_gate": 7}
 
 DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -98,14 +100,15 @@ def cu_from_lengths(lengths) -> list[int]:
 def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0,
                    device="cpu", cu_seqlens=None, with_S0: bool = False, block_tokens: int = 65536,
                    g_shift: float = 0.0, g_const: float | None = None, beta_const: float | None = None,
-                   gate_preact: bool = False, g_scale: float = 1.0):
+                   gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False):
     """Inputs of one prefill call.
 
     Returns a dict with q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H] in the I/O
     dtype, S0 [N,H,K,V] fp32 (or None) and cu_seqlens int32 [N+1] (or None).
     ``g_shift`` moves the pre-sigmoid draw of g (e.g. -6 for mild decay);
     ``g_const``/``beta_const`` replace the draw by a constant (stress cases);
-    ``gate_preact`` stores the pre-sigmoid draw g_scale * x + g_shift itself.
+    ``gate_preact`` stores the pre-sigmoid draw g_scale * x + g_shift itself;
+    ``with_o_gate`` adds an output-gate pre-activation ``o_gate`` [B,T,H,V].
     """
     dt = DTYPES[io]
     dev = torch.device(device)
@@ -114,6 +117,7 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
     g = torch.empty_like(q)
     v = torch.empty((B, T, H, V), dtype=dt, device=dev)
     beta = torch.empty((B, T, H), dtype=dt, device=dev)
+    og = torch.empty((B, T, H, V), dtype=dt, device=dev) if with_o_gate else None
     flat = B * T
     qf, kf, gf = q.view(flat, H, K), k.view(flat, H, K), g.view(flat, H, K)
     vf, bf = v.view(flat, H, V), beta.view(flat, H)
@@ -127,6 +131,8 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
         kf[a:b] = kr.to(dt)
         del kr
         vf[a:b] = _randn((n, H, V), seed, "v", blk, dev).to(dt)
+        if og is not None:
+            og.view(flat, H, V)[a:b] = _randn((n, H, V), seed, "o_gate", blk, dev).to(dt)
         if g_const is not None:
             gf[a:b] = torch.full((n, H, K), float(g_const), device=dev).to(dt)
         elif gate_preact:
@@ -145,7 +151,7 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
     S0 = None
     if with_S0:
         S0 = 0.02 * _randn((N, H, K, V), seed, "S0", 0, dev)
-    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0, "cu_seqlens": cu}
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0, "cu_seqlens": cu, "o_gate": og}
 
 
 def workload_prefill_inputs(w: Workload, device="cpu", **kw):
@@ -159,9 +165,10 @@ def workload_prefill_inputs(w: Workload, device="cpu", **kw):
 
 
 def decode_inputs(N: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0, step: int = 0,
-                  device="cpu", gate_preact: bool = False, g_scale: float = 1.0):
+                  device="cpu", gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False):
     """Per-step decode inputs q, k, g [N,H,K], v [N,H,V], beta [N,H] (step = block id).
-    ``gate_preact``: g is the pre-sigmoid draw g_scale * x itself."""
+    ``gate_preact``: g is the pre-sigmoid draw g_scale * x itself; ``with_o_gate``: also an
+    output-gate pre-activation o_gate [N,H,V] (else None)."""
     dt = DTYPES[io]
     dev = torch.device(device)
     q = _randn((N, H, K), seed, "q", step, dev).to(dt)
@@ -171,7 +178,8 @@ def decode_inputs(N: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 
     x = _randn((N, H, K), seed, "g", step, dev)
     g = (g_scale * x if gate_preact else -5.0 * torch.sigmoid(x)).to(dt)
     beta = torch.sigmoid(_randn((N, H), seed, "beta", step, dev)).to(dt)
-    return {"q": q, "k": k, "v": v, "g": g, "beta": beta}
+    og = _randn((N, H, V), seed, "o_gate", step, dev).to(dt) if with_o_gate else None
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "o_gate": og}
 
 
 def decode_state(N: int, H: int, K: int, V: int, seed: int = 0, device="cpu") -> torch.Tensor:

@@ -87,19 +87,36 @@ def scaled_sigmoid_gate(x) -> np.ndarray:
         return -5.0 / (1.0 + np.exp(-x))
 
 
+def output_gate(o, z) -> np.ndarray:
+    """The output gate, in fp64: o * sigmoid(z), channel by channel.
+
+    "Kimi K3 发布核实与 Moonshot AI 主干架构演变", section 3, paragraph
+    "K3 对 Kimi Linear 的进一步修改": KDA's low-rank output gate became an
+    input-dependent, full-rank channel gate, one value per output channel and
+    token. The pages name no activation; sigmoid, the plain form of a gate, is
+    the reading taken. z is the gate's pre-activation (the projection that
+    makes it from the layer input is upstream of this path).
+    """
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return _f64(o) * (1.0 / (1.0 + np.exp(-z)))
+
+
 def _log_decay(g, gate: str) -> np.ndarray:
     if gate not in GATES:
         raise ValueError("gate must be one of %s" % (GATES,))
     return scaled_sigmoid_gate(g) if gate == "scaled_sigmoid" else _f64(g)
 
 
-def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate: str = "log_decay"):
+def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate: str = "log_decay",
+              o_gate=None):
     """Run the fp64 recurrence over whole sequences.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H];
     S0: [N, H, K, V] or None (zeros); cu_seqlens: [N+1] or None.
     gate: "log_decay" (g is the log-decay) or "scaled_sigmoid" (g is the gate
     pre-activation; the log-decay is scaled_sigmoid_gate(g)).
+    o_gate: [B, T, H, V] or None; if given, o is output_gate(o, o_gate).
     Returns (o [B, T, H, V], S_final [N, H, K, V]) as float64 arrays.
     """
     g = _log_decay(g, gate)
@@ -126,14 +143,18 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate
                                       B, T, H, K, V, N, _ptr(o), _ptr(sf), int(threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    if o_gate is not None:
+        if tuple(o_gate.shape) != o.shape:
+            raise ValueError("o_gate shape %s != %s" % (tuple(o_gate.shape), o.shape))
+        o = output_gate(o, o_gate)
     return o, sf
 
 
-def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay"):
+def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay", o_gate=None):
     """One decode step. q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H]; S: [N, H, K, V].
 
-    gate as for chunk_fwd. Returns (o [N, H, V], S_new [N, H, K, V]); the
-    input S is not modified.
+    gate and o_gate ([N, H, V] or None) as for chunk_fwd. Returns
+    (o [N, H, V], S_new [N, H, K, V]); the input S is not modified.
     """
     g = _log_decay(g, gate)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
@@ -147,6 +168,10 @@ def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay"):
                                    N, H, K, V, int(threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    if o_gate is not None:
+        if tuple(o_gate.shape) != o.shape:
+            raise ValueError("o_gate shape %s != %s" % (tuple(o_gate.shape), o.shape))
+        o = output_gate(o, o_gate)
     return o, S_new
 
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -63,10 +63,11 @@ def test_workspace_bytes():
 
 def _fwd(**kw):
     lib = _lib.load()
-    a = dict(q=A, k=A, v=A, g=A, beta=A, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
+    a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
              gate=0, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
     a.update(kw)
-    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"], a["T"], a["H"],
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["B"], a["T"],
+                             a["H"],
                              a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["odt"], a["o"], a["Sf"], a["ws"],
                              a["wsb"], a["stream"])
 
@@ -79,6 +80,7 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(o=None), INVALID),
     (dict(k=A + 8), INVALID),            # misaligned
     (dict(S0=A + 4), INVALID),
+    (dict(og=A + 8), INVALID),           # o_gate misaligned
     (dict(cu=A + 2), INVALID),
     (dict(beta=A + 1), INVALID),         # bf16 beta needs 2-byte alignment
     (dict(beta=A + 2, io=0, odt=0), INVALID),  # fp32 beta needs 4-byte alignment
@@ -106,10 +108,11 @@ def test_chunk_fwd_rejects(kw, expect):
 
 def _dec(**kw):
     lib = _lib.load()
-    a = dict(q=A, k=A, v=A, g=A, beta=A, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, gate=0, odt=1,
+    a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, gate=0, odt=1,
              stream=None)
     a.update(kw)
-    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["o"], a["N"], a["H"], a["K"],
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S"], a["o"], a["N"], a["H"],
+                               a["K"],
                                a["V"], a["io"], a["gate"], a["odt"], a["stream"])
 
 
@@ -118,6 +121,8 @@ def _dec(**kw):
     (dict(beta=None), INVALID),
     (dict(v=A + 2), INVALID),
     (dict(S=A), INVALID),                 # S aliases q
+    (dict(og=A + 4096), INVALID),         # S aliases o_gate
+    (dict(og=A + 2), INVALID),            # o_gate misaligned
     (dict(N=-1), INVALID),
     (dict(H=0), INVALID),
     (dict(io=3), INVALID),

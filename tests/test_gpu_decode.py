@@ -15,20 +15,23 @@ def _announce(name, **kw):
     print("\n[case] %s %s" % (name, " ".join("%s=%s" % kv for kv in kw.items())), flush=True)
 
 
-def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0):
+def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0, o_gate=False):
     S = synth.decode_state(N, H, K, V, seed=seed, device=DEV)
     S_ref = S.double().cpu().numpy()
     worst = {"o": 0.0, "S": 0.0}
     pre = gate == "scaled_sigmoid"
     for step in range(steps):
-        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV, gate_preact=pre, g_scale=g_scale)
+        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV, gate_preact=pre, g_scale=g_scale,
+                                  with_o_gate=o_gate)
         args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+        og = inp["o_gate"]
         S32 = S.clone()
-        o = decode_step(*args, S, gate=gate)
-        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate)
+        o = decode_step(*args, S, gate=gate, o_gate=og)
+        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate, o_gate=og)
         torch.cuda.synchronize()
         assert torch.equal(S32, S)
-        o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate=gate)
+        o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate=gate,
+                                          o_gate=None if og is None else og.cpu())
         if io == "fp32":
             worst["o"] = max(worst["o"], err(o.cpu(), o_ref))
         else:
@@ -59,6 +62,13 @@ def test_decode_gate_fused(io, g_scale):
     kernel forms -5*sigmoid(x) in fp32, the oracle in fp64."""
     _announce("decode_gate", io=io, g_scale=g_scale)
     _steps(3, 2, 128, 128, io, steps=4, seed=34, gate="scaled_sigmoid", g_scale=g_scale)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_decode_output_gate(io):
+    """o * sigmoid(z) with z ~ N(0,1), together with the scaled-sigmoid decay gate."""
+    _announce("decode_output_gate", io=io)
+    _steps(3, 2, 128, 128, io, steps=4, seed=35, gate="scaled_sigmoid", o_gate=True)
 
 
 def test_decode_512_streams():

@@ -25,18 +25,21 @@ def _announce(name, **kw):
 
 def _oracle(inp, heads=None):
     q, k, v, g, beta, S0, cu = (inp[n] for n in ("q", "k", "v", "g", "beta", "S0", "cu_seqlens"))
+    og = inp.get("o_gate")
     if heads is not None:
         hs = list(heads)
         q, k, v, g, beta = (x[:, :, hs].contiguous() for x in (q, k, v, g, beta))
+        og = None if og is None else og[:, :, hs].contiguous()
         S0 = None if S0 is None else S0[:, hs].contiguous()
     return oracle.chunk_fwd(q.cpu(), k.cpu(), v.cpu(), g.cpu(), beta.cpu(), None if S0 is None else S0.cpu(),
-                            None if cu is None else cu.cpu(), gate=inp.get("gate", "log_decay"))
+                            None if cu is None else cu.cpu(), gate=inp.get("gate", "log_decay"),
+                            o_gate=None if og is None else og.cpu())
 
 
 def _run(inp, o_dtype=None, chunk=16):
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
                       cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk,
-                      gate=inp.get("gate", "log_decay"))
+                      gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"))
     torch.cuda.synchronize()
     return o, Sf
 
@@ -352,5 +355,60 @@ def test_gate_fused_k3_prefill_4k_sampled_heads():
     w = synth.WORKLOADS["prefill_4k"]
     _announce("gate_prefill_4k", seed=w.seed)
     inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True)
+    inp["gate"] = "scaled_sigmoid"
+    _check(inp, heads=(0, 31, 64, 95))
+
+
+# ------------------------------------------------------------ output gate
+#
+# With o_gate given, the state pass's o store multiplies by sigmoid(o_gate) in fp32; the oracle
+# applies the same gate in fp64 to its output.
+
+@CHUNKS
+@pytest.mark.parametrize("io,B,T,H,K,V", [("fp32", 2, 77, 3, 128, 128), ("fp32", 1, 50, 2, 64, 32),
+                                          ("bf16", 2, 200, 3, 128, 128), ("bf16", 1, 129, 2, 128, 64)])
+def test_output_gate_shapes(io, B, T, H, K, V, chunk):
+    _announce("output_gate", io=io, B=B, T=T, H=H, K=K, V=V, chunk=chunk, seed=50)
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=50, device=DEV, with_S0=True, with_o_gate=True)
+    _check(inp, io=io, chunk=chunk)
+
+
+@CHUNKS
+def test_output_gate_varlen_both_gates(chunk):
+    """Packed sequences (empty and ragged ones) with both gates formed in-kernel."""
+    lengths = [37, 0, 16, 1, 150, 64, 0, 65]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("both_gates_varlen", lengths=lengths, chunk=chunk, seed=51)
+    inp = _gate_inputs(1, cu[-1], 4, 128, 128, "bf16", 51, cu_seqlens=cu, with_S0=True, with_o_gate=True)
+    _check(inp, chunk=chunk)
+
+
+def test_output_gate_leaves_state_and_scales_o():
+    """fp32 I/O: the gate changes o only: S_final is bitwise that of the ungated call, and z = 0 halves o
+    (sigmoid(0) = 1/2 exactly, a power-of-two scale)."""
+    _announce("output_gate_exact", seed=52)
+    inp = synth.prefill_inputs(1, 300, 4, 64, 64, "fp32", seed=52, device=DEV, with_S0=True)
+    o1, S1 = _run(inp)
+    o2, S2 = _run(dict(inp, o_gate=torch.zeros_like(inp["v"])))
+    assert torch.equal(S1, S2) and torch.equal(o2, 0.5 * o1)
+
+
+def test_output_gate_pipelined_ranges():
+    """The combined state/prep kernel of a pipelined call applies the gate as the plain call does."""
+    _announce("output_gate_pipelined", seed=53)
+    inp = synth.prefill_inputs(1, 2500, 4, 128, 128, "bf16", seed=53, device=DEV, with_S0=True, with_o_gate=True)
+    with _Ranges(1):
+        o1, S1 = _run(inp)
+    with _Ranges(4):
+        o4, S4 = _run(inp)
+    assert torch.equal(o1, o4) and torch.equal(S1, S4)
+    _check(inp, heads=(0, 3))
+
+
+def test_output_gate_k3_prefill_4k_sampled_heads():
+    """The both-gates leg of the benchmark: H=96, T=4096, K=V=128, bf16, chunk 16; 4 heads checked."""
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("both_gates_prefill_4k", seed=w.seed)
+    inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True, with_o_gate=True)
     inp["gate"] = "scaled_sigmoid"
     _check(inp, heads=(0, 31, 64, 95))

@@ -121,6 +121,35 @@ def test_gate_drives_the_decay():
         oracle.chunk_fwd(q, k, v, x, np.zeros((1, T, 1)), gate="softplus")
 
 
+# ------------------------------------------------------------ the output gate
+
+def test_output_gate_closed_forms():
+    """o * sigmoid(z): z = 0 halves o exactly; sigmoid(z) + sigmoid(-z) = 1, so the outputs under z and -z
+    add up to the ungated output; z = ln 3 keeps 3/4; the ends saturate to o and 0; S_final does not depend
+    on the gate. Through both the prefill and the decode entry points."""
+    rng = np.random.default_rng(23)
+    B, T, H, K, V = 1, 9, 2, 4, 3
+    q, k, v, g, beta = kda_pins._rand_problem(rng, B, T, H, K, V)
+    S0 = rng.standard_normal((B, H, K, V))
+    o, Sf = oracle.chunk_fwd(q, k, v, g, beta, S0=S0)
+    z = rng.standard_normal((B, T, H, V)) * 3.0
+    o0, Sf0 = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=np.zeros_like(z))
+    assert np.array_equal(o0, 0.5 * o) and np.array_equal(Sf0, Sf)
+    op, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=z)
+    om, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=-z)
+    assert kda_pins.rel_err(op + om, o) < 1e-14
+    o3, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=np.full_like(z, np.log(3.0)))
+    assert kda_pins.rel_err(o3, 0.75 * o) < 1e-15
+    ohi, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=np.full_like(z, 800.0))
+    olo, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, o_gate=np.full_like(z, -800.0))
+    assert np.array_equal(ohi, o) and np.all(olo == 0.0)
+    od, Sd = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0)
+    odz, Sdz = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, o_gate=np.zeros_like(z[:, 0]))
+    assert np.array_equal(odz, 0.5 * od) and np.array_equal(Sdz, Sd)
+    with pytest.raises(ValueError):
+        oracle.chunk_fwd(q, k, v, g, beta, o_gate=z[..., :2])
+
+
 # ------------------------------------------------------------ planted mistakes
 #
 # A small numpy re-implementation with switches for plausible mistakes. The
