@@ -78,6 +78,15 @@ def test_decode_512_streams():
     _steps(w.N, w.H, w.K, w.V, "bf16", steps=3, seed=w.seed)
 
 
+@pytest.mark.parametrize("io,N,H,K,V", [("fp32", 1031, 5, 32, 64), ("bf16", 70, 64, 128, 128)])
+def test_decode_ragged_pairs_per_workgroup(io, N, H, K, V):
+    """More (sequence, head) pairs than one workgroup each (above 4096 pairs a workgroup walks several
+    and prefetches the next): N*H not a multiple of the grid, so workgroups take 1 or 2 pairs; both
+    gates on, 2 consecutive steps, every pair compared."""
+    _announce("decode_ragged_pairs", io=io, N=N, H=H, K=K, V=V)
+    _steps(N, H, K, V, io, steps=2, seed=36, gate="scaled_sigmoid", o_gate=True)
+
+
 def test_decode_steps_equal_prefill():
     """n decode steps from S equal one chunked prefill over the same n tokens from S."""
     _announce("decode_vs_prefill", n=21)
