@@ -102,6 +102,25 @@ def output_gate(o, z) -> np.ndarray:
         return _f64(o) * (1.0 / (1.0 + np.exp(-z)))
 
 
+L2NORM_EPS = 1e-6
+
+
+def l2_normalize(x) -> np.ndarray:
+    """Each vector along the last axis divided by its L2 norm, in fp64: x / sqrt(sum(x^2) + eps).
+
+    The pages give KDA's per-channel decay, the delta-rule write and the read
+    but say nothing about normalising q and k ("Kimi K3 发布核实与 Moonshot AI
+    主干架构演变", section 3, paragraph "KDA 为什么不同于 MLA"). The delta rule
+    of "Kimi K3 模型架构解析：KDA、AttnRes 与 Stable LatentMoE", section 二.3
+    (read what the key maps to, write back only the error) is an exact
+    overwrite only for a unit-norm key, so unit-norm keys (and queries) are
+    read as the optional prologue of the path. eps = 1e-6 under the root keeps
+    an all-zero vector at zero instead of dividing by zero.
+    """
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+
+
 def _log_decay(g, gate: str) -> np.ndarray:
     if gate not in GATES:
         raise ValueError("gate must be one of %s" % (GATES,))
@@ -109,7 +128,7 @@ def _log_decay(g, gate: str) -> np.ndarray:
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate: str = "log_decay",
-              o_gate=None):
+              o_gate=None, qk_norm: bool = False):
     """Run the fp64 recurrence over whole sequences.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H];
@@ -117,9 +136,13 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate
     gate: "log_decay" (g is the log-decay) or "scaled_sigmoid" (g is the gate
     pre-activation; the log-decay is scaled_sigmoid_gate(g)).
     o_gate: [B, T, H, V] or None; if given, o is output_gate(o, o_gate).
+    qk_norm: if true, q and k are replaced by l2_normalize(q), l2_normalize(k)
+    (per token and head, over the K key channels) before the recurrence.
     Returns (o [B, T, H, V], S_final [N, H, K, V]) as float64 arrays.
     """
     g = _log_decay(g, gate)
+    if qk_norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -150,13 +173,16 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate
     return o, sf
 
 
-def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay", o_gate=None):
+def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay", o_gate=None,
+                qk_norm: bool = False):
     """One decode step. q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H]; S: [N, H, K, V].
 
-    gate and o_gate ([N, H, V] or None) as for chunk_fwd. Returns
+    gate, o_gate ([N, H, V] or None) and qk_norm as for chunk_fwd. Returns
     (o [N, H, V], S_new [N, H, K, V]); the input S is not modified.
     """
     g = _log_decay(g, gate)
+    if qk_norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     S_new = _f64(S).copy()
     N, H, K = q.shape

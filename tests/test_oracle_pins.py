@@ -150,6 +150,71 @@ def test_output_gate_closed_forms():
         oracle.chunk_fwd(q, k, v, g, beta, o_gate=z[..., :2])
 
 
+# ------------------------------------------------------------ the q/k L2 normalisation
+
+def test_l2norm_closed_forms():
+    """(3, 4) -> (3/5, 4/5) and (0, -2, 0) -> (0, -1, 0) up to eps; an all-zero vector stays zero (no NaN);
+    the direction is kept and the norm of a result is sqrt(n2 / (n2 + eps)) for |x|^2 = n2."""
+    f = oracle.l2_normalize
+    eps = oracle.L2NORM_EPS
+    assert np.allclose(f(np.array([3.0, 4.0])), [0.6, 0.8], rtol=0, atol=1e-7)
+    assert np.allclose(f(np.array([0.0, -2.0, 0.0])), [0.0, -1.0, 0.0], rtol=0, atol=1e-6)
+    z = f(np.zeros((2, 5)))
+    assert np.all(z == 0.0)
+    x = np.random.default_rng(41).standard_normal((7, 3, 16)) * 4.0
+    y = f(x)
+    n2 = np.sum(x * x, axis=-1)
+    assert np.max(np.abs(np.linalg.norm(y, axis=-1) - np.sqrt(n2 / (n2 + eps)))) < 1e-14
+    cos = np.sum(x * y, axis=-1) / (np.linalg.norm(x, axis=-1) * np.linalg.norm(y, axis=-1))
+    assert np.max(np.abs(cos - 1.0)) < 1e-14
+
+
+def test_l2norm_read_after_write_with_raw_keys():
+    """With the normalisation on, beta = 1 and q_t = c_t k_t for any unnormalised k_t and any c_t > 0,
+    every output equals v_t for any S0 and g (the read-after-write identity, which needs a unit key):
+    o_t = S_t^T k^ = (D S)^T k^ - (D S)^T k^ + v_t |k^|^2, and |k^|^2 = 1 up to eps / |k|^2.
+    Without the normalisation the same inputs miss it by the factor c_t |k_t|^2."""
+    rng = np.random.default_rng(42)
+    B, T, H, K, V = 1, 11, 2, 8, 5
+    k = rng.standard_normal((B, T, H, K)) * 3.0
+    c = np.exp(rng.standard_normal((B, T, H, 1)))
+    q = c * k
+    v = rng.standard_normal((B, T, H, V))
+    g = -5.0 * rng.random((B, T, H, K))
+    beta = np.ones((B, T, H))
+    S0 = rng.standard_normal((B, H, K, V))
+    o, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, qk_norm=True)
+    n2 = np.sum(k * k, axis=-1, keepdims=True)
+    assert np.max(np.abs(o - v)) < 1e-6 * np.max(np.abs(v)) + 10 * oracle.L2NORM_EPS / np.min(n2)
+    o_raw, _ = oracle.chunk_fwd(q, k, v, g, beta, S0=S0)
+    assert np.max(np.abs(o_raw - v)) > 1.0
+    od, _ = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, qk_norm=True)
+    assert np.max(np.abs(od - v[:, 0])) < 1e-6
+
+
+def test_l2norm_scale_invariance():
+    """Scaling every q and k row by its own positive factor leaves o and S_final unchanged when the
+    normalisation is on (to the eps term, ~eps / |k|^2 relative), through prefill and decode; and the
+    normalised call equals the plain call on unit-norm rows scaled back (q, k on the sphere)."""
+    rng = np.random.default_rng(43)
+    B, T, H, K, V = 2, 13, 3, 6, 4
+    q, k, v, g, beta = kda_pins._rand_problem(rng, B, T, H, K, V)
+    q = q * 10.0
+    k = k * 10.0
+    S0 = rng.standard_normal((B, H, K, V))
+    cq = np.exp(rng.uniform(0.0, 1.5, (B, T, H, 1)))
+    ck = np.exp(rng.uniform(0.0, 1.5, (B, T, H, 1)))
+    o1, S1 = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, qk_norm=True)
+    o2, S2 = oracle.chunk_fwd(cq * q, ck * k, v, g, beta, S0=S0, qk_norm=True)
+    assert kda_pins.rel_err(o2, o1) < 1e-6 and kda_pins.rel_err(S2, S1) < 1e-6
+    un = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    o3, S3 = oracle.chunk_fwd(un(q), un(k), v, g, beta, S0=S0)
+    assert kda_pins.rel_err(o3, o1) < 1e-6 and kda_pins.rel_err(S3, S1) < 1e-6
+    od1, Sd1 = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, qk_norm=True)
+    od2, Sd2 = oracle.decode_step(3.0 * q[:, 0], 0.5 * k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0, qk_norm=True)
+    assert kda_pins.rel_err(od2, od1) < 1e-6 and kda_pins.rel_err(Sd2, Sd1) < 1e-6
+
+
 # ------------------------------------------------------------ planted mistakes
 #
 # A small numpy re-implementation with switches for plausible mistakes. The
