@@ -47,10 +47,12 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False):
+def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False, qk_norm=False):
     lib = _lib.load()
     gc = _lib.GATES[gate]
-    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"), with_o_gate=o_gate)
+    qkc = _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"), with_o_gate=o_gate,
+                                        raw_k=qk_norm)
     og = inp["o_gate"].data_ptr() if o_gate else None
     B, T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
@@ -64,7 +66,7 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def prep():
-        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1, gc,
+        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1, gc, qkc,
                                       ws.data_ptr(), wsb, sh), "kda_chunk_prep")
 
     def state():
@@ -73,7 +75,7 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False
 
     def fwd():
         _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, None, None, B, T, H, K, V, N, chunk,
-                                     1, gc, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
+                                     1, gc, qkc, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
 
     # the step: one kda_chunk_fwd call (where the state pass leaves CUs free, the library runs the
     # prep of later chunks beside the state pass of earlier ones)
@@ -108,20 +110,20 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False
             "state_ms": state_ms, "ws_bytes": wsb}
 
 
-def time_decode(w, steps, dev, gate="log_decay"):
+def time_decode(w, steps, dev, gate="log_decay", qk_norm=False):
     N, H, K, V = w.N, w.H, w.K, w.V
     S = synth.decode_state(N, H, K, V, seed=w.seed, device=dev)
     inputs = [synth.decode_inputs(N, H, K, V, w.io, seed=w.seed, step=s, device=dev,
-                                  gate_preact=(gate == "scaled_sigmoid")) for s in range(steps)]
+                                  gate_preact=(gate == "scaled_sigmoid"), raw_k=qk_norm) for s in range(steps)]
     o = torch.empty((N, H, V), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     for s in range(2):  # warm-up on the same state (its values only drift)
-        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate)
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate, qk_norm=qk_norm)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for s in range(steps):
-        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate)
+        decode_step(*(inputs[s][n] for n in ("q", "k", "v", "g", "beta")), S, out=o, gate=gate, qk_norm=qk_norm)
         ev[s + 1].record(stream)
     torch.cuda.synchronize()
     per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
@@ -296,6 +298,14 @@ def main():
                           "tokens_per_s": ro["B"] * ro["T"] / (mso * 1e-3), "ms_per_step": mso,
                           "kernels_ms": {"kda_chunk_prep (+chunk table)": ro["prep_ms"],
                                          "kda_state_pass": ro["state_ms"]}}
+    print("[bench] prefill %s with both gates and the q/k normalisation in-kernel: warmup %d, steps %d"
+          % (w.name, args.warmup, args.steps), file=sys.stderr, flush=True)
+    rn = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True, qk_norm=True)
+    msn = rn["wall_s"] * 1e3 / args.steps
+    out["prologue_epilogue_fused"] = {
+        "workload": "as gates_fused, with raw q, k ~ N(0,1) L2-normalised per (token, head) in kda_chunk_prep",
+        "tokens_per_s": rn["B"] * rn["T"] / (msn * 1e-3), "ms_per_step": msn,
+        "kernels_ms": {"kda_chunk_prep (+chunk table)": rn["prep_ms"], "kda_state_pass": rn["state_ms"]}}
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
         print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)
@@ -307,10 +317,12 @@ def main():
                          "tokens_per_s": d["N"] / (d["ms_per_step"] * 1e-3),
                          "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel", "achieved": gbs,
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                      "traffic": measured_traffic("kda::kda_decode_kernel<true, 128, 128>"),
+                                      "traffic": measured_traffic("kda::kda_decode_kernel<true, 128, 128,"),
                                       "algorithmic_bytes_per_launch": d["bytes_per_step"]}}
         dg = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid")
         out["decode"]["gate_fused_ms_per_step"] = dg["ms_per_step"]
+        dn = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid", qk_norm=True)
+        out["decode"]["gate_and_qk_norm_fused_ms_per_step"] = dn["ms_per_step"]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -77,6 +77,24 @@ typedef enum {
     KDA_GATE_SCALED_SIGMOID = 1
 } kda_gate_t;
 
+/*
+ * What happens to q and k before the recurrence.
+ *   KDA_QK_AS_GIVEN  used exactly as passed.
+ *   KDA_QK_L2NORM    each q_t and k_t (per token and head, over the K key
+ *                    channels) is divided by sqrt(|x|^2 + 1e-6) in fp32 as the
+ *                    kernels read it. The delta rule of the second page cited
+ *                    above (section 二.3: read what the key maps to, write
+ *                    back only the error) overwrites exactly only for a
+ *                    unit-norm key; the pages do not say where keys are
+ *                    normalised, so this lets the caller hand over raw
+ *                    projections and pay no pass and no bytes for it. The
+ *                    1e-6 keeps an all-zero row at zero.
+ */
+typedef enum {
+    KDA_QK_AS_GIVEN = 0,
+    KDA_QK_L2NORM = 1
+} kda_qk_norm_t;
+
 /* Version of this ABI (bumped on any signature change). */
 int kda_abi_version(void);
 
@@ -99,7 +117,8 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  * chunk", first page cited above).
  *
  * Inputs (dtype `io`):
- *   q, k, g   [B, T, H, K]   g as `gate` says. With KDA_GATE_LOG_DECAY the
+ *   q, k, g   [B, T, H, K]   q and k as `qk_norm` says, g as `gate` says.
+ *                            With KDA_GATE_LOG_DECAY the
  *                            chunk form assumes -5 <= g <= 0 (the bounded
  *                            gate); outside that range results are
  *                            unspecified. With KDA_GATE_SCALED_SIGMOID any
@@ -129,16 +148,16 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes().
  * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
  *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow,
- *   unknown dtype or gate),
+ *   unknown dtype, gate or qk_norm),
  *   NOT_SUPPORTED (K, V or chunk outside the supported set),
  *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                           int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype,
-                           void *o, float *S_final, void *workspace, size_t workspace_bytes,
-                           void *stream);
+                           int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm,
+                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
@@ -155,8 +174,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  *   (chunk, head), forms the cumulative log-decay, the beta-weighted
  *   decay-scaled key products, solves the chunk's unit lower-triangular
  *   system and stores the resulting factors in `workspace` (layout private to
- *   the library). Reads q, k, g (as `gate` says), beta; V only sizes the
- *   workspace check.
+ *   the library). Reads q, k (as `qk_norm` says), g (as `gate` says), beta;
+ *   V only sizes the workspace check.
  * kda_chunk_state: the sequential pass over the chunks of each (sequence,
  *   head): carries S from S0 (or 0), writes o (gated by o_gate, if given) and
  *   S_final. Reads v, o_gate, S0 and a
@@ -167,8 +186,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  */
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
+                            kda_qk_norm_t qk_norm, void *workspace, size_t workspace_bytes, void *stream);
 kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                              kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
@@ -179,7 +198,7 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
  * steps above applied once, with the fixed-size state updated in place
  * ("S_t = Update(S_{t-1}, k_t, v_t)", second page cited above).
  *   q, k, g [N, H, K]; v [N, H, V]; beta [N, H]      dtype `io`
- *   g       as `gate` says
+ *   g       as `gate` says; q and k as `qk_norm` says
  *   o_gate  [N, H, V] or NULL: output gate pre-activation, as for kda_chunk_fwd
  *   S       [N, H, K, V] fp32, read and overwritten in place
  *   o       [N, H, V] in `o_dtype`
@@ -188,7 +207,8 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
                              const void *o_gate, float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
-                             kda_dtype_t io, kda_gate_t gate, kda_dtype_t o_dtype, void *stream);
+                             kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype,
+                             void *stream);
 
 #ifdef __cplusplus
 }

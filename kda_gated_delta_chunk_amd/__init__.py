@@ -65,8 +65,13 @@ def _gate_code(gate: str) -> int:
     return _lib.GATES[gate]
 
 
+def _qk_code(qk_norm: bool) -> int:
+    return _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
-              output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None):
+              output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None,
+              qk_norm: bool = False):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
@@ -75,6 +80,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     (the log-decay itself) or "scaled_sigmoid" (the gate pre-activation,
     mapped to -5*sigmoid(g) inside the kernels). ``o_gate`` [B, T, H, V] (input
     dtype), if given, scales the output channel by channel: o * sigmoid(o_gate).
+    ``qk_norm``: if true the kernels divide each q and k row (per token and
+    head) by sqrt(|x|^2 + 1e-6) as they read it.
     """
     lib = _lib.load()
     dev = q.device
@@ -112,16 +119,18 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0),
                                _ptr(cu_seqlens),
-                               B, T, H, K, V, N, chunk, io, gc, _io_code(odt), _ptr(out), _ptr(S_final),
+                               B, T, H, K, V, N, chunk, io, gc, _qk_code(qk_norm), _io_code(odt), _ptr(out),
+                               _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(status, "kda_chunk_fwd")
     return out, S_final
 
 
-def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay", o_gate=None):
+def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay", o_gate=None,
+                qk_norm: bool = False):
     """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V].
 
-    ``gate`` and ``o_gate`` ([N, H, V]) as for :func:`chunk_fwd`.
+    ``gate``, ``o_gate`` ([N, H, V]) and ``qk_norm`` as for :func:`chunk_fwd`.
     """
     lib = _lib.load()
     dev = q.device
@@ -143,6 +152,6 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
     else:
         _need(out, "out", (N, H, V), odt, dev)
     status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S), _ptr(out),
-                                 N, H, K, V, io, gc, _io_code(odt), _stream(dev))
+                                 N, H, K, V, io, gc, _qk_code(qk_norm), _io_code(odt), _stream(dev))
     _lib.check(status, "kda_decode_step")
     return out

@@ -17,6 +17,7 @@ bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; }
 bool valid_gate(kda_gate_t g) { return g == KDA_GATE_LOG_DECAY || g == KDA_GATE_SCALED_SIGMOID; }
+bool valid_qk_norm(kda_qk_norm_t n) { return n == KDA_QK_AS_GIVEN || n == KDA_QK_L2NORM; }
 // beta is read one element at a time: natural alignment of its dtype suffices
 bool aligned_elem(const void *p, kda_dtype_t t) { return ((uintptr_t)p & (t == KDA_DTYPE_BF16 ? 1u : 3u)) == 0; }
 
@@ -57,7 +58,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 3; }
+int kda_abi_version(void) { return 4; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -87,9 +88,10 @@ namespace {
 kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
                           int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                          kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
+                          kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
                           size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm))
+        return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed);
     if (st != KDA_SUCCESS) return st;
@@ -112,6 +114,7 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
+    a.qk_l2norm = qk_norm == KDA_QK_L2NORM;
     a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
     a.chunk = chunk;
     a.n_chunks_max = nc;
@@ -122,11 +125,11 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
                            int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
-                           kda_gate_t gate, kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+                           kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *o, float *S_final,
+                           void *workspace, size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, v, g, beta, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
-                                   o_dtype, o, S_final, workspace, workspace_bytes, true, true, a);
+                                   qk_norm, o_dtype, o, S_final, workspace, workspace_bytes, true, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -134,11 +137,11 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
+                            kda_qk_norm_t qk_norm, void *workspace, size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
-                                   gate, io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
+                                   gate, qk_norm, io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -151,7 +154,8 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
                              size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs,
-                                   chunk, io, KDA_GATE_LOG_DECAY, o_dtype, o, S_final, workspace, workspace_bytes,
+                                   chunk, io, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, o_dtype, o, S_final, workspace,
+                                   workspace_bytes,
                                    false, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_state(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
@@ -161,8 +165,9 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
                              const void *o_gate, float *S,
                              void *o, int32_t N, int32_t H, int32_t K, int32_t V, kda_dtype_t io,
-                             kda_gate_t gate, kda_dtype_t o_dtype, void *stream) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+                             kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *stream) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm))
+        return KDA_ERROR_INVALID_VALUE;
     if (N < 0 || H < 1) return KDA_ERROR_INVALID_VALUE;
     if (!supported_dim(K) || !supported_dim(V)) return KDA_ERROR_NOT_SUPPORTED;
     if ((int64_t)N * H >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
@@ -185,6 +190,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
+    a.qk_l2norm = qk_norm == KDA_QK_L2NORM;
     if (kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }

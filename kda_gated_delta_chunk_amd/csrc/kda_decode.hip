@@ -39,7 +39,7 @@ template <bool BF, int K, int V, int NT>
 __global__ __launch_bounds__(NT) void kda_decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
     const void *__restrict__ gp, const void *__restrict__ bp, const void *__restrict__ zp, float *__restrict__ S,
-    void *__restrict__ op, int o_bf16, int gate, int32_t NH) {
+    void *__restrict__ op, int o_bf16, int gate, int qknorm, int32_t NH) {
     constexpr int CG = V / 4;          // column groups (float4) per row
     constexpr int RG = NT / CG;        // row groups
     constexpr int RPT = K / RG;        // rows per thread
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
     __shared__ float s_alpha[K], s_k[K], s_q[K], s_v[V];
     __shared__ f32x4 s_part[NW][2][CG];   // per wavefront: partial u, y of each column group
     __shared__ f32x4 s_delta[CG];
-    __shared__ float s_kq[NW];
+    __shared__ float s_kq[NW], s_kk[NW], s_qq[NW];
 
     const int t = threadIdx.x, cg = t % CG, rg = t / CG;
     const int lane = t & 63, wave = t >> 6;
@@ -81,19 +81,46 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
         float ktn = 0.f, qtn = 0.f, gtn = 0.f, vtn = 0.f, betan = 0.f;
         if (nx < NH) load_pair(nx, sn, ktn, qtn, gtn, vtn, betan);
 
-        // 2. token vectors to LDS; alpha = exp(log-decay); k.q by wave reduction, then across waves
-        float kq = 0.f;
+        // 2. token vectors to LDS; alpha = exp(log-decay); k.q (and |k|^2, |q|^2 when q and k are
+        //    normalised) by wave reduction, then across waves
+        float kq = 0.f, kk = 0.f, qq = 0.f;
         if (t < K) {
             s_alpha[t] = __builtin_amdgcn_exp2f(gate ? gate_log2_decay(gt) : gt * 1.4426950408889634f);
             s_k[t] = kt;
             s_q[t] = qt;
             kq = kt * qt;
+            kk = kt * kt;
+            qq = qt * qt;
         }
         if (t < V) s_v[t] = vt;
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) kq += __shfl_xor(kq, d);
         if (lane == 0) s_kq[wave] = kq;
+        if (qknorm) {  // uniform
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                kk += __shfl_xor(kk, d);
+                qq += __shfl_xor(qq, d);
+            }
+            if (lane == 0) {
+                s_kk[wave] = kk;
+                s_qq[wave] = qq;
+            }
+        }
         __syncthreads();
+        // L2 normalisation of q and k, applied as factors: u and the rank-1 update scale with 1/|k|,
+        // y with 1/|q|, k.q with both
+        float rk = 1.f, rq = 1.f;
+        if (qknorm) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                sk += s_kk[w];
+                sq += s_qq[w];
+            }
+            rk = rsqrtf(sk + 1e-6f);
+            rq = rsqrtf(sq + 1e-6f);
+        }
 
         // 3. decay, then both column reductions over this thread's rows
         f32x4 u = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -123,13 +150,15 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
             float kqs = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) kqs += s_kq[w];
-            const float bkq = beta * kqs;
+            const float bkq = beta * kqs * (rk * rq);
             f32x4 uu = s_part[0][0][t], yy = s_part[0][1][t];
 #pragma unroll
             for (int w = 1; w < NW; ++w) {
                 uu += s_part[w][0][t];
                 yy += s_part[w][1][t];
             }
+            uu *= rk;
+            yy *= rq;
             const f32x4 vv = {s_v[4 * t], s_v[4 * t + 1], s_v[4 * t + 2], s_v[4 * t + 3]};
             const f32x4 dl = vv - uu;
             s_delta[t] = dl;
@@ -155,7 +184,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
 #pragma unroll
         for (int j = 0; j < RPT; ++j) {
             const int r = rg + RG * j;
-            const float bk = beta * s_k[r];
+            const float bk = beta * rk * s_k[r];
             f32x4 w = s[j];
             w.x += bk * delta.x; w.y += bk * delta.y; w.z += bk * delta.z; w.w += bk * delta.w;
             __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(Sp + (size_t)r * V) + cg);
@@ -182,7 +211,7 @@ hipError_t launch_dkv(const DecodeArgs &a, int32_t NH, hipStream_t st) {
     // up to 4096 workgroups take one pair each; above that each workgroup walks about 4 pairs
     const int32_t grid = NH <= 4096 ? NH : (NH + 3) / 4 > 4096 ? (NH + 3) / 4 : 4096;
     hipLaunchKernelGGL((kda_decode_kernel<BF, K, V, NT>), dim3(grid), dim3(NT), 0, st, a.q, a.k, a.v, a.g, a.beta,
-                       a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, NH);
+                       a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm, NH);
     return hipGetLastError();
 }
 template <bool BF, int K>

@@ -17,6 +17,7 @@ struct PrefillArgs {
     int32_t H, K, V, num_seqs;
     bool io_bf16, o_bf16;
     bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
+    bool qk_l2norm;        // q and k are L2-normalised per (token, head) as they are read
     void *o;
     float *S_final;
     void *workspace;
@@ -44,6 +45,7 @@ struct DecodeArgs {
     int32_t N, H, K, V;
     bool io_bf16, o_bf16;
     bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
+    bool qk_l2norm;        // q and k are L2-normalised per (n, h) as they are read
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

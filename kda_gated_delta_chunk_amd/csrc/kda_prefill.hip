@@ -236,6 +236,25 @@ __device__ __forceinline__ void load8(const void *base, int64_t idx, float (&x)[
     }
 }
 
+// Divide this lane's part of a token row by the row's L2 norm, sqrt(|x|^2 + 1e-6): the row's K
+// channels are spread over the four lane groups of the wavefront (lanes r, r + 16, r + 32, r + 48).
+// Every lane of the wavefront must call it.
+template <int KS>
+__device__ __forceinline__ void l2norm_row(float (&x)[KS][8]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(x[s][j], x[s][j], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rn = rsqrtf(ss + 1e-6f);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[s][j] *= rn;
+}
+
 // mma32 operands from eight fp32 values: rounded (single) or split into hi + lo.
 __device__ __forceinline__ Frag8<true> frag8_of(const float (&x)[8], Frag8<true>) {
     Frag8<true> f;
@@ -413,7 +432,8 @@ __device__ __forceinline__ void solve16(const float *sAT, int n, float (&x)[16])
 struct PrepParams {
     const void *q, *k, *g, *beta;
     int32_t H, N;
-    int32_t gate;  // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
+    int32_t gate;    // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
+    int32_t qknorm;  // 1: q and k rows are L2-normalised as they are read (l2norm_row)
     ChunkTab tab;
     char *frags;
     int32_t g0, g1;
@@ -459,6 +479,10 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
         load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
         load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
         load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    }
+    if (pa.qknorm) {  // wave-uniform
+        l2norm_row<KS>(qv);
+        l2norm_row<KS>(kv);
     }
     float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
     beta = valid ? beta : 0.f;
@@ -681,6 +705,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
         load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
         load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    }
+    if (pa.qknorm) {  // wave-uniform
+        l2norm_row<KS>(qv);
+        l2norm_row<KS>(kv);
     }
     float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
     beta = valid ? beta : 0.f;
@@ -1757,6 +1785,7 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
     p.q = a.q; p.k = a.k; p.g = a.g; p.beta = a.beta;
     p.H = a.H; p.N = a.num_seqs;
     p.gate = a.gate_sigmoid ? 1 : 0;
+    p.qknorm = a.qk_l2norm ? 1 : 0;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     return p;

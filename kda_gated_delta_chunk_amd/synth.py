@@ -100,7 +100,8 @@ def cu_from_lengths(lengths) -> list[int]:
 def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0,
                    device="cpu", cu_seqlens=None, with_S0: bool = False, block_tokens: int = 65536,
                    g_shift: float = 0.0, g_const: float | None = None, beta_const: float | None = None,
-                   gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False):
+                   gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False,
+                   raw_k: bool = False):
     """Inputs of one prefill call.
 
     Returns a dict with q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H] in the I/O
@@ -108,7 +109,9 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
     ``g_shift`` moves the pre-sigmoid draw of g (e.g. -6 for mild decay);
     ``g_const``/``beta_const`` replace the draw by a constant (stress cases);
     ``gate_preact`` stores the pre-sigmoid draw g_scale * x + g_shift itself;
-    ``with_o_gate`` adds an output-gate pre-activation ``o_gate`` [B,T,H,V].
+    ``with_o_gate`` adds an output-gate pre-activation ``o_gate`` [B,T,H,V];
+    ``raw_k`` keeps the N(0, 1) draw of k as it is (no normalisation; for
+    calls that normalise q and k themselves).
     """
     dt = DTYPES[io]
     dev = torch.device(device)
@@ -127,7 +130,8 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
         n = b - a
         qf[a:b] = _randn((n, H, K), seed, "q", blk, dev).to(dt)
         kr = _randn((n, H, K), seed, "k", blk, dev)
-        kr = kr / torch.sqrt(torch.sum(kr * kr, dim=-1, keepdim=True))
+        if not raw_k:
+            kr = kr / torch.sqrt(torch.sum(kr * kr, dim=-1, keepdim=True))
         kf[a:b] = kr.to(dt)
         del kr
         vf[a:b] = _randn((n, H, V), seed, "v", blk, dev).to(dt)
@@ -165,15 +169,17 @@ def workload_prefill_inputs(w: Workload, device="cpu", **kw):
 
 
 def decode_inputs(N: int, H: int, K: int, V: int, io: str = "bf16", seed: int = 0, step: int = 0,
-                  device="cpu", gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False):
+                  device="cpu", gate_preact: bool = False, g_scale: float = 1.0, with_o_gate: bool = False,
+                  raw_k: bool = False):
     """Per-step decode inputs q, k, g [N,H,K], v [N,H,V], beta [N,H] (step = block id).
     ``gate_preact``: g is the pre-sigmoid draw g_scale * x itself; ``with_o_gate``: also an
-    output-gate pre-activation o_gate [N,H,V] (else None)."""
+    output-gate pre-activation o_gate [N,H,V] (else None); ``raw_k``: k is the N(0, 1) draw
+    itself, not normalised."""
     dt = DTYPES[io]
     dev = torch.device(device)
     q = _randn((N, H, K), seed, "q", step, dev).to(dt)
     kr = _randn((N, H, K), seed, "k", step, dev)
-    k = (kr / torch.sqrt(torch.sum(kr * kr, dim=-1, keepdim=True))).to(dt)
+    k = (kr if raw_k else kr / torch.sqrt(torch.sum(kr * kr, dim=-1, keepdim=True))).to(dt)
     v = _randn((N, H, V), seed, "v", step, dev).to(dt)
     x = _randn((N, H, K), seed, "g", step, dev)
     g = (g_scale * x if gate_preact else -5.0 * torch.sigmoid(x)).to(dt)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -64,11 +64,12 @@ def test_workspace_bytes():
 def _fwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
-             gate=0, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
+             gate=0, qkn=0, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["B"], a["T"],
                              a["H"],
-                             a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["odt"], a["o"], a["Sf"], a["ws"],
+                             a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["qkn"], a["odt"], a["o"], a["Sf"],
+                             a["ws"],
                              a["wsb"], a["stream"])
 
 
@@ -93,6 +94,8 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(odt=-1), INVALID),
     (dict(gate=2), INVALID),
     (dict(gate=-1), INVALID),
+    (dict(qkn=2), INVALID),
+    (dict(qkn=-1), INVALID),
     (dict(S0=A, Sf=A), INVALID),         # S0 aliases S_final
     (dict(T=1 << 40, H=96), INVALID),    # size overflow
     (dict(K=48), UNSUP),
@@ -108,12 +111,12 @@ def test_chunk_fwd_rejects(kw, expect):
 
 def _dec(**kw):
     lib = _lib.load()
-    a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, gate=0, odt=1,
-             stream=None)
+    a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, gate=0, qkn=0,
+             odt=1, stream=None)
     a.update(kw)
     return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S"], a["o"], a["N"], a["H"],
                                a["K"],
-                               a["V"], a["io"], a["gate"], a["odt"], a["stream"])
+                               a["V"], a["io"], a["gate"], a["qkn"], a["odt"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -127,6 +130,7 @@ def _dec(**kw):
     (dict(H=0), INVALID),
     (dict(io=3), INVALID),
     (dict(gate=5), INVALID),
+    (dict(qkn=3), INVALID),
     (dict(K=16), UNSUP),
     (dict(V=96), UNSUP),
 ])

@@ -15,23 +15,23 @@ def _announce(name, **kw):
     print("\n[case] %s %s" % (name, " ".join("%s=%s" % kv for kv in kw.items())), flush=True)
 
 
-def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0, o_gate=False):
+def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0, o_gate=False, qk_norm=False):
     S = synth.decode_state(N, H, K, V, seed=seed, device=DEV)
     S_ref = S.double().cpu().numpy()
     worst = {"o": 0.0, "S": 0.0}
     pre = gate == "scaled_sigmoid"
     for step in range(steps):
         inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV, gate_preact=pre, g_scale=g_scale,
-                                  with_o_gate=o_gate)
+                                  with_o_gate=o_gate, raw_k=qk_norm)
         args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
         og = inp["o_gate"]
         S32 = S.clone()
-        o = decode_step(*args, S, gate=gate, o_gate=og)
-        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate, o_gate=og)
+        o = decode_step(*args, S, gate=gate, o_gate=og, qk_norm=qk_norm)
+        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate, o_gate=og, qk_norm=qk_norm)
         torch.cuda.synchronize()
         assert torch.equal(S32, S)
         o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate=gate,
-                                          o_gate=None if og is None else og.cpu())
+                                          o_gate=None if og is None else og.cpu(), qk_norm=qk_norm)
         if io == "fp32":
             worst["o"] = max(worst["o"], err(o.cpu(), o_ref))
         else:
@@ -85,6 +85,15 @@ def test_decode_ragged_pairs_per_workgroup(io, N, H, K, V):
     gates on, 2 consecutive steps, every pair compared."""
     _announce("decode_ragged_pairs", io=io, N=N, H=H, K=K, V=V)
     _steps(N, H, K, V, io, steps=2, seed=36, gate="scaled_sigmoid", o_gate=True)
+
+
+@pytest.mark.parametrize("io,N,H,K,V", [("fp32", 3, 2, 128, 128), ("fp32", 5, 3, 32, 64), ("bf16", 4, 3, 128, 128),
+                                        ("bf16", 1031, 5, 64, 32)])
+def test_decode_qk_norm(io, N, H, K, V):
+    """Raw q, k ~ N(0,1) normalised in-kernel, with both gates; the last case walks several pairs per
+    workgroup."""
+    _announce("decode_qk_norm", io=io, N=N, H=H, K=K, V=V)
+    _steps(N, H, K, V, io, steps=3, seed=37, gate="scaled_sigmoid", o_gate=True, qk_norm=True)
 
 
 def test_decode_steps_equal_prefill():

@@ -33,13 +33,14 @@ def _oracle(inp, heads=None):
         S0 = None if S0 is None else S0[:, hs].contiguous()
     return oracle.chunk_fwd(q.cpu(), k.cpu(), v.cpu(), g.cpu(), beta.cpu(), None if S0 is None else S0.cpu(),
                             None if cu is None else cu.cpu(), gate=inp.get("gate", "log_decay"),
-                            o_gate=None if og is None else og.cpu())
+                            o_gate=None if og is None else og.cpu(), qk_norm=inp.get("qk_norm", False))
 
 
 def _run(inp, o_dtype=None, chunk=16):
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
                       cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk,
-                      gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"))
+                      gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"),
+                      qk_norm=inp.get("qk_norm", False))
     torch.cuda.synchronize()
     return o, Sf
 
@@ -411,4 +412,87 @@ def test_output_gate_k3_prefill_4k_sampled_heads():
     _announce("both_gates_prefill_4k", seed=w.seed)
     inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True, with_o_gate=True)
     inp["gate"] = "scaled_sigmoid"
+    _check(inp, heads=(0, 31, 64, 95))
+
+
+# ------------------------------------------------------------ q/k L2 normalisation in-kernel
+#
+# With qk_norm, the prep kernels divide each raw q and k row (per token and head) by
+# sqrt(|x|^2 + 1e-6) in fp32 as they read it; the oracle normalises the same raw rows in fp64.
+
+def _norm_inputs(B, T, H, K, V, io, seed, **kw):
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=seed, device=DEV, raw_k=True, **kw)
+    inp["qk_norm"] = True
+    return inp
+
+
+@CHUNKS
+@pytest.mark.parametrize("io,B,T,H,K,V", [("fp32", 2, 77, 3, 128, 128), ("fp32", 1, 130, 2, 32, 64),
+                                          ("bf16", 2, 200, 3, 128, 128), ("bf16", 1, 97, 2, 64, 32)])
+def test_qk_norm_shapes(io, B, T, H, K, V, chunk):
+    _announce("qk_norm", io=io, B=B, T=T, H=H, K=K, V=V, chunk=chunk, seed=60)
+    _check(_norm_inputs(B, T, H, K, V, io, 60, with_S0=True), io=io, chunk=chunk)
+
+
+@CHUNKS
+def test_qk_norm_varlen_with_both_gates(chunk):
+    """Packed sequences (empty and ragged ones), raw q and k normalised in-kernel, both gates formed
+    in-kernel: the whole prologue and epilogue at once."""
+    lengths = [37, 0, 16, 1, 150, 64, 0, 65]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("qk_norm_varlen_gates", lengths=lengths, chunk=chunk, seed=61)
+    inp = _norm_inputs(1, cu[-1], 4, 128, 128, "bf16", 61, cu_seqlens=cu, with_S0=True, gate_preact=True,
+                       with_o_gate=True)
+    inp["gate"] = "scaled_sigmoid"
+    _check(inp, chunk=chunk)
+
+
+def test_qk_norm_zero_and_tiny_rows():
+    """fp32: all-zero q and k rows stay zero (no NaN: the 1e-6 under the root), and rows scaled by
+    1e-3 are still normalised (their |x|^2 ~ 1e-4 is well above 1e-6)."""
+    _announce("qk_norm_zero_rows", seed=62)
+    inp = _norm_inputs(1, 70, 2, 64, 64, "fp32", 62, with_S0=True)
+    inp["q"][0, 5] = 0.0
+    inp["k"][0, 9] = 0.0
+    inp["k"][0, 20:40] *= 1e-3
+    inp["q"][0, 30:50] *= 1e-3
+    for chunk in (16, 64):
+        o, Sf = _check(inp, io="fp32", chunk=chunk)
+        assert torch.isfinite(o).all() and torch.isfinite(Sf).all()
+
+
+def test_qk_norm_matches_host_normalised():
+    """fp32: normalising raw rows in the kernel and passing rows normalised on the host (the oracle's
+    fp64 normalisation rounded to fp32) agree to the fp32 parity bound, through prefill and decode."""
+    _announce("qk_norm_vs_host", seed=63)
+    inp = _norm_inputs(1, 300, 4, 64, 64, "fp32", 63, with_S0=True)
+    o_a, S_a = _run(inp, chunk=16)
+    host = dict(inp, q=torch.from_numpy(oracle.l2_normalize(inp["q"].cpu())).float().to(DEV),
+                k=torch.from_numpy(oracle.l2_normalize(inp["k"].cpu())).float().to(DEV), qk_norm=False)
+    o_b, S_b = _run(host, chunk=16)
+    res = {"o": err(o_a.cpu(), o_b.cpu()), "S": err(S_a.cpu(), S_b.cpu())}
+    print("  differences", res, flush=True)
+    assert res["o"] <= TOL_FP32 and res["S"] <= TOL_FP32, res
+
+
+def test_qk_norm_pipelined_ranges():
+    """The combined state/prep kernel of a pipelined call normalises as the plain call does."""
+    _announce("qk_norm_pipelined", seed=64)
+    inp = _norm_inputs(1, 2500, 4, 128, 128, "bf16", 64, with_S0=True, with_o_gate=True)
+    with _Ranges(1):
+        o1, S1 = _run(inp)
+    with _Ranges(4):
+        o4, S4 = _run(inp)
+    assert torch.equal(o1, o4) and torch.equal(S1, S4)
+    _check(inp, heads=(0, 3))
+
+
+def test_all_fused_k3_prefill_4k_sampled_heads():
+    """The prologue-and-epilogue leg of the benchmark: H=96, T=4096, K=V=128, bf16, chunk 16, raw q
+    and k normalised in-kernel, both gates formed in-kernel; 4 heads checked."""
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("all_fused_prefill_4k", seed=w.seed)
+    inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True, with_o_gate=True, raw_k=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp["qk_norm"] = True
     _check(inp, heads=(0, 31, 64, 95))
