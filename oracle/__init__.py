@@ -121,6 +121,72 @@ def l2_normalize(x) -> np.ndarray:
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
 
 
+CONVS = ("none", "short4", "short4_silu")
+
+
+def silu(x) -> np.ndarray:
+    """x * sigmoid(x), in fp64."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def short_conv(x, w, seq_start, act: str = "short4") -> np.ndarray:
+    """Causal depthwise convolution of length 4 over tokens, in fp64.
+
+    "Kimi K3 模型架构解析：KDA、AttnRes 与 Stable LatentMoE", section 二.3 (last
+    paragraph): KDA is combined with a short convolution of length 4 that mixes
+    neighbouring tokens. The pages give neither the exact form nor an
+    activation; the reading taken is the plain causal depthwise one, each
+    channel of each head on its own:
+        y_t[h, c] = sum_{j=0..3} w[h, c, j] * x_{t-3+j}[h, c]
+    (w[..., 3] weights the current token), where tokens before the start of
+    t's sequence count as zero, optionally followed by SiLU (act
+    "short4_silu"). x: [T, H, D] of one packed row; w: [H, D, 4];
+    seq_start: [T] int, the first token of each token's sequence.
+    """
+    x = _f64(x)
+    w = _f64(w)
+    T = x.shape[0]
+    y = np.zeros_like(x)
+    for t in range(T):
+        for j in range(4):
+            tau = t - 3 + j
+            if tau >= seq_start[t]:
+                y[t] += w[:, :, j] * x[tau]
+    return silu(y) if act == "short4_silu" else y
+
+
+def _seq_starts(B, T, cu):
+    """First token of each token's sequence, per batch row ([B, T])."""
+    st = np.zeros((B, T), dtype=np.int64)
+    if cu is None:
+        return st
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        st[0, a:b] = a
+    return st
+
+
+def _apply_conv(q, k, v, conv, conv_w, cu):
+    """The short convolution of q, k and v (conv_w [H, K + K + V, 4]: q channels, then k, then v)."""
+    if conv not in CONVS:
+        raise ValueError("conv must be one of %s" % (CONVS,))
+    if conv == "none":
+        return q, k, v
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    w = _f64(conv_w)
+    if w.shape != (H, 2 * K + V, 4):
+        raise ValueError("conv_w shape %s != %s" % (w.shape, (H, 2 * K + V, 4)))
+    st = _seq_starts(B, T, cu)
+    out = []
+    for x, lo, hi in ((q, 0, K), (k, K, 2 * K), (v, 2 * K, 2 * K + V)):
+        out.append(np.stack([short_conv(x[b], w[:, lo:hi], st[b], conv) for b in range(B)]))
+    return out
+
+
 def _log_decay(g, gate: str) -> np.ndarray:
     if gate not in GATES:
         raise ValueError("gate must be one of %s" % (GATES,))
@@ -128,7 +194,7 @@ def _log_decay(g, gate: str) -> np.ndarray:
 
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate: str = "log_decay",
-              o_gate=None, qk_norm: bool = False):
+              o_gate=None, qk_norm: bool = False, conv: str = "none", conv_w=None):
     """Run the fp64 recurrence over whole sequences.
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H];
@@ -138,9 +204,17 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate
     o_gate: [B, T, H, V] or None; if given, o is output_gate(o, o_gate).
     qk_norm: if true, q and k are replaced by l2_normalize(q), l2_normalize(k)
     (per token and head, over the K key channels) before the recurrence.
+    conv: "none", "short4" or "short4_silu": q, k and v first go through
+    short_conv with the weights conv_w [H, K + K + V, 4] (q channels, then k,
+    then v), restarting at every sequence start; the normalisation follows.
     Returns (o [B, T, H, V], S_final [N, H, K, V]) as float64 arrays.
     """
     g = _log_decay(g, gate)
+    if conv != "none":
+        cu_np = None
+        if cu_seqlens is not None:
+            cu_np = cu_seqlens.detach().cpu().numpy() if hasattr(cu_seqlens, "detach") else np.asarray(cu_seqlens)
+        q, k, v = _apply_conv(q, k, v, conv, conv_w, cu_np)
     if qk_norm:
         q, k = l2_normalize(q), l2_normalize(k)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
@@ -174,13 +248,31 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0, gate
 
 
 def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay", o_gate=None,
-                qk_norm: bool = False):
+                qk_norm: bool = False, conv: str = "none", conv_w=None, conv_cache=None):
     """One decode step. q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H]; S: [N, H, K, V].
 
-    gate, o_gate ([N, H, V] or None) and qk_norm as for chunk_fwd. Returns
-    (o [N, H, V], S_new [N, H, K, V]); the input S is not modified.
+    gate, o_gate ([N, H, V] or None), qk_norm, conv and conv_w as for chunk_fwd.
+    With a conv, conv_cache [N, H, 3, K + K + V] holds the raw q | k | v of the
+    three previous tokens of each sequence, oldest first (zeros before the
+    sequence start): the token is convolved over those three and itself.
+    Returns (o [N, H, V], S_new [N, H, K, V]) and, with a conv, the new cache
+    (the last two rows moved up, the raw token appended); the inputs are not
+    modified.
     """
     g = _log_decay(g, gate)
+    new_cache = None
+    if conv != "none":
+        if conv not in CONVS:
+            raise ValueError("conv must be one of %s" % (CONVS,))
+        cache = _f64(conv_cache)
+        raw = np.concatenate([_f64(q), _f64(k), _f64(v)], axis=-1)  # [N, H, K + K + V]
+        Kq = q.shape[-1]
+        win = np.concatenate([cache, raw[:, :, None, :]], axis=2)   # [N, H, 4, K + K + V] oldest first
+        y = np.einsum("nhjc,hcj->nhc", win, _f64(conv_w))
+        if conv == "short4_silu":
+            y = silu(y)
+        q, k, v = y[..., :Kq], y[..., Kq:2 * Kq], y[..., 2 * Kq:]
+        new_cache = win[:, :, 1:, :].copy()
     if qk_norm:
         q, k = l2_normalize(q), l2_normalize(k)
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
@@ -198,6 +290,8 @@ def decode_step(q, k, v, g, beta, S, threads: int = 0, gate: str = "log_decay", 
         if tuple(o_gate.shape) != o.shape:
             raise ValueError("o_gate shape %s != %s" % (tuple(o_gate.shape), o.shape))
         o = output_gate(o, o_gate)
+    if conv != "none":
+        return o, S_new, new_cache
     return o, S_new
 
 

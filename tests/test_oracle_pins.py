@@ -215,6 +215,88 @@ def test_l2norm_scale_invariance():
     assert kda_pins.rel_err(od2, od1) < 1e-6 and kda_pins.rel_err(Sd2, Sd1) < 1e-6
 
 
+# ------------------------------------------------------------ the short convolution
+
+def test_short_conv_closed_forms():
+    """Taps (0,0,0,1) give x back; taps (0,0,1,0) give the previous token, zero at every sequence start;
+    taps (1,1,1,1) give the running sum of the last four tokens of the sequence. Against a direct
+    numpy.convolve per channel and sequence (an independent formulation) for random taps."""
+    rng = np.random.default_rng(51)
+    T, H, D = 23, 2, 5
+    x = rng.standard_normal((T, H, D))
+    cu = [0, 1, 7, 7, 23]
+    st = np.zeros(T, dtype=np.int64)
+    for a, b in zip(cu[:-1], cu[1:]):
+        st[a:b] = a
+    ident = np.zeros((H, D, 4)); ident[..., 3] = 1.0
+    assert np.array_equal(oracle.short_conv(x, ident, st), x)
+    shift = np.zeros((H, D, 4)); shift[..., 2] = 1.0
+    y = oracle.short_conv(x, shift, st)
+    for t in range(T):
+        assert np.array_equal(y[t], x[t - 1] if t - 1 >= st[t] else np.zeros((H, D)))
+    ones = np.ones((H, D, 4))
+    y = oracle.short_conv(x, ones, st)
+    for t in range(T):
+        ref = sum(x[tau] for tau in range(max(st[t], t - 3), t + 1))
+        assert np.max(np.abs(y[t] - ref)) < 1e-14
+    w = rng.standard_normal((H, D, 4))
+    y = oracle.short_conv(x, w, st)
+    for a, b in zip(cu[:-1], cu[1:]):
+        if a == b:
+            continue
+        for h in range(H):
+            for c in range(D):
+                ref = np.convolve(x[a:b, h, c], w[h, c, ::-1])[: b - a]
+                assert np.max(np.abs(y[a:b, h, c] - ref), initial=0.0) < 1e-13
+
+
+def test_silu_closed_forms():
+    """silu(0) = 0, silu(ln 3) = (3/4) ln 3, silu(x) - silu(-x) = x, silu -> x and -> 0 at the ends."""
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([np.log(3.0)]))[0] - 0.75 * np.log(3.0)) < 1e-15
+    x = np.random.default_rng(52).standard_normal(100) * 4
+    assert np.max(np.abs(oracle.silu(x) - oracle.silu(-x) - x)) < 1e-13
+    assert oracle.silu(np.array([800.0]))[0] == 800.0 and oracle.silu(np.array([-800.0]))[0] == 0.0
+
+
+def test_conv_through_prefill_and_decode():
+    """Identity taps leave prefill unchanged; with random taps, a prefill with the conv equals a plain
+    prefill on inputs convolved by short_conv; and decode steps that carry the 3-token cache reproduce
+    the prefill's outputs, state and (from the raw tokens) cache, with and without SiLU, per sequence."""
+    rng = np.random.default_rng(53)
+    B, T, H, K, V = 1, 13, 2, 4, 3
+    q, k, v, g, beta = kda_pins._rand_problem(rng, B, T, H, K, V)
+    S0 = rng.standard_normal((2, H, K, V))
+    cu = [0, 6, 13]
+    ident = np.zeros((H, 2 * K + V, 4)); ident[..., 3] = 1.0
+    o0, S_0 = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, cu_seqlens=cu)
+    o1, S_1 = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, cu_seqlens=cu, conv="short4", conv_w=ident)
+    assert np.array_equal(o0, o1) and np.array_equal(S_0, S_1)
+    w = rng.standard_normal((H, 2 * K + V, 4)) * 0.5
+    for act in ("short4", "short4_silu"):
+        o, Sf = oracle.chunk_fwd(q, k, v, g, beta, S0=S0, cu_seqlens=cu, conv=act, conv_w=w, qk_norm=True)
+        st = np.array([0] * 6 + [6] * 7)
+        qc = oracle.short_conv(q[0], w[:, :K], st, act)[None]
+        kc = oracle.short_conv(k[0], w[:, K:2 * K], st, act)[None]
+        vc = oracle.short_conv(v[0], w[:, 2 * K:], st, act)[None]
+        o2, S2 = oracle.chunk_fwd(qc, kc, vc, g, beta, S0=S0, cu_seqlens=cu, qk_norm=True)
+        assert kda_pins.rel_err(o, o2) < 1e-14 and kda_pins.rel_err(Sf, S2) < 1e-14
+        for n, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+            S = S0[n:n + 1]
+            cache = np.zeros((1, H, 3, 2 * K + V))
+            for t in range(a, b):
+                sl = (slice(0, 1), t)
+                od, S, cache = oracle.decode_step(q[sl], k[sl], v[sl], g[sl], beta[sl], S, conv=act, conv_w=w,
+                                                  conv_cache=cache, qk_norm=True)
+                assert kda_pins.rel_err(od[0], o[0, t]) < 1e-13
+            assert kda_pins.rel_err(S, Sf[n:n + 1]) < 1e-13
+            raw = np.concatenate([q[0], k[0], v[0]], axis=-1)
+            last = [raw[t] if t >= a else np.zeros((H, 2 * K + V)) for t in range(b - 3, b)]
+            assert np.array_equal(cache[0], np.stack(last, axis=1))
+    with pytest.raises(ValueError):
+        oracle.chunk_fwd(q, k, v, g, beta, conv="short4", conv_w=w[:, :K])
+
+
 # ------------------------------------------------------------ planted mistakes
 #
 # A small numpy re-implementation with switches for plausible mistakes. The
