@@ -47,7 +47,7 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False, qk_norm=False):
+def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False, qk_norm=False, conv="none"):
     lib = _lib.load()
     gc = _lib.GATES[gate]
     qkc = _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
@@ -59,7 +59,11 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False
     N = B
     o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
     Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1)
+    cc = _lib.CONVS[conv]
+    cw = None
+    if conv != "none":
+        cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev)
+    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -67,15 +71,18 @@ def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False
 
     def prep():
         _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1, gc, qkc,
-                                      ws.data_ptr(), wsb, sh), "kda_chunk_prep")
+                                      cc, None if cw is None else cw.data_ptr(), ws.data_ptr(), wsb, sh),
+                   "kda_chunk_prep")
 
     def state():
-        _lib.check(lib.kda_chunk_state(p["v"], og, None, None, B, T, H, K, V, N, chunk, 1, 1, o.data_ptr(),
-                                       Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
+        _lib.check(lib.kda_chunk_state(p["v"], og, None, None, B, T, H, K, V, N, chunk, 1, cc,
+                                       None if cw is None else cw.data_ptr(), 1, o.data_ptr(), Sf.data_ptr(),
+                                       ws.data_ptr(), wsb, sh), "kda_chunk_state")
 
     def fwd():
         _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, None, None, B, T, H, K, V, N, chunk,
-                                     1, gc, qkc, 1, o.data_ptr(), Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
+                                     1, gc, qkc, cc, None if cw is None else cw.data_ptr(), 1, o.data_ptr(),
+                                     Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
 
     # the step: one kda_chunk_fwd call (where the state pass leaves CUs free, the library runs the
     # prep of later chunks beside the state pass of earlier ones)
@@ -302,6 +309,17 @@ def main():
           % (w.name, args.warmup, args.steps), file=sys.stderr, flush=True)
     rn = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True, qk_norm=True)
     msn = rn["wall_s"] * 1e3 / args.steps
+    print("[bench] prefill %s with the short convolution as well: warmup %d, steps %d"
+          % (w.name, args.warmup, args.steps), file=sys.stderr, flush=True)
+    rc = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True, qk_norm=True,
+                      conv="short4_silu")
+    msc = rc["wall_s"] * 1e3 / args.steps
+    out["conv_prologue_epilogue_fused"] = {
+        "workload": "as prologue_epilogue_fused, plus the length-4 short convolution of q, k, v with SiLU "
+                    "(q, k in kda_chunk_prep; v by kda_conv_v into the workspace)",
+        "tokens_per_s": rc["B"] * rc["T"] / (msc * 1e-3), "ms_per_step": msc,
+        "kernels_ms": {"kda_chunk_prep (+chunk table)": rc["prep_ms"],
+                       "kda_conv_v + kda_state_pass": rc["state_ms"]}}
     out["prologue_epilogue_fused"] = {
         "workload": "as gates_fused, with raw q, k ~ N(0,1) L2-normalised per (token, head) in kda_chunk_prep",
         "tokens_per_s": rn["B"] * rn["T"] / (msn * 1e-3), "ms_per_step": msn,

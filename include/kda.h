@@ -95,6 +95,29 @@ typedef enum {
     KDA_QK_L2NORM = 1
 } kda_qk_norm_t;
 
+/*
+ * Short convolution of q, k and v before the recurrence ("Kimi K3 模型架构解析：
+ * KDA、AttnRes 与 Stable LatentMoE", section 二.3: KDA is combined with a short
+ * convolution of length 4 that mixes neighbouring tokens; the pages give no
+ * exact form). Read as the plain causal depthwise convolution, each channel
+ * of each head on its own:
+ *   y_t[c] = sum_{j=0..3} w[h][c][j] * x_{t-3+j}[c]     (w[..][3]: current token)
+ * with tokens before the start of t's sequence counted as zero, applied to
+ * the raw q, k and v (and before the q/k normalisation).
+ *   KDA_CONV_NONE        no convolution; conv_w is ignored (may be NULL).
+ *   KDA_CONV_SHORT4      the convolution above.
+ *   KDA_CONV_SHORT4_SILU the convolution, then SiLU (y * sigmoid(y)).
+ * conv_w: fp32 [H, K + K + V, 4], 16-byte aligned: the q channels of head h,
+ * then its k channels, then its v channels. The convolution runs in fp32; the
+ * prefill keeps the convolved v in the workspace (fp32, or for bf16 I/O as
+ * a bf16 hi + lo pair that carries about 16 significant bits).
+ */
+typedef enum {
+    KDA_CONV_NONE = 0,
+    KDA_CONV_SHORT4 = 1,
+    KDA_CONV_SHORT4_SILU = 2
+} kda_conv_t;
+
 /* Version of this ABI (bumped on any signature change). */
 int kda_abi_version(void);
 
@@ -106,10 +129,13 @@ const char *kda_status_string(kda_status_t status);
  *   B, T        batch rows and tokens per row (packed: B = 1, T = total tokens)
  *   num_seqs    number of sequences: B without cu_seqlens, else len(cu_seqlens)-1
  *   chunk, io   as for kda_chunk_fwd
+ *   conv        as for kda_chunk_fwd (a convolution needs room for the
+ *               convolved v: 4 * B * T * H * V bytes more, fp32 or a bf16
+ *               hi + lo pair)
  * Returns 0 if the sizes are invalid or unsupported.
  */
 size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                                     int32_t num_seqs, int32_t chunk, kda_dtype_t io);
+                                     int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_conv_t conv);
 
 /*
  * Chunked prefill over whole sequences: the recurrence above for every
@@ -117,14 +143,16 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  * chunk", first page cited above).
  *
  * Inputs (dtype `io`):
- *   q, k, g   [B, T, H, K]   q and k as `qk_norm` says, g as `gate` says.
+ *   q, k, g   [B, T, H, K]   q and k as `conv` and `qk_norm` say (in that
+ *                            order), g as `gate` says.
  *                            With KDA_GATE_LOG_DECAY the
  *                            chunk form assumes -5 <= g <= 0 (the bounded
  *                            gate); outside that range results are
  *                            unspecified. With KDA_GATE_SCALED_SIGMOID any
  *                            finite g is valid.
- *   v         [B, T, H, V]
+ *   v         [B, T, H, V]   as `conv` says
  *   beta      [B, T, H]      write strength, used as given
+ *   conv_w    fp32 [H, K + K + V, 4] when conv != KDA_CONV_NONE (see kda_conv_t)
  *   o_gate    [B, T, H, V] or NULL: the output gate's pre-activation z. When
  *             given, each output is scaled channel by channel,
  *             o_t = (S_t^T q_t) * sigmoid(z_t), computed in fp32 before the
@@ -148,7 +176,8 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes().
  * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
  *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow,
- *   unknown dtype, gate or qk_norm),
+ *   unknown dtype, gate, qk_norm or conv, NULL or misaligned conv_w with a
+ *   convolution),
  *   NOT_SUPPORTED (K, V or chunk outside the supported set),
  *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
  */
@@ -156,8 +185,8 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                            int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm,
-                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
-                           size_t workspace_bytes, void *stream);
+                           kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o,
+                           float *S_final, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
@@ -174,11 +203,13 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  *   (chunk, head), forms the cumulative log-decay, the beta-weighted
  *   decay-scaled key products, solves the chunk's unit lower-triangular
  *   system and stores the resulting factors in `workspace` (layout private to
- *   the library). Reads q, k (as `qk_norm` says), g (as `gate` says), beta;
- *   V only sizes the workspace check.
+ *   the library). Reads q, k (as `conv` and `qk_norm` say), g (as `gate`
+ *   says), beta and the q and k parts of conv_w; V only sizes the workspace
+ *   check.
  * kda_chunk_state: the sequential pass over the chunks of each (sequence,
  *   head): carries S from S0 (or 0), writes o (gated by o_gate, if given) and
- *   S_final. Reads v, o_gate, S0 and a
+ *   S_final. With a convolution it first convolves v (the v part of conv_w)
+ *   into the workspace. Reads v, o_gate, S0, conv_w and a
  *   workspace that kda_chunk_prep filled with the same sizes and the same
  *   cu_seqlens pointer (used here only to tell packed from batched input;
  *   not dereferenced). The workspace may not be modified in between.
@@ -187,28 +218,37 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                            kda_qk_norm_t qk_norm, void *workspace, size_t workspace_bytes, void *stream);
+                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, void *workspace,
+                            size_t workspace_bytes, void *stream);
 kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
-                             kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o, float *S_final,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step for N independent sequences, one new token each: the four
  * steps above applied once, with the fixed-size state updated in place
  * ("S_t = Update(S_{t-1}, k_t, v_t)", second page cited above).
  *   q, k, g [N, H, K]; v [N, H, V]; beta [N, H]      dtype `io`
- *   g       as `gate` says; q and k as `qk_norm` says
+ *   g       as `gate` says; q, k and v as `conv` says, then q and k as
+ *           `qk_norm` says
+ *   conv_w  fp32 [H, K + K + V, 4] when conv != KDA_CONV_NONE
+ *   conv_cache [N, H, 3, K + K + V] in dtype `io`, when conv != KDA_CONV_NONE
+ *           (else ignored, may be NULL): the raw q | k | v of the three
+ *           previous tokens of each sequence, oldest first, zeros before the
+ *           sequence start. Read and updated in place: the two newest rows
+ *           move up and this step's raw q | k | v becomes the last row. A
+ *           prefill hands over by filling it from the last three raw tokens.
  *   o_gate  [N, H, V] or NULL: output gate pre-activation, as for kda_chunk_fwd
  *   S       [N, H, K, V] fp32, read and overwritten in place
  *   o       [N, H, V] in `o_dtype`
  * Any finite g is accepted (no chunk-range assumption). S may not alias any
- * other argument. Errors as for kda_chunk_fwd.
+ * other argument, nor may conv_cache. Errors as for kda_chunk_fwd.
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
                              const void *o_gate, float *S, void *o, int32_t N, int32_t H, int32_t K, int32_t V,
-                             kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype,
-                             void *stream);
+                             kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv,
+                             const float *conv_w, void *conv_cache, kda_dtype_t o_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -69,9 +69,17 @@ def _qk_code(qk_norm: bool) -> int:
     return _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
 
 
+def _conv_code(conv: str, conv_w, H: int, C: int, dev) -> int:
+    if conv not in _lib.CONVS:
+        raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
+    if conv != "none":
+        _need(conv_w, "conv_w", (H, C, 4), torch.float32, dev)
+    return _lib.CONVS[conv]
+
+
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
               output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None,
-              qk_norm: bool = False):
+              qk_norm: bool = False, conv: str = "none", conv_w=None):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
@@ -81,7 +89,9 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     mapped to -5*sigmoid(g) inside the kernels). ``o_gate`` [B, T, H, V] (input
     dtype), if given, scales the output channel by channel: o * sigmoid(o_gate).
     ``qk_norm``: if true the kernels divide each q and k row (per token and
-    head) by sqrt(|x|^2 + 1e-6) as they read it.
+    head) by sqrt(|x|^2 + 1e-6) as they read it. ``conv``: "none", "short4" or
+    "short4_silu": the causal length-4 convolution of q, k and v with the taps
+    ``conv_w`` (fp32 [H, K + K + V, 4]), ahead of the normalisation.
     """
     lib = _lib.load()
     dev = q.device
@@ -111,7 +121,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     else:
         _need(out, "out", (B, T, H, V), odt, dev)
     S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
-    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io)
+    cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io, cc)
     if need == 0:
         raise KDAError(2, "kda_chunk_fwd_workspace_bytes(B=%d,T=%d,H=%d,K=%d,V=%d,N=%d,chunk=%d)"
                        % (B, T, H, K, V, N, chunk))
@@ -119,7 +130,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0),
                                _ptr(cu_seqlens),
-                               B, T, H, K, V, N, chunk, io, gc, _qk_code(qk_norm), _io_code(odt), _ptr(out),
+                               B, T, H, K, V, N, chunk, io, gc, _qk_code(qk_norm), cc, _ptr(conv_w), _io_code(odt),
+                               _ptr(out),
                                _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(status, "kda_chunk_fwd")
@@ -127,10 +139,13 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
 
 
 def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_decay", o_gate=None,
-                qk_norm: bool = False):
+                qk_norm: bool = False, conv: str = "none", conv_w=None, conv_cache=None):
     """One decode step; S [N, H, K, V] fp32 is updated in place. Returns o [N, H, V].
 
-    ``gate``, ``o_gate`` ([N, H, V]) and ``qk_norm`` as for :func:`chunk_fwd`.
+    ``gate``, ``o_gate`` ([N, H, V]), ``qk_norm``, ``conv`` and ``conv_w`` as for
+    :func:`chunk_fwd`. With a convolution, ``conv_cache`` [N, H, 3, K + K + V]
+    (input dtype) holds the raw q | k | v of the three previous tokens, oldest
+    first; it is updated in place.
     """
     lib = _lib.load()
     dev = q.device
@@ -151,7 +166,11 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
         out = torch.empty((N, H, V), dtype=odt, device=dev)
     else:
         _need(out, "out", (N, H, V), odt, dev)
+    cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
+    if cc:
+        _need(conv_cache, "conv_cache", (N, H, 3, 2 * K + V), dt, dev)
     status = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S), _ptr(out),
-                                 N, H, K, V, io, gc, _qk_code(qk_norm), _io_code(odt), _stream(dev))
+                                 N, H, K, V, io, gc, _qk_code(qk_norm), cc, _ptr(conv_w) if cc else None,
+                                 _ptr(conv_cache) if cc else None, _io_code(odt), _stream(dev))
     _lib.check(status, "kda_decode_step")
     return out

@@ -18,12 +18,13 @@ KDA_GATE_SCALED_SIGMOID = 1
 GATES = {"log_decay": KDA_GATE_LOG_DECAY, "scaled_sigmoid": KDA_GATE_SCALED_SIGMOID}
 KDA_QK_AS_GIVEN = 0
 KDA_QK_L2NORM = 1
+CONVS = {"none": 0, "short4": 1, "short4_silu": 2}
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
           3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_NO_DEVICE", 5: "KDA_ERROR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_prep", "kda_chunk_state", "kda_decode_step")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 _lib = None
 
 
@@ -51,19 +52,20 @@ def load() -> ctypes.CDLL:
     lib.kda_abi_version.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
-    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, vp]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp,
+                                  sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_int, vp, sz, vp]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
     lib.kda_chunk_prep.restype = ctypes.c_int
     lib.kda_chunk_state.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
-                                    vp, vp, vp, sz, vp]
+                                    vp, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.kda_chunk_state.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, vp]
+                                    ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -18,6 +18,9 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_BF16; }
 bool valid_gate(kda_gate_t g) { return g == KDA_GATE_LOG_DECAY || g == KDA_GATE_SCALED_SIGMOID; }
 bool valid_qk_norm(kda_qk_norm_t n) { return n == KDA_QK_AS_GIVEN || n == KDA_QK_L2NORM; }
+bool valid_conv(kda_conv_t c) { return c == KDA_CONV_NONE || c == KDA_CONV_SHORT4 || c == KDA_CONV_SHORT4_SILU; }
+// With a convolution the weights must be given and 16-byte aligned (one float4 per channel).
+bool valid_conv_w(kda_conv_t c, const float *w) { return c == KDA_CONV_NONE || (w && aligned16(w)); }
 // beta is read one element at a time: natural alignment of its dtype suffices
 bool aligned_elem(const void *p, kda_dtype_t t) { return ((uintptr_t)p & (t == KDA_DTYPE_BF16 ? 1u : 3u)) == 0; }
 
@@ -58,7 +61,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 4; }
+int kda_abi_version(void) { return 5; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -73,13 +76,14 @@ const char *kda_status_string(kda_status_t s) {
 }
 
 size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                                     int32_t chunk, kda_dtype_t io) {
-    if (!valid_dtype(io)) return 0;
+                                     int32_t chunk, kda_dtype_t io, kda_conv_t conv) {
+    if (!valid_dtype(io) || !valid_conv(conv)) return 0;
     // B == 1 may be packed (cu_seqlens) or not; the packed bound is the larger and covers both
     const bool packed = (B == 1);
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
-    return kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk);
+    return kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
+                                        conv != KDA_CONV_NONE);
 }
 
 namespace {
@@ -88,9 +92,11 @@ namespace {
 kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
                           int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                          kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
-                          size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm))
+                          kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o,
+                          float *S_final, const void *workspace, size_t workspace_bytes, bool need_prep,
+                          bool need_state, kda::PrefillArgs &a) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm) ||
+        !valid_conv(conv) || !valid_conv_w(conv, conv_w))
         return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed);
@@ -104,7 +110,8 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
-    const size_t need = kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk);
+    const size_t need = kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
+                                                     conv != KDA_CONV_NONE);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
@@ -115,6 +122,8 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
     a.qk_l2norm = qk_norm == KDA_QK_L2NORM;
+    a.conv = (int32_t)conv;
+    a.conv_w = conv == KDA_CONV_NONE ? nullptr : conv_w;
     a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
     a.chunk = chunk;
     a.n_chunks_max = nc;
@@ -125,11 +134,13 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
                            int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
-                           kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *o, float *S_final,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+                           kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w,
+                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                           void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, v, g, beta, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
-                                   qk_norm, o_dtype, o, S_final, workspace, workspace_bytes, true, true, a);
+                                   qk_norm, conv, conv_w, o_dtype, o, S_final, workspace, workspace_bytes, true, true,
+                                   a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -138,10 +149,12 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                            kda_qk_norm_t qk_norm, void *workspace, size_t workspace_bytes, void *stream) {
+                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, void *workspace,
+                            size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
-                                   gate, qk_norm, io, nullptr, nullptr, workspace, workspace_bytes, true, false, a);
+                                   gate, qk_norm, conv, conv_w, io, nullptr, nullptr, workspace, workspace_bytes, true,
+                                   false, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -150,12 +163,12 @@ kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const v
 kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens,
                              int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
-                             kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o, float *S_final,
+                             void *workspace, size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs,
-                                   chunk, io, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, o_dtype, o, S_final, workspace,
-                                   workspace_bytes,
+                                   chunk, io, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, conv, conv_w, o_dtype, o, S_final,
+                                   workspace, workspace_bytes,
                                    false, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_state(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
@@ -165,8 +178,10 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g, const void *beta,
                              const void *o_gate, float *S,
                              void *o, int32_t N, int32_t H, int32_t K, int32_t V, kda_dtype_t io,
-                             kda_gate_t gate, kda_qk_norm_t qk_norm, kda_dtype_t o_dtype, void *stream) {
-    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm))
+                             kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w,
+                             void *conv_cache, kda_dtype_t o_dtype, void *stream) {
+    if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm) ||
+        !valid_conv(conv) || !valid_conv_w(conv, conv_w))
         return KDA_ERROR_INVALID_VALUE;
     if (N < 0 || H < 1) return KDA_ERROR_INVALID_VALUE;
     if (!supported_dim(K) || !supported_dim(V)) return KDA_ERROR_NOT_SUPPORTED;
@@ -181,6 +196,12 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     if ((const void *)S == q || (const void *)S == k || (const void *)S == v || (const void *)S == g ||
         (const void *)S == beta || (const void *)S == o || (const void *)S == o_gate)
         return KDA_ERROR_INVALID_VALUE;
+    if (conv != KDA_CONV_NONE) {
+        if (!conv_cache || !aligned16(conv_cache)) return KDA_ERROR_INVALID_VALUE;
+        const void *others[] = {q, k, v, g, beta, o, o_gate, S, conv_w};
+        for (const void *p : others)
+            if (p == conv_cache) return KDA_ERROR_INVALID_VALUE;
+    }
     kda_status_t st = check_device();
     if (st != KDA_SUCCESS) return st;
     kda::DecodeArgs a;
@@ -191,6 +212,9 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     a.o_bf16 = o_dtype == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
     a.qk_l2norm = qk_norm == KDA_QK_L2NORM;
+    a.conv = (int32_t)conv;
+    a.conv_w = conv == KDA_CONV_NONE ? nullptr : conv_w;
+    a.conv_cache = conv == KDA_CONV_NONE ? nullptr : conv_cache;
     if (kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }

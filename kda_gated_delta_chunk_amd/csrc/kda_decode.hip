@@ -39,7 +39,8 @@ template <bool BF, int K, int V, int NT>
 __global__ __launch_bounds__(NT) void kda_decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
     const void *__restrict__ gp, const void *__restrict__ bp, const void *__restrict__ zp, float *__restrict__ S,
-    void *__restrict__ op, int o_bf16, int gate, int qknorm, int32_t NH) {
+    void *__restrict__ op, int o_bf16, int gate, int qknorm, int conv, const float *__restrict__ convw,
+    void *__restrict__ cachep, int32_t H, int32_t NH) {
     constexpr int CG = V / 4;          // column groups (float4) per row
     constexpr int RG = NT / CG;        // row groups
     constexpr int RPT = K / RG;        // rows per thread
@@ -56,30 +57,83 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
     int nh = blockIdx.x;
     if (nh >= NH) return;
 
-    // state rows and token values of one (n, h) pair, held in registers
+    // state rows and token values of one (n, h) pair, held in registers; with a convolution also
+    // the pair's cached raw q | k | v of the three previous tokens and the channel's taps
+    constexpr int CW = 2 * K + V;  // channels of a cache row and of a head's taps
+    struct Conv {
+        float cq[3], ck[3], cv[3];
+        float4 wq, wk, wv;
+    };
     f32x4 s[RPT];
     float kt = 0.f, qt = 0.f, gt = 0.f, vt = 0.f, beta;
-    auto load_pair = [&](int p, f32x4 (&st)[RPT], float &kk, float &qq, float &gg, float &vv, float &bb) {
+    Conv cv;
+    auto load_pair = [&](int p, f32x4 (&st)[RPT], float &kk, float &qq, float &gg, float &vv, float &bb, Conv &c) {
         const float *Sp = S + (size_t)p * K * V;
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             st[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (size_t)(rg + RG * j) * V) + cg);
+        const E *cache = conv ? reinterpret_cast<const E *>(cachep) + (size_t)p * 3 * CW : nullptr;
+        const float *wh = conv ? convw + (size_t)(p % H) * CW * 4 : nullptr;
         if (t < K) {
             kk = IO<BF>::ld(reinterpret_cast<const E *>(kp) + (size_t)p * K, t);
             qq = IO<BF>::ld(reinterpret_cast<const E *>(qp) + (size_t)p * K, t);
             gg = IO<BF>::ld(reinterpret_cast<const E *>(gp) + (size_t)p * K, t);
+            if (conv) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    c.cq[j] = IO<BF>::ld(cache, j * CW + t);
+                    c.ck[j] = IO<BF>::ld(cache, j * CW + K + t);
+                }
+                c.wq = *reinterpret_cast<const float4 *>(wh + 4 * t);
+                c.wk = *reinterpret_cast<const float4 *>(wh + 4 * (K + t));
+            }
         }
-        if (t < V) vv = IO<BF>::ld(reinterpret_cast<const E *>(vp) + (size_t)p * V, t);
+        if (t < V) {
+            vv = IO<BF>::ld(reinterpret_cast<const E *>(vp) + (size_t)p * V, t);
+            if (conv) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) c.cv[j] = IO<BF>::ld(cache, j * CW + 2 * K + t);
+                c.wv = *reinterpret_cast<const float4 *>(wh + 4 * (2 * K + t));
+            }
+        }
         bb = IO<BF>::ld(reinterpret_cast<const E *>(bp), p);
     };
-    load_pair(nh, s, kt, qt, gt, vt, beta);
+    // y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3} (cache row 2 is t-1), then SiLU for conv == 2
+    auto conv4 = [&](const float4 &w, const float (&c)[3], float x) {
+        const float y = w.w * x + w.z * c[2] + w.y * c[1] + w.x * c[0];
+        return conv == 2 ? y * sigmoid_f(y) : y;
+    };
+    load_pair(nh, s, kt, qt, gt, vt, beta, cv);
 
     for (;;) {
         // 1. the next pair's loads go out first; they stay in flight through this pair's work
         const int nx = nh + gridDim.x;
         f32x4 sn[RPT];
         float ktn = 0.f, qtn = 0.f, gtn = 0.f, vtn = 0.f, betan = 0.f;
-        if (nx < NH) load_pair(nx, sn, ktn, qtn, gtn, vtn, betan);
+        Conv cvn;
+        if (nx < NH) load_pair(nx, sn, ktn, qtn, gtn, vtn, betan, cvn);
+
+        // 1b. short convolution over the cached three previous raw tokens; the cache moves up one
+        //     row and takes this token's raw q | k | v (each lane rewrites only what it read)
+        if (conv) {
+            E *cache = reinterpret_cast<E *>(cachep) + (size_t)nh * 3 * CW;
+            if (t < K) {
+                IO<BF>::st(cache, t, cv.cq[1]);
+                IO<BF>::st(cache, CW + t, cv.cq[2]);
+                IO<BF>::st(cache, 2 * CW + t, qt);
+                IO<BF>::st(cache, K + t, cv.ck[1]);
+                IO<BF>::st(cache, CW + K + t, cv.ck[2]);
+                IO<BF>::st(cache, 2 * CW + K + t, kt);
+                qt = conv4(cv.wq, cv.cq, qt);
+                kt = conv4(cv.wk, cv.ck, kt);
+            }
+            if (t < V) {
+                IO<BF>::st(cache, 2 * K + t, cv.cv[1]);
+                IO<BF>::st(cache, CW + 2 * K + t, cv.cv[2]);
+                IO<BF>::st(cache, 2 * CW + 2 * K + t, vt);
+                vt = conv4(cv.wv, cv.cv, vt);
+            }
+        }
 
         // 2. token vectors to LDS; alpha = exp(log-decay); k.q (and |k|^2, |q|^2 when q and k are
         //    normalised) by wave reduction, then across waves
@@ -195,6 +249,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
 #pragma unroll
         for (int j = 0; j < RPT; ++j) s[j] = sn[j];
         kt = ktn; qt = qtn; gt = gtn; vt = vtn; beta = betan;
+        cv = cvn;
     }
 }
 
@@ -211,7 +266,8 @@ hipError_t launch_dkv(const DecodeArgs &a, int32_t NH, hipStream_t st) {
     // up to 4096 workgroups take one pair each; above that each workgroup walks about 4 pairs
     const int32_t grid = NH <= 4096 ? NH : (NH + 3) / 4 > 4096 ? (NH + 3) / 4 : 4096;
     hipLaunchKernelGGL((kda_decode_kernel<BF, K, V, NT>), dim3(grid), dim3(NT), 0, st, a.q, a.k, a.v, a.g, a.beta,
-                       a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm, NH);
+                       a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm, (int)a.conv, a.conv_w,
+                       a.conv_cache, a.H, NH);
     return hipGetLastError();
 }
 template <bool BF, int K>

@@ -18,6 +18,8 @@ struct PrefillArgs {
     bool io_bf16, o_bf16;
     bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
     bool qk_l2norm;        // q and k are L2-normalised per (token, head) as they are read
+    int32_t conv;          // 0: none; 1: short convolution; 2: short convolution then SiLU
+    const float *conv_w;   // [H, K + K + V, 4] fp32 (q, k, v channels), or null without a convolution
     void *o;
     float *S_final;
     void *workspace;
@@ -25,9 +27,9 @@ struct PrefillArgs {
     int64_t n_chunks_max;  // upper bound on chunks over all sequences
 };
 
-// Workspace bytes for a prefill with at most n_chunks_max chunks.
+// Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens.
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk);
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv);
 // Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
 // Enqueue the state pass over a workspace that launch_prep filled with the same sizes.
@@ -46,6 +48,9 @@ struct DecodeArgs {
     bool io_bf16, o_bf16;
     bool gate_sigmoid;     // g holds the gate pre-activation, not the log-decay
     bool qk_l2norm;        // q and k are L2-normalised per (n, h) as they are read
+    int32_t conv;          // as for PrefillArgs
+    const float *conv_w;
+    void *conv_cache;      // [N, H, 3, K + K + V] raw q | k | v of the previous 3 tokens (I/O dtype), or null
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

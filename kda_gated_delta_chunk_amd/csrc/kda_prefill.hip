@@ -255,6 +255,32 @@ __device__ __forceinline__ void l2norm_row(float (&x)[KS][8]) {
         for (int j = 0; j < 8; ++j) x[s][j] *= rn;
 }
 
+// Short convolution of one 8-channel run of a token row, in fp32: x (the run of token `tok`, already
+// loaded) becomes sum_{d=0..3} w[c][3-d] * x_{tok-d}[c] over the tokens of its sequence (tok - d >= seq0),
+// c = c0 .. c0+7; then SiLU when act == 2. base: [tokens][H][D] (row stride D); w: the tensor's weights
+// of head h, [D][4] fp32. Earlier rows are loaded clamped to the sequence start and dropped by a
+// select, so every load is unconditional and stays in flight with the others.
+template <bool BF>
+__device__ __forceinline__ void conv_run8(const void *base, int64_t tok, int64_t seq0, int32_t H, int h, int D,
+                                          int c0, const float *__restrict__ w, int act, float (&x)[8]) {
+    float p[3][8];
+    bool ok[3];
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        ok[d - 1] = tok - d >= seq0;
+        load8<BF>(base, ((ok[d - 1] ? tok - d : seq0) * H + h) * D + c0, p[d - 1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 wc = *reinterpret_cast<const float4 *>(w + 4 * (c0 + j));
+        float y = wc.w * x[j];
+        y = ok[0] ? __builtin_fmaf(wc.z, p[0][j], y) : y;
+        y = ok[1] ? __builtin_fmaf(wc.y, p[1][j], y) : y;
+        y = ok[2] ? __builtin_fmaf(wc.x, p[2][j], y) : y;
+        x[j] = act == 2 ? y * sigmoid_f(y) : y;
+    }
+}
+
 // mma32 operands from eight fp32 values: rounded (single) or split into hi + lo.
 __device__ __forceinline__ Frag8<true> frag8_of(const float (&x)[8], Frag8<true>) {
     Frag8<true> f;
@@ -434,6 +460,9 @@ struct PrepParams {
     int32_t H, N;
     int32_t gate;    // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
     int32_t qknorm;  // 1: q and k rows are L2-normalised as they are read (l2norm_row)
+    int32_t conv;    // 0: none; 1: short convolution of q and k (conv_run8); 2: the same, then SiLU
+    const float *convw;  // [H][K + K + V][4] fp32, or null
+    int32_t V;
     ChunkTab tab;
     char *frags;
     int32_t g0, g1;
@@ -442,7 +471,7 @@ struct PrepParams {
 // The 16-token prep of item (chunk g0 + item / H, head item % H) by one
 // wavefront, with D::WAVE bytes of LDS of its own at `lds`. No workgroup
 // barriers: wavefronts of a workgroup are independent.
-template <bool BF, int K>
+template <bool BF, int K, bool CONV = false>
 __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, char *lds) {
     using L = SubLayout<BF, K, 1>;
     using D = PrepLds<BF, K>;
@@ -474,11 +503,33 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     const bool valid = r < nvalid;
     const int64_t row = (tok0 + (valid ? r : nvalid - 1)) * H + h;
     float qv[KS][8], kv[KS][8], bl[KS][8];
+    if constexpr (CONV) {
+        // q, then k, one 8-channel run at a time: the run's row, the three earlier rows and its taps
+        // (the scheduling barriers keep one run's values live, not all of them); then g
+        const int64_t tokl = tok0 + (valid ? r : nvalid - 1);
+        const float *wh = pa.convw + (size_t)h * (2 * K + pa.V) * 4;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
-        load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
-        load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            conv_run8<BF>(qp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh, pa.conv, qv[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            conv_run8<BF>(kp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh + 4 * K, pa.conv, kv[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+        }
     }
     if (pa.qknorm) {  // wave-uniform
         l2norm_row<KS>(qv);
@@ -613,11 +664,11 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
 
 // At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
 // the matrix-core accumulators in VGPRs, as mfma_fence expects.
-template <bool BF, int K>
+template <bool BF, int K, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(PrepParams pa) {
     extern __shared__ __align__(16) char smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    prep16_item<BF, K>(pa, (int64_t)blockIdx.x * 4 + wave, smem + wave * PrepLds<BF, K>::WAVE);
+    prep16_item<BF, K, CONV>(pa, (int64_t)blockIdx.x * 4 + wave, smem + wave * PrepLds<BF, K>::WAVE);
 }
 
 // ------------------------------------------------- chunk prep, 64 tokens
@@ -666,7 +717,7 @@ __device__ __forceinline__ void scale8(const float (&x)[8], const float (&f)[8],
     for (int j = 0; j < 8; ++j) y[j] = x[j] * f[j];
 }
 
-template <bool BF, int K>
+template <bool BF, int K, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep64(PrepParams pa) {
     constexpr int CS = 4;
     using L = SubLayout<BF, K, CS>;
@@ -700,11 +751,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const bool valid = SUB * R + r < nvc;
     const int64_t row = (t0c + (valid ? SUB * R + r : nvc - 1)) * H + h;
     float qv[KS][8], kv[KS][8], bl[KS][8];
+    if constexpr (CONV) {
+        // q, then k, one 8-channel run at a time: the run's row, the three earlier rows and its taps
+        // (the scheduling barriers keep one run's values live, not all of them); then g
+        const int64_t tokl = t0c + (valid ? SUB * R + r : nvc - 1);
+        const float *wh = pa.convw + (size_t)h * (2 * K + pa.V) * 4;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
-        load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
-        load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            conv_run8<BF>(qp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh, pa.conv, qv[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            conv_run8<BF>(kp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh + 4 * K, pa.conv, kv[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+        }
     }
     if (pa.qknorm) {  // wave-uniform
         l2norm_row<KS>(qv);
@@ -982,6 +1055,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
+// ----------------------------------------------- short convolution of v
+// v convolved (conv_run8) into the workspace, where the state pass then reads it (bf16: as hi + lo
+// parts, so that the state pass's T V keeps the convolution's fp32 result). One workgroup per
+// (16-token sub-tile, head); thread t takes token row t / (V/8) of the sub-tile and the 8 channels
+// 8 (t % (V/8)) .. +7. Rows past the sequence end are not written (the state pass never reads them).
+template <bool BF, int V, int CS>
+__global__ __launch_bounds__(256) void kda_conv_v(const void *__restrict__ vp, const float *__restrict__ convw,
+                                                  int32_t K, int32_t act, int32_t H, int32_t N, ChunkTab tab,
+                                                  void *__restrict__ out, void *__restrict__ out_lo) {
+    constexpr int G = V / 8;  // 8-channel runs per row
+    const int t = threadIdx.x;
+    if (t >= 16 * G) return;  // no barriers in this kernel
+    const int64_t item = blockIdx.x;
+    const int h = (int)(item % H);
+    const int64_t su = item / H;  // global sub-tile: chunk su / CS, sub-tile su % CS
+    const int gc = (int)(su / CS), u = (int)(su % CS);
+    if (gc >= tab.off(N)) return;
+    const int n = tab.find(N, gc);
+    const int64_t seq0 = tab.tok(n), seq1 = tab.tok(n + 1);
+    const int64_t tok = seq0 + (int64_t)(gc - tab.off(n)) * (CS * SUB) + u * SUB + t / G;
+    if (tok >= seq1) return;
+    const int c0 = 8 * (t % G);
+    float x[8];
+    load8<BF>(vp, (tok * H + h) * V + c0, x);
+    conv_run8<BF>(vp, tok, seq0, H, h, V, c0, convw + ((size_t)h * (2 * K + V) + 2 * K) * 4, act, x);
+    if constexpr (BF) {  // hi = bf16(x), lo = bf16(x - hi): about 16 significant bits between them
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_bf16(x[2 * i], x[2 * i + 1], hi[i], lo[i]);
+        const int64_t e = (tok * H + h) * V + c0;
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_lo) + e) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    } else {
+        float *o = reinterpret_cast<float *>(out) + (tok * H + h) * V + c0;
+        *reinterpret_cast<float4 *>(o) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+}
+
 // ------------------------------------------------------ state pass (K3+K4)
 // Asynchronous global -> LDS copy of 16 bytes per lane (64 lanes = 1 KiB, lane
 // l lands at lds + 16*l). Issued from inline assembly so that the compiler
@@ -1062,7 +1174,9 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // chunks carry the chunk's earlier corrected values in registers and use one
 // tile per wavefront. Loader k copies sub-tiles k, k+NL, k+2NL, ..., one at a
 // time, each as soon as its slot is free.
-template <bool BF, int K, int V, int CS>
+// VLO: v comes as a bf16 hi + lo pair (a convolved v, whose values are not bf16 themselves); the
+// loaders copy both parts and the W product takes T V_hi + T V_lo.
+template <bool BF, int K, int V, int CS, bool VLO = false>
 struct StateCfg {
     using L = SubLayout<BF, K, CS>;
     // One 16-column tile per compute wavefront, four compute wavefronts per workgroup: at V = 128 a
@@ -1077,7 +1191,8 @@ struct StateCfg {
     static constexpr int KU = L::UNITS;
     static constexpr int VB = 16 * VT * ES;        // v tile bytes (16 tokens x VT columns)
     static constexpr int VU = (VB + 1023) / 1024;
-    static constexpr int U = KU + VU;              // 1 KiB copies per sub-tile
+    static constexpr int VUL = VLO ? VU : 0;       // copies of the lo part
+    static constexpr int U = KU + VU + VUL;        // 1 KiB copies per sub-tile
     static constexpr int SLOT = U * 1024;
     static constexpr int OPITCH = VT + 4;          // fp32 o staging row pitch (bank spread)
     static constexpr int OROWS = 16 * OPITCH * 4;  // one sub-tile's o rows
@@ -1131,6 +1246,7 @@ template <bool BF> __device__ __forceinline__ Frag4<BF> zero_frag4() {
 // launch that covers range 0 (`first`).
 struct StateParams {
     const void *v;
+    const void *vlo;    // lo parts of v (StateCfg VLO), else null
     const void *ogate;  // output-gate pre-activation [tokens][H][V] (I/O dtype), or null
     const float *S0;
     void *o;
@@ -1145,9 +1261,10 @@ struct StateParams {
 };
 
 // The state pass of workgroup `bid` (C::LDS bytes of LDS at smem).
-template <bool BF, int K, int V, int CS>
+template <bool BF, int K, int V, int CS, bool VLO = false>
 __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char *smem) {
-    using C = StateCfg<BF, K, V, CS>;
+    static_assert(!VLO || BF, "the lo part of v is for bf16 operands");
+    using C = StateCfg<BF, K, V, CS, VLO>;
     using L = SubLayout<BF, K, CS>;
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, D = C::D, NL = C::NL;
     constexpr int CT = C::CT, VT = C::VT, NT = C::NT;
@@ -1281,6 +1398,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                 const int64_t tok = (rw < nval) ? tok0 + rw : s1 - 1;
                 const char *src = vbase + ((tok * H + h) * V + (int64_t)tile * VT) * ES + within;
                 dma16(slot + (uint32_t)((C::KU + q) * 1024), src);
+                if constexpr (VLO)
+                    dma16(slot + (uint32_t)((C::KU + C::VU + q) * 1024),
+                          reinterpret_cast<const char *>(pa.vlo) + (src - vbase));
             }
         };
         // Loader k copies sub-tiles x = k, k+NL, ... (x to slot x % D once every compute
@@ -1364,9 +1484,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     // LDS at about 23 bytes per clock, so a step's 22 KiB of operands must stream in while
     // products run): T tiles, the v tile (raw row words, assembled into fragments when used),
     // -Wk, Q*Gamma (hi, lo). Part p of read_ahead covers a quarter of them.
-    Frag4<BF> tt[CS], vf[CT];
+    Frag4<BF> tt[CS], vf[CT], vfl[CT];
     Frag8<BF> wk[KS], qh[KS], ql[KS];
-    uint32_t vraw[4 * CT];
+    uint32_t vraw[4 * CT], vrawl[4 * CT];
     auto read_ahead = [&](const char *sl, int part) {
         if (part == 0) {
 #pragma unroll
@@ -1383,6 +1503,11 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int I = 0; I < CS; ++I) tt[I] = ld_frag4<BF>(sl + L::TT + (I * 64 + lane) * 4 * ES);
             const char *vt = sl + C::KU * 1024;
+            if constexpr (VLO) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    vrawl[j] = *reinterpret_cast<const uint16_t *>(vt + C::VU * 1024 + ((4 * tg + j) * VT + lc) * ES);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const char *row = vt + ((4 * tg + j) * VT + lc) * ES;  // token 4tg+j, columns lc ..
@@ -1405,6 +1530,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         } else if constexpr (BF) {
             vf[0].p[0] = vraw[0] | (vraw[1] << 16);
             vf[0].p[1] = vraw[2] | (vraw[3] << 16);
+            if constexpr (VLO) {
+                vfl[0].p[0] = vrawl[0] | (vrawl[1] << 16);
+                vfl[0].p[1] = vrawl[2] | (vrawl[3] << 16);
+            }
         } else if constexpr (CT == 2) {
             set4(vf[0], __uint_as_float(vraw[0]), __uint_as_float(vraw[2]), __uint_as_float(vraw[4]),
                  __uint_as_float(vraw[6]));
@@ -1418,7 +1547,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 
     // 64-token chunks: v fragments and corrected values of the chunk's earlier sub-tiles
     // (bf16: [Wh | Wh] and [Wl | Wl]; fp32: [W | 0] in whist)
-    Frag4<BF> vhist[CS][CT];
+    Frag4<BF> vhist[CS][CT], vhistl[CS][CT];
     Frag8<BF> whist[CS][CT], wlist[CS][CT];
     // o rows of a step: computed in step u, staged to obuf[u % NB] during step u+1 (once the
     // loader has read out sub-tile u - NB from that buffer)
@@ -1500,7 +1629,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         for (int I = 0; I < CS; ++I)
             if (I == R)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) vhist[I][ct] = vf[ct];
+                for (int ct = 0; ct < CT; ++ct) {
+                    vhist[I][ct] = vf[ct];
+                    if constexpr (VLO) vhistl[I][ct] = vfl[ct];
+                }
 
         // ---- phase A: W = sum_{I<=R} T_RI V_I + (-Wk) S (operands read one step ahead), while
         // this step's other operands are read. One accumulation chain per tile, every product
@@ -1515,8 +1647,17 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                 if (I > R) continue;
                 const bool two = I + 1 <= R;
                 const Frag4<BF> z = zero_frag4<BF>();
-                W[ct] = mma32(W[ct], cat4(tt[I], two ? tt[I + 1 < CS ? I + 1 : I] : z),
-                              cat4(vhist[I][ct], two ? vhist[I + 1 < CS ? I + 1 : I][ct] : z));
+                if constexpr (VLO) {
+                    // a lone tile takes its lo part in the other half: [T | T] x [V_hi | V_lo];
+                    // a pair takes a second product [T_I | T_I'] x [V_lo,I | V_lo,I']
+                    const int I1 = I + 1 < CS ? I + 1 : I;
+                    W[ct] = mma32(W[ct], cat4(tt[I], two ? tt[I1] : tt[I]),
+                                  cat4(vhist[I][ct], two ? vhist[I1][ct] : vhistl[I][ct]));
+                    if (two) W[ct] = mma32(W[ct], cat4(tt[I], tt[I1]), cat4(vhistl[I][ct], vhistl[I1][ct]));
+                } else {
+                    W[ct] = mma32(W[ct], cat4(tt[I], two ? tt[I + 1 < CS ? I + 1 : I] : z),
+                                  cat4(vhist[I][ct], two ? vhist[I + 1 < CS ? I + 1 : I][ct] : z));
+                }
             }
 #pragma unroll
             for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
@@ -1679,10 +1820,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     }
 }
 
-template <bool BF, int K, int V, int CS>
-__global__ __launch_bounds__((StateCfg<BF, K, V, CS>::THREADS)) void kda_state_pass(StateParams pa) {
+template <bool BF, int K, int V, int CS, bool VLO>
+__global__ __launch_bounds__((StateCfg<BF, K, V, CS, VLO>::THREADS)) void kda_state_pass(StateParams pa) {
     extern __shared__ __align__(1024) char smem[];
-    state_body<BF, K, V, CS>(pa, blockIdx.x, smem);
+    state_body<BF, K, V, CS, VLO>(pa, blockIdx.x, smem);
 }
 
 // Prep wavefronts per workgroup of the combined kernel below (each owns PrepLds::WAVE bytes of
@@ -1746,16 +1887,28 @@ struct WsPtrs {
     int32_t *chunk_off;
     char *frags;
     float *carry;  // state between chunk ranges (pipelined calls only)
+    char *vconv;     // convolved v [tokens][H][V] in the I/O dtype (calls with a convolution only); bf16:
+    char *vconv_lo;  // the hi parts, and here the lo parts (v - hi rounded to bf16)
 };
+bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk);
+// Workspace: chunk table | per-(chunk, head) factors | carry (pipelined calls) | convolved v (with a
+// convolution). The sizes depend only on the call's sizes, as prefill_workspace_bytes counts them.
+size_t frags_bytes(int64_t n_chunks_max, int32_t H, int32_t K, bool io_bf16, int32_t chunk) {
+    return align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk));
+}
+size_t carry_bytes(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t K, int32_t V, int32_t chunk) {
+    return can_pipeline(n_chunks_max, num_seqs, H, chunk) ? align_up((size_t)num_seqs * H * K * V * sizeof(float)) : 0;
+}
 WsPtrs ws_ptrs(const PrefillArgs &a) {
     WsPtrs w;
     char *base = reinterpret_cast<char *>(a.workspace);
     w.seq_tok = reinterpret_cast<int64_t *>(base);
     w.chunk_off = reinterpret_cast<int32_t *>(base + align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
     w.frags = base + table_bytes(a.num_seqs);
-    w.carry = reinterpret_cast<float *>(
-        base + table_bytes(a.num_seqs) +
-        align_up((size_t)a.n_chunks_max * (size_t)a.H * chunk_bytes_rt(a.io_bf16, a.K, a.chunk)));
+    char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk);
+    w.carry = reinterpret_cast<float *>(cp);
+    w.vconv = cp + carry_bytes(a.n_chunks_max, a.num_seqs, a.H, a.K, a.V, a.chunk);
+    w.vconv_lo = w.vconv + (size_t)a.B * a.T * a.H * a.V * 2;
     return w;
 }
 
@@ -1786,6 +1939,9 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
     p.H = a.H; p.N = a.num_seqs;
     p.gate = a.gate_sigmoid ? 1 : 0;
     p.qknorm = a.qk_l2norm ? 1 : 0;
+    p.conv = a.conv;
+    p.convw = a.conv_w;
+    p.V = a.V;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     return p;
@@ -1793,7 +1949,9 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
 
 StateParams state_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first) {
     StateParams p;
-    p.v = a.v; p.ogate = a.o_gate; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
+    p.v = a.conv ? static_cast<const void *>(w.vconv) : a.v;  // with a convolution: the convolved v
+    p.vlo = (a.conv && a.io_bf16) ? static_cast<const void *>(w.vconv_lo) : nullptr;  // and its lo parts (bf16)
+    p.ogate = a.o_gate; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
     p.H = a.H; p.N = a.num_seqs;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
@@ -1810,6 +1968,42 @@ hipError_t launch_table(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The short convolution of v into the workspace (calls with a convolution only; after the table).
+template <bool BF, int V>
+hipError_t launch_conv_v(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    if (!a.conv) return hipSuccess;
+    const int CS = a.chunk / 16;
+    const int64_t blocks = a.n_chunks_max * CS * a.H;
+    if (blocks <= 0) return hipSuccess;
+    if (CS == 4)
+        hipLaunchKernelGGL((kda_conv_v<BF, V, 4>), dim3((unsigned)blocks), dim3(256), 0, st, a.v, a.conv_w, a.K,
+                           a.conv, a.H, a.num_seqs, chunk_tab(a, w), static_cast<void *>(w.vconv),
+                           static_cast<void *>(w.vconv_lo));
+    else
+        hipLaunchKernelGGL((kda_conv_v<BF, V, 1>), dim3((unsigned)blocks), dim3(256), 0, st, a.v, a.conv_w, a.K,
+                           a.conv, a.H, a.num_seqs, chunk_tab(a, w), static_cast<void *>(w.vconv),
+                           static_cast<void *>(w.vconv_lo));
+    return hipGetLastError();
+}
+
+template <bool BF, int K, bool CONV>
+hipError_t prep_launch(int32_t chunk, int64_t items, const PrepParams &pp, hipStream_t st) {
+    if (chunk == 64) {
+        static bool lds_set = false;
+        constexpr int LDS = Prep64Lds<BF, K>::BYTES;
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K, CONV>), lds_set, LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kda_chunk_prep64<BF, K, CONV>), dim3((unsigned)items), dim3(256), LDS, st, pp);
+    } else {
+        static bool lds_set = false;
+        constexpr int LDS = 4 * PrepLds<BF, K>::WAVE;
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep<BF, K, CONV>), lds_set, LDS);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((kda_chunk_prep<BF, K, CONV>), dim3((unsigned)((items + 3) / 4)), dim3(256), LDS, st, pp);
+    }
+    return hipGetLastError();
+}
+
 // Prep of the chunk range [g0, g1) (g1 - g0 <= n_chunks_max).
 template <bool BF, int K>
 hipError_t prep_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, hipStream_t st) {
@@ -1817,20 +2011,7 @@ hipError_t prep_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t
     if (n <= 0) return hipSuccess;
     const int64_t items = n * a.H;
     const PrepParams pp = prep_params(a, w, g0, g1);
-    if (a.chunk == 64) {
-        static bool lds_set = false;
-        constexpr int LDS = Prep64Lds<BF, K>::BYTES;
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K>), lds_set, LDS);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_chunk_prep64<BF, K>), dim3((unsigned)items), dim3(256), LDS, st, pp);
-    } else {
-        static bool lds_set = false;
-        constexpr int LDS = 4 * PrepLds<BF, K>::WAVE;
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep<BF, K>), lds_set, LDS);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_chunk_prep<BF, K>), dim3((unsigned)((items + 3) / 4)), dim3(256), LDS, st, pp);
-    }
-    return hipGetLastError();
+    return a.conv ? prep_launch<BF, K, true>(a.chunk, items, pp, st) : prep_launch<BF, K, false>(a.chunk, items, pp, st);
 }
 
 template <bool BF, int K>
@@ -1846,20 +2027,30 @@ unsigned state_grid(const PrefillArgs &a) {
     return (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * StateCfg<BF, K, V, CS>::NT);
 }
 
+template <bool BF, int K, int V, int CS, bool VLO>
+hipError_t state_range_t(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
+    using C = StateCfg<BF, K, V, CS, VLO>;
+    static bool lds_set = false;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS, VLO>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS, VLO>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS),
+                       C::LDS, st, state_params(a, w, g0, g1, first));
+    return hipGetLastError();
+}
+// A convolved v on a bf16 path comes as hi + lo parts (the VLO variant).
 template <bool BF, int K, int V, int CS>
 hipError_t state_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
-    using C = StateCfg<BF, K, V, CS>;
-    static bool lds_set = false;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS>), lds_set, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS), C::LDS,
-                       st, state_params(a, w, g0, g1, first));
-    return hipGetLastError();
+    if constexpr (BF) {
+        if (a.conv) return state_range_t<BF, K, V, CS, true>(a, w, g0, g1, first, st);
+    }
+    return state_range_t<BF, K, V, CS, false>(a, w, g0, g1, first, st);
 }
 
 template <bool BF, int K, int V, int CS>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
-    return state_range<BF, K, V, CS>(a, ws_ptrs(a), 0, ALL_CHUNKS, true, st);
+    const WsPtrs w = ws_ptrs(a);
+    hipError_t e = launch_conv_v<BF, V>(a, w, st);
+    return e != hipSuccess ? e : state_range<BF, K, V, CS>(a, w, 0, ALL_CHUNKS, true, st);
 }
 
 // Pipelined forward over nseg chunk ranges (16-token chunks): prep(0); then per range s the
@@ -1873,6 +2064,7 @@ hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
     const int64_t per = (a.n_chunks_max + nseg - 1) / nseg;
     auto g = [&](int s) { return (int32_t)(per * s < a.n_chunks_max ? per * s : a.n_chunks_max); };
     hipError_t e = launch_table(a, w, st);
+    if (e == hipSuccess) e = launch_conv_v<BF, V>(a, w, st);
     if (e == hipSuccess) e = prep_range<BF, K>(a, w, g(0), g(1), st);
     if (e != hipSuccess) return e;
     static bool lds_set = false;
@@ -1935,14 +2127,16 @@ int pipeline_ranges(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t c
 }  // namespace
 
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk) {
-    size_t b = table_bytes(num_seqs) + align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk));
-    if (can_pipeline(n_chunks_max, num_seqs, H, chunk)) b += align_up((size_t)num_seqs * H * K * V * sizeof(float));
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv) {
+    size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk) +
+               carry_bytes(n_chunks_max, num_seqs, H, K, V, chunk);
+    if (conv) b += align_up((size_t)n_tokens * H * V * 4);  // fp32, or bf16 hi + lo
     return b;
 }
 
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t st) {
-    const int nseg = pipeline_ranges(a.n_chunks_max, a.num_seqs, a.H, a.chunk);
+    // the combined state/prep kernel has no convolution variant: calls with one run unpipelined
+    const int nseg = a.conv ? 1 : pipeline_ranges(a.n_chunks_max, a.num_seqs, a.H, a.chunk);
     if (nseg > 1) {
         if (a.io_bf16) {
             switch (a.K) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -42,7 +42,8 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = _lib.load()
-    ws = lib.kda_chunk_fwd_workspace_bytes
+    def ws(*a, conv=0):
+        return lib.kda_chunk_fwd_workspace_bytes(*a, conv)
     n1 = ws(1, 4096, 96, 128, 128, 1, 16, 1)
     assert n1 > 0
     # grows with tokens and heads; bf16 blocks are smaller than fp32 blocks
@@ -59,17 +60,21 @@ def test_workspace_bytes():
     assert ws(1, 4096, 96, 128, 128, 1, 32, 1) == 0
     assert ws(2, 4096, 96, 128, 128, 3, 16, 1) == 0
     assert ws(1, 4096, 0, 128, 128, 1, 16, 1) == 0
+    # a convolution adds exactly the convolved v (B*T*H*V fp32 elements, or bf16 hi + lo parts)
+    assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) == n1 + 4096 * 96 * 128 * 4
+    assert ws(1, 4096, 96, 128, 128, 1, 16, 0, conv=2) == ws(1, 4096, 96, 128, 128, 1, 16, 0) + 4096 * 96 * 128 * 4
+    assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=3) == 0
 
 
 def _fwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
-             gate=0, qkn=0, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
+             gate=0, qkn=0, conv=0, cw=None, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["B"], a["T"],
                              a["H"],
-                             a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["qkn"], a["odt"], a["o"], a["Sf"],
-                             a["ws"],
+                             a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["qkn"], a["conv"], a["cw"],
+                             a["odt"], a["o"], a["Sf"], a["ws"],
                              a["wsb"], a["stream"])
 
 
@@ -96,6 +101,9 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(gate=-1), INVALID),
     (dict(qkn=2), INVALID),
     (dict(qkn=-1), INVALID),
+    (dict(conv=3), INVALID),
+    (dict(conv=1), INVALID),             # a convolution needs its taps
+    (dict(conv=1, cw=A + 4), INVALID),   # taps misaligned
     (dict(S0=A, Sf=A), INVALID),         # S0 aliases S_final
     (dict(T=1 << 40, H=96), INVALID),    # size overflow
     (dict(K=48), UNSUP),
@@ -112,11 +120,12 @@ def test_chunk_fwd_rejects(kw, expect):
 def _dec(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S=A + 4096, o=A + 8192, N=4, H=2, K=32, V=32, io=1, gate=0, qkn=0,
-             odt=1, stream=None)
+             conv=0, cw=None, cache=None, odt=1, stream=None)
     a.update(kw)
     return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S"], a["o"], a["N"], a["H"],
                                a["K"],
-                               a["V"], a["io"], a["gate"], a["qkn"], a["odt"], a["stream"])
+                               a["V"], a["io"], a["gate"], a["qkn"], a["conv"], a["cw"], a["cache"], a["odt"],
+                               a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -131,6 +140,9 @@ def _dec(**kw):
     (dict(io=3), INVALID),
     (dict(gate=5), INVALID),
     (dict(qkn=3), INVALID),
+    (dict(conv=2, cw=A + 16384), INVALID),                # a convolution needs its cache
+    (dict(conv=2, cw=A + 16384, cache=A + 4096), INVALID),  # cache aliases S
+    (dict(conv=2, cw=A + 16384, cache=A + 20482), INVALID),  # cache misaligned
     (dict(K=16), UNSUP),
     (dict(V=96), UNSUP),
 ])

@@ -1,4 +1,5 @@
 """GPU parity of kda_decode_step (through the C ABI) against the fp64 oracle."""
+import numpy as np
 import pytest
 import torch
 
@@ -109,3 +110,64 @@ def test_decode_steps_equal_prefill():
     torch.cuda.synchronize()
     assert err(torch.stack(outs, 1).cpu(), o_p.cpu()) <= TOL_FP32
     assert err(S.cpu(), S_p.cpu()) <= TOL_FP32
+
+
+# ------------------------------------------------------------ short convolution with a 3-token cache
+
+def _conv_steps(N, H, K, V, io, steps, seed, conv):
+    g = torch.Generator().manual_seed(seed)
+    w = (0.5 * torch.randn((H, 2 * K + V, 4), generator=g)).to(DEV)
+    S = synth.decode_state(N, H, K, V, seed=seed, device=DEV)
+    cache = (0.5 * torch.randn((N, H, 3, 2 * K + V), generator=g)).to(synth.DTYPES[io]).to(DEV)
+    S_ref = S.double().cpu().numpy()
+    c_ref = cache.double().cpu().numpy()
+    worst = {"o": 0.0, "S": 0.0}
+    for step in range(steps):
+        inp = synth.decode_inputs(N, H, K, V, io, seed=seed, step=step, device=DEV, gate_preact=True,
+                                  with_o_gate=True, raw_k=True)
+        args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
+        o = decode_step(*args, S, o_dtype=torch.float32, gate="scaled_sigmoid", o_gate=inp["o_gate"], qk_norm=True,
+                        conv=conv, conv_w=w, conv_cache=cache)
+        torch.cuda.synchronize()
+        o_ref, S_ref, c_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate="scaled_sigmoid",
+                                                 o_gate=inp["o_gate"].cpu(), qk_norm=True, conv=conv,
+                                                 conv_w=w.cpu(), conv_cache=c_ref)
+        # the cache holds raw inputs: it must match exactly
+        assert np.array_equal(cache.double().cpu().numpy(), c_ref)
+        worst["o"] = max(worst["o"], err(o.cpu(), o_ref))
+        worst["S"] = max(worst["S"], err(S.cpu(), S_ref))
+    print("  errors", worst, flush=True)
+    tol = TOL_FP32 if io == "fp32" else TOL_BF16
+    assert worst["o"] <= tol and worst["S"] <= tol, worst
+
+
+@pytest.mark.parametrize("io,N,H,K,V,conv", [("fp32", 3, 2, 128, 128, "short4"), ("fp32", 5, 3, 32, 64, "short4_silu"),
+                                             ("bf16", 4, 3, 128, 128, "short4_silu"),
+                                             ("bf16", 1031, 5, 64, 32, "short4")])
+def test_decode_conv_cache(io, N, H, K, V, conv):
+    """Raw q, k, v convolved over the cached three previous tokens (cache updated in place, compared
+    exactly), then normalised, with both gates; the last case walks several pairs per workgroup."""
+    _announce("decode_conv", io=io, N=N, H=H, K=K, V=V, conv=conv)
+    _conv_steps(N, H, K, V, io, steps=4, seed=38, conv=conv)
+
+
+def test_prefill_with_conv_hands_over_to_decode():
+    """fp32: a convolved prefill over T tokens, then n decode steps whose cache holds the last three raw
+    tokens of the prefill, equal one convolved prefill over T + n tokens."""
+    _announce("conv_handoff", T=37, n=9)
+    N, H, K, V, T, n = 2, 2, 64, 64, 37, 9
+    inp = synth.prefill_inputs(N, T + n, H, K, V, "fp32", seed=39, device=DEV, with_S0=True, raw_k=True)
+    w = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(39))).to(DEV)
+    kw = dict(conv="short4_silu", conv_w=w, qk_norm=True)
+    o_all, S_all = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"], **kw)
+    head = {x: inp[x][:, :T].contiguous() for x in ("q", "k", "v", "g", "beta")}
+    o_p, S = chunk_fwd(head["q"], head["k"], head["v"], head["g"], head["beta"], S0=inp["S0"], **kw)
+    cache = torch.cat([inp["q"], inp["k"], inp["v"]], dim=-1)[:, T - 3:T].permute(0, 2, 1, 3).contiguous()
+    outs = []
+    for t in range(T, T + n):
+        outs.append(decode_step(*(inp[x][:, t].contiguous() for x in ("q", "k", "v", "g", "beta")), S,
+                                conv_cache=cache, **kw))
+    torch.cuda.synchronize()
+    assert err(o_p.cpu(), o_all[:, :T].cpu()) <= TOL_FP32
+    assert err(torch.stack(outs, 1).cpu(), o_all[:, T:].cpu()) <= TOL_FP32
+    assert err(S.cpu(), S_all.cpu()) <= TOL_FP32

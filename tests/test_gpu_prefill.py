@@ -33,14 +33,23 @@ def _oracle(inp, heads=None):
         S0 = None if S0 is None else S0[:, hs].contiguous()
     return oracle.chunk_fwd(q.cpu(), k.cpu(), v.cpu(), g.cpu(), beta.cpu(), None if S0 is None else S0.cpu(),
                             None if cu is None else cu.cpu(), gate=inp.get("gate", "log_decay"),
-                            o_gate=None if og is None else og.cpu(), qk_norm=inp.get("qk_norm", False))
+                            o_gate=None if og is None else og.cpu(), qk_norm=inp.get("qk_norm", False),
+                            conv=inp.get("conv", "none"), conv_w=_conv_w_heads(inp, heads))
+
+
+def _conv_w_heads(inp, heads):
+    w = inp.get("conv_w")
+    if w is None:
+        return None
+    w = w.cpu()
+    return w[list(heads)].contiguous() if heads is not None else w
 
 
 def _run(inp, o_dtype=None, chunk=16):
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
                       cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk,
                       gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"),
-                      qk_norm=inp.get("qk_norm", False))
+                      qk_norm=inp.get("qk_norm", False), conv=inp.get("conv", "none"), conv_w=inp.get("conv_w"))
     torch.cuda.synchronize()
     return o, Sf
 
@@ -495,4 +504,97 @@ def test_all_fused_k3_prefill_4k_sampled_heads():
     inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True, with_o_gate=True, raw_k=True)
     inp["gate"] = "scaled_sigmoid"
     inp["qk_norm"] = True
+    _check(inp, heads=(0, 31, 64, 95))
+
+
+# ------------------------------------------------------------ short convolution in-kernel
+#
+# With conv, the prep kernels convolve the raw q and k rows (length 4, causal, per channel, zero history
+# at each sequence start, optional SiLU) as they read them, and kda_conv_v convolves v into the workspace
+# for the state pass; the oracle convolves the same raw rows in fp64.
+
+def _conv_taps(H, K, V, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (0.5 * torch.randn((H, 2 * K + V, 4), generator=g)).to(DEV)
+
+
+def _conv_inputs(B, T, H, K, V, io, seed, conv="short4_silu", **kw):
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=seed, device=DEV, **kw)
+    inp["conv"] = conv
+    inp["conv_w"] = _conv_taps(H, K, V, seed)
+    return inp
+
+
+@CHUNKS
+@pytest.mark.parametrize("io,B,T,H,K,V,conv", [("fp32", 2, 77, 3, 128, 128, "short4"),
+                                               ("fp32", 1, 130, 2, 32, 64, "short4_silu"),
+                                               ("bf16", 2, 200, 3, 128, 128, "short4_silu"),
+                                               ("bf16", 1, 97, 2, 64, 32, "short4")])
+def test_conv_shapes(io, B, T, H, K, V, conv, chunk):
+    _announce("conv", io=io, B=B, T=T, H=H, K=K, V=V, conv=conv, chunk=chunk, seed=70)
+    _check(_conv_inputs(B, T, H, K, V, io, 70, conv=conv, with_S0=True), io=io, chunk=chunk)
+
+
+@CHUNKS
+def test_conv_varlen_whole_prologue(chunk):
+    """Packed sequences (empty, 1- and 2-token ones: the history restarts inside a chunk), convolution with
+    SiLU, q/k normalisation and both gates at once."""
+    lengths = [37, 0, 2, 1, 150, 64, 0, 65, 3]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("conv_varlen", lengths=lengths, chunk=chunk, seed=71)
+    inp = _conv_inputs(1, cu[-1], 4, 128, 128, "bf16", 71, cu_seqlens=cu, with_S0=True, gate_preact=True,
+                       with_o_gate=True, raw_k=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp["qk_norm"] = True
+    _check(inp, chunk=chunk)
+
+
+def test_conv_identity_taps_change_nothing():
+    """Taps (0, 0, 0, 1) without SiLU give every input back exactly, so o and S_final equal those of the call
+    without a convolution bit for bit (fp32 and bf16, both chunk sizes)."""
+    _announce("conv_identity", seed=72)
+    for io in ("fp32", "bf16"):
+        inp = synth.prefill_inputs(2, 90, 3, 64, 128, io, seed=72, device=DEV, with_S0=True)
+        w = torch.zeros((3, 2 * 64 + 128, 4), device=DEV)
+        w[..., 3] = 1.0
+        for chunk in (16, 64):
+            o1, S1 = _run(inp, chunk=chunk)
+            o2, S2 = _run(dict(inp, conv="short4", conv_w=w), chunk=chunk)
+            assert torch.equal(o1, o2) and torch.equal(S1, S2), (io, chunk)
+
+
+def test_conv_split_calls_match_one_call():
+    """kda_chunk_prep then kda_chunk_state with a convolution give bitwise what kda_chunk_fwd gives."""
+    from kda_gated_delta_chunk_amd import _lib
+    _announce("conv_split", seed=73)
+    lib = _lib.load()
+    B, T, H, K, V = 1, 300, 4, 128, 128
+    inp = _conv_inputs(B, T, H, K, V, "bf16", 73, with_S0=True)
+    o1, S1 = _run(inp)
+    cc = _lib.CONVS["short4_silu"]
+    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, B, 16, 1, cc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    o2 = torch.empty_like(o1)
+    S2 = torch.empty_like(S1)
+    sh = torch.cuda.current_stream().cuda_stream
+    p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta", "S0", "conv_w")}
+    _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, B, 16, 1, 0, 0, cc,
+                                  p["conv_w"], ws.data_ptr(), wsb, sh), "kda_chunk_prep")
+    _lib.check(lib.kda_chunk_state(p["v"], None, p["S0"], None, B, T, H, K, V, B, 16, 1, cc, p["conv_w"], 1,
+                                   o2.data_ptr(), S2.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_conv_k3_prefill_4k_sampled_heads():
+    """The convolution leg of the benchmark: H=96, T=4096, K=V=128, bf16, chunk 16, raw q and k, SiLU
+    convolution, normalisation and both gates in-kernel; 4 heads checked."""
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("conv_prefill_4k", seed=w.seed)
+    inp = synth.workload_prefill_inputs(w, device=DEV, gate_preact=True, with_o_gate=True, raw_k=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp["qk_norm"] = True
+    inp["conv"] = "short4_silu"
+    g = torch.Generator().manual_seed(7)
+    inp["conv_w"] = (0.5 * torch.randn((w.H, 2 * w.K + w.V, 4), generator=g)).to(DEV)
     _check(inp, heads=(0, 31, 64, 95))
