@@ -255,32 +255,6 @@ __device__ __forceinline__ void l2norm_row(float (&x)[KS][8]) {
         for (int j = 0; j < 8; ++j) x[s][j] *= rn;
 }
 
-// Short convolution of one 8-channel run of a token row, in fp32: x (the run of token `tok`, already
-// loaded) becomes sum_{d=0..3} w[c][3-d] * x_{tok-d}[c] over the tokens of its sequence (tok - d >= seq0),
-// c = c0 .. c0+7; then SiLU when act == 2. base: [tokens][H][D] (row stride D); w: the tensor's weights
-// of head h, [D][4] fp32. Earlier rows are loaded clamped to the sequence start and dropped by a
-// select, so every load is unconditional and stays in flight with the others.
-template <bool BF>
-__device__ __forceinline__ void conv_run8(const void *base, int64_t tok, int64_t seq0, int32_t H, int h, int D,
-                                          int c0, const float *__restrict__ w, int act, float (&x)[8]) {
-    float p[3][8];
-    bool ok[3];
-#pragma unroll
-    for (int d = 1; d <= 3; ++d) {
-        ok[d - 1] = tok - d >= seq0;
-        load8<BF>(base, ((ok[d - 1] ? tok - d : seq0) * H + h) * D + c0, p[d - 1]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float4 wc = *reinterpret_cast<const float4 *>(w + 4 * (c0 + j));
-        float y = wc.w * x[j];
-        y = ok[0] ? __builtin_fmaf(wc.z, p[0][j], y) : y;
-        y = ok[1] ? __builtin_fmaf(wc.y, p[1][j], y) : y;
-        y = ok[2] ? __builtin_fmaf(wc.x, p[2][j], y) : y;
-        x[j] = act == 2 ? y * sigmoid_f(y) : y;
-    }
-}
-
 // mma32 operands from eight fp32 values: rounded (single) or split into hi + lo.
 __device__ __forceinline__ Frag8<true> frag8_of(const float (&x)[8], Frag8<true>) {
     Frag8<true> f;
@@ -460,9 +434,7 @@ struct PrepParams {
     int32_t H, N;
     int32_t gate;    // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
     int32_t qknorm;  // 1: q and k rows are L2-normalised as they are read (l2norm_row)
-    int32_t conv;    // 0: none; 1: short convolution of q and k (conv_run8); 2: the same, then SiLU
-    const float *convw;  // [H][K + K + V][4] fp32, or null
-    int32_t V;
+
     ChunkTab tab;
     char *frags;
     int32_t g0, g1;
@@ -504,25 +476,13 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     const int64_t row = (tok0 + (valid ? r : nvalid - 1)) * H + h;
     float qv[KS][8], kv[KS][8], bl[KS][8];
     if constexpr (CONV) {
-        // q, then k, one 8-channel run at a time: the run's row, the three earlier rows and its taps
-        // (the scheduling barriers keep one run's values live, not all of them); then g
-        const int64_t tokl = tok0 + (valid ? r : nvalid - 1);
-        const float *wh = pa.convw + (size_t)h * (2 * K + pa.V) * 4;
+        // q and k were convolved into fp32 arrays of the workspace (kda_conv_x); g as given
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
-            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
-            conv_run8<BF>(qp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh, pa.conv, qv[s]);
+            load8<false>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            load8<false>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
-            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
-            conv_run8<BF>(kp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh + 4 * K, pa.conv, kv[s]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
     } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -752,25 +712,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int64_t row = (t0c + (valid ? SUB * R + r : nvc - 1)) * H + h;
     float qv[KS][8], kv[KS][8], bl[KS][8];
     if constexpr (CONV) {
-        // q, then k, one 8-channel run at a time: the run's row, the three earlier rows and its taps
-        // (the scheduling barriers keep one run's values live, not all of them); then g
-        const int64_t tokl = t0c + (valid ? SUB * R + r : nvc - 1);
-        const float *wh = pa.convw + (size_t)h * (2 * K + pa.V) * 4;
+        // q and k were convolved into fp32 arrays of the workspace (kda_conv_x); g as given
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
-            load8<BF>(qp, row * K + 32 * s + 8 * ag, qv[s]);
-            conv_run8<BF>(qp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh, pa.conv, qv[s]);
+            load8<false>(qp, row * K + 32 * s + 8 * ag, qv[s]);
+            load8<false>(kp, row * K + 32 * s + 8 * ag, kv[s]);
+            load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            __builtin_amdgcn_sched_barrier(0);
-            load8<BF>(kp, row * K + 32 * s + 8 * ag, kv[s]);
-            conv_run8<BF>(kp, tokl, tab.tok(n), H, h, K, 32 * s + 8 * ag, wh + 4 * K, pa.conv, kv[s]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
     } else {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -1055,42 +1003,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
 }
 
-// ----------------------------------------------- short convolution of v
-// v convolved (conv_run8) into the workspace, where the state pass then reads it (bf16: as hi + lo
-// parts, so that the state pass's T V keeps the convolution's fp32 result). One workgroup per
-// (16-token sub-tile, head); thread t takes token row t / (V/8) of the sub-tile and the 8 channels
-// 8 (t % (V/8)) .. +7. Rows past the sequence end are not written (the state pass never reads them).
-template <bool BF, int V, int CS>
-__global__ __launch_bounds__(256) void kda_conv_v(const void *__restrict__ vp, const float *__restrict__ convw,
-                                                  int32_t K, int32_t act, int32_t H, int32_t N, ChunkTab tab,
-                                                  void *__restrict__ out, void *__restrict__ out_lo) {
-    constexpr int G = V / 8;  // 8-channel runs per row
-    const int t = threadIdx.x;
-    if (t >= 16 * G) return;  // no barriers in this kernel
-    const int64_t item = blockIdx.x;
-    const int h = (int)(item % H);
-    const int64_t su = item / H;  // global sub-tile: chunk su / CS, sub-tile su % CS
+// ------------------------------------------------ short convolution (q, k, v)
+// One tensor x [tokens][H][D] convolved into the workspace: y_t = sum_{d=0..3} w[c][3-d] x_{t-d}[c] over
+// the tokens of t's sequence, then SiLU when act == 2, in fp32. One thread per (16-token sub-tile, head,
+// 8-channel run; runs of a row on consecutive lanes, so a row is one coalesced read): it loads the run's
+// taps once and walks the sub-tile's tokens in order with the three previous rows in registers, so
+// every row is read once more than the input itself (the history of the sub-tile's first token).
+// OUT: 0 = fp32 (q and k for the prep; v on an fp32 path), 1 = bf16 hi + lo parts (v on a bf16 path,
+// for the state pass's T V_hi + T V_lo). Tokens past the sequence end are not written.
+template <bool BF, int D, int CS, int OUT>
+__global__ __launch_bounds__(256) void kda_conv_x(const void *__restrict__ xp, const float *__restrict__ taps,
+                                                  int32_t CW, int32_t act, int32_t H, int32_t N, ChunkTab tab,
+                                                  int64_t n_items, void *__restrict__ out, void *__restrict__ out_lo) {
+    constexpr int G = D / 8;  // 8-channel runs per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= n_items) return;  // no barriers in this kernel
+    const int c0 = 8 * (int)(gid % G);
+    const int64_t rest = gid / G;
+    const int h = (int)(rest % H);
+    const int64_t su = rest / H;  // global sub-tile: chunk su / CS, sub-tile su % CS
     const int gc = (int)(su / CS), u = (int)(su % CS);
     if (gc >= tab.off(N)) return;
     const int n = tab.find(N, gc);
     const int64_t seq0 = tab.tok(n), seq1 = tab.tok(n + 1);
-    const int64_t tok = seq0 + (int64_t)(gc - tab.off(n)) * (CS * SUB) + u * SUB + t / G;
-    if (tok >= seq1) return;
-    const int c0 = 8 * (t % G);
-    float x[8];
-    load8<BF>(vp, (tok * H + h) * V + c0, x);
-    conv_run8<BF>(vp, tok, seq0, H, h, V, c0, convw + ((size_t)h * (2 * K + V) + 2 * K) * 4, act, x);
-    if constexpr (BF) {  // hi = bf16(x), lo = bf16(x - hi): about 16 significant bits between them
-        uint32_t hi[4], lo[4];
+    const int64_t t0 = seq0 + (int64_t)(gc - tab.off(n)) * (CS * SUB) + u * SUB;
+    if (t0 >= seq1) return;
+    const int nt = (int)(seq1 - t0 < SUB ? seq1 - t0 : SUB);
+    float4 w[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_bf16(x[2 * i], x[2 * i + 1], hi[i], lo[i]);
-        const int64_t e = (tok * H + h) * V + c0;
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_lo) + e) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    } else {
-        float *o = reinterpret_cast<float *>(out) + (tok * H + h) * V + c0;
-        *reinterpret_cast<float4 *>(o) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4 *>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c0 + j) * 4);
+    float p[3][8];  // p[d-1] = row t - d
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        if (t0 - d >= seq0) load8<BF>(xp, ((t0 - d) * H + h) * D + c0, p[d - 1]);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[d - 1][j] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        if (i >= nt) break;
+        const int64_t e = ((t0 + i) * H + h) * D + c0;
+        float x[8], y[8];
+        load8<BF>(xp, e, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = w[j].w * x[j];
+            v = __builtin_fmaf(w[j].z, p[0][j], v);
+            v = __builtin_fmaf(w[j].y, p[1][j], v);
+            v = __builtin_fmaf(w[j].x, p[2][j], v);
+            y[j] = act == 2 ? v * sigmoid_f(v) : v;
+            p[2][j] = p[1][j];
+            p[1][j] = p[0][j];
+            p[0][j] = x[j];
+        }
+        if constexpr (OUT == 1) {  // hi = bf16(y), lo = bf16(y - hi): about 16 significant bits together
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_bf16(y[2 * k], y[2 * k + 1], hi[k], lo[k]);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_lo) + e) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        } else {
+            float *o = reinterpret_cast<float *>(out) + e;
+            *reinterpret_cast<float4 *>(o) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4 *>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        }
     }
 }
 
@@ -1887,8 +1864,11 @@ struct WsPtrs {
     int32_t *chunk_off;
     char *frags;
     float *carry;  // state between chunk ranges (pipelined calls only)
-    char *vconv;     // convolved v [tokens][H][V] in the I/O dtype (calls with a convolution only); bf16:
-    char *vconv_lo;  // the hi parts, and here the lo parts (v - hi rounded to bf16)
+    // calls with a convolution only:
+    char *vconv;     // convolved v [tokens][H][V]: fp32, or on a bf16 path the hi parts,
+    char *vconv_lo;  // and here the lo parts (v - hi rounded to bf16)
+    char *qconv;     // convolved q [tokens][H][K] fp32
+    char *kconv;     // convolved k [tokens][H][K] fp32
 };
 bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk);
 // Workspace: chunk table | per-(chunk, head) factors | carry (pipelined calls) | convolved v (with a
@@ -1908,7 +1888,10 @@ WsPtrs ws_ptrs(const PrefillArgs &a) {
     char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk);
     w.carry = reinterpret_cast<float *>(cp);
     w.vconv = cp + carry_bytes(a.n_chunks_max, a.num_seqs, a.H, a.K, a.V, a.chunk);
-    w.vconv_lo = w.vconv + (size_t)a.B * a.T * a.H * a.V * 2;
+    const size_t nth = (size_t)a.B * a.T * a.H;
+    w.vconv_lo = w.vconv + nth * a.V * 2;
+    w.qconv = w.vconv + align_up(nth * a.V * 4);
+    w.kconv = w.qconv + align_up(nth * a.K * 4);
     return w;
 }
 
@@ -1935,13 +1918,12 @@ ChunkTab chunk_tab(const PrefillArgs &a, const WsPtrs &w) {
 
 PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1) {
     PrepParams p;
-    p.q = a.q; p.k = a.k; p.g = a.g; p.beta = a.beta;
+    p.q = a.conv ? static_cast<const void *>(w.qconv) : a.q;  // with a convolution: fp32 convolved q, k
+    p.k = a.conv ? static_cast<const void *>(w.kconv) : a.k;
+    p.g = a.g; p.beta = a.beta;
     p.H = a.H; p.N = a.num_seqs;
     p.gate = a.gate_sigmoid ? 1 : 0;
     p.qknorm = a.qk_l2norm ? 1 : 0;
-    p.conv = a.conv;
-    p.convw = a.conv_w;
-    p.V = a.V;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
     p.g0 = g0; p.g1 = g1;
     return p;
@@ -1968,22 +1950,35 @@ hipError_t launch_table(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
     return hipGetLastError();
 }
 
-// The short convolution of v into the workspace (calls with a convolution only; after the table).
+// The short convolution of one tensor (channels [coff, coff + D) of the taps) into the workspace
+// (calls with a convolution only; after the table).
+template <bool BF, int D, int OUT>
+hipError_t launch_conv(const PrefillArgs &a, const WsPtrs &w, const void *x, int coff, void *out, void *out_lo,
+                       hipStream_t st) {
+    const int CS = a.chunk / 16;
+    const int64_t items = a.n_chunks_max * CS * a.H * (D / 8);
+    if (items <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((items + 255) / 256);
+    const int32_t CW = 2 * a.K + a.V;
+    const float *taps = a.conv_w + (size_t)coff * 4;
+    if (CS == 4)
+        hipLaunchKernelGGL((kda_conv_x<BF, D, 4, OUT>), dim3(blocks), dim3(256), 0, st, x, taps, CW, a.conv, a.H,
+                           a.num_seqs, chunk_tab(a, w), items, out, out_lo);
+    else
+        hipLaunchKernelGGL((kda_conv_x<BF, D, 1, OUT>), dim3(blocks), dim3(256), 0, st, x, taps, CW, a.conv, a.H,
+                           a.num_seqs, chunk_tab(a, w), items, out, out_lo);
+    return hipGetLastError();
+}
 template <bool BF, int V>
 hipError_t launch_conv_v(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
     if (!a.conv) return hipSuccess;
-    const int CS = a.chunk / 16;
-    const int64_t blocks = a.n_chunks_max * CS * a.H;
-    if (blocks <= 0) return hipSuccess;
-    if (CS == 4)
-        hipLaunchKernelGGL((kda_conv_v<BF, V, 4>), dim3((unsigned)blocks), dim3(256), 0, st, a.v, a.conv_w, a.K,
-                           a.conv, a.H, a.num_seqs, chunk_tab(a, w), static_cast<void *>(w.vconv),
-                           static_cast<void *>(w.vconv_lo));
-    else
-        hipLaunchKernelGGL((kda_conv_v<BF, V, 1>), dim3((unsigned)blocks), dim3(256), 0, st, a.v, a.conv_w, a.K,
-                           a.conv, a.H, a.num_seqs, chunk_tab(a, w), static_cast<void *>(w.vconv),
-                           static_cast<void *>(w.vconv_lo));
-    return hipGetLastError();
+    return launch_conv<BF, V, BF ? 1 : 0>(a, w, a.v, 2 * a.K, w.vconv, w.vconv_lo, st);
+}
+template <bool BF, int K>
+hipError_t launch_conv_qk(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    if (!a.conv) return hipSuccess;
+    hipError_t e = launch_conv<BF, K, 0>(a, w, a.q, 0, w.qconv, nullptr, st);
+    return e != hipSuccess ? e : launch_conv<BF, K, 0>(a, w, a.k, a.K, w.kconv, nullptr, st);
 }
 
 template <bool BF, int K, bool CONV>
@@ -2018,6 +2013,7 @@ template <bool BF, int K>
 hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
     hipError_t e = launch_table(a, w, st);
+    if (e == hipSuccess) e = launch_conv_qk<BF, K>(a, w, st);
     if (e != hipSuccess) return e;
     return prep_range<BF, K>(a, w, 0, ALL_CHUNKS, st);
 }
@@ -2130,7 +2126,8 @@ size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32
                                bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv) {
     size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk) +
                carry_bytes(n_chunks_max, num_seqs, H, K, V, chunk);
-    if (conv) b += align_up((size_t)n_tokens * H * V * 4);  // fp32, or bf16 hi + lo
+    if (conv)  // convolved v (fp32, or bf16 hi + lo), q and k (fp32)
+        b += align_up((size_t)n_tokens * H * V * 4) + 2 * align_up((size_t)n_tokens * H * K * 4);
     return b;
 }
 
