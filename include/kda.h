@@ -109,8 +109,9 @@ typedef enum {
  *   KDA_CONV_SHORT4_SILU the convolution, then SiLU (y * sigmoid(y)).
  * conv_w: fp32 [H, K + K + V, 4], 16-byte aligned: the q channels of head h,
  * then its k channels, then its v channels. The convolution runs in fp32; the
- * prefill keeps the convolved v in the workspace (fp32, or for bf16 I/O as
- * a bf16 hi + lo pair that carries about 16 significant bits).
+ * prefill keeps the convolved q and k in the workspace in fp32 and the
+ * convolved v in fp32 or, for bf16 I/O, as a bf16 hi + lo pair (about 16
+ * significant bits), so no output of the convolution is rounded to bf16.
  */
 typedef enum {
     KDA_CONV_NONE = 0,
@@ -130,8 +131,7 @@ const char *kda_status_string(kda_status_t status);
  *   num_seqs    number of sequences: B without cu_seqlens, else len(cu_seqlens)-1
  *   chunk, io   as for kda_chunk_fwd
  *   conv        as for kda_chunk_fwd (a convolution needs room for the
- *               convolved v: 4 * B * T * H * V bytes more, fp32 or a bf16
- *               hi + lo pair)
+ *               convolved tensors: 4 * B * T * H * (K + K + V) bytes more)
  * Returns 0 if the sizes are invalid or unsupported.
  */
 size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
