@@ -35,11 +35,12 @@
 
 namespace kda {
 
-template <bool BF, int K, int V, int NT>
+// CONV: the short-convolution variant (the plain kernel keeps its registers for its prefetch).
+template <bool BF, int K, int V, int NT, bool CONV>
 __global__ __launch_bounds__(NT) void kda_decode_kernel(
     const void *__restrict__ qp, const void *__restrict__ kp, const void *__restrict__ vp,
     const void *__restrict__ gp, const void *__restrict__ bp, const void *__restrict__ zp, float *__restrict__ S,
-    void *__restrict__ op, int o_bf16, int gate, int qknorm, int conv, const float *__restrict__ convw,
+    void *__restrict__ op, int o_bf16, int gate, int qknorm, int act, const float *__restrict__ convw,
     void *__restrict__ cachep, int32_t H, int32_t NH) {
     constexpr int CG = V / 4;          // column groups (float4) per row
     constexpr int RG = NT / CG;        // row groups
@@ -72,13 +73,13 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             st[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (size_t)(rg + RG * j) * V) + cg);
-        const E *cache = conv ? reinterpret_cast<const E *>(cachep) + (size_t)p * 3 * CW : nullptr;
-        const float *wh = conv ? convw + (size_t)(p % H) * CW * 4 : nullptr;
+        const E *cache = CONV ? reinterpret_cast<const E *>(cachep) + (size_t)p * 3 * CW : nullptr;
+        const float *wh = CONV ? convw + (size_t)(p % H) * CW * 4 : nullptr;
         if (t < K) {
             kk = IO<BF>::ld(reinterpret_cast<const E *>(kp) + (size_t)p * K, t);
             qq = IO<BF>::ld(reinterpret_cast<const E *>(qp) + (size_t)p * K, t);
             gg = IO<BF>::ld(reinterpret_cast<const E *>(gp) + (size_t)p * K, t);
-            if (conv) {
+            if constexpr (CONV) {
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     c.cq[j] = IO<BF>::ld(cache, j * CW + t);
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
         }
         if (t < V) {
             vv = IO<BF>::ld(reinterpret_cast<const E *>(vp) + (size_t)p * V, t);
-            if (conv) {
+            if constexpr (CONV) {
 #pragma unroll
                 for (int j = 0; j < 3; ++j) c.cv[j] = IO<BF>::ld(cache, j * CW + 2 * K + t);
                 c.wv = *reinterpret_cast<const float4 *>(wh + 4 * (2 * K + t));
@@ -98,10 +99,10 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
         }
         bb = IO<BF>::ld(reinterpret_cast<const E *>(bp), p);
     };
-    // y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3} (cache row 2 is t-1), then SiLU for conv == 2
+    // y = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3} (cache row 2 is t-1), then SiLU for act == 2
     auto conv4 = [&](const float4 &w, const float (&c)[3], float x) {
         const float y = w.w * x + w.z * c[2] + w.y * c[1] + w.x * c[0];
-        return conv == 2 ? y * sigmoid_f(y) : y;
+        return act == 2 ? y * sigmoid_f(y) : y;
     };
     load_pair(nh, s, kt, qt, gt, vt, beta, cv);
 
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
 
         // 1b. short convolution over the cached three previous raw tokens; the cache moves up one
         //     row and takes this token's raw q | k | v (each lane rewrites only what it read)
-        if (conv) {
+        if constexpr (CONV) {
             E *cache = reinterpret_cast<E *>(cachep) + (size_t)nh * 3 * CW;
             if (t < K) {
                 IO<BF>::st(cache, t, cv.cq[1]);
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(
 #pragma unroll
         for (int j = 0; j < RPT; ++j) s[j] = sn[j];
         kt = ktn; qt = qtn; gt = gtn; vt = vtn; beta = betan;
-        cv = cvn;
+        if constexpr (CONV) cv = cvn;
     }
 }
 
@@ -265,9 +266,14 @@ hipError_t launch_dkv(const DecodeArgs &a, int32_t NH, hipStream_t st) {
     constexpr int NT = (K * V / 4 < 512) ? K * V / 4 : 512;
     // up to 4096 workgroups take one pair each; above that each workgroup walks about 4 pairs
     const int32_t grid = NH <= 4096 ? NH : (NH + 3) / 4 > 4096 ? (NH + 3) / 4 : 4096;
-    hipLaunchKernelGGL((kda_decode_kernel<BF, K, V, NT>), dim3(grid), dim3(NT), 0, st, a.q, a.k, a.v, a.g, a.beta,
-                       a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm, (int)a.conv, a.conv_w,
-                       a.conv_cache, a.H, NH);
+    if (a.conv)
+        hipLaunchKernelGGL((kda_decode_kernel<BF, K, V, NT, true>), dim3(grid), dim3(NT), 0, st, a.q, a.k, a.v, a.g,
+                           a.beta, a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm,
+                           (int)a.conv, a.conv_w, a.conv_cache, a.H, NH);
+    else
+        hipLaunchKernelGGL((kda_decode_kernel<BF, K, V, NT, false>), dim3(grid), dim3(NT), 0, st, a.q, a.k, a.v, a.g,
+                           a.beta, a.o_gate, a.S, a.o, (int)a.o_bf16, (int)a.gate_sigmoid, (int)a.qk_l2norm, 0,
+                           nullptr, nullptr, a.H, NH);
     return hipGetLastError();
 }
 template <bool BF, int K>
