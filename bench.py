@@ -29,6 +29,8 @@ from kda_gated_delta_chunk_amd.source_hash import csrc_hash
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix, TFLOP/s
+SIMDS = 256 * 4                 # MI355X: 256 compute units of 4 SIMDs (one matrix core each)
+CLOCK_HZ = 2.4e9                # peak engine clock
 
 
 def prefill_algorithmic_bytes(T, H, K, V, N, es=2, with_S0=False):
@@ -140,9 +142,10 @@ def time_decode(w, steps, dev, gate="log_decay", qk_norm=False):
             "bytes_per_step": bytes_step, "N": N, "H": H}
 
 
-def measured_traffic(kernel_prefix):
-    """HBM bytes per launch of a kernel from the committed counter summary
-    (profiles/traffic.json), or None if the kernels changed since it was taken."""
+def measured_counter(kernel_prefix, field="traffic_bytes"):
+    """A per-launch counter figure of a kernel from the committed counter summary
+    (profiles/traffic.json): HBM bytes ("traffic_bytes") or matrix-core busy cycles summed over
+    the device ("mfma_busy_cycles"); None if the kernels changed since it was taken."""
     p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
     try:
         with open(p) as f:
@@ -153,8 +156,43 @@ def measured_traffic(kernel_prefix):
         return None
     for name, v in t["kernels"].items():
         if name.startswith(kernel_prefix):
-            return v["traffic_bytes"]
+            return v.get(field)
     return None
+
+
+def measured_traffic(kernel_prefix):
+    return measured_counter(kernel_prefix, "traffic_bytes")
+
+
+def mfma_busy_frac(kernel_prefix, ms):
+    """Matrix-core busy fraction of the whole chip over a launch of `ms` milliseconds, from the
+    rocprof SQ_VALU_MFMA_BUSY_CYCLES per launch in profiles/traffic.json (None if absent or stale)."""
+    cyc = measured_counter(kernel_prefix, "mfma_busy_cycles")
+    if cyc is None or not ms:
+        return None
+    return cyc / (ms * 1e-3 * CLOCK_HZ * SIMDS)
+
+
+def mfma_from_counters(sq_csv, out_path):
+    """Add each kda kernel's SQ_VALU_MFMA_BUSY_CYCLES per launch (average over its dispatches, summed
+    over the device) from a rocprofv3 counter run of `bench.py --counters` to the counter summary,
+    if that summary was taken on the same kernel sources."""
+    import csv
+    from collections import defaultdict
+    with open(out_path) as fh:
+        out = json.load(fh)
+    if out.get("csrc_hash") != csrc_hash():
+        raise SystemExit("%s was taken on other kernel sources; take FETCH_SIZE/WRITE_SIZE again first" % out_path)
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(sq_csv)):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        if "kda" in name and r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
+            vals[name].append(float(r["Counter_Value"]))
+    for k, v in vals.items():
+        out["kernels"].setdefault(k, {})["mfma_busy_cycles"] = sum(v) / len(v)
+    with open(out_path, "w") as fh:
+        fh.write(json.dumps(out, indent=1) + "\n")
+    return out
 
 
 def traffic_from_counters(fetch_csv, write_csv, out_path):
@@ -220,11 +258,18 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two counter runs of --counters (FETCH_SIZE, WRITE_SIZE "
                          "run_counter_collection.csv) into per-kernel HBM bytes (profiles/traffic.json)")
+    ap.add_argument("--mfma-from", metavar="SQ_CSV",
+                    help="no GPU work: add SQ_VALU_MFMA_BUSY_CYCLES per launch from a counter run of --counters "
+                         "(run_counter_collection.csv) to the counter summary (--traffic-out)")
     ap.add_argument("--traffic-out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                           "traffic.json"))
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from, args.traffic_out)))
+        if not args.mfma_from:
+            return
+    if args.mfma_from:
+        print(json.dumps(mfma_from_counters(args.mfma_from, args.traffic_out)))
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (heads and sequences would "
@@ -267,11 +312,17 @@ def main():
                    "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
                      "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1>" if dom == "state"
-                                                 else "kda::kda_chunk_prep<true, 128>"),
-                     "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms},
+                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1, false>" if dom == "state"
+                                                 else "kda::kda_chunk_prep<true, 128, false>"),
+                     "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms,
+                     "mfma_busy_frac_rocprof": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false>"
+                                                              if dom == "state" else "kda::kda_chunk_prep<true, 128, false>",
+                                                              dom_ms)},
         "roofline_path": path_roofline(r, 16),
         "kernels_ms": kern_ms,
+        "kernels_mfma_busy_frac_rocprof": {
+            "kda_chunk_prep": mfma_busy_frac("kda::kda_chunk_prep<true, 128, false>", r["prep_ms"]),
+            "kda_state_pass": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false>", r["state_ms"])},
         "split_calls_ms": r["prep_ms"] + r["state_ms"],
         "workspace_bytes": r["ws_bytes"],
     }
