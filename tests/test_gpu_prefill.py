@@ -598,3 +598,20 @@ def test_conv_k3_prefill_4k_sampled_heads():
     g = torch.Generator().manual_seed(7)
     inp["conv_w"] = (0.5 * torch.randn((w.H, 2 * w.K + w.V, 4), generator=g)).to(DEV)
     _check(inp, heads=(0, 31, 64, 95))
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_conv_path_deterministic(chunk):
+    """The convolution variants (kda_conv_x, the conv prep, the hi + lo state pass) with the whole prologue
+    and epilogue give bitwise the same o and S_final on every call."""
+    _announce("conv_deterministic", chunk=chunk, seed=74)
+    lengths = [200, 3, 0, 77]
+    cu = synth.cu_from_lengths(lengths)
+    inp = _conv_inputs(1, cu[-1], 3, 128, 128, "bf16", 74, cu_seqlens=cu, with_S0=True, gate_preact=True,
+                       with_o_gate=True, raw_k=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp["qk_norm"] = True
+    o1, S1 = _run(inp, chunk=chunk)
+    for _ in range(3):
+        o2, S2 = _run(inp, chunk=chunk)
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
