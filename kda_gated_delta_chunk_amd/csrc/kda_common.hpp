@@ -52,6 +52,15 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t &hi, uint3
     lo = pack_bf16(a - bf_lo(hi), b - bf_hi(hi));
 }
 
+// Round two floats to fp16 (round-to-nearest-even) and pack (a in the low half).
+__device__ __forceinline__ uint32_t pack_h(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+    h2 p;
+    p[0] = (_Float16)a;
+    p[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
 // ------------------------------------------------------------ fragment types
 // Frag4: 4 reduction slots per lane (mma16 operand). Frag8: 8 slots (mma32 operand).
 template <bool BF> struct Frag4;
@@ -208,6 +217,21 @@ __device__ __forceinline__ float gate_log2_decay(float x) {
 // 1 / (1 + e^-x) in fp32 (the output gate's activation); exactly 0 below about -88, 1 for large x.
 __device__ __forceinline__ float sigmoid_f(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
+// fp16 operands (Frag4<true> / Frag8<true> holding fp16 bit pairs instead of bf16): D += A * B on
+// v_mfma_f32_16x16x16_f16 / v_mfma_f32_16x16x32_f16, with the same lane and slot layout as mma16 /
+// mma32.
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+__device__ __forceinline__ f32x4 mmah16(f32x4 acc, const Frag4<true> &a, const Frag4<true> &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, make_uint2(a.p[0], a.p[1])),
+                                                 __builtin_bit_cast(f16x4, make_uint2(b.p[0], b.p[1])), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mmah32(f32x4 acc, const Frag8<true> &a, const Frag8<true> &b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(f16x8, make_uint4(a.p[0], a.p[1], a.p[2], a.p[3])),
+        __builtin_bit_cast(f16x8, make_uint4(b.p[0], b.p[1], b.p[2], b.p[3])), acc, 0, 0, 0);
 }
 
 // I/O element access by dtype.

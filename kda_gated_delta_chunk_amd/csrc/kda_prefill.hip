@@ -77,19 +77,26 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 //   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
 //                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
 //                  columns 4a .. 4a+3
-template <bool BF, int K, int CS>
+// H16: the state pass's operands as fp16 singles (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b),
+// P, T and -Wk are bounded by |q|, |k| and the solve, so fp16's 11 significant bits replace the bf16
+// hi + lo pairs and bf16 singles in fewer bytes.
+template <bool BF, int K, int CS, bool H16 = false>
 struct SubLayout {
+    static_assert(!H16 || (BF && CS == 1), "fp16 operands: bf16 I/O, 16-token chunks");
     static constexpr int ES = BF ? 2 : 4;
     static constexpr int KS = K / 32;  // 32-deep reduction steps over key channels
     static constexpr int KT = K / 16;  // 16-row tiles of the state
     static constexpr int F8 = 64 * 8 * ES;
     static constexpr int F4 = 64 * 4 * ES;
+    static constexpr bool PAIRS = BF && !H16;           // bf16 hi + lo pairs
     static constexpr int WK = 0;                        // -Wk rows [KS][64][8]
-    static constexpr int QH = WK + KS * F8;             // Q*Gamma [KS][64][8] (hi)
-    static constexpr int QL = QH + KS * F8;             // Q*Gamma lo part (bf16 only)
-    static constexpr int KP = QL + (BF ? KS * F8 : 0);  // K*exp(b_C-b), bf16 [KT][64][8], fp32 [KT/2][64][8]
-    static constexpr int PP = KP + (BF ? KT : KT / 2) * F8;  // P tiles [CS][64][8] (hi | lo)
-    static constexpr int TT = PP + CS * (BF ? F8 : F4); // T tiles [CS][64][4]
+    static constexpr int QH = WK + KS * F8;             // Q*Gamma [KS][64][8] (hi; fp16: whole)
+    static constexpr int QL = QH + KS * F8;             // Q*Gamma lo part (bf16 pairs only)
+    static constexpr int KP = QL + (PAIRS ? KS * F8 : 0);  // K*exp(b_C-b): bf16 [KT][64][8] (hi | lo),
+                                                        // fp16 [KT][64][4], fp32 [KT/2][64][8]
+    static constexpr int PP = KP + (PAIRS ? KT * F8 : H16 ? KT * F4 : (KT / 2) * F8);  // P tiles [CS][64][8]
+                                                        // (hi | lo), fp16 [CS][64][4]
+    static constexpr int TT = PP + CS * (PAIRS ? F8 : F4); // T tiles [CS][64][4]
     static constexpr int GC = TT + CS * F4;             // Gamma_C [K] fp32 in state-row order (sub-tile 0)
     static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
     static constexpr int BYTES = UNITS * 1024;
@@ -351,6 +358,32 @@ __device__ __forceinline__ void st_run4(char *dst, float a, float b, float c, fl
     else *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
 }
 
+// fp16 variants (H16 layout): one element, four consecutive values (8 bytes).
+__device__ __forceinline__ void st_elem_h(char *base, int idx, float x) {
+    reinterpret_cast<uint16_t *>(base)[idx] = (uint16_t)pack_h(x, 0.f);
+}
+__device__ __forceinline__ void st_run4_h(char *dst, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_h(a, b), pack_h(c, d));
+}
+// K*exp(b_C - b) staged as fp16 [K][16 tokens] (H16), and out to the workspace as [KT][64][4]: lane
+// (a, m) of tile rt holds tokens 4a .. 4a+3 of key channel state_row_channel(16 rt + m) (the A operand
+// of a 16-deep product).
+template <int K>
+__device__ __forceinline__ void put_kp8_h(char *tile, int c0, int r, const float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st_elem_h(tile, (c0 + j) * 16 + r, x[j]);
+}
+template <int K>
+__device__ __forceinline__ void store_kp_h(const char *tile, char *dst, int lane) {
+    constexpr int KT = K / 16;
+    const int ag = lane >> 4, r = lane & 15;
+    const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile);
+#pragma unroll
+    for (int rt = 0; rt < KT; ++rt)
+        *reinterpret_cast<uint2 *>(dst + (rt * 64 + lane) * 8) =
+            *reinterpret_cast<const uint2 *>(t16 + state_row_channel(16 * rt + r) * 16 + 4 * ag);
+}
+
 // K*exp(b_C - b) staging: a per-wavefront LDS tile of one sub-tile, [K][16 tokens], channel-major.
 // bf16: hi parts [K][16], then lo parts [K][16] (hi + lo carries about 16 significant bits: the
 // state update is the one product whose rounding reaches S_final undamped); fp32: one [K][16] tile.
@@ -443,9 +476,9 @@ struct PrepParams {
 // The 16-token prep of item (chunk g0 + item / H, head item % H) by one
 // wavefront, with D::WAVE bytes of LDS of its own at `lds`. No workgroup
 // barriers: wavefronts of a workgroup are independent.
-template <bool BF, int K, bool CONV = false>
+template <bool BF, int K, bool CONV = false, bool H16 = false>
 __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, char *lds) {
-    using L = SubLayout<BF, K, 1>;
+    using L = SubLayout<BF, K, 1, H16>;
     using D = PrepLds<BF, K>;
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP;
     const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
@@ -524,14 +557,23 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
             kg[j] = kv[s][j] * e;
             ki[j] = kv[s][j] * ei;
             kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
-            st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
+            if constexpr (H16) st_elem_h(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
+            else st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
         }
-        put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
+        if constexpr (H16) put_kp8_h<K>(kx, 32 * s + 8 * ag, r, kpv);
+        else put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
         split8(qg, qh[s], ql[s]);
         kgf[s] = frag8_of(kg, Frag8<BF>{});
         split8(ki, kih[s], kil[s]);
-        st_frag8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES, qh[s]);
-        if constexpr (BF) st_frag8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES, ql[s]);
+        if constexpr (H16) {  // Q*Gamma for the state pass as fp16 (its A and P products here stay bf16)
+            Frag8<true> qf;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) qf.p[t] = pack_h(qg[2 * t], qg[2 * t + 1]);
+            st_frag8<true>(blk + L::QH + (s * 64 + lane) * 8 * ES, qf);
+        } else {
+            st_frag8<BF>(blk + L::QH + (s * 64 + lane) * 8 * ES, qh[s]);
+            if constexpr (BF) st_frag8<BF>(blk + L::QL + (s * 64 + lane) * 8 * ES, ql[s]);
+        }
     }
 
     // ---- A = K*Gamma (K/Gamma)^T and P = Q*Gamma (K/Gamma)^T over key channels: both
@@ -579,12 +621,19 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     {
         const float4 tv = *reinterpret_cast<const float4 *>(sT + r * MP + 4 * ag);
         const float4 pv = *reinterpret_cast<const float4 *>(sP + r * MP + 4 * ag);
-        set4(tf, tv.x, tv.y, tv.z, tv.w);
-        Frag4<BF> ph, pl;
-        split4(pv, ph, pl);
-        st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
-        if constexpr (BF) *reinterpret_cast<uint4 *>(blk + L::PP + lane * 16) = make_uint4(ph.p[0], ph.p[1], pl.p[0], pl.p[1]);
-        else st_frag4<BF>(blk + L::PP + lane * 16, ph);
+        if constexpr (H16) {  // T and P as fp16 (T also feeds the fp16 Wk product below)
+            tf.p[0] = pack_h(tv.x, tv.y);
+            tf.p[1] = pack_h(tv.z, tv.w);
+            st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
+            *reinterpret_cast<uint2 *>(blk + L::PP + lane * 8) = make_uint2(pack_h(pv.x, pv.y), pack_h(pv.z, pv.w));
+        } else {
+            set4(tf, tv.x, tv.y, tv.z, tv.w);
+            Frag4<BF> ph, pl;
+            split4(pv, ph, pl);
+            st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
+            if constexpr (BF) *reinterpret_cast<uint4 *>(blk + L::PP + lane * 16) = make_uint4(ph.p[0], ph.p[1], pl.p[0], pl.p[1]);
+            else st_frag4<BF>(blk + L::PP + lane * 16, ph);
+        }
     }
 
     // ---- Wk^T = (K*Gamma)^T T^T, one 16-channel tile t at a time: A operand from the
@@ -595,18 +644,21 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
         f32x4 w[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t)
-            w[t] = mma16(zero4(), ld_frag4<BF>(xt + ((16 * t + r) * 16 + 4 * ag) * ES), tf);
+            if constexpr (H16) w[t] = mmah16(zero4(), ld_frag4<BF>(xt + ((16 * t + r) * 16 + 4 * ag) * ES), tf);
+            else w[t] = mma16(zero4(), ld_frag4<BF>(xt + ((16 * t + r) * 16 + 4 * ag) * ES), tf);
         mfma_fence_all(w);
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
             const int dl = 16 * (2 * (t & 1) + (ag >> 1)) + r;
-            st_run4<BF>(blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES, -w[t][0], -w[t][1], -w[t][2],
-                        -w[t][3]);
+            char *wd = blk + L::WK + (((t >> 1) * 64 + dl) * 8 + 4 * (ag & 1)) * ES;
+            if constexpr (H16) st_run4_h(wd, -w[t][0], -w[t][1], -w[t][2], -w[t][3]);
+            else st_run4<BF>(wd, -w[t][0], -w[t][1], -w[t][2], -w[t][3]);
         }
     }
 
     // ---- K*exp(b_C - b) (staged in LDS since the start) out in state-row order
-    store_kp<BF, K>(kx, blk + L::KP, lane);
+    if constexpr (H16) store_kp_h<K>(kx, blk + L::KP, lane);
+    else store_kp<BF, K>(kx, blk + L::KP, lane);
 
     // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
     if (r == 0) {
@@ -624,11 +676,11 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
 
 // At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
 // the matrix-core accumulators in VGPRs, as mfma_fence expects.
-template <bool BF, int K, bool CONV>
+template <bool BF, int K, bool CONV, bool H16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_chunk_prep(PrepParams pa) {
     extern __shared__ __align__(16) char smem[];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    prep16_item<BF, K, CONV>(pa, (int64_t)blockIdx.x * 4 + wave, smem + wave * PrepLds<BF, K>::WAVE);
+    prep16_item<BF, K, CONV, H16>(pa, (int64_t)blockIdx.x * 4 + wave, smem + wave * PrepLds<BF, K>::WAVE);
 }
 
 // ------------------------------------------------- chunk prep, 64 tokens
@@ -1153,9 +1205,9 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // time, each as soon as its slot is free.
 // VLO: v comes as a bf16 hi + lo pair (a convolved v, whose values are not bf16 themselves); the
 // loaders copy both parts and the W product takes T V_hi + T V_lo.
-template <bool BF, int K, int V, int CS, bool VLO = false>
+template <bool BF, int K, int V, int CS, bool VLO = false, bool H16 = false>
 struct StateCfg {
-    using L = SubLayout<BF, K, CS>;
+    using L = SubLayout<BF, K, CS, H16>;
     // One 16-column tile per compute wavefront, four compute wavefronts per workgroup: at V = 128 a
     // head takes two workgroups (on one XCD). Measured at 4096 tokens, 96 heads: 224 us, against
     // 262 us for one workgroup per head with two tiles per wavefront (the per-step latency of a
@@ -1238,11 +1290,21 @@ struct StateParams {
 };
 
 // The state pass of workgroup `bid` (C::LDS bytes of LDS at smem).
-template <bool BF, int K, int V, int CS, bool VLO = false>
+template <bool BF, int K, int V, int CS, bool VLO = false, bool H16 = false>
 __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char *smem) {
     static_assert(!VLO || BF, "the lo part of v is for bf16 operands");
-    using C = StateCfg<BF, K, V, CS, VLO>;
-    using L = SubLayout<BF, K, CS>;
+    static_assert(!H16 || (BF && CS == 1 && !VLO), "fp16 operands: bf16 I/O, 16-token chunks, no hi + lo v");
+    using C = StateCfg<BF, K, V, CS, VLO, H16>;
+    using L = SubLayout<BF, K, CS, H16>;
+    // products on the operands' format: bf16 or, with H16, fp16
+    auto mm32 = [](f32x4 acc, const Frag8<BF> &a, const Frag8<BF> &b) {
+        if constexpr (H16) return mmah32(acc, a, b);
+        else return mma32(acc, a, b);
+    };
+    auto pk = [](float a, float b) {
+        if constexpr (H16) return pack_h(a, b);
+        else return pack_bf16(a, b);
+    };
     constexpr int KS = K / 32, KT = K / 16, ES = C::ES, NW = C::NW, D = C::D, NL = C::NL;
     constexpr int CT = C::CT, VT = C::VT, NT = C::NT;
     const void *__restrict__ vp = pa.v;
@@ -1442,10 +1504,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 if constexpr (BF) {
-                    sb[ct][s].p[0] = pack_bf16(S[ct][2 * s][0], S[ct][2 * s][1]);
-                    sb[ct][s].p[1] = pack_bf16(S[ct][2 * s][2], S[ct][2 * s][3]);
-                    sb[ct][s].p[2] = pack_bf16(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
-                    sb[ct][s].p[3] = pack_bf16(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
+                    sb[ct][s].p[0] = pk(S[ct][2 * s][0], S[ct][2 * s][1]);
+                    sb[ct][s].p[1] = pk(S[ct][2 * s][2], S[ct][2 * s][3]);
+                    sb[ct][s].p[2] = pk(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
+                    sb[ct][s].p[3] = pk(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1469,7 +1531,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int s = 0; s < KS; ++s) qh[s] = ld_frag8<BF>(sl + L::QH + (s * 64 + lane) * 8 * ES);
         } else if (part == 1) {
-            if constexpr (BF) {
+            if constexpr (BF && !H16) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s) ql[s] = ld_frag8<BF>(sl + L::QL + (s * 64 + lane) * 8 * ES);
             }
@@ -1504,6 +1566,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             vf[0].p[1] = (vraw[2] & 0xffffu) | (vraw[3] << 16);
             vf[CT - 1].p[0] = (vraw[0] >> 16) | (vraw[1] & 0xffff0000u);
             vf[CT - 1].p[1] = (vraw[2] >> 16) | (vraw[3] & 0xffff0000u);
+        } else if constexpr (H16) {  // the v tile arrives as bf16: widen exactly, round to fp16
+            vf[0].p[0] = pack_h(__uint_as_float(vraw[0] << 16), __uint_as_float(vraw[1] << 16));
+            vf[0].p[1] = pack_h(__uint_as_float(vraw[2] << 16), __uint_as_float(vraw[3] << 16));
         } else if constexpr (BF) {
             vf[0].p[0] = vraw[0] | (vraw[1] << 16);
             vf[0].p[1] = vraw[2] | (vraw[3] << 16);
@@ -1554,10 +1619,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             if constexpr (BF) {
-                sb[ct][s].p[0] = pack_bf16(S[ct][2 * s][0], S[ct][2 * s][1]);
-                sb[ct][s].p[1] = pack_bf16(S[ct][2 * s][2], S[ct][2 * s][3]);
-                sb[ct][s].p[2] = pack_bf16(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
-                sb[ct][s].p[3] = pack_bf16(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
+                sb[ct][s].p[0] = pk(S[ct][2 * s][0], S[ct][2 * s][1]);
+                sb[ct][s].p[1] = pk(S[ct][2 * s][2], S[ct][2 * s][3]);
+                sb[ct][s].p[2] = pk(S[ct][2 * s + 1][0], S[ct][2 * s + 1][1]);
+                sb[ct][s].p[3] = pk(S[ct][2 * s + 1][2], S[ct][2 * s + 1][3]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1632,30 +1697,37 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                                   cat4(vhist[I][ct], two ? vhist[I1][ct] : vhistl[I][ct]));
                     if (two) W[ct] = mma32(W[ct], cat4(tt[I], tt[I1]), cat4(vhistl[I][ct], vhistl[I1][ct]));
                 } else {
-                    W[ct] = mma32(W[ct], cat4(tt[I], two ? tt[I + 1 < CS ? I + 1 : I] : z),
-                                  cat4(vhist[I][ct], two ? vhist[I + 1 < CS ? I + 1 : I][ct] : z));
+                    W[ct] = mm32(W[ct], cat4(tt[I], two ? tt[I + 1 < CS ? I + 1 : I] : z),
+                                 cat4(vhist[I][ct], two ? vhist[I + 1 < CS ? I + 1 : I][ct] : z));
                 }
             }
 #pragma unroll
-            for (int s = 0; s < KS; ++s) W[ct] = mma32(W[ct], wk[s], sb[ct][s]);
+            for (int s = 0; s < KS; ++s) W[ct] = mm32(W[ct], wk[s], sb[ct][s]);
         }
         // the previous step's o rows (in LDS before this step's done flag)
         if (u > 0) write_o(u - 1);
-        constexpr int NKP = BF ? KT : KT / 2;  // bf16: [hi | lo] of tile rt; fp32: tiles 2p, 2p+1
+        constexpr int NKP = H16 ? 1 : BF ? KT : KT / 2;  // bf16: [hi | lo] of tile rt; fp32: tiles 2p, 2p+1
         Frag8<BF> kp2[NKP];
+        Frag4<true> kp4[H16 ? KT : 1];  // H16: tile rt, fp16
+        if constexpr (H16) {
 #pragma unroll
-        for (int p2 = 0; p2 < NKP; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
+            for (int rt = 0; rt < KT; ++rt) kp4[rt] = ld_frag4<true>(sl + L::KP + (rt * 64 + lane) * 8);
+        } else {
+#pragma unroll
+            for (int p2 = 0; p2 < NKP; ++p2) kp2[p2] = ld_frag8<BF>(sl + L::KP + (p2 * 64 + lane) * 8 * ES);
+        }
         // Gamma_C (first sub-tile of a chunk): lane (tg, cl) reads state rows 16(cl/2) + 4tg +
         // 2(cl%2) + {0, 1}; row rt, entry i of lane group tg then comes from lane 2rt + i/2 of the
         // same row (DPP row broadcast)
         float2 g2 = make_float2(1.f, 1.f);
         if (R == 0) g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
         Frag8<true> pp[CS];  // bf16: [Ph | Pl] of tile I
-        Frag4<BF> ph[CS];    // fp32: P tile I
+        Frag4<BF> ph[CS];    // fp32: P tile I; H16: P tile I as fp16
 #pragma unroll
         for (int I = 0; I < CS; ++I) {
             if (I > R) continue;
-            if constexpr (BF) pp[I] = ld_frag8<true>(sl + L::PP + (I * 64 + lane) * 16);
+            if constexpr (H16) ph[I] = ld_frag4<true>(sl + L::PP + (I * 64 + lane) * 8);
+            else if constexpr (BF) pp[I] = ld_frag8<true>(sl + L::PP + (I * 64 + lane) * 16);
             else ph[I] = ld_frag4<BF>(sl + L::PP + (I * 64 + lane) * 16);
         }
         // one product (per tile), then two reads, while the chain runs
@@ -1673,8 +1745,8 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             O[ct] = zero4();
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                O[ct] = mma32(O[ct], qh[s], sb[ct][s]);
-                if constexpr (BF) O[ct] = mma32(O[ct], ql[s], sb[ct][s]);
+                O[ct] = mm32(O[ct], qh[s], sb[ct][s]);
+                if constexpr (BF && !H16) O[ct] = mma32(O[ct], ql[s], sb[ct][s]);
             }
         }
         if constexpr (!BF) {
@@ -1686,9 +1758,13 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // multiplied by [Wh | Wh] and then by [Wl | Wl], the two products sum all four cross
         // terms. fp32: W kept whole ([W | 0]).
         Frag8<BF> whh[CT], wll[CT];
+        Frag4<true> w16[CT];  // H16: W as one fp16 operand (the B operand of 16-deep products)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            if constexpr (BF) {
+            if constexpr (H16) {
+                w16[ct].p[0] = pack_h(W[ct][0], W[ct][1]);
+                w16[ct].p[1] = pack_h(W[ct][2], W[ct][3]);
+            } else if constexpr (BF) {
                 uint32_t wh0, wl0, wh1, wl1;
                 split_bf16(W[ct][0], W[ct][1], wh0, wl0);
                 split_bf16(W[ct][2], W[ct][3], wh1, wl1);
@@ -1705,8 +1781,10 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             if (I == R)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    whist[I][ct] = whh[ct];
-                    if constexpr (BF) wlist[I][ct] = wll[ct];
+                    if constexpr (!H16) {
+                        whist[I][ct] = whh[ct];
+                        if constexpr (BF) wlist[I][ct] = wll[ct];
+                    }
                 }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -1731,7 +1809,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                     if (CS == 1 || R == 0) {
                         S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
                     }
-                    if constexpr (BF) {
+                    if constexpr (H16) {
+                        S[ct][rt] = mmah16(S[ct][rt], kp4[rt], w16[ct]);
+                    } else if constexpr (BF) {
                         S[ct][rt] = mma32(S[ct][rt], kp2[rt], whh[ct]);
                         S[ct][rt] = mma32(S[ct][rt], kp2[rt], wll[ct]);
                     } else {
@@ -1761,7 +1841,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int I = 0; I < CS; ++I) {
                 if (I > R) continue;
-                if constexpr (BF) {
+                if constexpr (H16) {
+                    O[ct] = mmah16(O[ct], ph[I], w16[ct]);
+                } else if constexpr (BF) {
                     O[ct] = mma32(O[ct], pp[I], whist[I][ct]);
                     O[ct] = mma32(O[ct], pp[I], wlist[I][ct]);
                 } else {
@@ -1797,17 +1879,17 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     }
 }
 
-template <bool BF, int K, int V, int CS, bool VLO>
-__global__ __launch_bounds__((StateCfg<BF, K, V, CS, VLO>::THREADS)) void kda_state_pass(StateParams pa) {
+template <bool BF, int K, int V, int CS, bool VLO, bool H16>
+__global__ __launch_bounds__((StateCfg<BF, K, V, CS, VLO, H16>::THREADS)) void kda_state_pass(StateParams pa) {
     extern __shared__ __align__(1024) char smem[];
-    state_body<BF, K, V, CS, VLO>(pa, blockIdx.x, smem);
+    state_body<BF, K, V, CS, VLO, H16>(pa, blockIdx.x, smem);
 }
 
 // Prep wavefronts per workgroup of the combined kernel below (each owns PrepLds::WAVE bytes of
 // the state pass's LDS).
-template <bool BF, int K, int V>
+template <bool BF, int K, int V, bool H16>
 constexpr int combined_prep_waves() {
-    using C = StateCfg<BF, K, V, 1>;
+    using C = StateCfg<BF, K, V, 1, false, H16>;
     constexpr int byl = C::LDS / PrepLds<BF, K>::WAVE, byw = C::THREADS / 64;
     return byl < byw ? byl : byw;
 }
@@ -1816,18 +1898,19 @@ constexpr int combined_prep_waves() {
 // first) and the 16-token prep of the next range (the remaining workgroups, on the CUs the state
 // pass leaves free). The state pass of H heads occupies 2H workgroups (V = 128), one per CU; the
 // prep of the following chunks then runs beside it instead of after it.
-template <bool BF, int K, int V>
-__global__ __launch_bounds__((StateCfg<BF, K, V, 1>::THREADS)) void kda_state_prep(StateParams sa, PrepParams pa,
-                                                                                   int32_t nstate) {
+template <bool BF, int K, int V, bool H16>
+__global__ __launch_bounds__((StateCfg<BF, K, V, 1, false, H16>::THREADS)) void kda_state_prep(StateParams sa,
+                                                                                              PrepParams pa,
+                                                                                              int32_t nstate) {
     extern __shared__ __align__(1024) char smem[];
     if ((int)blockIdx.x < nstate) {
-        state_body<BF, K, V, 1>(sa, blockIdx.x, smem);
+        state_body<BF, K, V, 1, false, H16>(sa, blockIdx.x, smem);
         return;
     }
-    constexpr int PW = combined_prep_waves<BF, K, V>();
+    constexpr int PW = combined_prep_waves<BF, K, V, H16>();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave >= PW) return;
-    prep16_item<BF, K>(pa, (int64_t)(blockIdx.x - nstate) * PW + wave, smem + wave * PrepLds<BF, K>::WAVE);
+    prep16_item<BF, K, false, H16>(pa, (int64_t)(blockIdx.x - nstate) * PW + wave, smem + wave * PrepLds<BF, K>::WAVE);
 }
 
 }  // namespace kda
@@ -1847,17 +1930,22 @@ size_t table_bytes(int32_t num_seqs) {
     return align_up((size_t)(num_seqs + 1) * sizeof(int64_t)) + align_up((size_t)(num_seqs + 1) * sizeof(int32_t));
 }
 
-template <bool BF, int K, int CS>
-size_t chunk_bytes() { return (size_t)CS * SubLayout<BF, K, CS>::BYTES; }
+template <bool BF, int K, int CS, bool H16>
+size_t chunk_bytes() { return (size_t)CS * SubLayout<BF, K, CS, H16>::BYTES; }
 
-template <bool BF, int CS>
+template <bool BF, int CS, bool H16 = false>
 size_t chunk_bytes_k(int K) {
-    return K == 32 ? chunk_bytes<BF, 32, CS>() : K == 64 ? chunk_bytes<BF, 64, CS>() : chunk_bytes<BF, 128, CS>();
+    return K == 32 ? chunk_bytes<BF, 32, CS, H16>() : K == 64 ? chunk_bytes<BF, 64, CS, H16>()
+                                                             : chunk_bytes<BF, 128, CS, H16>();
 }
-size_t chunk_bytes_rt(bool bf, int K, int chunk) {
+size_t chunk_bytes_rt(bool bf, int K, int chunk, bool h16) {
     if (chunk == 64) return bf ? chunk_bytes_k<true, 4>(K) : chunk_bytes_k<false, 4>(K);
+    if (h16) return chunk_bytes_k<true, 1, true>(K);
     return bf ? chunk_bytes_k<true, 1>(K) : chunk_bytes_k<false, 1>(K);
 }
+// The state pass's operands as fp16 singles (SubLayout H16): bf16 I/O at 16-token chunks, without a
+// short convolution (whose v comes as hi + lo parts).
+bool use_h16(bool io_bf16, int32_t chunk, bool conv) { return io_bf16 && chunk == 16 && !conv; }
 
 struct WsPtrs {
     int64_t *seq_tok;
@@ -1873,8 +1961,8 @@ struct WsPtrs {
 bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk);
 // Workspace: chunk table | per-(chunk, head) factors | carry (pipelined calls) | convolved v (with a
 // convolution). The sizes depend only on the call's sizes, as prefill_workspace_bytes counts them.
-size_t frags_bytes(int64_t n_chunks_max, int32_t H, int32_t K, bool io_bf16, int32_t chunk) {
-    return align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk));
+size_t frags_bytes(int64_t n_chunks_max, int32_t H, int32_t K, bool io_bf16, int32_t chunk, bool conv) {
+    return align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk, use_h16(io_bf16, chunk, conv)));
 }
 size_t carry_bytes(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t K, int32_t V, int32_t chunk) {
     return can_pipeline(n_chunks_max, num_seqs, H, chunk) ? align_up((size_t)num_seqs * H * K * V * sizeof(float)) : 0;
@@ -1885,7 +1973,7 @@ WsPtrs ws_ptrs(const PrefillArgs &a) {
     w.seq_tok = reinterpret_cast<int64_t *>(base);
     w.chunk_off = reinterpret_cast<int32_t *>(base + align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
     w.frags = base + table_bytes(a.num_seqs);
-    char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk);
+    char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk, a.conv != 0);
     w.carry = reinterpret_cast<float *>(cp);
     w.vconv = cp + carry_bytes(a.n_chunks_max, a.num_seqs, a.H, a.K, a.V, a.chunk);
     const size_t nth = (size_t)a.B * a.T * a.H;
@@ -1981,9 +2069,9 @@ hipError_t launch_conv_qk(const PrefillArgs &a, const WsPtrs &w, hipStream_t st)
     return e != hipSuccess ? e : launch_conv<BF, K, 0>(a, w, a.k, a.K, w.kconv, nullptr, st);
 }
 
-template <bool BF, int K, bool CONV>
+template <bool BF, int K, bool CONV, bool H16>
 hipError_t prep_launch(int32_t chunk, int64_t items, const PrepParams &pp, hipStream_t st) {
-    if (chunk == 64) {
+    if (!H16 && chunk == 64) {
         static bool lds_set = false;
         constexpr int LDS = Prep64Lds<BF, K>::BYTES;
         hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep64<BF, K, CONV>), lds_set, LDS);
@@ -1992,9 +2080,10 @@ hipError_t prep_launch(int32_t chunk, int64_t items, const PrepParams &pp, hipSt
     } else {
         static bool lds_set = false;
         constexpr int LDS = 4 * PrepLds<BF, K>::WAVE;
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep<BF, K, CONV>), lds_set, LDS);
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_chunk_prep<BF, K, CONV, H16>), lds_set, LDS);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((kda_chunk_prep<BF, K, CONV>), dim3((unsigned)((items + 3) / 4)), dim3(256), LDS, st, pp);
+        hipLaunchKernelGGL((kda_chunk_prep<BF, K, CONV, H16>), dim3((unsigned)((items + 3) / 4)), dim3(256), LDS, st,
+                           pp);
     }
     return hipGetLastError();
 }
@@ -2006,7 +2095,11 @@ hipError_t prep_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t
     if (n <= 0) return hipSuccess;
     const int64_t items = n * a.H;
     const PrepParams pp = prep_params(a, w, g0, g1);
-    return a.conv ? prep_launch<BF, K, true>(a.chunk, items, pp, st) : prep_launch<BF, K, false>(a.chunk, items, pp, st);
+    if constexpr (BF) {
+        if (use_h16(a.io_bf16, a.chunk, a.conv != 0)) return prep_launch<BF, K, false, true>(a.chunk, items, pp, st);
+    }
+    return a.conv ? prep_launch<BF, K, true, false>(a.chunk, items, pp, st)
+                  : prep_launch<BF, K, false, false>(a.chunk, items, pp, st);
 }
 
 template <bool BF, int K>
@@ -2023,13 +2116,13 @@ unsigned state_grid(const PrefillArgs &a) {
     return (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * StateCfg<BF, K, V, CS>::NT);
 }
 
-template <bool BF, int K, int V, int CS, bool VLO>
+template <bool BF, int K, int V, int CS, bool VLO, bool H16>
 hipError_t state_range_t(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
-    using C = StateCfg<BF, K, V, CS, VLO>;
+    using C = StateCfg<BF, K, V, CS, VLO, H16>;
     static bool lds_set = false;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS, VLO>), lds_set, C::LDS);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS, VLO, H16>), lds_set, C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS, VLO>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS),
+    hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS, VLO, H16>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS),
                        C::LDS, st, state_params(a, w, g0, g1, first));
     return hipGetLastError();
 }
@@ -2037,9 +2130,10 @@ hipError_t state_range_t(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int3
 template <bool BF, int K, int V, int CS>
 hipError_t state_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
     if constexpr (BF) {
-        if (a.conv) return state_range_t<BF, K, V, CS, true>(a, w, g0, g1, first, st);
+        if (a.conv) return state_range_t<BF, K, V, CS, true, false>(a, w, g0, g1, first, st);
+        if constexpr (CS == 1) return state_range_t<BF, K, V, CS, false, true>(a, w, g0, g1, first, st);  // H16
     }
-    return state_range_t<BF, K, V, CS, false>(a, w, g0, g1, first, st);
+    return state_range_t<BF, K, V, CS, false, false>(a, w, g0, g1, first, st);
 }
 
 template <bool BF, int K, int V, int CS>
@@ -2053,8 +2147,9 @@ hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
 // combined kernel {state(s), prep(s+1)}; then state(last).
 template <bool BF, int K, int V>
 hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
-    using C = StateCfg<BF, K, V, 1>;
-    constexpr int PW = combined_prep_waves<BF, K, V>();
+    constexpr bool H16 = BF;  // 16-token chunks, no convolution: bf16 I/O runs the fp16-operand variant
+    using C = StateCfg<BF, K, V, 1, false, H16>;
+    constexpr int PW = combined_prep_waves<BF, K, V, H16>();
     static_assert(PW >= 1, "no room for prep wavefronts");
     const WsPtrs w = ws_ptrs(a);
     const int64_t per = (a.n_chunks_max + nseg - 1) / nseg;
@@ -2064,13 +2159,13 @@ hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
     if (e == hipSuccess) e = prep_range<BF, K>(a, w, g(0), g(1), st);
     if (e != hipSuccess) return e;
     static bool lds_set = false;
-    e = allow_lds(reinterpret_cast<const void *>(&kda_state_prep<BF, K, V>), lds_set, C::LDS);
+    e = allow_lds(reinterpret_cast<const void *>(&kda_state_prep<BF, K, V, H16>), lds_set, C::LDS);
     if (e != hipSuccess) return e;
     const unsigned nstate = state_grid<BF, K, V, 1>(a);
     for (int s = 0; s + 1 < nseg; ++s) {
         const int64_t items = (int64_t)(g(s + 2) - g(s + 1)) * a.H;
         const unsigned grid = nstate + (unsigned)((items + PW - 1) / PW);
-        hipLaunchKernelGGL((kda_state_prep<BF, K, V>), dim3(grid), dim3(C::THREADS), C::LDS, st,
+        hipLaunchKernelGGL((kda_state_prep<BF, K, V, H16>), dim3(grid), dim3(C::THREADS), C::LDS, st,
                            state_params(a, w, g(s), g(s + 1), s == 0), prep_params(a, w, g(s + 1), g(s + 2)),
                            (int32_t)nstate);
         e = hipGetLastError();
@@ -2124,7 +2219,7 @@ int pipeline_ranges(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t c
 
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv) {
-    size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk) +
+    size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk, conv) +
                carry_bytes(n_chunks_max, num_seqs, H, K, V, chunk);
     if (conv)  // convolved v (fp32, or bf16 hi + lo), q and k (fp32)
         b += align_up((size_t)n_tokens * H * V * 4) + 2 * align_up((size_t)n_tokens * H * K * 4);

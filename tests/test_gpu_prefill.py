@@ -551,7 +551,9 @@ def test_conv_varlen_whole_prologue(chunk):
 
 def test_conv_identity_taps_change_nothing():
     """Taps (0, 0, 0, 1) without SiLU give every input back exactly, so o and S_final equal those of the call
-    without a convolution bit for bit (fp32 and bf16, both chunk sizes)."""
+    without a convolution bit for bit where both calls carry the same operand format (fp32; bf16 at 64-token
+    chunks). At 16-token chunks a bf16 call without a convolution carries the state pass's operands as fp16
+    and one with a convolution as bf16 hi + lo pairs: there the two agree to the parity bound."""
     _announce("conv_identity", seed=72)
     for io in ("fp32", "bf16"):
         inp = synth.prefill_inputs(2, 90, 3, 64, 128, io, seed=72, device=DEV, with_S0=True)
@@ -560,7 +562,12 @@ def test_conv_identity_taps_change_nothing():
         for chunk in (16, 64):
             o1, S1 = _run(inp, chunk=chunk)
             o2, S2 = _run(dict(inp, conv="short4", conv_w=w), chunk=chunk)
-            assert torch.equal(o1, o2) and torch.equal(S1, S2), (io, chunk)
+            if io == "bf16" and chunk == 16:
+                o1f, _ = _run(inp, chunk=chunk, o_dtype=torch.float32)
+                o2f, _ = _run(dict(inp, conv="short4", conv_w=w), chunk=chunk, o_dtype=torch.float32)
+                assert err(o1f.cpu(), o2f.cpu()) <= TOL_BF16 and err(S1.cpu(), S2.cpu()) <= TOL_BF16
+            else:
+                assert torch.equal(o1, o2) and torch.equal(S1, S2), (io, chunk)
 
 
 def test_conv_split_calls_match_one_call():
