@@ -52,6 +52,8 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t &hi, uint3
     lo = pack_bf16(a - bf_lo(hi), b - bf_hi(hi));
 }
 
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
 // Round two floats to fp16 (round-to-nearest-even) and pack (a in the low half).
 __device__ __forceinline__ uint32_t pack_h(float a, float b) {
     typedef __attribute__((ext_vector_type(2))) _Float16 h2;

@@ -77,9 +77,11 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 //   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
 //                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
 //                  columns 4a .. 4a+3
-// H16: the state pass's operands as fp16 singles (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b),
-// P, T and -Wk are bounded by |q|, |k| and the solve, so fp16's 11 significant bits replace the bf16
-// hi + lo pairs and bf16 singles in fewer bytes.
+// H16: the state pass's operands in fp16 (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b), T and
+// -Wk as singles, P as an fp16 hi + lo pair (P W, with W also split in registers, is the term that
+// decides the output's error; the state update takes W as one fp16). All are bounded by |q|, |k| and
+// the solve, so fp16's 11 significant bits replace the bf16 hi + lo pairs and bf16 singles in fewer
+// bytes.
 template <bool BF, int K, int CS, bool H16 = false>
 struct SubLayout {
     static_assert(!H16 || (BF && CS == 1), "fp16 operands: bf16 I/O, 16-token chunks");
@@ -95,8 +97,8 @@ struct SubLayout {
     static constexpr int KP = QL + (PAIRS ? KS * F8 : 0);  // K*exp(b_C-b): bf16 [KT][64][8] (hi | lo),
                                                         // fp16 [KT][64][4], fp32 [KT/2][64][8]
     static constexpr int PP = KP + (PAIRS ? KT * F8 : H16 ? KT * F4 : (KT / 2) * F8);  // P tiles [CS][64][8]
-                                                        // (hi | lo), fp16 [CS][64][4]
-    static constexpr int TT = PP + CS * (PAIRS ? F8 : F4); // T tiles [CS][64][4]
+                                                        // (hi | lo; fp16 hi | lo with H16)
+    static constexpr int TT = PP + CS * (BF ? F8 : F4); // T tiles [CS][64][4]
     static constexpr int GC = TT + CS * F4;             // Gamma_C [K] fp32 in state-row order (sub-tile 0)
     static constexpr int UNITS = (GC + K * 4 + 1023) / 1024;  // whole 1 KiB units (DMA granule)
     static constexpr int BYTES = UNITS * 1024;
@@ -621,11 +623,16 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     {
         const float4 tv = *reinterpret_cast<const float4 *>(sT + r * MP + 4 * ag);
         const float4 pv = *reinterpret_cast<const float4 *>(sP + r * MP + 4 * ag);
-        if constexpr (H16) {  // T and P as fp16 (T also feeds the fp16 Wk product below)
+        if constexpr (H16) {  // T as fp16 (it also feeds the fp16 Wk product below), P as an fp16 hi + lo pair
             tf.p[0] = pack_h(tv.x, tv.y);
             tf.p[1] = pack_h(tv.z, tv.w);
             st_frag4<BF>(blk + L::TT + lane * 4 * ES, tf);
-            *reinterpret_cast<uint2 *>(blk + L::PP + lane * 8) = make_uint2(pack_h(pv.x, pv.y), pack_h(pv.z, pv.w));
+            const uint32_t h0 = pack_h(pv.x, pv.y), h1 = pack_h(pv.z, pv.w);
+            const uint32_t l0 = pack_h(pv.x - (float)__builtin_bit_cast(f16x2_t, h0)[0],
+                                       pv.y - (float)__builtin_bit_cast(f16x2_t, h0)[1]);
+            const uint32_t l1 = pack_h(pv.z - (float)__builtin_bit_cast(f16x2_t, h1)[0],
+                                       pv.w - (float)__builtin_bit_cast(f16x2_t, h1)[1]);
+            *reinterpret_cast<uint4 *>(blk + L::PP + lane * 16) = make_uint4(h0, h1, l0, l1);
         } else {
             set4(tf, tv.x, tv.y, tv.z, tv.w);
             Frag4<BF> ph, pl;
@@ -1722,12 +1729,11 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         float2 g2 = make_float2(1.f, 1.f);
         if (R == 0) g2 = *reinterpret_cast<const float2 *>(sl + L::GC + (16 * (cl >> 1) + 4 * tg + 2 * (cl & 1)) * 4);
         Frag8<true> pp[CS];  // bf16: [Ph | Pl] of tile I
-        Frag4<BF> ph[CS];    // fp32: P tile I; H16: P tile I as fp16
+        Frag4<BF> ph[CS];    // fp32: P tile I
 #pragma unroll
         for (int I = 0; I < CS; ++I) {
             if (I > R) continue;
-            if constexpr (H16) ph[I] = ld_frag4<true>(sl + L::PP + (I * 64 + lane) * 8);
-            else if constexpr (BF) pp[I] = ld_frag8<true>(sl + L::PP + (I * 64 + lane) * 16);
+            if constexpr (BF) pp[I] = ld_frag8<true>(sl + L::PP + (I * 64 + lane) * 16);
             else ph[I] = ld_frag4<BF>(sl + L::PP + (I * 64 + lane) * 16);
         }
         // one product (per tile), then two reads, while the chain runs
@@ -1758,12 +1764,18 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // multiplied by [Wh | Wh] and then by [Wl | Wl], the two products sum all four cross
         // terms. fp32: W kept whole ([W | 0]).
         Frag8<BF> whh[CT], wll[CT];
-        Frag4<true> w16[CT];  // H16: W as one fp16 operand (the B operand of 16-deep products)
+        Frag4<true> w16[CT];  // H16: W rounded to fp16 (the state update's B operand); the output's P W
+                              // term takes W as an fp16 hi + lo pair (whh, wll), as it decides o's error
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             if constexpr (H16) {
-                w16[ct].p[0] = pack_h(W[ct][0], W[ct][1]);
-                w16[ct].p[1] = pack_h(W[ct][2], W[ct][3]);
+                const uint32_t h0 = pack_h(W[ct][0], W[ct][1]), h1 = pack_h(W[ct][2], W[ct][3]);
+                const f16x2_t a = __builtin_bit_cast(f16x2_t, h0), b = __builtin_bit_cast(f16x2_t, h1);
+                const uint32_t l0 = pack_h(W[ct][0] - (float)a[0], W[ct][1] - (float)a[1]);
+                const uint32_t l1 = pack_h(W[ct][2] - (float)b[0], W[ct][3] - (float)b[1]);
+                w16[ct].p[0] = h0; w16[ct].p[1] = h1;
+                whh[ct].p[0] = h0; whh[ct].p[1] = h1; whh[ct].p[2] = h0; whh[ct].p[3] = h1;
+                wll[ct].p[0] = l0; wll[ct].p[1] = l1; wll[ct].p[2] = l0; wll[ct].p[3] = l1;
             } else if constexpr (BF) {
                 uint32_t wh0, wl0, wh1, wl1;
                 split_bf16(W[ct][0], W[ct][1], wh0, wl0);
@@ -1841,8 +1853,9 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 #pragma unroll
             for (int I = 0; I < CS; ++I) {
                 if (I > R) continue;
-                if constexpr (H16) {
-                    O[ct] = mmah16(O[ct], ph[I], w16[ct]);
+                if constexpr (H16) {  // [P_hi | P_lo] x [W_hi | W_hi] + [P_hi | P_lo] x [W_lo | W_lo]
+                    O[ct] = mmah32(O[ct], pp[I], whh[ct]);
+                    O[ct] = mmah32(O[ct], pp[I], wll[ct]);
                 } else if constexpr (BF) {
                     O[ct] = mma32(O[ct], pp[I], whist[I][ct]);
                     O[ct] = mma32(O[ct], pp[I], wlist[I][ct]);
