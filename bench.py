@@ -312,17 +312,17 @@ def main():
                    "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
                      "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1, false>" if dom == "state"
-                                                 else "kda::kda_chunk_prep<true, 128, false>"),
+                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1, false, true>" if dom == "state"
+                                                 else "kda::kda_chunk_prep<true, 128, false, true>"),
                      "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms,
-                     "mfma_busy_frac_rocprof": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false>"
-                                                              if dom == "state" else "kda::kda_chunk_prep<true, 128, false>",
+                     "mfma_busy_frac_rocprof": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false, true>"
+                                                              if dom == "state" else "kda::kda_chunk_prep<true, 128, false, true>",
                                                               dom_ms)},
         "roofline_path": path_roofline(r, 16),
         "kernels_ms": kern_ms,
         "kernels_mfma_busy_frac_rocprof": {
-            "kda_chunk_prep": mfma_busy_frac("kda::kda_chunk_prep<true, 128, false>", r["prep_ms"]),
-            "kda_state_pass": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false>", r["state_ms"])},
+            "kda_chunk_prep": mfma_busy_frac("kda::kda_chunk_prep<true, 128, false, true>", r["prep_ms"]),
+            "kda_state_pass": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false, true>", r["state_ms"])},
         "split_calls_ms": r["prep_ms"] + r["state_ms"],
         "workspace_bytes": r["ws_bytes"],
     }

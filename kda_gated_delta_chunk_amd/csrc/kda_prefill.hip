@@ -1932,6 +1932,7 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, 1, false, H16>::THREADS)) void 
 #include "kda_launch.hpp"
 
 #include <stdlib.h>
+#include <string.h>
 
 namespace kda {
 namespace {
@@ -1956,9 +1957,15 @@ size_t chunk_bytes_rt(bool bf, int K, int chunk, bool h16) {
     if (h16) return chunk_bytes_k<true, 1, true>(K);
     return bf ? chunk_bytes_k<true, 1>(K) : chunk_bytes_k<false, 1>(K);
 }
-// The state pass's operands as fp16 singles (SubLayout H16): bf16 I/O at 16-token chunks, without a
-// short convolution (whose v comes as hi + lo parts).
-bool use_h16(bool io_bf16, int32_t chunk, bool conv) { return io_bf16 && chunk == 16 && !conv; }
+// The state pass's operands in fp16 (SubLayout H16): bf16 I/O at 16-token chunks, without a short
+// convolution (whose v comes as hi + lo parts), unless KDA_OPERANDS=bf16 (read at each call and by the
+// workspace query) asks for the bf16 hi + lo operands, which keep bf16's range for |v| and |S| beyond
+// what fp16 holds.
+bool use_h16(bool io_bf16, int32_t chunk, bool conv) {
+    if (!io_bf16 || chunk != 16 || conv) return false;
+    const char *e = getenv("KDA_OPERANDS");
+    return !(e && strcmp(e, "bf16") == 0);
+}
 
 struct WsPtrs {
     int64_t *seq_tok;
@@ -2144,7 +2151,9 @@ template <bool BF, int K, int V, int CS>
 hipError_t state_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
     if constexpr (BF) {
         if (a.conv) return state_range_t<BF, K, V, CS, true, false>(a, w, g0, g1, first, st);
-        if constexpr (CS == 1) return state_range_t<BF, K, V, CS, false, true>(a, w, g0, g1, first, st);  // H16
+        if constexpr (CS == 1) {
+            if (use_h16(a.io_bf16, a.chunk, false)) return state_range_t<BF, K, V, CS, false, true>(a, w, g0, g1, first, st);
+        }
     }
     return state_range_t<BF, K, V, CS, false, false>(a, w, g0, g1, first, st);
 }
@@ -2158,9 +2167,8 @@ hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
 
 // Pipelined forward over nseg chunk ranges (16-token chunks): prep(0); then per range s the
 // combined kernel {state(s), prep(s+1)}; then state(last).
-template <bool BF, int K, int V>
+template <bool BF, int K, int V, bool H16>
 hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
-    constexpr bool H16 = BF;  // 16-token chunks, no convolution: bf16 I/O runs the fp16-operand variant
     using C = StateCfg<BF, K, V, 1, false, H16>;
     constexpr int PW = combined_prep_waves<BF, K, V, H16>();
     static_assert(PW >= 1, "no room for prep wavefronts");
@@ -2187,13 +2195,20 @@ hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
     return state_range<BF, K, V, 1>(a, w, g(nseg - 1), ALL_CHUNKS, nseg == 1, st);
 }
 
+template <bool BF, int K, bool H16>
+hipError_t fwd_pipelined_h(const PrefillArgs &a, int nseg, hipStream_t st) {
+    switch (a.V) {
+        case 32: return fwd_pipelined<BF, K, 32, H16>(a, nseg, st);
+        case 64: return fwd_pipelined<BF, K, 64, H16>(a, nseg, st);
+        default: return fwd_pipelined<BF, K, 128, H16>(a, nseg, st);
+    }
+}
 template <bool BF, int K>
 hipError_t fwd_pipelined_v(const PrefillArgs &a, int nseg, hipStream_t st) {
-    switch (a.V) {
-        case 32: return fwd_pipelined<BF, K, 32>(a, nseg, st);
-        case 64: return fwd_pipelined<BF, K, 64>(a, nseg, st);
-        default: return fwd_pipelined<BF, K, 128>(a, nseg, st);
+    if constexpr (BF) {
+        if (use_h16(a.io_bf16, a.chunk, a.conv != 0)) return fwd_pipelined_h<BF, K, true>(a, nseg, st);
     }
+    return fwd_pipelined_h<BF, K, false>(a, nseg, st);
 }
 
 template <bool BF, int K, int CS>

@@ -622,3 +622,53 @@ def test_conv_path_deterministic(chunk):
     for _ in range(3):
         o2, S2 = _run(inp, chunk=chunk)
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# ------------------------------------------------------------ operand formats at 16-token chunks
+#
+# bf16 I/O at 16-token chunks carries the state pass's operands in fp16 by default; KDA_OPERANDS=bf16
+# (read at every call and by the workspace query) selects the bf16 hi + lo operands instead.
+
+class _Operands:
+    """Sets KDA_OPERANDS for the duration of a block."""
+
+    def __init__(self, fmt):
+        self.fmt = fmt
+
+    def __enter__(self):
+        self.old = os.environ.get("KDA_OPERANDS")
+        os.environ["KDA_OPERANDS"] = self.fmt
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            del os.environ["KDA_OPERANDS"]
+        else:
+            os.environ["KDA_OPERANDS"] = self.old
+
+
+def test_bf16_pair_operands_k3_prefill_4k_all_heads():
+    """The bf16 hi + lo operand format (KDA_OPERANDS=bf16) on the 4096-token workload, every head, and
+    its workspace query (larger than the fp16 one)."""
+    from kda_gated_delta_chunk_amd import _lib
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("k3_prefill_4k_bf16_operands", seed=w.seed)
+    lib = _lib.load()
+    n16 = lib.kda_chunk_fwd_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, 1, 0)
+    with _Operands("bf16"):
+        nbf = lib.kda_chunk_fwd_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, 1, 0)
+        assert nbf > n16
+        inp = synth.workload_prefill_inputs(w, device=DEV)
+        _check(inp)
+
+
+def test_bf16_pair_operands_pipelined_and_split():
+    """KDA_OPERANDS=bf16 through the pipelined ranges (bit-identical to one range) and the split calls."""
+    _announce("bf16_operands_pipelined", seed=75)
+    inp = synth.prefill_inputs(1, 2500, 4, 128, 128, "bf16", seed=75, device=DEV, with_S0=True, with_o_gate=True)
+    with _Operands("bf16"):
+        with _Ranges(1):
+            o1, S1 = _run(inp)
+        with _Ranges(4):
+            o4, S4 = _run(inp)
+        assert torch.equal(o1, o4) and torch.equal(S1, S4)
+        _check(inp, heads=(0, 3))
