@@ -34,6 +34,14 @@
  *     and no output is written. A fault inside a kernel surfaces at the
  *     caller's next synchronisation of the stream.
  *   - Supported sizes: K, V in {32, 64, 128}; chunk in {16, 64}.
+ *   - Prefill with bf16 I/O at 16-token chunks (and no short convolution)
+ *     carries the state pass's operands in fp16, which is faster and at
+ *     least as accurate at the magnitudes of normalised activations, but
+ *     needs |v| and the state's entries well inside fp16's range (|x| < 6e4):
+ *     beyond it results are not finite. The environment variable
+ *     KDA_OPERANDS=bf16 (read at each call, and by the workspace query,
+ *     which must see the same setting) selects bf16 operands with bf16's
+ *     range instead.
  *   - The functions keep no state between calls and may be called from
  *     several host threads on different streams (calls that share output
  *     buffers or a workspace race).

@@ -41,11 +41,19 @@
 //                    never interact (decay scales rows only), so the column
 //                    split is exact.
 //
-// Precision (bf16 I/O): operands that feed an output directly (Q*Gamma,
-// K/Gamma in P, P itself and W) are carried as a bf16 hi + lo pair, giving
-// about 16 significant bits; K*Gamma, K*exp(b_C-b), T, Wk and the state
-// operand are single bf16. Accumulation and the state itself are fp32.
-// fp32 I/O runs the same code with fp32 operands on v_mfma_f32_16x16x4_f32.
+// Precision (bf16 I/O). Inside the prep, A and P take K/Gamma (up to e^80 at
+// 16 tokens) and so need bf16's range: Q*Gamma and K/Gamma there are bf16
+// hi + lo pairs, K*Gamma single bf16. The state pass's operands are all
+// bounded by |q|, |k|, |v| and |S|:
+//   16-token chunks (default): fp16 (11 significant bits). Q*Gamma,
+//     K*exp(b_C-b), T, Wk, the state operand and v single; P and, for the
+//     P W term only, W as fp16 hi + lo pairs (the term that decides o's
+//     error). Needs |v|, |S| well inside fp16's range; KDA_OPERANDS=bf16
+//     selects the bf16 format below instead.
+//   otherwise: Q*Gamma, P, W and K*exp(b_C-b) as bf16 hi + lo pairs (about
+//     16 significant bits), T, Wk and the state operand single bf16.
+// Accumulation and the state itself are fp32. fp32 I/O runs the same code
+// with fp32 operands on v_mfma_f32_16x16x4_f32.
 
 #include "kda_common.hpp"
 #include <type_traits>
