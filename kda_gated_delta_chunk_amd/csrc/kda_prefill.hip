@@ -85,11 +85,11 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 //   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
 //                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
 //                  columns 4a .. 4a+3
-// H16: the state pass's operands in fp16 (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b), T and
-// -Wk as singles, P as an fp16 hi + lo pair (P W, with W also split in registers, is the term that
-// decides the output's error; the state update takes W as one fp16). All are bounded by |q|, |k| and
-// the solve, so fp16's 11 significant bits replace the bf16 hi + lo pairs and bf16 singles in fewer
-// bytes.
+// H16: the state pass's operands in fp16 (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b), T, -Wk
+// and v (a bf16 input, exact in fp16) as singles, P as an fp16 hi + lo pair, and W (in registers) split
+// into an fp16 hi + lo pair for the two products it feeds: P W decides the output's error and the state
+// update S_final's. All are bounded by |q|, |k|, |v| and the solve, so fp16's 11 significant bits replace
+// the bf16 hi + lo pairs and bf16 singles in fewer bytes.
 template <bool BF, int K, int CS, bool H16 = false>
 struct SubLayout {
     static_assert(!H16 || (BF && CS == 1), "fp16 operands: bf16 I/O, 16-token chunks");
@@ -1772,8 +1772,8 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // multiplied by [Wh | Wh] and then by [Wl | Wl], the two products sum all four cross
         // terms. fp32: W kept whole ([W | 0]).
         Frag8<BF> whh[CT], wll[CT];
-        Frag4<true> w16[CT];  // H16: W rounded to fp16 (the state update's B operand); the output's P W
-                              // term takes W as an fp16 hi + lo pair (whh, wll), as it decides o's error
+        Frag8<true> wpair[CT];  // H16: [W_hi | W_lo] (fp16 hi + lo), against [Kp | Kp] in the state update;
+                                // the output's P W term takes the same split as [Wh | Wh] and [Wl | Wl]
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             if constexpr (H16) {
@@ -1781,7 +1781,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                 const f16x2_t a = __builtin_bit_cast(f16x2_t, h0), b = __builtin_bit_cast(f16x2_t, h1);
                 const uint32_t l0 = pack_h(W[ct][0] - (float)a[0], W[ct][1] - (float)a[1]);
                 const uint32_t l1 = pack_h(W[ct][2] - (float)b[0], W[ct][3] - (float)b[1]);
-                w16[ct].p[0] = h0; w16[ct].p[1] = h1;
+                wpair[ct].p[0] = h0; wpair[ct].p[1] = h1; wpair[ct].p[2] = l0; wpair[ct].p[3] = l1;
                 whh[ct].p[0] = h0; whh[ct].p[1] = h1; whh[ct].p[2] = h0; whh[ct].p[3] = h1;
                 wll[ct].p[0] = l0; wll[ct].p[1] = l1; wll[ct].p[2] = l0; wll[ct].p[3] = l1;
             } else if constexpr (BF) {
@@ -1830,7 +1830,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                         S[ct][rt][0] *= gm[0]; S[ct][rt][1] *= gm[1]; S[ct][rt][2] *= gm[2]; S[ct][rt][3] *= gm[3];
                     }
                     if constexpr (H16) {
-                        S[ct][rt] = mmah16(S[ct][rt], kp4[rt], w16[ct]);
+                        S[ct][rt] = mmah32(S[ct][rt], cat4(kp4[rt], kp4[rt]), wpair[ct]);
                     } else if constexpr (BF) {
                         S[ct][rt] = mma32(S[ct][rt], kp2[rt], whh[ct]);
                         S[ct][rt] = mma32(S[ct][rt], kp2[rt], wll[ct]);
