@@ -16,6 +16,9 @@ Distributions (the workloads of the spec configurations):
   S0    ~ N(0, 0.02^2) (standard deviation 0.02), fp32
   o_gate ~ N(0, 1) per (token, head, value channel), where asked for: the
           output gate's pre-activation
+  do    ~ N(0, 1) per (token, head, value channel): the gradient of a loss
+          with respect to o, for the backward pass
+  dS_final ~ N(0, 0.02^2), fp32: the gradient with respect to S_final
 All draws are fp32 and then rounded to the I/O dtype with round-to-nearest-
 even (torch ``.to``). Generation is block-seeded over tokens so a
 million-token batch never needs more than one block of fp32 temporaries; a
@@ -29,7 +32,8 @@ import numpy as np
 import torch
 
 # tensor ids used in the block seeds
-_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "lengths": 6, "o_gate": 7}
+_TID = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "S0": 5, "lengths": 6, "o_gate": 7, "do": 8,
+        "dS_final": 9}
 
 DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -156,6 +160,24 @@ def prefill_inputs(B: int, T: int, H: int, K: int, V: int, io: str = "bf16", see
     if with_S0:
         S0 = 0.02 * _randn((N, H, K, V), seed, "S0", 0, dev)
     return {"q": q, "k": k, "v": v, "g": g, "beta": beta, "S0": S0, "cu_seqlens": cu, "o_gate": og}
+
+
+def output_grads(B: int, T: int, H: int, V: int, io: str = "bf16", seed: int = 0, device="cpu",
+                 num_seqs: int = 0, K: int = 0, block_tokens: int = 65536):
+    """Gradients fed to a backward call: do [B,T,H,V] in the I/O dtype and, when
+    num_seqs and K are given, dS_final [num_seqs,H,K,V] fp32 (else None)."""
+    dt = DTYPES[io]
+    dev = torch.device(device)
+    do = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    flat = B * T
+    df = do.view(flat, H, V)
+    for blk in range((flat + block_tokens - 1) // block_tokens):
+        a, b = blk * block_tokens, min(flat, (blk + 1) * block_tokens)
+        df[a:b] = _randn((b - a, H, V), seed, "do", blk, dev).to(dt)
+    dsf = None
+    if num_seqs and K:
+        dsf = 0.02 * _randn((num_seqs, H, K, V), seed, "dS_final", 0, dev)
+    return do, dsf
 
 
 def workload_prefill_inputs(w: Workload, device="cpu", **kw):

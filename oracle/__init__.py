@@ -304,3 +304,6 @@ def parity_error(x, ref) -> float:
     if rms == 0.0:
         return diff
     return diff / rms
+
+
+from .backward import chunk_bwd  # noqa: E402  (gradients of chunk_fwd, fp64 numpy)

@@ -1,0 +1,109 @@
+"""Gradients of the KDA recurrence: plain fp64 reverse pass (numpy).
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: only the tests, the
+smoke check and the benchmark's CPU baseline leg may use it.
+
+What it differentiates is the per-token recurrence of the forward oracle
+("Kimi K3 发布核实与 Moonshot AI 主干架构演变", section 3, paragraph
+"KDA 为什么不同于 MLA": decay per channel, then the delta-rule correction,
+then the read of the updated state; the same paragraph names the chunked
+form as the way the layer is trained). Per sequence and head, with
+S in R^{K x V}:
+
+    A_t = diag(exp(g_t)) S_{t-1}          decayed state
+    d_t = v_t - A_t^T k_t                 delta-rule error
+    S_t = A_t + beta_t k_t d_t^T          corrected state
+    o_t = S_t^T q_t                       read
+
+The pages print no backward pass; the gradients below are the chain rule
+applied to those four lines, token by token in reverse order. With
+G = dL/dS_t (starting from dL/dS_final, or zero) and do_t = dL/do_t:
+
+    G     += q_t do_t^T                   (o_t reads S_t)
+    dq_t   = S_t do_t
+    w      = G^T k_t                      (V-vector)
+    dv_t   = beta_t w                     (d_t enters S_t as beta k d^T)
+    dbeta_t= w . d_t
+    dk_t   = beta_t G d_t - A_t dv_t      (k in beta k d^T, and in d = v - A^T k)
+    GA     = G - k_t dv_t^T               (dL/dA_t: A_t enters S_t and d_t)
+    dg_t   = rowsum(GA * A_t)             (A_t = diag(e^g) S_{t-1}, dA/dg_r = A_t[r, :])
+    G      = diag(exp(g_t)) GA            (dL/dS_{t-1})
+
+and dL/dS0 is the final G. The forward states A_t and d_t are kept from a
+plain forward run (no recomputation). Parity of this function is pinned
+against central finite differences of the C forward oracle, exact linearity
+in (v, S0) and in q, and a closed form at beta = 0, g = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _sequences(B, T, cu):
+    """(batch row, first token, end token) of every sequence."""
+    if cu is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in cu]
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must run from 0 to T, non-decreasing, with B = 1")
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None):
+    """Gradients of (o, S_final) = chunk_fwd(q, k, v, g, beta, S0, cu_seqlens).
+
+    q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; beta: [B, T, H];
+    S0, dS_final: [N, H, K, V] or None (zeros). g is the log-decay as given.
+    Returns a dict of float64 arrays: dq, dk, dg [B, T, H, K]; dv [B, T, H, V];
+    dbeta [B, T, H]; dS0 [N, H, K, V]. cu_seqlens, if given, runs from 0 to T.
+    """
+    q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent input shapes")
+    if cu_seqlens is not None and hasattr(cu_seqlens, "detach"):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    seqs = _sequences(B, T, cu_seqlens)
+    N = len(seqs)
+    s0 = None if S0 is None else _f64(S0)
+    dsf = None if dS_final is None else _f64(dS_final)
+    for x in (s0, dsf):
+        if x is not None and x.shape != (N, H, K, V):
+            raise ValueError("state shape %s != %s" % (x.shape, (N, H, K, V)))
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dg": np.zeros_like(g), "dv": np.zeros_like(v),
+           "dbeta": np.zeros_like(beta), "dS0": np.zeros((N, H, K, V))}
+    for n, (b, t0, t1) in enumerate(seqs):
+        for h in range(H):
+            S = np.zeros((K, V)) if s0 is None else s0[n, h].copy()
+            A_hist, d_hist = [], []
+            for t in range(t0, t1):                      # forward, keeping A_t and d_t
+                A = np.exp(g[b, t, h])[:, None] * S
+                d = v[b, t, h] - A.T @ k[b, t, h]
+                S = A + beta[b, t, h] * np.outer(k[b, t, h], d)
+                A_hist.append(A)
+                d_hist.append(d)
+            G = np.zeros((K, V)) if dsf is None else dsf[n, h].copy()
+            for t in range(t1 - 1, t0 - 1, -1):          # reverse
+                A, d = A_hist[t - t0], d_hist[t - t0]
+                kt, qt, bt, dot = k[b, t, h], q[b, t, h], beta[b, t, h], do[b, t, h]
+                St = A + bt * np.outer(kt, d)
+                G = G + np.outer(qt, dot)
+                out["dq"][b, t, h] = St @ dot
+                w = G.T @ kt
+                dv = bt * w
+                out["dv"][b, t, h] = dv
+                out["dbeta"][b, t, h] = w @ d
+                out["dk"][b, t, h] = bt * (G @ d) - A @ dv
+                GA = G - np.outer(kt, dv)
+                out["dg"][b, t, h] = np.sum(GA * A, axis=1)
+                G = np.exp(g[b, t, h])[:, None] * GA
+            out["dS0"][n, h] = G
+    return out
