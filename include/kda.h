@@ -258,6 +258,43 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                              kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv,
                              const float *conv_w, void *conv_cache, kda_dtype_t o_dtype, void *stream);
 
+/*
+ * Backward pass: the gradients of kda_chunk_fwd's (o, S_final) with respect to
+ * q, k, v, g, beta and S0, given dL/do and dL/dS_final. The first page cited
+ * above names this as the form the layer is trained in; the pages print no
+ * backward, so the gradients are the chain rule through the four steps above,
+ * token by token in reverse order (with G = dL/dS_t):
+ *   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = beta_t w;
+ *   dbeta_t = w . (v_t - u);  dk_t = beta_t G (v_t - u) - A_t dv_t;
+ *   dg_t = rowsum((G - k_t dv_t^T) * A_t);  G = diag(exp(g_t)) (G - k_t dv_t^T)
+ * where A_t = diag(exp(g_t)) S_{t-1} and u = A_t^T k_t; dL/dS0 is the last G.
+ *   q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]   dtype `io`, the
+ *           forward's inputs (g is the log-decay as given: no gate, norm or
+ *           convolution options here)
+ *   S0      [num_seqs, H, K, V] fp32 or NULL (zero), cu_seqlens as for
+ *           kda_chunk_fwd
+ *   d_o     [B, T, H, V] dtype `io`: dL/do
+ *   dS_final [num_seqs, H, K, V] fp32 or NULL (zero): dL/dS_final
+ *   dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]: fp32 outputs;
+ *           rows of tokens outside every sequence are not written
+ *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
+ *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs):
+ *           the state every 8 tokens of every sequence and head (K * V * 4
+ *           bytes each) plus per-16-column partial sums of dq, dk, dg and
+ *           dbeta (V / 16 * B * T * H * (3K + 1) * 4 bytes); 0 means the sizes
+ *           are invalid
+ * The forward states are recomputed from the inputs; nothing from a forward
+ * call is needed. All arithmetic is fp32, any finite g is accepted, and the
+ * result is deterministic (fixed summation order). Outputs may not alias the
+ * inputs or each other. Errors as for kda_chunk_fwd (chunk does not apply).
+ */
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs);
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
+                           int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import KDAError, KDA_DTYPE_BF16, KDA_DTYPE_FP32
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_bytes", "KDAError", "abi_version"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_bytes", "bwd_workspace_bytes", "KDAError",
+           "abi_version"]
 
 _DT = {torch.bfloat16: KDA_DTYPE_BF16, torch.float32: KDA_DTYPE_FP32}
 _NAME = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -38,6 +39,11 @@ def _io_code(dtype) -> int:
 def workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16") -> int:
     """Device workspace bytes kda_chunk_fwd needs (0 = unsupported sizes)."""
     return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io)))
+
+
+def bwd_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int) -> int:
+    """Device workspace bytes kda_chunk_bwd needs (0 = unsupported sizes)."""
+    return int(_lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs))
 
 
 def _ptr(t):
@@ -173,4 +179,51 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
                                  N, H, K, V, io, gc, _qk_code(qk_norm), cc, _ptr(conv_w) if cc else None,
                                  _ptr(conv_cache) if cc else None, _io_code(odt), _stream(dev))
     _lib.check(status, "kda_decode_step")
+    return out
+
+
+def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
+              workspace=None):
+    """Gradients of chunk_fwd's (o, S_final) (log-decay g, no options) given dL/do and dL/dS_final.
+
+    ``do`` has o's shape and the input dtype; ``dS_final`` is fp32 [num_seqs, H, K, V] or None (zero).
+    Returns a dict of fp32 tensors: dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]; and
+    dS0 [num_seqs, H, K, V] when ``want_dS0``. ``workspace`` (uint8 CUDA tensor) may be passed to avoid
+    the allocation.
+    """
+    lib = _lib.load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be CUDA (HIP) tensors")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    io = _io_code(dt)
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, V))):
+        _need(t, name, shp, dt, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None:
+            _need(t, name, (N, H, K, V), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
+           "dg": torch.empty((B, T, H, K), **f32), "dv": torch.empty((B, T, H, V), **f32),
+           "dbeta": torch.empty((B, T, H), **f32)}
+    if want_dS0:
+        out["dS0"] = torch.empty((N, H, K, V), **f32)
+    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N))
+    if need == 0:
+        raise KDAError(2, "kda_chunk_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(do),
+                           _ptr(dS_final), B, T, H, K, V, N, io, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(workspace),
+                           workspace.numel(), _stream(dev))
+    _lib.check(st, "kda_chunk_bwd")
     return out

@@ -22,9 +22,9 @@ CONVS = {"none": 0, "short4": 1, "short4_silu": 2}
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
           3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_NO_DEVICE", 5: "KDA_ERROR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-           "kda_chunk_prep", "kda_chunk_state", "kda_decode_step")
+           "kda_chunk_prep", "kda_chunk_state", "kda_decode_step", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 _lib = None
 
 
@@ -67,6 +67,11 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_int,
+                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 

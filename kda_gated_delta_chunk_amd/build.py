@@ -15,7 +15,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkda.so"
-SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_api.hip"]
+SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_backward.hip", "kda_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -61,7 +61,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 5; }
+int kda_abi_version(void) { return 6; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -216,6 +216,56 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     a.conv_w = conv == KDA_CONV_NONE ? nullptr : conv_w;
     a.conv_cache = conv == KDA_CONV_NONE ? nullptr : conv_cache;
     if (kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs) {
+    const bool packed = (B == 1);  // the packed bound is the larger for B == 1 and covers both
+    if (check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed) != KDA_SUCCESS) return 0;
+    const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
+    return kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs);
+}
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
+                           int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(io)) return KDA_ERROR_INVALID_VALUE;
+    const bool packed = cu_seqlens != nullptr;
+    kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed);
+    if (st != KDA_SUCCESS) return st;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERROR_INVALID_VALUE;
+    const void *ptrs[] = {q, k, v, g, d_o, S0, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
+    if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
+    // outputs may not alias the inputs or each other
+    const void *outs[] = {dq, dk, dv, dg, dbeta, dS0};
+    const void *ins[] = {q, k, v, g, beta, d_o, S0, dS_final, cu_seqlens};
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i]) continue;
+        for (const void *p : ins)
+            if (p == outs[i]) return KDA_ERROR_INVALID_VALUE;
+        for (int j = i + 1; j < 6; ++j)
+            if (outs[j] == outs[i]) return KDA_ERROR_INVALID_VALUE;
+    }
+    const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
+    const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs);
+    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    st = check_device();
+    if (st != KDA_SUCCESS) return st;
+    kda::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.cu_seqlens = cu_seqlens;
+    a.dout = d_o; a.dS_final = dS_final;
+    a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
+    a.io_bf16 = io == KDA_DTYPE_BF16;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    a.workspace = workspace;
+    a.max_segs = segs;
+    if (kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }
 

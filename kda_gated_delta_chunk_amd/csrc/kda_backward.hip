@@ -1,0 +1,398 @@
+// Backward pass of the KDA recurrence on gfx950: gradients of (o, S_final) with respect to q, k, v, g,
+// beta and S0, given dL/do and dL/dS_final.
+//
+// The forward is the per-token recurrence of "Kimi K3 发布核实与 Moonshot AI 主干架构演变" (section 3,
+// paragraph "KDA 为什么不同于 MLA": per-channel decay, delta-rule correction, read of the updated
+// state), per sequence and head with S in R^{K x V}:
+//   A_t = diag(e^{g_t}) S_{t-1};  d_t = v_t - A_t^T k_t;  S_t = A_t + beta_t k_t d_t^T;  o_t = S_t^T q_t.
+// Its reverse, token by token with G = dL/dS_t:
+//   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = beta_t w;  dbeta_t = w . d_t;
+//   dk_t = beta_t G d_t - A_t dv_t;  GA = G - k_t dv_t^T;  dg_t = rowsum(GA * A_t);  G = diag(e^{g_t}) GA,
+// and dL/dS0 is the last G.
+//
+// The value columns of S evolve independently (decay scales rows), and so do the columns of G, so one
+// workgroup owns (sequence, head, 16-column tile) and walks the sequence twice:
+//   1. forward over the whole sequence, storing S at the start of every 8-token segment (checkpoints);
+//   2. backward over the segments, last first: reload the segment's checkpoint, recompute its 8 states
+//      into registers, then run the reverse steps over them.
+// The column-local results (dv, and G itself) are final per workgroup; dq, dk, dg and dbeta sum over all
+// V columns, so each workgroup writes its tile's partial sums and kda_bwd_reduce adds the tiles in a
+// fixed order (deterministic, no atomics). All arithmetic is fp32.
+//
+// Thread layout (256 threads, 4 wavefronts): lane = 4*rg + c4; column j = 4*wave + c4 of the tile; the
+// thread holds rows rg*R .. rg*R + R-1 (R = K/16) of S and G for column j. Sums over the key rows run
+// over the 16 lanes of equal c4 (two row rotations by DPP, then two lane swaps across rows); sums over
+// the 4 columns of a wavefront use DPP quad permutes, then LDS across the 4 wavefronts.
+
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int BL = 8;     // tokens per checkpoint segment
+constexpr int BVT = 16;   // value columns per workgroup
+constexpr int BNT = 256;  // threads per workgroup
+
+// ------------------------------------------------------------------ sequence table
+// seq_tok[n] = first flat token of sequence n (cu_seqlens clamped into [0, total] and made
+// non-decreasing; n = 0..N, seq_tok[N] = end of the last sequence); seg_off[n] = index of the first
+// checkpoint segment of sequence n (seg_off[N] = total segments).
+__device__ int64_t bwd_scan(int64_t x, int64_t *sh, bool is_max) {
+    const int t = threadIdx.x, nt = blockDim.x;
+    sh[t] = x;
+    __syncthreads();
+    for (int d = 1; d < nt; d <<= 1) {
+        const int64_t y = (t >= d) ? sh[t - d] : (int64_t)0;
+        __syncthreads();
+        if (t >= d) sh[t] = is_max ? (y > sh[t] ? y : sh[t]) : sh[t] + y;
+        __syncthreads();
+    }
+    const int64_t r = (t > 0) ? sh[t - 1] : (int64_t)0;  // exclusive
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict__ cu, int32_t N, int64_t T_row,
+                                                       int64_t total, int64_t *__restrict__ seq_tok,
+                                                       int64_t *__restrict__ seg_off) {
+    __shared__ int64_t sh[1024];
+    const int t = threadIdx.x, nt = blockDim.x;
+    const int64_t M = (int64_t)N + 1;
+    const int64_t per = (M + nt - 1) / nt;
+    const int64_t lo = t * per, hi = (lo + per < M) ? lo + per : M;
+    auto start_of = [&](int64_t m) -> int64_t {
+        if (!cu) return m * T_row;
+        const int64_t s = cu[m];
+        return s < 0 ? 0 : (s > total ? total : s);
+    };
+    int64_t run = 0;
+    for (int64_t m = lo; m < hi; ++m) run = start_of(m) > run ? start_of(m) : run;
+    const int64_t base = bwd_scan(run, sh, true);
+    // prefix maxima of this thread's entries, and the segments of the sequences they start
+    int64_t cur = base, segs = 0;
+    for (int64_t m = lo; m < hi; ++m) {
+        cur = start_of(m) > cur ? start_of(m) : cur;
+        seq_tok[m] = cur;
+        if (m < N) {
+            const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
+            segs += (nx - cur + BL - 1) / BL;
+        }
+    }
+    const int64_t sbase = bwd_scan(segs, sh, false);
+    int64_t acc = sbase;
+    cur = base;
+    for (int64_t m = lo; m < hi; ++m) {
+        seg_off[m] = acc;
+        cur = start_of(m) > cur ? start_of(m) : cur;
+        if (m < N) {
+            const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
+            acc += (nx - cur + BL - 1) / BL;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ lane sums
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
+                                                                 false));
+}
+// Sum over the 16 lanes of equal (lane & 3): within a 16-lane row the four lanes 4 apart (row_ror:4,
+// row_ror:8), then across the four rows (lane xor 16, 32). Every lane gets the total.
+__device__ __forceinline__ float sum_rows(float x) {
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+// Sum over the 4 lanes of a quad (the wavefront's 4 columns): quad_perm [1,0,3,2] then [2,3,0,1].
+__device__ __forceinline__ float sum_quad(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    return x;
+}
+
+// ------------------------------------------------------------------ main kernel
+template <bool BF, int K>
+__global__ __launch_bounds__(BNT) void kda_bwd_kernel(
+    const typename IO<BF>::T *__restrict__ q, const typename IO<BF>::T *__restrict__ k,
+    const typename IO<BF>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
+    const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
+    const float *__restrict__ S0, const float *__restrict__ dSf, const int64_t *__restrict__ seq_tok,
+    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows,
+    float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dS0) {
+    using io = IO<BF>;
+    constexpr int R = K / 16;          // rows per thread
+    constexpr int F = 3 * K + 1;       // partial row: dq | dk | dg | dbeta
+    constexpr int NE = BL * K / BNT;   // staged q/k/g elements per thread
+    static_assert(NE >= 1 && NE * BNT == BL * K, "segment staging");
+    __shared__ float sq[BL * K], sk[BL * K], sa[BL * K];  // q, k, e^g of the segment's tokens
+    __shared__ float sv[BL * BVT], sdo[BL * BVT], sb[BL];
+    __shared__ float red[BL * 4 * F];  // per-wavefront column sums, [token][wave][F]
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int c4 = lane & 3, rg = lane >> 2;
+    int64_t bid = blockIdx.x;
+    const int vt = (int)(bid % nvt);
+    bid /= nvt;
+    const int h = (int)(bid % H);
+    const int64_t n = bid / H;
+    const int col = vt * BVT + wv * 4 + c4;
+    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1];
+    const int nseg = (int)((t1 - t0 + BL - 1) / BL);
+    const int64_t ck0 = seg_off[n];
+    const int64_t sH = (int64_t)H, sV = (int64_t)V;
+
+    // ---- segment staging: global -> registers (one segment ahead) -> LDS
+    float pq[NE], pk[NE], pg[NE], pvd = 0.f, pb = 0.f;
+    auto fetch = [&](int s, bool with_q) {
+        const int64_t ft0 = t0 + (int64_t)s * BL;
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + BNT * m, tok = e / K, r = e % K;
+            const int64_t ft = ft0 + tok;
+            const bool ok = ft < t1;
+            const int64_t idx = (ft * sH + h) * K + r;
+            pk[m] = ok ? io::ld(k, idx) : 0.f;
+            pg[m] = ok ? io::ld(g, idx) : 0.f;
+            pq[m] = (ok && with_q) ? io::ld(q, idx) : 0.f;
+        }
+        {
+            const int e = tid & (BL * BVT - 1), tok = e / BVT, c = e % BVT;
+            const int64_t ft = ft0 + tok;
+            const bool isv = tid < BL * BVT;
+            const bool ok = ft < t1 && (isv || with_q);
+            pvd = ok ? io::ld(isv ? v : dout, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
+        }
+        pb = (tid < BL && ft0 + tid < t1) ? io::ld(beta, (ft0 + tid) * sH + h) : 0.f;
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            const int e = tid + BNT * m;
+            sq[e] = pq[m];
+            sk[e] = pk[m];
+            sa[e] = exp_e(pg[m]);
+        }
+        if (tid < BL * BVT) sv[tid] = pvd;
+        else if (tid < 2 * BL * BVT) sdo[tid - BL * BVT] = pvd;
+        if (tid < BL) sb[tid] = pb;
+    };
+    // checkpoint s of this workgroup: [seg][h][vt][R][256], thread-private and coalesced
+    auto ck_ptr = [&](int s) { return ckpt + (((ck0 + s) * sH + h) * nvt + vt) * (int64_t)(R * BNT) + tid; };
+
+    // ---- 1. forward: checkpoints
+    float S[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        S[i] = S0 ? S0[((n * sH + h) * K + rg * R + i) * sV + col] : 0.f;
+    if (nseg > 0) fetch(0, false);
+    for (int s = 0; s < nseg; ++s) {
+        __syncthreads();
+        stage();
+        __syncthreads();
+        if (s + 1 < nseg) fetch(s + 1, false);
+        float *cp = ck_ptr(s);
+#pragma unroll
+        for (int i = 0; i < R; ++i) cp[i * BNT] = S[i];
+#pragma unroll
+        for (int tt = 0; tt < BL; ++tt) {
+            float u = 0.f, kk[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                kk[i] = sk[tt * K + rg * R + i];
+                S[i] *= sa[tt * K + rg * R + i];
+                u += S[i] * kk[i];
+            }
+            u = sum_rows(u);
+            const float bd = sb[tt] * (sv[tt * BVT + wv * 4 + c4] - u);
+#pragma unroll
+            for (int i = 0; i < R; ++i) S[i] += kk[i] * bd;
+        }
+    }
+
+    // ---- 2. backward over the segments
+    float G[R], C[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        G[i] = dSf ? dSf[((n * sH + h) * K + rg * R + i) * sV + col] : 0.f;
+    if (nseg > 0) {
+        fetch(nseg - 1, true);
+        const float *cp = ck_ptr(nseg - 1);
+#pragma unroll
+        for (int i = 0; i < R; ++i) C[i] = cp[i * BNT];
+    }
+    for (int s = nseg - 1; s >= 0; --s) {
+        __syncthreads();  // the previous segment's LDS reads (staging and red) are done
+        stage();
+        float X[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) X[i] = C[i];
+        __syncthreads();
+        if (s > 0) {
+            fetch(s - 1, true);
+            const float *cp = ck_ptr(s - 1);
+#pragma unroll
+            for (int i = 0; i < R; ++i) C[i] = cp[i * BNT];
+        }
+        // recompute the segment's decayed states A_t and errors d_t (registers)
+        float A[BL][R], d[BL];
+#pragma unroll
+        for (int tt = 0; tt < BL; ++tt) {
+            float u = 0.f;
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                X[i] *= sa[tt * K + rg * R + i];
+                A[tt][i] = X[i];
+                u += X[i] * sk[tt * K + rg * R + i];
+            }
+            u = sum_rows(u);
+            d[tt] = sv[tt * BVT + wv * 4 + c4] - u;
+            const float bd = sb[tt] * d[tt];
+#pragma unroll
+            for (int i = 0; i < R; ++i) X[i] += sk[tt * K + rg * R + i] * bd;
+        }
+        // reverse steps (tokens past the sequence end are identities and write nothing)
+        const int64_t ft0 = t0 + (int64_t)s * BL;
+#pragma unroll
+        for (int tt = BL - 1; tt >= 0; --tt) {
+            if (ft0 + tt >= t1) continue;
+            const float b = sb[tt], o = sdo[tt * BVT + wv * 4 + c4];
+            float w = 0.f, pdq[R], pdk[R], pdg[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float kk = sk[tt * K + rg * R + i];
+                G[i] += sq[tt * K + rg * R + i] * o;
+                pdq[i] = (A[tt][i] + b * kk * d[tt]) * o;  // S_t do_t
+                w += G[i] * kk;
+            }
+            w = sum_rows(w);
+            const float dv = b * w;
+            if (rg == 0) dv_out[((ft0 + tt) * sH + h) * sV + col] = dv;
+            float pbeta = w * d[tt];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float kk = sk[tt * K + rg * R + i];
+                pdk[i] = b * d[tt] * G[i] - A[tt][i] * dv;
+                const float ga = G[i] - kk * dv;
+                pdg[i] = ga * A[tt][i];
+                G[i] = sa[tt * K + rg * R + i] * ga;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                pdq[i] = sum_quad(pdq[i]);
+                pdk[i] = sum_quad(pdk[i]);
+                pdg[i] = sum_quad(pdg[i]);
+            }
+            pbeta = sum_quad(pbeta);
+            if (c4 == 0) {
+                float *rr = red + (tt * 4 + wv) * F;
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    rr[rg * R + i] = pdq[i];
+                    rr[K + rg * R + i] = pdk[i];
+                    rr[2 * K + rg * R + i] = pdg[i];
+                }
+                if (rg == 0) rr[3 * K] = pbeta;
+            }
+        }
+        __syncthreads();
+        // the tile's partial sums over its 16 columns: [vt][flat token][h][F]
+        for (int e = tid; e < BL * F; e += BNT) {
+            const int tt = e / F, f = e % F;
+            const int64_t ft = ft0 + tt;
+            if (ft < t1) {
+                const float* rr = red + tt * 4 * F + f;
+                part[((int64_t)vt * n_rows + ft * sH + h) * F + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
+            }
+        }
+    }
+    if (dS0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) dS0[((n * sH + h) * K + rg * R + i) * sV + col] = G[i];
+    }
+}
+
+// dq, dk, dg, dbeta of every covered (token, head): the tiles' partial sums added in tile order.
+template <int K>
+__global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ part, int32_t nvt, int64_t n_rows,
+                                                      int32_t H, const int64_t *__restrict__ seq_tok, int32_t N,
+                                                      float *__restrict__ dq, float *__restrict__ dk,
+                                                      float *__restrict__ dg, float *__restrict__ dbeta) {
+    constexpr int F = 3 * K + 1;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_rows * F) return;
+    const int64_t row = idx / F;
+    const int f = (int)(idx % F);
+    const int64_t ft = row / H;
+    if (ft < seq_tok[0] || ft >= seq_tok[N]) return;  // outside every sequence: not written
+    float acc = 0.f;
+    for (int t = 0; t < nvt; ++t) acc += part[((int64_t)t * n_rows + row) * F + f];
+    if (f < K) dq[row * K + f] = acc;
+    else if (f < 2 * K) dk[row * K + f - K] = acc;
+    else if (f < 3 * K) dg[row * K + f - 2 * K] = acc;
+    else dbeta[row] = acc;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdWs {
+    int64_t *seq_tok, *seg_off;
+    float *ckpt, *part;
+};
+
+BwdWs bwd_ptrs(void *ws, int32_t N, int64_t max_segs, int32_t H, int32_t K, int32_t V) {
+    char *p = (char *)ws;
+    BwdWs r;
+    r.seq_tok = (int64_t *)p;
+    p += align256(sizeof(int64_t) * ((size_t)N + 1));
+    r.seg_off = (int64_t *)p;
+    p += align256(sizeof(int64_t) * ((size_t)N + 1));
+    r.ckpt = (float *)p;
+    p += align256(sizeof(float) * (size_t)max_segs * H * K * V);
+    r.part = (float *)p;
+    return r;
+}
+
+template <bool BF, int K>
+hipError_t bwd_launch(const BackwardArgs &a, hipStream_t st) {
+    using T = typename IO<BF>::T;
+    const int nvt = a.V / BVT;
+    const int64_t n_rows = a.B * a.T * a.H;
+    BwdWs w = bwd_ptrs(a.workspace, a.num_seqs, a.max_segs, a.H, a.K, a.V);
+    const int64_t T_row = a.cu_seqlens ? 0 : a.T;
+    hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, a.B * a.T,
+                       w.seq_tok, w.seg_off);
+    const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
+    hipLaunchKernelGGL((kda_bwd_kernel<BF, K>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const T *)a.q,
+                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, (const T *)a.dout, a.S0,
+                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, w.ckpt, w.part, a.dv, a.dS0);
+    const int64_t nel = n_rows * (3 * K + 1);
+    if (nel > 0)
+        hipLaunchKernelGGL((kda_bwd_reduce<K>), dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, st, w.part, nvt,
+                           n_rows, a.H, w.seq_tok, a.num_seqs, a.dq, a.dk, a.dg, a.dbeta);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
+                                int32_t num_seqs) {
+    return 2 * align256(sizeof(int64_t) * ((size_t)num_seqs + 1)) +
+           align256(sizeof(float) * (size_t)max_segs * H * K * V) +
+           sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 1);
+}
+
+int32_t backward_segment_tokens() { return BL; }
+
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
+    switch (a.K) {
+        case 32: return a.io_bf16 ? bwd_launch<true, 32>(a, st) : bwd_launch<false, 32>(a, st);
+        case 64: return a.io_bf16 ? bwd_launch<true, 64>(a, st) : bwd_launch<false, 64>(a, st);
+        default: return a.io_bf16 ? bwd_launch<true, 128>(a, st) : bwd_launch<false, 128>(a, st);
+    }
+}
+
+}  // namespace kda

@@ -54,4 +54,24 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+struct BackwardArgs {
+    const void *q, *k, *v, *g, *beta;  // the forward's inputs (g: the log-decay)
+    const float *S0;                   // or null (zero)
+    const int32_t *cu_seqlens;         // or null
+    const void *dout;                  // dL/do [B,T,H,V], I/O dtype
+    const float *dS_final;             // dL/dS_final [num_seqs,H,K,V], or null (zero)
+    int64_t B, T;
+    int32_t H, K, V, num_seqs;
+    bool io_bf16;
+    float *dq, *dk, *dv, *dg, *dbeta;  // fp32 gradients
+    float *dS0;                        // or null
+    void *workspace;
+    int64_t max_segs;                  // upper bound on checkpoint segments over all sequences
+};
+// Tokens per checkpoint segment of the backward pass.
+int32_t backward_segment_tokens();
+size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
+                                int32_t num_seqs);
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
+
 }  // namespace kda

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 5
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 6
 
 
 def test_status_strings():
@@ -156,6 +156,51 @@ def test_decode_empty_batch_is_a_no_op():
     assert _dec(N=0, q=None, S=None) == 0
 
 
+def _bwd(**kw):
+    lib = _lib.load()
+    a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, S0=None, cu=None, do=A + 20480, dSf=None,
+             B=1, T=64, H=2, K=32, V=32, N=1, io=1, dq=A + 65536, dk=A + 2 * 65536, dv=A + 3 * 65536,
+             dg=A + 4 * 65536, db=A + 5 * 65536, dS0=A + 6 * 65536, ws=A + 8 * 65536, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["do"], a["dSf"], a["B"],
+                             a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["dq"], a["dk"], a["dv"], a["dg"],
+                             a["db"], a["dS0"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(do=None), INVALID),
+    (dict(dg=None), INVALID),
+    (dict(q=A + 8), INVALID),             # misaligned
+    (dict(dSf=A + 4), INVALID),
+    (dict(beta=A + 16385), INVALID),      # bf16 beta needs 2-byte alignment
+    (dict(cu=A + 2), INVALID),
+    (dict(dq=A), INVALID),                # an output aliases an input
+    (dict(dS0=A + 65536), INVALID),       # two outputs alias
+    (dict(B=2, N=2, cu=A + 7 * 65536), INVALID),
+    (dict(N=3), INVALID),
+    (dict(io=4), INVALID),
+    (dict(H=0), INVALID),
+    (dict(K=48), UNSUP),
+    (dict(V=256), UNSUP),
+    (dict(wsb=100), WS_SMALL),
+    (dict(ws=None), WS_SMALL),
+])
+def test_chunk_bwd_rejects(kw, expect):
+    assert _bwd(**kw) == expect
+
+
+def test_bwd_workspace_bytes():
+    lib = _lib.load()
+    ws = lib.kda_chunk_bwd_workspace_bytes
+    # per sequence and head: a K*V fp32 state every 8 tokens; per token and head: V/16 partial rows of 3K+1 floats
+    B, T, H, K, V = 2, 64, 3, 32, 64
+    states = B * (T // 8) * H * K * V * 4
+    parts = (V // 16) * B * T * H * (3 * K + 1) * 4
+    assert states + parts <= ws(B, T, H, K, V, B) <= states + parts + 3 * 256
+    assert ws(1, 4096, 96, 128, 128, 16) > ws(1, 4096, 96, 128, 128, 1)  # one more partial segment per sequence
+    assert ws(1, 64, 2, 48, 32, 1) == 0 and ws(2, 64, 2, 32, 32, 1) == 0
+
+
 def _has_gpu():
     try:
         import torch
@@ -168,3 +213,4 @@ def _has_gpu():
 def test_valid_arguments_without_a_device_report_no_device():
     assert _fwd() == NO_DEV
     assert _dec() == NO_DEV
+    assert _bwd() == NO_DEV
