@@ -21,8 +21,13 @@
 //
 // Thread layout (256 threads, 4 wavefronts): lane = 4*rg + c4; column j = 4*wave + c4 of the tile; the
 // thread holds rows rg*R .. rg*R + R-1 (R = K/16) of S and G for column j. Sums over the key rows run
-// over the 16 lanes of equal c4 (two row rotations by DPP, then two lane swaps across rows); sums over
+// over the 16 lanes of equal c4 (two row rotations by DPP, then two permlane swaps across rows); sums over
 // the 4 columns of a wavefront use DPP quad permutes, then LDS across the 4 wavefronts.
+//
+// Occupancy: the launch bounds ask for 3 wavefronts per SIMD (3 workgroups per CU), which the compiler
+// meets by spilling about 90 registers; that ran faster than 2 wavefronts without spills (15.7 vs 18.0 ms
+// at 4096 tokens, 96 heads), since the kernel is bound by fp32 vector instruction issue (about 225
+// instructions per wavefront and token across the three walks), not by memory.
 
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -33,6 +38,7 @@ namespace {
 constexpr int BL = 8;     // tokens per checkpoint segment
 constexpr int BVT = 16;   // value columns per workgroup
 constexpr int BNT = 256;  // threads per workgroup
+constexpr int RT = 4;     // tokens per flush of the column sums (LDS holds RT tokens' worth)
 
 // ------------------------------------------------------------------ sequence table
 // seq_tok[n] = first flat token of sequence n (cu_seqlens clamped into [0, total] and made
@@ -99,13 +105,17 @@ __device__ __forceinline__ float dpp_mov(float x) {
                                                                  false));
 }
 // Sum over the 16 lanes of equal (lane & 3): within a 16-lane row the four lanes 4 apart (row_ror:4,
-// row_ror:8), then across the four rows (lane xor 16, 32). Every lane gets the total.
+// row_ror:8), then across the four rows with gfx950's lane swaps, which stay in the vector ALU: a
+// permlane16 swap of x with itself returns x with rows (0,1) and (2,3) exchanged as its two results, so
+// their sum holds rows 0+1 and 2+3; a permlane32 swap does the same for the two halves. Every lane gets
+// the total.
 __device__ __forceinline__ float sum_rows(float x) {
     x += dpp_mov<0x124>(x);
     x += dpp_mov<0x128>(x);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 // Sum over the 4 lanes of a quad (the wavefront's 4 columns): quad_perm [1,0,3,2] then [2,3,0,1].
 __device__ __forceinline__ float sum_quad(float x) {
@@ -116,7 +126,7 @@ __device__ __forceinline__ float sum_quad(float x) {
 
 // ------------------------------------------------------------------ main kernel
 template <bool BF, int K>
-__global__ __launch_bounds__(BNT) void kda_bwd_kernel(
+__global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     const typename IO<BF>::T *__restrict__ q, const typename IO<BF>::T *__restrict__ k,
     const typename IO<BF>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
     const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(BNT) void kda_bwd_kernel(
     static_assert(NE >= 1 && NE * BNT == BL * K, "segment staging");
     __shared__ float sq[BL * K], sk[BL * K], sa[BL * K];  // q, k, e^g of the segment's tokens
     __shared__ float sv[BL * BVT], sdo[BL * BVT], sb[BL];
-    __shared__ float red[BL * 4 * F];  // per-wavefront column sums, [token][wave][F]
+    __shared__ float red[RT * 4 * F];  // per-wavefront column sums, [token % RT][wave][F]
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c4 = lane & 3, rg = lane >> 2;
@@ -254,59 +264,64 @@ __global__ __launch_bounds__(BNT) void kda_bwd_kernel(
 #pragma unroll
             for (int i = 0; i < R; ++i) X[i] += sk[tt * K + rg * R + i] * bd;
         }
-        // reverse steps (tokens past the sequence end are identities and write nothing)
+        // reverse steps (tokens past the sequence end are identities and write nothing); the column sums
+        // go to LDS and are flushed every RT tokens
         const int64_t ft0 = t0 + (int64_t)s * BL;
+        auto flush = [&](int base) {
+            __syncthreads();
+            for (int e = tid; e < RT * F; e += BNT) {
+                const int tt = e / F, f = e % F;
+                const int64_t ft = ft0 + base + tt;
+                if (ft < t1) {
+                    const float *rr = red + tt * 4 * F + f;
+                    part[((int64_t)vt * n_rows + ft * sH + h) * F + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
+                }
+            }
+            __syncthreads();
+        };
 #pragma unroll
         for (int tt = BL - 1; tt >= 0; --tt) {
-            if (ft0 + tt >= t1) continue;
-            const float b = sb[tt], o = sdo[tt * BVT + wv * 4 + c4];
-            float w = 0.f, pdq[R], pdk[R], pdg[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float kk = sk[tt * K + rg * R + i];
-                G[i] += sq[tt * K + rg * R + i] * o;
-                pdq[i] = (A[tt][i] + b * kk * d[tt]) * o;  // S_t do_t
-                w += G[i] * kk;
-            }
-            w = sum_rows(w);
-            const float dv = b * w;
-            if (rg == 0) dv_out[((ft0 + tt) * sH + h) * sV + col] = dv;
-            float pbeta = w * d[tt];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float kk = sk[tt * K + rg * R + i];
-                pdk[i] = b * d[tt] * G[i] - A[tt][i] * dv;
-                const float ga = G[i] - kk * dv;
-                pdg[i] = ga * A[tt][i];
-                G[i] = sa[tt * K + rg * R + i] * ga;
-            }
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                pdq[i] = sum_quad(pdq[i]);
-                pdk[i] = sum_quad(pdk[i]);
-                pdg[i] = sum_quad(pdg[i]);
-            }
-            pbeta = sum_quad(pbeta);
-            if (c4 == 0) {
-                float *rr = red + (tt * 4 + wv) * F;
+            if (ft0 + tt < t1) {
+                const float b = sb[tt], o = sdo[tt * BVT + wv * 4 + c4];
+                float w = 0.f, pdq[R], pdk[R], pdg[R];
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    rr[rg * R + i] = pdq[i];
-                    rr[K + rg * R + i] = pdk[i];
-                    rr[2 * K + rg * R + i] = pdg[i];
+                    const float kk = sk[tt * K + rg * R + i];
+                    G[i] += sq[tt * K + rg * R + i] * o;
+                    pdq[i] = (A[tt][i] + b * kk * d[tt]) * o;  // S_t do_t
+                    w += G[i] * kk;
                 }
-                if (rg == 0) rr[3 * K] = pbeta;
+                w = sum_rows(w);
+                const float dv = b * w;
+                if (rg == 0) dv_out[((ft0 + tt) * sH + h) * sV + col] = dv;
+                float pbeta = w * d[tt];
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float kk = sk[tt * K + rg * R + i];
+                    pdk[i] = b * d[tt] * G[i] - A[tt][i] * dv;
+                    const float ga = G[i] - kk * dv;
+                    pdg[i] = ga * A[tt][i];
+                    G[i] = sa[tt * K + rg * R + i] * ga;
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    pdq[i] = sum_quad(pdq[i]);
+                    pdk[i] = sum_quad(pdk[i]);
+                    pdg[i] = sum_quad(pdg[i]);
+                }
+                pbeta = sum_quad(pbeta);
+                if (c4 == 0) {
+                    float *rr = red + ((tt % RT) * 4 + wv) * F;
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        rr[rg * R + i] = pdq[i];
+                        rr[K + rg * R + i] = pdk[i];
+                        rr[2 * K + rg * R + i] = pdg[i];
+                    }
+                    if (rg == 0) rr[3 * K] = pbeta;
+                }
             }
-        }
-        __syncthreads();
-        // the tile's partial sums over its 16 columns: [vt][flat token][h][F]
-        for (int e = tid; e < BL * F; e += BNT) {
-            const int tt = e / F, f = e % F;
-            const int64_t ft = ft0 + tt;
-            if (ft < t1) {
-                const float* rr = red + tt * 4 * F + f;
-                part[((int64_t)vt * n_rows + ft * sH + h) * F + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
-            }
+            if (tt % RT == 0) flush(tt);
         }
     }
     if (dS0) {
