@@ -7,7 +7,9 @@ are seeded synthetic tensors already resident in HBM. `value` is prefill
 tokens/s at chunk 16; the same workload is also timed at chunk 64 and
 reported under "chunk64". The decode half of the metric (N=512 streams,
 H=96, fp32 state of ~3.2 GB updated in place, 100 consecutive steps) is
-timed after the prefill steps and reported under "decode".
+timed after the prefill steps and reported under "decode". The backward pass
+(kda_chunk_bwd) on the prefill workload's inputs is timed last and reported
+under "backward", against the fp32 vector peak (it runs on the vector ALUs).
 
 Kernel durations come from HIP events recorded on the stream the kernels run
 on, around each phase of every timed step. Roofline figures use algorithmic
@@ -29,6 +31,7 @@ from kda_gated_delta_chunk_amd.source_hash import csrc_hash
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix, TFLOP/s
+FP32_VECTOR_PEAK_TFS = 157.3    # MI355X fp32 vector, TFLOP/s
 SIMDS = 256 * 4                 # MI355X: 256 compute units of 4 SIMDs (one matrix core each)
 CLOCK_HZ = 2.4e9                # peak engine clock
 
@@ -142,6 +145,47 @@ def time_decode(w, steps, dev, gate="log_decay", qk_norm=False):
             "bytes_per_step": bytes_step, "N": N, "H": H}
 
 
+def backward_flops(T, H, K, V):
+    """Flops of the per-token backward per call: one forward recompute (decay, read, write: 5KV) plus the
+    reverse step (G += q do^T, S_t do, G^T k, beta G d - A dv, G - k dv^T, rowsum(GA * A), decay: 19KV)."""
+    return 24 * K * V * T * H
+
+
+def time_backward(w, steps, warmup, dev):
+    """kda_chunk_bwd on the prefill workload's inputs, dL/do ~ N(0, 1), no dL/dS_final."""
+    lib = _lib.load()
+    inp = synth.workload_prefill_inputs(w, device=dev)
+    B, T, H, K = inp["q"].shape
+    V = inp["v"].shape[-1]
+    do, _ = synth.output_grads(B, T, H, V, w.io, w.seed, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = [torch.empty((B, T, H, K), **f32) for _ in range(3)] + [torch.empty((B, T, H, V), **f32),
+                                                                    torch.empty((B, T, H), **f32)]
+    dq, dk, dg, dv, db = (t.data_ptr() for t in outs)
+    dS0 = torch.empty((B, H, K, V), **f32)
+    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
+
+    def bwd():
+        _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, do.data_ptr(), None,
+                                     B, T, H, K, V, B, 1, dq, dk, dv, dg, db, dS0.data_ptr(), ws.data_ptr(), wsb,
+                                     stream.cuda_stream), "kda_chunk_bwd")
+
+    for _ in range(warmup):
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        bwd()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    return {"B": B, "T": T, "H": H, "K": K, "V": V, "ms": ms, "ws_bytes": wsb}
+
+
 def measured_counter(kernel_prefix, field="traffic_bytes"):
     """A per-launch counter figure of a kernel from the committed counter summary
     (profiles/traffic.json): HBM bytes ("traffic_bytes") or matrix-core busy cycles summed over
@@ -252,6 +296,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short pass for hardware-counter runs: a 1 GiB device copy (calibration of the byte "
                          "counters), then the prefill and decode steps, no CPU baseline")
@@ -392,6 +437,20 @@ def main():
         out["decode"]["gate_fused_ms_per_step"] = dg["ms_per_step"]
         dn = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid", qk_norm=True)
         out["decode"]["gate_and_qk_norm_fused_ms_per_step"] = dn["ms_per_step"]
+    if not args.no_backward:
+        print("[bench] backward %s: warmup 3, steps 10" % w.name, file=sys.stderr, flush=True)
+        rb = time_backward(w, 10, 3, dev)
+        fl = backward_flops(rb["T"], rb["H"], rb["K"], rb["V"])
+        tfs = fl / (rb["ms"] * 1e-3) / 1e12
+        out["backward"] = {
+            "workload": "kda_chunk_bwd on the prefill inputs (B=1 T=4096 H=96 K=V=128 bf16 in, fp32 gradients, "
+                        "dL/do ~ N(0,1), no dL/dS_final)",
+            "ms_per_step": rb["ms"], "tokens_per_s": rb["B"] * rb["T"] / (rb["ms"] * 1e-3),
+            "workspace_bytes": rb["ws_bytes"],
+            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd (checkpoint walk, reverse walk, tile sum)",
+                         "achieved": tfs, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_VECTOR_PEAK_TFS, "algorithmic_flops_per_call": fl,
+                         "timed": "whole call (3 launches)"}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -1,17 +1,21 @@
-"""Content hash of the HIP sources, used to tie stored hardware-counter figures
-to the exact kernels they were measured on."""
+"""Content hash of the HIP sources of the prefill and decode kernels, used to tie
+stored hardware-counter figures (HBM traffic, matrix-core cycles of those
+kernels) to the exact code they were measured on. The C ABI glue and the
+backward kernels do not enter it: they do not change the code of the kernels
+the figures describe."""
 import hashlib
 from pathlib import Path
 
 CSRC = Path(__file__).resolve().parent / "csrc"
+KERNEL_SOURCES = ("kda_common.hpp", "kda_decode.hip", "kda_prefill.hip")
 
 
 def csrc_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(CSRC.glob("*")):
-        if p.suffix in (".hip", ".hpp", ".h"):
-            h.update(p.name.encode())
-            h.update(p.read_bytes())
+    for name in KERNEL_SOURCES:
+        p = CSRC / name
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
     return h.hexdigest()[:16]
 
 
