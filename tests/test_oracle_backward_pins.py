@@ -108,3 +108,73 @@ def test_bwd_closed_form_no_write_no_decay():
         np.testing.assert_allclose(gr["dbeta"][0, :, h], dbeta, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(gr["dg"][0, :, h], np.sum(G * S0[None], axis=2), rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(gr["dS0"][0, h], G[0], rtol=1e-12, atol=1e-12)
+
+
+def _planted(kind):
+    """oracle.chunk_bwd with one plausible mistake planted in its reverse step (CPU only)."""
+    import oracle.backward as ob
+
+    def bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None):
+        q, k, v, g, beta, do = (ob._f64(x) for x in (q, k, v, g, beta, do))
+        B, T, H, K = q.shape
+        V = v.shape[-1]
+        out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dg": np.zeros_like(g), "dv": np.zeros_like(v),
+               "dbeta": np.zeros_like(beta), "dS0": np.zeros((B, H, K, V))}
+        for b in range(B):
+            for h in range(H):
+                S = ob._f64(S0)[b, h].copy()
+                As, ds = [], []
+                for t in range(T):
+                    A = np.exp(g[b, t, h])[:, None] * S
+                    d = v[b, t, h] - A.T @ k[b, t, h]
+                    S = A + beta[b, t, h] * np.outer(k[b, t, h], d)
+                    As.append(A)
+                    ds.append(d)
+                G = ob._f64(dS_final)[b, h].copy()
+                for t in range(T - 1, -1, -1):
+                    A, d, kt, qt, bt, dot = As[t], ds[t], k[b, t, h], q[b, t, h], beta[b, t, h], do[b, t, h]
+                    St = A + bt * np.outer(kt, d)
+                    if kind != "qdo_late":
+                        G = G + np.outer(qt, dot)
+                    out["dq"][b, t, h] = (A if kind == "dq_old_state" else St) @ dot
+                    w = G.T @ kt
+                    dv = bt * w
+                    out["dv"][b, t, h] = dv
+                    out["dbeta"][b, t, h] = w @ (v[b, t, h] if kind == "dbeta_uses_v" else d)
+                    dk = bt * (G @ d) - (0 if kind == "dk_drops_read" else A @ dv)
+                    out["dk"][b, t, h] = -dk if kind == "dk_sign" else dk
+                    GA = G - (0 if kind == "GA_drops_write" else np.outer(kt, dv))
+                    out["dg"][b, t, h] = np.sum((G if kind == "dg_uses_G" else GA) * A, axis=1)
+                    G = (GA if kind == "no_decay" else np.exp(g[b, t, h])[:, None] * GA)
+                    if kind == "qdo_late":  # q_t do_t^T added after the step's own transform
+                        G = G + np.outer(qt, dot)
+                out["dS0"][b, h] = G
+        return out
+    return bwd
+
+
+@pytest.mark.parametrize("kind", ["dq_old_state", "qdo_late", "dbeta_uses_v", "dk_drops_read", "dk_sign",
+                                  "GA_drops_write", "dg_uses_G", "no_decay"])
+def test_planted_backward_mistakes_fail_the_finite_difference_pin(kind):
+    # each mistake must move at least one gradient well away from the central differences of the C forward
+    rng = np.random.default_rng(21)
+    B, T, H, K, V = 1, 6, 1, 3, 2
+    x, do, dsf = _inputs(rng, B, T, H, K, V)
+    ok = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf)
+    bad = _planted(kind)(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf)
+    names = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "S0": "dS0"}
+    worst = 0.0
+    for name, gname in names.items():
+        fd = np.zeros_like(x[name])
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 1e-6
+            lp = _loss(x, do, dsf, None)
+            flat[i] = old - 1e-6
+            lm = _loss(x, do, dsf, None)
+            flat[i] = old
+            fd.reshape(-1)[i] = (lp - lm) / 2e-6
+        assert np.max(np.abs(fd - ok[gname])) < 1e-6 * max(1.0, np.max(np.abs(fd)))
+        worst = max(worst, np.max(np.abs(fd - bad[gname])) / max(1.0, np.max(np.abs(fd))))
+    assert worst > 1e-3, (kind, worst)
