@@ -99,10 +99,12 @@ __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict_
 }
 
 // ------------------------------------------------------------------ lane sums
+// (every control used here has a source lane for every lane; bound_ctrl set lets the compiler fold the
+// move into the consuming add)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
-                                                                 false));
+                                                                 true));
 }
 // Sum over the 16 lanes of equal (lane & 3): within a 16-lane row the four lanes 4 apart (row_ror:4,
 // row_ror:8), then across the four rows with gfx950's lane swaps, which stay in the vector ALU: a
@@ -310,7 +312,10 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
                     pdg[i] = sum_quad(pdg[i]);
                 }
                 pbeta = sum_quad(pbeta);
-                if (c4 == 0) {
+                // the 4 lanes of a quad hold equal sums and every lane of the wavefront the same pbeta, so
+                // all lanes store (equal values to equal addresses): no divergent branch, which lets the
+                // quad sums' DPP moves fuse into their adds
+                {
                     float *rr = red + ((tt % RT) * 4 + wv) * F;
 #pragma unroll
                     for (int i = 0; i < R; ++i) {
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
                         rr[K + rg * R + i] = pdk[i];
                         rr[2 * K + rg * R + i] = pdg[i];
                     }
-                    if (rg == 0) rr[3 * K] = pbeta;
+                    rr[3 * K] = pbeta;
                 }
             }
             if (tt % RT == 0) flush(tt);
