@@ -25,9 +25,8 @@
 // the 4 columns of a wavefront use DPP quad permutes, then LDS across the 4 wavefronts.
 //
 // Occupancy: the launch bounds ask for 3 wavefronts per SIMD (3 workgroups per CU), which the compiler
-// meets by spilling about 90 registers; that ran faster than 2 wavefronts without spills (15.7 vs 18.0 ms
-// at 4096 tokens, 96 heads), since the kernel is bound by fp32 vector instruction issue (about 225
-// instructions per wavefront and token across the three walks), not by memory.
+// meets by spilling 16 registers; the kernel is bound by instruction issue (about 530 instructions per
+// wavefront and token across the three walks), not by memory, so resident wavefronts matter more.
 
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
