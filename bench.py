@@ -170,7 +170,7 @@ def time_backward(w, steps, warmup, dev):
 
     def bwd():
         _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, do.data_ptr(), None,
-                                     B, T, H, K, V, B, 1, dq, dk, dv, dg, db, dS0.data_ptr(), ws.data_ptr(), wsb,
+                                     B, T, H, K, V, B, 1, 0, dq, dk, dv, dg, db, dS0.data_ptr(), ws.data_ptr(), wsb,
                                      stream.cuda_stream), "kda_chunk_bwd")
 
     for _ in range(warmup):

@@ -269,14 +269,17 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   dg_t = rowsum((G - k_t dv_t^T) * A_t);  G = diag(exp(g_t)) (G - k_t dv_t^T)
  * where A_t = diag(exp(g_t)) S_{t-1} and u = A_t^T k_t; dL/dS0 is the last G.
  *   q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]   dtype `io`, the
- *           forward's inputs (g is the log-decay as given: no gate, norm or
- *           convolution options here)
+ *           forward's inputs; g as `gate` says, as for kda_chunk_fwd (no
+ *           norm, convolution or output-gate options here)
  *   S0      [num_seqs, H, K, V] fp32 or NULL (zero), cu_seqlens as for
  *           kda_chunk_fwd
  *   d_o     [B, T, H, V] dtype `io`: dL/do
  *   dS_final [num_seqs, H, K, V] fp32 or NULL (zero): dL/dS_final
  *   dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]: fp32 outputs;
- *           rows of tokens outside every sequence are not written
+ *           dg is the gradient with respect to g as given: the log-decay, or
+ *           with KDA_GATE_SCALED_SIGMOID the pre-activation x (dL/dx =
+ *           dL/dlogdecay * -5 sigmoid(x) (1 - sigmoid(x))); rows of tokens
+ *           outside every sequence are not written
  *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs):
  *           the state every 8 tokens of every sequence and head (K * V * 4
@@ -292,8 +295,8 @@ size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
-                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
-                           size_t workspace_bytes, void *stream);
+                           kda_gate_t gate, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

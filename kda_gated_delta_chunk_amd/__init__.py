@@ -183,8 +183,10 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
 
 
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
-              workspace=None):
-    """Gradients of chunk_fwd's (o, S_final) (log-decay g, no options) given dL/do and dL/dS_final.
+              workspace=None, gate: str = "log_decay"):
+    """Gradients of chunk_fwd's (o, S_final) (no norm, convolution or output-gate options) given dL/do and
+    dL/dS_final. ``gate`` says what ``g`` holds, as for chunk_fwd; dg is the gradient with respect to g as given
+    (the log-decay, or the gate pre-activation).
 
     ``do`` has o's shape and the input dtype; ``dS_final`` is fp32 [num_seqs, H, K, V] or None (zero).
     Returns a dict of fp32 tensors: dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]; and
@@ -199,6 +201,7 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
     V = v.shape[-1]
     dt = q.dtype
     io = _io_code(dt)
+    gc = _gate_code(gate)
     for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
                          ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
@@ -222,7 +225,7 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(do),
-                           _ptr(dS_final), B, T, H, K, V, N, io, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(dS_final), B, T, H, K, V, N, io, gc, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(workspace),
                            workspace.numel(), _stream(dev))
     _lib.check(st, "kda_chunk_bwd")

@@ -61,7 +61,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 6; }
+int kda_abi_version(void) { return 7; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -229,9 +229,9 @@ size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
-                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
-                           size_t workspace_bytes, void *stream) {
-    if (!valid_dtype(io)) return KDA_ERROR_INVALID_VALUE;
+                           kda_gate_t gate, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (!valid_dtype(io) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed);
     if (st != KDA_SUCCESS) return st;
@@ -252,6 +252,8 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
         for (int j = i + 1; j < 6; ++j)
             if (outs[j] == outs[i]) return KDA_ERROR_INVALID_VALUE;
     }
+    // the tile-sum reduce runs one thread per (token, head, partial slot): its grid must stay launchable
+    if ((B * T * H * (3 * (int64_t)K + 1) + 255) / 256 >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
     const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
@@ -262,6 +264,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     a.dout = d_o; a.dS_final = dS_final;
     a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
     a.io_bf16 = io == KDA_DTYPE_BF16;
+    a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
     a.workspace = workspace;
     a.max_segs = segs;

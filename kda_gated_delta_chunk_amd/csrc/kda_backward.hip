@@ -132,7 +132,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     const typename IO<BF>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
     const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
     const float *__restrict__ S0, const float *__restrict__ dSf, const int64_t *__restrict__ seq_tok,
-    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows,
+    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows, bool gate_sig,
     float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dS0) {
     using io = IO<BF>;
     constexpr int R = K / 16;          // rows per thread
@@ -185,7 +185,8 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
             const int e = tid + BNT * m;
             sq[e] = pq[m];
             sk[e] = pk[m];
-            sa[e] = exp_e(pg[m]);
+            // the retention e^g, with g the log-decay as given or -5 sigmoid(x) formed here
+            sa[e] = gate_sig ? __builtin_amdgcn_exp2f(gate_log2_decay(pg[m])) : exp_e(pg[m]);
         }
         if (tid < BL * BVT) sv[tid] = pvd;
         else if (tid < 2 * BL * BVT) sdo[tid - BL * BVT] = pvd;
@@ -334,10 +335,13 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     }
 }
 
-// dq, dk, dg, dbeta of every covered (token, head): the tiles' partial sums added in tile order.
-template <int K>
+// dq, dk, dg, dbeta of every covered (token, head): the tiles' partial sums added in tile order. With the
+// scaled-sigmoid gate, g holds the pre-activation x and the log-decay gradient is carried through
+// d(-5 sigmoid(x))/dx = -5 sigmoid(x) (1 - sigmoid(x)).
+template <bool BF, int K>
 __global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ part, int32_t nvt, int64_t n_rows,
                                                       int32_t H, const int64_t *__restrict__ seq_tok, int32_t N,
+                                                      const typename IO<BF>::T *__restrict__ g, bool gate_sig,
                                                       float *__restrict__ dq, float *__restrict__ dk,
                                                       float *__restrict__ dg, float *__restrict__ dbeta) {
     constexpr int F = 3 * K + 1;
@@ -351,7 +355,13 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ 
     for (int t = 0; t < nvt; ++t) acc += part[((int64_t)t * n_rows + row) * F + f];
     if (f < K) dq[row * K + f] = acc;
     else if (f < 2 * K) dk[row * K + f - K] = acc;
-    else if (f < 3 * K) dg[row * K + f - 2 * K] = acc;
+    else if (f < 3 * K) {
+        if (gate_sig) {
+            const float sx = sigmoid_f(IO<BF>::ld(g, row * K + f - 2 * K));
+            acc *= -5.f * sx * (1.f - sx);
+        }
+        dg[row * K + f - 2 * K] = acc;
+    }
     else dbeta[row] = acc;
 }
 
@@ -387,11 +397,12 @@ hipError_t bwd_launch(const BackwardArgs &a, hipStream_t st) {
     const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
     hipLaunchKernelGGL((kda_bwd_kernel<BF, K>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const T *)a.q,
                        (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, (const T *)a.dout, a.S0,
-                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, w.ckpt, w.part, a.dv, a.dS0);
+                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, a.gate_sigmoid, w.ckpt, w.part, a.dv, a.dS0);
     const int64_t nel = n_rows * (3 * K + 1);
     if (nel > 0)
-        hipLaunchKernelGGL((kda_bwd_reduce<K>), dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, st, w.part, nvt,
-                           n_rows, a.H, w.seq_tok, a.num_seqs, a.dq, a.dk, a.dg, a.dbeta);
+        hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, st, w.part,
+                           nvt, n_rows, a.H, w.seq_tok, a.num_seqs, (const T *)a.g, a.gate_sigmoid, a.dq, a.dk,
+                           a.dg, a.dbeta);
     return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 struct BackwardArgs {
-    const void *q, *k, *v, *g, *beta;  // the forward's inputs (g: the log-decay)
+    const void *q, *k, *v, *g, *beta;  // the forward's inputs
     const float *S0;                   // or null (zero)
     const int32_t *cu_seqlens;         // or null
     const void *dout;                  // dL/do [B,T,H,V], I/O dtype
@@ -63,6 +63,7 @@ struct BackwardArgs {
     int64_t B, T;
     int32_t H, K, V, num_seqs;
     bool io_bf16;
+    bool gate_sigmoid;                 // g holds the gate pre-activation x (log-decay -5 sigmoid(x)); dg is dL/dx
     float *dq, *dk, *dv, *dg, *dbeta;  // fp32 gradients
     float *dS0;                        // or null
     void *workspace;

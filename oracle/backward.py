@@ -29,7 +29,10 @@ G = dL/dS_t (starting from dL/dS_final, or zero) and do_t = dL/do_t:
     dg_t   = rowsum(GA * A_t)             (A_t = diag(e^g) S_{t-1}, dA/dg_r = A_t[r, :])
     G      = diag(exp(g_t)) GA            (dL/dS_{t-1})
 
-and dL/dS0 is the final G. The forward states A_t and d_t are kept from a
+and dL/dS0 is the final G. With the scaled-sigmoid gate ("Kimi K3 发布核实与 Moonshot AI 主干架构演变",
+section 3, paragraph "K3 对 Kimi Linear 的进一步修改": the log-decay is a sigmoid scaled to a lower bound
+of -5) g holds the pre-activation x, the log-decay is -5 sigmoid(x), and its gradient is carried to x by
+the derivative -5 sigmoid(x) (1 - sigmoid(x)). The forward states A_t and d_t are kept from a
 plain forward run (no recomputation). Parity of this function is pinned
 against central finite differences of the C forward oracle, exact linearity
 in (v, S0) and in q, and a closed form at beta = 0, g = 0.
@@ -55,15 +58,22 @@ def _sequences(B, T, cu):
     return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
 
 
-def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None):
+def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gate: str = "log_decay"):
     """Gradients of (o, S_final) = chunk_fwd(q, k, v, g, beta, S0, cu_seqlens).
 
     q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; beta: [B, T, H];
-    S0, dS_final: [N, H, K, V] or None (zeros). g is the log-decay as given.
+    S0, dS_final: [N, H, K, V] or None (zeros). gate: "log_decay" (g is the log-decay) or "scaled_sigmoid"
+    (g is the gate pre-activation x; the returned dg is then dL/dx).
     Returns a dict of float64 arrays: dq, dk, dg [B, T, H, K]; dv [B, T, H, V];
     dbeta [B, T, H]; dS0 [N, H, K, V]. cu_seqlens, if given, runs from 0 to T.
     """
     q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    if gate not in ("log_decay", "scaled_sigmoid"):
+        raise ValueError("unknown gate %r" % (gate,))
+    x_pre = None
+    if gate == "scaled_sigmoid":
+        from . import scaled_sigmoid_gate
+        x_pre, g = g, scaled_sigmoid_gate(g)
     B, T, H, K = q.shape
     V = v.shape[-1]
     if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape \
@@ -106,4 +116,7 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None):
                 out["dg"][b, t, h] = np.sum(GA * A, axis=1)
                 G = np.exp(g[b, t, h])[:, None] * GA
             out["dS0"][n, h] = G
+    if x_pre is not None:
+        sx = 1.0 / (1.0 + np.exp(-x_pre))
+        out["dg"] = out["dg"] * (-5.0 * sx * (1.0 - sx))
     return out

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 6
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 7
 
 
 def test_status_strings():
@@ -159,11 +159,11 @@ def test_decode_empty_batch_is_a_no_op():
 def _bwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, S0=None, cu=None, do=A + 20480, dSf=None,
-             B=1, T=64, H=2, K=32, V=32, N=1, io=1, dq=A + 65536, dk=A + 2 * 65536, dv=A + 3 * 65536,
+             B=1, T=64, H=2, K=32, V=32, N=1, io=1, gate=0, dq=A + 65536, dk=A + 2 * 65536, dv=A + 3 * 65536,
              dg=A + 4 * 65536, db=A + 5 * 65536, dS0=A + 6 * 65536, ws=A + 8 * 65536, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["do"], a["dSf"], a["B"],
-                             a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["dq"], a["dk"], a["dv"], a["dg"],
+                             a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["gate"], a["dq"], a["dk"], a["dv"], a["dg"],
                              a["db"], a["dS0"], a["ws"], a["wsb"], a["stream"])
 
 
@@ -179,7 +179,9 @@ def _bwd(**kw):
     (dict(B=2, N=2, cu=A + 7 * 65536), INVALID),
     (dict(N=3), INVALID),
     (dict(io=4), INVALID),
+    (dict(gate=2), INVALID),
     (dict(H=0), INVALID),
+    (dict(T=1 << 26, H=96), INVALID),    # the tile-sum grid would not be launchable
     (dict(K=48), UNSUP),
     (dict(V=256), UNSUP),
     (dict(wsb=100), WS_SMALL),

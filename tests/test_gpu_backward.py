@@ -33,7 +33,8 @@ def _inputs(B, T, H, K, V, io, seed, cu=None, with_S0=True, with_dsf=True, **kw)
 
 def _gpu(inp, want_dS0=True):
     out = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
-                    dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0)
+                    dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0,
+                    gate=inp.get("gate", "log_decay"))
     torch.cuda.synchronize()
     return out
 
@@ -49,7 +50,8 @@ def _oracle(inp, heads=None):
         dsf = None if dsf is None else dsf[:, hs]
     cu = inp["cu_seqlens"]
     return oracle.chunk_bwd(*(x.cpu() for x in xs), S0=None if S0 is None else S0.cpu(),
-                            dS_final=None if dsf is None else dsf.cpu(), cu_seqlens=None if cu is None else cu.cpu())
+                            dS_final=None if dsf is None else dsf.cpu(), cu_seqlens=None if cu is None else cu.cpu(),
+                            gate=inp.get("gate", "log_decay"))
 
 
 def _compare(out, ref, heads=None, tol=TOL_FP32):
@@ -131,3 +133,12 @@ def test_bwd_4k_workload_sampled_heads():
         assert torch.isfinite(out[n]).all(), n
     heads = (0, 95)
     _compare(out, _oracle(inp, heads), heads)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_bwd_gate_preactivation(io):
+    # g holds the gate pre-activation x ~ 2 N(0, 1); the kernels form -5 sigmoid(x) and return dL/dx
+    _announce("bwd_gate", io=io, T=70, H=3, K=128, V=64, seed=77)
+    inp = _inputs(1, 70, 3, 128, 64, io, 77, gate_preact=True, g_scale=2.0)
+    inp["gate"] = "scaled_sigmoid"
+    _compare(_gpu(inp), _oracle(inp))

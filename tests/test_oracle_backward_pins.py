@@ -178,3 +178,32 @@ def test_planted_backward_mistakes_fail_the_finite_difference_pin(kind):
         assert np.max(np.abs(fd - ok[gname])) < 1e-6 * max(1.0, np.max(np.abs(fd)))
         worst = max(worst, np.max(np.abs(fd - bad[gname])) / max(1.0, np.max(np.abs(fd))))
     assert worst > 1e-3, (kind, worst)
+
+
+def test_bwd_gate_preactivation_matches_finite_differences():
+    # g holds the gate pre-activation x (log-decay -5 sigmoid(x)); dg must be dL/dx of the forward oracle run
+    # with the same gate switch
+    rng = np.random.default_rng(31)
+    B, T, H, K, V = 1, 7, 2, 3, 2
+    x, do, dsf = _inputs(rng, B, T, H, K, V)
+    x["g"] = 2.0 * rng.standard_normal((B, T, H, K))
+    gr = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf, gate="scaled_sigmoid")
+
+    def loss():
+        o, sf = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gate="scaled_sigmoid")
+        return float(np.sum(o * do) + np.sum(sf * dsf))
+    fd = np.zeros_like(x["g"])
+    flat = x["g"].reshape(-1)
+    for i in range(flat.size):
+        old = flat[i]
+        flat[i] = old + 1e-6
+        lp = loss()
+        flat[i] = old - 1e-6
+        lm = loss()
+        flat[i] = old
+        fd.reshape(-1)[i] = (lp - lm) / 2e-6
+    assert np.max(np.abs(fd - gr["dg"])) < 1e-7 * max(1.0, np.max(np.abs(fd)))
+    # the other gradients are those of the log-decay form at g = -5 sigmoid(x)
+    ref = oracle.chunk_bwd(x["q"], x["k"], x["v"], oracle.scaled_sigmoid_gate(x["g"]), x["beta"], do, x["S0"], dsf)
+    for n in ("dq", "dk", "dv", "dbeta", "dS0"):
+        assert np.array_equal(gr[n], ref[n]), n
