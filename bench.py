@@ -169,8 +169,9 @@ def time_backward(w, steps, warmup, dev):
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def bwd():
-        _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, do.data_ptr(), None,
-                                     B, T, H, K, V, B, 1, 0, dq, dk, dv, dg, db, dS0.data_ptr(), ws.data_ptr(), wsb,
+        _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, None, do.data_ptr(),
+                                     None, B, T, H, K, V, B, 1, 0, dq, dk, dv, dg, db, None, dS0.data_ptr(),
+                                     ws.data_ptr(), wsb,
                                      stream.cuda_stream), "kda_chunk_bwd")
 
     for _ in range(warmup):

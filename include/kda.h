@@ -270,7 +270,10 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  * where A_t = diag(exp(g_t)) S_{t-1} and u = A_t^T k_t; dL/dS0 is the last G.
  *   q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]   dtype `io`, the
  *           forward's inputs; g as `gate` says, as for kda_chunk_fwd (no
- *           norm, convolution or output-gate options here)
+ *           norm or convolution options here)
+ *   o_gate  [B, T, H, V] dtype `io` or NULL: the output gate's pre-activation
+ *           z of the forward (o = core output * sigmoid(z)); with it, d_o is
+ *           taken through the gate and d_o_gate receives dL/dz
  *   S0      [num_seqs, H, K, V] fp32 or NULL (zero), cu_seqlens as for
  *           kda_chunk_fwd
  *   d_o     [B, T, H, V] dtype `io`: dL/do
@@ -280,6 +283,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *           with KDA_GATE_SCALED_SIGMOID the pre-activation x (dL/dx =
  *           dL/dlogdecay * -5 sigmoid(x) (1 - sigmoid(x))); rows of tokens
  *           outside every sequence are not written
+ *   d_o_gate [B, T, H, V] fp32: dL/dz, required with o_gate (else ignored)
  *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs):
  *           the state every 8 tokens of every sequence and head (K * V * 4
@@ -293,10 +297,11 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  */
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs);
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                           const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
-                           int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
-                           kda_gate_t gate, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
-                           void *workspace, size_t workspace_bytes, void *stream);
+                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
+                           const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, float *dq, float *dk, float *dv,
+                           float *dg, float *dbeta, float *d_o_gate, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -183,10 +183,11 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
 
 
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
-              workspace=None, gate: str = "log_decay"):
-    """Gradients of chunk_fwd's (o, S_final) (no norm, convolution or output-gate options) given dL/do and
-    dL/dS_final. ``gate`` says what ``g`` holds, as for chunk_fwd; dg is the gradient with respect to g as given
-    (the log-decay, or the gate pre-activation).
+              workspace=None, gate: str = "log_decay", o_gate=None):
+    """Gradients of chunk_fwd's (o, S_final) (no norm or convolution options) given dL/do and dL/dS_final.
+    ``gate`` says what ``g`` holds, as for chunk_fwd; dg is the gradient with respect to g as given (the
+    log-decay, or the gate pre-activation). With ``o_gate`` (the forward's output-gate pre-activation z), ``do``
+    is the gradient of the gated output and the result also holds ``do_gate`` = dL/dz [B, T, H, V] fp32.
 
     ``do`` has o's shape and the input dtype; ``dS_final`` is fp32 [num_seqs, H, K, V] or None (zero).
     Returns a dict of fp32 tensors: dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]; and
@@ -205,6 +206,8 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
     for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
                          ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
+    if o_gate is not None:
+        _need(o_gate, "o_gate", (B, T, H, V), dt, dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
         N = cu_seqlens.numel() - 1
@@ -219,14 +222,18 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
            "dbeta": torch.empty((B, T, H), **f32)}
     if want_dS0:
         out["dS0"] = torch.empty((N, H, K, V), **f32)
+    if o_gate is not None:
+        out["do_gate"] = torch.empty((B, T, H, V), **f32)
     need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N))
     if need == 0:
         raise KDAError(2, "kda_chunk_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(do),
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0), _ptr(cu_seqlens),
+                           _ptr(do),
                            _ptr(dS_final), B, T, H, K, V, N, io, gc, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(workspace),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("do_gate")), _ptr(out.get("dS0")),
+                           _ptr(workspace),
                            workspace.numel(), _stream(dev))
     _lib.check(st, "kda_chunk_bwd")
     return out

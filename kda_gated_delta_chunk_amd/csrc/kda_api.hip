@@ -61,7 +61,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 7; }
+int kda_abi_version(void) { return 8; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -227,29 +227,31 @@ size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
 }
 
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                           const float *S0, const int32_t *cu_seqlens, const void *d_o, const float *dS_final,
-                           int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, kda_dtype_t io,
-                           kda_gate_t gate, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
+                           const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, float *dq, float *dk, float *dv,
+                           float *dg, float *dbeta, float *d_o_gate, float *dS0, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     if (!valid_dtype(io) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed);
     if (st != KDA_SUCCESS) return st;
     if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
         return KDA_ERROR_INVALID_VALUE;
-    const void *ptrs[] = {q, k, v, g, d_o, S0, dS_final, dq, dk, dv, dg, dbeta, dS0, workspace};
+    if (T > 0 && o_gate && !d_o_gate) return KDA_ERROR_INVALID_VALUE;  // an output gate needs its gradient
+    const void *ptrs[] = {q, k, v, g, o_gate, d_o, S0, dS_final, dq, dk, dv, dg, dbeta, d_o_gate, dS0, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
     if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     // outputs may not alias the inputs or each other
-    const void *outs[] = {dq, dk, dv, dg, dbeta, dS0};
-    const void *ins[] = {q, k, v, g, beta, d_o, S0, dS_final, cu_seqlens};
-    for (int i = 0; i < 6; ++i) {
+    const void *outs[] = {dq, dk, dv, dg, dbeta, o_gate ? d_o_gate : nullptr, dS0};
+    const void *ins[] = {q, k, v, g, beta, o_gate, d_o, S0, dS_final, cu_seqlens};
+    for (int i = 0; i < 7; ++i) {
         if (!outs[i]) continue;
         for (const void *p : ins)
             if (p == outs[i]) return KDA_ERROR_INVALID_VALUE;
-        for (int j = i + 1; j < 6; ++j)
+        for (int j = i + 1; j < 7; ++j)
             if (outs[j] == outs[i]) return KDA_ERROR_INVALID_VALUE;
     }
     // the tile-sum reduce runs one thread per (token, head, partial slot): its grid must stay launchable
@@ -262,6 +264,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     kda::BackwardArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.cu_seqlens = cu_seqlens;
     a.dout = d_o; a.dS_final = dS_final;
+    a.o_gate = o_gate; a.d_o_gate = o_gate ? d_o_gate : nullptr;
     a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;

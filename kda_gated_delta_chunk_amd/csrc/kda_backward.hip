@@ -5,6 +5,8 @@
 // paragraph "KDA 为什么不同于 MLA": per-channel decay, delta-rule correction, read of the updated
 // state), per sequence and head with S in R^{K x V}:
 //   A_t = diag(e^{g_t}) S_{t-1};  d_t = v_t - A_t^T k_t;  S_t = A_t + beta_t k_t d_t^T;  o_t = S_t^T q_t.
+// With an output gate o_t * sigmoid(z_t) on the forward's output, do_t below is the gated dL/do times
+// sigmoid(z_t), and dL/dz_t = dL/do * o_t * sigmoid(z_t) (1 - sigmoid(z_t)) with o_t the core output.
 // Its reverse, token by token with G = dL/dS_t:
 //   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = beta_t w;  dbeta_t = w . d_t;
 //   dk_t = beta_t G d_t - A_t dv_t;  GA = G - k_t dv_t^T;  dg_t = rowsum(GA * A_t);  G = diag(e^{g_t}) GA,
@@ -131,16 +133,18 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     const typename IO<BF>::T *__restrict__ q, const typename IO<BF>::T *__restrict__ k,
     const typename IO<BF>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
     const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
-    const float *__restrict__ S0, const float *__restrict__ dSf, const int64_t *__restrict__ seq_tok,
-    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows, bool gate_sig,
-    float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dS0) {
+    const typename IO<BF>::T *__restrict__ zg, const float *__restrict__ S0, const float *__restrict__ dSf,
+    const int64_t *__restrict__ seq_tok,    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows, bool gate_sig,
+    float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dz_out,
+    float *__restrict__ dS0) {
     using io = IO<BF>;
     constexpr int R = K / 16;          // rows per thread
     constexpr int F = 3 * K + 1;       // partial row: dq | dk | dg | dbeta
     constexpr int NE = BL * K / BNT;   // staged q/k/g elements per thread
     static_assert(NE >= 1 && NE * BNT == BL * K, "segment staging");
     __shared__ float sq[BL * K], sk[BL * K], sa[BL * K];  // q, k, e^g of the segment's tokens
-    __shared__ float sv[BL * BVT], sdo[BL * BVT], sb[BL];
+    // sdo: dL/do, times sigmoid(z) with an output gate; sdz: dL/do * sigmoid'(z)
+    __shared__ float sv[BL * BVT], sdo[BL * BVT], sdz[BL * BVT], sb[BL];
     __shared__ float red[RT * 4 * F];  // per-wavefront column sums, [token % RT][wave][F]
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     const int64_t sH = (int64_t)H, sV = (int64_t)V;
 
     // ---- segment staging: global -> registers (one segment ahead) -> LDS
-    float pq[NE], pk[NE], pg[NE], pvd = 0.f, pb = 0.f;
+    float pq[NE], pk[NE], pg[NE], pvd = 0.f, pz = 0.f, pb = 0.f;
     auto fetch = [&](int s, bool with_q) {
         const int64_t ft0 = t0 + (int64_t)s * BL;
 #pragma unroll
@@ -176,6 +180,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
             const bool isv = tid < BL * BVT;
             const bool ok = ft < t1 && (isv || with_q);
             pvd = ok ? io::ld(isv ? v : dout, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
+            pz = (ok && !isv && zg) ? io::ld(zg, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
         }
         pb = (tid < BL && ft0 + tid < t1) ? io::ld(beta, (ft0 + tid) * sH + h) : 0.f;
     };
@@ -188,8 +193,15 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
             // the retention e^g, with g the log-decay as given or -5 sigmoid(x) formed here
             sa[e] = gate_sig ? __builtin_amdgcn_exp2f(gate_log2_decay(pg[m])) : exp_e(pg[m]);
         }
-        if (tid < BL * BVT) sv[tid] = pvd;
-        else if (tid < 2 * BL * BVT) sdo[tid - BL * BVT] = pvd;
+        if (tid < BL * BVT) {
+            sv[tid] = pvd;
+        } else if (tid < 2 * BL * BVT) {
+            // the output gate o * sigmoid(z): the core output's gradient is do * sigmoid(z), and z's is
+            // do * o * sigmoid(z) (1 - sigmoid(z))
+            const float sz = zg ? sigmoid_f(pz) : 1.f;
+            sdo[tid - BL * BVT] = pvd * sz;
+            sdz[tid - BL * BVT] = pvd * sz * (1.f - sz);
+        }
         if (tid < BL) sb[tid] = pb;
     };
     // checkpoint s of this workgroup: [seg][h][vt][R][256], thread-private and coalesced
@@ -285,15 +297,21 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
         for (int tt = BL - 1; tt >= 0; --tt) {
             if (ft0 + tt < t1) {
                 const float b = sb[tt], o = sdo[tt * BVT + wv * 4 + c4];
-                float w = 0.f, pdq[R], pdk[R], pdg[R];
+                float w = 0.f, oc = 0.f, pdq[R], pdk[R], pdg[R];
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const float kk = sk[tt * K + rg * R + i];
-                    G[i] += sq[tt * K + rg * R + i] * o;
-                    pdq[i] = (A[tt][i] + b * kk * d[tt]) * o;  // S_t do_t
+                    const float kk = sk[tt * K + rg * R + i], qq = sq[tt * K + rg * R + i];
+                    const float st = A[tt][i] + b * kk * d[tt];  // S_t
+                    G[i] += qq * o;
+                    pdq[i] = st * o;  // S_t do_t
+                    oc += st * qq;    // the core output o_t = S_t^T q_t (used with an output gate)
                     w += G[i] * kk;
                 }
                 w = sum_rows(w);
+                if (zg) {
+                    oc = sum_rows(oc);
+                    if (rg == 0) dz_out[((ft0 + tt) * sH + h) * sV + col] = oc * sdz[tt * BVT + wv * 4 + c4];
+                }
                 const float dv = b * w;
                 if (rg == 0) dv_out[((ft0 + tt) * sH + h) * sV + col] = dv;
                 float pbeta = w * d[tt];
@@ -396,8 +414,8 @@ hipError_t bwd_launch(const BackwardArgs &a, hipStream_t st) {
                        w.seq_tok, w.seg_off);
     const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
     hipLaunchKernelGGL((kda_bwd_kernel<BF, K>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const T *)a.q,
-                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, (const T *)a.dout, a.S0,
-                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, a.gate_sigmoid, w.ckpt, w.part, a.dv, a.dS0);
+                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, (const T *)a.dout, (const T *)a.o_gate, a.S0,
+                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, a.gate_sigmoid, w.ckpt, w.part, a.dv, a.d_o_gate, a.dS0);
     const int64_t nel = n_rows * (3 * K + 1);
     if (nel > 0)
         hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, st, w.part,

@@ -59,12 +59,14 @@ struct BackwardArgs {
     const float *S0;                   // or null (zero)
     const int32_t *cu_seqlens;         // or null
     const void *dout;                  // dL/do [B,T,H,V], I/O dtype
+    const void *o_gate;                // output-gate pre-activation z [B,T,H,V], I/O dtype, or null
     const float *dS_final;             // dL/dS_final [num_seqs,H,K,V], or null (zero)
     int64_t B, T;
     int32_t H, K, V, num_seqs;
     bool io_bf16;
     bool gate_sigmoid;                 // g holds the gate pre-activation x (log-decay -5 sigmoid(x)); dg is dL/dx
     float *dq, *dk, *dv, *dg, *dbeta;  // fp32 gradients
+    float *d_o_gate;                   // dL/dz [B,T,H,V] fp32 (required with o_gate)
     float *dS0;                        // or null
     void *workspace;
     int64_t max_segs;                  // upper bound on checkpoint segments over all sequences

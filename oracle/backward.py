@@ -32,7 +32,10 @@ G = dL/dS_t (starting from dL/dS_final, or zero) and do_t = dL/do_t:
 and dL/dS0 is the final G. With the scaled-sigmoid gate ("Kimi K3 发布核实与 Moonshot AI 主干架构演变",
 section 3, paragraph "K3 对 Kimi Linear 的进一步修改": the log-decay is a sigmoid scaled to a lower bound
 of -5) g holds the pre-activation x, the log-decay is -5 sigmoid(x), and its gradient is carried to x by
-the derivative -5 sigmoid(x) (1 - sigmoid(x)). The forward states A_t and d_t are kept from a
+the derivative -5 sigmoid(x) (1 - sigmoid(x)). With the output gate (same paragraph: an input-dependent,
+full-rank channel gate on the output, read as o_t * sigmoid(z_t)), the reverse pass takes
+do_t * sigmoid(z_t) as the core output's gradient, and dL/dz_t = do_t * o_t * sigmoid(z_t) (1 - sigmoid(z_t))
+with o_t = S_t^T q_t the core output. The forward states A_t and d_t are kept from a
 plain forward run (no recomputation). Parity of this function is pinned
 against central finite differences of the C forward oracle, exact linearity
 in (v, S0) and in q, and a closed form at beta = 0, g = 0.
@@ -58,12 +61,15 @@ def _sequences(B, T, cu):
     return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
 
 
-def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gate: str = "log_decay"):
+def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gate: str = "log_decay",
+              o_gate=None):
     """Gradients of (o, S_final) = chunk_fwd(q, k, v, g, beta, S0, cu_seqlens).
 
     q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; beta: [B, T, H];
     S0, dS_final: [N, H, K, V] or None (zeros). gate: "log_decay" (g is the log-decay) or "scaled_sigmoid"
-    (g is the gate pre-activation x; the returned dg is then dL/dx).
+    (g is the gate pre-activation x; the returned dg is then dL/dx). o_gate: the output gate's pre-activation
+    z [B, T, H, V] or None; with it, do is the gradient of the gated output and the result also holds
+    "do_gate" = dL/dz.
     Returns a dict of float64 arrays: dq, dk, dg [B, T, H, K]; dv [B, T, H, V];
     dbeta [B, T, H]; dS0 [N, H, K, V]. cu_seqlens, if given, runs from 0 to T.
     """
@@ -76,6 +82,12 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
         x_pre, g = g, scaled_sigmoid_gate(g)
     B, T, H, K = q.shape
     V = v.shape[-1]
+    z = None if o_gate is None else _f64(o_gate)
+    if z is not None:
+        if z.shape != (B, T, H, V):
+            raise ValueError("o_gate shape %s != %s" % (z.shape, (B, T, H, V)))
+        sz = 1.0 / (1.0 + np.exp(-z))
+        do_raw, do = do, do * sz
     if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape \
             or beta.shape != (B, T, H):
         raise ValueError("inconsistent input shapes")
@@ -90,6 +102,8 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
             raise ValueError("state shape %s != %s" % (x.shape, (N, H, K, V)))
     out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dg": np.zeros_like(g), "dv": np.zeros_like(v),
            "dbeta": np.zeros_like(beta), "dS0": np.zeros((N, H, K, V))}
+    if z is not None:
+        out["do_gate"] = np.zeros_like(v)
     for n, (b, t0, t1) in enumerate(seqs):
         for h in range(H):
             S = np.zeros((K, V)) if s0 is None else s0[n, h].copy()
@@ -105,6 +119,9 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
                 A, d = A_hist[t - t0], d_hist[t - t0]
                 kt, qt, bt, dot = k[b, t, h], q[b, t, h], beta[b, t, h], do[b, t, h]
                 St = A + bt * np.outer(kt, d)
+                if z is not None:
+                    s_ = sz[b, t, h]
+                    out["do_gate"][b, t, h] = do_raw[b, t, h] * (St.T @ qt) * s_ * (1.0 - s_)
                 G = G + np.outer(qt, dot)
                 out["dq"][b, t, h] = St @ dot
                 w = G.T @ kt

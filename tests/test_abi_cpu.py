@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 7
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 8
 
 
 def test_status_strings():
@@ -158,13 +158,14 @@ def test_decode_empty_batch_is_a_no_op():
 
 def _bwd(**kw):
     lib = _lib.load()
-    a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, S0=None, cu=None, do=A + 20480, dSf=None,
+    a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, og=None, S0=None, cu=None, do=A + 20480,
+             dSf=None, dog=A + 7 * 65536 + 4096,
              B=1, T=64, H=2, K=32, V=32, N=1, io=1, gate=0, dq=A + 65536, dk=A + 2 * 65536, dv=A + 3 * 65536,
              dg=A + 4 * 65536, db=A + 5 * 65536, dS0=A + 6 * 65536, ws=A + 8 * 65536, wsb=1 << 40, stream=None)
     a.update(kw)
-    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["do"], a["dSf"], a["B"],
-                             a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["gate"], a["dq"], a["dk"], a["dv"], a["dg"],
-                             a["db"], a["dS0"], a["ws"], a["wsb"], a["stream"])
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["do"], a["dSf"],
+                             a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["gate"], a["dq"], a["dk"],
+                             a["dv"], a["dg"], a["db"], a["dog"], a["dS0"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -180,6 +181,9 @@ def _bwd(**kw):
     (dict(N=3), INVALID),
     (dict(io=4), INVALID),
     (dict(gate=2), INVALID),
+    (dict(og=A + 7 * 65536 + 8192, dog=None), INVALID),   # an output gate needs its gradient
+    (dict(og=A + 7 * 65536 + 8192, dog=A), INVALID),      # dL/dz aliases q
+    (dict(og=A + 7 * 65536 + 8200), INVALID),             # o_gate misaligned
     (dict(H=0), INVALID),
     (dict(T=1 << 26, H=96), INVALID),    # the tile-sum grid would not be launchable
     (dict(K=48), UNSUP),

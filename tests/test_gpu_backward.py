@@ -15,7 +15,7 @@ from tests.parity import TOL_FP32, err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "do_gate")
 
 
 def _announce(name, **kw):
@@ -34,7 +34,7 @@ def _inputs(B, T, H, K, V, io, seed, cu=None, with_S0=True, with_dsf=True, **kw)
 def _gpu(inp, want_dS0=True):
     out = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
                     dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0,
-                    gate=inp.get("gate", "log_decay"))
+                    gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"))
     torch.cuda.synchronize()
     return out
 
@@ -42,6 +42,9 @@ def _gpu(inp, want_dS0=True):
 def _oracle(inp, heads=None):
     names = ("q", "k", "v", "g", "beta", "do")
     xs = [inp[n] for n in names]
+    z = inp.get("o_gate")
+    if z is not None and heads is not None:
+        z = z[:, :, list(heads)]
     S0, dsf = inp["S0"], inp["dS_final"]
     if heads is not None:
         hs = list(heads)
@@ -51,7 +54,7 @@ def _oracle(inp, heads=None):
     cu = inp["cu_seqlens"]
     return oracle.chunk_bwd(*(x.cpu() for x in xs), S0=None if S0 is None else S0.cpu(),
                             dS_final=None if dsf is None else dsf.cpu(), cu_seqlens=None if cu is None else cu.cpu(),
-                            gate=inp.get("gate", "log_decay"))
+                            gate=inp.get("gate", "log_decay"), o_gate=None if z is None else z.cpu())
 
 
 def _compare(out, ref, heads=None, tol=TOL_FP32):
@@ -62,6 +65,7 @@ def _compare(out, ref, heads=None, tol=TOL_FP32):
         x = out[n]
         if heads is not None:
             x = x[:, :, list(heads)] if n != "dS0" else x[:, list(heads)]
+        assert n in ref, n
         errs[n] = err(x, ref[n])
     print("  errors " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
     for n, e in errs.items():
@@ -120,7 +124,7 @@ def test_bwd_is_deterministic():
     _announce("bwd_determinism", T=200, H=4, K=128, V=128, seed=76)
     inp = _inputs(1, 200, 4, 128, 128, "bf16", 76)
     a, b = _gpu(inp), _gpu(inp)
-    for n in NAMES:
+    for n in a:
         assert torch.equal(a[n], b[n]), n
 
 
@@ -129,7 +133,7 @@ def test_bwd_4k_workload_sampled_heads():
     _announce("bwd_4k", T=4096, H=96, K=128, V=128, io="bf16", seed=1001)
     inp = _inputs(1, 4096, 96, 128, 128, "bf16", 1001, with_S0=False)
     out = _gpu(inp)
-    for n in NAMES:
+    for n in out:
         assert torch.isfinite(out[n]).all(), n
     heads = (0, 95)
     _compare(out, _oracle(inp, heads), heads)
@@ -142,3 +146,14 @@ def test_bwd_gate_preactivation(io):
     inp = _inputs(1, 70, 3, 128, 64, io, 77, gate_preact=True, g_scale=2.0)
     inp["gate"] = "scaled_sigmoid"
     _compare(_gpu(inp), _oracle(inp))
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_bwd_output_gate_and_gate_preactivation(io):
+    # both gates of the forward: g is the pre-activation x, and o = core output * sigmoid(z); dL/dz is returned
+    _announce("bwd_gates", io=io, T=53, H=2, K=64, V=128, seed=78)
+    inp = _inputs(1, 53, 2, 64, 128, io, 78, gate_preact=True, with_o_gate=True)
+    inp["gate"] = "scaled_sigmoid"
+    out = _gpu(inp)
+    assert "do_gate" in out
+    _compare(out, _oracle(inp))

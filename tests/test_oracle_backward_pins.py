@@ -207,3 +207,30 @@ def test_bwd_gate_preactivation_matches_finite_differences():
     ref = oracle.chunk_bwd(x["q"], x["k"], x["v"], oracle.scaled_sigmoid_gate(x["g"]), x["beta"], do, x["S0"], dsf)
     for n in ("dq", "dk", "dv", "dbeta", "dS0"):
         assert np.array_equal(gr[n], ref[n]), n
+
+
+def test_bwd_output_gate_matches_finite_differences():
+    # o = core output * sigmoid(z): dL/dz, and the other gradients taken through the gate, against central
+    # differences of the forward oracle run with the same output gate
+    rng = np.random.default_rng(41)
+    B, T, H, K, V = 1, 6, 2, 3, 3
+    x, do, dsf = _inputs(rng, B, T, H, K, V)
+    x["z"] = rng.standard_normal((B, T, H, V))
+    gr = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf, o_gate=x["z"])
+
+    def loss():
+        o, sf = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], o_gate=x["z"])
+        return float(np.sum(o * do) + np.sum(sf * dsf))
+    for name, gname in (("z", "do_gate"), ("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
+                        ("S0", "dS0")):
+        fd = np.zeros_like(x[name])
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 1e-6
+            lp = loss()
+            flat[i] = old - 1e-6
+            lm = loss()
+            flat[i] = old
+            fd.reshape(-1)[i] = (lp - lm) / 2e-6
+        assert np.max(np.abs(fd - gr[gname])) < 1e-7 * max(1.0, np.max(np.abs(fd))), name
