@@ -1,15 +1,18 @@
 """Benchmark of the MI355X KDA hot path on one GPU; prints ONE JSON line.
 
-A step is one chunked prefill (kda_chunk_prep + kda_chunk_state, i.e. one
-kda_chunk_fwd) of the K3-shaped workload: B=1, T=4096, H=96, K=V=128, bf16
-q/k/v/g/beta, chunk 16, zero initial state, returning o and S_final. Inputs
-are seeded synthetic tensors already resident in HBM. `value` is prefill
-tokens/s at chunk 16; the same workload is also timed at chunk 64 and
-reported under "chunk64". The decode half of the metric (N=512 streams,
-H=96, fp32 state of ~3.2 GB updated in place, 100 consecutive steps) is
-timed after the prefill steps and reported under "decode". The backward pass
-(kda_chunk_bwd) on the prefill workload's inputs is timed last and reported
-under "backward", against the fp32 vector peak (it runs on the vector ALUs).
+A step is one kda_chunk_fwd call on the K3-shaped workload: B=1, T=4096, H=96,
+K=V=128, bf16 q/k/v/g/beta, chunk 16, zero initial state, default (bf16)
+state-pass operands, returning o and S_final. Inputs are seeded synthetic
+tensors already resident in HBM. Before anything is timed the headline step
+runs back to back for --settle-s seconds (the GPU clock needs tens of
+milliseconds of load to settle). `value` is prefill tokens/s. Further legs:
+chunk 64, fp16 operands, the gate/norm/convolution prologues and the output
+gate, the 16-sequence packed workload (about 130K tokens) and the
+1,048,576-token sequence. The decode half of the metric (N=512 streams, H=96,
+fp32 state of ~3.2 GB updated in place, 100 consecutive steps) is reported
+under "decode". The backward pass (kda_chunk_bwd) on the prefill workload's
+inputs is reported under "backward", against the fp32 vector peak (it runs
+on the vector ALUs).
 
 Kernel durations come from HIP events recorded on the stream the kernels run
 on, around each phase of every timed step. Roofline figures use algorithmic
@@ -26,7 +29,7 @@ import time
 
 import torch
 
-from kda_gated_delta_chunk_amd import _lib, decode_step, synth
+from kda_gated_delta_chunk_amd import _lib, decode_step, synth, workspace_status
 from kda_gated_delta_chunk_amd.source_hash import csrc_hash
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
@@ -52,74 +55,111 @@ def prefill_flops(T, H, K, V, C=16):
     return T * H * per
 
 
-def time_prefill(w, steps, warmup, dev, chunk=16, gate="log_decay", o_gate=False, qk_norm=False, conv="none"):
-    lib = _lib.load()
-    gc = _lib.GATES[gate]
-    qkc = _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
-    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=(gate == "scaled_sigmoid"), with_o_gate=o_gate,
-                                        raw_k=qk_norm)
-    og = inp["o_gate"].data_ptr() if o_gate else None
-    B, T, H, K = inp["q"].shape
-    V = inp["v"].shape[-1]
-    N = B
-    o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
-    Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    cc = _lib.CONVS[conv]
-    cw = None
-    if conv != "none":
-        cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev)
-    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
+class PrefillLeg:
+    """One prefill workload on the GPU: inputs resident in HBM, preallocated outputs and workspaces, and
+    the three ABI calls (kda_chunk_fwd, and the split kda_chunk_prep / kda_chunk_state) as closures."""
 
-    def prep():
-        _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, N, chunk, 1, gc, qkc,
-                                      cc, None if cw is None else cw.data_ptr(), ws.data_ptr(), wsb, sh),
-                   "kda_chunk_prep")
+    def __init__(self, dev, inp, chunk=16, gate="log_decay", qk_norm=False, conv="none", operands="bf16",
+                 with_split=True):
+        lib = self.lib = _lib.load()
+        self.inp = inp
+        gc = _lib.GATES[gate]
+        qkc = _lib.KDA_QK_L2NORM if qk_norm else _lib.KDA_QK_AS_GIVEN
+        og = inp["o_gate"].data_ptr() if inp.get("o_gate") is not None else None
+        B, T, H, K = inp["q"].shape
+        V = inp["v"].shape[-1]
+        cu = inp.get("cu_seqlens")
+        N = B if cu is None else cu.numel() - 1
+        self.B, self.T, self.H, self.K, self.V, self.N = B, T, H, K, V, N
+        cup = None if cu is None else cu.data_ptr()
+        s0 = None if inp.get("S0") is None else inp["S0"].data_ptr()
+        self.o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+        self.Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        cc = _lib.CONVS[conv]
+        oc = _lib.OPERANDS[operands]
+        cw = None
+        if conv != "none":
+            cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev)
+        cwp = None if cw is None else cw.data_ptr()
+        self.cw = cw
+        self.wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc, oc)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
+        self.swsb = lib.kda_chunk_prep_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc, oc) if with_split else 0
+        self.sws = torch.empty(self.swsb, dtype=torch.uint8, device=dev) if with_split else None
+        self.stream = torch.cuda.current_stream(dev)
+        sh = self.stream.cuda_stream
+        p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
+        o, Sf = self.o.data_ptr(), self.Sf.data_ptr()
 
-    def state():
-        _lib.check(lib.kda_chunk_state(p["v"], og, None, None, B, T, H, K, V, N, chunk, 1, cc,
-                                       None if cw is None else cw.data_ptr(), 1, o.data_ptr(), Sf.data_ptr(),
-                                       ws.data_ptr(), wsb, sh), "kda_chunk_state")
+        def fwd():
+            _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, s0, cup, B, T, H, K, V, N,
+                                         chunk, 1, gc, qkc, cc, cwp, oc, 1, o, Sf, self.ws.data_ptr(), self.wsb, sh),
+                       "kda_chunk_fwd")
 
-    def fwd():
-        _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, None, None, B, T, H, K, V, N, chunk,
-                                     1, gc, qkc, cc, None if cw is None else cw.data_ptr(), 1, o.data_ptr(),
-                                     Sf.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_fwd")
+        def prep():
+            _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], cup, B, T, H, K, V, N, chunk, 1, gc, qkc,
+                                          cc, cwp, oc, self.sws.data_ptr(), self.swsb, sh), "kda_chunk_prep")
 
-    # the step: one kda_chunk_fwd call (where the state pass leaves CUs free, the library runs the
-    # prep of later chunks beside the state pass of earlier ones)
-    for _ in range(warmup):
-        fwd()
-    evf = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
+        def state():
+            _lib.check(lib.kda_chunk_state(p["v"], og, s0, cup, B, T, H, K, V, N, chunk, 1, cc, cwp, 1, o, Sf,
+                                           self.sws.data_ptr(), self.swsb, sh), "kda_chunk_state")
+
+        self.fwd, self.prep, self.state = fwd, prep, state
+
+    def device_error(self):
+        """Error bits the kernels recorded in the workspaces (0: none)."""
+        e = workspace_status(self.ws)
+        if self.sws is not None:
+            e |= workspace_status(self.sws)
+        return e
+
+    def time_fwd(self, steps, warmup):
+        """The step: one kda_chunk_fwd call. Returns (wall ms per step, event ms per step)."""
+        for _ in range(warmup):
+            self.fwd()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(self.stream)
+        for _ in range(steps):
+            self.fwd()
+        ev[1].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / steps, ev[0].elapsed_time(ev[1]) / steps
+
+    def time_split(self, steps, warmup):
+        """Per-kernel durations: the two halves as separate calls, HIP events on the launch stream around
+        each. Returns (prep ms, state ms) averaged over the steps."""
+        for _ in range(warmup):
+            self.prep()
+            self.state()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[i][0].record(self.stream)
+            self.prep()
+            ev[i][1].record(self.stream)
+            self.state()
+            ev[i][2].record(self.stream)
+        torch.cuda.synchronize()
+        return (sum(e[0].elapsed_time(e[1]) for e in ev) / steps,
+                sum(e[1].elapsed_time(e[2]) for e in ev) / steps)
+
+
+def settle_clock(leg, seconds):
+    """Runs the headline step back to back for `seconds` of wall time before anything is timed: the GPU's
+    clock needs some tens of milliseconds of load to reach its steady state, and the first timed leg
+    would otherwise run on a rising clock."""
     t0 = time.perf_counter()
-    evf[0].record(stream)
-    for i in range(steps):
-        fwd()
-        evf[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = evf[0].elapsed_time(evf[steps]) / steps
-    # per-kernel durations: the two halves as separate calls (kda_chunk_prep, kda_chunk_state)
-    for _ in range(warmup):
-        prep()
-        state()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        prep()
-        ev[i][1].record(stream)
-        state()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    state_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    return {"B": B, "T": T, "H": H, "K": K, "V": V, "N": N, "wall_s": wall, "fwd_ms": fwd_ms, "prep_ms": prep_ms,
-            "state_ms": state_ms, "ws_bytes": wsb}
+    n = 0
+    while True:
+        for _ in range(20):
+            leg.fwd()
+        n += 20
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return {"seconds": time.perf_counter() - t0, "calls": n}
 
 
 def time_decode(w, steps, dev, gate="log_decay", qk_norm=False):
@@ -274,7 +314,9 @@ def traffic_from_counters(fetch_csv, write_csv, out_path):
 
 
 def cpu_baseline(w):
-    """The fp64 oracle on the host, on the full prefill workload (generation excluded)."""
+    """The fp64 oracle on the host, on the full 4096-token, 96-head prefill workload (generation excluded),
+    on every host core it may use, and on one core over a two-head sample of the same workload (scaled to
+    tokens of all heads)."""
     import oracle  # test infrastructure: only this baseline leg uses it
     inp = synth.workload_prefill_inputs(w, device="cpu")
     args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
@@ -283,21 +325,47 @@ def cpu_baseline(w):
     oracle.chunk_fwd(*args, threads=threads)
     dt = time.perf_counter() - t0
     B, T, H, _ = args[0].shape
+    hs = [0, H - 1]
+    sample = [a[:, :, hs].contiguous() for a in args]
+    t0 = time.perf_counter()
+    oracle.chunk_fwd(*sample, threads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "full workload: B=1 T=%d H=%d K=V=128 bf16 inputs, fp64 per-token recurrence, %.1f s" %
-                      (T, H, dt)}
+            "sample": "full workload: B=1 T=%d H=%d K=V=128 bf16 inputs, fp64 per-token recurrence, %.2f s wall "
+                      "on %d threads" % (T, H, dt, threads),
+            "one_core": {"value": B * T * len(hs) / H / dt1, "unit": "tokens/s (of all %d heads)" % H, "cores": 1,
+                         "sample": "heads %s of the same workload, %.2f s on one thread" % (hs, dt1)}}
+
+
+def leg_summary(leg, wall_ms, ev_ms, name, C=16, split=None):
+    """Throughput and whole-path roofline of one timed leg."""
+    T = leg.B * leg.T
+    has_S0 = leg.inp.get("S0") is not None
+    path_bytes, kb = prefill_algorithmic_bytes(T, leg.H, leg.K, leg.V, leg.N, with_S0=has_S0)
+    gbs = path_bytes / (ev_ms * 1e-3) / 1e9
+    tf = prefill_flops(T, leg.H, leg.K, leg.V, C) / (ev_ms * 1e-3) / 1e12
+    out = {"workload": name, "tokens_per_s": T / (wall_ms * 1e-3), "ms_per_step": wall_ms, "event_ms": ev_ms,
+           "roofline_path": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": path_bytes,
+                             "mfma_tflops_algorithmic": tf, "mfma_frac_algorithmic": tf / BF16_PEAK_TFLOPS},
+           "workspace_bytes": leg.wsb}
+    if split is not None:
+        out["split_calls_ms"] = {"kda_chunk_prep": split[0], "kda_chunk_state": split[1]}
+    return out, kb
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU clock needs some tens of milliseconds of load to settle")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before each timed leg")
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of back-to-back headline steps before the first timed leg (clock settle)")
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-large", action="store_true", help="skip the 130K-token packed and 1M-token legs")
     ap.add_argument("--counters", action="store_true",
                     help="short pass for hardware-counter runs: a 1 GiB device copy (calibration of the byte "
                          "counters), then the prefill and decode steps, no CPU baseline")
@@ -322,6 +390,10 @@ def main():
               "shard without communication; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+
+    def say(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
     if args.counters:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -329,101 +401,94 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         args.no_cpu_baseline = True
+        args.no_large = True
+        args.settle_s = 0.0
     w = synth.WORKLOADS["prefill_4k"]
-    print("[bench] prefill %s: warmup %d, steps %d" % (w.name, args.warmup, args.steps), file=sys.stderr,
-          flush=True)
-    r = time_prefill(w, args.steps, args.warmup, dev)
-    ms = r["wall_s"] * 1e3 / args.steps
-    tok_s = r["B"] * r["T"] / (ms * 1e-3)
-    path_bytes, kb = prefill_algorithmic_bytes(r["T"] * r["B"], r["H"], r["K"], r["V"], r["N"])
-    kern_ms = {"kda_chunk_prep (+chunk table)": r["prep_ms"], "kda_state_pass": r["state_ms"]}
-    dom = "state" if r["state_ms"] >= r["prep_ms"] else "prep"
-    dom_ms = r["state_ms"] if dom == "state" else r["prep_ms"]
+    inp = synth.workload_prefill_inputs(w, device=dev)
+    leg = PrefillLeg(dev, inp)
+    settle = settle_clock(leg, args.settle_s) if args.settle_s > 0 else {"seconds": 0.0, "calls": 0}
+    say("clock settled: %d headline steps in %.2f s; prefill %s: warmup %d, steps %d"
+        % (settle["calls"], settle["seconds"], w.name, args.warmup, args.steps))
+    wall_ms, ev_ms = leg.time_fwd(args.steps, args.warmup)
+    prep_ms, state_ms = leg.time_split(args.steps, args.warmup)
+    head, kb = leg_summary(leg, wall_ms, ev_ms, "", split=(prep_ms, state_ms))
+    errors = {"prefill_4k": leg.device_error()}
+    dom = "state" if state_ms >= prep_ms else "prep"
+    dom_ms = state_ms if dom == "state" else prep_ms
     dom_gbs = kb[dom] / (dom_ms * 1e-3) / 1e9
-
-    def path_roofline(rr, C):
-        pm = rr["fwd_ms"]
-        gbs = path_bytes / (pm * 1e-3) / 1e9
-        tf = prefill_flops(rr["T"] * rr["B"], rr["H"], rr["K"], rr["V"], C) / (pm * 1e-3) / 1e12
-        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "algorithmic_bytes": path_bytes, "event_ms": pm, "mfma_tflops_algorithmic": tf,
-                "mfma_frac_algorithmic": tf / BF16_PEAK_TFLOPS}
-
+    kname = "kda::kda_state_pass_fmt<128, 128>" if dom == "state" else "kda::kda_chunk_prep<true, 128, false, false>"
     out = {
         "metric": "KDA prefill tokens/s (H=96,d=128,bf16) + decode state GB/s, % of roofline",
-        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; q,v~N(0,1), k L2-normalised, g=-5*sigmoid(N(0,1)), beta=sigmoid(N(0,1)))",
-        "config": {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 16, zero S0", "global_batch": 1,
-                   "seq_len": r["T"], "heads": r["H"], "chunk": 16, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "kda_state_pass" if dom == "state" else "kda_chunk_prep",
-                     "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("kda::kda_state_pass<true, 128, 128, 1, false, true>" if dom == "state"
-                                                 else "kda::kda_chunk_prep<true, 128, false, true>"),
+        "config": {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 16, zero S0, bf16 operands (default)",
+                   "global_batch": 1, "seq_len": w.T, "heads": w.H, "chunk": 16, "parallelism": "single GPU"},
+        "clock_settle": settle,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(kname),
                      "algorithmic_bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms,
-                     "mfma_busy_frac_rocprof": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false, true>"
-                                                              if dom == "state" else "kda::kda_chunk_prep<true, 128, false, true>",
-                                                              dom_ms)},
-        "roofline_path": path_roofline(r, 16),
-        "kernels_ms": kern_ms,
-        "kernels_mfma_busy_frac_rocprof": {
-            "kda_chunk_prep": mfma_busy_frac("kda::kda_chunk_prep<true, 128, false, true>", r["prep_ms"]),
-            "kda_state_pass": mfma_busy_frac("kda::kda_state_pass<true, 128, 128, 1, false, true>", r["state_ms"])},
-        "split_calls_ms": r["prep_ms"] + r["state_ms"],
-        "workspace_bytes": r["ws_bytes"],
+                     "mfma_busy_frac_rocprof": mfma_busy_frac(kname, dom_ms)},
+        "roofline_path": head["roofline_path"],
+        "event_ms_per_step": ev_ms,
+        "kernels_ms": {"kda_chunk_prep (header + prep)": prep_ms, "kda_state_pass": state_ms},
+        "split_calls_ms": prep_ms + state_ms,
+        "workspace_bytes": leg.wsb,
     }
-    print("[bench] prefill %s at chunk 64: warmup %d, steps %d" % (w.name, args.warmup, args.steps),
-          file=sys.stderr, flush=True)
-    r64 = time_prefill(w, args.steps, args.warmup, dev, chunk=64)
-    ms64 = r64["wall_s"] * 1e3 / args.steps
-    out["chunk64"] = {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 64, zero S0",
-                      "tokens_per_s": r64["B"] * r64["T"] / (ms64 * 1e-3), "ms_per_step": ms64,
-                      "kernels_ms": {"kda_chunk_prep64 (+chunk table)": r64["prep_ms"],
-                                     "kda_state_pass": r64["state_ms"]},
-                      "split_calls_ms": r64["prep_ms"] + r64["state_ms"],
-                      "roofline_path": path_roofline(r64, 64), "workspace_bytes": r64["ws_bytes"]}
-    print("[bench] prefill %s with the gate formed in-kernel: warmup %d, steps %d" % (w.name, args.warmup,
-                                                                                    args.steps),
-          file=sys.stderr, flush=True)
-    rg = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid")
-    msg = rg["wall_s"] * 1e3 / args.steps
-    out["gate_fused"] = {"workload": "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 16, zero S0; g holds the gate "
-                                     "pre-activation x, log-decay -5*sigmoid(x) formed in kda_chunk_prep",
-                         "tokens_per_s": rg["B"] * rg["T"] / (msg * 1e-3), "ms_per_step": msg,
-                         "kernels_ms": {"kda_chunk_prep (+chunk table)": rg["prep_ms"],
-                                        "kda_state_pass": rg["state_ms"]}}
-    print("[bench] prefill %s with both gates formed in-kernel: warmup %d, steps %d" % (w.name, args.warmup,
-                                                                                      args.steps),
-          file=sys.stderr, flush=True)
-    ro = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True)
-    mso = ro["wall_s"] * 1e3 / args.steps
-    out["gates_fused"] = {"workload": "as gate_fused, plus an output gate: o * sigmoid(z), z [B,T,H,V] bf16 read "
-                                      "and applied where kda_state_pass stores o",
-                          "tokens_per_s": ro["B"] * ro["T"] / (mso * 1e-3), "ms_per_step": mso,
-                          "kernels_ms": {"kda_chunk_prep (+chunk table)": ro["prep_ms"],
-                                         "kda_state_pass": ro["state_ms"]}}
-    print("[bench] prefill %s with both gates and the q/k normalisation in-kernel: warmup %d, steps %d"
-          % (w.name, args.warmup, args.steps), file=sys.stderr, flush=True)
-    rn = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True, qk_norm=True)
-    msn = rn["wall_s"] * 1e3 / args.steps
-    print("[bench] prefill %s with the short convolution as well: warmup %d, steps %d"
-          % (w.name, args.warmup, args.steps), file=sys.stderr, flush=True)
-    rc = time_prefill(w, args.steps, args.warmup, dev, gate="scaled_sigmoid", o_gate=True, qk_norm=True,
-                      conv="short4_silu")
-    msc = rc["wall_s"] * 1e3 / args.steps
-    out["conv_prologue_epilogue_fused"] = {
-        "workload": "as prologue_epilogue_fused, plus the length-4 short convolution of q, k, v with SiLU "
-                    "(q, k in kda_chunk_prep; v by kda_conv_v into the workspace)",
-        "tokens_per_s": rc["B"] * rc["T"] / (msc * 1e-3), "ms_per_step": msc,
-        "kernels_ms": {"kda_chunk_prep (+chunk table)": rc["prep_ms"],
-                       "kda_conv_v + kda_state_pass": rc["state_ms"]}}
-    out["prologue_epilogue_fused"] = {
-        "workload": "as gates_fused, with raw q, k ~ N(0,1) L2-normalised per (token, head) in kda_chunk_prep",
-        "tokens_per_s": rn["B"] * rn["T"] / (msn * 1e-3), "ms_per_step": msn,
-        "kernels_ms": {"kda_chunk_prep (+chunk table)": rn["prep_ms"], "kda_state_pass": rn["state_ms"]}}
+    del leg
+
+    def prefill_leg(key, name, inp_, steps=args.steps, warmup=args.warmup, C=16, **kw):
+        say("prefill %s: warmup %d, steps %d" % (key, warmup, steps))
+        lg = PrefillLeg(dev, inp_, chunk=C, **kw)
+        wm, em = lg.time_fwd(steps, warmup)
+        sp = lg.time_split(steps, warmup) if lg.sws is not None else None
+        out[key], _ = leg_summary(lg, wm, em, name, C=C, split=sp)
+        errors[key] = lg.device_error()
+        del lg
+
+    prefill_leg("chunk64", "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 64, zero S0", inp, C=64)
+    prefill_leg("fp16_operands", "as the headline, fp16 state-pass operands (operands=fp16)", inp, operands="fp16")
+    del inp
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=True)
+    prefill_leg("gate_fused", "as the headline; g holds the gate pre-activation x, log-decay -5*sigmoid(x) formed "
+                              "in-kernel", inp, gate="scaled_sigmoid")
+    del inp
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=True, with_o_gate=True)
+    prefill_leg("gates_fused", "as gate_fused, plus an output gate: o * sigmoid(z), z [B,T,H,V] bf16 read and "
+                               "applied where o is stored", inp, gate="scaled_sigmoid")
+    del inp
+    inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=True, with_o_gate=True, raw_k=True)
+    prefill_leg("prologue_epilogue_fused", "as gates_fused, with raw q, k ~ N(0,1) L2-normalised per (token, head) "
+                                           "in-kernel", inp, gate="scaled_sigmoid", qk_norm=True)
+    prefill_leg("conv_prologue_epilogue_fused", "as prologue_epilogue_fused, plus the length-4 short convolution of "
+                                                "q, k, v with SiLU", inp, gate="scaled_sigmoid", qk_norm=True,
+                conv="short4_silu")
+    del inp
+    if not args.no_large:
+        wv = synth.WORKLOADS["varlen_16"]
+        inp = synth.workload_prefill_inputs(wv, device=dev)
+        T2 = inp["q"].shape[1]
+        prefill_leg("varlen_16", "16 packed sequences, lengths uniform in [256, 16384] (seed %d: %d tokens), "
+                                 "H=96 K=V=128 bf16 chunk 16, S0 ~ N(0, 0.02^2), cu_seqlens" % (wv.seed, T2), inp,
+                    steps=max(3, args.steps // 4), warmup=2)
+        del inp
+        w1 = synth.WORKLOADS["prefill_1m"]
+        torch.cuda.empty_cache()
+        free, _ = torch.cuda.mem_get_info()
+        io_bytes = w1.T * w1.H * (3 * w1.K + 2 * w1.V + 1) * 2
+        ws_bytes = _lib.load().kda_chunk_fwd_workspace_bytes(1, w1.T, w1.H, w1.K, w1.V, 1, 16, 1, 0, 0)
+        if free < io_bytes + ws_bytes + w1.H * w1.K * w1.V * 4 + (4 << 30):
+            out["prefill_1m"] = {"skipped": "needs %.0f GB of device memory, %.0f GB free"
+                                            % ((io_bytes + ws_bytes) / 1e9, free / 1e9)}
+        else:
+            inp = synth.workload_prefill_inputs(w1, device=dev)
+            prefill_leg("prefill_1m", "B=1 T=1,048,576 H=96 K=V=128 bf16 chunk 16, zero S0", inp,
+                        steps=max(2, min(5, args.steps // 10)), warmup=1, with_split=False)
+            del inp
+        torch.cuda.empty_cache()
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
-        print("[bench] decode %s: %d steps" % (wd.name, args.decode_steps), file=sys.stderr, flush=True)
+        say("decode %s: %d steps" % (wd.name, args.decode_steps))
         d = time_decode(wd, args.decode_steps, dev)
         gbs = d["bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9
         out["decode"] = {"workload": "decode N=512 H=96 K=V=128 bf16 in, fp32 state in place, %d steps" %
@@ -439,7 +504,7 @@ def main():
         dn = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid", qk_norm=True)
         out["decode"]["gate_and_qk_norm_fused_ms_per_step"] = dn["ms_per_step"]
     if not args.no_backward:
-        print("[bench] backward %s: warmup 3, steps 10" % w.name, file=sys.stderr, flush=True)
+        say("backward %s: warmup 3, steps 10" % w.name)
         rb = time_backward(w, 10, 3, dev)
         fl = backward_flops(rb["T"], rb["H"], rb["K"], rb["V"])
         tfs = fl / (rb["ms"] * 1e-3) / 1e12
@@ -452,8 +517,9 @@ def main():
                          "achieved": tfs, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_VECTOR_PEAK_TFS, "algorithmic_flops_per_call": fl,
                          "timed": "whole call (3 launches)"}}
+    out["device_errors"] = errors
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        say("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

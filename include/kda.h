@@ -34,14 +34,11 @@
  *     and no output is written. A fault inside a kernel surfaces at the
  *     caller's next synchronisation of the stream.
  *   - Supported sizes: K, V in {32, 64, 128}; chunk in {16, 64}.
- *   - Prefill with bf16 I/O at 16-token chunks (and no short convolution)
- *     carries the state pass's operands in fp16, which is faster and at
- *     least as accurate at the magnitudes of normalised activations, but
- *     needs |v| and the state's entries well inside fp16's range (|x| < 6e4):
- *     beyond it results are not finite. The environment variable
- *     KDA_OPERANDS=bf16 (read at each call, and by the workspace query,
- *     which must see the same setting) selects bf16 operands with bf16's
- *     range instead.
+ *   - Device-side errors (a bounded wait between wavefronts that gave up, a
+ *     workspace that does not describe the call) cannot be returned by the
+ *     asynchronous calls; the kernels record them in the workspace, where
+ *     kda_workspace_status reads them, and a prefill that hit one writes
+ *     NaN rather than numbers wherever it can.
  *   - The functions keep no state between calls and may be called from
  *     several host threads on different streams (calls that share output
  *     buffers or a workspace race).
@@ -127,6 +124,31 @@ typedef enum {
     KDA_CONV_SHORT4_SILU = 2
 } kda_conv_t;
 
+/*
+ * Operand format of the prefill's state pass (the matrix products that carry
+ * the state from chunk to chunk and form the output). Accumulation, the state
+ * itself, the cumulative decay and the triangular solve are fp32 in both.
+ *   KDA_OPERANDS_BF16  bf16 operands: the decay-scaled queries and keys, the
+ *                      intra-chunk P and the corrected values as bf16 hi + lo
+ *                      pairs (about 16 significant bits), the rest single
+ *                      bf16. bf16 keeps fp32's exponent range, so every finite
+ *                      input is in range; the first page above ties the -5
+ *                      bound of the decay to staying inside bf16's range
+ *                      (paragraph "K3 对 Kimi Linear 的进一步修改"). The default.
+ *   KDA_OPERANDS_FP16  fp16 operands (11 significant bits, fewer bytes and
+ *                      products: faster). fp16's largest value is 65504, so
+ *                      every |v|, every state entry and the decay-scaled
+ *                      query and key entries must stay well below it; beyond
+ *                      that the results are inf or NaN. Only for bf16 I/O at
+ *                      16-token chunks without a convolution (else
+ *                      KDA_ERROR_NOT_SUPPORTED).
+ * With fp32 I/O the operands are fp32 (KDA_OPERANDS_BF16 selects that).
+ */
+typedef enum {
+    KDA_OPERANDS_BF16 = 0,
+    KDA_OPERANDS_FP16 = 1
+} kda_operands_t;
+
 /* Version of this ABI (bumped on any signature change). */
 int kda_abi_version(void);
 
@@ -134,16 +156,38 @@ int kda_abi_version(void);
 const char *kda_status_string(kda_status_t status);
 
 /*
- * Bytes of device workspace that kda_chunk_fwd needs for these sizes.
+ * Bytes of device workspace that kda_chunk_fwd needs for these sizes
+ * (kda_chunk_fwd_workspace_bytes), and that a kda_chunk_prep / kda_chunk_state
+ * pair needs (kda_chunk_prep_workspace_bytes).
  *   B, T        batch rows and tokens per row (packed: B = 1, T = total tokens)
  *   num_seqs    number of sequences: B without cu_seqlens, else len(cu_seqlens)-1
  *   chunk, io   as for kda_chunk_fwd
  *   conv        as for kda_chunk_fwd (a convolution needs room for the
  *               convolved tensors: 4 * B * T * H * (K + K + V) bytes more)
- * Returns 0 if the sizes are invalid or unsupported.
+ *   operands    as for kda_chunk_fwd
+ * Returns 0 if the sizes or options are invalid or unsupported.
  */
-size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                                     int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_conv_t conv);
+size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands);
+size_t kda_chunk_prep_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                      int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands);
+
+/*
+ * Device-side error bits of the last prefill that used `workspace`: waits for
+ * `stream` to finish, then stores the bits in *device_error (0: none).
+ *   1  a bounded wait between the wavefronts of a prefill kernel gave up
+ *      (about 0.1 s without progress); its o and S_final are not to be used.
+ *   2  kda_chunk_state found a workspace that no kda_chunk_prep of the same
+ *      sizes, options, cu_seqlens pointer and workspace size had filled (or
+ *      that was modified); it wrote NaN to o and S_final instead of reading it.
+ * The bits stay set until the next kda_chunk_fwd or kda_chunk_prep on the
+ * workspace. Errors: INVALID_VALUE (NULL or misaligned pointer, or a
+ * workspace that no prefill has written), WORKSPACE_TOO_SMALL (fewer than
+ * 256 bytes), NO_DEVICE, HIP (the copy or the synchronisation failed, e.g.
+ * after a fault on the stream).
+ */
+kda_status_t kda_workspace_status(const void *workspace, size_t workspace_bytes, int32_t *device_error,
+                                  void *stream);
 
 /*
  * Chunked prefill over whole sequences: the recurrence above for every
@@ -181,53 +225,54 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
  *             fp32 result). Rows of tokens outside every sequence are not
  *             written.
  *   S_final   [num_seqs, H, K, V] fp32, or NULL to skip. May not alias S0.
- *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes().
+ *   operands  the state pass's operand format (kda_operands_t).
+ *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes();
+ *             its first 256 bytes hold a header (sizes, format, error bits).
  * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
  *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow,
- *   unknown dtype, gate, qk_norm or conv, NULL or misaligned conv_w with a
- *   convolution),
- *   NOT_SUPPORTED (K, V or chunk outside the supported set),
+ *   unknown dtype, gate, qk_norm, conv or operands, NULL or misaligned conv_w
+ *   with a convolution),
+ *   NOT_SUPPORTED (K, V or chunk outside the supported set, fp16 operands
+ *   outside bf16 I/O at 16-token chunks without a convolution),
  *   WORKSPACE_TOO_SMALL, NO_DEVICE, HIP (launch failure).
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens,
                            int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                            int32_t chunk, kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm,
-                           kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o,
-                           float *S_final, void *workspace, size_t workspace_bytes, void *stream);
+                           kda_conv_t conv, const float *conv_w, kda_operands_t operands, kda_dtype_t o_dtype,
+                           void *o, float *S_final, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
- * separately. kda_chunk_fwd returns bitwise the results of kda_chunk_prep
- * followed by kda_chunk_state on one stream; where the state pass leaves most
- * of the GPU idle (16-token chunks, num_seqs * H <= 64, at least 128 chunks)
- * it splits the chunks into ranges and runs the prep of each range beside the
- * state pass of the previous one. The environment variable
- * KDA_PIPELINE_RANGES (1 .. 16, read at each call) sets the number of ranges;
- * 1 turns this off.
+ * separately; they need kda_chunk_prep_workspace_bytes() of workspace.
  *
- * kda_chunk_prep: everything that does not depend on the state. Numbers the
- *   chunks (cu_seqlens as for kda_chunk_fwd, read on the device) and, per
- *   (chunk, head), forms the cumulative log-decay, the beta-weighted
- *   decay-scaled key products, solves the chunk's unit lower-triangular
- *   system and stores the resulting factors in `workspace` (layout private to
- *   the library). Reads q, k (as `conv` and `qk_norm` say), g (as `gate`
- *   says), beta and the q and k parts of conv_w; V only sizes the workspace
- *   check.
+ * kda_chunk_prep: everything that does not depend on the state. Writes the
+ *   workspace header, numbers the chunks (cu_seqlens as for kda_chunk_fwd,
+ *   read on the device) and, per (chunk, head), forms the cumulative
+ *   log-decay, the beta-weighted decay-scaled key products, solves the
+ *   chunk's unit lower-triangular system and stores the resulting factors in
+ *   `workspace` in the `operands` format (layout private to the library).
+ *   Reads q, k (as `conv` and `qk_norm` say), g (as `gate` says), beta and the
+ *   q and k parts of conv_w; V only sizes the workspace check.
  * kda_chunk_state: the sequential pass over the chunks of each (sequence,
  *   head): carries S from S0 (or 0), writes o (gated by o_gate, if given) and
  *   S_final. With a convolution it first convolves v (the v part of conv_w)
- *   into the workspace. Reads v, o_gate, S0, conv_w and a
- *   workspace that kda_chunk_prep filled with the same sizes and the same
- *   cu_seqlens pointer (used here only to tell packed from batched input;
- *   not dereferenced). The workspace may not be modified in between.
+ *   into the workspace. Reads v, o_gate, S0, conv_w and a workspace that
+ *   kda_chunk_prep filled; it takes the operand format from the workspace
+ *   header, so it has no `operands` argument. The header must describe the
+ *   same B, T, H, K, V, num_seqs, chunk, io, conv and cu_seqlens pointer (not
+ *   dereferenced here otherwise) and a layout that fits workspace_bytes;
+ *   if it does not, o and S_final are written as NaN and error bit 2 is set
+ *   (kda_workspace_status). The workspace may not be modified in between.
+ * The results of the pair equal those of kda_chunk_fwd bit for bit.
  * Errors as for kda_chunk_fwd.
  */
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, void *workspace,
-                            size_t workspace_bytes, void *stream);
+                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_operands_t operands,
+                            void *workspace, size_t workspace_bytes, void *stream);
 kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                              kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o, float *S_final,

@@ -17,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import KDAError, KDA_DTYPE_BF16, KDA_DTYPE_FP32
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "workspace_bytes", "bwd_workspace_bytes", "KDAError",
-           "abi_version"]
+__all__ = ["chunk_fwd", "chunk_prep", "chunk_state", "chunk_bwd", "decode_step", "workspace_bytes",
+           "prep_workspace_bytes", "workspace_status", "bwd_workspace_bytes", "KDAError", "abi_version"]
 
 _DT = {torch.bfloat16: KDA_DTYPE_BF16, torch.float32: KDA_DTYPE_FP32}
 _NAME = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -36,9 +36,41 @@ def _io_code(dtype) -> int:
     return _DT[dtype]
 
 
-def workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16") -> int:
-    """Device workspace bytes kda_chunk_fwd needs (0 = unsupported sizes)."""
-    return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io)))
+def _operands_code(operands: str) -> int:
+    if operands not in _lib.OPERANDS:
+        raise ValueError("operands must be one of %s" % sorted(_lib.OPERANDS))
+    return _lib.OPERANDS[operands]
+
+
+def workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16",
+                    conv: str = "none", operands: str = "bf16") -> int:
+    """Device workspace bytes kda_chunk_fwd needs (0 = unsupported sizes or options)."""
+    if conv not in _lib.CONVS:
+        raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
+    return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io),
+                                                         _lib.CONVS[conv], _operands_code(operands)))
+
+
+def prep_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16",
+                         conv: str = "none", operands: str = "bf16") -> int:
+    """Device workspace bytes a kda_chunk_prep / kda_chunk_state pair needs (0 = unsupported)."""
+    if conv not in _lib.CONVS:
+        raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
+    return int(_lib.load().kda_chunk_prep_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io),
+                                                          _lib.CONVS[conv], _operands_code(operands)))
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """Device-side error bits recorded in a prefill workspace (0 = none; _lib.WS_ERR_*). Synchronises
+    the stream (default: torch's current stream on the workspace's device)."""
+    import ctypes
+    lib = _lib.load()
+    dev = workspace.device
+    sh = _stream(dev) if stream is None else stream
+    out = ctypes.c_int32(-1)
+    _lib.check(lib.kda_workspace_status(_ptr(workspace), workspace.numel(), ctypes.byref(out), sh),
+               "kda_workspace_status")
+    return int(out.value)
 
 
 def bwd_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int) -> int:
@@ -85,12 +117,12 @@ def _conv_code(conv: str, conv_w, H: int, C: int, dev) -> int:
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
               output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None,
-              qk_norm: bool = False, conv: str = "none", conv_w=None):
+              qk_norm: bool = False, conv: str = "none", conv_w=None, operands: str = "bf16", final_state_out=None):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
-    [num_seqs, H, K, V]. ``workspace`` (uint8 CUDA tensor) and ``out`` may be
-    passed to avoid allocations. ``gate`` says what ``g`` holds: "log_decay"
+    [num_seqs, H, K, V]. ``workspace`` (uint8 CUDA tensor), ``out`` and
+    ``final_state_out`` may be passed to avoid allocations. ``gate`` says what ``g`` holds: "log_decay"
     (the log-decay itself) or "scaled_sigmoid" (the gate pre-activation,
     mapped to -5*sigmoid(g) inside the kernels). ``o_gate`` [B, T, H, V] (input
     dtype), if given, scales the output channel by channel: o * sigmoid(o_gate).
@@ -98,6 +130,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     head) by sqrt(|x|^2 + 1e-6) as they read it. ``conv``: "none", "short4" or
     "short4_silu": the causal length-4 convolution of q, k and v with the taps
     ``conv_w`` (fp32 [H, K + K + V, 4]), ahead of the normalisation.
+    ``operands``: "bf16" (hi + lo bf16 operand pairs, bf16's range) or "fp16"
+    (faster; |v| and the state must stay well inside fp16's range).
     """
     lib = _lib.load()
     dev = q.device
@@ -126,21 +160,82 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
         out = torch.empty((B, T, H, V), dtype=odt, device=dev)
     else:
         _need(out, "out", (B, T, H, V), odt, dev)
-    S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+    S_final = None
+    if final_state_out is not None:
+        _need(final_state_out, "final_state_out", (N, H, K, V), torch.float32, dev)
+        S_final = final_state_out
+    elif output_final_state:
+        S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
-    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io, cc)
+    oc = _operands_code(operands)
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io, cc, oc)
     if need == 0:
-        raise KDAError(2, "kda_chunk_fwd_workspace_bytes(B=%d,T=%d,H=%d,K=%d,V=%d,N=%d,chunk=%d)"
-                       % (B, T, H, K, V, N, chunk))
+        raise KDAError(2, "kda_chunk_fwd_workspace_bytes(B=%d,T=%d,H=%d,K=%d,V=%d,N=%d,chunk=%d,operands=%s)"
+                       % (B, T, H, K, V, N, chunk, operands))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     status = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0),
                                _ptr(cu_seqlens),
-                               B, T, H, K, V, N, chunk, io, gc, _qk_code(qk_norm), cc, _ptr(conv_w), _io_code(odt),
-                               _ptr(out),
-                               _ptr(S_final),
+                               B, T, H, K, V, N, chunk, io, gc, _qk_code(qk_norm), cc, _ptr(conv_w), oc,
+                               _io_code(odt), _ptr(out), _ptr(S_final),
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(status, "kda_chunk_fwd")
+    return out, S_final
+
+
+def chunk_prep(q, k, g, beta, workspace, cu_seqlens=None, V: int = None, chunk: int = 16, gate: str = "log_decay",
+               qk_norm: bool = False, conv: str = "none", conv_w=None, operands: str = "bf16"):
+    """The state-independent half of chunk_fwd (kda_chunk_prep): fills ``workspace`` (uint8 CUDA tensor of
+    at least prep_workspace_bytes()) with the chunk factors in the ``operands`` format. ``V`` is the value
+    width of the chunk_state call that follows (default K)."""
+    lib = _lib.load()
+    dev = q.device
+    B, T, H, K = q.shape
+    V = K if V is None else V
+    dt = q.dtype
+    io = _io_code(dt)
+    for name, t, shp in (("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)), ("beta", beta, (B, T, H))):
+        _need(t, name, shp, dt, dev)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
+    st = lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), B, T, H, K, V, N, chunk, io,
+                            _gate_code(gate), _qk_code(qk_norm), cc, _ptr(conv_w), _operands_code(operands),
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st, "kda_chunk_prep")
+
+
+def chunk_state(v, workspace, K: int, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None, out=None,
+                output_final_state: bool = True, o_gate=None, conv: str = "none", conv_w=None, final_state_out=None):
+    """The sequential half of chunk_fwd (kda_chunk_state) over a workspace chunk_prep filled; the operand
+    format comes from the workspace. Returns (o, S_final or None)."""
+    lib = _lib.load()
+    dev = v.device
+    B, T, H, V = v.shape
+    dt = v.dtype
+    io = _io_code(dt)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o_gate is not None:
+        _need(o_gate, "o_gate", (B, T, H, V), dt, dev)
+    if S0 is not None:
+        _need(S0, "S0", (N, H, K, V), torch.float32, dev)
+    odt = dt if o_dtype is None else (_NAME[o_dtype] if isinstance(o_dtype, str) else o_dtype)
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=odt, device=dev)
+    else:
+        _need(out, "out", (B, T, H, V), odt, dev)
+    S_final = None
+    if final_state_out is not None:
+        _need(final_state_out, "final_state_out", (N, H, K, V), torch.float32, dev)
+        S_final = final_state_out
+    elif output_final_state:
+        S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
+    st = lib.kda_chunk_state(_ptr(v), _ptr(o_gate), _ptr(S0), _ptr(cu_seqlens), B, T, H, K, V, N, chunk, io, cc,
+                             _ptr(conv_w), _io_code(odt), _ptr(out), _ptr(S_final), _ptr(workspace),
+                             workspace.numel(), _stream(dev))
+    _lib.check(st, "kda_chunk_state")
     return out, S_final
 
 

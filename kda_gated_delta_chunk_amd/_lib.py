@@ -19,12 +19,17 @@ GATES = {"log_decay": KDA_GATE_LOG_DECAY, "scaled_sigmoid": KDA_GATE_SCALED_SIGM
 KDA_QK_AS_GIVEN = 0
 KDA_QK_L2NORM = 1
 CONVS = {"none": 0, "short4": 1, "short4_silu": 2}
+OPERANDS = {"bf16": 0, "fp16": 1}
+# device-side error bits of a prefill workspace (kda_workspace_status)
+WS_ERR_WAIT_TIMEOUT = 1
+WS_ERR_HEADER_MISMATCH = 2
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
           3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_NO_DEVICE", 5: "KDA_ERROR_HIP"}
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-           "kda_chunk_prep", "kda_chunk_state", "kda_decode_step", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_prep_workspace_bytes",
+           "kda_workspace_status", "kda_chunk_fwd", "kda_chunk_prep", "kda_chunk_state", "kda_decode_step",
+           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 _lib = None
 
 
@@ -52,14 +57,17 @@ def load() -> ctypes.CDLL:
     lib.kda_abi_version.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
-    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
-    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    ci = ctypes.c_int
+    for fn in (lib.kda_chunk_fwd_workspace_bytes, lib.kda_chunk_prep_workspace_bytes):
+        fn.argtypes = [i64, i64, i32, i32, i32, i32, i32, ci, ci, ci]
+        fn.restype = sz
+    lib.kda_workspace_status.argtypes = [vp, sz, ctypes.POINTER(i32), vp]
+    lib.kda_workspace_status.restype = ci
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, vp, vp,
-                                  sz, vp]
+                                  ci, ci, ci, ci, vp, ci, ci, vp, vp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
-    lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
+    lib.kda_chunk_prep.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ci,
+                                   ci, ci, ci, vp, ci, vp, sz, vp]
     lib.kda_chunk_prep.restype = ctypes.c_int
     lib.kda_chunk_state.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                     vp, ctypes.c_int, vp, vp, vp, sz, vp]

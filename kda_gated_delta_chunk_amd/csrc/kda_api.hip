@@ -19,6 +19,11 @@ bool valid_dtype(kda_dtype_t t) { return t == KDA_DTYPE_FP32 || t == KDA_DTYPE_B
 bool valid_gate(kda_gate_t g) { return g == KDA_GATE_LOG_DECAY || g == KDA_GATE_SCALED_SIGMOID; }
 bool valid_qk_norm(kda_qk_norm_t n) { return n == KDA_QK_AS_GIVEN || n == KDA_QK_L2NORM; }
 bool valid_conv(kda_conv_t c) { return c == KDA_CONV_NONE || c == KDA_CONV_SHORT4 || c == KDA_CONV_SHORT4_SILU; }
+bool valid_operands(kda_operands_t f) { return f == KDA_OPERANDS_BF16 || f == KDA_OPERANDS_FP16; }
+// fp16 state-pass operands exist for bf16 I/O at 16-token chunks without a convolution.
+bool operands_supported(kda_operands_t f, kda_dtype_t io, int32_t chunk, kda_conv_t conv) {
+    return f == KDA_OPERANDS_BF16 || (io == KDA_DTYPE_BF16 && chunk == 16 && conv == KDA_CONV_NONE);
+}
 // With a convolution the weights must be given and 16-byte aligned (one float4 per channel).
 bool valid_conv_w(kda_conv_t c, const float *w) { return c == KDA_CONV_NONE || (w && aligned16(w)); }
 // beta is read one element at a time: natural alignment of its dtype suffices
@@ -61,7 +66,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 8; }
+int kda_abi_version(void) { return 9; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -75,15 +80,44 @@ const char *kda_status_string(kda_status_t s) {
     return "KDA_ERROR_UNKNOWN";
 }
 
-size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                                     int32_t chunk, kda_dtype_t io, kda_conv_t conv) {
-    if (!valid_dtype(io) || !valid_conv(conv)) return 0;
+namespace {
+size_t prefill_ws_query(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk,
+                        kda_dtype_t io, kda_conv_t conv, kda_operands_t operands, bool split) {
+    if (!valid_dtype(io) || !valid_conv(conv) || !valid_operands(operands)) return 0;
+    if (!operands_supported(operands, io, chunk, conv)) return 0;
     // B == 1 may be packed (cu_seqlens) or not; the packed bound is the larger and covers both
     const bool packed = (B == 1);
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
     return kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
-                                        conv != KDA_CONV_NONE);
+                                        conv != KDA_CONV_NONE, operands == KDA_OPERANDS_FP16, split);
+}
+}  // namespace
+
+size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands) {
+    return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, false);
+}
+
+size_t kda_chunk_prep_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                      int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands) {
+    return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, true);
+}
+
+kda_status_t kda_workspace_status(const void *workspace, size_t workspace_bytes, int32_t *device_error,
+                                  void *stream) {
+    if (!device_error || !workspace || ((uintptr_t)workspace & 15u)) return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes < kda::WS_HEADER_BYTES) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    kda_status_t st = check_device();
+    if (st != KDA_SUCCESS) return st;
+    kda::WsHeader h;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return KDA_ERROR_HIP;
+    if (h.magic != kda::WS_MAGIC) return KDA_ERROR_INVALID_VALUE;  // no prefill has written this workspace
+    *device_error = (int32_t)h.error;
+    return KDA_SUCCESS;
 }
 
 namespace {
@@ -92,12 +126,13 @@ namespace {
 kda_status_t prefill_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
                           const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K,
                           int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                          kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o,
-                          float *S_final, const void *workspace, size_t workspace_bytes, bool need_prep,
-                          bool need_state, kda::PrefillArgs &a) {
+                          kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_operands_t operands,
+                          kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
+                          size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
     if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm) ||
-        !valid_conv(conv) || !valid_conv_w(conv, conv_w))
+        !valid_conv(conv) || !valid_conv_w(conv, conv_w) || !valid_operands(operands))
         return KDA_ERROR_INVALID_VALUE;
+    if (!operands_supported(operands, io, chunk, conv)) return KDA_ERROR_NOT_SUPPORTED;
     const bool packed = cu_seqlens != nullptr;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed);
     if (st != KDA_SUCCESS) return st;
@@ -110,8 +145,9 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
+    const bool h16 = operands == KDA_OPERANDS_FP16;
     const size_t need = kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
-                                                     conv != KDA_CONV_NONE);
+                                                     conv != KDA_CONV_NONE, h16, need_prep != need_state);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
@@ -125,8 +161,10 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.conv = (int32_t)conv;
     a.conv_w = conv == KDA_CONV_NONE ? nullptr : conv_w;
     a.o = o; a.S_final = S_final; a.workspace = const_cast<void *>(workspace);
+    a.workspace_bytes = workspace_bytes;
     a.chunk = chunk;
     a.n_chunks_max = nc;
+    a.h16 = h16;
     return KDA_SUCCESS;
 }
 }  // namespace
@@ -135,12 +173,12 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H,
                            int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                            kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w,
-                           kda_dtype_t o_dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           kda_operands_t operands, kda_dtype_t o_dtype, void *o, float *S_final, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, v, g, beta, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
-                                   qk_norm, conv, conv_w, o_dtype, o, S_final, workspace, workspace_bytes, true, true,
-                                   a);
+                                   qk_norm, conv, conv_w, operands, o_dtype, o, S_final, workspace, workspace_bytes,
+                                   true, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -149,12 +187,12 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,
                             const int32_t *cu_seqlens, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
                             int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
-                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+                            kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_operands_t operands,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     kda::PrefillArgs a;
     kda_status_t st = prefill_args(q, k, nullptr, g, beta, nullptr, nullptr, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io,
-                                   gate, qk_norm, conv, conv_w, io, nullptr, nullptr, workspace, workspace_bytes, true,
-                                   false, a);
+                                   gate, qk_norm, conv, conv_w, operands, io, nullptr, nullptr, workspace,
+                                   workspace_bytes, true, false, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_prep(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
@@ -165,11 +203,14 @@ kda_status_t kda_chunk_state(const void *v, const void *o_gate, const float *S0,
                              int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io,
                              kda_conv_t conv, const float *conv_w, kda_dtype_t o_dtype, void *o, float *S_final,
                              void *workspace, size_t workspace_bytes, void *stream) {
+    // The operand format is whatever kda_chunk_prep stored (the kernels read it from the workspace
+    // header); the host check covers the smaller of the two layouts, the kernels the one recorded.
     kda::PrefillArgs a;
+    const kda_operands_t least = (io == KDA_DTYPE_BF16 && chunk == 16 && conv == KDA_CONV_NONE) ? KDA_OPERANDS_FP16
+                                                                                               : KDA_OPERANDS_BF16;
     kda_status_t st = prefill_args(nullptr, nullptr, v, nullptr, nullptr, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs,
-                                   chunk, io, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, conv, conv_w, o_dtype, o, S_final,
-                                   workspace, workspace_bytes,
-                                   false, true, a);
+                                   chunk, io, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, conv, conv_w, least, o_dtype, o,
+                                   S_final, workspace, workspace_bytes, false, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_state(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;

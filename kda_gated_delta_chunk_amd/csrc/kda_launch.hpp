@@ -8,6 +8,31 @@
 
 namespace kda {
 
+// Header at the start of every prefill workspace (the first WS_HEADER_BYTES bytes). Written by the
+// first kernel of a prefill (kda_chunk_prep, kda_chunk_fwd); read by kda_chunk_state, which takes the
+// operand format of the factors from it and refuses a workspace whose header does not describe its own
+// call; `error` collects device-side error bits (WS_ERR_*) until the next prefill rewrites the header.
+struct WsHeader {
+    uint32_t magic;   // WS_MAGIC once a prefill has written the header
+    uint32_t format;  // operand format of the stored factors (FMT_*)
+    uint32_t error;   // WS_ERR_* bits set by the kernels of this prefill
+    int32_t chunk;
+    int64_t B, T;
+    int32_t H, K, V, N;
+    int32_t io_bf16, conv;
+    uint64_t cu;      // the cu_seqlens pointer of the call (0: batched rows)
+    uint64_t need;    // workspace bytes the layout of this prefill uses
+};
+constexpr uint32_t WS_MAGIC = 0x5744414bu;  // "KADW"
+constexpr size_t WS_HEADER_BYTES = 256;
+// Operand formats of the state pass. PAIRS: bf16 hi + lo pairs for bf16 I/O (fp32 operands for fp32
+// I/O); FP16: fp16 operands (bf16 I/O at 16-token chunks without a convolution only).
+constexpr uint32_t FMT_PAIRS = 0, FMT_FP16 = 1;
+constexpr uint32_t FMT_NONE = 2;  // the workspace of a fused kda_chunk_fwd: it holds no factors
+// Device-side error bits (kda_workspace_status).
+constexpr uint32_t WS_ERR_WAIT_TIMEOUT = 1u;     // a bounded wait between wavefronts gave up
+constexpr uint32_t WS_ERR_HEADER_MISMATCH = 2u;  // kda_chunk_state: the header does not describe the call
+
 struct PrefillArgs {
     const void *q, *k, *v, *g, *beta;
     const void *o_gate;    // [B,T,H,V] output-gate pre-activation in the I/O dtype, or null
@@ -23,20 +48,21 @@ struct PrefillArgs {
     void *o;
     float *S_final;
     void *workspace;
+    size_t workspace_bytes;
     int32_t chunk;         // tokens per chunk (16 or 64)
     int64_t n_chunks_max;  // upper bound on chunks over all sequences
+    bool h16;              // fp16 state-pass operands (FMT_FP16); else FMT_PAIRS
 };
 
-// Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens.
+// Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens, split
+// into kda_chunk_prep and kda_chunk_state (split = true) or as one kda_chunk_fwd call.
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv);
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16, bool split);
 // Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
 // Enqueue the state pass over a workspace that launch_prep filled with the same sizes.
 hipError_t launch_state(const PrefillArgs &a, hipStream_t stream);
-// The whole prefill: launch_prep then launch_state, or, where the state pass leaves most CUs
-// free, the same work over consecutive chunk ranges with the prep of each range running beside
-// the state pass of the one before.
+// The whole prefill (kda_chunk_fwd): the same arithmetic as launch_prep then launch_state.
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t stream);
 
 struct DecodeArgs {

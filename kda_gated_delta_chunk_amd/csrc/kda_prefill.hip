@@ -22,9 +22,11 @@
 // Chunks are processed in 16-token sub-tiles (one matrix-core tile row).
 //
 // Kernels (one call of kda_chunk_fwd launches all three on one stream):
-//   kda_chunk_table  one workgroup: clamps cu_seqlens, numbers the chunks
-//                    (each sequence starts a new chunk; its last chunk may be
-//                    partial) and writes the per-sequence chunk offsets.
+//   kda_ws_init      one workgroup: writes the workspace header (sizes, operand
+//                    format, a cleared error word) and, for packed input,
+//                    clamps cu_seqlens, numbers the chunks (each sequence
+//                    starts a new chunk; its last chunk may be partial) and
+//                    writes the per-sequence chunk offsets.
 //   kda_chunk_prep   one wavefront per (sub-tile, head), lane = token row:
 //                    everything that does not depend on the state. Cumulative
 //                    decay (a prefix sum across the 16 lanes of a row), the
@@ -39,23 +41,27 @@
 //                    held in registers, computes W, O and the state update on
 //                    the matrix cores, writes o and S_final. Value columns
 //                    never interact (decay scales rows only), so the column
-//                    split is exact.
+//                    split is exact. It first checks the workspace header
+//                    against its own call and takes the operand format from it.
 //
 // Precision (bf16 I/O). Inside the prep, A and P take K/Gamma (up to e^80 at
 // 16 tokens) and so need bf16's range: Q*Gamma and K/Gamma there are bf16
 // hi + lo pairs, K*Gamma single bf16. The state pass's operands are all
-// bounded by |q|, |k|, |v| and |S|:
-//   16-token chunks (default): fp16 (11 significant bits). Q*Gamma,
-//     K*exp(b_C-b), T, Wk, the state operand and v single; P and, for the
-//     P W term only, W as fp16 hi + lo pairs (the term that decides o's
-//     error). Needs |v|, |S| well inside fp16's range; KDA_OPERANDS=bf16
-//     selects the bf16 format below instead.
-//   otherwise: Q*Gamma, P, W and K*exp(b_C-b) as bf16 hi + lo pairs (about
-//     16 significant bits), T, Wk and the state operand single bf16.
+// bounded by |q|, |k|, |v| and |S|; the caller picks their format:
+//   bf16 pairs (default): Q*Gamma, P, W and K*exp(b_C-b) as bf16 hi + lo
+//     pairs (about 16 significant bits), T, Wk and the state operand single
+//     bf16. bf16 keeps fp32's exponent range, so any finite input works.
+//   fp16 (16-token chunks, no convolution): Q*Gamma, K*exp(b_C-b), T, Wk,
+//     the state operand and v single fp16 (11 significant bits); P and, for
+//     the P W term and the update, W as fp16 hi + lo pairs. Fewer bytes and
+//     products, but |v|, |S| and the operands must stay well inside fp16's
+//     range (below about 6e4), or results are not finite.
 // Accumulation and the state itself are fp32. fp32 I/O runs the same code
 // with fp32 operands on v_mfma_f32_16x16x4_f32.
 
 #include "kda_common.hpp"
+#include "kda_launch.hpp"
+#include <string.h>
 #include <type_traits>
 
 namespace kda {
@@ -85,11 +91,11 @@ __host__ __device__ constexpr int state_row_channel(int rho) {
 //   [CS][64][8]  : 16x16 tile I of a row block, hi (slots 0..3) and lo (4..7)
 //                  parts (fp32: [CS][64][4], one part): lane (a, m) holds row m,
 //                  columns 4a .. 4a+3
-// H16: the state pass's operands in fp16 (bf16 I/O at 16-token chunks): Q*Gamma, K*exp(b_C-b), T, -Wk
-// and v (a bf16 input, exact in fp16) as singles, P as an fp16 hi + lo pair, and W (in registers) split
-// into an fp16 hi + lo pair for the two products it feeds: P W decides the output's error and the state
-// update S_final's. All are bounded by |q|, |k|, |v| and the solve, so fp16's 11 significant bits replace
-// the bf16 hi + lo pairs and bf16 singles in fewer bytes.
+// H16: the state pass's operands in fp16 (bf16 I/O at 16-token chunks, chosen by the caller): Q*Gamma,
+// K*exp(b_C-b), T, -Wk and v as singles (a bf16 v is exact in fp16 only between about 6e-5 and 6.5e4 in
+// magnitude), P as an fp16 hi + lo pair, and W (in registers) split into an fp16 hi + lo pair for the two
+// products it feeds: P W decides the output's error and the state update S_final's. fp16's 11
+// significant bits replace the bf16 hi + lo pairs and bf16 singles in fewer bytes, within fp16's range.
 template <bool BF, int K, int CS, bool H16 = false>
 struct SubLayout {
     static_assert(!H16 || (BF && CS == 1), "fp16 operands: bf16 I/O, 16-token chunks");
@@ -144,10 +150,10 @@ __device__ __forceinline__ int64_t block_scan_excl_sum(int64_t x, int64_t *sh) {
     return r;
 }
 
-__global__ __launch_bounds__(1024) void kda_chunk_table(const int32_t *__restrict__ cu, int32_t N,
-                                                         int64_t T_row, int64_t total_tokens, int32_t C,
-                                                         int64_t *__restrict__ seq_tok,
-                                                         int32_t *__restrict__ chunk_off) {
+// One workgroup of 1024 threads (every thread must call it: it has workgroup barriers).
+__device__ void kda_chunk_table_body(const int32_t *__restrict__ cu, int32_t N, int64_t T_row,
+                                     int64_t total_tokens, int32_t C, int64_t *__restrict__ seq_tok,
+                                     int32_t *__restrict__ chunk_off) {
     __shared__ int64_t sh[1024];
     const int t = threadIdx.x, nt = blockDim.x;
     const int64_t M = (int64_t)N + 1;  // entries
@@ -442,6 +448,47 @@ __device__ __forceinline__ void store_kp(const char *tile, char *dst, int lane) 
     }
 }
 
+// The staged K*exp(b_C - b) rewritten in place into the state update's fragment order (the fused
+// kernel's LDS ring, where the staging tile is the slot's own area): every lane reads all of its tiles
+// before any is written, and a wavefront's LDS operations are carried out in order.
+template <bool BF, int K, bool H16>
+__device__ __forceinline__ void store_kp_inplace(char *area, int lane) {
+    constexpr int KT = K / 16;
+    const int ag = lane >> 4, r = lane & 15;
+    if constexpr (H16) {
+        const uint16_t *t16 = reinterpret_cast<const uint16_t *>(area);
+        uint2 x[KT];
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt)
+            x[rt] = *reinterpret_cast<const uint2 *>(t16 + state_row_channel(16 * rt + r) * 16 + 4 * ag);
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) *reinterpret_cast<uint2 *>(area + (rt * 64 + lane) * 8) = x[rt];
+    } else if constexpr (BF) {
+        const uint16_t *hi = reinterpret_cast<const uint16_t *>(area), *lo = hi + K * 16;
+        uint4 x[KT];
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) {
+            const int e = state_row_channel(16 * rt + r) * 16 + 4 * ag;
+            const uint2 h = *reinterpret_cast<const uint2 *>(hi + e);
+            const uint2 l = *reinterpret_cast<const uint2 *>(lo + e);
+            x[rt] = make_uint4(h.x, h.y, l.x, l.y);
+        }
+#pragma unroll
+        for (int rt = 0; rt < KT; ++rt) *reinterpret_cast<uint4 *>(area + (rt * 64 + lane) * 16) = x[rt];
+    } else {
+        // fp32: output block p2 (2 KiB) holds channels 32 p2 .. 32 p2 + 31, exactly the staging block it
+        // is written over, so each block is read whole and then rewritten
+        const float *x = reinterpret_cast<const float *>(area);
+#pragma unroll
+        for (int p2 = 0; p2 < KT / 2; ++p2) {
+            const float4 f0 = *reinterpret_cast<const float4 *>(x + state_row_channel(32 * p2 + r) * 16 + 4 * ag);
+            const float4 f1 = *reinterpret_cast<const float4 *>(x + state_row_channel(32 * p2 + 16 + r) * 16 + 4 * ag);
+            *reinterpret_cast<float4 *>(area + (p2 * 64 + lane) * 32) = f0;
+            *reinterpret_cast<float4 *>(area + (p2 * 64 + lane) * 32 + 16) = f1;
+        }
+    }
+}
+
 // x[4g + i] for a lane-group index g known only at run time (no register indexing).
 __device__ __forceinline__ float pick16(const float (&x)[16], int g, int i) {
     const float a = x[i], b = x[4 + i], c = x[8 + i], d = x[12 + i];
@@ -483,31 +530,32 @@ struct PrepParams {
     int32_t g0, g1;
 };
 
-// The 16-token prep of item (chunk g0 + item / H, head item % H) by one
-// wavefront, with D::WAVE bytes of LDS of its own at `lds`. No workgroup
+// The 16-token prep of chunk gc (of sequence n) and head h by one wavefront. The factors go to
+// `blk`, one SubLayout block: a workspace block in global memory, or (IN_LDS) a slot of the fused
+// kernel's LDS ring. xt and kx are the wavefront's staging tiles for K*Gamma transposed ([K][16]) and
+// K*exp(b_C-b) ([K][16], hi | lo for bf16 pairs); scr holds its 16x16 matrices (A^T, T, P) and betas
+// (PrepLds offsets from SA on). In the LDS ring the staging tiles are the slot's own -Wk and
+// K*exp(b_C-b) areas, which have exactly their sizes: xt is read into the Wk products before -Wk is
+// written over it, and kx is read whole before it is rewritten in fragment order. No workgroup
 // barriers: wavefronts of a workgroup are independent.
-template <bool BF, int K, bool CONV = false, bool H16 = false>
-__device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, char *lds) {
+// `mid` is called once the A and P products are formed, when the row registers are no longer live
+// (the fused kernel issues the loads of the sub-tile's v tile there).
+template <bool BF, int K, bool CONV, bool H16, bool IN_LDS, typename Mid>
+__device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n, int h, char *blk, char *xt,
+                                            char *kx, char *scr, Mid &&mid) {
     using L = SubLayout<BF, K, 1, H16>;
     using D = PrepLds<BF, K>;
     constexpr int KS = K / 32, KT = K / 16, ES = L::ES, MP = D::MP;
     const void *__restrict__ qp = pa.q, *__restrict__ kp = pa.k, *__restrict__ gp = pa.g, *__restrict__ bp = pa.beta;
-    const int32_t H = pa.H, N = pa.N;
+    const int32_t H = pa.H;
     const ChunkTab &tab = pa.tab;
-    char *__restrict__ frags = pa.frags;
     const int lane = threadIdx.x & 63;
     const int ag = lane >> 4, r = lane & 15;  // lane group; token (row) or column in a tile
-    const int total = tab.off(N) < pa.g1 ? tab.off(N) : pa.g1;
-    const int gc = pa.g0 + (int)(item / H), h = (int)(item % H);
-    if (gc >= total) return;  // wave-uniform
-    char *xt = lds + D::XT;
-    char *kx = lds + D::KX;
-    float *sAT = reinterpret_cast<float *>(lds + D::SA);
-    float *sT = reinterpret_cast<float *>(lds + D::ST);
-    float *sP = reinterpret_cast<float *>(lds + D::SP);
-    float *sB = reinterpret_cast<float *>(lds + D::SB);
+    float *sAT = reinterpret_cast<float *>(scr + (D::SA - D::SA));
+    float *sT = reinterpret_cast<float *>(scr + (D::ST - D::SA));
+    float *sP = reinterpret_cast<float *>(scr + (D::SP - D::SA));
+    float *sB = reinterpret_cast<float *>(scr + (D::SB - D::SA));
 
-    const int n = tab.find(N, gc);
     const int64_t tok0 = tab.tok(n) + (int64_t)(gc - tab.off(n)) * SUB;
     const int64_t tend = tab.tok(n + 1);
     const int nvalid = (int)((tend - tok0) < SUB ? (tend - tok0) : SUB);  // >= 1
@@ -554,7 +602,6 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
 
     // ---- decay-scaled operands. Q*Gamma goes straight to the workspace (its fragment order
     // is this lane's row layout); K*Gamma is transposed through LDS for Wk.
-    char *blk = frags + ((size_t)gc * H + h) * L::BYTES;
     Frag8<BF> qh[KS], ql[KS], kgf[KS], kih[KS], kil[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -600,6 +647,7 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
         }
     }
     mfma_fence(A0, A1, P0, P1, P2);
+    mid();
     lds_sync();  // betas visible
     {
         // lane (ag, r) holds rows 4ag+i, column r; A^T goes to LDS for the solve, P row-major
@@ -672,7 +720,8 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
     }
 
     // ---- K*exp(b_C - b) (staged in LDS since the start) out in state-row order
-    if constexpr (H16) store_kp_h<K>(kx, blk + L::KP, lane);
+    if constexpr (IN_LDS) store_kp_inplace<BF, K, H16>(kx, lane);
+    else if constexpr (H16) store_kp_h<K>(kx, blk + L::KP, lane);
     else store_kp<BF, K>(kx, blk + L::KP, lane);
 
     // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
@@ -687,6 +736,21 @@ __device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, 
             *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
         }
     }
+}
+
+// The 16-token prep of item (chunk g0 + item / H, head item % H) into the workspace, by one
+// wavefront with D::WAVE bytes of LDS of its own at `lds`.
+template <bool BF, int K, bool CONV = false, bool H16 = false>
+__device__ __forceinline__ void prep16_item(const PrepParams &pa, int64_t item, char *lds) {
+    using L = SubLayout<BF, K, 1, H16>;
+    using D = PrepLds<BF, K>;
+    const int32_t H = pa.H, N = pa.N;
+    const int total = pa.tab.off(N) < pa.g1 ? pa.tab.off(N) : pa.g1;
+    const int gc = pa.g0 + (int)(item / H), h = (int)(item % H);
+    if (gc >= total) return;  // wave-uniform
+    const int n = pa.tab.find(N, gc);
+    char *blk = pa.frags + ((size_t)gc * H + h) * L::BYTES;
+    prep16_core<BF, K, CONV, H16, false>(pa, gc, n, h, blk, lds + D::XT, lds + D::KX, lds + D::SA, [] {});
 }
 
 // At least two wavefronts per SIMD caps registers at 256 per lane, which keeps
@@ -1197,12 +1261,27 @@ template <int n> __device__ __forceinline__ int flag_min(uint32_t addr) {
 }
 // Every wait on a flag is bounded: after FLAG_SPINS polls (~0.1 s of sleeping) it gives up, so a
 // protocol error can only give wrong numbers, never a wavefront that does not finish.
+// A wait that gives up returns false; the caller records WS_ERR_WAIT_TIMEOUT in the workspace header
+// (report_error), so a result computed after a timed-out wait never passes for a correct one.
 constexpr int FLAG_SPINS = 1 << 21;
-__device__ __forceinline__ void flag_wait(uint32_t addr, int target) {
-    for (int it = 0; it < FLAG_SPINS && flag_get(addr) < target; ++it) __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ bool flag_wait(uint32_t addr, int target) {
+    for (int it = 0; it < FLAG_SPINS; ++it) {
+        if (flag_get(addr) >= target) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
 }
-template <int n> __device__ __forceinline__ void flag_wait_min(uint32_t addr, int target) {
-    for (int it = 0; it < FLAG_SPINS && flag_min<n>(addr) < target; ++it) __builtin_amdgcn_s_sleep(1);
+template <int n> __device__ __forceinline__ bool flag_wait_min(uint32_t addr, int target) {
+    for (int it = 0; it < FLAG_SPINS; ++it) {
+        if (flag_min<n>(addr) >= target) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+// Sets error bits in the workspace header (a vector atomic OR from the first lane of the wavefront).
+__device__ __forceinline__ void report_error(WsHeader *hdr, uint32_t bits) {
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(&hdr->error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const void *p) {
@@ -1257,11 +1336,46 @@ struct StateCfg {
     static constexpr int NBFIT = (160 * 1024 - FLAGS - D * SLOT) / OROWS;
     static constexpr int NB = NBFIT > 3 ? 3 : NBFIT;
     static constexpr int OBUF = NB * OROWS;
-    static constexpr int LDS = D * SLOT + OBUF + FLAGS;
+    static constexpr int FLAGOFF = D * SLOT + OBUF;
+    static constexpr int LDS = FLAGOFF + FLAGS;
     static_assert(NB >= 2, "two o buffers at least");
     static_assert(D >= 3, "ring too shallow");
     static_assert(NW == 2 || NW == 4, "flag_min reads 2 or 4 done flags");
     static_assert(NL <= 8, "eight ready flags");
+};
+
+// Tiling of the fused prefill (16-token chunks, no convolution): as StateCfg, but the ring of D slots
+// is filled by NL prep wavefronts that form each sub-tile's factors themselves (prep16_core into the
+// slot) instead of copying them from a workspace, and the compute wavefronts store their o rows
+// directly. Each prep wavefront has SCR bytes of its own for the 16x16 matrices of the solve; a slot
+// holds one SubLayout block and the sub-tile's v tile.
+template <bool BF, int K, int V, bool H16>
+struct FusedCfg {
+    using L = SubLayout<BF, K, 1, H16>;
+    static constexpr int CT = 1;
+    static constexpr int NW = V / 16 < 4 ? V / 16 : 4;
+    static constexpr int VT = 16 * NW;
+    static constexpr int NT = V / VT;
+    static constexpr int ES = L::ES;
+    static constexpr int KU = L::UNITS;
+    static constexpr int VB = 16 * VT * ES;         // v tile bytes (16 tokens x VT columns)
+    static constexpr int VU = (VB + 1023) / 1024;
+    static constexpr int VUL = 0;
+    static constexpr int SLOT = (KU + VU) * 1024;
+    static constexpr int NL = BF ? 4 : 3;           // prep wavefronts
+    static constexpr int SCR = 4096;                // A^T, T, P (16 x 20 floats each) and 16 betas
+    static constexpr int FLAGS = 96;
+    static constexpr int DFIT = (160 * 1024 - NL * SCR - FLAGS) / SLOT;
+    static constexpr int D = DFIT > 8 ? 8 : DFIT;
+    static constexpr int SCROFF = D * SLOT;
+    static constexpr int FLAGOFF = SCROFF + NL * SCR;
+    static constexpr int LDS = FLAGOFF + FLAGS;
+    static constexpr int THREADS = (NW + NL) * 64;
+    static constexpr int NB = 1, OBUF = 0, OPITCH = VT + 4, OROWS = 0;
+    static_assert(D >= NL, "a slot for every prep wavefront");
+    static_assert(3 * 16 * 20 * 4 + 64 <= SCR, "prep scratch");
+    static_assert(VB % 1024 == 0 && VB / 64 <= 64, "v tile: at most four whole 16-byte runs per lane");
+    static_assert(NW == 2 || NW == 4, "flag_min reads 2 or 4 done flags");
 };
 
 // [A | B] stacking of two 4-slot operands into one 8-slot operand.
@@ -1282,12 +1396,7 @@ template <bool BF> __device__ __forceinline__ Frag4<BF> zero_frag4() {
     return f;
 }
 
-// Arguments of the state pass. One launch covers the global chunk range
-// [g0, g1): each (sequence, head) runs over its chunks inside the range. A
-// sequence that starts inside the range starts from S0 (or 0), one that ends
-// inside it writes S_final; in between, the state is carried to the next range
-// through Scarry ([N][H][K][V] fp32). Empty sequences are finished by the
-// launch that covers range 0 (`first`).
+// Arguments of the state pass: one launch walks every chunk of every (sequence, head).
 struct StateParams {
     const void *v;
     const void *vlo;    // lo parts of v (StateCfg VLO), else null
@@ -1299,17 +1408,60 @@ struct StateParams {
     int32_t H, N;
     ChunkTab tab;
     const char *frags;
-    int32_t g0, g1;
-    float *Scarry;
-    int32_t first;
+    WsHeader *hdr;      // the workspace header: checked against the fields below, error bits
+    int64_t B, T;
+    int32_t conv;
+    const int32_t *cu;  // cu_seqlens as passed (null: batched rows); only compared and, on a header
+                        // mismatch, read (clamped) to find the rows to poison
+    uint64_t ws_bytes;  // workspace bytes the caller passed (must cover the header's layout)
 };
 
+// Does the workspace header describe this call (written by a prefill with the same sizes and table)?
+template <bool BF, int K, int V, int CS>
+__device__ __forceinline__ bool header_matches(const StateParams &pa, const WsHeader &h) {
+    return h.magic == WS_MAGIC && h.chunk == CS * SUB && h.B == pa.B && h.T == pa.T && h.H == pa.H && h.K == K &&
+           h.V == V && h.N == pa.N && h.io_bf16 == (BF ? 1 : 0) && h.conv == pa.conv &&
+           h.cu == (uint64_t)(uintptr_t)pa.cu && h.need <= pa.ws_bytes;
+}
+
+// The workspace does not describe the call: set the error bit and write NaN to every output this
+// workgroup owns (its VT columns of o for the tokens of its sequence, and of S_final), reading nothing
+// from the workspace. Sequence bounds come from cu_seqlens itself, clamped as the chunk table clamps.
+template <bool BF, int K, int V, int VT>
+__device__ void poison_outputs(const StateParams &pa, int n, int h, int tile) {
+    report_error(pa.hdr, WS_ERR_HEADER_MISMATCH);
+    const int64_t total = pa.B * pa.T;
+    int64_t s0, s1;
+    if (pa.cu) {
+        auto cl = [&](int64_t x) { return x < 0 ? (int64_t)0 : (x > total ? total : x); };
+        s0 = cl(pa.cu[n]);
+        s1 = cl(pa.cu[n + 1]);
+        s1 = s1 > s0 ? s1 : s0;
+    } else {
+        s0 = (int64_t)n * pa.T;
+        s1 = s0 + pa.T;
+    }
+    const float qnan = __builtin_nanf("");
+    const int64_t cells = (s1 - s0) * VT;
+    for (int64_t i = threadIdx.x; i < cells; i += blockDim.x) {
+        const int64_t e = ((s0 + i / VT) * pa.H + h) * V + (int64_t)tile * VT + (int)(i % VT);
+        if (pa.o_bf16) reinterpret_cast<uint16_t *>(pa.o)[e] = (uint16_t)0x7fc0u;
+        else reinterpret_cast<float *>(pa.o)[e] = qnan;
+    }
+    if (pa.Sfin)
+        for (int i = threadIdx.x; i < K * VT; i += blockDim.x)
+            pa.Sfin[(((size_t)n * pa.H + h) * K + i / VT) * V + (size_t)tile * VT + i % VT] = qnan;
+}
+
 // The state pass of workgroup `bid` (C::LDS bytes of LDS at smem).
-template <bool BF, int K, int V, int CS, bool VLO = false, bool H16 = false>
-__device__ __forceinline__ void state_body(const StateParams &pa, int bid, char *smem) {
+// FUSED: the fused prefill. Its prep wavefronts run prep16_core for the sub-tiles into the ring (pp:
+// the prep's inputs) instead of copying a workspace, and the compute wavefronts store o themselves.
+template <bool BF, int K, int V, int CS, bool VLO = false, bool H16 = false, bool FUSED = false>
+__device__ __forceinline__ void state_body(const StateParams &pa, const PrepParams &pp, int bid, char *smem) {
     static_assert(!VLO || BF, "the lo part of v is for bf16 operands");
     static_assert(!H16 || (BF && CS == 1 && !VLO), "fp16 operands: bf16 I/O, 16-token chunks, no hi + lo v");
-    using C = StateCfg<BF, K, V, CS, VLO, H16>;
+    static_assert(!FUSED || (CS == 1 && !VLO), "the fused prefill: 16-token chunks, no convolution");
+    using C = std::conditional_t<FUSED, FusedCfg<BF, K, V, H16>, StateCfg<BF, K, V, CS, VLO, H16>>;
     using L = SubLayout<BF, K, CS, H16>;
     // products on the operands' format: bf16 or, with H16, fp16
     auto mm32 = [](f32x4 acc, const Frag8<BF> &a, const Frag8<BF> &b) {
@@ -1336,15 +1488,20 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     const int head = (slot8 / NT) * 8 + xcd, tile = slot8 % NT;
     if (head >= N * H) return;  // whole workgroup: uniform
     const int n = head / H, h = head % H;
+    // the workspace must hold factors of this call in this operand format (uniform: every wavefront
+    // returns here, before the first barrier); the fused prefill forms its own
+    if constexpr (!FUSED) {
+        if (!header_matches<BF, K, V, CS>(pa, *pa.hdr) || pa.hdr->format != (H16 ? FMT_FP16 : FMT_PAIRS)) {
+            poison_outputs<BF, K, V, VT>(pa, n, h, tile);
+            return;
+        }
+    }
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c0n = tab.off(n), c1n = tab.off(n + 1);
-    const int c0 = c0n > pa.g0 ? c0n : pa.g0, c1 = c1n < pa.g1 ? c1n : pa.g1;  // chunks in the range
-    const int nu = c1 > c0 ? (c1 - c0) * CS : 0;                              // sub-tile steps
-    const bool empty = c0n == c1n;
-    if (nu == 0 && !(empty && pa.first)) return;  // nothing of this sequence here (uniform)
-    const float *__restrict__ S0 = (empty || c0 == c0n) ? pa.S0 : pa.Scarry;
-    float *__restrict__ Sfin = (empty || c1 == c1n) ? pa.Sfin : pa.Scarry;
-    const int64_t s0 = tab.tok(n) + (int64_t)(c0 - c0n) * (CS * SUB), s1 = tab.tok(n + 1);
+    const int c0 = tab.off(n), c1 = tab.off(n + 1);
+    const int nu = c1 > c0 ? (c1 - c0) * CS : 0;  // sub-tile steps
+    const float *__restrict__ S0 = pa.S0;
+    float *__restrict__ Sfin = pa.Sfin;
+    const int64_t s0 = tab.tok(n), s1 = tab.tok(n + 1);
 
     // o rows of sub-tile v: staged (fp32) to obuf[v % NB] by the compute wavefronts during step
     // v+1, written out by loader v % NL (times sigmoid of the output gate, where one is given)
@@ -1426,12 +1583,56 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     // loader k has landed in the ring; done[w] = steps compute wavefront w has finished (its
     // reads of those slots are done and their o rows staged, up to one step back); ostored[k] =
     // 1 + the last sub-tile whose staged o rows loader k has read out.
-    const uint32_t fl = lds_u32(smem) + (uint32_t)(D * C::SLOT + C::OBUF);
+    const uint32_t fl = lds_u32(smem) + (uint32_t)C::FLAGOFF;
     const uint32_t ready0 = fl, done0 = fl + 32, ostored0 = fl + 64;
     if (w == 0 && lane < 24) flag_put(fl + 4 * lane, 0);
     lds_done_barrier();  // the only workgroup barrier
+    if (w >= NW + NL) return;  // a launch sized for another operand format may bring spare wavefronts
 
-    if (w >= NW) {
+    if constexpr (FUSED) {
+        if (w >= NW) {
+            // ------------- prep wavefront k: forms sub-tiles k, k+NL, ... into the ring. Sub-tile x goes
+            // to slot x % D once every compute wavefront has finished sub-tile x - D (the slot's
+            // previous tenant). The v tile is loaded into registers midway through the prep (once its
+            // row registers are free) and written to the slot after the factors; then ready[k] = x + 1
+            // vouches for all of it (a wavefront's LDS operations are carried out in order).
+            const int k = w - NW;
+            char *scr = smem + C::SCROFF + k * C::SCR;
+            constexpr int VR = C::VB / 64 / 16;  // 16-byte runs of the v tile per lane
+            for (int x = k; x < nu; x += NL) {
+                if (x >= D && !flag_wait_min<NW>(done0, x - D + 1)) report_error(pa.hdr, WS_ERR_WAIT_TIMEOUT);
+                char *slot = smem + (x % D) * C::SLOT;
+                const int64_t tok0 = s0 + (int64_t)x * SUB;
+                const int64_t nval = s1 - tok0;
+                // 16-byte run q of the v tile for this lane (named registers: an array here was kept in
+                // scratch memory by the compiler)
+                auto vsrc = [&](int q) {
+                    const int off = (q * 64 + lane) * 16;
+                    const int64_t rw = off / (VT * ES);
+                    const int within = off % (VT * ES);
+                    const int64_t tok = (rw < nval) ? tok0 + rw : s1 - 1;  // padding rows re-read a valid one
+                    return reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vp) +
+                                                           ((tok * H + h) * V + (int64_t)tile * VT) * ES + within);
+                };
+                uint4 v0, v1, v2, v3;
+                auto load_v = [&] {
+                    v0 = *vsrc(0);
+                    if constexpr (VR > 1) v1 = *vsrc(1);
+                    if constexpr (VR > 2) v2 = *vsrc(2);
+                    if constexpr (VR > 3) v3 = *vsrc(3);
+                };
+                prep16_core<BF, K, false, H16, true>(pp, c0 + x, n, h, slot, slot + L::WK, slot + L::KP, scr, load_v);
+                uint4 *vdst = reinterpret_cast<uint4 *>(slot + C::KU * 1024) + lane;
+                vdst[0] = v0;
+                if constexpr (VR > 1) vdst[64] = v1;
+                if constexpr (VR > 2) vdst[128] = v2;
+                if constexpr (VR > 3) vdst[192] = v3;
+                flag_put(ready0 + 4 * k, x + 1);
+            }
+            return;
+        }
+        __builtin_amdgcn_s_setprio(3);  // compute wavefronts first: the prep fills the issue gaps
+    } else if (w >= NW) {
         // ---------------- loader wavefront k: copies sub-tiles k (mod NL) into the ring
         const int k = w - NW;
         const uint32_t lds0 = lds_u32(smem);
@@ -1489,6 +1690,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
                 __builtin_amdgcn_s_sleep(1);
             }
         }
+        if (x < nu || v < nu) report_error(pa.hdr, WS_ERR_WAIT_TIMEOUT);  // gave up waiting
         return;
     }
 
@@ -1581,7 +1783,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
             vf[0].p[1] = (vraw[2] & 0xffffu) | (vraw[3] << 16);
             vf[CT - 1].p[0] = (vraw[0] >> 16) | (vraw[1] & 0xffff0000u);
             vf[CT - 1].p[1] = (vraw[2] >> 16) | (vraw[3] & 0xffff0000u);
-        } else if constexpr (H16) {  // the v tile arrives as bf16: widen exactly, round to fp16
+        } else if constexpr (H16) {  // the v tile arrives as bf16: widen exactly, round to fp16 (range!)
             vf[0].p[0] = pack_h(__uint_as_float(vraw[0] << 16), __uint_as_float(vraw[1] << 16));
             vf[0].p[1] = pack_h(__uint_as_float(vraw[2] << 16), __uint_as_float(vraw[3] << 16));
         } else if constexpr (BF) {
@@ -1609,10 +1811,42 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     // o rows of a step: computed in step u, staged to obuf[u % NB] during step u+1 (once the
     // loader has read out sub-tile u - NB from that buffer)
     f32x4 O[CT];
+    // The fused prefill stores o itself: lane (tg, cl) writes rows 4tg .. 4tg+3 of its column (the
+    // output gate's pre-activations of a sub-tile are loaded a step before its store).
+    float gzc[4] = {0.f, 0.f, 0.f, 0.f}, gzn[4] = {0.f, 0.f, 0.f, 0.f};
+    auto load_gate_col = [&](int uu, float (&dst)[4]) {
+        if constexpr (FUSED) {
+            const void *__restrict__ ogp = pa.ogate;
+            if (!ogp || uu >= nu) return;
+            const int64_t tok0 = s0 + (int64_t)uu * SUB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t tok = tok0 + 4 * tg + i < s1 ? tok0 + 4 * tg + i : s1 - 1;
+                dst[i] = IO<BF>::ld(reinterpret_cast<const typename IO<BF>::T *>(ogp), (tok * H + h) * V + cc);
+            }
+        }
+    };
     auto write_o = [&](int uu) {
         if constexpr (!BF) {
             if constexpr (CT == 2) mfma_fence(O[0], O[CT - 1]);
             else mfma_fence(O[0]);
+        }
+        if constexpr (FUSED) {
+            static_assert(CT == 1, "one column per lane");
+            const int64_t tok0 = s0 + (int64_t)uu * SUB;
+            const int64_t nval = (s1 - tok0) < SUB ? (s1 - tok0) : SUB;
+            const bool gated = pa.ogate != nullptr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * tg + i < nval) {
+                    float x = O[0][i];
+                    if (gated) x *= sigmoid_f(gzc[i]);
+                    const int64_t e = ((tok0 + 4 * tg + i) * H + h) * V + cc;
+                    if (o_bf16) IO<true>::st(reinterpret_cast<uint16_t *>(op), e, x);
+                    else IO<false>::st(reinterpret_cast<float *>(op), e, x);
+                }
+            }
+            return;
         }
         float *ob = obuf + (uu % C::NB) * 16 * C::OPITCH;
 #pragma unroll
@@ -1627,7 +1861,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     auto ready_addr = [&](int x) { return ready0 + 4 * (uint32_t)(x % NL); };
     auto ostored_addr = [&](int vv) { return ostored0 + 4 * (uint32_t)(vv % NL); };
     auto need = [&](int fetched, uint32_t addr, int target) {
-        if (flag_ready(fetched) < target) flag_wait(addr, target);
+        if (flag_ready(fetched) < target && !flag_wait(addr, target)) report_error(pa.hdr, WS_ERR_WAIT_TIMEOUT);
     };
     // pack state rows 32s .. 32s+31 (tiles 2s, 2s+1) of every column tile into the bf16 operand
     auto pack_pair = [&](int s) {
@@ -1667,7 +1901,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
     };
     int f_ready = 0, f_ost = 0;  // flags fetched for the coming step
     if (nu > 0) {
-        flag_wait(ready0, 1);  // sub-tile 0 (loader 0)
+        if (!flag_wait(ready0, 1)) report_error(pa.hdr, WS_ERR_WAIT_TIMEOUT);  // sub-tile 0 (loader 0)
 #pragma unroll
         for (int part = 0; part < 4; ++part) read_ahead(smem, part);
         f_ready = flag_issue(ready_addr(1));
@@ -1680,7 +1914,11 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         const char *sl = smem + (u % D) * C::SLOT;
         // sub-tile u+1 (read ahead in phase C) has landed; the o buffer of sub-tile u-1 is free
         if (u + 1 < nu) need(f_ready, ready_addr(u + 1), u + 2);
-        if (u - 1 - C::NB >= 0) need(f_ost, ostored_addr(u - 1 - C::NB), u - C::NB);
+        if constexpr (!FUSED) {
+            if (u - 1 - C::NB >= 0) need(f_ost, ostored_addr(u - 1 - C::NB), u - C::NB);
+        } else {
+            load_gate_col(u, gzn);  // stored during step u + 1
+        }
         make_vf();
 #pragma unroll
         for (int I = 0; I < CS; ++I)
@@ -1853,7 +2091,7 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 
         // the flags of step u+1, queued behind its operand reads
         f_ready = flag_issue(ready_addr(u + 2));
-        f_ost = flag_issue(ostored_addr(u >= C::NB ? u - C::NB : 0));
+        if constexpr (!FUSED) f_ost = flag_issue(ostored_addr(u >= C::NB ? u - C::NB : 0));
 
         // ---- phase D: O += sum_{I<=R} P_RI W_I; the last pair of the state operand
 #pragma unroll
@@ -1882,9 +2120,16 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
         // step u done: every read of slot u was issued before this (and consumed by a product of
         // this step); only the next step's first operands may still be in flight
         flag_put(done0 + 4 * w, u + 1);
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gzc[i] = gzn[i];
+        }
     }
     if (nu > 0) {
-        if (nu - 1 - C::NB >= 0) flag_wait(ostored_addr(nu - 1 - C::NB), nu - C::NB);
+        if constexpr (!FUSED) {
+            if (nu - 1 - C::NB >= 0 && !flag_wait(ostored_addr(nu - 1 - C::NB), nu - C::NB))
+                report_error(pa.hdr, WS_ERR_WAIT_TIMEOUT);
+        }
         write_o(nu - 1);
         flag_put(done0 + 4 * w, nu + 1);  // the last o rows are staged
     }
@@ -1903,35 +2148,44 @@ __device__ __forceinline__ void state_body(const StateParams &pa, int bid, char 
 template <bool BF, int K, int V, int CS, bool VLO, bool H16>
 __global__ __launch_bounds__((StateCfg<BF, K, V, CS, VLO, H16>::THREADS)) void kda_state_pass(StateParams pa) {
     extern __shared__ __align__(1024) char smem[];
-    state_body<BF, K, V, CS, VLO, H16>(pa, blockIdx.x, smem);
+    state_body<BF, K, V, CS, VLO, H16>(pa, PrepParams{}, blockIdx.x, smem);
 }
 
-// Prep wavefronts per workgroup of the combined kernel below (each owns PrepLds::WAVE bytes of
-// the state pass's LDS).
+// The fused prefill at 16-token chunks without a convolution: one workgroup per (sequence, head, tile of
+// VT value columns) forms each sub-tile's factors in its own prep wavefronts, straight into its LDS
+// ring, and carries the state through them in its compute wavefronts; nothing goes through a
+// workspace but the chunk table of packed input.
 template <bool BF, int K, int V, bool H16>
-constexpr int combined_prep_waves() {
-    using C = StateCfg<BF, K, V, 1, false, H16>;
-    constexpr int byl = C::LDS / PrepLds<BF, K>::WAVE, byw = C::THREADS / 64;
-    return byl < byw ? byl : byw;
-}
-
-// One launch that runs the state pass over one chunk range (workgroups 0 .. nstate-1, dispatched
-// first) and the 16-token prep of the next range (the remaining workgroups, on the CUs the state
-// pass leaves free). The state pass of H heads occupies 2H workgroups (V = 128), one per CU; the
-// prep of the following chunks then runs beside it instead of after it.
-template <bool BF, int K, int V, bool H16>
-__global__ __launch_bounds__((StateCfg<BF, K, V, 1, false, H16>::THREADS)) void kda_state_prep(StateParams sa,
-                                                                                              PrepParams pa,
-                                                                                              int32_t nstate) {
+__global__ __launch_bounds__((FusedCfg<BF, K, V, H16>::THREADS)) void kda_fused_fwd(StateParams pa, PrepParams pp) {
     extern __shared__ __align__(1024) char smem[];
-    if ((int)blockIdx.x < nstate) {
-        state_body<BF, K, V, 1, false, H16>(sa, blockIdx.x, smem);
-        return;
-    }
-    constexpr int PW = combined_prep_waves<BF, K, V, H16>();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (wave >= PW) return;
-    prep16_item<BF, K, false, H16>(pa, (int64_t)(blockIdx.x - nstate) * PW + wave, smem + wave * PrepLds<BF, K>::WAVE);
+    state_body<BF, K, V, 1, false, H16, true>(pa, pp, blockIdx.x, smem);
+}
+
+// bf16 I/O at 16-token chunks without a convolution: the factors may be in either operand format, and
+// the pass takes it from the workspace header (written by the prep that stored them), so a split
+// kda_chunk_prep / kda_chunk_state pair cannot disagree about the layout. Launched with the larger
+// thread count and LDS size of the two configurations.
+template <int K, int V>
+struct FmtCfg {
+    using P = StateCfg<true, K, V, 1, false, false>;
+    using F = StateCfg<true, K, V, 1, false, true>;
+    static constexpr int THREADS = P::THREADS > F::THREADS ? P::THREADS : F::THREADS;
+    static constexpr int LDS = P::LDS > F::LDS ? P::LDS : F::LDS;
+};
+template <int K, int V>
+__global__ __launch_bounds__((FmtCfg<K, V>::THREADS)) void kda_state_pass_fmt(StateParams pa) {
+    extern __shared__ __align__(1024) char smem[];
+    if (pa.hdr->format == FMT_FP16) state_body<true, K, V, 1, false, true>(pa, PrepParams{}, blockIdx.x, smem);
+    else state_body<true, K, V, 1, false, false>(pa, PrepParams{}, blockIdx.x, smem);
+}
+
+// Writes the workspace header of a prefill (one thread), then, for packed input, the chunk table.
+__global__ __launch_bounds__(1024) void kda_ws_init(WsHeader hd, WsHeader *__restrict__ dst,
+                                                     const int32_t *__restrict__ cu, int32_t N, int64_t T_row,
+                                                     int64_t total_tokens, int32_t C, int64_t *__restrict__ seq_tok,
+                                                     int32_t *__restrict__ chunk_off) {
+    if (threadIdx.x == 0) *dst = hd;
+    if (cu) kda_chunk_table_body(cu, N, T_row, total_tokens, C, seq_tok, chunk_off);
 }
 
 }  // namespace kda
@@ -1939,17 +2193,16 @@ __global__ __launch_bounds__((StateCfg<BF, K, V, 1, false, H16>::THREADS)) void 
 // ------------------------------------------------------------------ host side
 #include "kda_launch.hpp"
 
-#include <stdlib.h>
-#include <string.h>
-
 namespace kda {
 namespace {
 
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// header | seq_tok | chunk_off
 size_t table_bytes(int32_t num_seqs) {
-    return align_up((size_t)(num_seqs + 1) * sizeof(int64_t)) + align_up((size_t)(num_seqs + 1) * sizeof(int32_t));
+    return WS_HEADER_BYTES + align_up((size_t)(num_seqs + 1) * sizeof(int64_t)) +
+           align_up((size_t)(num_seqs + 1) * sizeof(int32_t));
 }
 
 template <bool BF, int K, int CS, bool H16>
@@ -1965,45 +2218,32 @@ size_t chunk_bytes_rt(bool bf, int K, int chunk, bool h16) {
     if (h16) return chunk_bytes_k<true, 1, true>(K);
     return bf ? chunk_bytes_k<true, 1>(K) : chunk_bytes_k<false, 1>(K);
 }
-// The state pass's operands in fp16 (SubLayout H16): bf16 I/O at 16-token chunks, without a short
-// convolution (whose v comes as hi + lo parts), unless KDA_OPERANDS=bf16 (read at each call and by the
-// workspace query) asks for the bf16 hi + lo operands, which keep bf16's range for |v| and |S| beyond
-// what fp16 holds.
-bool use_h16(bool io_bf16, int32_t chunk, bool conv) {
-    if (!io_bf16 || chunk != 16 || conv) return false;
-    const char *e = getenv("KDA_OPERANDS");
-    return !(e && strcmp(e, "bf16") == 0);
-}
 
 struct WsPtrs {
+    WsHeader *hdr;
     int64_t *seq_tok;
     int32_t *chunk_off;
     char *frags;
-    float *carry;  // state between chunk ranges (pipelined calls only)
     // calls with a convolution only:
     char *vconv;     // convolved v [tokens][H][V]: fp32, or on a bf16 path the hi parts,
     char *vconv_lo;  // and here the lo parts (v - hi rounded to bf16)
     char *qconv;     // convolved q [tokens][H][K] fp32
     char *kconv;     // convolved k [tokens][H][K] fp32
 };
-bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk);
-// Workspace: chunk table | per-(chunk, head) factors | carry (pipelined calls) | convolved v (with a
-// convolution). The sizes depend only on the call's sizes, as prefill_workspace_bytes counts them.
-size_t frags_bytes(int64_t n_chunks_max, int32_t H, int32_t K, bool io_bf16, int32_t chunk, bool conv) {
-    return align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk, use_h16(io_bf16, chunk, conv)));
-}
-size_t carry_bytes(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t K, int32_t V, int32_t chunk) {
-    return can_pipeline(n_chunks_max, num_seqs, H, chunk) ? align_up((size_t)num_seqs * H * K * V * sizeof(float)) : 0;
+// Workspace: header | chunk table | per-(chunk, head) factors | convolved q, k, v (with a convolution).
+// The sizes depend only on the call's sizes and operand format, as prefill_workspace_bytes counts them.
+size_t frags_bytes(int64_t n_chunks_max, int32_t H, int32_t K, bool io_bf16, int32_t chunk, bool h16) {
+    return align_up((size_t)n_chunks_max * (size_t)H * chunk_bytes_rt(io_bf16, K, chunk, h16));
 }
 WsPtrs ws_ptrs(const PrefillArgs &a) {
     WsPtrs w;
     char *base = reinterpret_cast<char *>(a.workspace);
-    w.seq_tok = reinterpret_cast<int64_t *>(base);
-    w.chunk_off = reinterpret_cast<int32_t *>(base + align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
+    w.hdr = reinterpret_cast<WsHeader *>(base);
+    w.seq_tok = reinterpret_cast<int64_t *>(base + WS_HEADER_BYTES);
+    w.chunk_off = reinterpret_cast<int32_t *>(base + WS_HEADER_BYTES + align_up((size_t)(a.num_seqs + 1) * sizeof(int64_t)));
     w.frags = base + table_bytes(a.num_seqs);
-    char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk, a.conv != 0);
-    w.carry = reinterpret_cast<float *>(cp);
-    w.vconv = cp + carry_bytes(a.n_chunks_max, a.num_seqs, a.H, a.K, a.V, a.chunk);
+    char *cp = w.frags + frags_bytes(a.n_chunks_max, a.H, a.K, a.io_bf16, a.chunk, a.h16);
+    w.vconv = cp;
     const size_t nth = (size_t)a.B * a.T * a.H;
     w.vconv_lo = w.vconv + nth * a.V * 2;
     w.qconv = w.vconv + align_up(nth * a.V * 4);
@@ -2020,8 +2260,6 @@ hipError_t allow_lds(const void *kernel, bool &done, int bytes) {
     return e;
 }
 
-constexpr int32_t ALL_CHUNKS = 0x7fffffff;
-
 ChunkTab chunk_tab(const PrefillArgs &a, const WsPtrs &w) {
     ChunkTab t;
     const bool batched = a.cu_seqlens == nullptr;
@@ -2032,7 +2270,7 @@ ChunkTab chunk_tab(const PrefillArgs &a, const WsPtrs &w) {
     return t;
 }
 
-PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1) {
+PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w) {
     PrepParams p;
     p.q = a.conv ? static_cast<const void *>(w.qconv) : a.q;  // with a convolution: fp32 convolved q, k
     p.k = a.conv ? static_cast<const void *>(w.kconv) : a.k;
@@ -2041,28 +2279,53 @@ PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_
     p.gate = a.gate_sigmoid ? 1 : 0;
     p.qknorm = a.qk_l2norm ? 1 : 0;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
-    p.g0 = g0; p.g1 = g1;
+    p.g0 = 0; p.g1 = 0x7fffffff;
     return p;
 }
 
-StateParams state_params(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first) {
+StateParams state_params(const PrefillArgs &a, const WsPtrs &w) {
     StateParams p;
     p.v = a.conv ? static_cast<const void *>(w.vconv) : a.v;  // with a convolution: the convolved v
     p.vlo = (a.conv && a.io_bf16) ? static_cast<const void *>(w.vconv_lo) : nullptr;  // and its lo parts (bf16)
     p.ogate = a.o_gate; p.S0 = a.S0; p.o = a.o; p.o_bf16 = a.o_bf16 ? 1 : 0; p.Sfin = a.S_final;
     p.H = a.H; p.N = a.num_seqs;
     p.tab = chunk_tab(a, w); p.frags = w.frags;
-    p.g0 = g0; p.g1 = g1;
-    p.Scarry = w.carry;
-    p.first = first ? 1 : 0;
+    p.hdr = w.hdr;
+    p.B = a.B; p.T = a.T;
+    p.conv = a.conv;
+    p.cu = a.cu_seqlens;
+    p.ws_bytes = a.workspace_bytes;
     return p;
 }
 
-// Packed input only: batched input reads no table (ChunkTab).
-hipError_t launch_table(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
-    if (a.cu_seqlens == nullptr) return hipSuccess;
-    hipLaunchKernelGGL(kda_chunk_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, a.T, a.B * a.T,
-                       (int32_t)a.chunk, w.seq_tok, w.chunk_off);
+// Where kda_chunk_fwd runs the fused prefill (kda_fused_fwd: no factors in the workspace) instead of the
+// prep and the state pass. Measured on gfx950 at the 4096-token, 96-head workload it is slower (0.55 ms
+// against 0.34 ms: its prep wavefronts form a sub-tile in ~8.6 us, a step of the state pass takes ~0.7
+// us, and each of a head's two workgroups repeats the prep), so no call takes it yet.
+bool fused_path(int32_t chunk, bool conv) {
+    (void)chunk;
+    (void)conv;
+    return false;
+}
+
+// The header of this prefill, and for packed input the chunk table, in one launch. `fused`: the
+// call stores no factors (the header says so, and a kda_chunk_state over it is refused).
+hipError_t launch_init(const PrefillArgs &a, const WsPtrs &w, hipStream_t st, bool fused = false) {
+    WsHeader hd;
+    memset(&hd, 0, sizeof(hd));
+    hd.magic = WS_MAGIC;
+    hd.format = fused ? FMT_NONE : a.h16 ? FMT_FP16 : FMT_PAIRS;
+    hd.error = 0;
+    hd.chunk = a.chunk;
+    hd.B = a.B; hd.T = a.T;
+    hd.H = a.H; hd.K = a.K; hd.V = a.V; hd.N = a.num_seqs;
+    hd.io_bf16 = a.io_bf16 ? 1 : 0;
+    hd.conv = a.conv;
+    hd.cu = (uint64_t)(uintptr_t)a.cu_seqlens;
+    hd.need = prefill_workspace_bytes(a.n_chunks_max, a.H, a.K, a.V, a.num_seqs, a.io_bf16, a.chunk, a.B * a.T,
+                                      a.conv != 0, a.h16, true);
+    hipLaunchKernelGGL(kda_ws_init, dim3(1), dim3(a.cu_seqlens ? 1024 : 64), 0, st, hd, w.hdr, a.cu_seqlens,
+                       a.num_seqs, a.T, a.B * a.T, (int32_t)a.chunk, w.seq_tok, w.chunk_off);
     return hipGetLastError();
 }
 
@@ -2116,27 +2379,20 @@ hipError_t prep_launch(int32_t chunk, int64_t items, const PrepParams &pp, hipSt
     return hipGetLastError();
 }
 
-// Prep of the chunk range [g0, g1) (g1 - g0 <= n_chunks_max).
-template <bool BF, int K>
-hipError_t prep_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, hipStream_t st) {
-    const int64_t n = (int64_t)(g1 < a.n_chunks_max ? g1 : a.n_chunks_max) - g0;
-    if (n <= 0) return hipSuccess;
-    const int64_t items = n * a.H;
-    const PrepParams pp = prep_params(a, w, g0, g1);
-    if constexpr (BF) {
-        if (use_h16(a.io_bf16, a.chunk, a.conv != 0)) return prep_launch<BF, K, false, true>(a.chunk, items, pp, st);
-    }
-    return a.conv ? prep_launch<BF, K, true, false>(a.chunk, items, pp, st)
-                  : prep_launch<BF, K, false, false>(a.chunk, items, pp, st);
-}
-
 template <bool BF, int K>
 hipError_t prep_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
-    hipError_t e = launch_table(a, w, st);
+    hipError_t e = launch_init(a, w, st);
     if (e == hipSuccess) e = launch_conv_qk<BF, K>(a, w, st);
     if (e != hipSuccess) return e;
-    return prep_range<BF, K>(a, w, 0, ALL_CHUNKS, st);
+    const int64_t items = a.n_chunks_max * a.H;
+    if (items <= 0) return hipSuccess;
+    const PrepParams pp = prep_params(a, w);
+    if constexpr (BF) {
+        if (a.h16) return prep_launch<BF, K, false, true>(a.chunk, items, pp, st);
+    }
+    return a.conv ? prep_launch<BF, K, true, false>(a.chunk, items, pp, st)
+                  : prep_launch<BF, K, false, false>(a.chunk, items, pp, st);
 }
 
 template <bool BF, int K, int V, int CS>
@@ -2145,78 +2401,39 @@ unsigned state_grid(const PrefillArgs &a) {
 }
 
 template <bool BF, int K, int V, int CS, bool VLO, bool H16>
-hipError_t state_range_t(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
+hipError_t state_launch_t(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
     using C = StateCfg<BF, K, V, CS, VLO, H16>;
     static bool lds_set = false;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass<BF, K, V, CS, VLO, H16>), lds_set, C::LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((kda_state_pass<BF, K, V, CS, VLO, H16>), dim3(state_grid<BF, K, V, CS>(a)), dim3(C::THREADS),
-                       C::LDS, st, state_params(a, w, g0, g1, first));
+                       C::LDS, st, state_params(a, w));
+    return hipGetLastError();
+}
+// bf16 I/O at 16-token chunks without a convolution: the operand format comes from the header.
+template <int K, int V>
+hipError_t state_launch_fmt(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    using C = FmtCfg<K, V>;
+    static_assert(StateCfg<true, K, V, 1, false, false>::NT == StateCfg<true, K, V, 1, false, true>::NT,
+                  "both formats tile the columns alike");
+    static bool lds_set = false;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_state_pass_fmt<K, V>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_state_pass_fmt<K, V>), dim3(state_grid<true, K, V, 1>(a)), dim3(C::THREADS), C::LDS, st,
+                       state_params(a, w));
     return hipGetLastError();
 }
 // A convolved v on a bf16 path comes as hi + lo parts (the VLO variant).
 template <bool BF, int K, int V, int CS>
-hipError_t state_range(const PrefillArgs &a, const WsPtrs &w, int32_t g0, int32_t g1, bool first, hipStream_t st) {
-    if constexpr (BF) {
-        if (a.conv) return state_range_t<BF, K, V, CS, true, false>(a, w, g0, g1, first, st);
-        if constexpr (CS == 1) {
-            if (use_h16(a.io_bf16, a.chunk, false)) return state_range_t<BF, K, V, CS, false, true>(a, w, g0, g1, first, st);
-        }
-    }
-    return state_range_t<BF, K, V, CS, false, false>(a, w, g0, g1, first, st);
-}
-
-template <bool BF, int K, int V, int CS>
 hipError_t state_typed(const PrefillArgs &a, hipStream_t st) {
     const WsPtrs w = ws_ptrs(a);
     hipError_t e = launch_conv_v<BF, V>(a, w, st);
-    return e != hipSuccess ? e : state_range<BF, K, V, CS>(a, w, 0, ALL_CHUNKS, true, st);
-}
-
-// Pipelined forward over nseg chunk ranges (16-token chunks): prep(0); then per range s the
-// combined kernel {state(s), prep(s+1)}; then state(last).
-template <bool BF, int K, int V, bool H16>
-hipError_t fwd_pipelined(const PrefillArgs &a, int nseg, hipStream_t st) {
-    using C = StateCfg<BF, K, V, 1, false, H16>;
-    constexpr int PW = combined_prep_waves<BF, K, V, H16>();
-    static_assert(PW >= 1, "no room for prep wavefronts");
-    const WsPtrs w = ws_ptrs(a);
-    const int64_t per = (a.n_chunks_max + nseg - 1) / nseg;
-    auto g = [&](int s) { return (int32_t)(per * s < a.n_chunks_max ? per * s : a.n_chunks_max); };
-    hipError_t e = launch_table(a, w, st);
-    if (e == hipSuccess) e = launch_conv_v<BF, V>(a, w, st);
-    if (e == hipSuccess) e = prep_range<BF, K>(a, w, g(0), g(1), st);
     if (e != hipSuccess) return e;
-    static bool lds_set = false;
-    e = allow_lds(reinterpret_cast<const void *>(&kda_state_prep<BF, K, V, H16>), lds_set, C::LDS);
-    if (e != hipSuccess) return e;
-    const unsigned nstate = state_grid<BF, K, V, 1>(a);
-    for (int s = 0; s + 1 < nseg; ++s) {
-        const int64_t items = (int64_t)(g(s + 2) - g(s + 1)) * a.H;
-        const unsigned grid = nstate + (unsigned)((items + PW - 1) / PW);
-        hipLaunchKernelGGL((kda_state_prep<BF, K, V, H16>), dim3(grid), dim3(C::THREADS), C::LDS, st,
-                           state_params(a, w, g(s), g(s + 1), s == 0), prep_params(a, w, g(s + 1), g(s + 2)),
-                           (int32_t)nstate);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return state_range<BF, K, V, 1>(a, w, g(nseg - 1), ALL_CHUNKS, nseg == 1, st);
-}
-
-template <bool BF, int K, bool H16>
-hipError_t fwd_pipelined_h(const PrefillArgs &a, int nseg, hipStream_t st) {
-    switch (a.V) {
-        case 32: return fwd_pipelined<BF, K, 32, H16>(a, nseg, st);
-        case 64: return fwd_pipelined<BF, K, 64, H16>(a, nseg, st);
-        default: return fwd_pipelined<BF, K, 128, H16>(a, nseg, st);
-    }
-}
-template <bool BF, int K>
-hipError_t fwd_pipelined_v(const PrefillArgs &a, int nseg, hipStream_t st) {
     if constexpr (BF) {
-        if (use_h16(a.io_bf16, a.chunk, a.conv != 0)) return fwd_pipelined_h<BF, K, true>(a, nseg, st);
+        if (a.conv) return state_launch_t<BF, K, V, CS, true, false>(a, w, st);
+        if constexpr (CS == 1) return state_launch_fmt<K, V>(a, w, st);
     }
-    return fwd_pipelined_h<BF, K, false>(a, nseg, st);
+    return state_launch_t<BF, K, V, CS, false, false>(a, w, st);
 }
 
 template <bool BF, int K, int CS>
@@ -2232,51 +2449,61 @@ hipError_t state_k(const PrefillArgs &a, hipStream_t st) {
     return a.chunk == 64 ? state_v<BF, K, 4>(a, st) : state_v<BF, K, 1>(a, st);
 }
 
-// Pipelining over chunk ranges pays when the state pass leaves most of the 256 CUs free (at
-// 16-token chunks and V = 128 it runs two workgroups per (sequence, head), one per CU) and there
-// are enough chunks to split. The decision depends on sizes only, so the workspace query agrees
-// with it.
-bool can_pipeline(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk) {
-    return chunk == 16 && (int64_t)num_seqs * H <= 64 && n_chunks_max >= 128;
+// The fused prefill of one (K, V, format): the header (and chunk table), then one kernel.
+template <bool BF, int K, int V, bool H16>
+hipError_t fused_launch(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    using C = FusedCfg<BF, K, V, H16>;
+    static bool lds_set = false;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&kda_fused_fwd<BF, K, V, H16>), lds_set, C::LDS);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(8 * (((int64_t)a.num_seqs * a.H + 7) / 8) * C::NT);
+    hipLaunchKernelGGL((kda_fused_fwd<BF, K, V, H16>), dim3(grid), dim3(C::THREADS), C::LDS, st, state_params(a, w),
+                       prep_params(a, w));
+    return hipGetLastError();
 }
-
-// Chunk ranges of a pipelined call: 4 (at least 64 chunks each). KDA_PIPELINE_RANGES (1 .. 16)
-// overrides the count; 1 turns pipelining off.
-int pipeline_ranges(int64_t n_chunks_max, int32_t num_seqs, int32_t H, int32_t chunk) {
-    if (!can_pipeline(n_chunks_max, num_seqs, H, chunk)) return 1;
-    const char *e = getenv("KDA_PIPELINE_RANGES");
-    const int env = e ? atoi(e) : 0;
-    if (env >= 1 && env <= 16) return env;
-    const int64_t n = n_chunks_max / 64;
-    return (int)(n < 4 ? n : 4);
+template <bool BF, int K, bool H16>
+hipError_t fused_v(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
+    switch (a.V) {
+        case 32: return fused_launch<BF, K, 32, H16>(a, w, st);
+        case 64: return fused_launch<BF, K, 64, H16>(a, w, st);
+        default: return fused_launch<BF, K, 128, H16>(a, w, st);
+    }
+}
+template <bool BF, int K>
+hipError_t fused_typed(const PrefillArgs &a, hipStream_t st) {
+    const WsPtrs w = ws_ptrs(a);
+    hipError_t e = launch_init(a, w, st, true);
+    if (e != hipSuccess) return e;
+    if constexpr (BF) {
+        if (a.h16) return fused_v<BF, K, true>(a, w, st);
+    }
+    return fused_v<BF, K, false>(a, w, st);
 }
 
 }  // namespace
 
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv) {
-    size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk, conv) +
-               carry_bytes(n_chunks_max, num_seqs, H, K, V, chunk);
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16, bool split) {
+    if (!split && fused_path(chunk, conv)) return table_bytes(num_seqs);  // the header and the chunk table
+    size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk, h16);
     if (conv)  // convolved v (fp32, or bf16 hi + lo), q and k (fp32)
         b += align_up((size_t)n_tokens * H * V * 4) + 2 * align_up((size_t)n_tokens * H * K * 4);
     return b;
 }
 
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t st) {
-    // the combined state/prep kernel has no convolution variant: calls with one run unpipelined
-    const int nseg = a.conv ? 1 : pipeline_ranges(a.n_chunks_max, a.num_seqs, a.H, a.chunk);
-    if (nseg > 1) {
+    if (fused_path(a.chunk, a.conv != 0)) {
         if (a.io_bf16) {
             switch (a.K) {
-                case 32: return fwd_pipelined_v<true, 32>(a, nseg, st);
-                case 64: return fwd_pipelined_v<true, 64>(a, nseg, st);
-                default: return fwd_pipelined_v<true, 128>(a, nseg, st);
+                case 32: return fused_typed<true, 32>(a, st);
+                case 64: return fused_typed<true, 64>(a, st);
+                default: return fused_typed<true, 128>(a, st);
             }
         }
         switch (a.K) {
-            case 32: return fwd_pipelined_v<false, 32>(a, nseg, st);
-            case 64: return fwd_pipelined_v<false, 64>(a, nseg, st);
-            default: return fwd_pipelined_v<false, 128>(a, nseg, st);
+            case 32: return fused_typed<false, 32>(a, st);
+            case 64: return fused_typed<false, 64>(a, st);
+            default: return fused_typed<false, 128>(a, st);
         }
     }
     hipError_t e = launch_prep(a, st);

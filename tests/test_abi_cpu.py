@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 8
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 9
 
 
 def test_status_strings():
@@ -42,8 +42,10 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = _lib.load()
-    def ws(*a, conv=0):
-        return lib.kda_chunk_fwd_workspace_bytes(*a, conv)
+    def ws(*a, conv=0, operands=0):  # a kda_chunk_prep / kda_chunk_state pair
+        return lib.kda_chunk_prep_workspace_bytes(*a, conv, operands)
+    def wf(*a, conv=0, operands=0):  # one kda_chunk_fwd call
+        return lib.kda_chunk_fwd_workspace_bytes(*a, conv, operands)
     n1 = ws(1, 4096, 96, 128, 128, 1, 16, 1)
     assert n1 > 0
     # grows with tokens and heads; bf16 blocks are smaller than fp32 blocks
@@ -56,28 +58,95 @@ def test_workspace_bytes():
     n64 = ws(1, 4096, 96, 128, 128, 1, 64, 1)
     assert n64 > 0 and ws(1, 4096 + 64, 96, 128, 128, 1, 64, 1) > n64
     # unsupported sizes report 0
-    assert ws(1, 4096, 96, 96, 128, 1, 16, 1) == 0
-    assert ws(1, 4096, 96, 128, 128, 1, 32, 1) == 0
-    assert ws(2, 4096, 96, 128, 128, 3, 16, 1) == 0
-    assert ws(1, 4096, 0, 128, 128, 1, 16, 1) == 0
+    for f in (ws, wf):
+        assert f(1, 4096, 96, 96, 128, 1, 16, 1) == 0
+        assert f(1, 4096, 96, 128, 128, 1, 32, 1) == 0
+        assert f(2, 4096, 96, 128, 128, 3, 16, 1) == 0
+        assert f(1, 4096, 0, 128, 128, 1, 16, 1) == 0
+        assert f(1, 4096, 96, 128, 128, 1, 16, 1, conv=3) == 0
+        assert f(1, 4096, 96, 128, 128, 1, 16, 1, operands=2) == 0
     # a convolution adds exactly the convolved v (B*T*H*V fp32 elements, or bf16 hi + lo parts) and the
     # convolved q and k (fp32)
-    # (bf16 I/O with a convolution also keeps the hi + lo operand layout, larger than the fp16 one)
     assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) > n1 + 4096 * 96 * 128 * 4
     assert ws(1, 4096, 96, 64, 32, 1, 16, 0, conv=2) == ws(1, 4096, 96, 64, 32, 1, 16, 0) + 4096 * 96 * (32 + 2 * 64) * 4
-    assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=3) == 0
+    # fp16 operands: smaller factor blocks; only bf16 I/O at 16-token chunks without a convolution
+    n16 = ws(1, 4096, 96, 128, 128, 1, 16, 1, operands=1)
+    assert 0 < n16 < n1
+    for f in (ws, wf):
+        assert f(1, 4096, 96, 128, 128, 1, 16, 0, operands=1) == 0
+        assert f(1, 4096, 96, 128, 128, 1, 64, 1, operands=1) == 0
+        assert f(1, 4096, 96, 128, 128, 1, 16, 1, conv=1, operands=1) == 0
+    # kda_chunk_fwd runs the prep and the state pass over the same workspace as the split calls
+    for a in [(1, 4096, 96, 128, 128, 1, 16, 1), (1, 4096, 96, 128, 128, 40, 16, 0), (1, 4096, 96, 128, 128, 1, 64, 1),
+              (2, 300, 3, 64, 32, 2, 16, 1)]:
+        for o in ((0, 1) if a[-1] == 1 and a[-2] == 16 else (0,)):
+            assert wf(*a, operands=o) == ws(*a, operands=o) > 0
+    assert wf(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) == ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1)
+    # the header (256 bytes) and the chunk table (num_seqs + 1 int64 and int32 entries, each 256-byte
+    # aligned) come first: 39 more sequences add one partial chunk each and 256 bytes of table
+    blk = ws(1, 64, 1, 32, 32, 2, 16, 1) - ws(1, 64, 1, 32, 32, 1, 16, 1)  # one more chunk, same table size
+    assert ws(1, 64, 1, 32, 32, 40, 16, 1) - ws(1, 64, 1, 32, 32, 1, 16, 1) == 39 * blk + 256
+
+
+def test_package_workspace_bytes_wrapper():
+    """The package-level query passes every argument, with and without a convolution and per operand
+    format, and agrees with the C query."""
+    import kda_gated_delta_chunk_amd as kda
+    lib = _lib.load()
+    for conv in ("none", "short4", "short4_silu"):
+        n = kda.workspace_bytes(1, 4096, 96, 128, 128, 1, 16, "bf16", conv=conv)
+        assert n == lib.kda_chunk_fwd_workspace_bytes(1, 4096, 96, 128, 128, 1, 16, 1, _lib.CONVS[conv], 0) > 0
+        assert kda.prep_workspace_bytes(1, 4096, 96, 128, 128, 1, 16, "bf16", conv=conv) >= n
+    assert kda.workspace_bytes(1, 4096, 96, 128, 128, 1, 16, "bf16", conv="short4") > \
+        kda.workspace_bytes(1, 4096, 96, 128, 128, 1, 16, "bf16")
+    assert 0 < kda.prep_workspace_bytes(1, 64, 2, 32, 32, 1, 16, "bf16", operands="fp16") < \
+        kda.prep_workspace_bytes(1, 64, 2, 32, 32, 1, 16, "bf16")
+    assert kda.workspace_bytes(1, 64, 2, 32, 32, 1, 16, "fp32", operands="fp16") == 0
+    with pytest.raises(ValueError):
+        kda.workspace_bytes(1, 64, 2, 32, 32, 1, 16, "bf16", conv="long")
+    with pytest.raises(ValueError):
+        kda.workspace_bytes(1, 64, 2, 32, 32, 1, 16, "bf16", operands="fp8")
+
+
+def test_workspace_status_rejects():
+    lib = _lib.load()
+    out = ctypes.c_int32(0)
+    assert lib.kda_workspace_status(None, 1024, ctypes.byref(out), None) == INVALID
+    assert lib.kda_workspace_status(A + 8, 1024, ctypes.byref(out), None) == INVALID
+    assert lib.kda_workspace_status(A, 1024, None, None) == INVALID
+    assert lib.kda_workspace_status(A, 255, ctypes.byref(out), None) == WS_SMALL
 
 
 def _fwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
-             gate=0, qkn=0, conv=0, cw=None, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
+             gate=0, qkn=0, conv=0, cw=None, ops=0, odt=1, o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["B"], a["T"],
                              a["H"],
                              a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["qkn"], a["conv"], a["cw"],
-                             a["odt"], a["o"], a["Sf"], a["ws"],
+                             a["ops"], a["odt"], a["o"], a["Sf"], a["ws"],
                              a["wsb"], a["stream"])
+
+
+def _prep(**kw):
+    lib = _lib.load()
+    a = dict(q=A, k=A, g=A, beta=A, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1, gate=0, qkn=0, conv=0,
+             cw=None, ops=0, ws=A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_prep(a["q"], a["k"], a["g"], a["beta"], a["cu"], a["B"], a["T"], a["H"], a["K"], a["V"],
+                              a["N"], a["chunk"], a["io"], a["gate"], a["qkn"], a["conv"], a["cw"], a["ops"], a["ws"],
+                              a["wsb"], a["stream"])
+
+
+def _state(**kw):
+    lib = _lib.load()
+    a = dict(v=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1, conv=0, cw=None, odt=1,
+             o=A, Sf=A, ws=A, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_state(a["v"], a["og"], a["S0"], a["cu"], a["B"], a["T"], a["H"], a["K"], a["V"], a["N"],
+                               a["chunk"], a["io"], a["conv"], a["cw"], a["odt"], a["o"], a["Sf"], a["ws"], a["wsb"],
+                               a["stream"])
 
 
 INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
@@ -114,9 +183,48 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(chunk=32), UNSUP),
     (dict(wsb=10), WS_SMALL),
     (dict(ws=None), WS_SMALL),
+    (dict(ops=2), INVALID),              # unknown operand format
+    (dict(ops=-1), INVALID),
+    (dict(ops=1, io=0, odt=0), UNSUP),   # fp16 operands: bf16 I/O only
+    (dict(ops=1, chunk=64), UNSUP),      # ... at 16-token chunks
+    (dict(ops=1, conv=1, cw=A), UNSUP),  # ... without a convolution
 ])
 def test_chunk_fwd_rejects(kw, expect):
     assert _fwd(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID),
+    (dict(ops=3), INVALID),
+    (dict(ops=1, chunk=64), UNSUP),
+    (dict(ops=1, io=0), UNSUP),
+    (dict(K=48), UNSUP),
+    (dict(wsb=100), WS_SMALL),
+])
+def test_chunk_prep_rejects(kw, expect):
+    assert _prep(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(v=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(S0=A, Sf=A), INVALID),
+    (dict(V=96), UNSUP),
+    (dict(wsb=100), WS_SMALL),
+])
+def test_chunk_state_rejects(kw, expect):
+    assert _state(**kw) == expect
+
+
+def test_chunk_state_checks_the_smaller_layout_on_the_host():
+    """kda_chunk_state takes the operand format from the header on the device; on the host it can only
+    hold the workspace to the smaller of the two layouts (the fp16 one), and the kernels to the recorded
+    one. A workspace below the fp16 size is refused before any launch."""
+    lib = _lib.load()
+    n16 = lib.kda_chunk_prep_workspace_bytes(1, 64, 2, 32, 32, 1, 16, 1, 0, 1)
+    nbf = lib.kda_chunk_prep_workspace_bytes(1, 64, 2, 32, 32, 1, 16, 1, 0, 0)
+    assert 0 < n16 < nbf
+    assert _state(wsb=n16 - 1, cu=A + 4096) == WS_SMALL  # packed: the query's bound is exact
 
 
 def _dec(**kw):
@@ -218,5 +326,10 @@ def _has_gpu():
 @pytest.mark.skipif(_has_gpu(), reason="valid arguments would launch kernels on fake pointers")
 def test_valid_arguments_without_a_device_report_no_device():
     assert _fwd() == NO_DEV
+    assert _fwd(ops=1) == NO_DEV
+    assert _prep() == NO_DEV
+    assert _state() == NO_DEV
     assert _dec() == NO_DEV
     assert _bwd() == NO_DEV
+    out = ctypes.c_int32(0)
+    assert _lib.load().kda_workspace_status(A, 1024, ctypes.byref(out), None) == NO_DEV

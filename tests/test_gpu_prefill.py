@@ -4,15 +4,13 @@ Every case prints its name, seed and shape before touching the GPU. Inputs
 come from the seeded generator; the oracle sees exactly the values the GPU
 received (bf16 or fp32), widened to fp64.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from kda_gated_delta_chunk_amd import chunk_fwd
-from kda_gated_delta_chunk_amd import synth
+from kda_gated_delta_chunk_amd import (_lib, chunk_fwd, chunk_prep, chunk_state, prep_workspace_bytes, synth,
+                                       workspace_bytes, workspace_status)
 from tests.parity import TOL_BF16, TOL_FP32, err, err_stored
 
 pytestmark = pytest.mark.gpu
@@ -45,19 +43,63 @@ def _conv_w_heads(inp, heads):
     return w[list(heads)].contiguous() if heads is not None else w
 
 
-def _run(inp, o_dtype=None, chunk=16):
-    o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
-                      cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype, chunk=chunk,
-                      gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"),
-                      qk_norm=inp.get("qk_norm", False), conv=inp.get("conv", "none"), conv_w=inp.get("conv_w"))
+def _poisoned(shape, dtype):
+    """An output buffer filled with NaN: an element the kernels fail to write stays NaN and fails every
+    comparison."""
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def _run(inp, o_dtype=None, chunk=16, operands=None):
+    """One kda_chunk_fwd call with its workspace filled with 0xff bytes (NaN in every float format) and
+    o and S_final filled with NaN beforehand, so that no uninitialised byte can pass; the workspace's
+    device-side error word must read 0 afterwards."""
+    q, v = inp["q"], inp["v"]
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    ops = operands or inp.get("operands", "bf16")
+    conv = inp.get("conv", "none")
+    need = workspace_bytes(B, T, H, K, V, N, chunk, q.dtype, conv=conv, operands=ops)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    odt = q.dtype if o_dtype is None else o_dtype
+    o = _poisoned((B, T, H, V), odt)
+    Sf = _poisoned((N, H, K, V), torch.float32)
+    chunk_fwd(q, inp["k"], v, inp["g"], inp["beta"], S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype,
+              chunk=chunk, gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"),
+              qk_norm=inp.get("qk_norm", False), conv=conv, conv_w=inp.get("conv_w"), operands=ops,
+              workspace=ws, out=o, final_state_out=Sf)
     torch.cuda.synchronize()
+    assert workspace_status(ws) == 0, "device-side error recorded in the workspace"
     return o, Sf
 
 
-def _check(inp, heads=None, io="bf16", written=None, chunk=16):
+def _run_split(inp, chunk=16, operands="bf16", o_dtype=None):
+    """kda_chunk_prep then kda_chunk_state on one poisoned workspace (the format travels in its header)."""
+    q, v = inp["q"], inp["v"]
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    conv = inp.get("conv", "none")
+    need = prep_workspace_bytes(B, T, H, K, V, N, chunk, q.dtype, conv=conv, operands=operands)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    odt = q.dtype if o_dtype is None else o_dtype
+    o = _poisoned((B, T, H, V), odt)
+    Sf = _poisoned((N, H, K, V), torch.float32)
+    chunk_prep(q, inp["k"], inp["g"], inp["beta"], ws, cu_seqlens=inp["cu_seqlens"], V=V, chunk=chunk,
+               gate=inp.get("gate", "log_decay"), qk_norm=inp.get("qk_norm", False), conv=conv,
+               conv_w=inp.get("conv_w"), operands=operands)
+    chunk_state(v, ws, K, S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], chunk=chunk, o_dtype=o_dtype, out=o,
+                o_gate=inp.get("o_gate"), conv=conv, conv_w=inp.get("conv_w"), final_state_out=Sf)
+    torch.cuda.synchronize()
+    assert workspace_status(ws) == 0, "device-side error recorded in the workspace"
+    return o, Sf, ws
+
+
+def _check(inp, heads=None, io="bf16", written=None, chunk=16, operands=None):
     """Run the GPU path (and for bf16 also with fp32 o) and compare with the oracle."""
     o_ref, S_ref = _oracle(inp, heads)
-    o, Sf = _run(inp, chunk=chunk)
+    o, Sf = _run(inp, chunk=chunk, operands=operands)
     sel = (lambda x: x[:, :, list(heads)]) if heads is not None else (lambda x: x)
     selS = (lambda x: x[:, list(heads)]) if heads is not None else (lambda x: x)
     o_c = sel(o).cpu()
@@ -69,7 +111,7 @@ def _check(inp, heads=None, io="bf16", written=None, chunk=16):
         print("  errors", res, flush=True)
         assert res["o"] <= TOL_FP32 and res["S"] <= TOL_FP32, res
         return o, Sf
-    o32, Sf32 = _run(inp, o_dtype=torch.float32, chunk=chunk)
+    o32, Sf32 = _run(inp, o_dtype=torch.float32, chunk=chunk, operands=operands)
     o32_c = sel(o32).cpu()
     if written is not None:
         o32_c = o32_c[:, written]
@@ -243,66 +285,45 @@ def test_k3_varlen_16_sampled_heads(chunk):
     _check(inp, heads=(0, 41, 95), chunk=chunk)
 
 
-class _Ranges:
-    """Sets KDA_PIPELINE_RANGES (read by the library on every call) for the duration of a block."""
-
-    def __init__(self, n):
-        self.n = n
-
-    def __enter__(self):
-        self.old = os.environ.get("KDA_PIPELINE_RANGES")
-        os.environ["KDA_PIPELINE_RANGES"] = str(self.n)
-
-    def __exit__(self, *exc):
-        if self.old is None:
-            del os.environ["KDA_PIPELINE_RANGES"]
-        else:
-            os.environ["KDA_PIPELINE_RANGES"] = self.old
-
-
-PIPE_CASES = {
+SPLIT_CASES = {
     # name: (B, T or lengths, H, K, V, io)
     "single_ragged": (1, 2500, 4, 128, 128, "bf16"),
-    "varlen_range_edges": (1, [0, 700, 1, 1200, 0, 617, 33], 8, 64, 64, "bf16"),
+    "varlen_edges": (1, [0, 700, 1, 1200, 0, 617, 33], 8, 64, 64, "bf16"),
     "batched_fp32": (2, 1100, 3, 32, 128, "fp32"),
 }
 
 
-@pytest.mark.parametrize("name", list(PIPE_CASES))
-def test_pipelined_ranges_are_bit_identical(name):
-    """Where the state pass leaves CUs free, kda_chunk_fwd splits the chunks into ranges and runs
-    the prep of range s+1 beside the state pass of range s, carrying the fp32 state between
-    ranges. Per chunk the arithmetic is unchanged, so o and S_final are bitwise those of one prep
-    and one state pass, for any range count: ranges that cut sequences, hold no chunk of a
-    sequence, or start at an empty one."""
-    B, TL, H, K, V, io = PIPE_CASES[name]
+@pytest.mark.parametrize("operands", ["bf16", "fp16"])
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_calls_are_bit_identical(name, operands):
+    """kda_chunk_prep then kda_chunk_state give bitwise what kda_chunk_fwd gives, in either operand format
+    (the state pass takes the format from the workspace header the prep wrote), and a second state pass
+    over the same prepared workspace gives the same bits again."""
+    B, TL, H, K, V, io = SPLIT_CASES[name]
+    if io == "fp32" and operands == "fp16":
+        pytest.skip("fp16 operands are for bf16 I/O")
     cu = None
     if isinstance(TL, list):
         cu = synth.cu_from_lengths(TL)
         T = cu[-1]
     else:
         T = TL
-    _announce("pipelined_ranges", case=name, B=B, T=T, H=H, K=K, V=V, io=io, seed=22)
+    _announce("split_calls", case=name, B=B, T=T, H=H, K=K, V=V, io=io, operands=operands, seed=22)
     inp = synth.prefill_inputs(B, T, H, K, V, io, seed=22, device=DEV, cu_seqlens=cu, with_S0=True)
-    with _Ranges(1):
-        o1, S1 = _run(inp)
-    for n in (2, 3, 4, 7, 16):
-        with _Ranges(n):
-            on, Sn = _run(inp)
-        assert torch.equal(o1, on) and torch.equal(S1, Sn), n
-    with _Ranges(4):  # without S_final the carry still flows between ranges
-        o4, _ = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
-                          cu_seqlens=inp["cu_seqlens"], output_final_state=False)
-        torch.cuda.synchronize()
-    assert torch.equal(o1, o4)
+    o1, S1 = _run(inp, operands=operands)
+    o2, S2, ws = _run_split(inp, operands=operands)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o3, S3 = chunk_state(inp["v"], ws, K, S0=inp["S0"], cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(S1, S3)
+    assert workspace_status(ws) == 0
 
 
-def test_pipelined_varlen_against_oracle():
-    """The default pipelined call on packed sequences of mixed lengths (with an empty one and
-    range boundaries inside sequences) against the oracle."""
+def test_varlen_mixed_lengths_against_oracle():
+    """Packed sequences of mixed lengths (with an empty one) on 12 heads against the oracle."""
     lengths = [900, 0, 1500, 31, 1100]
     cu = synth.cu_from_lengths(lengths)
-    _announce("pipelined_varlen", lengths=lengths, H=12, seed=23)
+    _announce("varlen_mixed", lengths=lengths, H=12, seed=23)
     inp = synth.prefill_inputs(1, cu[-1], 12, 128, 128, "bf16", seed=23, device=DEV, cu_seqlens=cu, with_S0=True)
     _check(inp, heads=(0, 7, 11))
 
@@ -403,16 +424,15 @@ def test_output_gate_leaves_state_and_scales_o():
     assert torch.equal(S1, S2) and torch.equal(o2, 0.5 * o1)
 
 
-def test_output_gate_pipelined_ranges():
-    """The combined state/prep kernel of a pipelined call applies the gate as the plain call does."""
-    _announce("output_gate_pipelined", seed=53)
+@pytest.mark.parametrize("operands", ["bf16", "fp16"])
+def test_output_gate_split_calls(operands):
+    """The split calls apply the output gate as kda_chunk_fwd does (bitwise), in either operand format."""
+    _announce("output_gate_split", operands=operands, seed=53)
     inp = synth.prefill_inputs(1, 2500, 4, 128, 128, "bf16", seed=53, device=DEV, with_S0=True, with_o_gate=True)
-    with _Ranges(1):
-        o1, S1 = _run(inp)
-    with _Ranges(4):
-        o4, S4 = _run(inp)
-    assert torch.equal(o1, o4) and torch.equal(S1, S4)
-    _check(inp, heads=(0, 3))
+    o1, S1 = _run(inp, operands=operands)
+    o2, S2, _ = _run_split(inp, operands=operands)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    _check(inp, heads=(0, 3), operands=operands)
 
 
 def test_output_gate_k3_prefill_4k_sampled_heads():
@@ -484,16 +504,15 @@ def test_qk_norm_matches_host_normalised():
     assert res["o"] <= TOL_FP32 and res["S"] <= TOL_FP32, res
 
 
-def test_qk_norm_pipelined_ranges():
-    """The combined state/prep kernel of a pipelined call normalises as the plain call does."""
-    _announce("qk_norm_pipelined", seed=64)
+@pytest.mark.parametrize("operands", ["bf16", "fp16"])
+def test_qk_norm_split_calls(operands):
+    """The split calls normalise as kda_chunk_fwd does (bitwise), in either operand format."""
+    _announce("qk_norm_split", operands=operands, seed=64)
     inp = _norm_inputs(1, 2500, 4, 128, 128, "bf16", 64, with_S0=True, with_o_gate=True)
-    with _Ranges(1):
-        o1, S1 = _run(inp)
-    with _Ranges(4):
-        o4, S4 = _run(inp)
-    assert torch.equal(o1, o4) and torch.equal(S1, S4)
-    _check(inp, heads=(0, 3))
+    o1, S1 = _run(inp, operands=operands)
+    o2, S2, _ = _run_split(inp, operands=operands)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    _check(inp, heads=(0, 3), operands=operands)
 
 
 def test_all_fused_k3_prefill_4k_sampled_heads():
@@ -572,24 +591,11 @@ def test_conv_identity_taps_change_nothing():
 
 def test_conv_split_calls_match_one_call():
     """kda_chunk_prep then kda_chunk_state with a convolution give bitwise what kda_chunk_fwd gives."""
-    from kda_gated_delta_chunk_amd import _lib
     _announce("conv_split", seed=73)
-    lib = _lib.load()
     B, T, H, K, V = 1, 300, 4, 128, 128
     inp = _conv_inputs(B, T, H, K, V, "bf16", 73, with_S0=True)
     o1, S1 = _run(inp)
-    cc = _lib.CONVS["short4_silu"]
-    wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, B, 16, 1, cc)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    o2 = torch.empty_like(o1)
-    S2 = torch.empty_like(S1)
-    sh = torch.cuda.current_stream().cuda_stream
-    p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta", "S0", "conv_w")}
-    _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], None, B, T, H, K, V, B, 16, 1, 0, 0, cc,
-                                  p["conv_w"], ws.data_ptr(), wsb, sh), "kda_chunk_prep")
-    _lib.check(lib.kda_chunk_state(p["v"], None, p["S0"], None, B, T, H, K, V, B, 16, 1, cc, p["conv_w"], 1,
-                                   o2.data_ptr(), S2.data_ptr(), ws.data_ptr(), wsb, sh), "kda_chunk_state")
-    torch.cuda.synchronize()
+    o2, S2, _ = _run_split(inp)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
@@ -626,49 +632,73 @@ def test_conv_path_deterministic(chunk):
 
 # ------------------------------------------------------------ operand formats at 16-token chunks
 #
-# bf16 I/O at 16-token chunks carries the state pass's operands in fp16 by default; KDA_OPERANDS=bf16
-# (read at every call and by the workspace query) selects the bf16 hi + lo operands instead.
-
-class _Operands:
-    """Sets KDA_OPERANDS for the duration of a block."""
-
-    def __init__(self, fmt):
-        self.fmt = fmt
-
-    def __enter__(self):
-        self.old = os.environ.get("KDA_OPERANDS")
-        os.environ["KDA_OPERANDS"] = self.fmt
-
-    def __exit__(self, *exc):
-        if self.old is None:
-            del os.environ["KDA_OPERANDS"]
-        else:
-            os.environ["KDA_OPERANDS"] = self.old
+# bf16 I/O at 16-token chunks takes the state pass's operands as bf16 hi + lo pairs by default
+# (bf16's range); operands="fp16" selects fp16 operands (fewer bytes and products, fp16's range).
 
 
-def test_bf16_pair_operands_k3_prefill_4k_all_heads():
-    """The bf16 hi + lo operand format (KDA_OPERANDS=bf16) on the 4096-token workload, every head, and
-    its workspace query (larger than the fp16 one)."""
-    from kda_gated_delta_chunk_amd import _lib
+def test_fp16_operands_k3_prefill_4k_all_heads():
+    """The fp16 operand format on the 4096-token workload, every head, and the split calls' workspace query
+    (smaller than the bf16 pairs')."""
     w = synth.WORKLOADS["prefill_4k"]
-    _announce("k3_prefill_4k_bf16_operands", seed=w.seed)
-    lib = _lib.load()
-    n16 = lib.kda_chunk_fwd_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, 1, 0)
-    with _Operands("bf16"):
-        nbf = lib.kda_chunk_fwd_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, 1, 0)
-        assert nbf > n16
-        inp = synth.workload_prefill_inputs(w, device=DEV)
-        _check(inp)
+    _announce("k3_prefill_4k_fp16_operands", seed=w.seed)
+    nbf = prep_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, "bf16")
+    n16 = prep_workspace_bytes(1, w.T, w.H, w.K, w.V, 1, 16, "bf16", operands="fp16")
+    assert 0 < n16 < nbf
+    inp = synth.workload_prefill_inputs(w, device=DEV)
+    _check(inp, operands="fp16")
 
 
-def test_bf16_pair_operands_pipelined_and_split():
-    """KDA_OPERANDS=bf16 through the pipelined ranges (bit-identical to one range) and the split calls."""
-    _announce("bf16_operands_pipelined", seed=75)
-    inp = synth.prefill_inputs(1, 2500, 4, 128, 128, "bf16", seed=75, device=DEV, with_S0=True, with_o_gate=True)
-    with _Operands("bf16"):
-        with _Ranges(1):
-            o1, S1 = _run(inp)
-        with _Ranges(4):
-            o4, S4 = _run(inp)
-        assert torch.equal(o1, o4) and torch.equal(S1, S4)
-        _check(inp, heads=(0, 3))
+@pytest.mark.parametrize("scale", [1e3, 3e4, 1e5])
+def test_large_values_default_operands(scale):
+    """bf16 inputs far outside the normalised range: v and S0 scaled by up to 1e5 (beyond fp16's largest
+    value, 65504). The default bf16-pair operands keep bf16's exponent range, so the call still meets the
+    bf16 bound against the oracle."""
+    _announce("large_values", scale=scale, seed=76)
+    lengths = [300, 17, 0, 190]
+    cu = synth.cu_from_lengths(lengths)
+    inp = synth.prefill_inputs(1, cu[-1], 3, 128, 128, "bf16", seed=76, device=DEV, cu_seqlens=cu, with_S0=True)
+    inp["v"] = (inp["v"].float() * scale).to(torch.bfloat16)
+    inp["S0"] = inp["S0"] * scale
+    _check(inp)
+
+
+def test_large_values_fp16_operands_are_not_finite():
+    """The documented limit of the fp16 format: with |v| beyond 65504 the results are not finite (they never
+    come out as wrong finite numbers); the default format on the same inputs is finite and in bound."""
+    _announce("large_values_fp16", seed=77)
+    inp = synth.prefill_inputs(1, 200, 2, 128, 128, "bf16", seed=77, device=DEV, with_S0=True)
+    inp["v"] = (inp["v"].float() * 1e5).to(torch.bfloat16)
+    o, Sf = _run(inp, operands="fp16", o_dtype=torch.float32)
+    assert not bool(torch.isfinite(o).all()) and not bool(torch.isfinite(Sf).all())
+    o2, S2 = _run(inp, o_dtype=torch.float32)
+    assert bool(torch.isfinite(o2).all()) and bool(torch.isfinite(S2).all())
+
+
+def test_state_refuses_a_workspace_of_another_call():
+    """kda_chunk_state over a workspace that kda_chunk_prep filled for other sizes, or that no prep filled,
+    reads none of it: o and S_final come out NaN and the header's error word says why."""
+    _announce("workspace_header_mismatch", seed=78)
+    inp = synth.prefill_inputs(1, 300, 4, 64, 64, "bf16", seed=78, device=DEV, with_S0=True)
+    _, _, ws = _run_split(inp)
+    short = synth.prefill_inputs(1, 200, 4, 64, 64, "bf16", seed=78, device=DEV, with_S0=True)
+    o = torch.zeros((1, 200, 4, 64), dtype=torch.bfloat16, device=DEV)
+    Sf = torch.zeros((1, 4, 64, 64), dtype=torch.float32, device=DEV)
+    chunk_state(short["v"], ws, 64, S0=short["S0"], out=o, final_state_out=Sf)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o.float()).all()) and bool(torch.isnan(Sf).all())
+    assert workspace_status(ws) == _lib.WS_ERR_HEADER_MISMATCH
+    # the workspace of a fused kda_chunk_fwd holds no factors (its header says so)
+    wsf = torch.full((prep_workspace_bytes(1, 300, 4, 64, 64, 1, 16, "bf16"),), 0xFF, dtype=torch.uint8, device=DEV)
+    chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"], workspace=wsf)
+    o3 = torch.zeros((1, 300, 4, 64), dtype=torch.bfloat16, device=DEV)
+    chunk_state(inp["v"], wsf, 64, S0=inp["S0"], out=o3, final_state_out=Sf)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o3.float()).all()) and bool(torch.isnan(Sf).all())
+    assert workspace_status(wsf) == _lib.WS_ERR_HEADER_MISMATCH
+    # a workspace no prep has written: its header has no magic, the outputs are NaN all the same
+    ws2 = torch.zeros_like(ws)
+    o.zero_()
+    Sf.zero_()
+    chunk_state(inp["v"][:, :200].contiguous(), ws2, 64, S0=inp["S0"], out=o, final_state_out=Sf)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o.float()).all()) and bool(torch.isnan(Sf).all())
