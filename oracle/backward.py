@@ -36,9 +36,20 @@ the derivative -5 sigmoid(x) (1 - sigmoid(x)). With the output gate (same paragr
 full-rank channel gate on the output, read as o_t * sigmoid(z_t)), the reverse pass takes
 do_t * sigmoid(z_t) as the core output's gradient, and dL/dz_t = do_t * o_t * sigmoid(z_t) (1 - sigmoid(z_t))
 with o_t = S_t^T q_t the core output. The forward states A_t and d_t are kept from a
-plain forward run (no recomputation). Parity of this function is pinned
-against central finite differences of the C forward oracle, exact linearity
-in (v, S0) and in q, and a closed form at beta = 0, g = 0.
+plain forward run (no recomputation).
+
+The prologue of the forward oracle (oracle.chunk_fwd) is taken back through the chain rule as well:
+- the q/k normalisation x_n = r x with r = (|x|^2 + eps)^(-1/2) ("Kimi K3 模型架构解析：KDA、AttnRes 与
+  Stable LatentMoE", section 二.3: the delta rule overwrites exactly for unit-norm keys) has
+  dL/dx = r (dL/dx_n - (x_n . dL/dx_n) x_n);
+- the short convolution y_t = sum_j w_j x_{t-3+j} over the tokens of t's sequence (same page, last
+  paragraph of section 二.3), optionally followed by SiLU z = y sigmoid(y) with dz/dy =
+  sigmoid(y) (1 + y (1 - sigmoid(y))), has dL/dx_s = sum_j w_j dL/dy_{s+3-j} over the t = s+3-j of s's
+  sequence and dL/dw_j = sum_t dL/dy_t x_{t-3+j} over the pairs inside a sequence.
+
+Parity of this function is pinned against central finite differences of the C forward oracle (through
+its own gate, output-gate, normalisation and convolution switches), exact linearity in (v, S0) and in q,
+and a closed form at beta = 0, g = 0.
 """
 from __future__ import annotations
 
@@ -61,9 +72,45 @@ def _sequences(B, T, cu):
     return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
 
 
+def _conv_back(x, w, dz, seq_start, act):
+    """The short convolution's reverse for one tensor of one packed row: x [T, H, D] (the convolution's
+    input), w [H, D, 4], dz [T, H, D] = dL/d(output), seq_start [T]. Returns (dL/dx, dL/dw)."""
+    T = x.shape[0]
+    y = np.zeros_like(x)
+    for t in range(T):
+        for j in range(4):
+            tau = t - 3 + j
+            if tau >= seq_start[t]:
+                y[t] += w[:, :, j] * x[tau]
+    if act == "short4_silu":
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-y))
+        dy = dz * sg * (1.0 + y * (1.0 - sg))
+    else:
+        dy = dz
+    dx = np.zeros_like(x)
+    dw = np.zeros_like(w)
+    for t in range(T):
+        for j in range(4):
+            tau = t - 3 + j
+            if tau >= seq_start[t]:
+                dx[tau] += w[:, :, j] * dy[t]
+                dw[:, :, j] += dy[t] * x[tau]
+    return dx, dw
+
+
+def _norm_back(xn, r, dxn):
+    """The reverse of x_n = r x, r = (|x|^2 + eps)^(-1/2), along the last axis: dL/dx from x_n, r and
+    dL/dx_n."""
+    return r * (dxn - np.sum(xn * dxn, axis=-1, keepdims=True) * xn)
+
+
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gate: str = "log_decay",
-              o_gate=None):
-    """Gradients of (o, S_final) = chunk_fwd(q, k, v, g, beta, S0, cu_seqlens).
+              o_gate=None, qk_norm: bool = False, conv: str = "none", conv_w=None):
+    """Gradients of (o, S_final) = chunk_fwd(q, k, v, g, beta, S0, cu_seqlens, gate=..., o_gate=...,
+    qk_norm=..., conv=..., conv_w=...): with the prologue, q, k and v are the raw inputs the forward
+    convolves and normalises, their gradients are taken back through both, and the result also holds
+    "dconv_w" [H, K + K + V, 4] (with a convolution).
 
     q, k, g: [B, T, H, K]; v, do: [B, T, H, V]; beta: [B, T, H];
     S0, dS_final: [N, H, K, V] or None (zeros). gate: "log_decay" (g is the log-decay) or "scaled_sigmoid"
@@ -76,6 +123,22 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
     q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
     if gate not in ("log_decay", "scaled_sigmoid"):
         raise ValueError("unknown gate %r" % (gate,))
+    if conv not in ("none", "short4", "short4_silu"):
+        raise ValueError("unknown conv %r" % (conv,))
+    if cu_seqlens is not None and hasattr(cu_seqlens, "detach"):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    # the prologue, forward: convolution (with SiLU), then the q/k normalisation
+    q_raw, k_raw, v_raw = q, k, v
+    if conv != "none":
+        from . import _apply_conv
+        q, k, v = _apply_conv(q, k, v, conv, conv_w, cu_seqlens)
+    q_c, k_c = q, k
+    rq = rk = None
+    if qk_norm:
+        from . import L2NORM_EPS
+        rq = 1.0 / np.sqrt(np.sum(q_c * q_c, axis=-1, keepdims=True) + L2NORM_EPS)
+        rk = 1.0 / np.sqrt(np.sum(k_c * k_c, axis=-1, keepdims=True) + L2NORM_EPS)
+        q, k = q_c * rq, k_c * rk
     x_pre = None
     if gate == "scaled_sigmoid":
         from . import scaled_sigmoid_gate
@@ -91,8 +154,6 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
     if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, V) or do.shape != v.shape \
             or beta.shape != (B, T, H):
         raise ValueError("inconsistent input shapes")
-    if cu_seqlens is not None and hasattr(cu_seqlens, "detach"):
-        cu_seqlens = cu_seqlens.detach().cpu().numpy()
     seqs = _sequences(B, T, cu_seqlens)
     N = len(seqs)
     s0 = None if S0 is None else _f64(S0)
@@ -136,4 +197,20 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, gat
     if x_pre is not None:
         sx = 1.0 / (1.0 + np.exp(-x_pre))
         out["dg"] = out["dg"] * (-5.0 * sx * (1.0 - sx))
+    # the prologue, reverse: normalisation, then convolution
+    if qk_norm:
+        for name, xn, r in (("dq", q, rq), ("dk", k, rk)):
+            out[name] = _norm_back(xn, r, out[name])
+    if conv != "none":
+        from . import _seq_starts
+        w = _f64(conv_w)
+        st = _seq_starts(B, T, cu_seqlens)
+        dw = np.zeros_like(w)
+        for name, x, lo, hi in (("dq", q_raw, 0, K), ("dk", k_raw, K, 2 * K), ("dv", v_raw, 2 * K, 2 * K + V)):
+            dx = np.zeros_like(x)
+            for b in range(B):
+                dx[b], dwb = _conv_back(x[b], w[:, lo:hi], out[name][b], st[b], conv)
+                dw[:, lo:hi] += dwb
+            out[name] = dx
+        out["dconv_w"] = dw
     return out

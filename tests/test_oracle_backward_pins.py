@@ -234,3 +234,123 @@ def test_bwd_output_gate_matches_finite_differences():
             flat[i] = old
             fd.reshape(-1)[i] = (lp - lm) / 2e-6
         assert np.max(np.abs(fd - gr[gname])) < 1e-7 * max(1.0, np.max(np.abs(fd))), name
+
+
+PROLOGUE_CASES = [
+    # (qk_norm, conv, cu_seqlens): the normalisation alone, each convolution with and without it, packed
+    # sequences (an empty and a one-token one) so that the history restarts inside the row
+    (True, "none", None),
+    (False, "short4", None),
+    (True, "short4_silu", None),
+    (True, "short4_silu", [0, 4, 4, 5, 9]),
+    (False, "short4", [0, 2, 9]),
+]
+
+
+@pytest.mark.parametrize("qk_norm,conv,cu", PROLOGUE_CASES)
+def test_bwd_prologue_matches_finite_differences(qk_norm, conv, cu):
+    # raw q, k, v go through the short convolution and the normalisation inside the forward oracle: the
+    # gradients of every raw input, of the taps and of the other inputs against central differences of the
+    # forward oracle run with the same switches (both gates on, so every path of the prologue is taken)
+    rng = np.random.default_rng(51)
+    B, T, H, K, V = 1, 9, 2, 3, 2
+    N = B if cu is None else len(cu) - 1
+    x, do, dsf = _inputs(rng, B, T, H, K, V, N)
+    x["q"] = rng.standard_normal((B, T, H, K))
+    x["k"] = rng.standard_normal((B, T, H, K))
+    x["g"] = 2.0 * rng.standard_normal((B, T, H, K))
+    x["z"] = rng.standard_normal((B, T, H, V))
+    x["w"] = 0.7 * rng.standard_normal((H, 2 * K + V, 4))
+    cw = x["w"] if conv != "none" else None
+    kw = dict(gate="scaled_sigmoid", o_gate=x["z"], qk_norm=qk_norm, conv=conv, conv_w=cw)
+    gr = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf, cu, **kw)
+
+    def loss():
+        o, sf = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], cu, **kw)
+        return float(np.sum(o * do) + np.sum(sf * dsf))
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"), ("S0", "dS0"), ("z", "do_gate")]
+    if conv != "none":
+        names.append(("w", "dconv_w"))
+    else:
+        assert "dconv_w" not in gr
+    for name, gname in names:
+        fd = np.zeros_like(x[name])
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 1e-6
+            lp = loss()
+            flat[i] = old - 1e-6
+            lm = loss()
+            flat[i] = old
+            fd.reshape(-1)[i] = (lp - lm) / 2e-6
+        err = np.max(np.abs(fd - gr[gname])) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
+
+
+def test_bwd_prologue_identity_taps_and_no_norm_change_nothing():
+    # taps (0, 0, 0, 1) make the convolution the identity: every gradient equals the plain one's, and the
+    # taps' gradient of the current-token tap is sum_t dL/dy_t x_t
+    rng = np.random.default_rng(52)
+    B, T, H, K, V = 2, 5, 1, 3, 2
+    x, do, dsf = _inputs(rng, B, T, H, K, V)
+    w = np.zeros((H, 2 * K + V, 4))
+    w[..., 3] = 1.0
+    ref = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf)
+    gr = oracle.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf, conv="short4", conv_w=w)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        assert np.allclose(gr[n], ref[n], rtol=0, atol=1e-12), n
+    tap3 = np.concatenate([np.einsum("bthc,bthc->hc", ref["dq"], x["q"]), np.einsum("bthc,bthc->hc", ref["dk"], x["k"]),
+                           np.einsum("bthc,bthc->hc", ref["dv"], x["v"])], axis=1)
+    assert np.allclose(gr["dconv_w"][..., 3], tap3, rtol=1e-12, atol=1e-12)
+
+
+PROLOGUE_MISTAKES = ["norm_without_projection", "silu_derivative_dropped", "no_restart_at_sequences",
+                     "taps_gradient_transposed"]
+
+
+@pytest.mark.parametrize("kind", PROLOGUE_MISTAKES)
+def test_planted_prologue_mistakes_fail_the_finite_difference_pin(kind, monkeypatch):
+    # the prologue's reverse with one planted mistake: some gradient moves off the central differences of the
+    # forward oracle by more than 1e-3 (relative), where the correct reverse is within 1e-7
+    import oracle.backward as ob
+    rng = np.random.default_rng(53)
+    B, T, H, K, V = 1, 7, 2, 3, 2
+    cu = [0, 3, 7]
+    x, do, dsf = _inputs(rng, B, T, H, K, V, 2)
+    x["q"] = rng.standard_normal((B, T, H, K))
+    x["k"] = rng.standard_normal((B, T, H, K))
+    x["w"] = 0.7 * rng.standard_normal((H, 2 * K + V, 4))
+    kw = dict(qk_norm=True, conv="short4_silu", conv_w=x["w"])
+    good_conv_back = ob._conv_back
+    if kind == "norm_without_projection":
+        monkeypatch.setattr(ob, "_norm_back", lambda xn, r, dxn: r * dxn)
+    elif kind == "silu_derivative_dropped":
+        monkeypatch.setattr(ob, "_conv_back", lambda x_, w_, dz, st, act: good_conv_back(x_, w_, dz, st, "short4"))
+    elif kind == "no_restart_at_sequences":
+        monkeypatch.setattr(ob, "_conv_back",
+                            lambda x_, w_, dz, st, act: good_conv_back(x_, w_, dz, np.zeros_like(st), act))
+    else:
+        def flipped(x_, w_, dz, st, act):
+            dx, dw = good_conv_back(x_, w_, dz, st, act)
+            return dx, dw[:, :, ::-1].copy()
+        monkeypatch.setattr(ob, "_conv_back", flipped)
+    gr = ob.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["S0"], dsf, cu, **kw)
+
+    def loss():
+        o, sf = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], cu, **kw)
+        return float(np.sum(o * do) + np.sum(sf * dsf))
+    worst = 0.0
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("w", "dconv_w")):
+        fd = np.zeros_like(x[name])
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 1e-6
+            lp = loss()
+            flat[i] = old - 1e-6
+            lm = loss()
+            flat[i] = old
+            fd.reshape(-1)[i] = (lp - lm) / 2e-6
+        worst = max(worst, np.max(np.abs(fd - gr[gname])) / max(1.0, np.max(np.abs(fd))))
+    assert worst > 1e-3, (kind, worst)
