@@ -22,6 +22,7 @@ durations, against MI355X's published 8 TB/s HBM3E bandwidth.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -60,7 +61,7 @@ class PrefillLeg:
     the three ABI calls (kda_chunk_fwd, and the split kda_chunk_prep / kda_chunk_state) as closures."""
 
     def __init__(self, dev, inp, chunk=16, gate="log_decay", qk_norm=False, conv="none", operands="bf16",
-                 with_split=True):
+                 with_split=True, low_memory=False):
         lib = self.lib = _lib.load()
         self.inp = inp
         gc = _lib.GATES[gate]
@@ -82,7 +83,8 @@ class PrefillLeg:
             cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev)
         cwp = None if cw is None else cw.data_ptr()
         self.cw = cw
-        self.wsb = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc, oc)
+        query = lib.kda_chunk_fwd_min_workspace_bytes if low_memory else lib.kda_chunk_fwd_workspace_bytes
+        self.wsb = query(B, T, H, K, V, N, chunk, 1, cc, oc)
         self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
         self.swsb = lib.kda_chunk_prep_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc, oc) if with_split else 0
         self.sws = torch.empty(self.swsb, dtype=torch.uint8, device=dev) if with_split else None
@@ -436,6 +438,7 @@ def main():
         "workspace_bytes": leg.wsb,
     }
     del leg
+    gc.collect()
 
     def prefill_leg(key, name, inp_, steps=args.steps, warmup=args.warmup, C=16, **kw):
         say("prefill %s: warmup %d, steps %d" % (key, warmup, steps))
@@ -445,9 +448,41 @@ def main():
         out[key], _ = leg_summary(lg, wm, em, name, C=C, split=sp)
         errors[key] = lg.device_error()
         del lg
+        gc.collect()  # the leg's closures refer back to it: free its buffers now
+        torch.cuda.empty_cache()
+
+    if not args.no_large:
+        wv = synth.WORKLOADS["varlen_16"]
+        inpv = synth.workload_prefill_inputs(wv, device=dev)
+        T2 = inpv["q"].shape[1]
+        prefill_leg("varlen_16", "16 packed sequences, lengths uniform in [256, 16384] (seed %d: %d tokens), "
+                                 "H=96 K=V=128 bf16 chunk 16, S0 ~ N(0, 0.02^2), cu_seqlens" % (wv.seed, T2), inpv,
+                    steps=max(3, args.steps // 4), warmup=2)
+        del inpv
+        w1 = synth.WORKLOADS["prefill_1m"]
+        gc.collect()
+        torch.cuda.empty_cache()
+        free, _ = torch.cuda.mem_get_info()
+        io_bytes = w1.T * w1.H * (3 * w1.K + 2 * w1.V + 1) * 2
+        ws_bytes = _lib.load().kda_chunk_fwd_workspace_bytes(1, w1.T, w1.H, w1.K, w1.V, 1, 16, 1, 0, 0)
+        inp1 = synth.workload_prefill_inputs(w1, device=dev)
+        name1 = "B=1 T=1,048,576 H=96 K=V=128 bf16 chunk 16, zero S0"
+        n1 = max(2, min(5, args.steps // 10))
+        if free < io_bytes + ws_bytes + w1.H * w1.K * w1.V * 4 + (4 << 30):
+            out["prefill_1m"] = {"skipped": "two passes need %.0f GB of device memory, %.0f GB free"
+                                            % ((io_bytes + ws_bytes) / 1e9, free / 1e9)}
+        else:
+            prefill_leg("prefill_1m", name1 + ", two passes", inp1, steps=n1, warmup=1, with_split=False)
+        torch.cuda.empty_cache()
+        prefill_leg("prefill_1m_low_memory", name1 + ", low-memory form (one fused kernel)", inp1, steps=n1,
+                    warmup=1, with_split=False, low_memory=True)
+        del inp1
+        torch.cuda.empty_cache()
 
     prefill_leg("chunk64", "prefill B=1 T=4096 H=96 K=V=128 bf16 chunk 64, zero S0", inp, C=64)
     prefill_leg("fp16_operands", "as the headline, fp16 state-pass operands (operands=fp16)", inp, operands="fp16")
+    prefill_leg("low_memory", "as the headline, low-memory form (one fused kernel, workspace = header only)", inp,
+                with_split=False, low_memory=True)
     del inp
     inp = synth.workload_prefill_inputs(w, device=dev, gate_preact=True)
     prefill_leg("gate_fused", "as the headline; g holds the gate pre-activation x, log-decay -5*sigmoid(x) formed "
@@ -464,28 +499,6 @@ def main():
                                                 "q, k, v with SiLU", inp, gate="scaled_sigmoid", qk_norm=True,
                 conv="short4_silu")
     del inp
-    if not args.no_large:
-        wv = synth.WORKLOADS["varlen_16"]
-        inp = synth.workload_prefill_inputs(wv, device=dev)
-        T2 = inp["q"].shape[1]
-        prefill_leg("varlen_16", "16 packed sequences, lengths uniform in [256, 16384] (seed %d: %d tokens), "
-                                 "H=96 K=V=128 bf16 chunk 16, S0 ~ N(0, 0.02^2), cu_seqlens" % (wv.seed, T2), inp,
-                    steps=max(3, args.steps // 4), warmup=2)
-        del inp
-        w1 = synth.WORKLOADS["prefill_1m"]
-        torch.cuda.empty_cache()
-        free, _ = torch.cuda.mem_get_info()
-        io_bytes = w1.T * w1.H * (3 * w1.K + 2 * w1.V + 1) * 2
-        ws_bytes = _lib.load().kda_chunk_fwd_workspace_bytes(1, w1.T, w1.H, w1.K, w1.V, 1, 16, 1, 0, 0)
-        if free < io_bytes + ws_bytes + w1.H * w1.K * w1.V * 4 + (4 << 30):
-            out["prefill_1m"] = {"skipped": "needs %.0f GB of device memory, %.0f GB free"
-                                            % ((io_bytes + ws_bytes) / 1e9, free / 1e9)}
-        else:
-            inp = synth.workload_prefill_inputs(w1, device=dev)
-            prefill_leg("prefill_1m", "B=1 T=1,048,576 H=96 K=V=128 bf16 chunk 16, zero S0", inp,
-                        steps=max(2, min(5, args.steps // 10)), warmup=1, with_split=False)
-            del inp
-        torch.cuda.empty_cache()
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_512"]
         say("decode %s: %d steps" % (wd.name, args.decode_steps))

@@ -156,9 +156,23 @@ int kda_abi_version(void);
 const char *kda_status_string(kda_status_t status);
 
 /*
- * Bytes of device workspace that kda_chunk_fwd needs for these sizes
- * (kda_chunk_fwd_workspace_bytes), and that a kda_chunk_prep / kda_chunk_state
- * pair needs (kda_chunk_prep_workspace_bytes).
+ * Bytes of device workspace for these sizes:
+ *   kda_chunk_fwd_workspace_bytes      kda_chunk_fwd as two passes (the chunk
+ *                                      factors stored per chunk and head,
+ *                                      about 1.4 KB per token and head with
+ *                                      bf16 operands at K = 128): the fast form;
+ *   kda_chunk_fwd_min_workspace_bytes  the least kda_chunk_fwd accepts. At
+ *                                      16-token chunks without a convolution
+ *                                      that is the 256-byte header and the
+ *                                      chunk table: with less than the
+ *                                      two-pass size kda_chunk_fwd runs one
+ *                                      fused kernel that forms each chunk's
+ *                                      factors on chip (same results to
+ *                                      rounding, slower; for sequences whose
+ *                                      factors would not fit in memory).
+ *                                      Otherwise it equals the two-pass size;
+ *   kda_chunk_prep_workspace_bytes     a kda_chunk_prep / kda_chunk_state pair
+ *                                      (the two-pass size).
  *   B, T        batch rows and tokens per row (packed: B = 1, T = total tokens)
  *   num_seqs    number of sequences: B without cu_seqlens, else len(cu_seqlens)-1
  *   chunk, io   as for kda_chunk_fwd
@@ -169,6 +183,8 @@ const char *kda_status_string(kda_status_t status);
  */
 size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                      int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands);
+size_t kda_chunk_fwd_min_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                         int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands);
 size_t kda_chunk_prep_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                       int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands);
 
@@ -226,8 +242,10 @@ kda_status_t kda_workspace_status(const void *workspace, size_t workspace_bytes,
  *             written.
  *   S_final   [num_seqs, H, K, V] fp32, or NULL to skip. May not alias S0.
  *   operands  the state pass's operand format (kda_operands_t).
- *   workspace device scratch of at least kda_chunk_fwd_workspace_bytes();
- *             its first 256 bytes hold a header (sizes, format, error bits).
+ *   workspace device scratch of at least kda_chunk_fwd_min_workspace_bytes();
+ *             with kda_chunk_fwd_workspace_bytes() or more the call runs as
+ *             two passes (faster), with less as one fused kernel. Its first
+ *             256 bytes hold a header (sizes, format, error bits).
  * Errors: INVALID_VALUE (null required pointer, misalignment, non-positive
  *   sizes, B != 1 with cu_seqlens, num_seqs != B without it, size overflow,
  *   unknown dtype, gate, qk_norm, conv or operands, NULL or misaligned conv_w
@@ -265,7 +283,7 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
  *   dereferenced here otherwise) and a layout that fits workspace_bytes;
  *   if it does not, o and S_final are written as NaN and error bit 2 is set
  *   (kda_workspace_status). The workspace may not be modified in between.
- * The results of the pair equal those of kda_chunk_fwd bit for bit.
+ * The results of the pair equal those of kda_chunk_fwd bit for bit (either form).
  * Errors as for kda_chunk_fwd.
  */
 kda_status_t kda_chunk_prep(const void *q, const void *k, const void *g, const void *beta,

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import KDAError, KDA_DTYPE_BF16, KDA_DTYPE_FP32
 
 __all__ = ["chunk_fwd", "chunk_prep", "chunk_state", "chunk_bwd", "decode_step", "workspace_bytes",
-           "prep_workspace_bytes", "workspace_status", "bwd_workspace_bytes", "KDAError", "abi_version"]
+           "min_workspace_bytes", "prep_workspace_bytes", "workspace_status", "bwd_workspace_bytes", "KDAError",
+           "abi_version"]
 
 _DT = {torch.bfloat16: KDA_DTYPE_BF16, torch.float32: KDA_DTYPE_FP32}
 _NAME = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -49,6 +50,16 @@ def workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk
         raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
     return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io),
                                                          _lib.CONVS[conv], _operands_code(operands)))
+
+
+def min_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16",
+                        conv: str = "none", operands: str = "bf16") -> int:
+    """The least workspace kda_chunk_fwd accepts (below workspace_bytes() it runs the fused low-memory
+    form where one exists; 0 = unsupported)."""
+    if conv not in _lib.CONVS:
+        raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
+    return int(_lib.load().kda_chunk_fwd_min_workspace_bytes(B, T, H, K, V, num_seqs, chunk, _io_code(io),
+                                                             _lib.CONVS[conv], _operands_code(operands)))
 
 
 def prep_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, chunk: int = 16, io="bf16",
@@ -117,7 +128,8 @@ def _conv_code(conv: str, conv_w, H: int, C: int, dev) -> int:
 
 def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dtype=None,
               output_final_state: bool = True, workspace=None, out=None, gate: str = "log_decay", o_gate=None,
-              qk_norm: bool = False, conv: str = "none", conv_w=None, operands: str = "bf16", final_state_out=None):
+              qk_norm: bool = False, conv: str = "none", conv_w=None, operands: str = "bf16", final_state_out=None,
+              low_memory: bool = False):
     """Chunked KDA prefill. Returns (o, S_final or None).
 
     o is in ``o_dtype`` (default: the input dtype); S_final is fp32
@@ -132,6 +144,9 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
     ``conv_w`` (fp32 [H, K + K + V, 4]), ahead of the normalisation.
     ``operands``: "bf16" (hi + lo bf16 operand pairs, bf16's range) or "fp16"
     (faster; |v| and the state must stay well inside fp16's range).
+    ``low_memory``: allocate only the least workspace the call accepts, so that
+    it runs as one fused kernel where one exists (no per-chunk factors in memory;
+    slower). A ``workspace`` passed in decides the same way by its size.
     """
     lib = _lib.load()
     dev = q.device
@@ -168,7 +183,8 @@ def chunk_fwd(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk: int = 16, o_dty
         S_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
     oc = _operands_code(operands)
-    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, K, V, N, chunk, io, cc, oc)
+    query = lib.kda_chunk_fwd_min_workspace_bytes if low_memory else lib.kda_chunk_fwd_workspace_bytes
+    need = query(B, T, H, K, V, N, chunk, io, cc, oc)
     if need == 0:
         raise KDAError(2, "kda_chunk_fwd_workspace_bytes(B=%d,T=%d,H=%d,K=%d,V=%d,N=%d,chunk=%d,operands=%s)"
                        % (B, T, H, K, V, N, chunk, operands))

@@ -25,7 +25,8 @@ WS_ERR_WAIT_TIMEOUT = 1
 WS_ERR_HEADER_MISMATCH = 2
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
           3: "KDA_ERROR_WORKSPACE_TOO_SMALL", 4: "KDA_ERROR_NO_DEVICE", 5: "KDA_ERROR_HIP"}
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_prep_workspace_bytes",
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_min_workspace_bytes",
+           "kda_chunk_prep_workspace_bytes",
            "kda_workspace_status", "kda_chunk_fwd", "kda_chunk_prep", "kda_chunk_state", "kda_decode_step",
            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
 
@@ -58,7 +59,8 @@ def load() -> ctypes.CDLL:
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     ci = ctypes.c_int
-    for fn in (lib.kda_chunk_fwd_workspace_bytes, lib.kda_chunk_prep_workspace_bytes):
+    for fn in (lib.kda_chunk_fwd_workspace_bytes, lib.kda_chunk_fwd_min_workspace_bytes,
+               lib.kda_chunk_prep_workspace_bytes):
         fn.argtypes = [i64, i64, i32, i32, i32, i32, i32, ci, ci, ci]
         fn.restype = sz
     lib.kda_workspace_status.argtypes = [vp, sz, ctypes.POINTER(i32), vp]

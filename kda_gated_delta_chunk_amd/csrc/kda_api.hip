@@ -82,15 +82,16 @@ const char *kda_status_string(kda_status_t s) {
 
 namespace {
 size_t prefill_ws_query(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk,
-                        kda_dtype_t io, kda_conv_t conv, kda_operands_t operands, bool split) {
+                        kda_dtype_t io, kda_conv_t conv, kda_operands_t operands, bool least) {
     if (!valid_dtype(io) || !valid_conv(conv) || !valid_operands(operands)) return 0;
     if (!operands_supported(operands, io, chunk, conv)) return 0;
     // B == 1 may be packed (cu_seqlens) or not; the packed bound is the larger and covers both
     const bool packed = (B == 1);
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, chunk, packed) != KDA_SUCCESS) return 0;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
-    return kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
-                                        conv != KDA_CONV_NONE, operands == KDA_OPERANDS_FP16, split);
+    const bool bf = io == KDA_DTYPE_BF16, cv = conv != KDA_CONV_NONE, h16 = operands == KDA_OPERANDS_FP16;
+    return least ? kda::prefill_min_workspace_bytes(nc, H, K, V, num_seqs, bf, chunk, B * T, cv, h16)
+                 : kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, bf, chunk, B * T, cv, h16);
 }
 }  // namespace
 
@@ -99,9 +100,14 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
     return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, false);
 }
 
+size_t kda_chunk_fwd_min_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                         int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands) {
+    return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, true);
+}
+
 size_t kda_chunk_prep_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                       int32_t chunk, kda_dtype_t io, kda_conv_t conv, kda_operands_t operands) {
-    return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, true);
+    return prefill_ws_query(B, T, H, K, V, num_seqs, chunk, io, conv, operands, false);
 }
 
 kda_status_t kda_workspace_status(const void *workspace, size_t workspace_bytes, int32_t *device_error,
@@ -146,8 +152,12 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     if (S0 && S_final && S0 == S_final) return KDA_ERROR_INVALID_VALUE;
     const int64_t nc = max_chunks(B, T, num_seqs, packed, chunk);
     const bool h16 = operands == KDA_OPERANDS_FP16;
-    const size_t need = kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
-                                                     conv != KDA_CONV_NONE, h16, need_prep != need_state);
+    // kda_chunk_fwd (need_prep and need_state) accepts the fused prefill's smaller workspace
+    const size_t need = (need_prep && need_state)
+                            ? kda::prefill_min_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk,
+                                                               B * T, conv != KDA_CONV_NONE, h16)
+                            : kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
+                                                           conv != KDA_CONV_NONE, h16);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;

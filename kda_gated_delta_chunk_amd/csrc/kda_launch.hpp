@@ -54,15 +54,19 @@ struct PrefillArgs {
     bool h16;              // fp16 state-pass operands (FMT_FP16); else FMT_PAIRS
 };
 
-// Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens, split
-// into kda_chunk_prep and kda_chunk_state (split = true) or as one kda_chunk_fwd call.
+// Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens as two
+// passes (kda_chunk_prep, kda_chunk_state; kda_chunk_fwd with at least this much), and the least that
+// kda_chunk_fwd accepts (where the fused prefill applies, the header and the chunk table).
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16, bool split);
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16);
+size_t prefill_min_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                   bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16);
 // Enqueue the chunk-table and chunk-prep kernels (fills the workspace). Sizes are valid.
 hipError_t launch_prep(const PrefillArgs &a, hipStream_t stream);
 // Enqueue the state pass over a workspace that launch_prep filled with the same sizes.
 hipError_t launch_state(const PrefillArgs &a, hipStream_t stream);
-// The whole prefill (kda_chunk_fwd): the same arithmetic as launch_prep then launch_state.
+// The whole prefill (kda_chunk_fwd): launch_prep then launch_state, or, with a workspace smaller than the
+// two passes need, the fused prefill (the same arithmetic in one kernel).
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t stream);
 
 struct DecodeArgs {

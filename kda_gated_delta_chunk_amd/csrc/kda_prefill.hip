@@ -2298,15 +2298,13 @@ StateParams state_params(const PrefillArgs &a, const WsPtrs &w) {
     return p;
 }
 
-// Where kda_chunk_fwd runs the fused prefill (kda_fused_fwd: no factors in the workspace) instead of the
-// prep and the state pass. Measured on gfx950 at the 4096-token, 96-head workload it is slower (0.55 ms
-// against 0.34 ms: its prep wavefronts form a sub-tile in ~8.6 us, a step of the state pass takes ~0.7
-// us, and each of a head's two workgroups repeats the prep), so no call takes it yet.
-bool fused_path(int32_t chunk, bool conv) {
-    (void)chunk;
-    (void)conv;
-    return false;
-}
+// The fused prefill (kda_fused_fwd: no factors in the workspace) exists for 16-token chunks without a
+// convolution. kda_chunk_fwd takes it only when its workspace is too small for the two passes: measured
+// on gfx950 at the 4096-token, 96-head workload it is slower (0.55 ms against 0.34 ms: a prep wavefront
+// needs ~18,000 cycles per sub-tile, ~5,000 of them waiting for its rows, a step of the state pass
+// ~1,950, and each of a head's two workgroups repeats the prep), but it needs only the header and the
+// chunk table, against ~1.4 KB of factors per token and head for the two passes.
+bool fused_possible(int32_t chunk, bool conv) { return chunk == 16 && !conv; }
 
 // The header of this prefill, and for packed input the chunk table, in one launch. `fused`: the
 // call stores no factors (the header says so, and a kda_chunk_state over it is refused).
@@ -2323,7 +2321,7 @@ hipError_t launch_init(const PrefillArgs &a, const WsPtrs &w, hipStream_t st, bo
     hd.conv = a.conv;
     hd.cu = (uint64_t)(uintptr_t)a.cu_seqlens;
     hd.need = prefill_workspace_bytes(a.n_chunks_max, a.H, a.K, a.V, a.num_seqs, a.io_bf16, a.chunk, a.B * a.T,
-                                      a.conv != 0, a.h16, true);
+                                      a.conv != 0, a.h16);
     hipLaunchKernelGGL(kda_ws_init, dim3(1), dim3(a.cu_seqlens ? 1024 : 64), 0, st, hd, w.hdr, a.cu_seqlens,
                        a.num_seqs, a.T, a.B * a.T, (int32_t)a.chunk, w.seq_tok, w.chunk_off);
     return hipGetLastError();
@@ -2482,9 +2480,14 @@ hipError_t fused_typed(const PrefillArgs &a, hipStream_t st) {
 
 }  // namespace
 
+size_t prefill_min_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                   bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16) {
+    if (fused_possible(chunk, conv)) return table_bytes(num_seqs);  // the header and the chunk table
+    return prefill_workspace_bytes(n_chunks_max, H, K, V, num_seqs, io_bf16, chunk, n_tokens, conv, h16);
+}
+
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
-                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16, bool split) {
-    if (!split && fused_path(chunk, conv)) return table_bytes(num_seqs);  // the header and the chunk table
+                               bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16) {
     size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk, h16);
     if (conv)  // convolved v (fp32, or bf16 hi + lo), q and k (fp32)
         b += align_up((size_t)n_tokens * H * V * 4) + 2 * align_up((size_t)n_tokens * H * K * 4);
@@ -2492,7 +2495,9 @@ size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32
 }
 
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t st) {
-    if (fused_path(a.chunk, a.conv != 0)) {
+    const size_t two_pass = prefill_workspace_bytes(a.n_chunks_max, a.H, a.K, a.V, a.num_seqs, a.io_bf16, a.chunk,
+                                                    a.B * a.T, a.conv != 0, a.h16);
+    if (a.workspace_bytes < two_pass && fused_possible(a.chunk, a.conv != 0)) {
         if (a.io_bf16) {
             switch (a.K) {
                 case 32: return fused_typed<true, 32>(a, st);

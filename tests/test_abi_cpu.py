@@ -76,7 +76,19 @@ def test_workspace_bytes():
         assert f(1, 4096, 96, 128, 128, 1, 16, 0, operands=1) == 0
         assert f(1, 4096, 96, 128, 128, 1, 64, 1, operands=1) == 0
         assert f(1, 4096, 96, 128, 128, 1, 16, 1, conv=1, operands=1) == 0
-    # kda_chunk_fwd runs the prep and the state pass over the same workspace as the split calls
+    # the least kda_chunk_fwd accepts: at 16-token chunks without a convolution the header and the chunk
+    # table (the fused kernel), whatever the tokens; otherwise the two-pass size
+    def wm(*a, conv=0, operands=0):
+        return lib.kda_chunk_fwd_min_workspace_bytes(*a, conv, operands)
+    for io in (0, 1):
+        for o in ((0, 1) if io else (0,)):
+            assert wm(1, 4096, 96, 128, 128, 1, 16, io, operands=o) == wm(1, 1 << 20, 96, 128, 128, 1, 16, io,
+                                                                          operands=o) == 256 + 256 + 256
+            assert wm(1, 4096, 96, 128, 128, 40, 16, io, operands=o) == 256 + 512 + 256
+    assert wm(1, 4096, 96, 128, 128, 1, 64, 1) == n64
+    assert wm(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) == ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1)
+    assert wm(1, 4096, 96, 128, 128, 1, 16, 1, operands=2) == 0 and wm(1, 4096, 96, 96, 128, 1, 16, 1) == 0
+    # kda_chunk_fwd as two passes needs the split calls' workspace
     for a in [(1, 4096, 96, 128, 128, 1, 16, 1), (1, 4096, 96, 128, 128, 40, 16, 0), (1, 4096, 96, 128, 128, 1, 64, 1),
               (2, 300, 3, 64, 32, 2, 16, 1)]:
         for o in ((0, 1) if a[-1] == 1 and a[-2] == 16 else (0,)):
@@ -188,6 +200,8 @@ INVALID, UNSUP, WS_SMALL, NO_DEV = 1, 2, 3, 4
     (dict(ops=1, io=0, odt=0), UNSUP),   # fp16 operands: bf16 I/O only
     (dict(ops=1, chunk=64), UNSUP),      # ... at 16-token chunks
     (dict(ops=1, conv=1, cw=A), UNSUP),  # ... without a convolution
+    (dict(wsb=767), WS_SMALL),           # below the header and chunk table of the fused form
+    (dict(wsb=10, chunk=64), WS_SMALL),  # 64-token chunks have no fused form
 ])
 def test_chunk_fwd_rejects(kw, expect):
     assert _fwd(**kw) == expect
@@ -327,6 +341,7 @@ def _has_gpu():
 def test_valid_arguments_without_a_device_report_no_device():
     assert _fwd() == NO_DEV
     assert _fwd(ops=1) == NO_DEV
+    assert _fwd(wsb=768) == NO_DEV  # the fused form's workspace
     assert _prep() == NO_DEV
     assert _state() == NO_DEV
     assert _dec() == NO_DEV

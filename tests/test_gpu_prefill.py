@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import oracle
-from kda_gated_delta_chunk_amd import (_lib, chunk_fwd, chunk_prep, chunk_state, prep_workspace_bytes, synth,
-                                       workspace_bytes, workspace_status)
+from kda_gated_delta_chunk_amd import (_lib, chunk_fwd, chunk_prep, chunk_state, min_workspace_bytes,
+                                       prep_workspace_bytes, synth, workspace_bytes, workspace_status)
 from tests.parity import TOL_BF16, TOL_FP32, err, err_stored
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +69,27 @@ def _run(inp, o_dtype=None, chunk=16, operands=None):
               chunk=chunk, gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"),
               qk_norm=inp.get("qk_norm", False), conv=conv, conv_w=inp.get("conv_w"), operands=ops,
               workspace=ws, out=o, final_state_out=Sf)
+    torch.cuda.synchronize()
+    assert workspace_status(ws) == 0, "device-side error recorded in the workspace"
+    return o, Sf
+
+
+def _run_low_memory(inp, o_dtype=None, operands="bf16"):
+    """kda_chunk_fwd with only the least workspace it accepts: the fused kernel (16-token chunks, no
+    convolution), on poisoned outputs and workspace."""
+    q, v = inp["q"], inp["v"]
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    need = min_workspace_bytes(B, T, H, K, V, N, 16, q.dtype, operands=operands)
+    assert 0 < need < workspace_bytes(B, T, H, K, V, N, 16, q.dtype, operands=operands)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    odt = q.dtype if o_dtype is None else o_dtype
+    o = _poisoned((B, T, H, V), odt)
+    Sf = _poisoned((N, H, K, V), torch.float32)
+    chunk_fwd(q, inp["k"], v, inp["g"], inp["beta"], S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], o_dtype=o_dtype,
+              gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"), qk_norm=inp.get("qk_norm", False),
+              operands=operands, workspace=ws, out=o, final_state_out=Sf)
     torch.cuda.synchronize()
     assert workspace_status(ws) == 0, "device-side error recorded in the workspace"
     return o, Sf
@@ -687,9 +708,12 @@ def test_state_refuses_a_workspace_of_another_call():
     torch.cuda.synchronize()
     assert bool(torch.isnan(o.float()).all()) and bool(torch.isnan(Sf).all())
     assert workspace_status(ws) == _lib.WS_ERR_HEADER_MISMATCH
-    # the workspace of a fused kda_chunk_fwd holds no factors (its header says so)
+    # the workspace of a fused (low-memory) kda_chunk_fwd holds no factors, and its header says so: the
+    # call runs on the leading min_workspace_bytes of a buffer as large as the two passes need, and the
+    # state pass is then handed the whole buffer (its size passes the host check; the header does not)
     wsf = torch.full((prep_workspace_bytes(1, 300, 4, 64, 64, 1, 16, "bf16"),), 0xFF, dtype=torch.uint8, device=DEV)
-    chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"], workspace=wsf)
+    chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S0=inp["S0"],
+              workspace=wsf[:min_workspace_bytes(1, 300, 4, 64, 64, 1, 16, "bf16")])
     o3 = torch.zeros((1, 300, 4, 64), dtype=torch.bfloat16, device=DEV)
     chunk_state(inp["v"], wsf, 64, S0=inp["S0"], out=o3, final_state_out=Sf)
     torch.cuda.synchronize()
@@ -702,3 +726,57 @@ def test_state_refuses_a_workspace_of_another_call():
     chunk_state(inp["v"][:, :200].contiguous(), ws2, 64, S0=inp["S0"], out=o, final_state_out=Sf)
     torch.cuda.synchronize()
     assert bool(torch.isnan(o.float()).all()) and bool(torch.isnan(Sf).all())
+
+
+# ------------------------------------------------------------ the low-memory (fused) form
+#
+# With less workspace than the two passes need (but at least min_workspace_bytes), kda_chunk_fwd runs one
+# kernel whose prep wavefronts form each sub-tile's factors straight into the state pass's LDS ring: the
+# same arithmetic as kda_chunk_prep + kda_chunk_state, so the same bits.
+
+LOWMEM_CASES = {
+    "batched_ragged": (2, 200, 3, 128, 128, "bf16", None),
+    "varlen_edges": (1, [37, 0, 16, 1, 150, 64, 0, 65], 4, 64, 64, "bf16", None),
+    "small_dims": (1, 130, 2, 32, 128, "bf16", None),
+    "fp32": (2, 77, 3, 128, 64, "fp32", None),
+}
+
+
+@pytest.mark.parametrize("operands", ["bf16", "fp16"])
+@pytest.mark.parametrize("name", list(LOWMEM_CASES))
+def test_low_memory_form_is_bit_identical_and_in_bound(name, operands):
+    B, TL, H, K, V, io, _ = LOWMEM_CASES[name]
+    if io == "fp32" and operands == "fp16":
+        pytest.skip("fp16 operands are for bf16 I/O")
+    cu = None
+    if isinstance(TL, list):
+        cu = synth.cu_from_lengths(TL)
+        T = cu[-1]
+    else:
+        T = TL
+    _announce("low_memory", case=name, B=B, T=T, H=H, K=K, V=V, io=io, operands=operands, seed=81)
+    inp = synth.prefill_inputs(B, T, H, K, V, io, seed=81, device=DEV, cu_seqlens=cu, with_S0=True)
+    o1, S1 = _run(inp, operands=operands)
+    o2, S2 = _run_low_memory(inp, operands=operands)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_low_memory_form_with_gates_and_norm():
+    """Both gates and the q/k normalisation through the fused form: bitwise the two-pass result."""
+    _announce("low_memory_prologue", seed=82)
+    inp = _norm_inputs(1, 700, 4, 128, 128, "bf16", 82, with_S0=True, with_o_gate=True)
+    o1, S1 = _run(inp)
+    o2, S2 = _run_low_memory(inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_low_memory_form_k3_prefill_4k_all_heads():
+    """The 4096-token, 96-head workload through the fused form against the oracle (every head)."""
+    w = synth.WORKLOADS["prefill_4k"]
+    _announce("low_memory_prefill_4k", seed=w.seed)
+    inp = synth.workload_prefill_inputs(w, device=DEV)
+    o_ref, S_ref = _oracle(inp)
+    o, Sf = _run_low_memory(inp, o_dtype=torch.float32)
+    res = {"o_fp32": err(o.cpu(), o_ref), "S": err(Sf.cpu(), S_ref)}
+    print("  errors", res, flush=True)
+    assert res["o_fp32"] <= TOL_BF16 and res["S"] <= TOL_BF16, res

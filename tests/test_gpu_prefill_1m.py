@@ -1,8 +1,10 @@
 """Million-token prefill (B=1, T=1,048,576, H=96, K=V=128, bf16, chunk 16) against the oracle.
 
 One kda_chunk_fwd call over the whole sequence (about 129 GB of q/k/v/g/o plus a
-142 GB workspace in HBM). The oracle cannot redo all 96 heads end to end in a
-test's time, so the check has two parts:
+142 GB workspace in HBM), and the same call in its low-memory form (one fused
+kernel, no workspace beyond a header), which must give the same bits. The
+oracle cannot redo all 96 heads end to end in a test's time, so the check has
+two parts:
 
 * four seeded heads end to end: the fp64 recurrence is streamed over blocks of
   65,536 tokens, carrying its state from block to block, and every output row
@@ -55,7 +57,14 @@ def test_k3_prefill_1m():
     _say("  inputs generated")
     o, Sf = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], chunk=w.chunk)
     torch.cuda.synchronize()
-    _say("  gpu call done")
+    _say("  gpu call done (two passes)")
+    # the low-memory form (one fused kernel, no per-chunk factors in memory) gives the same bits
+    o2, Sf2 = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], chunk=w.chunk, low_memory=True)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o, o2)) and bool(torch.equal(Sf, Sf2))
+    _say("  gpu call done (low-memory form): bitwise equal %s" % same)
+    assert same
+    del o2, Sf2
     T = w.T
 
     # ---- four heads end to end, oracle streamed over token blocks
