@@ -205,14 +205,15 @@ def time_backward(w, steps, warmup, dev):
                                                                     torch.empty((B, T, H), **f32)]
     dq, dk, dg, dv, db = (t.data_ptr() for t in outs)
     dS0 = torch.empty((B, H, K, V), **f32)
-    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B)
+    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B, 0, 0)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def bwd():
         _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, None, do.data_ptr(),
-                                     None, B, T, H, K, V, B, 1, 0, dq, dk, dv, dg, db, None, dS0.data_ptr(),
+                                     None, B, T, H, K, V, B, 1, 0, 0, 0, None, dq, dk, dv, dg, db, None, None,
+                                     dS0.data_ptr(),
                                      ws.data_ptr(), wsb,
                                      stream.cuda_stream), "kda_chunk_bwd")
 

@@ -332,8 +332,17 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   dg_t = rowsum((G - k_t dv_t^T) * A_t);  G = diag(exp(g_t)) (G - k_t dv_t^T)
  * where A_t = diag(exp(g_t)) S_{t-1} and u = A_t^T k_t; dL/dS0 is the last G.
  *   q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]   dtype `io`, the
- *           forward's inputs; g as `gate` says, as for kda_chunk_fwd (no
- *           norm or convolution options here)
+ *           forward's raw inputs; g as `gate` says, q, k and v as `conv` and
+ *           `qk_norm` say, as for kda_chunk_fwd
+ *   conv_w  fp32 [H, K + K + V, 4] when conv != KDA_CONV_NONE (else ignored)
+ * With a prologue (qk_norm or conv) the gradients are carried on through it
+ * (chain rule, fp32): the normalisation x_n = r x, r = (|x|^2 + 1e-6)^(-1/2),
+ * gives dL/dx = r (dL/dx_n - (x_n . dL/dx_n) x_n); the convolution
+ * y_t = sum_j w_j x_{t-3+j} within t's sequence (then z = y, or SiLU(y) with
+ * dL/dy = dL/dz sigmoid(y) (1 + y (1 - sigmoid(y)))) gives
+ * dL/dx_s = sum_j w_j dL/dy_{s+3-j} over the tokens of s's sequence and
+ * dL/dw_j = sum_t dL/dy_t x_{t-3+j}. dq, dk and dv are then with respect to
+ * the raw q, k and v.
  *   o_gate  [B, T, H, V] dtype `io` or NULL: the output gate's pre-activation
  *           z of the forward (o = core output * sigmoid(z)); with it, d_o is
  *           taken through the gate and d_o_gate receives dL/dz
@@ -347,23 +356,31 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *           dL/dlogdecay * -5 sigmoid(x) (1 - sigmoid(x))); rows of tokens
  *           outside every sequence are not written
  *   d_o_gate [B, T, H, V] fp32: dL/dz, required with o_gate (else ignored)
+ *   d_conv_w [H, K + K + V, 4] fp32: dL/d(conv_w), required with a
+ *           convolution (written also when T == 0: zeros), else ignored
  *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
- *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs):
- *           the state every 8 tokens of every sequence and head (K * V * 4
- *           bytes each) plus per-16-column partial sums of dq, dk, dg and
- *           dbeta (V / 16 * B * T * H * (3K + 1) * 4 bytes); 0 means the sizes
- *           are invalid
+ *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
+ *           qk_norm, conv): the state every 8 tokens of every sequence and
+ *           head (K * V * 4 bytes each) plus per-16-column partial sums of dq,
+ *           dk, dg and dbeta (V / 16 * B * T * H * (3K + 1) * 4 bytes); with a
+ *           prologue also the prologue's fp32 outputs and the recurrence's
+ *           gradients with respect to them (4 B T H K floats, plus 2 B T H V
+ *           with a convolution), 2 B T H norm factors with qk_norm and the
+ *           taps' partial sums (ceil(B T / 64) H (2K + V) 4 floats) with a
+ *           convolution; 0 means the sizes or options are invalid
  * The forward states are recomputed from the inputs; nothing from a forward
  * call is needed. All arithmetic is fp32, any finite g is accepted, and the
  * result is deterministic (fixed summation order). Outputs may not alias the
  * inputs or each other. Errors as for kda_chunk_fwd (chunk does not apply).
  */
-size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs);
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     kda_qk_norm_t qk_norm, kda_conv_t conv);
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
                            const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, float *dq, float *dk, float *dv,
-                           float *dg, float *dbeta, float *d_o_gate, float *dS0, void *workspace,
+                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm,
+                           kda_conv_t conv, const float *conv_w, float *dq, float *dk, float *dv, float *dg,
+                           float *dbeta, float *d_o_gate, float *d_conv_w, float *dS0, void *workspace,
                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus

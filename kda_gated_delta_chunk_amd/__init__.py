@@ -294,11 +294,14 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
 
 
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
-              workspace=None, gate: str = "log_decay", o_gate=None):
-    """Gradients of chunk_fwd's (o, S_final) (no norm or convolution options) given dL/do and dL/dS_final.
-    ``gate`` says what ``g`` holds, as for chunk_fwd; dg is the gradient with respect to g as given (the
-    log-decay, or the gate pre-activation). With ``o_gate`` (the forward's output-gate pre-activation z), ``do``
-    is the gradient of the gated output and the result also holds ``do_gate`` = dL/dz [B, T, H, V] fp32.
+              workspace=None, gate: str = "log_decay", o_gate=None, qk_norm: bool = False, conv: str = "none",
+              conv_w=None):
+    """Gradients of chunk_fwd's (o, S_final) given dL/do and dL/dS_final, with respect to the raw inputs.
+    ``gate``, ``qk_norm``, ``conv`` and ``conv_w`` say what the forward did, as for chunk_fwd; dg is the
+    gradient with respect to g as given (the log-decay, or the gate pre-activation). With ``o_gate`` (the
+    forward's output-gate pre-activation z), ``do`` is the gradient of the gated output and the result also
+    holds ``do_gate`` = dL/dz [B, T, H, V] fp32. With a convolution the result also holds ``dconv_w``
+    [H, K + K + V, 4] fp32.
 
     ``do`` has o's shape and the input dtype; ``dS_final`` is fp32 [num_seqs, H, K, V] or None (zero).
     Returns a dict of fp32 tensors: dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]; and
@@ -314,6 +317,8 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
     dt = q.dtype
     io = _io_code(dt)
     gc = _gate_code(gate)
+    qc = _qk_code(qk_norm)
+    cc = _conv_code(conv, conv_w, H, 2 * K + V, dev)
     for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
                          ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H)), ("do", do, (B, T, H, V))):
         _need(t, name, shp, dt, dev)
@@ -335,16 +340,17 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
         out["dS0"] = torch.empty((N, H, K, V), **f32)
     if o_gate is not None:
         out["do_gate"] = torch.empty((B, T, H, V), **f32)
-    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N))
+    if cc != 0:
+        out["dconv_w"] = torch.empty((H, 2 * K + V, 4), **f32)
+    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc))
     if need == 0:
         raise KDAError(2, "kda_chunk_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0), _ptr(cu_seqlens),
-                           _ptr(do),
-                           _ptr(dS_final), B, T, H, K, V, N, io, gc, _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
-                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("do_gate")), _ptr(out.get("dS0")),
-                           _ptr(workspace),
-                           workspace.numel(), _stream(dev))
+                           _ptr(do), _ptr(dS_final), B, T, H, K, V, N, io, gc, qc, cc,
+                           _ptr(conv_w if cc != 0 else None), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("do_gate")), _ptr(out.get("dconv_w")),
+                           _ptr(out.get("dS0")), _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(st, "kda_chunk_bwd")
     return out

@@ -30,7 +30,7 @@ EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_byte
            "kda_workspace_status", "kda_chunk_fwd", "kda_chunk_prep", "kda_chunk_state", "kda_decode_step",
            "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd")
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 _lib = None
 
 
@@ -77,10 +77,11 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, vp]
     lib.kda_decode_step.restype = ctypes.c_int
-    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_int,
-                                  ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  sz, vp]
     lib.kda_chunk_bwd.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -66,7 +66,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 9; }
+int kda_abi_version(void) { return 10; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -270,45 +270,56 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     return KDA_SUCCESS;
 }
 
-size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs) {
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                     kda_qk_norm_t qk_norm, kda_conv_t conv) {
+    if (!valid_qk_norm(qk_norm) || !valid_conv(conv)) return 0;
     const bool packed = (B == 1);  // the packed bound is the larger for B == 1 and covers both
     if (check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed) != KDA_SUCCESS) return 0;
     const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
-    return kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs);
+    return kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM,
+                                         conv != KDA_CONV_NONE);
 }
 
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
                            const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
-                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, float *dq, float *dk, float *dv,
-                           float *dg, float *dbeta, float *d_o_gate, float *dS0, void *workspace,
+                           int32_t num_seqs, kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm,
+                           kda_conv_t conv, const float *conv_w, float *dq, float *dk, float *dv, float *dg,
+                           float *dbeta, float *d_o_gate, float *d_conv_w, float *dS0, void *workspace,
                            size_t workspace_bytes, void *stream) {
-    if (!valid_dtype(io) || !valid_gate(gate)) return KDA_ERROR_INVALID_VALUE;
+    if (!valid_dtype(io) || !valid_gate(gate) || !valid_qk_norm(qk_norm) || !valid_conv(conv) ||
+        !valid_conv_w(conv, conv_w))
+        return KDA_ERROR_INVALID_VALUE;
     const bool packed = cu_seqlens != nullptr;
+    const bool has_conv = conv != KDA_CONV_NONE;
     kda_status_t st = check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed);
     if (st != KDA_SUCCESS) return st;
     if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
         return KDA_ERROR_INVALID_VALUE;
     if (T > 0 && o_gate && !d_o_gate) return KDA_ERROR_INVALID_VALUE;  // an output gate needs its gradient
-    const void *ptrs[] = {q, k, v, g, o_gate, d_o, S0, dS_final, dq, dk, dv, dg, dbeta, d_o_gate, dS0, workspace};
+    if (has_conv && !d_conv_w) return KDA_ERROR_INVALID_VALUE;         // so do the taps (also at T == 0)
+    const void *ptrs[] = {q,  k,  v,     g,        o_gate, d_o,     S0,
+                          dS_final, dq, dk, dv, dg, dbeta, d_o_gate, d_conv_w, dS0, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERROR_INVALID_VALUE;
     if (beta && !aligned_elem(beta, io)) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u)) return KDA_ERROR_INVALID_VALUE;
     // outputs may not alias the inputs or each other
-    const void *outs[] = {dq, dk, dv, dg, dbeta, o_gate ? d_o_gate : nullptr, dS0};
-    const void *ins[] = {q, k, v, g, beta, o_gate, d_o, S0, dS_final, cu_seqlens};
-    for (int i = 0; i < 7; ++i) {
+    constexpr int NOUT = 8;
+    const void *outs[NOUT] = {dq, dk, dv, dg, dbeta, o_gate ? d_o_gate : nullptr, has_conv ? d_conv_w : nullptr, dS0};
+    const void *ins[] = {q, k, v, g, beta, o_gate, d_o, S0, dS_final, cu_seqlens, has_conv ? conv_w : nullptr};
+    for (int i = 0; i < NOUT; ++i) {
         if (!outs[i]) continue;
         for (const void *p : ins)
             if (p == outs[i]) return KDA_ERROR_INVALID_VALUE;
-        for (int j = i + 1; j < 7; ++j)
+        for (int j = i + 1; j < NOUT; ++j)
             if (outs[j] == outs[i]) return KDA_ERROR_INVALID_VALUE;
     }
     // the tile-sum reduce runs one thread per (token, head, partial slot): its grid must stay launchable
     if ((B * T * H * (3 * (int64_t)K + 1) + 255) / 256 >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
-    const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs);
+    const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM,
+                                                      has_conv);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
     st = check_device();
     if (st != KDA_SUCCESS) return st;
@@ -319,6 +330,10 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     a.B = B; a.T = T; a.H = H; a.K = K; a.V = V; a.num_seqs = num_seqs;
     a.io_bf16 = io == KDA_DTYPE_BF16;
     a.gate_sigmoid = gate == KDA_GATE_SCALED_SIGMOID;
+    a.qk_l2norm = qk_norm == KDA_QK_L2NORM;
+    a.conv = (int32_t)conv;
+    a.conv_w = has_conv ? conv_w : nullptr;
+    a.d_conv_w = has_conv ? d_conv_w : nullptr;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
     a.workspace = workspace;
     a.max_segs = segs;

@@ -128,16 +128,20 @@ __device__ __forceinline__ float sum_quad(float x) {
 }
 
 // ------------------------------------------------------------------ main kernel
-template <bool BF, int K>
+// QK32 / V32: q and k (v) come as fp32 arrays (the prologue's normalised or convolved values) instead of
+// the I/O dtype.
+template <bool BF, int K, bool QK32, bool V32>
 __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
-    const typename IO<BF>::T *__restrict__ q, const typename IO<BF>::T *__restrict__ k,
-    const typename IO<BF>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
+    const typename IO<BF && !QK32>::T *__restrict__ q, const typename IO<BF && !QK32>::T *__restrict__ k,
+    const typename IO<BF && !V32>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
     const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
     const typename IO<BF>::T *__restrict__ zg, const float *__restrict__ S0, const float *__restrict__ dSf,
     const int64_t *__restrict__ seq_tok,    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows, bool gate_sig,
     float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dz_out,
     float *__restrict__ dS0) {
     using io = IO<BF>;
+    using qkio = IO<BF && !QK32>;
+    using vio = IO<BF && !V32>;
     constexpr int R = K / 16;          // rows per thread
     constexpr int F = 3 * K + 1;       // partial row: dq | dk | dg | dbeta
     constexpr int NE = BL * K / BNT;   // staged q/k/g elements per thread
@@ -170,16 +174,17 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
             const int64_t ft = ft0 + tok;
             const bool ok = ft < t1;
             const int64_t idx = (ft * sH + h) * K + r;
-            pk[m] = ok ? io::ld(k, idx) : 0.f;
+            pk[m] = ok ? qkio::ld(k, idx) : 0.f;
             pg[m] = ok ? io::ld(g, idx) : 0.f;
-            pq[m] = (ok && with_q) ? io::ld(q, idx) : 0.f;
+            pq[m] = (ok && with_q) ? qkio::ld(q, idx) : 0.f;
         }
         {
             const int e = tid & (BL * BVT - 1), tok = e / BVT, c = e % BVT;
             const int64_t ft = ft0 + tok;
             const bool isv = tid < BL * BVT;
             const bool ok = ft < t1 && (isv || with_q);
-            pvd = ok ? io::ld(isv ? v : dout, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
+            const int64_t ve = (ft * sH + h) * sV + vt * BVT + c;
+            pvd = ok ? (isv ? vio::ld(v, ve) : io::ld(dout, ve)) : 0.f;
             pz = (ok && !isv && zg) ? io::ld(zg, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
         }
         pb = (tid < BL && ft0 + tid < t1) ? io::ld(beta, (ft0 + tid) * sH + h) : 0.f;
@@ -383,54 +388,353 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ 
     else dbeta[row] = acc;
 }
 
+// ------------------------------------------------------------------ prologue and its reverse
+// With the q/k normalisation and the short convolution (the prologue of kda_chunk_fwd), the gradients
+// run back through them after the recurrence's reverse: the recurrence sees the prologue's outputs,
+// formed here in fp32 (xq, xk, xv), and its gradients with respect to them (gq, gk, gv) are taken back
+// to the raw inputs:
+//   normalisation x_n = r x, r = (|x|^2 + 1e-6)^(-1/2):  dL/dx = r (dL/dx_n - (x_n . dL/dx_n) x_n);
+//   convolution y_t = sum_j w_j x_{t-3+j} (tokens of t's sequence), z = y or SiLU(y):
+//     dL/dy = dL/dz (SiLU: times sigmoid(y) (1 + y (1 - sigmoid(y)))),
+//     dL/dx_s = sum_j w_j dL/dy_{s+3-j} over the t = s+3-j of s's sequence,
+//     dL/dw_j = sum_t dL/dy_t x_{t-3+j}.
+
+// The sequence of flat token t (seq_tok[0] <= t < seq_tok[N]): the largest n with seq_tok[n] <= t.
+__device__ __forceinline__ int bwd_find_seq(const int64_t *seq_tok, int N, int64_t t) {
+    int lo = 0, hi = N;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (seq_tok[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// The convolution (and SiLU for act == 2) of one tensor x [tokens][H][D] into out (fp32), one thread per
+// (token, head, channel); rows of tokens outside every sequence get zeros.
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void kda_bwd_conv_fwd(const typename IO<BF>::T *__restrict__ x,
+                                                        const float *__restrict__ taps, int32_t CW, int32_t act,
+                                                        int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
+                                                        int64_t n_el, float *__restrict__ out) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_el) return;
+    const int c = (int)(idx % D);
+    const int64_t row = idx / D;
+    const int h = (int)(row % H);
+    const int64_t t = row / H;
+    if (t < seq_tok[0] || t >= seq_tok[N]) {
+        out[idx] = 0.f;
+        return;
+    }
+    const int64_t s0 = seq_tok[bwd_find_seq(seq_tok, N, t)];
+    const float4 w = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c) * 4);
+    const int64_t step = (int64_t)H * D;
+    float y = w.w * IO<BF>::ld(x, idx);
+    if (t - 1 >= s0) y = __builtin_fmaf(w.z, IO<BF>::ld(x, idx - step), y);
+    if (t - 2 >= s0) y = __builtin_fmaf(w.y, IO<BF>::ld(x, idx - 2 * step), y);
+    if (t - 3 >= s0) y = __builtin_fmaf(w.x, IO<BF>::ld(x, idx - 3 * step), y);
+    out[idx] = act == 2 ? y * sigmoid_f(y) : y;
+}
+
+// Sum over the 16 lanes of an aligned lane group.
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
+    return x;
+}
+
+// The normalisation of every (token, head) row of K channels, in fp32: xn = x r, r = 1 / sqrt(|x|^2 + 1e-6),
+// and r kept for the reverse. x is the I/O-dtype input (FROM_IO) or the fp32 buffer itself (xn, in place).
+// 16 lanes per row, K / 16 consecutive channels each (a row is one coalesced read).
+template <bool BF, int K, bool FROM_IO>
+__global__ __launch_bounds__(256) void kda_bwd_norm_fwd(const typename IO<BF>::T *__restrict__ x, float *xn,
+                                                        float *__restrict__ r, int64_t n_rows) {
+    constexpr int E = K / 16;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = gid >> 4;
+    const int c0 = (int)(gid & 15) * E;
+    const bool ok = row < n_rows;  // every lane takes part in the group sums
+    float v[E];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < E; ++c) {
+        v[c] = ok ? (FROM_IO ? IO<BF>::ld(x, row * K + c0 + c) : xn[row * K + c0 + c]) : 0.f;
+        ss = __builtin_fmaf(v[c], v[c], ss);
+    }
+    const float rr = rsqrtf(sum16(ss) + 1e-6f);
+    if (!ok) return;
+#pragma unroll
+    for (int c = 0; c < E; ++c) xn[row * K + c0 + c] = v[c] * rr;
+    if (c0 == 0) r[row] = rr;
+}
+
+// The normalisation's reverse per row (row-local, so dx may be dxn itself): dx = r (dxn - (xn . dxn) xn).
+// Rows of tokens outside every sequence are not written. 16 lanes per row, as above.
+template <int K>
+__global__ __launch_bounds__(256) void kda_bwd_norm_back(const float *__restrict__ xn, const float *__restrict__ r,
+                                                         const float *dxn, float *dx, int64_t n_rows, int32_t H,
+                                                         int32_t N, const int64_t *__restrict__ seq_tok) {
+    constexpr int E = K / 16;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = gid >> 4;
+    const int c0 = (int)(gid & 15) * E;
+    const bool ok = row < n_rows;
+    float a[E], d[E];
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < E; ++c) {
+        a[c] = ok ? xn[row * K + c0 + c] : 0.f;
+        d[c] = ok ? dxn[row * K + c0 + c] : 0.f;
+        dot = __builtin_fmaf(a[c], d[c], dot);
+    }
+    dot = sum16(dot);
+    if (!ok) return;
+    const int64_t t = row / H;
+    if (t < seq_tok[0] || t >= seq_tok[N]) return;
+    const float rr = r[row];
+#pragma unroll
+    for (int c = 0; c < E; ++c) dx[row * K + c0 + c] = rr * __builtin_fmaf(-dot, a[c], d[c]);
+}
+
+constexpr int CONV_TILE = 64;  // flat tokens per thread of the convolution's reverse
+
+// The convolution's reverse for one tensor: raw x [tokens][H][D] (I/O dtype), dz = dL/d(conv output)
+// [tokens][H][D] fp32. One thread per (64-token tile of the flat rows, head, channel) walks the tile's
+// tokens and the three after it, forming dL/dy_t = dz_t act'(y_t) (y_t recomputed), and writes dL/dx for
+// the tile's tokens (rows outside every sequence are not written) and the tile's partial sums of dL/dw,
+// dw_part[tile][h][coff + c][4].
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::T *__restrict__ x,
+                                                         const float *__restrict__ dz, const float *__restrict__ taps,
+                                                         int32_t CW, int32_t coff, int32_t act, int32_t H, int32_t N,
+                                                         const int64_t *__restrict__ seq_tok, int64_t total,
+                                                         int64_t n_items, float *__restrict__ dx,
+                                                         float *__restrict__ dw_part) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_items) return;
+    const int c = (int)(idx % D);
+    const int64_t rest = idx / D;
+    const int h = (int)(rest % H);
+    const int64_t tile = rest / H;
+    const int64_t t0 = tile * CONV_TILE, t1 = (t0 + CONV_TILE < total) ? t0 + CONV_TILE : total;
+    const int64_t lo = seq_tok[0], hi = seq_tok[N];
+    const float4 w = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c) * 4);
+    const int64_t step = (int64_t)H * D;
+    auto el = [&](int64_t t) { return (t * H + h) * D + c; };
+    // sequence of token t and its start (sid -1: outside every sequence or past the rows)
+    int n = (t0 >= lo && t0 < hi) ? bwd_find_seq(seq_tok, N, t0) : (t0 < lo ? 0 : N);
+    // window of dL/dy and sequence ids for tokens t-3 .. t (index 3 = t)
+    float dyw[4] = {0.f, 0.f, 0.f, 0.f};
+    int sw[4] = {-1, -1, -1, -1};
+    float dw0 = 0.f, dw1 = 0.f, dw2 = 0.f, dw3 = 0.f;
+    for (int64_t t = t0; t < t1 + 3; ++t) {
+        int sid = -1;
+        float dy = 0.f;
+        if (t < total && t >= lo && t < hi) {
+            while (n + 1 < N && seq_tok[n + 1] <= t) ++n;
+            sid = n;
+            const int64_t s0 = seq_tok[n];
+            const float x0 = IO<BF>::ld(x, el(t));
+            const float x1 = t - 1 >= s0 ? IO<BF>::ld(x, el(t) - step) : 0.f;
+            const float x2 = t - 2 >= s0 ? IO<BF>::ld(x, el(t) - 2 * step) : 0.f;
+            const float x3 = t - 3 >= s0 ? IO<BF>::ld(x, el(t) - 3 * step) : 0.f;
+            float y = w.w * x0;
+            y = __builtin_fmaf(w.z, x1, y);
+            y = __builtin_fmaf(w.y, x2, y);
+            y = __builtin_fmaf(w.x, x3, y);
+            dy = dz[el(t)];
+            if (act == 2) {
+                const float sg = sigmoid_f(y);
+                dy *= sg * __builtin_fmaf(y, 1.f - sg, 1.f);
+            }
+            if (t < t1) {  // the taps' sums over this tile's tokens
+                dw3 = __builtin_fmaf(dy, x0, dw3);
+                dw2 = __builtin_fmaf(dy, x1, dw2);
+                dw1 = __builtin_fmaf(dy, x2, dw1);
+                dw0 = __builtin_fmaf(dy, x3, dw0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            dyw[i] = dyw[i + 1];
+            sw[i] = sw[i + 1];
+        }
+        dyw[3] = dy;
+        sw[3] = sid;
+        // dL/dx_tau for tau = t - 3: w3 dy_tau + w2 dy_{tau+1} + w1 dy_{tau+2} + w0 dy_{tau+3}, same sequence
+        const int64_t tau = t - 3;
+        if (tau >= t0 && sw[0] >= 0) {
+            float g = w.w * dyw[0];
+            if (sw[1] == sw[0]) g = __builtin_fmaf(w.z, dyw[1], g);
+            if (sw[2] == sw[0]) g = __builtin_fmaf(w.y, dyw[2], g);
+            if (sw[3] == sw[0]) g = __builtin_fmaf(w.x, dyw[3], g);
+            dx[el(tau)] = g;
+        }
+    }
+    *reinterpret_cast<float4 *>(dw_part + ((size_t)tile * H + h) * CW * 4 + (size_t)(coff + c) * 4) =
+        make_float4(dw0, dw1, dw2, dw3);
+}
+
+// dL/dw = the tiles' partial sums added in tile order (deterministic); one thread per (head, channel, tap).
+__global__ __launch_bounds__(256) void kda_bwd_convw_reduce(const float *__restrict__ dw_part, int64_t n_tiles,
+                                                            int64_t n_el, float *__restrict__ dw) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_el) return;
+    float acc = 0.f;
+    for (int64_t t = 0; t < n_tiles; ++t) acc += dw_part[t * n_el + idx];
+    dw[idx] = acc;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
     int64_t *seq_tok, *seg_off;
     float *ckpt, *part;
+    // with the prologue: its outputs (xq, xk, xv), the recurrence's gradients with respect to them
+    // (gq, gk, gv), the normalisation's factors (rq, rk) and the taps' partial sums (dw_part)
+    float *xq, *xk, *xv, *gq, *gk, *gv, *rq, *rk, *dw_part;
 };
 
-BwdWs bwd_ptrs(void *ws, int32_t N, int64_t max_segs, int32_t H, int32_t K, int32_t V) {
+int64_t conv_tiles(int64_t n_tokens) { return (n_tokens + CONV_TILE - 1) / CONV_TILE; }
+
+BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_segs, int32_t H, int32_t K, int32_t V, bool norm,
+               bool conv, size_t *total = nullptr) {
     char *p = (char *)ws;
     BwdWs r;
-    r.seq_tok = (int64_t *)p;
-    p += align256(sizeof(int64_t) * ((size_t)N + 1));
-    r.seg_off = (int64_t *)p;
-    p += align256(sizeof(int64_t) * ((size_t)N + 1));
-    r.ckpt = (float *)p;
-    p += align256(sizeof(float) * (size_t)max_segs * H * K * V);
-    r.part = (float *)p;
+    auto take = [&](size_t bytes) {
+        char *q = p;
+        p += align256(bytes);
+        return q;
+    };
+    r.seq_tok = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
+    r.seg_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
+    r.ckpt = (float *)take(sizeof(float) * (size_t)max_segs * H * K * V);
+    r.part = (float *)take(sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 1));
+    const size_t nk = (size_t)n_tokens * H * K * sizeof(float), nv = (size_t)n_tokens * H * V * sizeof(float);
+    const bool pro = norm || conv;
+    r.xq = pro ? (float *)take(nk) : nullptr;
+    r.xk = pro ? (float *)take(nk) : nullptr;
+    r.gq = pro ? (float *)take(nk) : nullptr;
+    r.gk = pro ? (float *)take(nk) : nullptr;
+    r.xv = conv ? (float *)take(nv) : nullptr;
+    r.gv = conv ? (float *)take(nv) : nullptr;
+    r.rq = norm ? (float *)take((size_t)n_tokens * H * sizeof(float)) : nullptr;
+    r.rk = norm ? (float *)take((size_t)n_tokens * H * sizeof(float)) : nullptr;
+    r.dw_part = conv ? (float *)take((size_t)conv_tiles(n_tokens) * H * (2 * K + V) * 4 * sizeof(float)) : nullptr;
+    if (total) *total = (size_t)(p - (char *)ws);
     return r;
+}
+
+unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+template <bool BF, int K, bool QK32, bool V32>
+void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void *ks, const void *vs, float *dv_dst,
+              float *dq_dst, float *dk_dst, hipStream_t st) {
+    using T = typename IO<BF>::T;
+    using TQ = typename IO<BF && !QK32>::T;
+    using TV = typename IO<BF && !V32>::T;
+    const int nvt = a.V / BVT;
+    const int64_t n_rows = a.B * a.T * a.H;
+    const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
+    hipLaunchKernelGGL((kda_bwd_kernel<BF, K, QK32, V32>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const TQ *)qs,
+                       (const TQ *)ks, (const TV *)vs, (const T *)a.g, (const T *)a.beta, (const T *)a.dout,
+                       (const T *)a.o_gate, a.S0, a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows,
+                       a.gate_sigmoid, w.ckpt, w.part, dv_dst, a.d_o_gate, a.dS0);
+    const int64_t nel = n_rows * (3 * K + 1);
+    if (nel > 0)
+        hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3(blocks_of(nel)), dim3(256), 0, st, w.part, nvt, n_rows, a.H,
+                           w.seq_tok, a.num_seqs, (const T *)a.g, a.gate_sigmoid, dq_dst, dk_dst, a.dg, a.dbeta);
+}
+
+template <bool BF, int D>
+void conv_back_one(const BackwardArgs &a, const BwdWs &w, const void *x, const float *dz, int coff, float *dx,
+                   hipStream_t st) {
+    using T = typename IO<BF>::T;
+    const int64_t total = a.B * a.T;
+    const int64_t items = conv_tiles(total) * a.H * D;
+    if (items > 0)
+        hipLaunchKernelGGL((kda_bwd_conv_back<BF, D>), dim3(blocks_of(items)), dim3(256), 0, st, (const T *)x, dz,
+                           a.conv_w + (size_t)coff * 4, 2 * a.K + a.V, coff, a.conv, a.H, a.num_seqs, w.seq_tok,
+                           total, items, dx, w.dw_part);
+}
+
+template <bool BF, int K, int V>
+hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
+    using T = typename IO<BF>::T;
+    const int64_t n_tok = a.B * a.T, n_rows = n_tok * a.H;
+    const bool norm = a.qk_l2norm, conv = a.conv != 0;
+    BwdWs w = bwd_ptrs(a.workspace, n_tok, a.num_seqs, a.max_segs, a.H, K, V, norm, conv);
+    const int64_t T_row = a.cu_seqlens ? 0 : a.T;
+    hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, n_tok,
+                       w.seq_tok, w.seg_off);
+    if (!norm && !conv) {
+        bwd_core<BF, K, false, false>(a, w, a.q, a.k, a.v, a.dv, a.dq, a.dk, st);
+        return hipGetLastError();
+    }
+    // prologue, forward: convolution into xq, xk, xv; normalisation of q and k (in place, or from the input)
+    const int32_t CW = 2 * K + V;
+    if (conv) {
+        const int64_t nk = n_rows * K, nv = n_rows * V;
+        if (nk > 0) {
+            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(nk)), dim3(256), 0, st, (const T *)a.q,
+                               a.conv_w, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nk, w.xq);
+            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(nk)), dim3(256), 0, st, (const T *)a.k,
+                               a.conv_w + (size_t)K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nk, w.xk);
+            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, V>), dim3(blocks_of(nv)), dim3(256), 0, st, (const T *)a.v,
+                               a.conv_w + (size_t)2 * K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nv, w.xv);
+        }
+    }
+    if (norm && n_rows > 0) {
+        if (conv) {
+            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, false>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                               (const T *)nullptr, w.xq, w.rq, n_rows);
+            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, false>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                               (const T *)nullptr, w.xk, w.rk, n_rows);
+        } else {
+            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, true>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                               (const T *)a.q, w.xq, w.rq, n_rows);
+            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, true>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                               (const T *)a.k, w.xk, w.rk, n_rows);
+        }
+    }
+    // the recurrence's reverse on the prologue's outputs
+    if (conv) bwd_core<BF, K, true, true>(a, w, w.xq, w.xk, w.xv, w.gv, w.gq, w.gk, st);
+    else bwd_core<BF, K, true, false>(a, w, w.xq, w.xk, a.v, a.dv, w.gq, w.gk, st);
+    // prologue, reverse: normalisation (into gq, gk when a convolution follows), then convolution
+    if (norm && n_rows > 0) {
+        hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xq, w.rq, w.gq,
+                           conv ? w.gq : a.dq, n_rows, a.H, a.num_seqs, w.seq_tok);
+        hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xk, w.rk, w.gk,
+                           conv ? w.gk : a.dk, n_rows, a.H, a.num_seqs, w.seq_tok);
+    }
+    if (conv) {
+        conv_back_one<BF, K>(a, w, a.q, w.gq, 0, a.dq, st);
+        conv_back_one<BF, K>(a, w, a.k, w.gk, K, a.dk, st);
+        conv_back_one<BF, V>(a, w, a.v, w.gv, 2 * K, a.dv, st);
+        const int64_t nel = (int64_t)a.H * CW * 4;
+        hipLaunchKernelGGL(kda_bwd_convw_reduce, dim3(blocks_of(nel)), dim3(256), 0, st, w.dw_part,
+                           conv_tiles(n_tok), nel, a.d_conv_w);
+    }
+    return hipGetLastError();
 }
 
 template <bool BF, int K>
 hipError_t bwd_launch(const BackwardArgs &a, hipStream_t st) {
-    using T = typename IO<BF>::T;
-    const int nvt = a.V / BVT;
-    const int64_t n_rows = a.B * a.T * a.H;
-    BwdWs w = bwd_ptrs(a.workspace, a.num_seqs, a.max_segs, a.H, a.K, a.V);
-    const int64_t T_row = a.cu_seqlens ? 0 : a.T;
-    hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, a.B * a.T,
-                       w.seq_tok, w.seg_off);
-    const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
-    hipLaunchKernelGGL((kda_bwd_kernel<BF, K>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const T *)a.q,
-                       (const T *)a.k, (const T *)a.v, (const T *)a.g, (const T *)a.beta, (const T *)a.dout, (const T *)a.o_gate, a.S0,
-                       a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows, a.gate_sigmoid, w.ckpt, w.part, a.dv, a.d_o_gate, a.dS0);
-    const int64_t nel = n_rows * (3 * K + 1);
-    if (nel > 0)
-        hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, st, w.part,
-                           nvt, n_rows, a.H, w.seq_tok, a.num_seqs, (const T *)a.g, a.gate_sigmoid, a.dq, a.dk,
-                           a.dg, a.dbeta);
-    return hipGetLastError();
+    switch (a.V) {
+        case 32: return bwd_launch_kv<BF, K, 32>(a, st);
+        case 64: return bwd_launch_kv<BF, K, 64>(a, st);
+        default: return bwd_launch_kv<BF, K, 128>(a, st);
+    }
 }
 
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
-                                int32_t num_seqs) {
-    return 2 * align256(sizeof(int64_t) * ((size_t)num_seqs + 1)) +
-           align256(sizeof(float) * (size_t)max_segs * H * K * V) +
-           sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 1);
+                                int32_t num_seqs, bool qk_norm, bool conv) {
+    size_t total = 0;
+    bwd_ptrs(nullptr, n_tokens, num_seqs, max_segs, H, K, V, qk_norm, conv, &total);
+    return total;
 }
 
 int32_t backward_segment_tokens() { return BL; }

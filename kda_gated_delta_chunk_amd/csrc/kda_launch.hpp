@@ -95,6 +95,10 @@ struct BackwardArgs {
     int32_t H, K, V, num_seqs;
     bool io_bf16;
     bool gate_sigmoid;                 // g holds the gate pre-activation x (log-decay -5 sigmoid(x)); dg is dL/dx
+    bool qk_l2norm;                    // the forward normalised q and k (after the convolution)
+    int32_t conv;                      // the forward's short convolution (0: none; 1; 2: with SiLU)
+    const float *conv_w;               // its taps [H, K + K + V, 4], or null
+    float *d_conv_w;                   // dL/d(taps) [H, K + K + V, 4] fp32 (with a convolution)
     float *dq, *dk, *dv, *dg, *dbeta;  // fp32 gradients
     float *d_o_gate;                   // dL/dz [B,T,H,V] fp32 (required with o_gate)
     float *dS0;                        // or null
@@ -104,7 +108,7 @@ struct BackwardArgs {
 // Tokens per checkpoint segment of the backward pass.
 int32_t backward_segment_tokens();
 size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
-                                int32_t num_seqs);
+                                int32_t num_seqs, bool qk_norm, bool conv);
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
 
 }  // namespace kda

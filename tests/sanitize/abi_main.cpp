@@ -26,7 +26,7 @@ int main() {
     int ndev = 0;
     const bool device = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0;
     (void)hipGetLastError();
-    CHECK(kda_abi_version() == 9);
+    CHECK(kda_abi_version() == 10);
     for (int s = -1; s < 8; ++s) CHECK(strlen(kda_status_string((kda_status_t)s)) > 0);
     // workspace queries over a sweep of sizes and options (valid and not)
     const int64_t Ts[] = {0, 1, 15, 16, 17, 4096, (int64_t)1 << 40};
@@ -43,8 +43,11 @@ int main() {
                                                                             KDA_CONV_SHORT4, (kda_operands_t)ops);
                             CHECK(a < ((size_t)1 << 62) && b < ((size_t)1 << 62));
                         }
-    CHECK(kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1) > 0);
-    CHECK(kda_chunk_bwd_workspace_bytes(2, 64, 2, 48, 32, 2) == 0);
+    CHECK(kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE) > 0);
+    CHECK(kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_L2NORM, KDA_CONV_SHORT4_SILU) >
+          kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE));
+    CHECK(kda_chunk_bwd_workspace_bytes(2, 64, 2, 48, 32, 2, KDA_QK_AS_GIVEN, KDA_CONV_NONE) == 0);
+    CHECK(kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_AS_GIVEN, (kda_conv_t)3) == 0);
     // prefill: rejected arguments
     CHECK(fwd(nullptr, A, A, 1 << 30, 64, 32, 16, KDA_DTYPE_BF16, KDA_OPERANDS_BF16, nullptr, 1) == KDA_ERROR_INVALID_VALUE);
     CHECK(fwd(A + 8, A, A, 1 << 30, 64, 32, 16, KDA_DTYPE_BF16, KDA_OPERANDS_BF16, nullptr, 1) == KDA_ERROR_INVALID_VALUE);
@@ -71,8 +74,9 @@ int main() {
           KDA_ERROR_INVALID_VALUE);
     float *f = (float *)A;
     CHECK(kda_chunk_bwd(A, A, A, A, A, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 64, 2, 32, 32, 1,
-                        KDA_DTYPE_BF16, KDA_GATE_LOG_DECAY, f + 4096, f + 8192, f + 12288, f + 16384, f + 20480,
-                        nullptr, nullptr, A, 1 << 30, nullptr) == KDA_ERROR_INVALID_VALUE);  // d_o missing
+                        KDA_DTYPE_BF16, KDA_GATE_LOG_DECAY, KDA_QK_AS_GIVEN, KDA_CONV_NONE, nullptr, f + 4096,
+                        f + 8192, f + 12288, f + 16384, f + 20480, nullptr, nullptr, nullptr, A, 1 << 30,
+                        nullptr) == KDA_ERROR_INVALID_VALUE);  // d_o missing
     int32_t err = 0;
     CHECK(kda_workspace_status(nullptr, 1024, &err, nullptr) == KDA_ERROR_INVALID_VALUE);
     CHECK(kda_workspace_status(A, 100, &err, nullptr) == KDA_ERROR_WORKSPACE_TOO_SMALL);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 9
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 10
 
 
 def test_status_strings():
@@ -282,12 +282,17 @@ def _bwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, og=None, S0=None, cu=None, do=A + 20480,
              dSf=None, dog=A + 7 * 65536 + 4096,
-             B=1, T=64, H=2, K=32, V=32, N=1, io=1, gate=0, dq=A + 65536, dk=A + 2 * 65536, dv=A + 3 * 65536,
-             dg=A + 4 * 65536, db=A + 5 * 65536, dS0=A + 6 * 65536, ws=A + 8 * 65536, wsb=1 << 40, stream=None)
+             B=1, T=64, H=2, K=32, V=32, N=1, io=1, gate=0, qk=0, conv=0, cw=None, dq=A + 65536, dk=A + 2 * 65536,
+             dv=A + 3 * 65536, dg=A + 4 * 65536, db=A + 5 * 65536, dcw=None, dS0=A + 6 * 65536, ws=A + 8 * 65536,
+             wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["do"], a["dSf"],
-                             a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["gate"], a["dq"], a["dk"],
-                             a["dv"], a["dg"], a["db"], a["dog"], a["dS0"], a["ws"], a["wsb"], a["stream"])
+                             a["B"], a["T"], a["H"], a["K"], a["V"], a["N"], a["io"], a["gate"], a["qk"], a["conv"],
+                             a["cw"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dog"], a["dcw"], a["dS0"], a["ws"],
+                             a["wsb"], a["stream"])
+
+
+CW, DCW = A + 9 * 65536, A + 10 * 65536  # conv taps and their gradient (fake addresses)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -312,6 +317,15 @@ def _bwd(**kw):
     (dict(V=256), UNSUP),
     (dict(wsb=100), WS_SMALL),
     (dict(ws=None), WS_SMALL),
+    (dict(qk=2), INVALID),
+    (dict(conv=3, cw=CW, dcw=DCW), INVALID),
+    (dict(conv=1, cw=None, dcw=DCW), INVALID),            # a convolution needs its taps
+    (dict(conv=1, cw=CW, dcw=None), INVALID),             # ... and their gradient
+    (dict(conv=2, cw=CW, dcw=None, T=0), INVALID),        # also when there are no tokens
+    (dict(conv=1, cw=CW + 4, dcw=DCW), INVALID),          # taps misaligned
+    (dict(conv=1, cw=CW, dcw=DCW + 8), INVALID),          # gradient misaligned
+    (dict(conv=1, cw=CW, dcw=CW), INVALID),               # the gradient aliases the taps
+    (dict(conv=1, cw=CW, dcw=A + 65536), INVALID),        # ... or dq
 ])
 def test_chunk_bwd_rejects(kw, expect):
     assert _bwd(**kw) == expect
@@ -324,9 +338,25 @@ def test_bwd_workspace_bytes():
     B, T, H, K, V = 2, 64, 3, 32, 64
     states = B * (T // 8) * H * K * V * 4
     parts = (V // 16) * B * T * H * (3 * K + 1) * 4
-    assert states + parts <= ws(B, T, H, K, V, B) <= states + parts + 3 * 256
-    assert ws(1, 4096, 96, 128, 128, 16) > ws(1, 4096, 96, 128, 128, 1)  # one more partial segment per sequence
-    assert ws(1, 64, 2, 48, 32, 1) == 0 and ws(2, 64, 2, 32, 32, 1) == 0
+    assert states + parts <= ws(B, T, H, K, V, B, 0, 0) <= states + parts + 3 * 256
+    assert ws(1, 4096, 96, 128, 128, 16, 0, 0) > ws(1, 4096, 96, 128, 128, 1, 0, 0)  # one more segment per sequence
+    assert ws(1, 64, 2, 48, 32, 1, 0, 0) == 0 and ws(2, 64, 2, 32, 32, 1, 0, 0) == 0
+    assert ws(B, T, H, K, V, B, 2, 0) == 0 and ws(B, T, H, K, V, B, 0, 3) == 0
+
+
+def test_bwd_workspace_bytes_with_prologue():
+    # the prologue adds its fp32 outputs and gradients (q, k; v with a convolution), the norm factors and the
+    # taps' per-64-token partial sums
+    ws = _lib.load().kda_chunk_bwd_workspace_bytes
+    B, T, H, K, V = 2, 64, 3, 32, 64
+    base = ws(B, T, H, K, V, B, 0, 0)
+    n = B * T * H
+    qk = 4 * n * K * 4
+    norm = 2 * n * 4
+    conv = 2 * n * V * 4 + -(-B * T // 64) * H * (2 * K + V) * 4 * 4
+    for qc, cc, extra in ((1, 0, qk + norm), (0, 1, qk + conv), (0, 2, qk + conv), (1, 2, qk + norm + conv)):
+        got = ws(B, T, H, K, V, B, qc, cc) - base
+        assert extra <= got <= extra + 8 * 256, (qc, cc, got, extra)
 
 
 def _has_gpu():
@@ -346,5 +376,6 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _state() == NO_DEV
     assert _dec() == NO_DEV
     assert _bwd() == NO_DEV
+    assert _bwd(qk=1, conv=2, cw=CW, dcw=DCW) == NO_DEV
     out = ctypes.c_int32(0)
     assert _lib.load().kda_workspace_status(A, 1024, ctypes.byref(out), None) == NO_DEV

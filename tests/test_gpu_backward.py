@@ -15,7 +15,7 @@ from tests.parity import TOL_FP32, err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "do_gate")
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "do_gate", "dconv_w")
 
 
 def _announce(name, **kw):
@@ -34,7 +34,8 @@ def _inputs(B, T, H, K, V, io, seed, cu=None, with_S0=True, with_dsf=True, **kw)
 def _gpu(inp, want_dS0=True):
     out = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
                     dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0,
-                    gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"))
+                    gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"), qk_norm=inp.get("qk_norm", False),
+                    conv=inp.get("conv", "none"), conv_w=inp.get("conv_w"))
     torch.cuda.synchronize()
     return out
 
@@ -52,9 +53,14 @@ def _oracle(inp, heads=None):
         S0 = None if S0 is None else S0[:, hs]
         dsf = None if dsf is None else dsf[:, hs]
     cu = inp["cu_seqlens"]
+    cw = inp.get("conv_w")
+    if cw is not None and heads is not None:
+        cw = cw[list(heads)]
     return oracle.chunk_bwd(*(x.cpu() for x in xs), S0=None if S0 is None else S0.cpu(),
                             dS_final=None if dsf is None else dsf.cpu(), cu_seqlens=None if cu is None else cu.cpu(),
-                            gate=inp.get("gate", "log_decay"), o_gate=None if z is None else z.cpu())
+                            gate=inp.get("gate", "log_decay"), o_gate=None if z is None else z.cpu(),
+                            qk_norm=inp.get("qk_norm", False), conv=inp.get("conv", "none"),
+                            conv_w=None if cw is None else cw.cpu())
 
 
 def _compare(out, ref, heads=None, tol=TOL_FP32):
@@ -64,7 +70,12 @@ def _compare(out, ref, heads=None, tol=TOL_FP32):
             continue
         x = out[n]
         if heads is not None:
-            x = x[:, :, list(heads)] if n != "dS0" else x[:, list(heads)]
+            if n == "dconv_w":
+                x = x[list(heads)]
+            elif n == "dS0":
+                x = x[:, list(heads)]
+            else:
+                x = x[:, :, list(heads)]
         assert n in ref, n
         errs[n] = err(x, ref[n])
     print("  errors " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
@@ -157,3 +168,117 @@ def test_bwd_output_gate_and_gate_preactivation(io):
     out = _gpu(inp)
     assert "do_gate" in out
     _compare(out, _oracle(inp))
+
+
+# ------------------------------------------------------------ through the prologue
+#
+# The forward's q/k normalisation and short convolution (length 4, causal, restarting at each sequence
+# start, optional SiLU) are taken back by the chain rule: dq, dk and dv are with respect to the raw inputs,
+# and dconv_w is the gradient of the taps. The oracle runs the same prologue in fp64.
+
+def _taps(H, K, V, seed, scale=0.5):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn((H, 2 * K + V, 4), generator=g)).to(DEV)
+
+
+def _prologue(inp, qk_norm, conv, seed):
+    inp["qk_norm"] = qk_norm
+    inp["conv"] = conv
+    if conv != "none":
+        H, K, V = inp["q"].shape[2], inp["q"].shape[3], inp["v"].shape[3]
+        inp["conv_w"] = _taps(H, K, V, seed)
+    return inp
+
+
+PROLOGUES = [(True, "none"), (False, "short4"), (False, "short4_silu"), (True, "short4_silu")]
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+@pytest.mark.parametrize("qk_norm,conv", PROLOGUES)
+def test_bwd_prologue_matches_oracle(io, qk_norm, conv):
+    # two batch rows of 150 tokens: several 64-token tiles of the taps' partial sums and a ragged tail
+    _announce("bwd_prologue", io=io, qk_norm=qk_norm, conv=conv, B=2, T=150, H=3, K=64, V=128, seed=81)
+    inp = _prologue(_inputs(2, 150, 3, 64, 128, io, 81, raw_k=qk_norm), qk_norm, conv, 81)
+    out = _gpu(inp)
+    assert ("dconv_w" in out) == (conv != "none")
+    _compare(out, _oracle(inp))
+
+
+@pytest.mark.parametrize("K,V", [(32, 32), (128, 128), (128, 64)])
+def test_bwd_prologue_head_sizes(K, V):
+    _announce("bwd_prologue_sizes", K=K, V=V, T=70, H=2, seed=82)
+    inp = _prologue(_inputs(1, 70, 2, K, V, "bf16", 82, raw_k=True), True, "short4_silu", 82)
+    _compare(_gpu(inp), _oracle(inp))
+
+
+def test_bwd_prologue_varlen_and_both_gates():
+    """Packed sequences (empty, 1- and 2-token ones, so the convolution's history restarts inside a 64-token
+    tile and a tile's window crosses sequence ends), both gates, the normalisation and SiLU at once."""
+    lengths = [37, 0, 2, 1, 150, 64, 0, 65, 3]
+    cu = synth.cu_from_lengths(lengths)
+    _announce("bwd_prologue_varlen", lengths=lengths, H=2, K=128, V=64, seed=83)
+    inp = _inputs(1, cu[-1], 2, 128, 64, "bf16", 83, cu=cu, gate_preact=True, with_o_gate=True, raw_k=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp = _prologue(inp, True, "short4_silu", 83)
+    out = _gpu(inp)
+    assert "do_gate" in out and "dconv_w" in out
+    _compare(out, _oracle(inp))
+
+
+def test_bwd_prologue_packed_rows_past_the_last_sequence():
+    # cu_seqlens ends before B * T: rows past it are read by no sequence; their gradients are not written
+    cu = [0, 30, 61]
+    _announce("bwd_prologue_tail", cu=cu, T=100, H=2, K=64, V=64, seed=84)
+    inp = _inputs(1, 100, 2, 64, 64, "fp32", 84, cu=cu, raw_k=True)
+    inp = _prologue(inp, True, "short4", 84)
+    out = _gpu(inp)
+    sl = {n: (out[n][:, :61] if n not in ("dS0", "dconv_w") else out[n]) for n in out}
+    ins = dict(inp)
+    for n in ("q", "k", "v", "g", "beta", "do"):
+        ins[n] = inp[n][:, :61]
+    _compare(sl, _oracle(ins))
+
+
+def test_bwd_identity_taps_change_nothing():
+    """Taps (0, 0, 0, 1) without SiLU hand every input through unchanged, so every gradient equals that of
+    the call without a convolution bit for bit, and dconv_w (the only new output) matches the oracle."""
+    _announce("bwd_identity_taps", T=90, H=3, K=64, V=128, seed=85)
+    for io in ("fp32", "bf16"):
+        inp = _inputs(2, 90, 3, 64, 128, io, 85)
+        plain = _gpu(inp)
+        w = torch.zeros((3, 2 * 64 + 128, 4), device=DEV)
+        w[..., 3] = 1.0
+        inp["conv"], inp["conv_w"] = "short4", w
+        out = _gpu(inp)
+        for n in plain:
+            assert torch.equal(out[n], plain[n]), (io, n)
+        ref = _oracle(inp)
+        assert err(out["dconv_w"], ref["dconv_w"]) <= TOL_FP32
+
+
+def test_bwd_prologue_empty_batch_zeroes_dconv_w():
+    _announce("bwd_prologue_empty", T=0, H=2, K=32, V=32)
+    inp = _prologue(_inputs(1, 0, 2, 32, 32, "fp32", 86), True, "short4_silu", 86)
+    out = _gpu(inp)
+    assert torch.equal(out["dS0"], inp["dS_final"])
+    assert torch.equal(out["dconv_w"], torch.zeros_like(out["dconv_w"]))
+
+
+def test_bwd_prologue_is_deterministic():
+    _announce("bwd_prologue_determinism", T=300, H=4, K=128, V=128, seed=87)
+    inp = _prologue(_inputs(1, 300, 4, 128, 128, "bf16", 87, raw_k=True), True, "short4_silu", 87)
+    a, b = _gpu(inp), _gpu(inp)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_prologue_4k_workload_sampled_heads():
+    # the 4096-token, 96-head bf16 workload with the whole prologue; heads 0 and 95 end to end
+    _announce("bwd_prologue_4k", T=4096, H=96, K=128, V=128, io="bf16", seed=1002)
+    inp = _inputs(1, 4096, 96, 128, 128, "bf16", 1002, with_S0=False, raw_k=True)
+    inp = _prologue(inp, True, "short4_silu", 1002)
+    out = _gpu(inp)
+    for n in out:
+        assert torch.isfinite(out[n]).all(), n
+    heads = (0, 95)
+    _compare(out, _oracle(inp, heads), heads)
