@@ -262,6 +262,33 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            void *o, float *S_final, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It allocates nothing: in place of the
+ * workspace it uses a library-owned device array of
+ * KDA_NO_ALLOC_SCRATCH_BYTES, one per GPU, looked up on the first call on
+ * that device and held until the process ends. Arguments, results and
+ * errors are those of kda_chunk_fwd given a workspace of that size: the
+ * call runs as two passes when kda_chunk_fwd_workspace_bytes() fits in it,
+ * else as the fused kernel; when even kda_chunk_fwd_min_workspace_bytes()
+ * exceeds it (a convolution over many tokens, or millions of sequences) it
+ * returns WORKSPACE_TOO_SMALL before touching the device. The stream must
+ * belong to the current device (else INVALID_VALUE). If a wait inside the
+ * kernels gives up (error bit 1 of kda_workspace_status), o and S_final are
+ * filled with NaN, since the scratch's header is out of the caller's view.
+ * Every call on one GPU uses the same array and it keeps the last call's
+ * contents: calls that overlap on one GPU (different streams or threads
+ * without ordering) race and give wrong results.
+ */
+#define KDA_NO_ALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+kda_status_t kda_chunk_fwd_no_alloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                                    const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B,
+                                    int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk,
+                                    kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv,
+                                    const float *conv_w, kda_operands_t operands, kda_dtype_t o_dtype, void *o,
+                                    float *S_final, void *stream);
+
+/*
  * The two halves of kda_chunk_fwd, for callers that overlap or time them
  * separately; they need kda_chunk_prep_workspace_bytes() of workspace.
  *

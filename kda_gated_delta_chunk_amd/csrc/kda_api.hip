@@ -8,6 +8,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+// Device scratch of kda_chunk_fwd_no_alloc, in place of a workspace: one copy per GPU, held until the
+// process ends. Host code never uses this name as an address: each device's copy is found once with
+// hipGetSymbolAddress (device_scratch below) and that pointer is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[KDA_NO_ALLOC_SCRATCH_BYTES];
+
 namespace {
 
 bool supported_chunk(int32_t c) { return c == 16 || c == 64; }
@@ -134,7 +141,8 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
                           int32_t V, int32_t num_seqs, int32_t chunk, kda_dtype_t io, kda_gate_t gate,
                           kda_qk_norm_t qk_norm, kda_conv_t conv, const float *conv_w, kda_operands_t operands,
                           kda_dtype_t o_dtype, void *o, float *S_final, const void *workspace,
-                          size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a) {
+                          size_t workspace_bytes, bool need_prep, bool need_state, kda::PrefillArgs &a,
+                          bool no_alloc = false) {
     if (!valid_dtype(io) || !valid_dtype(o_dtype) || !valid_gate(gate) || !valid_qk_norm(qk_norm) ||
         !valid_conv(conv) || !valid_conv_w(conv, conv_w) || !valid_operands(operands))
         return KDA_ERROR_INVALID_VALUE;
@@ -158,7 +166,12 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
                                                                B * T, conv != KDA_CONV_NONE, h16)
                             : kda::prefill_workspace_bytes(nc, H, K, V, num_seqs, io == KDA_DTYPE_BF16, chunk, B * T,
                                                            conv != KDA_CONV_NONE, h16);
-    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    if (no_alloc) {  // the device scratch stands in for the workspace: its size is the limit
+        if (need > (size_t)KDA_NO_ALLOC_SCRATCH_BYTES) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+        workspace_bytes = (size_t)KDA_NO_ALLOC_SCRATCH_BYTES;
+    } else if (!workspace || workspace_bytes < need) {
+        return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    }
     st = check_device();
     if (st != KDA_SUCCESS) return st;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o_gate = o_gate;
@@ -175,6 +188,38 @@ kda_status_t prefill_args(const void *q, const void *k, const void *v, const voi
     a.chunk = chunk;
     a.n_chunks_max = nc;
     a.h16 = h16;
+    a.poison_on_error = false;
+    return KDA_SUCCESS;
+}
+
+// This device's copy of `scratch`, looked up once per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+kda_status_t device_scratch(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return KDA_ERROR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERROR_NOT_SUPPORTED;
+    if (stream) {  // the kernels run on the stream's device: it must be the one whose copy is used
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return KDA_ERROR_HIP;
+        }
+        if (sdev != dev) return KDA_ERROR_INVALID_VALUE;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return KDA_ERROR_HIP;
+    *out = g_scratch_ptr[dev];
     return KDA_SUCCESS;
 }
 }  // namespace
@@ -191,6 +236,25 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
                                    true, true, a);
     if (st != KDA_SUCCESS) return st;
     if (kda::launch_fwd(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
+    return KDA_SUCCESS;
+}
+
+kda_status_t kda_chunk_fwd_no_alloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                                    const void *o_gate, const float *S0, const int32_t *cu_seqlens, int64_t B,
+                                    int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs, int32_t chunk,
+                                    kda_dtype_t io, kda_gate_t gate, kda_qk_norm_t qk_norm, kda_conv_t conv,
+                                    const float *conv_w, kda_operands_t operands, kda_dtype_t o_dtype, void *o,
+                                    float *S_final, void *stream) {
+    kda::PrefillArgs a;
+    kda_status_t st = prefill_args(q, k, v, g, beta, o_gate, S0, cu_seqlens, B, T, H, K, V, num_seqs, chunk, io, gate,
+                                   qk_norm, conv, conv_w, operands, o_dtype, o, S_final, nullptr, 0, true, true, a,
+                                   true);
+    if (st != KDA_SUCCESS) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = device_scratch(s, &a.workspace);
+    if (st != KDA_SUCCESS) return st;
+    a.poison_on_error = true;  // the error word lives in the scratch, out of the caller's view
+    if (kda::launch_fwd(a, s) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }
 

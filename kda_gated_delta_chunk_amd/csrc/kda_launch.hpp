@@ -52,6 +52,7 @@ struct PrefillArgs {
     int32_t chunk;         // tokens per chunk (16 or 64)
     int64_t n_chunks_max;  // upper bound on chunks over all sequences
     bool h16;              // fp16 state-pass operands (FMT_FP16); else FMT_PAIRS
+    bool poison_on_error;  // after the prefill, fill o and S_final with NaN if the header's error word is set
 };
 
 // Workspace bytes for a prefill with at most n_chunks_max chunks over n_tokens (B * T) tokens as two

@@ -2188,6 +2188,22 @@ __global__ __launch_bounds__(1024) void kda_ws_init(WsHeader hd, WsHeader *__res
     if (cu) kda_chunk_table_body(cu, N, T_row, total_tokens, C, seq_tok, chunk_off);
 }
 
+// Fills o (I/O or bf16 dtype) and S_final with NaN when the header's error word is set (a wait gave up),
+// so that a caller with no view of the workspace cannot take such a result for a correct one.
+__global__ __launch_bounds__(256) void kda_poison_if_error(const WsHeader *__restrict__ hdr, void *__restrict__ o,
+                                                           bool o_bf16, int64_t n_o, float *__restrict__ Sf,
+                                                           int64_t n_s) {
+    if (hdr->error == 0) return;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_o; i += stride) {
+        if (o_bf16) reinterpret_cast<uint16_t *>(o)[i] = 0x7FC0u;
+        else reinterpret_cast<float *>(o)[i] = __builtin_nanf("");
+    }
+    if (Sf)
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_s; i += stride)
+            Sf[i] = __builtin_nanf("");
+}
+
 }  // namespace kda
 
 // ------------------------------------------------------------------ host side
@@ -2494,7 +2510,21 @@ size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32
     return b;
 }
 
+hipError_t launch_fwd_body(const PrefillArgs &a, hipStream_t st);
+
 hipError_t launch_fwd(const PrefillArgs &a, hipStream_t st) {
+    hipError_t e = launch_fwd_body(a, st);
+    if (e != hipSuccess || !a.poison_on_error) return e;
+    const int64_t n_o = a.B * a.T * a.H * a.V, n_s = (int64_t)a.num_seqs * a.H * a.K * a.V;
+    const int64_t n = n_o > n_s ? n_o : n_s;
+    const unsigned grid = (unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_poison_if_error, dim3(grid), dim3(256), 0, st, ws_ptrs(a).hdr, a.o, a.o_bf16, n_o,
+                       a.S_final, n_s);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_body(const PrefillArgs &a, hipStream_t st) {
     const size_t two_pass = prefill_workspace_bytes(a.n_chunks_max, a.H, a.K, a.V, a.num_seqs, a.io_bf16, a.chunk,
                                                     a.B * a.T, a.conv != 0, a.h16);
     if (a.workspace_bytes < two_pass && fused_possible(a.chunk, a.conv != 0)) {

@@ -278,6 +278,40 @@ def test_decode_empty_batch_is_a_no_op():
     assert _dec(N=0, q=None, S=None) == 0
 
 
+def _fwd_no_alloc(**kw):
+    lib = _lib.load()
+    a = dict(q=A, k=A, v=A, g=A, beta=A, og=None, S0=None, cu=None, B=1, T=64, H=2, K=32, V=32, N=1, chunk=16, io=1,
+             gate=0, qkn=0, conv=0, cw=None, ops=0, odt=1, o=A, Sf=A, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd_no_alloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["og"], a["S0"], a["cu"], a["B"],
+                                      a["T"], a["H"], a["K"], a["V"], a["N"], a["chunk"], a["io"], a["gate"], a["qkn"],
+                                      a["conv"], a["cw"], a["ops"], a["odt"], a["o"], a["Sf"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID),
+    (dict(o=A + 8), INVALID),
+    (dict(K=48), UNSUP),
+    (dict(chunk=64, ops=1), UNSUP),
+    (dict(S0=A + 4096, Sf=A + 4096), INVALID),
+    # the least workspace over the scratch's 16 MiB: a convolution keeps the convolved q, k, v (4096 x 8 heads)
+    (dict(T=4096, H=8, K=128, V=128, conv=2, cw=A), WS_SMALL),
+    # ... or the chunk table of 2M packed sequences
+    (dict(T=1 << 21, H=1, N=1 << 21, cu=A), WS_SMALL),
+])
+def test_no_alloc_rejects(kw, expect):
+    assert _fwd_no_alloc(**kw) == expect
+
+
+def test_no_alloc_scratch_limits():
+    # what kda_chunk_fwd_no_alloc accepts is what fits in its scratch under kda_chunk_fwd's least workspace
+    lib = _lib.load()
+    least = lib.kda_chunk_fwd_min_workspace_bytes
+    assert least(1, 4096, 8, 128, 128, 1, 16, 1, 2, 0) > _lib.NO_ALLOC_SCRATCH_BYTES
+    assert least(1, 1 << 21, 1, 32, 32, 1 << 21, 16, 1, 0, 0) > _lib.NO_ALLOC_SCRATCH_BYTES
+    assert least(1, 1 << 20, 96, 128, 128, 1, 16, 1, 0, 0) <= _lib.NO_ALLOC_SCRATCH_BYTES  # 1M tokens, fused
+
+
 def _bwd(**kw):
     lib = _lib.load()
     a = dict(q=A, k=A + 4096, v=A + 8192, g=A + 12288, beta=A + 16384, og=None, S0=None, cu=None, do=A + 20480,
@@ -376,6 +410,8 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _state() == NO_DEV
     assert _dec() == NO_DEV
     assert _bwd() == NO_DEV
+    assert _fwd_no_alloc() == NO_DEV
+    assert _fwd_no_alloc(T=1 << 20, H=96, K=128, V=128) == NO_DEV  # fits in the scratch as the fused kernel
     assert _bwd(qk=1, conv=2, cw=CW, dcw=DCW) == NO_DEV
     out = ctypes.c_int32(0)
     assert _lib.load().kda_workspace_status(A, 1024, ctypes.byref(out), None) == NO_DEV
