@@ -259,6 +259,28 @@ __device__ __forceinline__ void load8(const void *base, int64_t idx, float (&x)[
     }
 }
 
+// The short convolution of one 8-channel run in the 16-token prep's lane layout (lane 16 ag + r holds
+// token r of the sub-tile): y_t = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3} with w = taps[c] =
+// (w0, w1, w2, w3), then SiLU when act == 2. x is this lane's raw run; hx, on lanes 13..15, the run of
+// token r - 16 (the three rows before the sub-tile; zeros before the sequence start). Token r - d is
+// lane r - d of x or, for r < d, lane r - d + 16 of hx: one rotation of the 16-lane row by d of a
+// source that takes hx on lanes 16 - d .. 15 (the lanes whose values wrap around) and x elsewhere.
+__device__ __forceinline__ void conv_run8(const float (&x)[8], const float (&hx)[8], const float4 *__restrict__ taps,
+                                          int r, int act, float (&y)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 w = taps[j];
+        const float p1 = dpp_f<0x121, false>(r >= 15 ? hx[j] : x[j]);  // row_ror:1
+        const float p2 = dpp_f<0x122, false>(r >= 14 ? hx[j] : x[j]);  // row_ror:2
+        const float p3 = dpp_f<0x123, false>(r >= 13 ? hx[j] : x[j]);  // row_ror:3
+        float v = w.w * x[j];
+        v = __builtin_fmaf(w.z, p1, v);
+        v = __builtin_fmaf(w.y, p2, v);
+        v = __builtin_fmaf(w.x, p3, v);
+        y[j] = act == 2 ? v * sigmoid_f(v) : v;
+    }
+}
+
 // Divide this lane's part of a token row by the row's L2 norm, sqrt(|x|^2 + 1e-6): the row's K
 // channels are spread over the four lane groups of the wavefront (lanes r, r + 16, r + 32, r + 48).
 // Every lane of the wavefront must call it.
@@ -524,6 +546,11 @@ struct PrepParams {
     int32_t H, N;
     int32_t gate;    // 0: g is the log-decay; 1: g is the gate pre-activation (gate_log2_decay)
     int32_t qknorm;  // 1: q and k rows are L2-normalised as they are read (l2norm_row)
+    // the 16-token bf16 prep with a convolution (CONV) convolves the raw q and k rows as it reads them:
+    // taps [H][cw][4] (q channels first, then k), cw = K + K + V, conv = 1 (plain) or 2 (with SiLU); the
+    // 64-token and the fp32 preps read q and k convolved in the workspace (fp32) instead
+    const float *conv_w;
+    int32_t conv, cw;
 
     ChunkTab tab;
     char *frags;
@@ -566,13 +593,40 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
     const bool valid = r < nvalid;
     const int64_t row = (tok0 + (valid ? r : nvalid - 1)) * H + h;
     float qv[KS][8], kv[KS][8], bl[KS][8];
-    if constexpr (CONV) {
-        // q and k were convolved into fp32 arrays of the workspace (kda_conv_x); g as given
+    if constexpr (CONV && BF) {
+        // raw q and k rows convolved here (conv_run8): lanes 13..15 also read the three rows before the
+        // sub-tile when the sequence has them (a sub-tile starts at the sequence start or 16k tokens
+        // after it); g as given. (fp32 I/O reads q and k convolved in the workspace instead, through
+        // the plain loads below: the fp32 operands leave no registers for the convolution.)
+        const bool hv = r >= 13 && tok0 - 16 + r >= tab.tok(n);
+        const int64_t hrow = hv ? (tok0 - 16 + r) * H + h : row;  // other lanes re-read their own row
+        // the head's q and k taps (2K float4, contiguous in conv_w) staged in the K*exp(b_C-b) area, free
+        // until the decay-scaled operands are formed (64K bytes, the taps 32K), and read back from there
+        // (the 16 lanes of a row read the same taps: LDS broadcasts)
+        {
+            const float4 *src = reinterpret_cast<const float4 *>(pa.conv_w) + (size_t)h * pa.cw;
+            float4 *dst = reinterpret_cast<float4 *>(kx);
+#pragma unroll
+            for (int i = 0; i < 2 * K / 64; ++i) dst[lane + 64 * i] = src[lane + 64 * i];
+        }
+        lds_sync();
+        const float4 *tq = reinterpret_cast<const float4 *>(kx);
+        const float4 *tk = tq + K;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            load8<false>(qp, row * K + 32 * s + 8 * ag, qv[s]);
-            load8<false>(kp, row * K + 32 * s + 8 * ag, kv[s]);
-            load8<BF>(gp, row * K + 32 * s + 8 * ag, bl[s]);
+            const int c = 32 * s + 8 * ag;
+            float x[8], hx[8];
+            load8<BF>(qp, row * K + c, x);
+            load8<BF>(qp, hrow * K + c, hx);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hx[j] = hv ? hx[j] : 0.f;
+            conv_run8(x, hx, tq + c, r, pa.conv, qv[s]);
+            load8<BF>(kp, row * K + c, x);
+            load8<BF>(kp, hrow * K + c, hx);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hx[j] = hv ? hx[j] : 0.f;
+            conv_run8(x, hx, tk + c, r, pa.conv, kv[s]);
+            load8<BF>(gp, row * K + c, bl[s]);
         }
     } else {
 #pragma unroll
@@ -2235,6 +2289,10 @@ size_t chunk_bytes_rt(bool bf, int K, int chunk, bool h16) {
     return bf ? chunk_bytes_k<true, 1>(K) : chunk_bytes_k<false, 1>(K);
 }
 
+// Where q and k are convolved: by kda_conv_x into the workspace (fp32) for the 64-token prep and for
+// fp32 I/O, by the 16-token bf16 prep itself as it reads the raw rows.
+bool qk_conv_in_workspace(bool conv, int32_t chunk, bool io_bf16) { return conv && (chunk == 64 || !io_bf16); }
+
 struct WsPtrs {
     WsHeader *hdr;
     int64_t *seq_tok;
@@ -2243,8 +2301,8 @@ struct WsPtrs {
     // calls with a convolution only:
     char *vconv;     // convolved v [tokens][H][V]: fp32, or on a bf16 path the hi parts,
     char *vconv_lo;  // and here the lo parts (v - hi rounded to bf16)
-    char *qconv;     // convolved q [tokens][H][K] fp32
-    char *kconv;     // convolved k [tokens][H][K] fp32
+    char *qconv;     // convolved q [tokens][H][K] fp32 (qk_conv_in_workspace only)
+    char *kconv;     // convolved k [tokens][H][K] fp32 (qk_conv_in_workspace only)
 };
 // Workspace: header | chunk table | per-(chunk, head) factors | convolved q, k, v (with a convolution).
 // The sizes depend only on the call's sizes and operand format, as prefill_workspace_bytes counts them.
@@ -2288,8 +2346,12 @@ ChunkTab chunk_tab(const PrefillArgs &a, const WsPtrs &w) {
 
 PrepParams prep_params(const PrefillArgs &a, const WsPtrs &w) {
     PrepParams p;
-    p.q = a.conv ? static_cast<const void *>(w.qconv) : a.q;  // with a convolution: fp32 convolved q, k
-    p.k = a.conv ? static_cast<const void *>(w.kconv) : a.k;
+    // with a convolution the 64-token and the fp32 preps read q and k convolved in the workspace (fp32);
+    // the 16-token bf16 prep convolves the raw rows itself
+    const bool qk_ws = qk_conv_in_workspace(a.conv != 0, a.chunk, a.io_bf16);
+    p.q = qk_ws ? static_cast<const void *>(w.qconv) : a.q;
+    p.k = qk_ws ? static_cast<const void *>(w.kconv) : a.k;
+    p.conv_w = a.conv_w; p.conv = a.conv; p.cw = 2 * a.K + a.V;
     p.g = a.g; p.beta = a.beta;
     p.H = a.H; p.N = a.num_seqs;
     p.gate = a.gate_sigmoid ? 1 : 0;
@@ -2369,7 +2431,7 @@ hipError_t launch_conv_v(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) 
 }
 template <bool BF, int K>
 hipError_t launch_conv_qk(const PrefillArgs &a, const WsPtrs &w, hipStream_t st) {
-    if (!a.conv) return hipSuccess;
+    if (!qk_conv_in_workspace(a.conv != 0, a.chunk, a.io_bf16)) return hipSuccess;
     hipError_t e = launch_conv<BF, K, 0>(a, w, a.q, 0, w.qconv, nullptr, st);
     return e != hipSuccess ? e : launch_conv<BF, K, 0>(a, w, a.k, a.K, w.kconv, nullptr, st);
 }
@@ -2505,8 +2567,9 @@ size_t prefill_min_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, i
 size_t prefill_workspace_bytes(int64_t n_chunks_max, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                bool io_bf16, int32_t chunk, int64_t n_tokens, bool conv, bool h16) {
     size_t b = table_bytes(num_seqs) + frags_bytes(n_chunks_max, H, K, io_bf16, chunk, h16);
-    if (conv)  // convolved v (fp32, or bf16 hi + lo), q and k (fp32)
-        b += align_up((size_t)n_tokens * H * V * 4) + 2 * align_up((size_t)n_tokens * H * K * 4);
+    if (conv)  // convolved v (fp32, or bf16 hi + lo); q and k (fp32) where the prep reads them convolved
+        b += align_up((size_t)n_tokens * H * V * 4) +
+             (qk_conv_in_workspace(conv, chunk, io_bf16) ? 2 * align_up((size_t)n_tokens * H * K * 4) : 0);
     return b;
 }
 

@@ -65,9 +65,11 @@ def test_workspace_bytes():
         assert f(1, 4096, 0, 128, 128, 1, 16, 1) == 0
         assert f(1, 4096, 96, 128, 128, 1, 16, 1, conv=3) == 0
         assert f(1, 4096, 96, 128, 128, 1, 16, 1, operands=2) == 0
-    # a convolution adds exactly the convolved v (B*T*H*V fp32 elements, or bf16 hi + lo parts) and the
-    # convolved q and k (fp32)
-    assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) > n1 + 4096 * 96 * 128 * 4
+    # a convolution adds exactly the convolved v (B*T*H*V fp32 elements, or bf16 hi + lo parts), and where
+    # the prep reads them convolved (fp32 I/O, 64-token chunks) the convolved q and k (fp32); the 16-token
+    # bf16 prep convolves q and k as it reads them
+    assert ws(1, 4096, 96, 128, 128, 1, 16, 1, conv=1) == n1 + 4096 * 96 * 128 * 4
+    assert ws(1, 4096, 96, 128, 128, 1, 64, 1, conv=1) == n64 + 4096 * 96 * (128 + 2 * 128) * 4
     assert ws(1, 4096, 96, 64, 32, 1, 16, 0, conv=2) == ws(1, 4096, 96, 64, 32, 1, 16, 0) + 4096 * 96 * (32 + 2 * 64) * 4
     # fp16 operands: smaller factor blocks; only bf16 I/O at 16-token chunks without a convolution
     n16 = ws(1, 4096, 96, 128, 128, 1, 16, 1, operands=1)
