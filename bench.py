@@ -187,16 +187,40 @@ def time_decode(w, steps, dev, gate="log_decay", qk_norm=False):
             "bytes_per_step": bytes_step, "N": N, "H": H}
 
 
+def time_copy(dev, nbytes=2 << 30, reps=10):
+    """A plain device-to-device copy of nbytes (torch's copy kernel): the HBM rate a streaming kernel
+    reaches on this GPU (bytes read + bytes written per second), as a reference for the rooflines."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_copied": nbytes, "ms": ms, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def backward_flops(T, H, K, V):
     """Flops of the per-token backward per call: one forward recompute (decay, read, write: 5KV) plus the
     reverse step (G += q do^T, S_t do, G^T k, beta G d - A dv, G - k dv^T, rowsum(GA * A), decay: 19KV)."""
     return 24 * K * V * T * H
 
 
-def time_backward(w, steps, warmup, dev):
-    """kda_chunk_bwd on the prefill workload's inputs, dL/do ~ N(0, 1), no dL/dS_final."""
+def time_backward(w, steps, warmup, dev, prologue=False):
+    """kda_chunk_bwd on the prefill workload's inputs, dL/do ~ N(0, 1), no dL/dS_final. prologue: the
+    forward normalised q and k and ran the short convolution with SiLU (raw k, taps ~ N(0, 0.5^2)), so the
+    gradients also run back through both and dL/d(taps) is formed."""
     lib = _lib.load()
-    inp = synth.workload_prefill_inputs(w, device=dev)
+    inp = synth.workload_prefill_inputs(w, device=dev, raw_k=prologue)
     B, T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
     do, _ = synth.output_grads(B, T, H, V, w.io, w.seed, dev)
@@ -205,17 +229,19 @@ def time_backward(w, steps, warmup, dev):
                                                                     torch.empty((B, T, H), **f32)]
     dq, dk, dg, dv, db = (t.data_ptr() for t in outs)
     dS0 = torch.empty((B, H, K, V), **f32)
-    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B, 0, 0)
+    qc, cc = (_lib.KDA_QK_L2NORM, _lib.CONVS["short4_silu"]) if prologue else (0, 0)
+    cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev) if prologue else None
+    dcw = torch.empty((H, 2 * K + V, 4), **f32) if prologue else None
+    cwp, dcwp = (cw.data_ptr(), dcw.data_ptr()) if prologue else (None, None)
+    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B, qc, cc)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def bwd():
         _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, None, do.data_ptr(),
-                                     None, B, T, H, K, V, B, 1, 0, 0, 0, None, dq, dk, dv, dg, db, None, None,
-                                     dS0.data_ptr(),
-                                     ws.data_ptr(), wsb,
-                                     stream.cuda_stream), "kda_chunk_bwd")
+                                     None, B, T, H, K, V, B, 1, 0, qc, cc, cwp, dq, dk, dv, dg, db, None, dcwp,
+                                     dS0.data_ptr(), ws.data_ptr(), wsb, stream.cuda_stream), "kda_chunk_bwd")
 
     for _ in range(warmup):
         bwd()
@@ -273,7 +299,7 @@ def mfma_from_counters(sq_csv, out_path):
         raise SystemExit("%s was taken on other kernel sources; take FETCH_SIZE/WRITE_SIZE again first" % out_path)
     vals = defaultdict(list)
     for r in csv.DictReader(open(sq_csv)):
-        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         if "kda" in name and r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
             vals[name].append(float(r["Counter_Value"]))
     for k, v in vals.items():
@@ -294,10 +320,12 @@ def traffic_from_counters(fetch_csv, write_csv, out_path):
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        # the calibration copy is the run's first device copy of at least 256 MiB (rows are in dispatch order)
+        copy = next(float(r["Counter_Value"]) for r in rows
+                    if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024.0 >= (1 << 28))
         vals = defaultdict(list)
         for r in rows:
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             if "kda" in name:
                 vals[name].append(float(r["Counter_Value"]))
         return copy, {k: sum(v) / len(v) for k, v in vals.items()}
@@ -517,6 +545,10 @@ def main():
         out["decode"]["gate_fused_ms_per_step"] = dg["ms_per_step"]
         dn = time_decode(wd, args.decode_steps, dev, gate="scaled_sigmoid", qk_norm=True)
         out["decode"]["gate_and_qk_norm_fused_ms_per_step"] = dn["ms_per_step"]
+        cp = time_copy(dev) if not args.counters else {"GB_per_s": float("nan")}
+        out["hbm_copy_reference"] = dict(cp, what="torch device-to-device copy of 2 GiB: read + write bytes "
+                                                  "per second, the rate a plain streaming kernel reaches")
+        out["decode"]["frac_of_copy_rate"] = gbs / cp["GB_per_s"]
     if not args.no_backward:
         say("backward %s: warmup 3, steps 10" % w.name)
         rb = time_backward(w, 10, 3, dev)
@@ -531,6 +563,10 @@ def main():
                          "achieved": tfs, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_VECTOR_PEAK_TFS, "algorithmic_flops_per_call": fl,
                          "timed": "whole call (3 launches)"}}
+        say("backward with the prologue (q/k norm, short convolution with SiLU): warmup 2, steps 5")
+        rp = time_backward(w, 5, 2, dev, prologue=True)
+        out["backward"]["with_prologue"] = {"ms_per_step": rp["ms"], "workspace_bytes": rp["ws_bytes"],
+                                            "tokens_per_s": rp["B"] * rp["T"] / (rp["ms"] * 1e-3)}
     out["device_errors"] = errors
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle)")

@@ -410,31 +410,96 @@ __device__ __forceinline__ int bwd_find_seq(const int64_t *seq_tok, int N, int64
     return lo;
 }
 
-// The convolution (and SiLU for act == 2) of one tensor x [tokens][H][D] into out (fp32), one thread per
-// (token, head, channel); rows of tokens outside every sequence get zeros.
+// Eight consecutive values of a row (one 16-byte bf16 load, or two fp32 loads).
+template <bool BF>
+__device__ __forceinline__ void bwd_ld8(const typename IO<BF>::T *base, int64_t idx, float (&x)[8]) {
+    if constexpr (BF) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(base + idx);
+        x[0] = bf_lo(w.x); x[1] = bf_hi(w.x); x[2] = bf_lo(w.y); x[3] = bf_hi(w.y);
+        x[4] = bf_lo(w.z); x[5] = bf_hi(w.z); x[6] = bf_lo(w.w); x[7] = bf_hi(w.w);
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(base + idx);
+        const float4 b = *reinterpret_cast<const float4 *>(base + idx + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+}
+__device__ __forceinline__ void bwd_st8(float *p, const float (&y)[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(y[4], y[5], y[6], y[7]);
+}
+
+constexpr int CONV_FWD_TILE = 16;  // flat tokens per thread of the convolution's forward
+
+// The convolution (and SiLU for act == 2) of one tensor x [tokens][H][D] into out (fp32). One thread per
+// (16-token tile of the flat rows, head, 8-channel run; runs of a row on consecutive lanes): it loads its
+// taps once and walks the tile's tokens with the three previous rows in registers, starting them from zero
+// at each sequence start. Rows of tokens outside every sequence get zeros.
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void kda_bwd_conv_fwd(const typename IO<BF>::T *__restrict__ x,
                                                         const float *__restrict__ taps, int32_t CW, int32_t act,
                                                         int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
-                                                        int64_t n_el, float *__restrict__ out) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n_el) return;
-    const int c = (int)(idx % D);
-    const int64_t row = idx / D;
-    const int h = (int)(row % H);
-    const int64_t t = row / H;
-    if (t < seq_tok[0] || t >= seq_tok[N]) {
-        out[idx] = 0.f;
-        return;
+                                                        int64_t total, int64_t n_items, float *__restrict__ out) {
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= n_items) return;
+    const int c0 = 8 * (int)(gid % G);
+    const int64_t rest = gid / G;
+    const int h = (int)(rest % H);
+    const int64_t t0 = (rest / H) * CONV_FWD_TILE;
+    const int64_t t1 = t0 + CONV_FWD_TILE < total ? t0 + CONV_FWD_TILE : total;
+    const int64_t lo = seq_tok[0], hi = seq_tok[N];
+    float4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c0 + j) * 4);
+    auto row = [&](int64_t t) { return (t * H + h) * D + c0; };
+    float p[3][8];  // p[d - 1] = row t - d of t's sequence (zeros before its start)
+    int n = 0;
+    int64_t s0 = lo;
+    if (t0 >= lo && t0 < hi) {
+        n = bwd_find_seq(seq_tok, N, t0);
+        s0 = seq_tok[n];
     }
-    const int64_t s0 = seq_tok[bwd_find_seq(seq_tok, N, t)];
-    const float4 w = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c) * 4);
-    const int64_t step = (int64_t)H * D;
-    float y = w.w * IO<BF>::ld(x, idx);
-    if (t - 1 >= s0) y = __builtin_fmaf(w.z, IO<BF>::ld(x, idx - step), y);
-    if (t - 2 >= s0) y = __builtin_fmaf(w.y, IO<BF>::ld(x, idx - 2 * step), y);
-    if (t - 3 >= s0) y = __builtin_fmaf(w.x, IO<BF>::ld(x, idx - 3 * step), y);
-    out[idx] = act == 2 ? y * sigmoid_f(y) : y;
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        if (t0 >= lo && t0 < hi && t0 - d >= s0) bwd_ld8<BF>(x, row(t0 - d), p[d - 1]);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[d - 1][j] = 0.f;
+    }
+    for (int64_t t = t0; t < t1; ++t) {
+        float y[8];
+        if (t < lo || t >= hi) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = 0.f;
+            bwd_st8(out + row(t), y);
+            continue;
+        }
+        bool fresh = false;  // t starts a sequence: no history
+        while (n + 1 < N && seq_tok[n + 1] <= t) {
+            ++n;
+            fresh = true;
+        }
+        if (t == seq_tok[n]) fresh = true;
+        if (fresh)
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p[d][j] = 0.f;
+        float xt[8];
+        bwd_ld8<BF>(x, row(t), xt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = w[j].w * xt[j];
+            v = __builtin_fmaf(w[j].z, p[0][j], v);
+            v = __builtin_fmaf(w[j].y, p[1][j], v);
+            v = __builtin_fmaf(w[j].x, p[2][j], v);
+            y[j] = act == 2 ? v * sigmoid_f(v) : v;
+            p[2][j] = p[1][j];
+            p[1][j] = p[0][j];
+            p[0][j] = xt[j];
+        }
+        bwd_st8(out + row(t), y);
+    }
 }
 
 // Sum over the 16 lanes of an aligned lane group.
@@ -500,10 +565,11 @@ __global__ __launch_bounds__(256) void kda_bwd_norm_back(const float *__restrict
 constexpr int CONV_TILE = 64;  // flat tokens per thread of the convolution's reverse
 
 // The convolution's reverse for one tensor: raw x [tokens][H][D] (I/O dtype), dz = dL/d(conv output)
-// [tokens][H][D] fp32. One thread per (64-token tile of the flat rows, head, channel) walks the tile's
-// tokens and the three after it, forming dL/dy_t = dz_t act'(y_t) (y_t recomputed), and writes dL/dx for
-// the tile's tokens (rows outside every sequence are not written) and the tile's partial sums of dL/dw,
-// dw_part[tile][h][coff + c][4].
+// [tokens][H][D] fp32. One thread per (64-token tile of the flat rows, head, 8-channel run) walks the
+// tile's tokens and the three after it with windows in registers: the raw rows t-3..t (to recompute y_t,
+// zeros before the sequence start) and dL/dy of tokens t-3..t with their sequence ids. It forms
+// dL/dy_t = dz_t act'(y_t), writes dL/dx_{t-3} (rows outside every sequence are not written) and sums the
+// tile's part of dL/dw into dw_part[tile][h][coff + c][4].
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::T *__restrict__ x,
                                                          const float *__restrict__ dz, const float *__restrict__ taps,
@@ -511,69 +577,114 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::
                                                          const int64_t *__restrict__ seq_tok, int64_t total,
                                                          int64_t n_items, float *__restrict__ dx,
                                                          float *__restrict__ dw_part) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n_items) return;
-    const int c = (int)(idx % D);
-    const int64_t rest = idx / D;
+    constexpr int G = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= n_items) return;
+    const int c0 = 8 * (int)(gid % G);
+    const int64_t rest = gid / G;
     const int h = (int)(rest % H);
     const int64_t tile = rest / H;
     const int64_t t0 = tile * CONV_TILE, t1 = (t0 + CONV_TILE < total) ? t0 + CONV_TILE : total;
     const int64_t lo = seq_tok[0], hi = seq_tok[N];
-    const float4 w = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c) * 4);
-    const int64_t step = (int64_t)H * D;
-    auto el = [&](int64_t t) { return (t * H + h) * D + c; };
-    // sequence of token t and its start (sid -1: outside every sequence or past the rows)
-    int n = (t0 >= lo && t0 < hi) ? bwd_find_seq(seq_tok, N, t0) : (t0 < lo ? 0 : N);
-    // window of dL/dy and sequence ids for tokens t-3 .. t (index 3 = t)
-    float dyw[4] = {0.f, 0.f, 0.f, 0.f};
+    float4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const float4 *>(taps + ((size_t)h * CW + c0 + j) * 4);
+    auto row = [&](int64_t t) { return (t * H + h) * D + c0; };
+    int n = 0;
+    int64_t s0 = lo;
+    if (t0 >= lo && t0 < hi) {
+        n = bwd_find_seq(seq_tok, N, t0);
+        s0 = seq_tok[n];
+    }
+    float xw[3][8];  // raw rows t-1, t-2, t-3 of t's sequence
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        if (t0 >= lo && t0 < hi && t0 - d >= s0) bwd_ld8<BF>(x, row(t0 - d), xw[d - 1]);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xw[d - 1][j] = 0.f;
+    }
+    float dyw[4][8];  // dL/dy of tokens t-3 .. t (index 3 = t)
     int sw[4] = {-1, -1, -1, -1};
-    float dw0 = 0.f, dw1 = 0.f, dw2 = 0.f, dw3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dyw[i][j] = 0.f;
+    float dw[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dw[j][0] = dw[j][1] = dw[j][2] = dw[j][3] = 0.f;
     for (int64_t t = t0; t < t1 + 3; ++t) {
         int sid = -1;
-        float dy = 0.f;
+        float dy[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dy[j] = 0.f;
         if (t < total && t >= lo && t < hi) {
-            while (n + 1 < N && seq_tok[n + 1] <= t) ++n;
-            sid = n;
-            const int64_t s0 = seq_tok[n];
-            const float x0 = IO<BF>::ld(x, el(t));
-            const float x1 = t - 1 >= s0 ? IO<BF>::ld(x, el(t) - step) : 0.f;
-            const float x2 = t - 2 >= s0 ? IO<BF>::ld(x, el(t) - 2 * step) : 0.f;
-            const float x3 = t - 3 >= s0 ? IO<BF>::ld(x, el(t) - 3 * step) : 0.f;
-            float y = w.w * x0;
-            y = __builtin_fmaf(w.z, x1, y);
-            y = __builtin_fmaf(w.y, x2, y);
-            y = __builtin_fmaf(w.x, x3, y);
-            dy = dz[el(t)];
-            if (act == 2) {
-                const float sg = sigmoid_f(y);
-                dy *= sg * __builtin_fmaf(y, 1.f - sg, 1.f);
+            bool fresh = false;
+            while (n + 1 < N && seq_tok[n + 1] <= t) {
+                ++n;
+                fresh = true;
             }
-            if (t < t1) {  // the taps' sums over this tile's tokens
-                dw3 = __builtin_fmaf(dy, x0, dw3);
-                dw2 = __builtin_fmaf(dy, x1, dw2);
-                dw1 = __builtin_fmaf(dy, x2, dw1);
-                dw0 = __builtin_fmaf(dy, x3, dw0);
+            if (t == seq_tok[n]) fresh = true;
+            if (fresh)
+#pragma unroll
+                for (int d = 0; d < 3; ++d)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xw[d][j] = 0.f;
+            sid = n;
+            float xt[8], g[8];
+            bwd_ld8<BF>(x, row(t), xt);
+            bwd_ld8<false>(dz, row(t), g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float y = w[j].w * xt[j];
+                y = __builtin_fmaf(w[j].z, xw[0][j], y);
+                y = __builtin_fmaf(w[j].y, xw[1][j], y);
+                y = __builtin_fmaf(w[j].x, xw[2][j], y);
+                float d = g[j];
+                if (act == 2) {
+                    const float sg = sigmoid_f(y);
+                    d *= sg * __builtin_fmaf(y, 1.f - sg, 1.f);
+                }
+                dy[j] = d;
+                if (t < t1) {  // the taps' sums over this tile's tokens
+                    dw[j][3] = __builtin_fmaf(d, xt[j], dw[j][3]);
+                    dw[j][2] = __builtin_fmaf(d, xw[0][j], dw[j][2]);
+                    dw[j][1] = __builtin_fmaf(d, xw[1][j], dw[j][1]);
+                    dw[j][0] = __builtin_fmaf(d, xw[2][j], dw[j][0]);
+                }
+                xw[2][j] = xw[1][j];
+                xw[1][j] = xw[0][j];
+                xw[0][j] = xt[j];
             }
         }
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
-            dyw[i] = dyw[i + 1];
             sw[i] = sw[i + 1];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dyw[i][j] = dyw[i + 1][j];
         }
-        dyw[3] = dy;
         sw[3] = sid;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dyw[3][j] = dy[j];
         // dL/dx_tau for tau = t - 3: w3 dy_tau + w2 dy_{tau+1} + w1 dy_{tau+2} + w0 dy_{tau+3}, same sequence
         const int64_t tau = t - 3;
         if (tau >= t0 && sw[0] >= 0) {
-            float g = w.w * dyw[0];
-            if (sw[1] == sw[0]) g = __builtin_fmaf(w.z, dyw[1], g);
-            if (sw[2] == sw[0]) g = __builtin_fmaf(w.y, dyw[2], g);
-            if (sw[3] == sw[0]) g = __builtin_fmaf(w.x, dyw[3], g);
-            dx[el(tau)] = g;
+            const bool m1 = sw[1] == sw[0], m2 = sw[2] == sw[0], m3 = sw[3] == sw[0];
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float gx = w[j].w * dyw[0][j];
+                if (m1) gx = __builtin_fmaf(w[j].z, dyw[1][j], gx);
+                if (m2) gx = __builtin_fmaf(w[j].y, dyw[2][j], gx);
+                if (m3) gx = __builtin_fmaf(w[j].x, dyw[3][j], gx);
+                o[j] = gx;
+            }
+            bwd_st8(dx + row(tau), o);
         }
     }
-    *reinterpret_cast<float4 *>(dw_part + ((size_t)tile * H + h) * CW * 4 + (size_t)(coff + c) * 4) =
-        make_float4(dw0, dw1, dw2, dw3);
+    float *dst = dw_part + ((size_t)tile * H + h) * CW * 4 + (size_t)(coff + c0) * 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4 *>(dst + 4 * j) = make_float4(dw[j][0], dw[j][1], dw[j][2], dw[j][3]);
 }
 
 // dL/dw = the tiles' partial sums added in tile order (deterministic); one thread per (head, channel, tap).
@@ -652,7 +763,7 @@ void conv_back_one(const BackwardArgs &a, const BwdWs &w, const void *x, const f
                    hipStream_t st) {
     using T = typename IO<BF>::T;
     const int64_t total = a.B * a.T;
-    const int64_t items = conv_tiles(total) * a.H * D;
+    const int64_t items = conv_tiles(total) * a.H * (D / 8);
     if (items > 0)
         hipLaunchKernelGGL((kda_bwd_conv_back<BF, D>), dim3(blocks_of(items)), dim3(256), 0, st, (const T *)x, dz,
                            a.conv_w + (size_t)coff * 4, 2 * a.K + a.V, coff, a.conv, a.H, a.num_seqs, w.seq_tok,
@@ -674,16 +785,15 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
     }
     // prologue, forward: convolution into xq, xk, xv; normalisation of q and k (in place, or from the input)
     const int32_t CW = 2 * K + V;
-    if (conv) {
-        const int64_t nk = n_rows * K, nv = n_rows * V;
-        if (nk > 0) {
-            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(nk)), dim3(256), 0, st, (const T *)a.q,
-                               a.conv_w, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nk, w.xq);
-            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(nk)), dim3(256), 0, st, (const T *)a.k,
-                               a.conv_w + (size_t)K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nk, w.xk);
-            hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, V>), dim3(blocks_of(nv)), dim3(256), 0, st, (const T *)a.v,
-                               a.conv_w + (size_t)2 * K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, nv, w.xv);
-        }
+    if (conv && n_tok > 0) {
+        const int64_t tiles = (n_tok + CONV_FWD_TILE - 1) / CONV_FWD_TILE;
+        const int64_t ik = tiles * a.H * (K / 8), iv = tiles * a.H * (V / 8);
+        hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.q, a.conv_w,
+                           CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, ik, w.xq);
+        hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.k,
+                           a.conv_w + (size_t)K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, ik, w.xk);
+        hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, V>), dim3(blocks_of(iv)), dim3(256), 0, st, (const T *)a.v,
+                           a.conv_w + (size_t)2 * K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, iv, w.xv);
     }
     if (norm && n_rows > 0) {
         if (conv) {
