@@ -288,9 +288,9 @@ def mfma_busy_frac(kernel_prefix, ms):
 
 
 def mfma_from_counters(sq_csv, out_path):
-    """Add each kda kernel's SQ_VALU_MFMA_BUSY_CYCLES per launch (average over its dispatches, summed
-    over the device) from a rocprofv3 counter run of `bench.py --counters` to the counter summary,
-    if that summary was taken on the same kernel sources."""
+    """Add each kda kernel's SQ_VALU_MFMA_BUSY_CYCLES per launch (summed over the device; average over its
+    first bench leg, as the byte counters) from a rocprofv3 counter run of `bench.py --counters` to the
+    counter summary, if that summary was taken on the same kernel sources."""
     import csv
     from collections import defaultdict
     with open(out_path) as fh:
@@ -298,12 +298,13 @@ def mfma_from_counters(sq_csv, out_path):
     if out.get("csrc_hash") != csrc_hash():
         raise SystemExit("%s was taken on other kernel sources; take FETCH_SIZE/WRITE_SIZE again first" % out_path)
     vals = defaultdict(list)
-    for r in csv.DictReader(open(sq_csv)):
+    rows = sorted(csv.DictReader(open(sq_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
         name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         if "kda" in name and r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
             vals[name].append(float(r["Counter_Value"]))
     for k, v in vals.items():
-        out["kernels"].setdefault(k, {})["mfma_busy_cycles"] = sum(v) / len(v)
+        out["kernels"].setdefault(k, {})["mfma_busy_cycles"] = sum(v[:3]) / len(v[:3])
     with open(out_path, "w") as fh:
         fh.write(json.dumps(out, indent=1) + "\n")
     return out
@@ -320,7 +321,8 @@ def traffic_from_counters(fetch_csv, write_csv, out_path):
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        # the calibration copy is the run's first device copy of at least 256 MiB (rows are in dispatch order)
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        # the calibration copy is the run's first device copy of at least 256 MiB
         copy = next(float(r["Counter_Value"]) for r in rows
                     if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024.0 >= (1 << 28))
         vals = defaultdict(list)
@@ -328,7 +330,9 @@ def traffic_from_counters(fetch_csv, write_csv, out_path):
             name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             if "kda" in name:
                 vals[name].append(float(r["Counter_Value"]))
-        return copy, {k: sum(v) / len(v) for k, v in vals.items()}
+        # per kernel: its first bench leg (the first three dispatches: one warm-up and two steps of the first
+        # leg that runs it; for the chunk-16 kernels that leg is the headline) and the average over all legs
+        return copy, {k: (sum(v[:3]) / len(v[:3]), sum(v) / len(v)) for k, v in vals.items()}
 
     fcopy, f = per_kernel(fetch_csv, "FETCH_SIZE")
     wcopy, w = per_kernel(write_csv, "WRITE_SIZE")
@@ -336,9 +340,10 @@ def traffic_from_counters(fetch_csv, write_csv, out_path):
     wscale = copy_bytes / (wcopy * 1024.0)
     out = {"csrc_hash": csrc_hash(), "fetch_scale": fscale, "write_scale": wscale, "kernels": {}}
     for k in sorted(set(f) | set(w)):
-        fb = f.get(k, 0.0) * 1024.0 * fscale
-        wb = w.get(k, 0.0) * 1024.0 * wscale
-        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb}
+        fb, fa = (x * 1024.0 * fscale for x in f.get(k, (0.0, 0.0)))
+        wb, wa = (x * 1024.0 * wscale for x in w.get(k, (0.0, 0.0)))
+        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+                             "traffic_bytes_all_legs": fa + wa}
     with open(out_path, "w") as fh:
         fh.write(json.dumps(out, indent=1) + "\n")
     return out
@@ -417,7 +422,7 @@ def main():
         print(json.dumps(mfma_from_counters(args.mfma_from, args.traffic_out)))
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (heads and sequences would "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (heads and sequences would "
               "shard without communication; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")

@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
     KDA_SUCCESS = 0,
     KDA_ERROR_INVALID_VALUE = 1,      /* null/misaligned pointer, bad size, overflow   */
-    KDA_ERROR_NOT_SUPPORTED = 2,      /* valid request this build does not implement   */
+    KDA_ERROR_NOT_SUPPORTED = 2,      /* valid request the library does not implement  */
     KDA_ERROR_WORKSPACE_TOO_SMALL = 3,
     KDA_ERROR_NO_DEVICE = 4,          /* no HIP device visible                         */
     KDA_ERROR_HIP = 5                 /* a HIP runtime call or a launch failed         */

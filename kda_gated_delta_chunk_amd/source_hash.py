@@ -1,13 +1,13 @@
-"""Content hash of the HIP sources of the prefill and decode kernels, used to tie
-stored hardware-counter figures (HBM traffic, matrix-core cycles of those
-kernels) to the exact code they were measured on. The C ABI glue and the
-backward kernels do not enter it: they do not change the code of the kernels
-the figures describe."""
+"""Content hash of the HIP kernel sources (prefill, decode, backward and the
+headers they include), used to tie stored hardware-counter figures (HBM
+traffic, matrix-core cycles of those kernels) to the exact code they were
+measured on. The C ABI glue does not enter it: it does not change the code of
+the kernels the figures describe."""
 import hashlib
 from pathlib import Path
 
 CSRC = Path(__file__).resolve().parent / "csrc"
-KERNEL_SOURCES = ("kda_common.hpp", "kda_decode.hip", "kda_prefill.hip")
+KERNEL_SOURCES = ("kda_common.hpp", "kda_launch.hpp", "kda_decode.hip", "kda_prefill.hip", "kda_backward.hip")
 
 
 def csrc_hash() -> str:
