@@ -74,7 +74,8 @@ class PrefillLeg:
         self.B, self.T, self.H, self.K, self.V, self.N = B, T, H, K, V, N
         cup = None if cu is None else cu.data_ptr()
         s0 = None if inp.get("S0") is None else inp["S0"].data_ptr()
-        self.o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+        io = 1 if inp["q"].dtype == torch.bfloat16 else 0  # kda_dtype_t of the inputs (and of o)
+        self.o = torch.empty((B, T, H, V), dtype=inp["q"].dtype, device=dev)
         self.Sf = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
         cc = _lib.CONVS[conv]
         oc = _lib.OPERANDS[operands]
@@ -84,9 +85,9 @@ class PrefillLeg:
         cwp = None if cw is None else cw.data_ptr()
         self.cw = cw
         query = lib.kda_chunk_fwd_min_workspace_bytes if low_memory else lib.kda_chunk_fwd_workspace_bytes
-        self.wsb = query(B, T, H, K, V, N, chunk, 1, cc, oc)
+        self.wsb = query(B, T, H, K, V, N, chunk, io, cc, oc)
         self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
-        self.swsb = lib.kda_chunk_prep_workspace_bytes(B, T, H, K, V, N, chunk, 1, cc, oc) if with_split else 0
+        self.swsb = lib.kda_chunk_prep_workspace_bytes(B, T, H, K, V, N, chunk, io, cc, oc) if with_split else 0
         self.sws = torch.empty(self.swsb, dtype=torch.uint8, device=dev) if with_split else None
         self.stream = torch.cuda.current_stream(dev)
         sh = self.stream.cuda_stream
@@ -95,15 +96,15 @@ class PrefillLeg:
 
         def fwd():
             _lib.check(lib.kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], og, s0, cup, B, T, H, K, V, N,
-                                         chunk, 1, gc, qkc, cc, cwp, oc, 1, o, Sf, self.ws.data_ptr(), self.wsb, sh),
+                                         chunk, io, gc, qkc, cc, cwp, oc, io, o, Sf, self.ws.data_ptr(), self.wsb, sh),
                        "kda_chunk_fwd")
 
         def prep():
-            _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], cup, B, T, H, K, V, N, chunk, 1, gc, qkc,
+            _lib.check(lib.kda_chunk_prep(p["q"], p["k"], p["g"], p["beta"], cup, B, T, H, K, V, N, chunk, io, gc, qkc,
                                           cc, cwp, oc, self.sws.data_ptr(), self.swsb, sh), "kda_chunk_prep")
 
         def state():
-            _lib.check(lib.kda_chunk_state(p["v"], og, s0, cup, B, T, H, K, V, N, chunk, 1, cc, cwp, 1, o, Sf,
+            _lib.check(lib.kda_chunk_state(p["v"], og, s0, cup, B, T, H, K, V, N, chunk, io, cc, cwp, io, o, Sf,
                                            self.sws.data_ptr(), self.swsb, sh), "kda_chunk_state")
 
         self.fwd, self.prep, self.state = fwd, prep, state
@@ -377,7 +378,7 @@ def leg_summary(leg, wall_ms, ev_ms, name, C=16, split=None):
     """Throughput and whole-path roofline of one timed leg."""
     T = leg.B * leg.T
     has_S0 = leg.inp.get("S0") is not None
-    path_bytes, kb = prefill_algorithmic_bytes(T, leg.H, leg.K, leg.V, leg.N, with_S0=has_S0)
+    path_bytes, kb = prefill_algorithmic_bytes(T, leg.H, leg.K, leg.V, leg.N, es=leg.o.element_size(), with_S0=has_S0)
     gbs = path_bytes / (ev_ms * 1e-3) / 1e9
     tf = prefill_flops(T, leg.H, leg.K, leg.V, C) / (ev_ms * 1e-3) / 1e12
     out = {"workload": name, "tokens_per_s": T / (wall_ms * 1e-3), "ms_per_step": wall_ms, "event_ms": ev_ms,
@@ -388,6 +389,45 @@ def leg_summary(leg, wall_ms, ev_ms, name, C=16, split=None):
     if split is not None:
         out["split_calls_ms"] = {"kda_chunk_prep": split[0], "kda_chunk_state": split[1]}
     return out, kb
+
+
+def run_config(idx, args, dev, say):
+    """One workload of the five preset configurations, timed as in the full run."""
+    names = {0: "tiny_fp32", 1: "prefill_4k", 2: "varlen_16", 3: "decode_512", 4: "prefill_1m"}
+    w = synth.WORKLOADS[names[idx]]
+    out = {"config_index": idx, "workload": w.name, "steps": args.steps, "warmup": args.warmup}
+    if w.kind == "decode":
+        say("decode %s: %d steps" % (w.name, args.decode_steps))
+        d = time_decode(w, args.decode_steps, dev)
+        gbs = d["bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9
+        out.update({"ms_per_step": d["ms_per_step"], "tokens_per_s": d["N"] / (d["ms_per_step"] * 1e-3),
+                    "GB_per_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
+        return out
+    inp = synth.workload_prefill_inputs(w, device=dev)
+    large = w.B * w.T * w.H > (1 << 26)
+    low_memory = False
+    if large:  # the two passes only when their workspace fits beside the inputs
+        free, _ = torch.cuda.mem_get_info()
+        wsb = _lib.load().kda_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.K, w.V, 1, 16, 1, 0, 0)
+        low_memory = wsb + (4 << 30) > free
+    leg = PrefillLeg(dev, inp, with_split=not large, low_memory=low_memory)
+    if args.settle_s > 0 and not large:
+        out["clock_settle"] = settle_clock(leg, args.settle_s)
+    steps, warmup = (max(2, args.steps // 10), 1) if large else (args.steps, args.warmup)
+    say("prefill %s: warmup %d, steps %d" % (w.name, warmup, steps))
+    wall_ms, ev_ms = leg.time_fwd(steps, warmup)
+    split = leg.time_split(steps, warmup) if not large else None
+    out["chunk16"], _ = leg_summary(leg, wall_ms, ev_ms, w.name + (", low-memory form" if low_memory else ""),
+                                    split=split)
+    out["device_error"] = leg.device_error()
+    if idx == 1:
+        del leg
+        gc.collect()
+        lg = PrefillLeg(dev, inp, chunk=64)
+        wm, em = lg.time_fwd(args.steps, args.warmup)
+        out["chunk64"], _ = leg_summary(lg, wm, em, w.name + ", chunk 64", C=64,
+                                        split=lg.time_split(args.steps, args.warmup))
+    return out
 
 
 def main():
@@ -413,6 +453,10 @@ def main():
                          "(run_counter_collection.csv) to the counter summary (--traffic-out)")
     ap.add_argument("--traffic-out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                                           "traffic.json"))
+    ap.add_argument("--config", type=int, choices=range(5), default=None,
+                    help="time one workload only and print its JSON line: 0 tiny fp32 prefill (T=64, H=2, d=32), "
+                         "1 prefill T=4096 H=96 d=128 bf16 (chunk 16 and 64), 2 16 packed sequences (~130K tokens), "
+                         "3 decode N=512 H=96, 4 prefill T=1,048,576 H=96")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from, args.traffic_out)))
@@ -429,6 +473,10 @@ def main():
 
     def say(msg):
         print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    if args.config is not None:
+        print(json.dumps(run_config(args.config, args, dev, say)), flush=True)
+        return
 
     if args.counters:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB

@@ -295,7 +295,7 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
 
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
               workspace=None, gate: str = "log_decay", o_gate=None, qk_norm: bool = False, conv: str = "none",
-              conv_w=None):
+              conv_w=None, out=None):
     """Gradients of chunk_fwd's (o, S_final) given dL/do and dL/dS_final, with respect to the raw inputs.
     ``gate``, ``qk_norm``, ``conv`` and ``conv_w`` say what the forward did, as for chunk_fwd; dg is the
     gradient with respect to g as given (the log-decay, or the gate pre-activation). With ``o_gate`` (the
@@ -306,7 +306,7 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
     ``do`` has o's shape and the input dtype; ``dS_final`` is fp32 [num_seqs, H, K, V] or None (zero).
     Returns a dict of fp32 tensors: dq, dk, dg [B, T, H, K]; dv [B, T, H, V]; dbeta [B, T, H]; and
     dS0 [num_seqs, H, K, V] when ``want_dS0``. ``workspace`` (uint8 CUDA tensor) may be passed to avoid
-    the allocation.
+    the allocation, and ``out`` (a dict with some of the result's keys) preallocated fp32 result tensors.
     """
     lib = _lib.load()
     dev = q.device
@@ -333,15 +333,19 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
         if t is not None:
             _need(t, name, (N, H, K, V), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
-           "dg": torch.empty((B, T, H, K), **f32), "dv": torch.empty((B, T, H, V), **f32),
-           "dbeta": torch.empty((B, T, H), **f32)}
+    shapes = {"dq": (B, T, H, K), "dk": (B, T, H, K), "dg": (B, T, H, K), "dv": (B, T, H, V), "dbeta": (B, T, H)}
     if want_dS0:
-        out["dS0"] = torch.empty((N, H, K, V), **f32)
+        shapes["dS0"] = (N, H, K, V)
     if o_gate is not None:
-        out["do_gate"] = torch.empty((B, T, H, V), **f32)
+        shapes["do_gate"] = (B, T, H, V)
     if cc != 0:
-        out["dconv_w"] = torch.empty((H, 2 * K + V, 4), **f32)
+        shapes["dconv_w"] = (H, 2 * K + V, 4)
+    given = dict(out or {})
+    for name in given:
+        if name not in shapes:
+            raise ValueError("out[%r]: not a result of this call" % (name,))
+        _need(given[name], "out[%r]" % (name,), shapes[name], torch.float32, dev)
+    out = {name: given.get(name) if name in given else torch.empty(shp, **f32) for name, shp in shapes.items()}
     need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc))
     if need == 0:
         raise KDAError(2, "kda_chunk_bwd_workspace_bytes")

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from kda_gated_delta_chunk_amd import chunk_bwd
+from kda_gated_delta_chunk_amd import _lib, chunk_bwd
 from kda_gated_delta_chunk_amd import synth
 from tests.parity import TOL_FP32, err
 
@@ -31,13 +31,36 @@ def _inputs(B, T, H, K, V, io, seed, cu=None, with_S0=True, with_dsf=True, **kw)
     return inp
 
 
+def _nan(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+
+
 def _gpu(inp, want_dS0=True):
-    out = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
+    """The GPU gradients, written over NaN-filled outputs and a NaN-filled workspace (so an element the kernels
+    leave unwritten, or a workspace byte read before it is written, shows up in the comparison)."""
+    B, T, H, K = inp["q"].shape
+    V = inp["v"].shape[-1]
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    out = {"dq": _nan((B, T, H, K)), "dk": _nan((B, T, H, K)), "dg": _nan((B, T, H, K)), "dv": _nan((B, T, H, V)),
+           "dbeta": _nan((B, T, H))}
+    if want_dS0:
+        out["dS0"] = _nan((N, H, K, V))
+    if inp.get("o_gate") is not None:
+        out["do_gate"] = _nan((B, T, H, V))
+    if inp.get("conv", "none") != "none":
+        out["dconv_w"] = _nan((H, 2 * K + V, 4))
+    qc = _lib.KDA_QK_L2NORM if inp.get("qk_norm", False) else _lib.KDA_QK_AS_GIVEN
+    cc = _lib.CONVS[inp.get("conv", "none")]
+    wsb = _lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc)
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN patterns in every fp32 word
+    got = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
                     dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0,
                     gate=inp.get("gate", "log_decay"), o_gate=inp.get("o_gate"), qk_norm=inp.get("qk_norm", False),
-                    conv=inp.get("conv", "none"), conv_w=inp.get("conv_w"))
+                    conv=inp.get("conv", "none"), conv_w=inp.get("conv_w"), workspace=ws, out=out)
     torch.cuda.synchronize()
-    return out
+    for name in out:
+        assert got[name] is out[name], name
+    return got
 
 
 def _oracle(inp, heads=None):

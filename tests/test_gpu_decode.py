@@ -27,8 +27,11 @@ def _steps(N, H, K, V, io, steps, seed, gate="log_decay", g_scale=1.0, o_gate=Fa
         args = [inp[n] for n in ("q", "k", "v", "g", "beta")]
         og = inp["o_gate"]
         S32 = S.clone()
-        o = decode_step(*args, S, gate=gate, o_gate=og, qk_norm=qk_norm)
-        o32 = decode_step(*args, S32, o_dtype=torch.float32, gate=gate, o_gate=og, qk_norm=qk_norm)
+        # outputs filled with NaN beforehand: every element must be written
+        o = torch.full((N, H, V), float("nan"), dtype=args[0].dtype, device=DEV)
+        o32 = torch.full((N, H, V), float("nan"), dtype=torch.float32, device=DEV)
+        decode_step(*args, S, out=o, gate=gate, o_gate=og, qk_norm=qk_norm)
+        decode_step(*args, S32, o_dtype=torch.float32, out=o32, gate=gate, o_gate=og, qk_norm=qk_norm)
         torch.cuda.synchronize()
         assert torch.equal(S32, S)
         o_ref, S_ref = oracle.decode_step(*(a.cpu() for a in args), S_ref, gate=gate,
