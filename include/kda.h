@@ -389,7 +389,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
  *           qk_norm, conv): the state every 8 tokens of every sequence and
  *           head (K * V * 4 bytes each) plus per-16-column partial sums of dq,
- *           dk, dg and dbeta (V / 16 * B * T * H * (3K + 1) * 4 bytes); with a
+ *           dk, dg and dbeta (V / 16 * B * T * H * (3K + 4) * 4 bytes); with a
  *           prologue also the prologue's fp32 outputs and the recurrence's
  *           gradients with respect to them (4 B T H K floats, plus 2 B T H V
  *           with a convolution), 2 B T H norm factors with qk_norm and the

@@ -144,6 +144,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
     using vio = IO<BF && !V32>;
     constexpr int R = K / 16;          // rows per thread
     constexpr int F = 3 * K + 1;       // partial row: dq | dk | dg | dbeta
+    constexpr int FP = 3 * K + 4;      // its pitch in the partial buffer (whole 16-byte groups)
     constexpr int NE = BL * K / BNT;   // staged q/k/g elements per thread
     static_assert(NE >= 1 && NE * BNT == BL * K, "segment staging");
     __shared__ float sq[BL * K], sk[BL * K], sa[BL * K];  // q, k, e^g of the segment's tokens
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
                 const int64_t ft = ft0 + base + tt;
                 if (ft < t1) {
                     const float *rr = red + tt * 4 * F + f;
-                    part[((int64_t)vt * n_rows + ft * sH + h) * F + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
+                    part[((int64_t)vt * n_rows + ft * sH + h) * FP + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
                 }
             }
             __syncthreads();
@@ -360,32 +361,44 @@ __global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
 
 // dq, dk, dg, dbeta of every covered (token, head): the tiles' partial sums added in tile order. With the
 // scaled-sigmoid gate, g holds the pre-activation x and the log-decay gradient is carried through
-// d(-5 sigmoid(x))/dx = -5 sigmoid(x) (1 - sigmoid(x)).
+// d(-5 sigmoid(x))/dx = -5 sigmoid(x) (1 - sigmoid(x)). One thread per 4 consecutive entries of a partial row
+// (rows have a pitch of 3K + 4 floats, so every group is one 16-byte load per tile); group 3K/4 holds dbeta.
 template <bool BF, int K>
 __global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ part, int32_t nvt, int64_t n_rows,
                                                       int32_t H, const int64_t *__restrict__ seq_tok, int32_t N,
                                                       const typename IO<BF>::T *__restrict__ g, bool gate_sig,
                                                       float *__restrict__ dq, float *__restrict__ dk,
                                                       float *__restrict__ dg, float *__restrict__ dbeta) {
-    constexpr int F = 3 * K + 1;
+    constexpr int FP = 3 * K + 4, G = FP / 4;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n_rows * F) return;
-    const int64_t row = idx / F;
-    const int f = (int)(idx % F);
+    if (idx >= n_rows * G) return;
+    const int64_t row = idx / G;
+    const int f = 4 * (int)(idx % G);
     const int64_t ft = row / H;
     if (ft < seq_tok[0] || ft >= seq_tok[N]) return;  // outside every sequence: not written
-    float acc = 0.f;
-    for (int t = 0; t < nvt; ++t) acc += part[((int64_t)t * n_rows + row) * F + f];
-    if (f < K) dq[row * K + f] = acc;
-    else if (f < 2 * K) dk[row * K + f - K] = acc;
-    else if (f < 3 * K) {
-        if (gate_sig) {
-            const float sx = sigmoid_f(IO<BF>::ld(g, row * K + f - 2 * K));
-            acc *= -5.f * sx * (1.f - sx);
-        }
-        dg[row * K + f - 2 * K] = acc;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = 0; t < nvt; ++t) {
+        const float4 x = *reinterpret_cast<const float4 *>(part + ((int64_t)t * n_rows + row) * FP + f);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
     }
-    else dbeta[row] = acc;
+    if (f < K) {
+        *reinterpret_cast<float4 *>(dq + row * K + f) = acc;
+    } else if (f < 2 * K) {
+        *reinterpret_cast<float4 *>(dk + row * K + f - K) = acc;
+    } else if (f < 3 * K) {
+        if (gate_sig) {
+            float a[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sx = sigmoid_f(IO<BF>::ld(g, row * K + f - 2 * K + i));
+                a[i] *= -5.f * sx * (1.f - sx);
+            }
+            acc = make_float4(a[0], a[1], a[2], a[3]);
+        }
+        *reinterpret_cast<float4 *>(dg + row * K + f - 2 * K) = acc;
+    } else {
+        dbeta[row] = acc.x;
+    }
 }
 
 // ------------------------------------------------------------------ prologue and its reverse
@@ -721,7 +734,7 @@ BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_segs, int32_t 
     r.seq_tok = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.seg_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.ckpt = (float *)take(sizeof(float) * (size_t)max_segs * H * K * V);
-    r.part = (float *)take(sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 1));
+    r.part = (float *)take(sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 4));
     const size_t nk = (size_t)n_tokens * H * K * sizeof(float), nv = (size_t)n_tokens * H * V * sizeof(float);
     const bool pro = norm || conv;
     r.xq = pro ? (float *)take(nk) : nullptr;
@@ -752,7 +765,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
                        (const TQ *)ks, (const TV *)vs, (const T *)a.g, (const T *)a.beta, (const T *)a.dout,
                        (const T *)a.o_gate, a.S0, a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows,
                        a.gate_sigmoid, w.ckpt, w.part, dv_dst, a.d_o_gate, a.dS0);
-    const int64_t nel = n_rows * (3 * K + 1);
+    const int64_t nel = n_rows * ((3 * K + 4) / 4);
     if (nel > 0)
         hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3(blocks_of(nel)), dim3(256), 0, st, w.part, nvt, n_rows, a.H,
                            w.seq_tok, a.num_seqs, (const T *)a.g, a.gate_sigmoid, dq_dst, dk_dst, a.dg, a.dbeta);
