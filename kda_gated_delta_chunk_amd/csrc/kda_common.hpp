@@ -147,8 +147,8 @@ __device__ __forceinline__ void mfma_fence_all(f32x4 (&x)[8]) {
 }
 
 // Cross-lane moves inside a 16-lane row (DPP). row_scan16 is the inclusive
-// prefix sum over the 16 lanes of each row; row_last broadcasts lane 15 of each
-// row to the whole row.
+// prefix sum over the 16 lanes of each row; row_suffix16 the exclusive suffix
+// sum; row_last broadcasts lane 15 of each row to the whole row.
 template <int CTRL, bool BOUND_ZERO>
 __device__ __forceinline__ float dpp_f(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
@@ -159,6 +159,17 @@ __device__ __forceinline__ float row_scan16(float x) {
     x += dpp_f<0x112, true>(x);  // row_shr:2
     x += dpp_f<0x114, true>(x);  // row_shr:4
     x += dpp_f<0x118, true>(x);  // row_shr:8
+    return x;
+}
+// Exclusive suffix sum over the 16 lanes of each row: lane r gets the sum of lanes r+1 .. 15 (0 on lane 15).
+// A decay exponent spanning tokens r+1 .. 15 is summed from those tokens' own terms: formed as the row total
+// minus the inclusive prefix it would carry an error of the total's size, not of its own.
+__device__ __forceinline__ float row_suffix16(float x) {
+    x = dpp_f<0x101, true>(x);   // row_shl:1, lane 15 has no source and takes 0
+    x += dpp_f<0x101, true>(x);  // row_shl:1
+    x += dpp_f<0x102, true>(x);  // row_shl:2
+    x += dpp_f<0x104, true>(x);  // row_shl:4
+    x += dpp_f<0x108, true>(x);  // row_shl:8
     return x;
 }
 __device__ __forceinline__ float row_last(float x) { return dpp_f<0x15f, false>(x); }  // row_newbcast:15

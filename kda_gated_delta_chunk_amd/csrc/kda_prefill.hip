@@ -557,6 +557,14 @@ struct PrepParams {
     int32_t g0, g1;
 };
 
+// Gamma_C of channels 32s + 8ag .. +7 into a block's Gamma_C area, in state-row order: rows
+// 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j.
+__device__ __forceinline__ void store_gamma_c8(char *gc_area, int s, int ag, const float (&e)[8]) {
+    float *gcp = reinterpret_cast<float *>(gc_area);
+    *reinterpret_cast<float4 *>(gcp + 32 * s + 4 * ag) = make_float4(e[0], e[1], e[2], e[3]);
+    *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
+}
+
 // The 16-token prep of chunk gc (of sequence n) and head h by one wavefront. The factors go to
 // `blk`, one SubLayout block: a workspace block in global memory, or (IN_LDS) a slot of the fused
 // kernel's LDS ring. xt and kx are the wavefront's staging tiles for K*Gamma transposed ([K][16]) and
@@ -643,15 +651,33 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
     float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
     beta = valid ? beta : 0.f;
 
-    // ---- cumulative log-decay in base 2 (prefix over the 16 token lanes) and the chunk total
+    // ---- cumulative log-decay in base 2 (prefix over the 16 token lanes). With bf16 I/O, bt holds the
+    // chunk total b_C and K*exp(b_C-b) takes exp2(bt - b). With fp32 I/O the exponent is the suffix sum of
+    // the decays after this token, summed from its own terms: as b_C - b it would carry an error of |b_C|
+    // times fp32's rounding, up to about 1e-5 relative in the factor, which the state carries forward.
+    // (With bf16 I/O the factor is rounded to a bf16 pair of that size anyway.) The fp32 path stages
+    // K*exp(b_C-b) in LDS and stores Gamma_C (rows 32s + 16h + 4ag + j of the state-row order hold
+    // channels 32s + 8ag + 4h + j) at once, holding neither through the solve.
     float bt[KS][8];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+        float kpv[8], gce[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bl[s][j] = row_scan16(valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f);
-            bt[s][j] = row_last(bl[s][j]);
+            const float x = valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f;
+            bl[s][j] = row_scan16(x);
+            if constexpr (BF) {
+                bt[s][j] = row_last(bl[s][j]);
+            } else {
+                kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(row_suffix16(x));
+                gce[j] = __builtin_amdgcn_exp2f(row_last(bl[s][j]));
+            }
         }
+        if constexpr (!BF) {
+            put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
+            if (r == 0) store_gamma_c8(blk + L::GC, s, ag, gce);
+        }
+    }
     if (ag == 0) sB[r] = beta;
 
     // ---- decay-scaled operands. Q*Gamma goes straight to the workspace (its fragment order
@@ -667,12 +693,12 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
             qg[j] = qv[s][j] * e;
             kg[j] = kv[s][j] * e;
             ki[j] = kv[s][j] * ei;
-            kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
+            if constexpr (BF) kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
             if constexpr (H16) st_elem_h(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
             else st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kg[j]);
         }
         if constexpr (H16) put_kp8_h<K>(kx, 32 * s + 8 * ag, r, kpv);
-        else put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
+        else if constexpr (BF) put_kp8<BF, K>(kx, 32 * s + 8 * ag, r, kpv);
         split8(qg, qh[s], ql[s]);
         kgf[s] = frag8_of(kg, Frag8<BF>{});
         split8(ki, kih[s], kil[s]);
@@ -778,16 +804,16 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
     else if constexpr (H16) store_kp_h<K>(kx, blk + L::KP, lane);
     else store_kp<BF, K>(kx, blk + L::KP, lane);
 
-    // ---- Gamma_C in state-row order: rows 32s + 16h + 4ag + j hold channels 32s + 8ag + 4h + j
-    if (r == 0) {
-        float *gcp = reinterpret_cast<float *>(blk + L::GC);
+    // ---- Gamma_C (bf16 I/O: bt holds the chunk total)
+    if constexpr (BF) {
+        if (r == 0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            float e[8];
+            for (int s = 0; s < KS; ++s) {
+                float e[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(bt[s][j]);
-            *reinterpret_cast<float4 *>(gcp + 32 * s + 4 * ag) = make_float4(e[0], e[1], e[2], e[3]);
-            *reinterpret_cast<float4 *>(gcp + 32 * s + 16 + 4 * ag) = make_float4(e[4], e[5], e[6], e[7]);
+                for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(bt[s][j]);
+                store_gamma_c8(blk + L::GC, s, ag, e);
+            }
         }
     }
 }
@@ -823,7 +849,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // sub-tiles' totals); on top of it:
 //   off-diagonal tiles I < R of A and P: exp(b_r - b_i) = exp(bl_r) *
 //     exp(B_R - B_{I+1}) * exp(bt_I - bl_i) with bl the sub-tile prefix and bt
-//     its total, every factor at most 1 (the left operand is this wavefront's
+//     its total (the last exponent summed as the suffix after token i), every
+//     factor at most 1 (the left operand is this wavefront's
 //     K or Q scaled by the first two, the right one the keys of sub-tile I
 //     scaled to its end, shared through LDS);
 //   X = (I + A)^{-1} by blocks: each wavefront solves its diagonal 16x16 block,
@@ -918,20 +945,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     float beta = BF ? bf2f(reinterpret_cast<const uint16_t *>(bp)[row]) : reinterpret_cast<const float *>(bp)[row];
     beta = valid ? beta : 0.f;
-    // ---- sub-tile prefix of the log-decay (base 2) and its total; totals to LDS
+    // ---- sub-tile prefix of the log-decay (base 2) and the sub-tile total; totals to LDS. bt holds, with
+    // bf16 I/O, the sub-tile total (the decay from token i to the sub-tile end is exp2(bt - bl)); with fp32
+    // I/O the suffix sum of the decays after this token in the sub-tile, summed from its own terms (as in
+    // the 16-token prep).
     float bt[KS][8];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+        float tot[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            bl[s][j] = row_scan16(valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f);
-            bt[s][j] = row_last(bl[s][j]);
+            const float x = valid ? (pa.gate ? gate_log2_decay(bl[s][j]) : bl[s][j] * LOG2E) : 0.f;
+            bl[s][j] = row_scan16(x);
+            tot[j] = row_last(bl[s][j]);
+            bt[s][j] = BF ? tot[j] : row_suffix16(x);
         }
-    if (r == 0) {
+        if constexpr (!BF) {
+            if (r == 0) {
+                *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+                *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag + 4) = make_float4(tot[4], tot[5], tot[6], tot[7]);
+            }
+        }
+    }
+    if constexpr (BF) {
+        if (r == 0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag) = make_float4(bt[s][0], bt[s][1], bt[s][2], bt[s][3]);
-            *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag + 4) = make_float4(bt[s][4], bt[s][5], bt[s][6], bt[s][7]);
+            for (int s = 0; s < KS; ++s) {
+                *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag) = make_float4(bt[s][0], bt[s][1], bt[s][2], bt[s][3]);
+                *reinterpret_cast<float4 *>(lb + R * K + 32 * s + 8 * ag + 4) = make_float4(bt[s][4], bt[s][5], bt[s][6], bt[s][7]);
+            }
         }
     }
     if (ag == 0) b64[SUB * R + r] = beta;
@@ -942,7 +984,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         for (int s = 0; s < KS; ++s) {
             float ke[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ke[j] = kv[s][j] * __builtin_amdgcn_exp2f(bt[s][j] - bl[s][j]);
+            for (int j = 0; j < 8; ++j) ke[j] = kv[s][j] * __builtin_amdgcn_exp2f(BF ? bt[s][j] - bl[s][j] : bt[s][j]);
             Frag8<BF> eh, el;
             split8(ke, eh, el);
             st_frag8<BF>(kep + (s * 64 + lane) * 8 * ES, eh);
@@ -951,8 +993,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();
 
-    // ---- decay-scaled operands of this sub-tile. br = B_R (sum of the earlier sub-tiles' totals),
-    // bc = B_4 (chunk total), for this lane's channels.
+    // ---- decay-scaled operands of this sub-tile, for this lane's channels. br = B_R (sum of the earlier
+    // sub-tiles' totals). bc: with bf16 I/O B_4 (the chunk total), and b_C - b = bc - br - bl; with fp32 I/O
+    // the sum of the later sub-tiles' totals, and b_C - b = bc + (the suffix in bt), summed from the decays
+    // it spans (as B_4 - B_R - bl it would cancel against the chunk total, whose magnitude reaches
+    // hundreds, and leave a relative error of that size times fp32's in the factor).
     char *blk = frags + (((size_t)gc * H + h) * CS + R) * L::BYTES;
     Frag8<BF> kgf[KS], kih[KS], kil[KS], qlh[KS], qll[KS];
 #pragma unroll
@@ -968,7 +1013,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (I < R) br[j] += x[j];
-                bc[j] += x[j];
+                if (BF || I > R) bc[j] += x[j];
             }
         }
         float kg[8], ki[8], qg[8], qgc[8], kpv[8];
@@ -980,7 +1025,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             qg[j] = qv[s][j] * e;
             ki[j] = kv[s][j] * __builtin_amdgcn_exp2f(-bl[s][j]);
             qgc[j] = qv[s][j] * gam;
-            kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(bc[j] - br[j] - bl[s][j]);
+            kpv[j] = kv[s][j] * __builtin_amdgcn_exp2f(BF ? bc[j] - br[j] - bl[s][j] : bc[j] + bt[s][j]);
             st_elem<BF>(xt, (32 * s + 8 * ag + j) * 16 + r, kv[s][j] * gam);
         }
         // Q*Gamma (chunk-relative) straight to the workspace
