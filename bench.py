@@ -211,8 +211,10 @@ def time_copy(dev, nbytes=2 << 30, reps=10):
 
 
 def backward_flops(T, H, K, V):
-    """Flops of the per-token backward per call: one forward recompute (decay, read, write: 5KV) plus the
-    reverse step (G += q do^T, S_t do, G^T k, beta G d - A dv, G - k dv^T, rowsum(GA * A), decay: 19KV)."""
+    """Algorithmic flops of the backward per call, counted on the per-token reverse recurrence: one forward
+    recompute (decay, read, write: 5KV) plus the reverse step (G += q do^T, S_t do, G^T k, beta G d - A dv,
+    G - k dv^T, rowsum(GA * A), decay: 19KV). The chunk form the library runs performs about 16KV per token
+    plus O(16 (K + V)), some 0.78 of this count at K = V = 128."""
     return 24 * K * V * T * H
 
 
@@ -612,10 +614,10 @@ def main():
                         "dL/do ~ N(0,1), no dL/dS_final)",
             "ms_per_step": rb["ms"], "tokens_per_s": rb["B"] * rb["T"] / (rb["ms"] * 1e-3),
             "workspace_bytes": rb["ws_bytes"],
-            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd (checkpoint walk, reverse walk, tile sum)",
+            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd (chunk factors, state pass, reverse pass, gradients)",
                          "achieved": tfs, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_VECTOR_PEAK_TFS, "algorithmic_flops_per_call": fl,
-                         "timed": "whole call (3 launches)"}}
+                         "timed": "whole call (5 launches)"}}
         say("backward with the prologue (q/k norm, short convolution with SiLU): warmup 2, steps 5")
         rp = time_backward(w, 5, 2, dev, prologue=True)
         out["backward"]["with_prologue"] = {"ms_per_step": rp["ms"], "workspace_bytes": rp["ws_bytes"],

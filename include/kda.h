@@ -351,16 +351,21 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
 /*
  * Backward pass: the gradients of kda_chunk_fwd's (o, S_final) with respect to
  * q, k, v, g, beta and S0, given dL/do and dL/dS_final. The first page cited
- * above names this as the form the layer is trained in; the pages print no
- * backward, so the gradients are the chain rule through the four steps above,
- * token by token in reverse order (with G = dL/dS_t):
+ * above names the chunk form as the form the layer is trained in; the pages
+ * print no backward, so the gradients are the chain rule through the four
+ * steps above. Token by token in reverse order (with G = dL/dS_t) they are:
  *   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = beta_t w;
  *   dbeta_t = w . (v_t - u);  dk_t = beta_t G (v_t - u) - A_t dv_t;
  *   dg_t = rowsum((G - k_t dv_t^T) * A_t);  G = diag(exp(g_t)) (G - k_t dv_t^T)
  * where A_t = diag(exp(g_t)) S_{t-1} and u = A_t^T k_t; dL/dS0 is the last G.
+ * The library evaluates the same gradients in the chunk form of 16-token
+ * chunks (the reverse of the prefill's products, chunk by chunk), in fp32.
  *   q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]   dtype `io`, the
  *           forward's raw inputs; g as `gate` says, q, k and v as `conv` and
- *           `qk_norm` say, as for kda_chunk_fwd
+ *           `qk_norm` say, as for kda_chunk_fwd, with the same range: with
+ *           KDA_GATE_LOG_DECAY the chunk form assumes -5 <= g <= 0 (outside
+ *           it results are unspecified); with KDA_GATE_SCALED_SIGMOID any
+ *           finite g is valid
  *   conv_w  fp32 [H, K + K + V, 4] when conv != KDA_CONV_NONE (else ignored)
  * With a prologue (qk_norm or conv) the gradients are carried on through it
  * (chain rule, fp32): the normalisation x_n = r x, r = (|x|^2 + 1e-6)^(-1/2),
@@ -387,18 +392,22 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *           convolution (written also when T == 0: zeros), else ignored
  *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
- *           qk_norm, conv): the state every 8 tokens of every sequence and
- *           head (K * V * 4 bytes each) plus per-16-column partial sums of dq,
- *           dk, dg and dbeta (V / 16 * B * T * H * (3K + 4) * 4 bytes); with a
- *           prologue also the prologue's fp32 outputs and the recurrence's
- *           gradients with respect to them (4 B T H K floats, plus 2 B T H V
- *           with a convolution), 2 B T H norm factors with qk_norm and the
- *           taps' partial sums (ceil(B T / 64) H (2K + V) 4 floats) with a
- *           convolution; 0 means the sizes or options are invalid
+ *           qk_norm, conv). Per 16-token chunk and head (at most
+ *           ceil(T / 16) B chunks, one more per sequence when packed) it holds
+ *           the chunk's factors (4 * 16 * K + 4 * 16 * 16 + K floats, rounded
+ *           up to 64), the state entering it and the state's gradient leaving
+ *           it (K * V floats each) and three 16 * V blocks. It also holds
+ *           B * T * H * V floats for dL/do * sigmoid(z) with an output gate.
+ *           With a prologue it adds the prologue's fp32 outputs and the
+ *           recurrence's gradients with respect to them (4 B T H K floats,
+ *           plus 2 B T H V with a convolution), 2 B T H norm factors with
+ *           qk_norm, and the taps' partial sums (ceil(B T / 64) H (2K + V) 4
+ *           floats) with a convolution. 0 means the sizes or options are
+ *           invalid.
  * The forward states are recomputed from the inputs; nothing from a forward
- * call is needed. All arithmetic is fp32, any finite g is accepted, and the
- * result is deterministic (fixed summation order). Outputs may not alias the
- * inputs or each other. Errors as for kda_chunk_fwd (chunk does not apply).
+ * call is needed. All arithmetic is fp32 and the result is deterministic
+ * (fixed summation order). Outputs may not alias the inputs or each other.
+ * Errors as for kda_chunk_fwd (chunk does not apply).
  */
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                      kda_qk_norm_t qk_norm, kda_conv_t conv);

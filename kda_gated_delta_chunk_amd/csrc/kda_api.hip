@@ -379,9 +379,10 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
         for (int j = i + 1; j < NOUT; ++j)
             if (outs[j] == outs[i]) return KDA_ERROR_INVALID_VALUE;
     }
-    // the tile-sum reduce runs one thread per (token, head, 4 partial slots): its grid must stay launchable
-    if ((B * T * H * ((3 * (int64_t)K + 4) / 4) + 255) / 256 >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     const int64_t segs = max_chunks(B, T, num_seqs, packed, kda::backward_segment_tokens());
+    // the chunk kernels run one workgroup per (chunk, head), the prologue's one per 16 (token, head) rows:
+    // their grids must stay launchable
+    if (segs * H >= ((int64_t)1 << 31) || (B * T * H + 15) / 16 >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM,
                                                       has_conv);
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;

@@ -5,30 +5,15 @@
 // paragraph "KDA 为什么不同于 MLA": per-channel decay, delta-rule correction, read of the updated
 // state), per sequence and head with S in R^{K x V}:
 //   A_t = diag(e^{g_t}) S_{t-1};  d_t = v_t - A_t^T k_t;  S_t = A_t + beta_t k_t d_t^T;  o_t = S_t^T q_t.
-// With an output gate o_t * sigmoid(z_t) on the forward's output, do_t below is the gated dL/do times
-// sigmoid(z_t), and dL/dz_t = dL/do * o_t * sigmoid(z_t) (1 - sigmoid(z_t)) with o_t the core output.
-// Its reverse, token by token with G = dL/dS_t:
-//   G += q_t do_t^T;  dq_t = S_t do_t;  w = G^T k_t;  dv_t = beta_t w;  dbeta_t = w . d_t;
-//   dk_t = beta_t G d_t - A_t dv_t;  GA = G - k_t dv_t^T;  dg_t = rowsum(GA * A_t);  G = diag(e^{g_t}) GA,
-// and dL/dS0 is the last G.
+// With an output gate o_t * sigmoid(z_t) on the forward's output, the core output's gradient is
+// do_t * sigmoid(z_t), and dL/dz_t = dL/do * o_t * sigmoid(z_t) (1 - sigmoid(z_t)) with o_t the core output.
 //
-// The value columns of S evolve independently (decay scales rows), and so do the columns of G, so one
-// workgroup owns (sequence, head, 16-column tile) and walks the sequence twice:
-//   1. forward over the whole sequence, storing S at the start of every 8-token segment (checkpoints);
-//   2. backward over the segments, last first: reload the segment's checkpoint, recompute its 8 states
-//      into registers, then run the reverse steps over them.
-// The column-local results (dv, and G itself) are final per workgroup; dq, dk, dg and dbeta sum over all
-// V columns, so each workgroup writes its tile's partial sums and kda_bwd_reduce adds the tiles in a
-// fixed order (deterministic, no atomics). All arithmetic is fp32.
-//
-// Thread layout (256 threads, 4 wavefronts): lane = 4*rg + c4; column j = 4*wave + c4 of the tile; the
-// thread holds rows rg*R .. rg*R + R-1 (R = K/16) of S and G for column j. Sums over the key rows run
-// over the 16 lanes of equal c4 (two row rotations by DPP, then two permlane swaps across rows); sums over
-// the 4 columns of a wavefront use DPP quad permutes, then LDS across the 4 wavefronts.
-//
-// Occupancy: the launch bounds ask for 3 wavefronts per SIMD (3 workgroups per CU), which the compiler
-// meets by spilling 16 registers; the kernel is bound by instruction issue (about 530 instructions per
-// wavefront and token across the three walks), not by memory, so resident wavefronts matter more.
+// The reverse runs in the chunk form of the same recurrence (the one the prefill uses, and the form the
+// same section names for training): the gradients of a chunk's products are products again, so the work
+// is four launches, two of them parallel over (chunk, head) and two sequential passes over the chunks
+// of each sequence, instead of a walk over every token (the derivation is in the section "chunked
+// reverse" below). With the q/k normalisation and the short convolution, the chain rule runs through
+// them around the recurrence's reverse (the section "prologue and its reverse").
 
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
@@ -36,15 +21,14 @@
 namespace kda {
 namespace {
 
-constexpr int BL = 8;     // tokens per checkpoint segment
-constexpr int BVT = 16;   // value columns per workgroup
-constexpr int BNT = 256;  // threads per workgroup
-constexpr int RT = 4;     // tokens per flush of the column sums (LDS holds RT tokens' worth)
+constexpr int CB = 16;    // tokens per chunk
+constexpr int CVT = 32;   // value columns per workgroup of the sequential passes
+constexpr int CNT = 256;  // threads per workgroup
 
 // ------------------------------------------------------------------ sequence table
 // seq_tok[n] = first flat token of sequence n (cu_seqlens clamped into [0, total] and made
 // non-decreasing; n = 0..N, seq_tok[N] = end of the last sequence); seg_off[n] = index of the first
-// checkpoint segment of sequence n (seg_off[N] = total segments).
+// chunk of sequence n (seg_off[N] = total chunks).
 __device__ int64_t bwd_scan(int64_t x, int64_t *sh, bool is_max) {
     const int t = threadIdx.x, nt = blockDim.x;
     sh[t] = x;
@@ -83,7 +67,7 @@ __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict_
         seq_tok[m] = cur;
         if (m < N) {
             const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
-            segs += (nx - cur + BL - 1) / BL;
+            segs += (nx - cur + CB - 1) / CB;
         }
     }
     const int64_t sbase = bwd_scan(segs, sh, false);
@@ -94,310 +78,691 @@ __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict_
         cur = start_of(m) > cur ? start_of(m) : cur;
         if (m < N) {
             const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
-            acc += (nx - cur + BL - 1) / BL;
+            acc += (nx - cur + CB - 1) / CB;
         }
     }
 }
 
 // ------------------------------------------------------------------ lane sums
-// (every control used here has a source lane for every lane; bound_ctrl set lets the compiler fold the
-// move into the consuming add)
+// (every control used here has a source lane for every lane within its quad; bound_ctrl set lets the
+// compiler fold the move into the consuming add)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
                                                                  true));
 }
-// Sum over the 16 lanes of equal (lane & 3): within a 16-lane row the four lanes 4 apart (row_ror:4,
-// row_ror:8), then across the four rows with gfx950's lane swaps, which stay in the vector ALU: a
-// permlane16 swap of x with itself returns x with rows (0,1) and (2,3) exchanged as its two results, so
-// their sum holds rows 0+1 and 2+3; a permlane32 swap does the same for the two halves. Every lane gets
-// the total.
-__device__ __forceinline__ float sum_rows(float x) {
-    x += dpp_mov<0x124>(x);
-    x += dpp_mov<0x128>(x);
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// ------------------------------------------------------------------ chunked reverse
+// Sequences are cut into chunks of CB tokens (each sequence starts a chunk). Per (chunk, head), with b the
+// cumulative log-decay inside the chunk (per key channel), s = b_C - b the decay after each token, and
+// Q~ = Q*e^b, K~ = K*e^b, K^ = K*e^{-b}, Kc = K*e^s, Gc = e^{b_C}:
+//   Ab = tril_strict(K~ K^^T),  A = diag(beta) Ab,  M = (I + A)^{-1},  T = M diag(beta),
+//   P = tril(Q~ K^^T),  Wk = T K~;
+// the forward over the chunk with S its entering state:
+//   X = V - K~ S,  W = T X,  O = Q~ S + P W,  S' = diag(Gc) S + Kc^T W,
+// and its reverse given dO and dS' = dL/dS':
+//   dW = P^T dO + Kc dS',  dS = diag(Gc) dS' + Q~^T dO - Wk^T dW,
+//   dX = T^T dW (= dv),  dT = dW X^T,  dP = tril(dO W^T),  dM = dT diag(beta),
+//   dA = -tril_strict(M^T dM M^T),  dbeta_j = sum_i M_ij dT_ij + sum_{i<j} dA_ji Ab_ji,
+//   dq = e^b (dO S^T + dP K^),  dk = e^b (-dX S^T + diag(beta) dA K^) + e^{-b} (dP^T Q~ + (diag(beta) dA)^T K~)
+//        + e^s (W dS'^T),
+//   dg_t = sum_{u>=t} (dO S^T)_u q_u e^{b_u} - (dX S^T)_u k_u e^{b_u}  +  sum_{u<t} (W dS'^T)_u k_u e^{s_u}
+//        + Gc rowsum(S * dS')  +  sum_{j<t<=i} (beta_i dA_ij k_i + dP_ij q_i) k_j e^{b_i - b_j}.
+// The last form of dg_t (the derivative of everything through the decays b_u, u >= t, regrouped) has no
+// cancelling terms: every pair (i, j) of the in-chunk products enters only where it straddles t, weighted
+// by e^{b_i - b_j} summed from the decays between them, instead of as +E at i and -E at j, which in fp32
+// left the rounding of e^{+-b} (|b| up to 80) in dg. The chain runs in four launches:
+//   kda_cb_factors  (chunk, head): the factors above;
+//   kda_cb_fwd      (sequence, head, 32-column tile): the states S entering every chunk, X and W (and with an
+//                   output gate the core output, do * sigmoid(z) and dL/dz);
+//   kda_cb_rev      (sequence, head, 32-column tile): dS' leaving every chunk, dW, and dL/dS0;
+//   kda_cb_grad     (chunk, head): dq, dk, dv, dg, dbeta from the stored S, dS', X, W, dW.
+// Each column of S and of dS evolves on its own (decay scales rows), so the two sequential passes split V
+// into tiles; their thread (row group, column) holds K/8 rows of one column and sums over key rows go
+// through LDS. All arithmetic is fp32, deterministic (fixed summation orders, no atomics).
+// Factor block of one (chunk, head), fp32: Q~, K~, Kc, Wk [CB][K] row-major; T, P, M, Ab [CB][CB]; Gc [K].
+constexpr int64_t fac_floats(int K) { return ((4 * CB * K + 4 * CB * CB + K) + 63) / 64 * 64; }
+template <int K> struct FacL {
+    static constexpr int QG = 0, KG = CB * K, KC = 2 * CB * K, WK = 3 * CB * K;
+    static constexpr int TT = 4 * CB * K, PP = TT + CB * CB, MM = PP + CB * CB, AB = MM + CB * CB;
+    static constexpr int GC = AB + CB * CB;
+};
+
+// element i of an array of bf16 (bf) or fp32 values
+__device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
+    return bf ? bf2f(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
 }
-// Sum over the 4 lanes of a quad (the wavefront's 4 columns): quad_perm [1,0,3,2] then [2,3,0,1].
-__device__ __forceinline__ float sum_quad(float x) {
-    x += dpp_mov<0xB1>(x);
-    x += dpp_mov<0x4E>(x);
-    return x;
+// the log-decay of a gate input: as given, or -5 sigmoid(x)
+__device__ __forceinline__ float log_decay_of(float x, bool gate_sig) { return gate_sig ? -5.f * sigmoid_f(x) : x; }
+
+struct ChunkAt {
+    int n, nval;
+    int64_t tok0;
+};
+// chunk c (< chunk_off[N]): its sequence (the largest n < N with chunk_off[n] <= c), first token and
+// number of valid tokens
+__device__ __forceinline__ ChunkAt chunk_at(const int64_t *seq_tok, const int64_t *chunk_off, int N, int64_t c) {
+    int lo = 0, hi = N;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (chunk_off[mid] <= c) lo = mid;
+        else hi = mid;
+    }
+    ChunkAt r;
+    r.n = lo;
+    r.tok0 = seq_tok[lo] + (c - chunk_off[lo]) * CB;
+    const int64_t left = seq_tok[lo + 1] - r.tok0;
+    r.nval = (int)(left < CB ? left : CB);
+    return r;
 }
 
-// ------------------------------------------------------------------ main kernel
-// QK32 / V32: q and k (v) come as fp32 arrays (the prologue's normalised or convolved values) instead of
-// the I/O dtype.
-template <bool BF, int K, bool QK32, bool V32>
-__global__ __launch_bounds__(BNT, 3) void kda_bwd_kernel(
-    const typename IO<BF && !QK32>::T *__restrict__ q, const typename IO<BF && !QK32>::T *__restrict__ k,
-    const typename IO<BF && !V32>::T *__restrict__ v, const typename IO<BF>::T *__restrict__ g,
-    const typename IO<BF>::T *__restrict__ beta, const typename IO<BF>::T *__restrict__ dout,
-    const typename IO<BF>::T *__restrict__ zg, const float *__restrict__ S0, const float *__restrict__ dSf,
-    const int64_t *__restrict__ seq_tok,    const int64_t *__restrict__ seg_off, int32_t H, int32_t V, int32_t nvt, int64_t n_rows, bool gate_sig,
-    float *__restrict__ ckpt, float *__restrict__ part, float *__restrict__ dv_out, float *__restrict__ dz_out,
-    float *__restrict__ dS0) {
-    using io = IO<BF>;
-    using qkio = IO<BF && !QK32>;
-    using vio = IO<BF && !V32>;
-    constexpr int R = K / 16;          // rows per thread
-    constexpr int F = 3 * K + 1;       // partial row: dq | dk | dg | dbeta
-    constexpr int FP = 3 * K + 4;      // its pitch in the partial buffer (whole 16-byte groups)
-    constexpr int NE = BL * K / BNT;   // staged q/k/g elements per thread
-    static_assert(NE >= 1 && NE * BNT == BL * K, "segment staging");
-    __shared__ float sq[BL * K], sk[BL * K], sa[BL * K];  // q, k, e^g of the segment's tokens
-    // sdo: dL/do, times sigmoid(z) with an output gate; sdz: dL/do * sigmoid'(z)
-    __shared__ float sv[BL * BVT], sdo[BL * BVT], sdz[BL * BVT], sb[BL];
-    __shared__ float red[RT * 4 * F];  // per-wavefront column sums, [token % RT][wave][F]
+// ---- factors: one workgroup per (chunk, head). K-major copies of K~, K^ and Q~ (pitch CB + 1) serve the
+// CB x CB products without bank conflicts.
+template <int K>
+__global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q, const void *__restrict__ k,
+                                                      bool qk_bf, const void *__restrict__ g,
+                                                      const void *__restrict__ beta, bool io_bf, bool gate_sig,
+                                                      const int64_t *__restrict__ seq_tok,
+                                                      const int64_t *__restrict__ chunk_off, int32_t N, int32_t H,
+                                                      float *__restrict__ fac) {
+    using L = FacL<K>;
+    constexpr int KP = CB + 1;
+    __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
+    __shared__ float tKG[K * KP], tKI[K * KP], tQG[K * KP];
+    __shared__ float sA[CB * CB], sT[CB * CB], sb[CB];
+    const int tid = threadIdx.x;
+    const int64_t c = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    if (c >= chunk_off[N]) return;  // past the last chunk (the grid covers an upper bound)
+    const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+    float *blk = fac + ((int64_t)c * H + h) * fac_floats(K);
+    for (int e = tid; e < CB * K; e += CNT) {
+        const int t = e / K, ch = e % K;
+        const bool ok = t < at.nval;
+        const int64_t idx = ((at.tok0 + t) * H + h) * K + ch;
+        sq[e] = ok ? ld_as(q, idx, qk_bf) : 0.f;
+        sk[e] = ok ? ld_as(k, idx, qk_bf) : 0.f;
+        sg[e] = ok ? log_decay_of(ld_as(g, idx, io_bf), gate_sig) : 0.f;
+    }
+    if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * H + h, io_bf) : 0.f;
+    __syncthreads();
+    // prefix b, suffix s (each summed from its own terms), the scaled rows and Gc
+    for (int e = tid; e < CB * K; e += CNT) {
+        const int t = e / K, ch = e % K;
+        float b = 0.f, s = 0.f;
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const float x = sg[u * K + ch];
+            if (u <= t) b += x;
+            else s += x;
+        }
+        const float eb = exp_e(b), kv = sk[e], qv = sq[e];
+        const float kg = kv * eb, kh = kv * exp_e(-b), qg = qv * eb;
+        tKG[ch * KP + t] = kg;
+        tKI[ch * KP + t] = kh;
+        tQG[ch * KP + t] = qg;
+        blk[L::QG + e] = qg;
+        blk[L::KG + e] = kg;
+        blk[L::KC + e] = kv * exp_e(s);
+        if (t == CB - 1) blk[L::GC + ch] = eb;
+    }
+    __syncthreads();
+    // Ab and P: thread (i, j)
+    {
+        const int i = tid / CB, j = tid % CB;
+        float a = 0.f, p = 0.f;
+        for (int ch = 0; ch < K; ++ch) {
+            const float kh = tKI[ch * KP + j];
+            a += tKG[ch * KP + i] * kh;
+            p += tQG[ch * KP + i] * kh;
+        }
+        a = j < i ? a : 0.f;
+        p = j <= i ? p : 0.f;
+        blk[L::AB + tid] = a;
+        blk[L::PP + tid] = p;
+        sA[tid] = sb[i] * a;
+    }
+    __syncthreads();
+    // M = (I + A)^{-1} by forward substitution, one column per thread; T = M diag(beta)
+    if (tid < CB) {
+        const int j = tid;
+        float m[CB];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            float s = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int l = 0; l < i; ++l) s -= sA[i * CB + l] * m[l];
+            m[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const float tv = m[i] * sb[j];
+            blk[L::MM + i * CB + j] = m[i];
+            blk[L::TT + i * CB + j] = tv;
+            sT[i * CB + j] = tv;
+        }
+    }
+    __syncthreads();
+    // Wk = T K~
+    for (int e = tid; e < CB * K; e += CNT) {
+        const int t = e / K, ch = e % K;
+        float w = 0.f;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) w += sT[t * CB + j] * tKG[ch * KP + j];
+        blk[L::WK + e] = w;
+    }
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int c4 = lane & 3, rg = lane >> 2;
+// Workgroup barrier over LDS only: each wavefront's LDS operations are complete before it arrives, while
+// its global stores (states, X, W) stay in flight (a __syncthreads would wait for those as well).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Dot product of a thread's run of RPT consecutive entries of an LDS row (read as float4) with S, and the
+// update S += w * run.
+template <int RPT>
+__device__ __forceinline__ float dot_run(const float *lds_row, const float (&S)[RPT]) {
+    const float4 *p = reinterpret_cast<const float4 *>(lds_row);
+    float a = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT / 4; ++m) {
+        const float4 x = p[m];
+        a += x.x * S[4 * m] + x.y * S[4 * m + 1] + x.z * S[4 * m + 2] + x.w * S[4 * m + 3];
+    }
+    return a;
+}
+template <int RPT>
+__device__ __forceinline__ void axpy_run(float (&S)[RPT], const float *lds_row, float w) {
+    const float4 *p = reinterpret_cast<const float4 *>(lds_row);
+#pragma unroll
+    for (int m = 0; m < RPT / 4; ++m) {
+        const float4 x = p[m];
+        S[4 * m] += x.x * w;
+        S[4 * m + 1] += x.y * w;
+        S[4 * m + 2] += x.z * w;
+        S[4 * m + 3] += x.w * w;
+    }
+}
+
+// ---- forward states: one workgroup per (sequence, head, tile of CVT columns). Thread (rg, col) holds rows
+// rg*RPT .. +RPT-1 of column col of S. The next chunk's factors and v tile are fetched into registers while
+// the current chunk is processed.
+template <int K>
+__global__ __launch_bounds__(CNT) void kda_cb_fwd(const void *__restrict__ v, bool v_bf, const float *__restrict__ fac,
+                                                  const float *__restrict__ S0, const int64_t *__restrict__ seq_tok,
+                                                  const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                  int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
+                                                  float *__restrict__ Wbuf, const void *__restrict__ dout,
+                                                  const void *__restrict__ zg, bool io_bf, float *__restrict__ doe,
+                                                  float *__restrict__ dz) {
+    using L = FacL<K>;
+    constexpr int RG = CNT / CVT, RPT = K / RG, NE = CB * K / CNT, NV = CB * CVT / CNT;
+    static_assert(CB * CB == CNT && RPT % 4 == 0, "layout");
+    __shared__ __align__(16) float sKG[CB * K];
+    __shared__ __align__(16) float sKc[CB * K];
+    __shared__ __align__(16) float sQG[CB * K];
+    __shared__ float sT[CB * CB], sP[CB * CB], sGC[K];
+    __shared__ float sv[CB * CVT], sX[CB * CVT], sW[CB * CVT], red[RG * CB * CVT], red2[RG * CB * CVT];
+    const bool og = zg != nullptr;
+    const int tid = threadIdx.x, col = tid % CVT, rg = tid / CVT;
     int64_t bid = blockIdx.x;
     const int vt = (int)(bid % nvt);
     bid /= nvt;
     const int h = (int)(bid % H);
     const int64_t n = bid / H;
-    const int col = vt * BVT + wv * 4 + c4;
-    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1];
-    const int nseg = (int)((t1 - t0 + BL - 1) / BL);
-    const int64_t ck0 = seg_off[n];
-    const int64_t sH = (int64_t)H, sV = (int64_t)V;
-
-    // ---- segment staging: global -> registers (one segment ahead) -> LDS
-    float pq[NE], pk[NE], pg[NE], pvd = 0.f, pz = 0.f, pb = 0.f;
-    auto fetch = [&](int s, bool with_q) {
-        const int64_t ft0 = t0 + (int64_t)s * BL;
+    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
+    const int nch = (int)((t1 - t0 + CB - 1) / CB);
+    const int vc = vt * CVT + col;
+    const int64_t sH = H, sV = V;
+    float S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) S[i] = S0 ? S0[((n * sH + h) * K + rg * RPT + i) * sV + vc] : 0.f;
+    float pKG[NE], pKc[NE], pQG[NE], pT = 0.f, pP = 0.f, pGC = 0.f, pv[NV], pdo[NV], pz[NV];
+    auto fetch = [&](int ci) {
+        const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
+        const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
+        const float *blk = fac + (c * sH + h) * fac_floats(K);
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
-            const int e = tid + BNT * m, tok = e / K, r = e % K;
-            const int64_t ft = ft0 + tok;
-            const bool ok = ft < t1;
-            const int64_t idx = (ft * sH + h) * K + r;
-            pk[m] = ok ? qkio::ld(k, idx) : 0.f;
-            pg[m] = ok ? io::ld(g, idx) : 0.f;
-            pq[m] = (ok && with_q) ? qkio::ld(q, idx) : 0.f;
+            pKG[m] = blk[L::KG + tid + CNT * m];
+            pKc[m] = blk[L::KC + tid + CNT * m];
+            pQG[m] = og ? blk[L::QG + tid + CNT * m] : 0.f;
         }
-        {
-            const int e = tid & (BL * BVT - 1), tok = e / BVT, c = e % BVT;
-            const int64_t ft = ft0 + tok;
-            const bool isv = tid < BL * BVT;
-            const bool ok = ft < t1 && (isv || with_q);
-            const int64_t ve = (ft * sH + h) * sV + vt * BVT + c;
-            pvd = ok ? (isv ? vio::ld(v, ve) : io::ld(dout, ve)) : 0.f;
-            pz = (ok && !isv && zg) ? io::ld(zg, (ft * sH + h) * sV + vt * BVT + c) : 0.f;
+        pT = blk[L::TT + tid];
+        pP = og ? blk[L::PP + tid] : 0.f;
+        pGC = tid < K ? blk[L::GC + tid] : 0.f;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+            const bool ok = t < nval;
+            const int64_t idx = ((tok0 + t) * sH + h) * sV + vt * CVT + cc;
+            pv[m] = ok ? ld_as(v, idx, v_bf) : 0.f;
+            pdo[m] = (ok && og) ? ld_as(dout, idx, io_bf) : 0.f;
+            pz[m] = (ok && og) ? ld_as(zg, idx, io_bf) : 0.f;
         }
-        pb = (tid < BL && ft0 + tid < t1) ? io::ld(beta, (ft0 + tid) * sH + h) : 0.f;
     };
-    auto stage = [&]() {
+    if (nch > 0) fetch(0);
+    for (int ci = 0; ci < nch; ++ci) {
+        const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
+        const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
+        lds_barrier();  // the previous chunk's LDS reads are done
 #pragma unroll
         for (int m = 0; m < NE; ++m) {
-            const int e = tid + BNT * m;
-            sq[e] = pq[m];
-            sk[e] = pk[m];
-            // the retention e^g, with g the log-decay as given or -5 sigmoid(x) formed here
-            sa[e] = gate_sig ? __builtin_amdgcn_exp2f(gate_log2_decay(pg[m])) : exp_e(pg[m]);
+            sKG[tid + CNT * m] = pKG[m];
+            sKc[tid + CNT * m] = pKc[m];
+            if (og) sQG[tid + CNT * m] = pQG[m];
         }
-        if (tid < BL * BVT) {
-            sv[tid] = pvd;
-        } else if (tid < 2 * BL * BVT) {
-            // the output gate o * sigmoid(z): the core output's gradient is do * sigmoid(z), and z's is
-            // do * o * sigmoid(z) (1 - sigmoid(z))
-            const float sz = zg ? sigmoid_f(pz) : 1.f;
-            sdo[tid - BL * BVT] = pvd * sz;
-            sdz[tid - BL * BVT] = pvd * sz * (1.f - sz);
+        sT[tid] = pT;
+        if (og) sP[tid] = pP;
+        if (tid < K) sGC[tid] = pGC;
+        float cdo[NV], cz[NV];
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            sv[tid + CNT * m] = pv[m];
+            cdo[m] = pdo[m];
+            cz[m] = pz[m];
         }
-        if (tid < BL) sb[tid] = pb;
+        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) sp[(rg * RPT + i) * sV + vc] = S[i];
+        lds_barrier();
+        if (ci + 1 < nch) fetch(ci + 1);
+        // partial sums over this thread's rows: (K~ S)[t][col], (Q~ S)[t][col]
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            red[(rg * CB + t) * CVT + col] = dot_run<RPT>(sKG + t * K + rg * RPT, S);
+            if (og) red2[(rg * CB + t) * CVT + col] = dot_run<RPT>(sQG + t * K + rg * RPT, S);
+        }
+        lds_barrier();
+        float oi[NV];
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+            float s = 0.f, o = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                s += red[(r * CB + t) * CVT + cc];
+                if (og) o += red2[(r * CB + t) * CVT + cc];
+            }
+            sX[e] = sv[e] - s;
+            oi[m] = o;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+            float w = 0.f;
+#pragma unroll
+            for (int j = 0; j < CB; ++j) w += sT[t * CB + j] * sX[j * CVT + cc];
+            sW[e] = w;
+            const int64_t xo = ((c * sH + h) * CB + t) * sV + vt * CVT + cc;
+            Xbuf[xo] = sX[e];
+            Wbuf[xo] = w;
+        }
+        lds_barrier();
+        if (og) {  // core output O = Q~ S + P W; do * sigmoid(z) for the reverse, and dL/dz
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+                if (t < nval) {
+                    float o = oi[m];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) o += sP[t * CB + j] * sW[j * CVT + cc];
+                    const int64_t idx = ((tok0 + t) * sH + h) * sV + vt * CVT + cc;
+                    const float sz = sigmoid_f(cz[m]);
+                    doe[idx] = cdo[m] * sz;
+                    dz[idx] = cdo[m] * o * sz * (1.f - sz);
+                }
+            }
+        }
+        // S' = diag(Gc) S + Kc^T W
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) S[i] *= sGC[rg * RPT + i];
+#pragma unroll
+        for (int t = 0; t < CB; ++t) axpy_run<RPT>(S, sKc + t * K + rg * RPT, sW[t * CVT + col]);
+    }
+}
+
+// ---- reverse: one workgroup per (sequence, head, tile of CVT columns), chunks last to first.
+template <int K>
+__global__ __launch_bounds__(CNT) void kda_cb_rev(const void *__restrict__ dout, bool do_bf,
+                                                  const float *__restrict__ fac, const float *__restrict__ dSf,
+                                                  const int64_t *__restrict__ seq_tok,
+                                                  const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                  int32_t nvt, float *__restrict__ dSbuf, float *__restrict__ dWbuf,
+                                                  float *__restrict__ dS0) {
+    using L = FacL<K>;
+    constexpr int RG = CNT / CVT, RPT = K / RG, NE = CB * K / CNT, NV = CB * CVT / CNT;
+    static_assert(CB * CB == CNT && RPT % 4 == 0, "layout");
+    __shared__ __align__(16) float sKc[CB * K];
+    __shared__ __align__(16) float sQG[CB * K];
+    __shared__ __align__(16) float sWk[CB * K];
+    __shared__ float sP[CB * CB], sGC[K], sdo[CB * CVT], sdW[CB * CVT], red[RG * CB * CVT];
+    const int tid = threadIdx.x, col = tid % CVT, rg = tid / CVT;
+    int64_t bid = blockIdx.x;
+    const int vt = (int)(bid % nvt);
+    bid /= nvt;
+    const int h = (int)(bid % H);
+    const int64_t n = bid / H;
+    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
+    const int nch = (int)((t1 - t0 + CB - 1) / CB);
+    const int vc = vt * CVT + col;
+    const int64_t sH = H, sV = V;
+    float dS[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) dS[i] = dSf ? dSf[((n * sH + h) * K + rg * RPT + i) * sV + vc] : 0.f;
+    float pKc[NE], pQG[NE], pWk[NE], pP = 0.f, pGC = 0.f, pdo[NV];
+    auto fetch = [&](int ci) {
+        const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
+        const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
+        const float *blk = fac + (c * sH + h) * fac_floats(K);
+#pragma unroll
+        for (int m = 0; m < NE; ++m) {
+            pKc[m] = blk[L::KC + tid + CNT * m];
+            pQG[m] = blk[L::QG + tid + CNT * m];
+            pWk[m] = blk[L::WK + tid + CNT * m];
+        }
+        pP = blk[L::PP + tid];
+        pGC = tid < K ? blk[L::GC + tid] : 0.f;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+            pdo[m] = t < nval ? ld_as(dout, ((tok0 + t) * sH + h) * sV + vt * CVT + cc, do_bf) : 0.f;
+        }
     };
-    // checkpoint s of this workgroup: [seg][h][vt][R][256], thread-private and coalesced
-    auto ck_ptr = [&](int s) { return ckpt + (((ck0 + s) * sH + h) * nvt + vt) * (int64_t)(R * BNT) + tid; };
-
-    // ---- 1. forward: checkpoints
-    float S[R];
+    if (nch > 0) fetch(nch - 1);
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const int64_t c = c0 + ci;
+        lds_barrier();
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-        S[i] = S0 ? S0[((n * sH + h) * K + rg * R + i) * sV + col] : 0.f;
-    if (nseg > 0) fetch(0, false);
-    for (int s = 0; s < nseg; ++s) {
-        __syncthreads();
-        stage();
-        __syncthreads();
-        if (s + 1 < nseg) fetch(s + 1, false);
-        float *cp = ck_ptr(s);
-#pragma unroll
-        for (int i = 0; i < R; ++i) cp[i * BNT] = S[i];
-#pragma unroll
-        for (int tt = 0; tt < BL; ++tt) {
-            float u = 0.f, kk[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                kk[i] = sk[tt * K + rg * R + i];
-                S[i] *= sa[tt * K + rg * R + i];
-                u += S[i] * kk[i];
-            }
-            u = sum_rows(u);
-            const float bd = sb[tt] * (sv[tt * BVT + wv * 4 + c4] - u);
-#pragma unroll
-            for (int i = 0; i < R; ++i) S[i] += kk[i] * bd;
+        for (int m = 0; m < NE; ++m) {
+            sKc[tid + CNT * m] = pKc[m];
+            sQG[tid + CNT * m] = pQG[m];
+            sWk[tid + CNT * m] = pWk[m];
         }
-    }
-
-    // ---- 2. backward over the segments
-    float G[R], C[R];
+        sP[tid] = pP;
+        if (tid < K) sGC[tid] = pGC;
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-        G[i] = dSf ? dSf[((n * sH + h) * K + rg * R + i) * sV + col] : 0.f;
-    if (nseg > 0) {
-        fetch(nseg - 1, true);
-        const float *cp = ck_ptr(nseg - 1);
+        for (int m = 0; m < NV; ++m) sdo[tid + CNT * m] = pdo[m];
+        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V);
 #pragma unroll
-        for (int i = 0; i < R; ++i) C[i] = cp[i * BNT];
-    }
-    for (int s = nseg - 1; s >= 0; --s) {
-        __syncthreads();  // the previous segment's LDS reads (staging and red) are done
-        stage();
-        float X[R];
+        for (int i = 0; i < RPT; ++i) dp[(rg * RPT + i) * sV + vc] = dS[i];
+        lds_barrier();
+        if (ci > 0) fetch(ci - 1);
 #pragma unroll
-        for (int i = 0; i < R; ++i) X[i] = C[i];
-        __syncthreads();
-        if (s > 0) {
-            fetch(s - 1, true);
-            const float *cp = ck_ptr(s - 1);
+        for (int t = 0; t < CB; ++t) red[(rg * CB + t) * CVT + col] = dot_run<RPT>(sKc + t * K + rg * RPT, dS);
+        lds_barrier();
 #pragma unroll
-            for (int i = 0; i < R; ++i) C[i] = cp[i * BNT];
+        for (int m = 0; m < NV; ++m) {
+            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+            float s = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) s += red[(r * CB + t) * CVT + cc];
+#pragma unroll
+            for (int j = 0; j < CB; ++j) s += sP[j * CB + t] * sdo[j * CVT + cc];
+            sdW[e] = s;
+            dWbuf[((c * sH + h) * CB + t) * sV + vt * CVT + cc] = s;
         }
-        // recompute the segment's decayed states A_t and errors d_t (registers)
-        float A[BL][R], d[BL];
+        lds_barrier();
+        // dS = diag(Gc) dS' + Q~^T dO - Wk^T dW
 #pragma unroll
-        for (int tt = 0; tt < BL; ++tt) {
-            float u = 0.f;
+        for (int i = 0; i < RPT; ++i) dS[i] *= sGC[rg * RPT + i];
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                X[i] *= sa[tt * K + rg * R + i];
-                A[tt][i] = X[i];
-                u += X[i] * sk[tt * K + rg * R + i];
-            }
-            u = sum_rows(u);
-            d[tt] = sv[tt * BVT + wv * 4 + c4] - u;
-            const float bd = sb[tt] * d[tt];
-#pragma unroll
-            for (int i = 0; i < R; ++i) X[i] += sk[tt * K + rg * R + i] * bd;
-        }
-        // reverse steps (tokens past the sequence end are identities and write nothing); the column sums
-        // go to LDS and are flushed every RT tokens
-        const int64_t ft0 = t0 + (int64_t)s * BL;
-        auto flush = [&](int base) {
-            __syncthreads();
-            for (int e = tid; e < RT * F; e += BNT) {
-                const int tt = e / F, f = e % F;
-                const int64_t ft = ft0 + base + tt;
-                if (ft < t1) {
-                    const float *rr = red + tt * 4 * F + f;
-                    part[((int64_t)vt * n_rows + ft * sH + h) * FP + f] = ((rr[0] + rr[F]) + rr[2 * F]) + rr[3 * F];
-                }
-            }
-            __syncthreads();
-        };
-#pragma unroll
-        for (int tt = BL - 1; tt >= 0; --tt) {
-            if (ft0 + tt < t1) {
-                const float b = sb[tt], o = sdo[tt * BVT + wv * 4 + c4];
-                float w = 0.f, oc = 0.f, pdq[R], pdk[R], pdg[R];
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const float kk = sk[tt * K + rg * R + i], qq = sq[tt * K + rg * R + i];
-                    const float st = A[tt][i] + b * kk * d[tt];  // S_t
-                    G[i] += qq * o;
-                    pdq[i] = st * o;  // S_t do_t
-                    oc += st * qq;    // the core output o_t = S_t^T q_t (used with an output gate)
-                    w += G[i] * kk;
-                }
-                w = sum_rows(w);
-                if (zg) {
-                    oc = sum_rows(oc);
-                    if (rg == 0) dz_out[((ft0 + tt) * sH + h) * sV + col] = oc * sdz[tt * BVT + wv * 4 + c4];
-                }
-                const float dv = b * w;
-                if (rg == 0) dv_out[((ft0 + tt) * sH + h) * sV + col] = dv;
-                float pbeta = w * d[tt];
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const float kk = sk[tt * K + rg * R + i];
-                    pdk[i] = b * d[tt] * G[i] - A[tt][i] * dv;
-                    const float ga = G[i] - kk * dv;
-                    pdg[i] = ga * A[tt][i];
-                    G[i] = sa[tt * K + rg * R + i] * ga;
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    pdq[i] = sum_quad(pdq[i]);
-                    pdk[i] = sum_quad(pdk[i]);
-                    pdg[i] = sum_quad(pdg[i]);
-                }
-                pbeta = sum_quad(pbeta);
-                // the 4 lanes of a quad hold equal sums and every lane of the wavefront the same pbeta, so
-                // all lanes store (equal values to equal addresses): no divergent branch, which lets the
-                // quad sums' DPP moves fuse into their adds
-                {
-                    float *rr = red + ((tt % RT) * 4 + wv) * F;
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        rr[rg * R + i] = pdq[i];
-                        rr[K + rg * R + i] = pdk[i];
-                        rr[2 * K + rg * R + i] = pdg[i];
-                    }
-                    rr[3 * K] = pbeta;
-                }
-            }
-            if (tt % RT == 0) flush(tt);
+        for (int t = 0; t < CB; ++t) {
+            axpy_run<RPT>(dS, sQG + t * K + rg * RPT, sdo[t * CVT + col]);
+            axpy_run<RPT>(dS, sWk + t * K + rg * RPT, -sdW[t * CVT + col]);
         }
     }
     if (dS0) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) dS0[((n * sH + h) * K + rg * R + i) * sV + col] = G[i];
+        for (int i = 0; i < RPT; ++i) dS0[((n * sH + h) * K + rg * RPT + i) * sV + vc] = dS[i];
     }
 }
 
-// dq, dk, dg, dbeta of every covered (token, head): the tiles' partial sums added in tile order. With the
-// scaled-sigmoid gate, g holds the pre-activation x and the log-decay gradient is carried through
-// d(-5 sigmoid(x))/dx = -5 sigmoid(x) (1 - sigmoid(x)). One thread per 4 consecutive entries of a partial row
-// (rows have a pitch of 3K + 4 floats, so every group is one 16-byte load per tile); group 3K/4 holds dbeta.
-template <bool BF, int K>
-__global__ __launch_bounds__(256) void kda_bwd_reduce(const float *__restrict__ part, int32_t nvt, int64_t n_rows,
-                                                      int32_t H, const int64_t *__restrict__ seq_tok, int32_t N,
-                                                      const typename IO<BF>::T *__restrict__ g, bool gate_sig,
-                                                      float *__restrict__ dq, float *__restrict__ dk,
-                                                      float *__restrict__ dg, float *__restrict__ dbeta) {
-    constexpr int FP = 3 * K + 4, G = FP / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n_rows * G) return;
-    const int64_t row = idx / G;
-    const int f = 4 * (int)(idx % G);
-    const int64_t ft = row / H;
-    if (ft < seq_tok[0] || ft >= seq_tok[N]) return;  // outside every sequence: not written
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int t = 0; t < nvt; ++t) {
-        const float4 x = *reinterpret_cast<const float4 *>(part + ((int64_t)t * n_rows + row) * FP + f);
-        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+// sum over the TPR consecutive lanes that share a key row (TPR = 2, 4 or 8)
+template <int TPR>
+__device__ __forceinline__ float sum_lanes(float x) {
+    x += dpp_mov<0xB1>(x);                        // quad_perm [1,0,3,2]
+    if constexpr (TPR >= 4) x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
+    if constexpr (TPR >= 8) x += __shfl_xor(x, 4);
+    return x;
+}
+
+// ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) floats; the
+// four [CB][VM] buffers hold dO, X (then dX), W, dW, and afterwards the per-(token, channel) terms of dg
+// and the factors e^{+-b}.
+template <int K, int V>
+__global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
+    const void *__restrict__ q, const void *__restrict__ k, bool qk_bf, const void *__restrict__ g,
+    const void *__restrict__ beta, bool io_bf, bool gate_sig, const void *__restrict__ dout, bool do_bf,
+    const float *__restrict__ fac, const float *__restrict__ Sbuf, const float *__restrict__ dSbuf,
+    const float *__restrict__ Xbuf, const float *__restrict__ Wbuf, const float *__restrict__ dWbuf,
+    const int64_t *__restrict__ seq_tok, const int64_t *__restrict__ chunk_off, int32_t N, int32_t H,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
+    float *__restrict__ dbeta) {
+    using L = FacL<K>;
+    constexpr int VM = K > V ? K : V;
+    constexpr int TPR = CNT / K, VPT = V / TPR;  // threads per key row; value columns per thread
+    constexpr int CPT = K / 16;                  // channels per thread in the per-(token, channel) phase
+    __shared__ float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
+    __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
+    __shared__ float sT[CB * CB], sM[CB * CB], sP[CB * CB], sAb[CB * CB], sdT[CB * CB], sdP[CB * CB];
+    __shared__ float sY[CB * CB], sdA[CB * CB], sbdA[CB * CB], sb[CB], sdbT[CB], sdGC[K], sGC[K];
+    const int tid = threadIdx.x;
+    const int64_t c = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    if (c >= chunk_off[N]) return;
+    const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+    const int64_t sH = H, sV = V, ch0 = c * sH + h;
+    const float *blk = fac + ch0 * fac_floats(K);
+    // ---- a. loads
+    for (int e = tid; e < CB * V; e += CNT) {
+        const int t = e / V, vv = e % V;
+        const int64_t xo = (ch0 * CB + t) * sV + vv;
+        b0[t * VM + vv] = t < at.nval ? ld_as(dout, ((at.tok0 + t) * sH + h) * sV + vv, do_bf) : 0.f;
+        b1[t * VM + vv] = Xbuf[xo];
+        b2[t * VM + vv] = Wbuf[xo];
+        b3[t * VM + vv] = dWbuf[xo];
     }
-    if (f < K) {
-        *reinterpret_cast<float4 *>(dq + row * K + f) = acc;
-    } else if (f < 2 * K) {
-        *reinterpret_cast<float4 *>(dk + row * K + f - K) = acc;
-    } else if (f < 3 * K) {
-        if (gate_sig) {
-            float a[4] = {acc.x, acc.y, acc.z, acc.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sx = sigmoid_f(IO<BF>::ld(g, row * K + f - 2 * K + i));
-                a[i] *= -5.f * sx * (1.f - sx);
-            }
-            acc = make_float4(a[0], a[1], a[2], a[3]);
+    for (int e = tid; e < CB * K; e += CNT) {
+        const int t = e / K, ch = e % K;
+        const bool ok = t < at.nval;
+        const int64_t idx = ((at.tok0 + t) * sH + h) * K + ch;
+        sq[e] = ok ? ld_as(q, idx, qk_bf) : 0.f;
+        sk[e] = ok ? ld_as(k, idx, qk_bf) : 0.f;
+        sg[e] = ok ? log_decay_of(ld_as(g, idx, io_bf), gate_sig) : 0.f;
+    }
+    sT[tid] = blk[L::TT + tid];
+    sM[tid] = blk[L::MM + tid];
+    sP[tid] = blk[L::PP + tid];
+    sAb[tid] = blk[L::AB + tid];
+    for (int e = tid; e < K; e += CNT) sGC[e] = blk[L::GC + e];
+    if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * sH + h, io_bf) : 0.f;
+    __syncthreads();
+    // ---- b. dT = dW X^T, dP = tril(dO W^T): thread (i, j); the column order is rotated by j so that the 16
+    // rows j of a wavefront fall in distinct banks
+    {
+        const int i = tid / CB, j = tid % CB;
+        float dt = 0.f, dp = 0.f;
+        for (int u = 0; u < V; ++u) {
+            const int vv = (u + j) & (V - 1);
+            dt += b3[i * VM + vv] * b1[j * VM + vv];
+            dp += b0[i * VM + vv] * b2[j * VM + vv];
         }
-        *reinterpret_cast<float4 *>(dg + row * K + f - 2 * K) = acc;
-    } else {
-        dbeta[row] = acc.x;
+        sdT[tid] = dt;
+        sdP[tid] = j <= i ? dp : 0.f;
+    }
+    __syncthreads();
+    // ---- c. dX = T^T dW (= dv), into b1; dbeta's T part
+    for (int e = tid; e < CB * V; e += CNT) {
+        const int t = e / V, vv = e % V;
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < CB; ++i) s += sT[i * CB + t] * b3[i * VM + vv];
+        b1[t * VM + vv] = s;
+        if (t < at.nval) dv[((at.tok0 + t) * sH + h) * sV + vv] = s;
+    }
+    if (tid < CB) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < CB; ++i) s += sM[i * CB + tid] * sdT[i * CB + tid];
+        sdbT[tid] = s;
+    }
+    __syncthreads();
+    // ---- d. Y = dM M^T with dM = dT diag(beta)
+    {
+        const int i = tid / CB, j = tid % CB;
+        float y = 0.f;
+#pragma unroll
+        for (int l = 0; l < CB; ++l) y += sdT[i * CB + l] * sb[l] * sM[j * CB + l];
+        sY[tid] = y;
+    }
+    __syncthreads();
+    // ---- e. dA = -tril_strict(M^T Y)
+    {
+        const int i = tid / CB, j = tid % CB;
+        float a = 0.f;
+#pragma unroll
+        for (int l = 0; l < CB; ++l) a -= sM[l * CB + i] * sY[l * CB + j];
+        a = j < i ? a : 0.f;
+        sdA[tid] = a;
+        sbdA[tid] = sb[i] * a;
+    }
+    // ---- f. contractions over V with S and dS': (dO S^T), (dX S^T), (W dS'^T) [CB][K] and rowsum(S * dS')
+    float a1[CB], a2[CB], a3[CB], fsd = 0.f;
+#pragma unroll
+    for (int t = 0; t < CB; ++t) a1[t] = a2[t] = a3[t] = 0.f;
+    const int r = tid / TPR, part = tid % TPR;
+    {
+        const float *Sr = Sbuf + (ch0 * K + r) * sV + part * VPT;
+        const float *dSr = dSbuf + (ch0 * K + r) * sV + part * VPT;
+        for (int v0 = 0; v0 < VPT; v0 += 4) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(Sr + v0);
+            const float4 d4 = *reinterpret_cast<const float4 *>(dSr + v0);
+            fsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+            const int vo = part * VPT + v0;
+#pragma unroll
+            for (int t = 0; t < CB; ++t) {
+                const float4 o = *reinterpret_cast<const float4 *>(b0 + t * VM + vo);
+                const float4 x = *reinterpret_cast<const float4 *>(b1 + t * VM + vo);
+                const float4 w = *reinterpret_cast<const float4 *>(b2 + t * VM + vo);
+                a1[t] += o.x * s4.x + o.y * s4.y + o.z * s4.z + o.w * s4.w;
+                a2[t] += x.x * s4.x + x.y * s4.y + x.z * s4.z + x.w * s4.w;
+                a3[t] += w.x * d4.x + w.y * d4.y + w.z * d4.z + w.w * d4.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < CB; ++t) {
+        a1[t] = sum_lanes<TPR>(a1[t]);
+        a2[t] = sum_lanes<TPR>(a2[t]);
+        a3[t] = sum_lanes<TPR>(a3[t]);
+    }
+    fsd = sum_lanes<TPR>(fsd);
+    __syncthreads();  // every read of b0..b3 is done
+    if (part == 0) {
+#pragma unroll
+        for (int t = 0; t < CB; ++t) {
+            b0[t * VM + r] = a1[t];
+            b1[t * VM + r] = a2[t];
+            b2[t * VM + r] = a3[t];
+        }
+        sdGC[r] = fsd;
+    }
+    if (tid < CB && tid < at.nval) {  // dbeta
+        const int i = tid;
+        float s = sdbT[i];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) s += sdA[i * CB + j] * sAb[i * CB + j];
+        dbeta[(at.tok0 + i) * sH + h] = s;
+    }
+    __syncthreads();
+    // ---- g. per key channel (threads 0 .. K-1), over the chunk's 16 tokens. alpha_u = e^{g_u}; e^{b_u} and
+    // e^{s_u} are running products of them, and so is the weight e^{b_i - b_j} of every pair j < i (a product
+    // of the decays between the two tokens, accurate to the pair's own length). The accumulators of dq, dk
+    // and of dg's difference array live in this thread's column of b0, b1, b2 (row u at u * VM), and the
+    // remaining terms of dg in b3.
+    if (tid < K) {
+        const int ch = tid;
+        float *aq = b0 + ch, *ak = b1 + ch, *aD = b2 + ch, *base = b3 + ch;
+        float qv[CB], kv[CB], al[CB];
+        {
+            float run = 1.f;
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                qv[u] = sq[u * K + ch];
+                kv[u] = sk[u * K + ch];
+                al[u] = exp_e(sg[u * K + ch]);
+                run *= al[u];
+                base[u * VM] = run;  // e^{b_u} for the next loop
+            }
+        }
+        // token-local terms, last token first:
+        //   dq_t = e^{b_t} (dO S^T)_t + dP_tt k_t,  dk_t = -e^{b_t} (dX S^T)_t + dP_tt q_t + e^{s_t} (W dS'^T)_t,
+        //   base_t = sum_{u>=t} ((dO S^T)_u q_u - (dX S^T)_u k_u) e^{b_u}, and in D_t the Kc term
+        //   (W dS'^T)_t k_t e^{s_t}, whose exclusive prefix sum the loop after adds to base
+        {
+            float esr = 1.f, suf = 0.f;
+#pragma unroll
+            for (int u = CB - 1; u >= 0; --u) {
+                const float ebu = base[u * VM];
+                const float r1 = aq[u * VM], r2 = ak[u * VM], r3 = aD[u * VM], dpd = sdP[u * CB + u];
+                aq[u * VM] = ebu * r1 + dpd * kv[u];
+                ak[u * VM] = -ebu * r2 + dpd * qv[u] + esr * r3;
+                suf += (r1 * qv[u] - r2 * kv[u]) * ebu;
+                base[u * VM] = suf;
+                aD[u * VM] = r3 * kv[u] * esr;
+                esr *= al[u];
+            }
+        }
+        {
+            const float gcd = sdGC[ch] * sGC[ch];  // Gc rowsum(S * dS')
+            float pre = 0.f;
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const float d = aD[u * VM];
+                base[u * VM] += pre + gcd;
+                pre += d;
+                aD[u * VM] = 0.f;
+            }
+        }
+        // pairs j < i: Z = dP_ij q_i + beta_i dA_ij k_i
+        //   dk_j += Z w,  dq_i += dP_ij k_j w,  dk_i += beta_i dA_ij k_j w,
+        //   and E = Z k_j w enters dg_t for j < t <= i (D_{j+1} += E, D_{i+1} -= E)
+#pragma unroll
+        for (int j = 0; j < CB - 1; ++j) {
+            const float kj = kv[j];
+            float w = 1.f, dkj = 0.f, Dj = 0.f;
+#pragma unroll
+            for (int i = j + 1; i < CB; ++i) {
+                w *= al[i];
+                const float pz = sdP[i * CB + j], az = sbdA[i * CB + j];
+                const float Z = pz * qv[i] + az * kv[i];
+                const float kw = kj * w;
+                dkj += Z * w;
+                aq[i * VM] += pz * kw;
+                ak[i * VM] += az * kw;
+                const float E = Z * kw;
+                Dj += E;
+                if (i + 1 < CB) aD[(i + 1) * VM] -= E;
+            }
+            ak[j * VM] += dkj;
+            aD[(j + 1) * VM] += Dj;
+        }
+        float F = 0.f;
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            F += aD[u * VM];
+            if (u < at.nval) {
+                const int64_t idx = ((at.tok0 + u) * sH + h) * K + ch;
+                float dgv = base[u * VM] + F;
+                if (gate_sig) {
+                    const float sx = sigmoid_f(ld_as(g, idx, io_bf));
+                    dgv *= -5.f * sx * (1.f - sx);
+                }
+                dq[idx] = aq[u * VM];
+                dk[idx] = ak[u * VM];
+                dg[idx] = dgv;
+            }
+        }
     }
 }
 
@@ -714,7 +1079,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
     int64_t *seq_tok, *seg_off;
-    float *ckpt, *part;
+    // the chunk form: factor blocks per (chunk, head); the state entering and the state gradient leaving every
+    // (chunk, head) [K][V]; X, W, dW per (chunk, head) [CB][V]; do * sigmoid(z) per token (output gate)
+    float *fac, *Sb, *dSb, *Xb, *Wb, *dWb, *doe;
     // with the prologue: its outputs (xq, xk, xv), the recurrence's gradients with respect to them
     // (gq, gk, gv), the normalisation's factors (rq, rk) and the taps' partial sums (dw_part)
     float *xq, *xk, *xv, *gq, *gk, *gv, *rq, *rk, *dw_part;
@@ -722,8 +1089,8 @@ struct BwdWs {
 
 int64_t conv_tiles(int64_t n_tokens) { return (n_tokens + CONV_TILE - 1) / CONV_TILE; }
 
-BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_segs, int32_t H, int32_t K, int32_t V, bool norm,
-               bool conv, size_t *total = nullptr) {
+BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_chunks, int32_t H, int32_t K, int32_t V,
+               bool norm, bool conv, size_t *total = nullptr) {
     char *p = (char *)ws;
     BwdWs r;
     auto take = [&](size_t bytes) {
@@ -731,11 +1098,17 @@ BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_segs, int32_t 
         p += align256(bytes);
         return q;
     };
+    const size_t ch = (size_t)max_chunks * H;
     r.seq_tok = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.seg_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
-    r.ckpt = (float *)take(sizeof(float) * (size_t)max_segs * H * K * V);
-    r.part = (float *)take(sizeof(float) * (size_t)(V / BVT) * n_tokens * H * (3 * K + 4));
+    r.fac = (float *)take(sizeof(float) * ch * (size_t)fac_floats(K));
+    r.Sb = (float *)take(sizeof(float) * ch * K * V);
+    r.dSb = (float *)take(sizeof(float) * ch * K * V);
+    r.Xb = (float *)take(sizeof(float) * ch * CB * V);
+    r.Wb = (float *)take(sizeof(float) * ch * CB * V);
+    r.dWb = (float *)take(sizeof(float) * ch * CB * V);
     const size_t nk = (size_t)n_tokens * H * K * sizeof(float), nv = (size_t)n_tokens * H * V * sizeof(float);
+    r.doe = (float *)take(nv);  // used with an output gate (the size query does not know whether one comes)
     const bool pro = norm || conv;
     r.xq = pro ? (float *)take(nk) : nullptr;
     r.xk = pro ? (float *)take(nk) : nullptr;
@@ -752,23 +1125,33 @@ BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_segs, int32_t 
 
 unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-template <bool BF, int K, bool QK32, bool V32>
-void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void *ks, const void *vs, float *dv_dst,
-              float *dq_dst, float *dk_dst, hipStream_t st) {
-    using T = typename IO<BF>::T;
-    using TQ = typename IO<BF && !QK32>::T;
-    using TV = typename IO<BF && !V32>::T;
-    const int nvt = a.V / BVT;
-    const int64_t n_rows = a.B * a.T * a.H;
-    const int64_t nblk = (int64_t)a.num_seqs * a.H * nvt;
-    hipLaunchKernelGGL((kda_bwd_kernel<BF, K, QK32, V32>), dim3((unsigned)nblk), dim3(BNT), 0, st, (const TQ *)qs,
-                       (const TQ *)ks, (const TV *)vs, (const T *)a.g, (const T *)a.beta, (const T *)a.dout,
-                       (const T *)a.o_gate, a.S0, a.dS_final, w.seq_tok, w.seg_off, a.H, a.V, nvt, n_rows,
-                       a.gate_sigmoid, w.ckpt, w.part, dv_dst, a.d_o_gate, a.dS0);
-    const int64_t nel = n_rows * ((3 * K + 4) / 4);
-    if (nel > 0)
-        hipLaunchKernelGGL((kda_bwd_reduce<BF, K>), dim3(blocks_of(nel)), dim3(256), 0, st, w.part, nvt, n_rows, a.H,
-                           w.seq_tok, a.num_seqs, (const T *)a.g, a.gate_sigmoid, dq_dst, dk_dst, a.dg, a.dbeta);
+// The recurrence's reverse: q and k (qk_bf: bf16, else fp32) and v (v_bf) as the recurrence saw them; dq, dk
+// and dv go to the given fp32 arrays (the outputs, or the prologue's gradients).
+template <int K, int V>
+void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void *ks, bool qk_bf, const void *vs,
+              bool v_bf, float *dv_dst, float *dq_dst, float *dk_dst, hipStream_t st) {
+    const bool io_bf = a.io_bf16, og = a.o_gate != nullptr;
+    const int32_t nvt = V / CVT > 0 ? V / CVT : 1;
+    const int64_t nchunk_blocks = a.max_segs * a.H;
+    const int64_t npass_blocks = (int64_t)a.num_seqs * a.H * nvt;
+    if (nchunk_blocks > 0)
+        hipLaunchKernelGGL((kda_cb_factors<K>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
+                           a.beta, io_bf, a.gate_sigmoid, w.seq_tok, w.seg_off, a.num_seqs, a.H, w.fac);
+    if (npass_blocks > 0) {
+        hipLaunchKernelGGL((kda_cb_fwd<K>), dim3((unsigned)npass_blocks), dim3(CNT), 0, st, vs, v_bf,
+                           (const float *)w.fac, a.S0, w.seq_tok, w.seg_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout,
+                           a.o_gate, io_bf, w.doe, a.d_o_gate);
+        // with an output gate the reverse reads do * sigmoid(z), formed by the forward pass
+        hipLaunchKernelGGL((kda_cb_rev<K>), dim3((unsigned)npass_blocks), dim3(CNT), 0, st,
+                           og ? (const void *)w.doe : a.dout, og ? false : io_bf, (const float *)w.fac, a.dS_final,
+                           w.seq_tok, w.seg_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
+    }
+    if (nchunk_blocks > 0)
+        hipLaunchKernelGGL((kda_cb_grad<K, V>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
+                           a.beta, io_bf, a.gate_sigmoid, og ? (const void *)w.doe : a.dout, og ? false : io_bf,
+                           (const float *)w.fac, (const float *)w.Sb, (const float *)w.dSb, (const float *)w.Xb,
+                           (const float *)w.Wb, (const float *)w.dWb, w.seq_tok, w.seg_off, a.num_seqs, a.H, dq_dst,
+                           dk_dst, dv_dst, a.dg, a.dbeta);
 }
 
 template <bool BF, int D>
@@ -793,7 +1176,7 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, n_tok,
                        w.seq_tok, w.seg_off);
     if (!norm && !conv) {
-        bwd_core<BF, K, false, false>(a, w, a.q, a.k, a.v, a.dv, a.dq, a.dk, st);
+        bwd_core<K, V>(a, w, a.q, a.k, a.io_bf16, a.v, a.io_bf16, a.dv, a.dq, a.dk, st);
         return hipGetLastError();
     }
     // prologue, forward: convolution into xq, xk, xv; normalisation of q and k (in place, or from the input)
@@ -822,8 +1205,8 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
         }
     }
     // the recurrence's reverse on the prologue's outputs
-    if (conv) bwd_core<BF, K, true, true>(a, w, w.xq, w.xk, w.xv, w.gv, w.gq, w.gk, st);
-    else bwd_core<BF, K, true, false>(a, w, w.xq, w.xk, a.v, a.dv, w.gq, w.gk, st);
+    if (conv) bwd_core<K, V>(a, w, w.xq, w.xk, false, w.xv, false, w.gv, w.gq, w.gk, st);
+    else bwd_core<K, V>(a, w, w.xq, w.xk, false, a.v, a.io_bf16, a.dv, w.gq, w.gk, st);
     // prologue, reverse: normalisation (into gq, gk when a convolution follows), then convolution
     if (norm && n_rows > 0) {
         hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xq, w.rq, w.gq,
@@ -860,7 +1243,7 @@ size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, i
     return total;
 }
 
-int32_t backward_segment_tokens() { return BL; }
+int32_t backward_segment_tokens() { return CB; }
 
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     switch (a.K) {

@@ -348,7 +348,7 @@ CW, DCW = A + 9 * 65536, A + 10 * 65536  # conv taps and their gradient (fake ad
     (dict(og=A + 7 * 65536 + 8192, dog=A), INVALID),      # dL/dz aliases q
     (dict(og=A + 7 * 65536 + 8200), INVALID),             # o_gate misaligned
     (dict(H=0), INVALID),
-    (dict(T=1 << 28, H=96), INVALID),    # the tile-sum grid would not be launchable
+    (dict(T=1 << 28, H=128), INVALID),   # the per-(chunk, head) grids would not be launchable
     (dict(K=48), UNSUP),
     (dict(V=256), UNSUP),
     (dict(wsb=100), WS_SMALL),
@@ -370,13 +370,15 @@ def test_chunk_bwd_rejects(kw, expect):
 def test_bwd_workspace_bytes():
     lib = _lib.load()
     ws = lib.kda_chunk_bwd_workspace_bytes
-    # per sequence and head: a K*V fp32 state every 8 tokens; per token and head: V/16 partial rows of 3K+1 floats
-    # at a pitch of 3K+4
+    # per (16-token chunk, head): a factor block (4 x 16 x K + 4 x 16 x 16 + K floats, rounded up to 64 floats),
+    # the state entering and the state gradient leaving the chunk (K x V each) and X, W, dW (16 x V each); per
+    # token and head: do * sigmoid(z) (V floats, used with an output gate)
     B, T, H, K, V = 2, 64, 3, 32, 64
-    states = B * (T // 8) * H * K * V * 4
-    parts = (V // 16) * B * T * H * (3 * K + 4) * 4
-    assert states + parts <= ws(B, T, H, K, V, B, 0, 0) <= states + parts + 3 * 256
-    assert ws(1, 4096, 96, 128, 128, 16, 0, 0) > ws(1, 4096, 96, 128, 128, 1, 0, 0)  # one more segment per sequence
+    nc = B * (T // 16)
+    fac = -(-(4 * 16 * K + 4 * 16 * 16 + K) // 64) * 64
+    need = nc * H * (fac + 2 * K * V + 3 * 16 * V) * 4 + B * T * H * V * 4
+    assert need <= ws(B, T, H, K, V, B, 0, 0) <= need + 10 * 256
+    assert ws(1, 4096, 96, 128, 128, 16, 0, 0) > ws(1, 4096, 96, 128, 128, 1, 0, 0)  # one more chunk per sequence
     assert ws(1, 64, 2, 48, 32, 1, 0, 0) == 0 and ws(2, 64, 2, 32, 32, 1, 0, 0) == 0
     assert ws(B, T, H, K, V, B, 2, 0) == 0 and ws(B, T, H, K, V, B, 0, 3) == 0
 
