@@ -22,7 +22,6 @@ namespace kda {
 namespace {
 
 constexpr int CB = 16;    // tokens per chunk
-constexpr int CVT = 32;   // value columns per workgroup of the sequential passes
 constexpr int CNT = 256;  // threads per workgroup
 
 // ------------------------------------------------------------------ sequence table
@@ -119,13 +118,29 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // Each column of S and of dS evolves on its own (decay scales rows), so the two sequential passes split V
 // into tiles; their thread (row group, column) holds K/8 rows of one column and sums over key rows go
 // through LDS. All arithmetic is fp32, deterministic (fixed summation orders, no atomics).
-// Factor block of one (chunk, head), fp32: Q~, K~, Kc, Wk [CB][K] row-major; T, P, M, Ab [CB][CB]; Gc [K].
-constexpr int64_t fac_floats(int K) { return ((4 * CB * K + 4 * CB * CB + K) + 63) / 64 * 64; }
+// Factor block of one (chunk, head), fp32. The sequential passes read their matrix-core operands in
+// fragment order: for v_mfma_f32_16x16x4f32, lane l = m + 16 q supplies row m and k slot q of A, row slot q and
+// column m of B, and receives rows 4 q + i (i = 0..3) of column m of D. A state tile (16 key rows) is then B
+// for four products with the k slot q of product i standing for row 4 q + i; the A operand of product i holds
+// the matching columns. Arrays "o1" of a [CB][K] matrix X are [K/16][64][4]: lane l of group r holds
+// X[m][16 r + 4 q + i] (i = 0..3), A for X times a state; "o2" arrays hold X^T the same way, lane l of group r
+// holding X[4 q + i][16 r + m], A for X^T times a [CB][16] tile in accumulator layout; "t" arrays of a
+// [CB][CB] matrix Y are [64][4] with lane l holding Y[m][4 q + i], and "tT" arrays hold Y^T
+// (Y[4 q + i][m]). The row-major T, M, P, Ab and Gc serve the local-gradient kernel.
 template <int K> struct FacL {
-    static constexpr int QG = 0, KG = CB * K, KC = 2 * CB * K, WK = 3 * CB * K;
-    static constexpr int TT = 4 * CB * K, PP = TT + CB * CB, MM = PP + CB * CB, AB = MM + CB * CB;
+    static constexpr int NKG1 = 0;                   // -K~, o1: X = V - K~ S
+    static constexpr int QG1 = CB * K;               // Q~, o1: O = Q~ S + P W
+    static constexpr int KC1 = 2 * CB * K;           // Kc, o1: dW = P^T dO + Kc dS'
+    static constexpr int KC2 = 3 * CB * K;           // Kc, o2: S' = diag(Gc) S + Kc^T W
+    static constexpr int QG2 = 4 * CB * K;           // Q~, o2: dS = diag(Gc) dS' + Q~^T dO - Wk^T dW
+    static constexpr int NWK2 = 5 * CB * K;          // -Wk, o2
+    static constexpr int T1 = 6 * CB * K;            // T, t: W = T X
+    static constexpr int P1 = T1 + CB * CB;          // P, t
+    static constexpr int PT1 = P1 + CB * CB;         // P, tT: P^T dO
+    static constexpr int TT = PT1 + CB * CB, PP = TT + CB * CB, MM = PP + CB * CB, AB = MM + CB * CB;
     static constexpr int GC = AB + CB * CB;
 };
+constexpr int64_t fac_floats(int K) { return ((6 * CB * K + 7 * CB * CB + K) + 63) / 64 * 64; }
 
 // element i of an array of bf16 (bf) or fp32 values
 __device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
@@ -167,8 +182,8 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
     using L = FacL<K>;
     constexpr int KP = CB + 1;
     __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
-    __shared__ float tKG[K * KP], tKI[K * KP], tQG[K * KP];
-    __shared__ float sA[CB * CB], sT[CB * CB], sb[CB];
+    __shared__ float tKG[K * KP], tKI[K * KP], tQG[K * KP], tKc[K * KP], tWk[K * KP];
+    __shared__ float sA[CB * CB], sT[CB * CB], sP[CB * CB], sb[CB];
     const int tid = threadIdx.x;
     const int64_t c = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
     }
     if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * H + h, io_bf) : 0.f;
     __syncthreads();
-    // prefix b, suffix s (each summed from its own terms), the scaled rows and Gc
+    // prefix b, suffix s (each summed from its own terms), the scaled rows (key-major) and Gc
     for (int e = tid; e < CB * K; e += CNT) {
         const int t = e / K, ch = e % K;
         float b = 0.f, s = 0.f;
@@ -195,14 +210,11 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
             if (u <= t) b += x;
             else s += x;
         }
-        const float eb = exp_e(b), kv = sk[e], qv = sq[e];
-        const float kg = kv * eb, kh = kv * exp_e(-b), qg = qv * eb;
-        tKG[ch * KP + t] = kg;
-        tKI[ch * KP + t] = kh;
-        tQG[ch * KP + t] = qg;
-        blk[L::QG + e] = qg;
-        blk[L::KG + e] = kg;
-        blk[L::KC + e] = kv * exp_e(s);
+        const float eb = exp_e(b), kv = sk[e];
+        tKG[ch * KP + t] = kv * eb;
+        tKI[ch * KP + t] = kv * exp_e(-b);
+        tQG[ch * KP + t] = sq[e] * eb;
+        tKc[ch * KP + t] = kv * exp_e(s);
         if (t == CB - 1) blk[L::GC + ch] = eb;
     }
     __syncthreads();
@@ -220,6 +232,7 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
         blk[L::AB + tid] = a;
         blk[L::PP + tid] = p;
         sA[tid] = sb[i] * a;
+        sP[tid] = p;
     }
     __syncthreads();
     // M = (I + A)^{-1} by forward substitution, one column per thread; T = M diag(beta)
@@ -242,13 +255,32 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
         }
     }
     __syncthreads();
-    // Wk = T K~
+    // Wk = T K~ (key-major in LDS)
     for (int e = tid; e < CB * K; e += CNT) {
-        const int t = e / K, ch = e % K;
+        const int t = e % CB, ch = e / CB;
         float w = 0.f;
 #pragma unroll
         for (int j = 0; j < CB; ++j) w += sT[t * CB + j] * tKG[ch * KP + j];
-        blk[L::WK + e] = w;
+        tWk[ch * KP + t] = w;
+    }
+    __syncthreads();
+    // fragment orders: element e = (r * 64 + l) * 4 + i, lane l = m + 16 qq
+    for (int e = tid; e < CB * K; e += CNT) {
+        const int i = e & 3, l = (e >> 2) & 63, r = e >> 8, m = l & 15, qq = l >> 4;
+        const int k1 = 16 * r + 4 * qq + i, t1 = m;   // o1: X[m][16 r + 4 q + i]
+        const int k2 = 16 * r + m, t2 = 4 * qq + i;   // o2: X[4 q + i][16 r + m]
+        blk[L::NKG1 + e] = -tKG[k1 * KP + t1];
+        blk[L::QG1 + e] = tQG[k1 * KP + t1];
+        blk[L::KC1 + e] = tKc[k1 * KP + t1];
+        blk[L::KC2 + e] = tKc[k2 * KP + t2];
+        blk[L::QG2 + e] = tQG[k2 * KP + t2];
+        blk[L::NWK2 + e] = -tWk[k2 * KP + t2];
+    }
+    {
+        const int e = tid, i = e & 3, l = e >> 2, m = l & 15, qq = l >> 4;  // CB * CB == CNT elements
+        blk[L::T1 + e] = sT[m * CB + 4 * qq + i];
+        blk[L::P1 + e] = sP[m * CB + 4 * qq + i];
+        blk[L::PT1 + e] = sP[(4 * qq + i) * CB + m];
     }
 }
 
@@ -256,53 +288,85 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
 // its global stores (states, X, W) stay in flight (a __syncthreads would wait for those as well).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Dot product of a thread's run of RPT consecutive entries of an LDS row (read as float4) with S, and the
-// update S += w * run.
-template <int RPT>
-__device__ __forceinline__ float dot_run(const float *lds_row, const float (&S)[RPT]) {
-    const float4 *p = reinterpret_cast<const float4 *>(lds_row);
-    float a = 0.f;
-#pragma unroll
-    for (int m = 0; m < RPT / 4; ++m) {
-        const float4 x = p[m];
-        a += x.x * S[4 * m] + x.y * S[4 * m + 1] + x.z * S[4 * m + 2] + x.w * S[4 * m + 3];
-    }
-    return a;
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-template <int RPT>
-__device__ __forceinline__ void axpy_run(float (&S)[RPT], const float *lds_row, float w) {
-    const float4 *p = reinterpret_cast<const float4 *>(lds_row);
+// D += A B over four k slots: lane's A values a.{x,y,z,w} for products 0..3, B = the four accumulator
+// registers of a [16][16] tile (k slot q of product i = row 4 q + i)
+__device__ __forceinline__ f32x4 mfma_x4(f32x4 d, const float4 &a, const f32x4 &b) {
+    d = mfma4(a.x, b[0], d);
+    d = mfma4(a.y, b[1], d);
+    d = mfma4(a.z, b[2], d);
+    return mfma4(a.w, b[3], d);
+}
+template <int N>
+__device__ __forceinline__ void fence_tiles(f32x4 (&x)[N]) {
+    if constexpr (N == 2 || N == 4 || N == 8) {
+        mfma_fence_all(x);
+    } else {
 #pragma unroll
-    for (int m = 0; m < RPT / 4; ++m) {
-        const float4 x = p[m];
-        S[4 * m] += x.x * w;
-        S[4 * m + 1] += x.y * w;
-        S[4 * m + 2] += x.z * w;
-        S[4 * m + 3] += x.w * w;
+        for (int i = 0; i < N; ++i) mfma_fence(x[i]);
     }
 }
 
-// ---- forward states: one workgroup per (sequence, head, tile of CVT columns). Thread (rg, col) holds rows
-// rg*RPT .. +RPT-1 of column col of S. The next chunk's factors and v tile are fetched into registers while
-// the current chunk is processed.
-template <int K>
-__global__ __launch_bounds__(CNT) void kda_cb_fwd(const void *__restrict__ v, bool v_bf, const float *__restrict__ fac,
-                                                  const float *__restrict__ S0, const int64_t *__restrict__ seq_tok,
-                                                  const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
-                                                  int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
-                                                  float *__restrict__ Wbuf, const void *__restrict__ dout,
-                                                  const void *__restrict__ zg, bool io_bf, float *__restrict__ doe,
-                                                  float *__restrict__ dz) {
+// One element of a bf16 (BF) or fp32 array as its raw bits, and those bits as a float. Prefetches keep the raw
+// word so that nothing waits for the load before the value is used.
+template <bool BF>
+__device__ __forceinline__ uint32_t ld_raw(const void *p, int64_t i) {
+    if constexpr (BF) return reinterpret_cast<const uint16_t *>(p)[i];
+    else return reinterpret_cast<const uint32_t *>(p)[i];
+}
+template <bool BF>
+__device__ __forceinline__ float raw_f(uint32_t r) {
+    return BF ? __uint_as_float(r << 16) : __uint_as_float(r);
+}
+
+// Cooperative copy of n floats (a multiple of 4) global -> registers (float4 per thread and round) and
+// registers -> LDS, for NT threads.
+template <int NFL, int NT>
+struct Stage {
+    static constexpr int R = (NFL / 4 + NT - 1) / NT;
+    f32x4 v[R];  // (a vector type: copies of the float4 struct go through private memory)
+    // (the index is clamped rather than the value selected: a select on a loaded value would make the
+    // compiler wait for the load, and with it for every memory operation issued before, right here)
+    __device__ __forceinline__ void load(const float *src, int tid) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int e = tid + NT * j;
+            v[j] = reinterpret_cast<const f32x4 *>(src)[e < NFL / 4 ? e : NFL / 4 - 1];
+        }
+    }
+    __device__ __forceinline__ void store(float *dst, int tid) const {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int e = tid + NT * j;
+            if (e < NFL / 4) reinterpret_cast<f32x4 *>(dst)[e] = v[j];
+        }
+    }
+};
+
+// ---- forward states: one workgroup of NW wavefronts per (sequence, head, 16 NW columns); wavefront w owns
+// the 16-column tile 16 w and keeps its K x 16 slice of S as K/16 accumulator tiles. Operands are fetched two
+// chunks ahead into one of two register sets (a fetch takes several microseconds; one chunk's work does not
+// cover it). OG: with an output gate.
+template <int K, int NW, bool OG, bool VBF, bool IOBF>
+__global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v,
+                                                      const float *__restrict__ fac, const float *__restrict__ S0,
+                                                      const int64_t *__restrict__ seq_tok,
+                                                      const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                      int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
+                                                      float *__restrict__ Wbuf, const void *__restrict__ dout,
+                                                      const void *__restrict__ zg, float *__restrict__ doe,
+                                                      float *__restrict__ dz) {
     using L = FacL<K>;
-    constexpr int RG = CNT / CVT, RPT = K / RG, NE = CB * K / CNT, NV = CB * CVT / CNT;
-    static_assert(CB * CB == CNT && RPT % 4 == 0, "layout");
-    __shared__ __align__(16) float sKG[CB * K];
-    __shared__ __align__(16) float sKc[CB * K];
-    __shared__ __align__(16) float sQG[CB * K];
-    __shared__ float sT[CB * CB], sP[CB * CB], sGC[K];
-    __shared__ float sv[CB * CVT], sX[CB * CVT], sW[CB * CVT], red[RG * CB * CVT], red2[RG * CB * CVT];
-    const bool og = zg != nullptr;
-    const int tid = threadIdx.x, col = tid % CVT, rg = tid / CVT;
+    constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
+    __shared__ __align__(16) float fKG[FK];
+    __shared__ __align__(16) float fKc[FK];
+    __shared__ __align__(16) float fQG[OG ? FK : 4];
+    __shared__ __align__(16) float fT[CB * CB];
+    __shared__ __align__(16) float fP[OG ? CB * CB : 4];
+    __shared__ __align__(16) float sGC[K];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
     int64_t bid = blockIdx.x;
     const int vt = (int)(bid % nvt);
     bid /= nvt;
@@ -310,133 +374,147 @@ __global__ __launch_bounds__(CNT) void kda_cb_fwd(const void *__restrict__ v, bo
     const int64_t n = bid / H;
     const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
-    const int vc = vt * CVT + col;
     const int64_t sH = H, sV = V;
-    float S[RPT];
+    const int col = vt * 16 * NW + 16 * w + m;
+    f32x4 S[KT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) S[i] = S0 ? S0[((n * sH + h) * K + rg * RPT + i) * sV + vc] : 0.f;
-    float pKG[NE], pKc[NE], pQG[NE], pT = 0.f, pP = 0.f, pGC = 0.f, pv[NV], pdo[NV], pz[NV];
-    auto fetch = [&](int ci) {
+    for (int r = 0; r < KT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[r][i] = S0 ? S0[((n * sH + h) * K + 16 * r + 4 * qq + i) * sV + col] : 0.f;
+    struct Set {
+        Stage<FK, NT> KG, Kc;
+        Stage<OG ? FK : 4, NT> QG;
+        Stage<CB * CB, NT> T;
+        Stage<OG ? CB * CB : 4, NT> P;
+        Stage<K, NT> GC;
+        uint32_t v[4], d[OG ? 4 : 1], z[OG ? 4 : 1];  // raw words of rows 4 qq + i (clamped to the last valid row)
+    };
+    Set sa, sb;
+    auto fetch = [&](Set &st, int ci) {
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         const float *blk = fac + (c * sH + h) * fac_floats(K);
+        st.KG.load(blk + L::NKG1, tid);
+        st.Kc.load(blk + L::KC2, tid);
+        if constexpr (OG) st.QG.load(blk + L::QG1, tid);
+        st.T.load(blk + L::T1, tid);
+        if constexpr (OG) st.P.load(blk + L::P1, tid);
+        st.GC.load(blk + L::GC, tid);
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            pKG[m] = blk[L::KG + tid + CNT * m];
-            pKc[m] = blk[L::KC + tid + CNT * m];
-            pQG[m] = og ? blk[L::QG + tid + CNT * m] : 0.f;
-        }
-        pT = blk[L::TT + tid];
-        pP = og ? blk[L::PP + tid] : 0.f;
-        pGC = tid < K ? blk[L::GC + tid] : 0.f;
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
-            const bool ok = t < nval;
-            const int64_t idx = ((tok0 + t) * sH + h) * sV + vt * CVT + cc;
-            pv[m] = ok ? ld_as(v, idx, v_bf) : 0.f;
-            pdo[m] = (ok && og) ? ld_as(dout, idx, io_bf) : 0.f;
-            pz[m] = (ok && og) ? ld_as(zg, idx, io_bf) : 0.f;
+        for (int i = 0; i < 4; ++i) {  // this lane's rows 4 qq + i of the v (do, z) tile
+            const int t = 4 * qq + i < nval ? 4 * qq + i : nval - 1;
+            const int64_t idx = ((tok0 + t) * sH + h) * sV + col;
+            st.v[i] = ld_raw<VBF>(v, idx);
+            if constexpr (OG) {
+                st.d[i] = ld_raw<IOBF>(dout, idx);
+                st.z[i] = ld_raw<IOBF>(zg, idx);
+            }
         }
     };
-    if (nch > 0) fetch(0);
-    for (int ci = 0; ci < nch; ++ci) {
+    auto step = [&](Set &st, int ci) {
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         lds_barrier();  // the previous chunk's LDS reads are done
+        st.KG.store(fKG, tid);
+        st.Kc.store(fKc, tid);
+        if constexpr (OG) st.QG.store(fQG, tid);
+        st.T.store(fT, tid);
+        if constexpr (OG) st.P.store(fP, tid);
+        st.GC.store(sGC, tid);
+        f32x4 X0, X1 = zero4();
+        float cd[4], cz[4];
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            sKG[tid + CNT * m] = pKG[m];
-            sKc[tid + CNT * m] = pKc[m];
-            if (og) sQG[tid + CNT * m] = pQG[m];
-        }
-        sT[tid] = pT;
-        if (og) sP[tid] = pP;
-        if (tid < K) sGC[tid] = pGC;
-        float cdo[NV], cz[NV];
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            sv[tid + CNT * m] = pv[m];
-            cdo[m] = pdo[m];
-            cz[m] = pz[m];
-        }
-        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) sp[(rg * RPT + i) * sV + vc] = S[i];
-        lds_barrier();
-        if (ci + 1 < nch) fetch(ci + 1);
-        // partial sums over this thread's rows: (K~ S)[t][col], (Q~ S)[t][col]
-#pragma unroll
-        for (int t = 0; t < CB; ++t) {
-            red[(rg * CB + t) * CVT + col] = dot_run<RPT>(sKG + t * K + rg * RPT, S);
-            if (og) red2[(rg * CB + t) * CVT + col] = dot_run<RPT>(sQG + t * K + rg * RPT, S);
-        }
-        lds_barrier();
-        float oi[NV];
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
-            float s = 0.f, o = 0.f;
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                s += red[(r * CB + t) * CVT + cc];
-                if (og) o += red2[(r * CB + t) * CVT + cc];
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = 4 * qq + i < nval;
+            X0[i] = ok ? raw_f<VBF>(st.v[i]) : 0.f;
+            if constexpr (OG) {
+                cd[i] = raw_f<IOBF>(st.d[i]);
+                cz[i] = raw_f<IOBF>(st.z[i]);
             }
-            sX[e] = sv[e] - s;
-            oi[m] = o;
         }
+        // the state entering the chunk, in fragment order ([V/16][K/16][4][64] per chunk and head): whole
+        // 256-byte runs per store
+        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + lane;
+#pragma unroll
+        for (int r = 0; r < KT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp[(r * 4 + i) * 64] = S[r][i];
         lds_barrier();
+        if (ci + 2 < nch) fetch(st, ci + 2);
+        // X = V - K~ S (two independent product chains)
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
-            float w = 0.f;
-#pragma unroll
-            for (int j = 0; j < CB; ++j) w += sT[t * CB + j] * sX[j * CVT + cc];
-            sW[e] = w;
-            const int64_t xo = ((c * sH + h) * CB + t) * sV + vt * CVT + cc;
-            Xbuf[xo] = sX[e];
-            Wbuf[xo] = w;
+        for (int r = 0; r < KT; r += 2) {
+            X0 = mfma_x4(X0, reinterpret_cast<const float4 *>(fKG)[r * 64 + lane], S[r]);
+            X1 = mfma_x4(X1, reinterpret_cast<const float4 *>(fKG)[(r + 1) * 64 + lane], S[r + 1]);
         }
-        lds_barrier();
-        if (og) {  // core output O = Q~ S + P W; do * sigmoid(z) for the reverse, and dL/dz
+        mfma_fence(X0, X1);
+        const f32x4 X = X0 + X1;
+        // W = T X
+        f32x4 W = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fT)[lane], X);
+        mfma_fence(W);
+        const int64_t xo = ((c * sH + h) * CB + 4 * qq) * sV + col;
 #pragma unroll
-            for (int m = 0; m < NV; ++m) {
-                const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
+        for (int i = 0; i < 4; ++i) {
+            Xbuf[xo + i * sV] = X[i];
+            Wbuf[xo + i * sV] = W[i];
+        }
+        if constexpr (OG) {  // core output O = Q~ S + P W; do * sigmoid(z) for the reverse, and dL/dz
+            f32x4 O0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fP)[lane], W), O1 = zero4();
+#pragma unroll
+            for (int r = 0; r < KT; r += 2) {
+                O0 = mfma_x4(O0, reinterpret_cast<const float4 *>(fQG)[r * 64 + lane], S[r]);
+                O1 = mfma_x4(O1, reinterpret_cast<const float4 *>(fQG)[(r + 1) * 64 + lane], S[r + 1]);
+            }
+            mfma_fence(O0, O1);
+            const f32x4 O = O0 + O1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * qq + i;
                 if (t < nval) {
-                    float o = oi[m];
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) o += sP[t * CB + j] * sW[j * CVT + cc];
-                    const int64_t idx = ((tok0 + t) * sH + h) * sV + vt * CVT + cc;
-                    const float sz = sigmoid_f(cz[m]);
-                    doe[idx] = cdo[m] * sz;
-                    dz[idx] = cdo[m] * o * sz * (1.f - sz);
+                    const int64_t idx = ((tok0 + t) * sH + h) * sV + col;
+                    const float sz = sigmoid_f(cz[i]);
+                    doe[idx] = cd[i] * sz;
+                    dz[idx] = cd[i] * O[i] * sz * (1.f - sz);
                 }
             }
         }
         // S' = diag(Gc) S + Kc^T W
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) S[i] *= sGC[rg * RPT + i];
-#pragma unroll
-        for (int t = 0; t < CB; ++t) axpy_run<RPT>(S, sKc + t * K + rg * RPT, sW[t * CVT + col]);
+        for (int r = 0; r < KT; ++r) {
+            const float4 gc = reinterpret_cast<const float4 *>(sGC)[4 * r + qq];  // rows 16 r + 4 qq + i
+            S[r][0] *= gc.x;
+            S[r][1] *= gc.y;
+            S[r][2] *= gc.z;
+            S[r][3] *= gc.w;
+            S[r] = mfma_x4(S[r], reinterpret_cast<const float4 *>(fKc)[r * 64 + lane], W);
+        }
+        fence_tiles(S);
+    };
+    if (nch > 0) fetch(sa, 0);
+    if (nch > 1) fetch(sb, 1);
+    for (int ci = 0; ci < nch; ci += 2) {
+        step(sa, ci);
+        if (ci + 1 < nch) step(sb, ci + 1);
     }
 }
 
-// ---- reverse: one workgroup per (sequence, head, tile of CVT columns), chunks last to first.
-template <int K>
-__global__ __launch_bounds__(CNT) void kda_cb_rev(const void *__restrict__ dout, bool do_bf,
-                                                  const float *__restrict__ fac, const float *__restrict__ dSf,
-                                                  const int64_t *__restrict__ seq_tok,
-                                                  const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
-                                                  int32_t nvt, float *__restrict__ dSbuf, float *__restrict__ dWbuf,
-                                                  float *__restrict__ dS0) {
+// ---- reverse: as the forward pass, chunks last to first, with dS' (the state gradient leaving the chunk) in
+// the accumulator tiles.
+template <int K, int NW, bool DBF>
+__global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ dout,
+                                                      const float *__restrict__ fac, const float *__restrict__ dSf,
+                                                      const int64_t *__restrict__ seq_tok,
+                                                      const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                      int32_t nvt, float *__restrict__ dSbuf,
+                                                      float *__restrict__ dWbuf, float *__restrict__ dS0) {
     using L = FacL<K>;
-    constexpr int RG = CNT / CVT, RPT = K / RG, NE = CB * K / CNT, NV = CB * CVT / CNT;
-    static_assert(CB * CB == CNT && RPT % 4 == 0, "layout");
-    __shared__ __align__(16) float sKc[CB * K];
-    __shared__ __align__(16) float sQG[CB * K];
-    __shared__ __align__(16) float sWk[CB * K];
-    __shared__ float sP[CB * CB], sGC[K], sdo[CB * CVT], sdW[CB * CVT], red[RG * CB * CVT];
-    const int tid = threadIdx.x, col = tid % CVT, rg = tid / CVT;
+    constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
+    __shared__ __align__(16) float fKc[FK];
+    __shared__ __align__(16) float fQG[FK];
+    __shared__ __align__(16) float fWk[FK];
+    __shared__ __align__(16) float fPT[CB * CB];
+    __shared__ __align__(16) float sGC[K];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
     int64_t bid = blockIdx.x;
     const int vt = (int)(bid % nvt);
     bid /= nvt;
@@ -444,86 +522,91 @@ __global__ __launch_bounds__(CNT) void kda_cb_rev(const void *__restrict__ dout,
     const int64_t n = bid / H;
     const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
-    const int vc = vt * CVT + col;
     const int64_t sH = H, sV = V;
-    float dS[RPT];
+    const int col = vt * 16 * NW + 16 * w + m;
+    f32x4 dS[KT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) dS[i] = dSf ? dSf[((n * sH + h) * K + rg * RPT + i) * sV + vc] : 0.f;
-    float pKc[NE], pQG[NE], pWk[NE], pP = 0.f, pGC = 0.f, pdo[NV];
-    auto fetch = [&](int ci) {
+    for (int r = 0; r < KT; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[r][i] = dSf ? dSf[((n * sH + h) * K + 16 * r + 4 * qq + i) * sV + col] : 0.f;
+    struct Set {
+        Stage<FK, NT> Kc, QG, Wk;
+        Stage<CB * CB, NT> PT;
+        Stage<K, NT> GC;
+        uint32_t d[4];  // raw words of rows 4 qq + i of dO (clamped to the chunk's last valid row)
+    };
+    Set sa, sb;
+    auto fetch = [&](Set &st, int ci) {
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         const float *blk = fac + (c * sH + h) * fac_floats(K);
+        st.Kc.load(blk + L::KC1, tid);
+        st.QG.load(blk + L::QG2, tid);
+        st.Wk.load(blk + L::NWK2, tid);
+        st.PT.load(blk + L::PT1, tid);
+        st.GC.load(blk + L::GC, tid);
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            pKc[m] = blk[L::KC + tid + CNT * m];
-            pQG[m] = blk[L::QG + tid + CNT * m];
-            pWk[m] = blk[L::WK + tid + CNT * m];
-        }
-        pP = blk[L::PP + tid];
-        pGC = tid < K ? blk[L::GC + tid] : 0.f;
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
-            pdo[m] = t < nval ? ld_as(dout, ((tok0 + t) * sH + h) * sV + vt * CVT + cc, do_bf) : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * qq + i < nval ? 4 * qq + i : nval - 1;
+            st.d[i] = ld_raw<DBF>(dout, ((tok0 + t) * sH + h) * sV + col);
         }
     };
-    if (nch > 0) fetch(nch - 1);
-    for (int ci = nch - 1; ci >= 0; --ci) {
-        const int64_t c = c0 + ci;
+    auto step = [&](Set &st, int ci) {
+        const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
+        const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         lds_barrier();
+        st.Kc.store(fKc, tid);
+        st.QG.store(fQG, tid);
+        st.Wk.store(fWk, tid);
+        st.PT.store(fPT, tid);
+        st.GC.store(sGC, tid);
+        f32x4 dO;
 #pragma unroll
-        for (int m = 0; m < NE; ++m) {
-            sKc[tid + CNT * m] = pKc[m];
-            sQG[tid + CNT * m] = pQG[m];
-            sWk[tid + CNT * m] = pWk[m];
+        for (int i = 0; i < 4; ++i) dO[i] = 4 * qq + i < nval ? raw_f<DBF>(st.d[i]) : 0.f;
+        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + lane;
+#pragma unroll
+        for (int r = 0; r < KT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dp[(r * 4 + i) * 64] = dS[r][i];
+        lds_barrier();
+        if (ci >= 2) fetch(st, ci - 2);
+        // dW = P^T dO + Kc dS' (two independent product chains)
+        f32x4 dW0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fPT)[lane], dO), dW1 = zero4();
+#pragma unroll
+        for (int r = 0; r < KT; r += 2) {
+            dW0 = mfma_x4(dW0, reinterpret_cast<const float4 *>(fKc)[r * 64 + lane], dS[r]);
+            dW1 = mfma_x4(dW1, reinterpret_cast<const float4 *>(fKc)[(r + 1) * 64 + lane], dS[r + 1]);
         }
-        sP[tid] = pP;
-        if (tid < K) sGC[tid] = pGC;
+        mfma_fence(dW0, dW1);
+        const f32x4 dW = dW0 + dW1;
+        const int64_t wo = ((c * sH + h) * CB + 4 * qq) * sV + col;
 #pragma unroll
-        for (int m = 0; m < NV; ++m) sdo[tid + CNT * m] = pdo[m];
-        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) dp[(rg * RPT + i) * sV + vc] = dS[i];
-        lds_barrier();
-        if (ci > 0) fetch(ci - 1);
-#pragma unroll
-        for (int t = 0; t < CB; ++t) red[(rg * CB + t) * CVT + col] = dot_run<RPT>(sKc + t * K + rg * RPT, dS);
-        lds_barrier();
-#pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int e = tid + CNT * m, t = e / CVT, cc = e % CVT;
-            float s = 0.f;
-#pragma unroll
-            for (int r = 0; r < RG; ++r) s += red[(r * CB + t) * CVT + cc];
-#pragma unroll
-            for (int j = 0; j < CB; ++j) s += sP[j * CB + t] * sdo[j * CVT + cc];
-            sdW[e] = s;
-            dWbuf[((c * sH + h) * CB + t) * sV + vt * CVT + cc] = s;
-        }
-        lds_barrier();
+        for (int i = 0; i < 4; ++i) dWbuf[wo + i * sV] = dW[i];
         // dS = diag(Gc) dS' + Q~^T dO - Wk^T dW
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dS[i] *= sGC[rg * RPT + i];
-#pragma unroll
-        for (int t = 0; t < CB; ++t) {
-            axpy_run<RPT>(dS, sQG + t * K + rg * RPT, sdo[t * CVT + col]);
-            axpy_run<RPT>(dS, sWk + t * K + rg * RPT, -sdW[t * CVT + col]);
+        for (int r = 0; r < KT; ++r) {
+            const float4 gc = reinterpret_cast<const float4 *>(sGC)[4 * r + qq];
+            dS[r][0] *= gc.x;
+            dS[r][1] *= gc.y;
+            dS[r][2] *= gc.z;
+            dS[r][3] *= gc.w;
+            dS[r] = mfma_x4(dS[r], reinterpret_cast<const float4 *>(fQG)[r * 64 + lane], dO);
+            dS[r] = mfma_x4(dS[r], reinterpret_cast<const float4 *>(fWk)[r * 64 + lane], dW);
         }
+        fence_tiles(dS);
+    };
+    if (nch > 0) fetch(sa, nch - 1);
+    if (nch > 1) fetch(sb, nch - 2);
+    for (int ci = nch - 1; ci >= 0; ci -= 2) {
+        step(sa, ci);
+        if (ci >= 1) step(sb, ci - 1);
     }
     if (dS0) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dS0[((n * sH + h) * K + rg * RPT + i) * sV + vc] = dS[i];
+        for (int r = 0; r < KT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dS0[((n * sH + h) * K + 16 * r + 4 * qq + i) * sV + col] = dS[r][i];
     }
-}
-
-// sum over the TPR consecutive lanes that share a key row (TPR = 2, 4 or 8)
-template <int TPR>
-__device__ __forceinline__ float sum_lanes(float x) {
-    x += dpp_mov<0xB1>(x);                        // quad_perm [1,0,3,2]
-    if constexpr (TPR >= 4) x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
-    if constexpr (TPR >= 8) x += __shfl_xor(x, 4);
-    return x;
 }
 
 // ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) floats; the
@@ -539,8 +622,8 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta) {
     using L = FacL<K>;
-    constexpr int VM = K > V ? K : V;
-    constexpr int TPR = CNT / K, VPT = V / TPR;  // threads per key row; value columns per thread
+    constexpr int VM = (K > V ? K : V) + 4;  // row pitch: float4 reads of 16 rows fall in distinct banks
+    constexpr int KT = K / 16, NZ = (KT + 3) / 4;  // 16-row tiles of K; tiles per wavefront in phase f
     constexpr int CPT = K / 16;                  // channels per thread in the per-(token, channel) phase
     __shared__ float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
     __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
@@ -553,6 +636,7 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
     const int64_t sH = H, sV = V, ch0 = c * sH + h;
     const float *blk = fac + ch0 * fac_floats(K);
+    const int lane = tid & 63, wv = tid >> 6, m = lane & 15, qq = lane >> 4;
     // ---- a. loads
     for (int e = tid; e < CB * V; e += CNT) {
         const int t = e / V, vv = e % V;
@@ -626,46 +710,65 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         sdA[tid] = a;
         sbdA[tid] = sb[i] * a;
     }
-    // ---- f. contractions over V with S and dS': (dO S^T), (dX S^T), (W dS'^T) [CB][K] and rowsum(S * dS')
-    float a1[CB], a2[CB], a3[CB], fsd = 0.f;
+    // ---- f. contractions over V on the matrix cores: (dO S^T), (dX S^T), (W dS'^T) [CB][K], tile rt of 16 key
+    // rows with wavefront rt % 4, and rowsum(S * dS') alongside. Lane l = m + 16 qq: k slot qq of product j
+    // stands for column 16 s + 4 qq + j, so one float4 of a row of S or dS' (and of dO, dX, W) serves four
+    // products; the results come back as D[t][r] with t = 4 qq + i, r = 16 rt + m.
+    f32x4 a1[NZ], a2[NZ], a3[NZ];
+    float fsd[NZ];
 #pragma unroll
-    for (int t = 0; t < CB; ++t) a1[t] = a2[t] = a3[t] = 0.f;
-    const int r = tid / TPR, part = tid % TPR;
-    {
-        const float *Sr = Sbuf + (ch0 * K + r) * sV + part * VPT;
-        const float *dSr = dSbuf + (ch0 * K + r) * sV + part * VPT;
-        for (int v0 = 0; v0 < VPT; v0 += 4) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(Sr + v0);
-            const float4 d4 = *reinterpret_cast<const float4 *>(dSr + v0);
-            fsd += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
-            const int vo = part * VPT + v0;
+    for (int z = 0; z < NZ; ++z) {
+        a1[z] = a2[z] = a3[z] = zero4();
+        fsd[z] = 0.f;
+        const int rt = wv + 4 * z;
+        if (rt < KT) {  // wavefront-uniform
+            // row 16 rt + m, columns 16 sv + 4 qq .. +3 of S and dS': in their fragment order the four values
+            // are consecutive, at ((sv K/16 + rt) 4 + m % 4) 64 + (m / 4) 16 + 4 qq
+            const int64_t so = ch0 * (int64_t)(K * V) + (rt * 4 + (m & 3)) * 64 + (m >> 2) * 16 + 4 * qq;
+            float4 s4r[V / 16], d4r[V / 16];
 #pragma unroll
-            for (int t = 0; t < CB; ++t) {
-                const float4 o = *reinterpret_cast<const float4 *>(b0 + t * VM + vo);
-                const float4 x = *reinterpret_cast<const float4 *>(b1 + t * VM + vo);
-                const float4 w = *reinterpret_cast<const float4 *>(b2 + t * VM + vo);
-                a1[t] += o.x * s4.x + o.y * s4.y + o.z * s4.z + o.w * s4.w;
-                a2[t] += x.x * s4.x + x.y * s4.y + x.z * s4.z + x.w * s4.w;
-                a3[t] += w.x * d4.x + w.y * d4.y + w.z * d4.z + w.w * d4.w;
+            for (int sv = 0; sv < V / 16; ++sv) {
+                s4r[sv] = *reinterpret_cast<const float4 *>(Sbuf + so + sv * (KT * 256));
+                d4r[sv] = *reinterpret_cast<const float4 *>(dSbuf + so + sv * (KT * 256));
             }
-        }
-    }
 #pragma unroll
-    for (int t = 0; t < CB; ++t) {
-        a1[t] = sum_lanes<TPR>(a1[t]);
-        a2[t] = sum_lanes<TPR>(a2[t]);
-        a3[t] = sum_lanes<TPR>(a3[t]);
+            for (int sv = 0; sv < V / 16; ++sv) {
+                const float4 s4 = s4r[sv], d4 = d4r[sv];
+                const float4 o4 = *reinterpret_cast<const float4 *>(b0 + m * VM + 16 * sv + 4 * qq);
+                const float4 x4 = *reinterpret_cast<const float4 *>(b1 + m * VM + 16 * sv + 4 * qq);
+                const float4 w4 = *reinterpret_cast<const float4 *>(b2 + m * VM + 16 * sv + 4 * qq);
+                a1[z] = mfma4(o4.x, s4.x, a1[z]);
+                a1[z] = mfma4(o4.y, s4.y, a1[z]);
+                a1[z] = mfma4(o4.z, s4.z, a1[z]);
+                a1[z] = mfma4(o4.w, s4.w, a1[z]);
+                a2[z] = mfma4(x4.x, s4.x, a2[z]);
+                a2[z] = mfma4(x4.y, s4.y, a2[z]);
+                a2[z] = mfma4(x4.z, s4.z, a2[z]);
+                a2[z] = mfma4(x4.w, s4.w, a2[z]);
+                a3[z] = mfma4(w4.x, d4.x, a3[z]);
+                a3[z] = mfma4(w4.y, d4.y, a3[z]);
+                a3[z] = mfma4(w4.z, d4.z, a3[z]);
+                a3[z] = mfma4(w4.w, d4.w, a3[z]);
+                fsd[z] += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+            }
+            mfma_fence(a1[z], a2[z], a3[z]);
+        }
+        fsd[z] += __shfl_xor(fsd[z], 16);  // the four lanes of a key row (qq = 0..3)
+        fsd[z] += __shfl_xor(fsd[z], 32);
     }
-    fsd = sum_lanes<TPR>(fsd);
     __syncthreads();  // every read of b0..b3 is done
-    if (part == 0) {
 #pragma unroll
-        for (int t = 0; t < CB; ++t) {
-            b0[t * VM + r] = a1[t];
-            b1[t * VM + r] = a2[t];
-            b2[t * VM + r] = a3[t];
+    for (int z = 0; z < NZ; ++z) {
+        const int rt = wv + 4 * z;
+        if (rt < KT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b0[(4 * qq + i) * VM + 16 * rt + m] = a1[z][i];
+                b1[(4 * qq + i) * VM + 16 * rt + m] = a2[z][i];
+                b2[(4 * qq + i) * VM + 16 * rt + m] = a3[z][i];
+            }
+            if (qq == 0) sdGC[16 * rt + m] = fsd[z];
         }
-        sdGC[r] = fsd;
     }
     if (tid < CB && tid < at.nval) {  // dbeta
         const int i = tid;
@@ -1131,20 +1234,32 @@ template <int K, int V>
 void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void *ks, bool qk_bf, const void *vs,
               bool v_bf, float *dv_dst, float *dq_dst, float *dk_dst, hipStream_t st) {
     const bool io_bf = a.io_bf16, og = a.o_gate != nullptr;
-    const int32_t nvt = V / CVT > 0 ? V / CVT : 1;
+    constexpr int NW = V / 16 < 4 ? V / 16 : 4;  // wavefronts (16-column tiles) per workgroup of the two passes
+    const int32_t nvt = V / (16 * NW);
     const int64_t nchunk_blocks = a.max_segs * a.H;
     const int64_t npass_blocks = (int64_t)a.num_seqs * a.H * nvt;
     if (nchunk_blocks > 0)
         hipLaunchKernelGGL((kda_cb_factors<K>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
                            a.beta, io_bf, a.gate_sigmoid, w.seq_tok, w.seg_off, a.num_seqs, a.H, w.fac);
     if (npass_blocks > 0) {
-        hipLaunchKernelGGL((kda_cb_fwd<K>), dim3((unsigned)npass_blocks), dim3(CNT), 0, st, vs, v_bf,
-                           (const float *)w.fac, a.S0, w.seq_tok, w.seg_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout,
-                           a.o_gate, io_bf, w.doe, a.d_o_gate);
-        // with an output gate the reverse reads do * sigmoid(z), formed by the forward pass
-        hipLaunchKernelGGL((kda_cb_rev<K>), dim3((unsigned)npass_blocks), dim3(CNT), 0, st,
-                           og ? (const void *)w.doe : a.dout, og ? false : io_bf, (const float *)w.fac, a.dS_final,
-                           w.seq_tok, w.seg_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
+        auto fwd = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
+                               a.S0, w.seq_tok, w.seg_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate, w.doe,
+                               a.d_o_gate);
+        };
+        if (og) {
+            if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
+            else io_bf ? fwd(kda_cb_fwd<K, NW, true, false, true>) : fwd(kda_cb_fwd<K, NW, true, false, false>);
+        } else {
+            v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
+        }
+        // with an output gate the reverse reads do * sigmoid(z) (fp32), formed by the forward pass
+        auto rev = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st,
+                               og ? (const void *)w.doe : a.dout, (const float *)w.fac, a.dS_final, w.seq_tok,
+                               w.seg_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
+        };
+        (!og && io_bf) ? rev(kda_cb_rev<K, NW, true>) : rev(kda_cb_rev<K, NW, false>);
     }
     if (nchunk_blocks > 0)
         hipLaunchKernelGGL((kda_cb_grad<K, V>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
