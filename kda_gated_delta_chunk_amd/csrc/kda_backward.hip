@@ -146,6 +146,23 @@ constexpr int64_t fac_floats(int K) { return ((6 * CB * K + 7 * CB * CB + K) + 6
 __device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
     return bf ? bf2f(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
 }
+// Four consecutive elements (index i, a multiple of 4) of a bf16 (bf) or fp32 array as raw words, and those
+// words as floats. The split lets a thread issue all its loads before it waits for any of them.
+__device__ __forceinline__ uint4 ld_raw4(const void *p, int64_t i, bool bf) {
+    if (bf) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+        return make_uint4(w.x, w.y, 0u, 0u);
+    }
+    return *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p) + i);
+}
+__device__ __forceinline__ f32x4 raw4_f(uint4 r, bool bf) {
+    f32x4 x;
+    x[0] = __uint_as_float(bf ? r.x << 16 : r.x);
+    x[1] = __uint_as_float(bf ? r.x & 0xffff0000u : r.y);
+    x[2] = __uint_as_float(bf ? r.y << 16 : r.z);
+    x[3] = __uint_as_float(bf ? r.y & 0xffff0000u : r.w);
+    return x;
+}
 // the log-decay of a gate input: as given, or -5 sigmoid(x)
 __device__ __forceinline__ float log_decay_of(float x, bool gate_sig) { return gate_sig ? -5.f * sigmoid_f(x) : x; }
 
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
                                                       float *__restrict__ fac) {
     using L = FacL<K>;
     constexpr int KP = CB + 1;
-    __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
+    __shared__ __align__(16) float sq[CB * K], sk[CB * K], sg[CB * K];
     __shared__ float tKG[K * KP], tKI[K * KP], tQG[K * KP], tKc[K * KP], tWk[K * KP];
     __shared__ float sA[CB * CB], sT[CB * CB], sP[CB * CB], sb[CB];
     const int tid = threadIdx.x;
@@ -190,15 +207,36 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
     if (c >= chunk_off[N]) return;  // past the last chunk (the grid covers an upper bound)
     const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
     float *blk = fac + ((int64_t)c * H + h) * fac_floats(K);
-    for (int e = tid; e < CB * K; e += CNT) {
-        const int t = e / K, ch = e % K;
-        const bool ok = t < at.nval;
-        const int64_t idx = ((at.tok0 + t) * H + h) * K + ch;
-        sq[e] = ok ? ld_as(q, idx, qk_bf) : 0.f;
-        sk[e] = ok ? ld_as(k, idx, qk_bf) : 0.f;
-        sg[e] = ok ? log_decay_of(ld_as(g, idx, io_bf), gate_sig) : 0.f;
+    {  // runs of 4 channels; rows past the chunk's valid tokens re-read its last valid row and are zeroed
+        constexpr int RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
+        uint4 rq[NK], rk[NK], rg[NK];
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4), c4 = e % (K / 4);
+            const int tt = t < at.nval ? t : at.nval - 1;
+            const int64_t idx = ((at.tok0 + tt) * H + h) * K + 4 * c4;
+            if (e < RK) {
+                rq[j] = ld_raw4(q, idx, qk_bf);
+                rk[j] = ld_raw4(k, idx, qk_bf);
+                rg[j] = ld_raw4(g, idx, io_bf);
+            }
+        }
+        if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * H + h, io_bf) : 0.f;
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4);
+            if (e < RK) {
+                const bool ok = t < at.nval;
+                const f32x4 z = zero4(), gv = raw4_f(rg[j], io_bf);
+                f32x4 ld;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
+                reinterpret_cast<f32x4 *>(sq)[e] = ok ? raw4_f(rq[j], qk_bf) : z;
+                reinterpret_cast<f32x4 *>(sk)[e] = ok ? raw4_f(rk[j], qk_bf) : z;
+                reinterpret_cast<f32x4 *>(sg)[e] = ok ? ld : z;
+            }
+        }
     }
-    if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * H + h, io_bf) : 0.f;
     __syncthreads();
     // prefix b, suffix s (each summed from its own terms), the scaled rows (key-major) and Gc
     for (int e = tid; e < CB * K; e += CNT) {
@@ -625,8 +663,8 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     constexpr int VM = (K > V ? K : V) + 4;  // row pitch: float4 reads of 16 rows fall in distinct banks
     constexpr int KT = K / 16, NZ = (KT + 3) / 4;  // 16-row tiles of K; tiles per wavefront in phase f
     constexpr int CPT = K / 16;                  // channels per thread in the per-(token, channel) phase
-    __shared__ float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
-    __shared__ float sq[CB * K], sk[CB * K], sg[CB * K];
+    __shared__ __align__(16) float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
+    __shared__ __align__(16) float sq[CB * K], sk[CB * K], sg[CB * K];
     __shared__ float sT[CB * CB], sM[CB * CB], sP[CB * CB], sAb[CB * CB], sdT[CB * CB], sdP[CB * CB];
     __shared__ float sY[CB * CB], sdA[CB * CB], sbdA[CB * CB], sb[CB], sdbT[CB], sdGC[K], sGC[K];
     const int tid = threadIdx.x;
@@ -637,29 +675,71 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     const int64_t sH = H, sV = V, ch0 = c * sH + h;
     const float *blk = fac + ch0 * fac_floats(K);
     const int lane = tid & 63, wv = tid >> 6, m = lane & 15, qq = lane >> 4;
-    // ---- a. loads
-    for (int e = tid; e < CB * V; e += CNT) {
-        const int t = e / V, vv = e % V;
-        const int64_t xo = (ch0 * CB + t) * sV + vv;
-        b0[t * VM + vv] = t < at.nval ? ld_as(dout, ((at.tok0 + t) * sH + h) * sV + vv, do_bf) : 0.f;
-        b1[t * VM + vv] = Xbuf[xo];
-        b2[t * VM + vv] = Wbuf[xo];
-        b3[t * VM + vv] = dWbuf[xo];
+    // ---- a. loads, in runs of 4 columns, all issued before any is waited for; rows past the chunk's valid
+    // tokens re-read its last valid row, and dO, q, k, g are zeroed there (X, W and dW are zero there already)
+    {
+        constexpr int RV = CB * V / 4, NV = (RV + CNT - 1) / CNT, RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
+        uint4 rdo[NV], rq[NK], rk[NK], rg[NK];
+        f32x4 rx[NV], rw[NV], rdw[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = tid + CNT * j, t = e / (V / 4), c4 = e % (V / 4);
+            const int tt = t < at.nval ? t : at.nval - 1;
+            const int64_t xo = (ch0 * CB + t) * sV + 4 * c4;
+            if (e < RV) {
+                rdo[j] = ld_raw4(dout, ((at.tok0 + tt) * sH + h) * sV + 4 * c4, do_bf);
+                rx[j] = *reinterpret_cast<const f32x4 *>(Xbuf + xo);
+                rw[j] = *reinterpret_cast<const f32x4 *>(Wbuf + xo);
+                rdw[j] = *reinterpret_cast<const f32x4 *>(dWbuf + xo);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4), c4 = e % (K / 4);
+            const int tt = t < at.nval ? t : at.nval - 1;
+            const int64_t idx = ((at.tok0 + tt) * sH + h) * K + 4 * c4;
+            if (e < RK) {
+                rq[j] = ld_raw4(q, idx, qk_bf);
+                rk[j] = ld_raw4(k, idx, qk_bf);
+                rg[j] = ld_raw4(g, idx, io_bf);
+            }
+        }
+        const float fT = blk[L::TT + tid], fM = blk[L::MM + tid], fP = blk[L::PP + tid], fA = blk[L::AB + tid];
+        const float fG = tid < K ? blk[L::GC + tid] : 0.f;
+        const float fb = tid < CB ? ld_as(beta, (at.tok0 + (tid < at.nval ? tid : at.nval - 1)) * sH + h, io_bf) : 0.f;
+        const f32x4 z = zero4();
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int e = tid + CNT * j, t = e / (V / 4), c4 = e % (V / 4);
+            if (e < RV) {
+                const int o = t * VM + 4 * c4;
+                *reinterpret_cast<f32x4 *>(b0 + o) = t < at.nval ? raw4_f(rdo[j], do_bf) : z;
+                *reinterpret_cast<f32x4 *>(b1 + o) = rx[j];
+                *reinterpret_cast<f32x4 *>(b2 + o) = rw[j];
+                *reinterpret_cast<f32x4 *>(b3 + o) = rdw[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4);
+            if (e < RK) {
+                const bool ok = t < at.nval;
+                const f32x4 gv = raw4_f(rg[j], io_bf);
+                f32x4 ld;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
+                reinterpret_cast<f32x4 *>(sq)[e] = ok ? raw4_f(rq[j], qk_bf) : z;
+                reinterpret_cast<f32x4 *>(sk)[e] = ok ? raw4_f(rk[j], qk_bf) : z;
+                reinterpret_cast<f32x4 *>(sg)[e] = ok ? ld : z;
+            }
+        }
+        sT[tid] = fT;
+        sM[tid] = fM;
+        sP[tid] = fP;
+        sAb[tid] = fA;
+        if (tid < K) sGC[tid] = fG;
+        if (tid < CB) sb[tid] = tid < at.nval ? fb : 0.f;
     }
-    for (int e = tid; e < CB * K; e += CNT) {
-        const int t = e / K, ch = e % K;
-        const bool ok = t < at.nval;
-        const int64_t idx = ((at.tok0 + t) * sH + h) * K + ch;
-        sq[e] = ok ? ld_as(q, idx, qk_bf) : 0.f;
-        sk[e] = ok ? ld_as(k, idx, qk_bf) : 0.f;
-        sg[e] = ok ? log_decay_of(ld_as(g, idx, io_bf), gate_sig) : 0.f;
-    }
-    sT[tid] = blk[L::TT + tid];
-    sM[tid] = blk[L::MM + tid];
-    sP[tid] = blk[L::PP + tid];
-    sAb[tid] = blk[L::AB + tid];
-    for (int e = tid; e < K; e += CNT) sGC[e] = blk[L::GC + e];
-    if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * sH + h, io_bf) : 0.f;
     __syncthreads();
     // ---- b. dT = dW X^T, dP = tril(dO W^T): thread (i, j); the column order is rotated by j so that the 16
     // rows j of a wavefront fall in distinct banks
