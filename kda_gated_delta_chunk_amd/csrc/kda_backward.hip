@@ -148,12 +148,21 @@ __device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
 }
 // Four consecutive elements (index i, a multiple of 4) of a bf16 (bf) or fp32 array as raw words, and those
 // words as floats. The split lets a thread issue all its loads before it waits for any of them.
+// Both loads are issued for either type (bf16 reads its 8 bytes twice), so that no branch or select touches
+// a loaded value before it is converted.
 __device__ __forceinline__ uint4 ld_raw4(const void *p, int64_t i, bool bf) {
-    if (bf) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
-        return make_uint4(w.x, w.y, 0u, 0u);
-    }
-    return *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(p) + i);
+    const char *b = reinterpret_cast<const char *>(p) + i * (bf ? 2 : 4);
+    const uint2 lo = *reinterpret_cast<const uint2 *>(b);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(bf ? b : b + 8);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+// One element as two 16-bit halves (the bf16 value twice, or the fp32 word's low and high halves).
+__device__ __forceinline__ uint2 ld_raw1(const void *p, int64_t i, bool bf) {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(p) + (bf ? i : 2 * i);
+    return make_uint2(h[0], h[bf ? 0 : 1]);
+}
+__device__ __forceinline__ float raw1_f(uint2 r, bool bf) {
+    return __uint_as_float(bf ? r.x << 16 : r.x | r.y << 16);
 }
 __device__ __forceinline__ f32x4 raw4_f(uint4 r, bool bf) {
     f32x4 x;
@@ -169,6 +178,10 @@ __device__ __forceinline__ float log_decay_of(float x, bool gate_sig) { return g
 struct ChunkAt {
     int n, nval;
     int64_t tok0;
+};
+// One entry per chunk: its first token and number of valid tokens (0 past the last chunk).
+struct ChunkEnt {
+    int64_t tok0, nval;
 };
 // chunk c (< chunk_off[N]): its sequence (the largest n < N with chunk_off[n] <= c), first token and
 // number of valid tokens
@@ -187,14 +200,29 @@ __device__ __forceinline__ ChunkAt chunk_at(const int64_t *seq_tok, const int64_
     return r;
 }
 
+// The chunk table of the per-(chunk, head) kernels, written once so that each of their workgroups finds its
+// chunk with one load instead of a chain of dependent ones.
+__global__ __launch_bounds__(256) void kda_bwd_chunks(const int64_t *__restrict__ seq_tok,
+                                                      const int64_t *__restrict__ chunk_off, int32_t N,
+                                                      int64_t n_entries, ChunkEnt *__restrict__ ctab) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= n_entries) return;
+    ChunkEnt e = {0, 0};
+    if (c < chunk_off[N]) {
+        const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+        e.tok0 = at.tok0;
+        e.nval = at.nval;
+    }
+    ctab[c] = e;
+}
+
 // ---- factors: one workgroup per (chunk, head). K-major copies of K~, K^ and Q~ (pitch CB + 1) serve the
 // CB x CB products without bank conflicts.
 template <int K>
 __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q, const void *__restrict__ k,
                                                       bool qk_bf, const void *__restrict__ g,
                                                       const void *__restrict__ beta, bool io_bf, bool gate_sig,
-                                                      const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off, int32_t N, int32_t H,
+                                                      const ChunkEnt *__restrict__ ctab, int32_t H,
                                                       float *__restrict__ fac) {
     using L = FacL<K>;
     constexpr int KP = CB + 1;
@@ -204,8 +232,11 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
     const int tid = threadIdx.x;
     const int64_t c = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
-    if (c >= chunk_off[N]) return;  // past the last chunk (the grid covers an upper bound)
-    const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+    const ChunkEnt ce = ctab[c];
+    if (ce.nval == 0) return;  // past the last chunk (the grid covers an upper bound)
+    ChunkAt at;
+    at.tok0 = ce.tok0;
+    at.nval = (int)ce.nval;
     float *blk = fac + ((int64_t)c * H + h) * fac_floats(K);
     {  // runs of 4 channels; rows past the chunk's valid tokens re-read its last valid row and are zeroed
         constexpr int RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
@@ -656,7 +687,7 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     const void *__restrict__ beta, bool io_bf, bool gate_sig, const void *__restrict__ dout, bool do_bf,
     const float *__restrict__ fac, const float *__restrict__ Sbuf, const float *__restrict__ dSbuf,
     const float *__restrict__ Xbuf, const float *__restrict__ Wbuf, const float *__restrict__ dWbuf,
-    const int64_t *__restrict__ seq_tok, const int64_t *__restrict__ chunk_off, int32_t N, int32_t H,
+    const ChunkEnt *__restrict__ ctab, int32_t H,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta) {
     using L = FacL<K>;
@@ -670,8 +701,11 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     const int tid = threadIdx.x;
     const int64_t c = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
-    if (c >= chunk_off[N]) return;
-    const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+    const ChunkEnt ce = ctab[c];
+    if (ce.nval == 0) return;
+    ChunkAt at;
+    at.tok0 = ce.tok0;
+    at.nval = (int)ce.nval;
     const int64_t sH = H, sV = V, ch0 = c * sH + h;
     const float *blk = fac + ch0 * fac_floats(K);
     const int lane = tid & 63, wv = tid >> 6, m = lane & 15, qq = lane >> 4;
@@ -706,7 +740,7 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         }
         const float fT = blk[L::TT + tid], fM = blk[L::MM + tid], fP = blk[L::PP + tid], fA = blk[L::AB + tid];
         const float fG = tid < K ? blk[L::GC + tid] : 0.f;
-        const float fb = tid < CB ? ld_as(beta, (at.tok0 + (tid < at.nval ? tid : at.nval - 1)) * sH + h, io_bf) : 0.f;
+        const uint2 fb = ld_raw1(beta, (at.tok0 + (tid < at.nval ? tid % CB : at.nval - 1)) * sH + h, io_bf);
         const f32x4 z = zero4();
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -738,31 +772,72 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         sP[tid] = fP;
         sAb[tid] = fA;
         if (tid < K) sGC[tid] = fG;
-        if (tid < CB) sb[tid] = tid < at.nval ? fb : 0.f;
+        if (tid < CB) sb[tid] = tid < at.nval ? raw1_f(fb, io_bf) : 0.f;
     }
     __syncthreads();
-    // ---- b. dT = dW X^T, dP = tril(dO W^T): thread (i, j); the column order is rotated by j so that the 16
-    // rows j of a wavefront fall in distinct banks
-    {
-        const int i = tid / CB, j = tid % CB;
-        float dt = 0.f, dp = 0.f;
-        for (int u = 0; u < V; ++u) {
-            const int vv = (u + j) & (V - 1);
-            dt += b3[i * VM + vv] * b1[j * VM + vv];
-            dp += b0[i * VM + vv] * b2[j * VM + vv];
-        }
-        sdT[tid] = dt;
-        sdP[tid] = j <= i ? dp : 0.f;
-    }
-    __syncthreads();
-    // ---- c. dX = T^T dW (= dv), into b1; dbeta's T part
-    for (int e = tid; e < CB * V; e += CNT) {
-        const int t = e / V, vv = e % V;
-        float s = 0.f;
+    // ---- the rows of S and dS' that phase f multiplies: all issued here (and kept here by the scheduling
+    // barrier), so that their latency overlaps phases b to e. Row 16 rt + m, columns 16 sv + 4 qq .. +3: in
+    // their fragment order the four values are consecutive, at ((sv K/16 + rt) 4 + m % 4) 64 + (m / 4) 16 + 4 qq.
+    f32x4 s4r[NZ][V / 16], d4r[NZ][V / 16];
 #pragma unroll
-        for (int i = 0; i < CB; ++i) s += sT[i * CB + t] * b3[i * VM + vv];
-        b1[t * VM + vv] = s;
-        if (t < at.nval) dv[((at.tok0 + t) * sH + h) * sV + vv] = s;
+    for (int z = 0; z < NZ; ++z) {
+        const int rt = wv + 4 * z;
+        if (rt < KT) {  // wavefront-uniform
+            const int64_t so = ch0 * (int64_t)(K * V) + (rt * 4 + (m & 3)) * 64 + (m >> 2) * 16 + 4 * qq;
+#pragma unroll
+            for (int sv = 0; sv < V / 16; ++sv) {
+                s4r[z][sv] = *reinterpret_cast<const f32x4 *>(Sbuf + so + sv * (KT * 256));
+                d4r[z][sv] = *reinterpret_cast<const f32x4 *>(dSbuf + so + sv * (KT * 256));
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- b. dT = dW X^T (wavefront 0) and dP = tril(dO W^T) (wavefront 1) on the matrix cores, the sum over V
+    // in two chains. Lane l = m + 16 qq: k slot qq of product j stands for column 16 s + 4 qq + j, so one float4
+    // of row m of each operand serves four products; the result comes back as D[4 qq + i][m].
+    if (wv < 2) {  // wavefront-uniform
+        const float *ra = wv == 0 ? b3 : b0, *rb = wv == 0 ? b1 : b2;
+        f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int sv = 0; sv < V / 16; sv += 2) {
+            d0 = mfma_x4(d0, *reinterpret_cast<const float4 *>(ra + m * VM + 16 * sv + 4 * qq),
+                         *reinterpret_cast<const f32x4 *>(rb + m * VM + 16 * sv + 4 * qq));
+            if (sv + 1 < V / 16)
+                d1 = mfma_x4(d1, *reinterpret_cast<const float4 *>(ra + m * VM + 16 * (sv + 1) + 4 * qq),
+                             *reinterpret_cast<const f32x4 *>(rb + m * VM + 16 * (sv + 1) + 4 * qq));
+        }
+        mfma_fence(d0, d1);
+        const f32x4 d = d0 + d1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * qq + i;
+            if (wv == 0) sdT[r * CB + m] = d[i];
+            else sdP[r * CB + m] = m <= r ? d[i] : 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- c. dX = T^T dW (= dv) on the matrix cores, into b1: wavefront w takes the 16-column tiles w, w + 4, ...;
+    // k slot qq of product j stands for row 4 qq + j of dW
+    {
+        float4 ta;  // T^T[m][4 qq + j] = T[4 qq + j][m]
+        ta.x = sT[(4 * qq + 0) * CB + m];
+        ta.y = sT[(4 * qq + 1) * CB + m];
+        ta.z = sT[(4 * qq + 2) * CB + m];
+        ta.w = sT[(4 * qq + 3) * CB + m];
+#pragma unroll
+        for (int vt = wv; vt < V / 16; vt += 4) {
+            f32x4 bw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bw[j] = b3[(4 * qq + j) * VM + 16 * vt + m];
+            f32x4 d = mfma_x4(zero4(), ta, bw);
+            mfma_fence(d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * qq + i;
+                b1[t * VM + 16 * vt + m] = d[i];
+                if (t < at.nval) dv[((at.tok0 + t) * sH + h) * sV + 16 * vt + m] = d[i];
+            }
+        }
     }
     if (tid < CB) {
         float s = 0.f;
@@ -802,34 +877,25 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         fsd[z] = 0.f;
         const int rt = wv + 4 * z;
         if (rt < KT) {  // wavefront-uniform
-            // row 16 rt + m, columns 16 sv + 4 qq .. +3 of S and dS': in their fragment order the four values
-            // are consecutive, at ((sv K/16 + rt) 4 + m % 4) 64 + (m / 4) 16 + 4 qq
-            const int64_t so = ch0 * (int64_t)(K * V) + (rt * 4 + (m & 3)) * 64 + (m >> 2) * 16 + 4 * qq;
-            float4 s4r[V / 16], d4r[V / 16];
 #pragma unroll
             for (int sv = 0; sv < V / 16; ++sv) {
-                s4r[sv] = *reinterpret_cast<const float4 *>(Sbuf + so + sv * (KT * 256));
-                d4r[sv] = *reinterpret_cast<const float4 *>(dSbuf + so + sv * (KT * 256));
-            }
-#pragma unroll
-            for (int sv = 0; sv < V / 16; ++sv) {
-                const float4 s4 = s4r[sv], d4 = d4r[sv];
+                const f32x4 s4 = s4r[z][sv], d4 = d4r[z][sv];
                 const float4 o4 = *reinterpret_cast<const float4 *>(b0 + m * VM + 16 * sv + 4 * qq);
                 const float4 x4 = *reinterpret_cast<const float4 *>(b1 + m * VM + 16 * sv + 4 * qq);
                 const float4 w4 = *reinterpret_cast<const float4 *>(b2 + m * VM + 16 * sv + 4 * qq);
-                a1[z] = mfma4(o4.x, s4.x, a1[z]);
-                a1[z] = mfma4(o4.y, s4.y, a1[z]);
-                a1[z] = mfma4(o4.z, s4.z, a1[z]);
-                a1[z] = mfma4(o4.w, s4.w, a1[z]);
-                a2[z] = mfma4(x4.x, s4.x, a2[z]);
-                a2[z] = mfma4(x4.y, s4.y, a2[z]);
-                a2[z] = mfma4(x4.z, s4.z, a2[z]);
-                a2[z] = mfma4(x4.w, s4.w, a2[z]);
-                a3[z] = mfma4(w4.x, d4.x, a3[z]);
-                a3[z] = mfma4(w4.y, d4.y, a3[z]);
-                a3[z] = mfma4(w4.z, d4.z, a3[z]);
-                a3[z] = mfma4(w4.w, d4.w, a3[z]);
-                fsd[z] += s4.x * d4.x + s4.y * d4.y + s4.z * d4.z + s4.w * d4.w;
+                a1[z] = mfma4(o4.x, s4[0], a1[z]);
+                a1[z] = mfma4(o4.y, s4[1], a1[z]);
+                a1[z] = mfma4(o4.z, s4[2], a1[z]);
+                a1[z] = mfma4(o4.w, s4[3], a1[z]);
+                a2[z] = mfma4(x4.x, s4[0], a2[z]);
+                a2[z] = mfma4(x4.y, s4[1], a2[z]);
+                a2[z] = mfma4(x4.z, s4[2], a2[z]);
+                a2[z] = mfma4(x4.w, s4[3], a2[z]);
+                a3[z] = mfma4(w4.x, d4[0], a3[z]);
+                a3[z] = mfma4(w4.y, d4[1], a3[z]);
+                a3[z] = mfma4(w4.z, d4[2], a3[z]);
+                a3[z] = mfma4(w4.w, d4[3], a3[z]);
+                fsd[z] += s4[0] * d4[0] + s4[1] * d4[1] + s4[2] * d4[2] + s4[3] * d4[3];
             }
             mfma_fence(a1[z], a2[z], a3[z]);
         }
@@ -858,60 +924,62 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         dbeta[(at.tok0 + i) * sH + h] = s;
     }
     __syncthreads();
-    // ---- g. per key channel (threads 0 .. K-1), over the chunk's 16 tokens. alpha_u = e^{g_u}; e^{b_u} and
-    // e^{s_u} are running products of them, and so is the weight e^{b_i - b_j} of every pair j < i (a product
-    // of the decays between the two tokens, accurate to the pair's own length). The accumulators of dq, dk
-    // and of dg's difference array live in this thread's column of b0, b1, b2 (row u at u * VM), and the
-    // remaining terms of dg in b3.
-    if (tid < K) {
-        const int ch = tid;
-        float *aq = b0 + ch, *ak = b1 + ch, *aD = b2 + ch, *base = b3 + ch;
-        float qv[CB], kv[CB], al[CB];
-        {
-            float run = 1.f;
+    // ---- g. per key channel, over the chunk's 16 tokens, two threads per channel (thread tid: channel tid % K,
+    // half tid / K). alpha_u = e^{g_u}; e^{b_u} and e^{s_u} are running products of them, and so is the weight
+    // e^{b_i - b_j} of every pair j < i (a product of the decays between the two tokens, accurate to the pair's
+    // own length). Half 0 takes the token-local terms and the pairs with j < 4 or j >= 12, half 1 the pairs
+    // with 4 <= j < 12 (60 pairs each); half 1 hands its sums to half 0 through b0..b2.
+    const int gch = tid % K, half = tid / K;
+    float qv[CB], kv[CB], al[CB], aq[CB], ak[CB], aD[CB], bs[CB];
+    if (half < 2) {
 #pragma unroll
-            for (int u = 0; u < CB; ++u) {
-                qv[u] = sq[u * K + ch];
-                kv[u] = sk[u * K + ch];
-                al[u] = exp_e(sg[u * K + ch]);
-                run *= al[u];
-                base[u * VM] = run;  // e^{b_u} for the next loop
-            }
+        for (int u = 0; u < CB; ++u) {
+            qv[u] = sq[u * K + gch];
+            kv[u] = sk[u * K + gch];
+            al[u] = exp_e(sg[u * K + gch]);
+            aq[u] = ak[u] = aD[u] = bs[u] = 0.f;
         }
+    }
+    if (half == 0) {
         // token-local terms, last token first:
         //   dq_t = e^{b_t} (dO S^T)_t + dP_tt k_t,  dk_t = -e^{b_t} (dX S^T)_t + dP_tt q_t + e^{s_t} (W dS'^T)_t,
-        //   base_t = sum_{u>=t} ((dO S^T)_u q_u - (dX S^T)_u k_u) e^{b_u}, and in D_t the Kc term
-        //   (W dS'^T)_t k_t e^{s_t}, whose exclusive prefix sum the loop after adds to base
-        {
-            float esr = 1.f, suf = 0.f;
+        //   bs_t = sum_{u>=t} ((dO S^T)_u q_u - (dX S^T)_u k_u) e^{b_u}, plus the exclusive prefix sum of the Kc
+        //   terms (W dS'^T)_u k_u e^{s_u} and Gc rowsum(S * dS')
+        float eb[CB], kcd[CB];
+        float run = 1.f;
 #pragma unroll
-            for (int u = CB - 1; u >= 0; --u) {
-                const float ebu = base[u * VM];
-                const float r1 = aq[u * VM], r2 = ak[u * VM], r3 = aD[u * VM], dpd = sdP[u * CB + u];
-                aq[u * VM] = ebu * r1 + dpd * kv[u];
-                ak[u * VM] = -ebu * r2 + dpd * qv[u] + esr * r3;
-                suf += (r1 * qv[u] - r2 * kv[u]) * ebu;
-                base[u * VM] = suf;
-                aD[u * VM] = r3 * kv[u] * esr;
-                esr *= al[u];
-            }
+        for (int u = 0; u < CB; ++u) {
+            run *= al[u];
+            eb[u] = run;
         }
-        {
-            const float gcd = sdGC[ch] * sGC[ch];  // Gc rowsum(S * dS')
-            float pre = 0.f;
+        float esr = 1.f, suf = 0.f;
 #pragma unroll
-            for (int u = 0; u < CB; ++u) {
-                const float d = aD[u * VM];
-                base[u * VM] += pre + gcd;
-                pre += d;
-                aD[u * VM] = 0.f;
-            }
+        for (int u = CB - 1; u >= 0; --u) {
+            const float r1 = b0[u * VM + gch], r2 = b1[u * VM + gch], r3 = b2[u * VM + gch];
+            const float dpd = sdP[u * CB + u];
+            aq[u] = eb[u] * r1 + dpd * kv[u];
+            ak[u] = -eb[u] * r2 + dpd * qv[u] + esr * r3;
+            suf += (r1 * qv[u] - r2 * kv[u]) * eb[u];
+            bs[u] = suf;
+            kcd[u] = r3 * kv[u] * esr;
+            esr *= al[u];
         }
-        // pairs j < i: Z = dP_ij q_i + beta_i dA_ij k_i
-        //   dk_j += Z w,  dq_i += dP_ij k_j w,  dk_i += beta_i dA_ij k_j w,
-        //   and E = Z k_j w enters dg_t for j < t <= i (D_{j+1} += E, D_{i+1} -= E)
+        const float gcd = sdGC[gch] * sGC[gch];  // Gc rowsum(S * dS')
+        float pre = 0.f;
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            bs[u] += pre + gcd;
+            pre += kcd[u];
+        }
+    }
+    __syncthreads();  // b0..b2 are read; half 1 may overwrite them
+    // pairs j < i: Z = dP_ij q_i + beta_i dA_ij k_i
+    //   dk_j += Z w,  dq_i += dP_ij k_j w,  dk_i += beta_i dA_ij k_j w,
+    //   and E = Z k_j w enters dg_t for j < t <= i (D_{j+1} += E, D_{i+1} -= E)
+    if (half < 2) {
 #pragma unroll
         for (int j = 0; j < CB - 1; ++j) {
+            if ((j < 4 || j >= 12) != (half == 0)) continue;
             const float kj = kv[j];
             float w = 1.f, dkj = 0.f, Dj = 0.f;
 #pragma unroll
@@ -921,28 +989,39 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
                 const float Z = pz * qv[i] + az * kv[i];
                 const float kw = kj * w;
                 dkj += Z * w;
-                aq[i * VM] += pz * kw;
-                ak[i * VM] += az * kw;
+                aq[i] += pz * kw;
+                ak[i] += az * kw;
                 const float E = Z * kw;
                 Dj += E;
-                if (i + 1 < CB) aD[(i + 1) * VM] -= E;
+                if (i + 1 < CB) aD[i + 1] -= E;
             }
-            ak[j * VM] += dkj;
-            aD[(j + 1) * VM] += Dj;
+            ak[j] += dkj;
+            aD[j + 1] += Dj;
         }
+    }
+    if (half == 1) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            b0[u * VM + gch] = aq[u];
+            b1[u * VM + gch] = ak[u];
+            b2[u * VM + gch] = aD[u];
+        }
+    }
+    __syncthreads();
+    if (half == 0) {
         float F = 0.f;
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
-            F += aD[u * VM];
+            F += aD[u] + b2[u * VM + gch];
             if (u < at.nval) {
-                const int64_t idx = ((at.tok0 + u) * sH + h) * K + ch;
-                float dgv = base[u * VM] + F;
-                if (gate_sig) {
-                    const float sx = sigmoid_f(ld_as(g, idx, io_bf));
-                    dgv *= -5.f * sx * (1.f - sx);
+                const int64_t idx = ((at.tok0 + u) * sH + h) * K + gch;
+                float dgv = bs[u] + F;
+                if (gate_sig) {  // d(-5 sigmoid(x))/dx = -5 s (1 - s) = l (1 + l / 5) with l = -5 s
+                    const float l = sg[u * K + gch];
+                    dgv *= l * (1.f + 0.2f * l);
                 }
-                dq[idx] = aq[u * VM];
-                dk[idx] = ak[u * VM];
+                dq[idx] = aq[u] + b0[u * VM + gch];
+                dk[idx] = ak[u] + b1[u * VM + gch];
                 dg[idx] = dgv;
             }
         }
@@ -1262,6 +1341,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
     int64_t *seq_tok, *seg_off;
+    ChunkEnt *ctab;  // per chunk: first token, valid tokens
     // the chunk form: factor blocks per (chunk, head); the state entering and the state gradient leaving every
     // (chunk, head) [K][V]; X, W, dW per (chunk, head) [CB][V]; do * sigmoid(z) per token (output gate)
     float *fac, *Sb, *dSb, *Xb, *Wb, *dWb, *doe;
@@ -1284,6 +1364,7 @@ BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_chunks, int32_
     const size_t ch = (size_t)max_chunks * H;
     r.seq_tok = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.seg_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
+    r.ctab = (ChunkEnt *)take(sizeof(ChunkEnt) * (size_t)max_chunks);
     r.fac = (float *)take(sizeof(float) * ch * (size_t)fac_floats(K));
     r.Sb = (float *)take(sizeof(float) * ch * K * V);
     r.dSb = (float *)take(sizeof(float) * ch * K * V);
@@ -1320,7 +1401,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
     const int64_t npass_blocks = (int64_t)a.num_seqs * a.H * nvt;
     if (nchunk_blocks > 0)
         hipLaunchKernelGGL((kda_cb_factors<K>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
-                           a.beta, io_bf, a.gate_sigmoid, w.seq_tok, w.seg_off, a.num_seqs, a.H, w.fac);
+                           a.beta, io_bf, a.gate_sigmoid, (const ChunkEnt *)w.ctab, a.H, w.fac);
     if (npass_blocks > 0) {
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
@@ -1345,7 +1426,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         hipLaunchKernelGGL((kda_cb_grad<K, V>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
                            a.beta, io_bf, a.gate_sigmoid, og ? (const void *)w.doe : a.dout, og ? false : io_bf,
                            (const float *)w.fac, (const float *)w.Sb, (const float *)w.dSb, (const float *)w.Xb,
-                           (const float *)w.Wb, (const float *)w.dWb, w.seq_tok, w.seg_off, a.num_seqs, a.H, dq_dst,
+                           (const float *)w.Wb, (const float *)w.dWb, (const ChunkEnt *)w.ctab, a.H, dq_dst,
                            dk_dst, dv_dst, a.dg, a.dbeta);
 }
 
@@ -1370,6 +1451,9 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
     const int64_t T_row = a.cu_seqlens ? 0 : a.T;
     hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, n_tok,
                        w.seq_tok, w.seg_off);
+    if (a.max_segs > 0)
+        hipLaunchKernelGGL(kda_bwd_chunks, dim3(blocks_of(a.max_segs)), dim3(256), 0, st, (const int64_t *)w.seq_tok,
+                           (const int64_t *)w.seg_off, a.num_seqs, a.max_segs, w.ctab);
     if (!norm && !conv) {
         bwd_core<K, V>(a, w, a.q, a.k, a.io_bf16, a.v, a.io_bf16, a.dv, a.dq, a.dk, st);
         return hipGetLastError();
