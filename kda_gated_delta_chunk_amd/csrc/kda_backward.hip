@@ -90,6 +90,35 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
                                                                  true));
 }
+// 4 x 4 transpose inside each lane quad: with x_i of lane 4a + b holding M[i][b] on entry, it holds M[b][i] on
+// return. Two butterfly stages (partner lane b ^ 1, then b ^ 2) each trade the elements whose index bit
+// differs from the lane's.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
+    {
+        const bool o = b & 1;
+        const float r0 = dpp_mov<0xB1>(o ? x[0] : x[1]), r1 = dpp_mov<0xB1>(o ? x[2] : x[3]);  // quad_perm 1,0,3,2
+        if (o) {
+            x[0] = r0;
+            x[2] = r1;
+        } else {
+            x[1] = r0;
+            x[3] = r1;
+        }
+    }
+    {
+        const bool o = b & 2;
+        const float r0 = dpp_mov<0x4E>(o ? x[0] : x[2]), r1 = dpp_mov<0x4E>(o ? x[1] : x[3]);  // quad_perm 2,3,0,1
+        if (o) {
+            x[0] = r0;
+            x[1] = r1;
+        } else {
+            x[2] = r0;
+            x[3] = r1;
+        }
+    }
+    return x;
+}
+
 // ------------------------------------------------------------------ chunked reverse
 // Sequences are cut into chunks of CB tokens (each sequence starts a chunk). Per (chunk, head), with b the
 // cumulative log-decay inside the chunk (per key channel), s = b_C - b the decay after each token, and
@@ -216,143 +245,6 @@ __global__ __launch_bounds__(256) void kda_bwd_chunks(const int64_t *__restrict_
     ctab[c] = e;
 }
 
-// ---- factors: one workgroup per (chunk, head). K-major copies of K~, K^ and Q~ (pitch CB + 1) serve the
-// CB x CB products without bank conflicts.
-template <int K>
-__global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q, const void *__restrict__ k,
-                                                      bool qk_bf, const void *__restrict__ g,
-                                                      const void *__restrict__ beta, bool io_bf, bool gate_sig,
-                                                      const ChunkEnt *__restrict__ ctab, int32_t H,
-                                                      float *__restrict__ fac) {
-    using L = FacL<K>;
-    constexpr int KP = CB + 1;
-    __shared__ __align__(16) float sq[CB * K], sk[CB * K], sg[CB * K];
-    __shared__ float tKG[K * KP], tKI[K * KP], tQG[K * KP], tKc[K * KP], tWk[K * KP];
-    __shared__ float sA[CB * CB], sT[CB * CB], sP[CB * CB], sb[CB];
-    const int tid = threadIdx.x;
-    const int64_t c = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
-    const ChunkEnt ce = ctab[c];
-    if (ce.nval == 0) return;  // past the last chunk (the grid covers an upper bound)
-    ChunkAt at;
-    at.tok0 = ce.tok0;
-    at.nval = (int)ce.nval;
-    float *blk = fac + ((int64_t)c * H + h) * fac_floats(K);
-    {  // runs of 4 channels; rows past the chunk's valid tokens re-read its last valid row and are zeroed
-        constexpr int RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
-        uint4 rq[NK], rk[NK], rg[NK];
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int e = tid + CNT * j, t = e / (K / 4), c4 = e % (K / 4);
-            const int tt = t < at.nval ? t : at.nval - 1;
-            const int64_t idx = ((at.tok0 + tt) * H + h) * K + 4 * c4;
-            if (e < RK) {
-                rq[j] = ld_raw4(q, idx, qk_bf);
-                rk[j] = ld_raw4(k, idx, qk_bf);
-                rg[j] = ld_raw4(g, idx, io_bf);
-            }
-        }
-        if (tid < CB) sb[tid] = tid < at.nval ? ld_as(beta, (at.tok0 + tid) * H + h, io_bf) : 0.f;
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int e = tid + CNT * j, t = e / (K / 4);
-            if (e < RK) {
-                const bool ok = t < at.nval;
-                const f32x4 z = zero4(), gv = raw4_f(rg[j], io_bf);
-                f32x4 ld;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
-                reinterpret_cast<f32x4 *>(sq)[e] = ok ? raw4_f(rq[j], qk_bf) : z;
-                reinterpret_cast<f32x4 *>(sk)[e] = ok ? raw4_f(rk[j], qk_bf) : z;
-                reinterpret_cast<f32x4 *>(sg)[e] = ok ? ld : z;
-            }
-        }
-    }
-    __syncthreads();
-    // prefix b, suffix s (each summed from its own terms), the scaled rows (key-major) and Gc
-    for (int e = tid; e < CB * K; e += CNT) {
-        const int t = e / K, ch = e % K;
-        float b = 0.f, s = 0.f;
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            const float x = sg[u * K + ch];
-            if (u <= t) b += x;
-            else s += x;
-        }
-        const float eb = exp_e(b), kv = sk[e];
-        tKG[ch * KP + t] = kv * eb;
-        tKI[ch * KP + t] = kv * exp_e(-b);
-        tQG[ch * KP + t] = sq[e] * eb;
-        tKc[ch * KP + t] = kv * exp_e(s);
-        if (t == CB - 1) blk[L::GC + ch] = eb;
-    }
-    __syncthreads();
-    // Ab and P: thread (i, j)
-    {
-        const int i = tid / CB, j = tid % CB;
-        float a = 0.f, p = 0.f;
-        for (int ch = 0; ch < K; ++ch) {
-            const float kh = tKI[ch * KP + j];
-            a += tKG[ch * KP + i] * kh;
-            p += tQG[ch * KP + i] * kh;
-        }
-        a = j < i ? a : 0.f;
-        p = j <= i ? p : 0.f;
-        blk[L::AB + tid] = a;
-        blk[L::PP + tid] = p;
-        sA[tid] = sb[i] * a;
-        sP[tid] = p;
-    }
-    __syncthreads();
-    // M = (I + A)^{-1} by forward substitution, one column per thread; T = M diag(beta)
-    if (tid < CB) {
-        const int j = tid;
-        float m[CB];
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            float s = i == j ? 1.f : 0.f;
-#pragma unroll
-            for (int l = 0; l < i; ++l) s -= sA[i * CB + l] * m[l];
-            m[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const float tv = m[i] * sb[j];
-            blk[L::MM + i * CB + j] = m[i];
-            blk[L::TT + i * CB + j] = tv;
-            sT[i * CB + j] = tv;
-        }
-    }
-    __syncthreads();
-    // Wk = T K~ (key-major in LDS)
-    for (int e = tid; e < CB * K; e += CNT) {
-        const int t = e % CB, ch = e / CB;
-        float w = 0.f;
-#pragma unroll
-        for (int j = 0; j < CB; ++j) w += sT[t * CB + j] * tKG[ch * KP + j];
-        tWk[ch * KP + t] = w;
-    }
-    __syncthreads();
-    // fragment orders: element e = (r * 64 + l) * 4 + i, lane l = m + 16 qq
-    for (int e = tid; e < CB * K; e += CNT) {
-        const int i = e & 3, l = (e >> 2) & 63, r = e >> 8, m = l & 15, qq = l >> 4;
-        const int k1 = 16 * r + 4 * qq + i, t1 = m;   // o1: X[m][16 r + 4 q + i]
-        const int k2 = 16 * r + m, t2 = 4 * qq + i;   // o2: X[4 q + i][16 r + m]
-        blk[L::NKG1 + e] = -tKG[k1 * KP + t1];
-        blk[L::QG1 + e] = tQG[k1 * KP + t1];
-        blk[L::KC1 + e] = tKc[k1 * KP + t1];
-        blk[L::KC2 + e] = tKc[k2 * KP + t2];
-        blk[L::QG2 + e] = tQG[k2 * KP + t2];
-        blk[L::NWK2 + e] = -tWk[k2 * KP + t2];
-    }
-    {
-        const int e = tid, i = e & 3, l = e >> 2, m = l & 15, qq = l >> 4;  // CB * CB == CNT elements
-        blk[L::T1 + e] = sT[m * CB + 4 * qq + i];
-        blk[L::P1 + e] = sP[m * CB + 4 * qq + i];
-        blk[L::PT1 + e] = sP[(4 * qq + i) * CB + m];
-    }
-}
-
 // Workgroup barrier over LDS only: each wavefront's LDS operations are complete before it arrives, while
 // its global stores (states, X, W) stay in flight (a __syncthreads would wait for those as well).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -375,6 +267,181 @@ __device__ __forceinline__ void fence_tiles(f32x4 (&x)[N]) {
     } else {
 #pragma unroll
         for (int i = 0; i < N; ++i) mfma_fence(x[i]);
+    }
+}
+
+// ---- factors: one workgroup per (chunk, head). The scaled rows sit in LDS token-major (pitch K + 4, so that 16
+// rows read at one column fall in distinct banks); the CB x CB products and Wk run on the matrix cores.
+template <int K>
+__global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q, const void *__restrict__ k,
+                                                      bool qk_bf, const void *__restrict__ g,
+                                                      const void *__restrict__ beta, bool io_bf, bool gate_sig,
+                                                      const ChunkEnt *__restrict__ ctab, int32_t H,
+                                                      float *__restrict__ fac) {
+    using L = FacL<K>;
+    constexpr int KP = K + 4;
+    // q, k, g as loaded; q and k become Q~ and K~ in place, K^ and Kc go to their own rows
+    __shared__ __align__(16) float sQG[CB * KP], sKG[CB * KP], sg[CB * KP], sKI[CB * KP], sKc[CB * KP];
+    __shared__ __align__(16) float sA[CB * CB], sT[CB * CB], sP[CB * CB], sb[CB];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 15, qq = lane >> 4;
+    const int64_t c = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    const ChunkEnt ce = ctab[c];
+    if (ce.nval == 0) return;  // past the last chunk (the grid covers an upper bound)
+    ChunkAt at;
+    at.tok0 = ce.tok0;
+    at.nval = (int)ce.nval;
+    float *blk = fac + ((int64_t)c * H + h) * fac_floats(K);
+    {  // runs of 4 channels; rows past the chunk's valid tokens re-read its last valid row and are zeroed
+        constexpr int RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
+        uint4 rq[NK], rk[NK], rg[NK];
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4), c4 = e % (K / 4);
+            const int tt = t < at.nval ? t : at.nval - 1;
+            const int64_t idx = ((at.tok0 + tt) * H + h) * K + 4 * c4;
+            if (e < RK) {
+                rq[j] = ld_raw4(q, idx, qk_bf);
+                rk[j] = ld_raw4(k, idx, qk_bf);
+                rg[j] = ld_raw4(g, idx, io_bf);
+            }
+        }
+        const uint2 rb = ld_raw1(beta, (at.tok0 + (tid < at.nval ? tid % CB : at.nval - 1)) * H + h, io_bf);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int e = tid + CNT * j, t = e / (K / 4), c4 = e % (K / 4);
+            if (e < RK) {
+                const bool ok = t < at.nval;
+                const f32x4 z = zero4(), gv = raw4_f(rg[j], io_bf);
+                f32x4 ld;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
+                const int o = t * KP + 4 * c4;
+                *reinterpret_cast<f32x4 *>(sQG + o) = ok ? raw4_f(rq[j], qk_bf) : z;
+                *reinterpret_cast<f32x4 *>(sKG + o) = ok ? raw4_f(rk[j], qk_bf) : z;
+                *reinterpret_cast<f32x4 *>(sg + o) = ok ? ld : z;
+            }
+        }
+        if (tid < CB) sb[tid] = tid < at.nval ? raw1_f(rb, io_bf) : 0.f;
+    }
+    __syncthreads();
+    // the decays: thread (channel, half) takes tokens 8 half .. 8 half + 7 of one channel. b (prefix) and s
+    // (suffix) are each summed from their own terms; Kc first, from the raw k, then the rows scaled by e^{+-b}.
+    {
+        const int ch = tid % K, half = tid / K;
+        if (half < 2) {
+            float gv[CB];
+#pragma unroll
+            for (int u = 0; u < CB; ++u) gv[u] = sg[u * KP + ch];
+            const int t0 = 8 * half;
+            float sfx = 0.f;
+#pragma unroll
+            for (int u = CB - 1; u >= 0; --u) {  // s_t = sum of g_u over u > t
+                if (u < t0 + 8 && u >= t0) sKc[u * KP + ch] = sKG[u * KP + ch] * exp_e(sfx);
+                sfx += gv[u];
+            }
+            float b = 0.f;
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                b += gv[u];
+                if (u >= t0 && u < t0 + 8) {
+                    const float eb = exp_e(b), kv = sKG[u * KP + ch];
+                    sKG[u * KP + ch] = kv * eb;
+                    sKI[u * KP + ch] = kv * exp_e(-b);
+                    sQG[u * KP + ch] *= eb;
+                    if (u == CB - 1) blk[L::GC + ch] = eb;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // Ab = tril_strict(K~ K^^T) (wavefront 0) and P = tril(Q~ K^^T) (wavefront 1): k slot qq of product j stands
+    // for channel 16 s + 4 qq + j, so one float4 of row m of each operand serves four products; the result comes
+    // back as D[4 qq + i][m]
+    if (wv < 2) {  // wavefront-uniform
+        const float *ra = wv == 0 ? sKG : sQG;
+        f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int sv = 0; sv < K / 16; sv += 2) {
+            d0 = mfma_x4(d0, *reinterpret_cast<const float4 *>(ra + m * KP + 16 * sv + 4 * qq),
+                         *reinterpret_cast<const f32x4 *>(sKI + m * KP + 16 * sv + 4 * qq));
+            d1 = mfma_x4(d1, *reinterpret_cast<const float4 *>(ra + m * KP + 16 * (sv + 1) + 4 * qq),
+                         *reinterpret_cast<const f32x4 *>(sKI + m * KP + 16 * (sv + 1) + 4 * qq));
+        }
+        mfma_fence(d0, d1);
+        const f32x4 d = d0 + d1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * qq + i;
+            if (wv == 0) {
+                const float a = m < r ? d[i] : 0.f;
+                blk[L::AB + r * CB + m] = a;
+                sA[r * CB + m] = sb[r] * a;
+            } else {
+                const float pv = m <= r ? d[i] : 0.f;
+                blk[L::PP + r * CB + m] = pv;
+                sP[r * CB + m] = pv;
+            }
+        }
+    }
+    __syncthreads();
+    // M = (I + A)^{-1} by forward substitution, one column per thread; T = M diag(beta)
+    if (tid < CB) {
+        const int j = tid;
+        float mc[CB];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            float sacc = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int l = 0; l < i; ++l) sacc -= sA[i * CB + l] * mc[l];
+            mc[i] = sacc;
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const float tv = mc[i] * sb[j];
+            blk[L::MM + i * CB + j] = mc[i];
+            blk[L::TT + i * CB + j] = tv;
+            sT[i * CB + j] = tv;
+        }
+    }
+    __syncthreads();
+    // -Wk = -T K~ on the matrix cores, channel tile r by wavefront r % 4: the lane's D[4 qq + i][16 r + m] are its
+    // four values of the o2 order, stored as one float4
+    {
+        const float4 ta = *reinterpret_cast<const float4 *>(sT + m * CB + 4 * qq);  // T[m][4 qq + j]
+#pragma unroll
+        for (int r = wv; r < K / 16; r += 4) {
+            f32x4 bk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bk[j] = sKG[(4 * qq + j) * KP + 16 * r + m];
+            f32x4 d = mfma_x4(zero4(), ta, bk);
+            mfma_fence(d);
+            *reinterpret_cast<f32x4 *>(blk + L::NWK2 + (r * 64 + lane) * 4) = -d;
+        }
+    }
+    // the other operand arrays: group e4 = r 64 + l (lane l = m' + 16 q') of the o1 order is row m', channels
+    // 16 r + 4 q' .. +3 (one float4 of a row); of the o2 order, rows 4 q' .. 4 q' + 3 at channel 16 r + m'
+    for (int e4 = tid; e4 < CB * K / 4; e4 += CNT) {
+        const int r = e4 >> 6, l = e4 & 63, mm = l & 15, q4 = l >> 4;
+        const int o1 = mm * KP + 16 * r + 4 * q4, o2 = 4 * q4 * KP + 16 * r + mm;
+        const f32x4 kg = *reinterpret_cast<const f32x4 *>(sKG + o1);
+        *reinterpret_cast<f32x4 *>(blk + L::NKG1 + 4 * e4) = -kg;
+        *reinterpret_cast<f32x4 *>(blk + L::QG1 + 4 * e4) = *reinterpret_cast<const f32x4 *>(sQG + o1);
+        *reinterpret_cast<f32x4 *>(blk + L::KC1 + 4 * e4) = *reinterpret_cast<const f32x4 *>(sKc + o1);
+        f32x4 kc2, qg2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kc2[i] = sKc[o2 + i * KP];
+            qg2[i] = sQG[o2 + i * KP];
+        }
+        *reinterpret_cast<f32x4 *>(blk + L::KC2 + 4 * e4) = kc2;
+        *reinterpret_cast<f32x4 *>(blk + L::QG2 + 4 * e4) = qg2;
+    }
+    {
+        const int e = tid, i = e & 3, l = e >> 2, mm = l & 15, q4 = l >> 4;  // CB * CB == CNT elements
+        blk[L::T1 + e] = sT[mm * CB + 4 * q4 + i];
+        blk[L::P1 + e] = sP[mm * CB + 4 * q4 + i];
+        blk[L::PT1 + e] = sP[(4 * q4 + i) * CB + mm];
     }
 }
 
@@ -445,6 +512,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
     const int col = vt * 16 * NW + 16 * w + m;
+    const int slot = 4 * qq + (m & 3) + 16 * (m >> 2);  // where this lane's quad-transposed values go
     f32x4 S[KT];
 #pragma unroll
     for (int r = 0; r < KT; ++r)
@@ -501,13 +569,13 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
                 cz[i] = raw_f<IOBF>(st.z[i]);
             }
         }
-        // the state entering the chunk, in fragment order ([V/16][K/16][4][64] per chunk and head): whole
-        // 256-byte runs per store
-        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + lane;
+        // the state entering the chunk, as [V/16][K/16][64][4] per chunk and head: slot l = m' + 16 q' of tile
+        // (column block, row block) holds row m' of the row block, columns 4 q' .. 4 q' + 3 of the column block
+        // (a quad transpose turns this lane's four rows of one column into one row's four columns); each store
+        // writes a whole 1 KiB tile
+        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + 4 * slot;
 #pragma unroll
-        for (int r = 0; r < KT; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sp[(r * 4 + i) * 64] = S[r][i];
+        for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(sp + r * 256) = quad_transpose(S[r], m & 3);
         lds_barrier();
         if (ci + 2 < nch) fetch(st, ci + 2);
         // X = V - K~ S (two independent product chains)
@@ -521,12 +589,9 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         // W = T X
         f32x4 W = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fT)[lane], X);
         mfma_fence(W);
-        const int64_t xo = ((c * sH + h) * CB + 4 * qq) * sV + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Xbuf[xo + i * sV] = X[i];
-            Wbuf[xo + i * sV] = W[i];
-        }
+        const int64_t xo = ((c * sH + h) * CB + 4 * qq + (m & 3)) * sV + col - m + 4 * (m >> 2);  // row-major
+        *reinterpret_cast<f32x4 *>(Xbuf + xo) = quad_transpose(X, m & 3);
+        *reinterpret_cast<f32x4 *>(Wbuf + xo) = quad_transpose(W, m & 3);
         if constexpr (OG) {  // core output O = Q~ S + P W; do * sigmoid(z) for the reverse, and dL/dz
             f32x4 O0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fP)[lane], W), O1 = zero4();
 #pragma unroll
@@ -593,6 +658,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
     const int col = vt * 16 * NW + 16 * w + m;
+    const int slot = 4 * qq + (m & 3) + 16 * (m >> 2);
     f32x4 dS[KT];
 #pragma unroll
     for (int r = 0; r < KT; ++r)
@@ -632,11 +698,9 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         f32x4 dO;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dO[i] = 4 * qq + i < nval ? raw_f<DBF>(st.d[i]) : 0.f;
-        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + lane;
+        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + 4 * slot;
 #pragma unroll
-        for (int r = 0; r < KT; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dp[(r * 4 + i) * 64] = dS[r][i];
+        for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(dp + r * 256) = quad_transpose(dS[r], m & 3);
         lds_barrier();
         if (ci >= 2) fetch(st, ci - 2);
         // dW = P^T dO + Kc dS' (two independent product chains)
@@ -648,9 +712,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         }
         mfma_fence(dW0, dW1);
         const f32x4 dW = dW0 + dW1;
-        const int64_t wo = ((c * sH + h) * CB + 4 * qq) * sV + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dWbuf[wo + i * sV] = dW[i];
+        const int64_t wo = ((c * sH + h) * CB + 4 * qq + (m & 3)) * sV + col - m + 4 * (m >> 2);
+        *reinterpret_cast<f32x4 *>(dWbuf + wo) = quad_transpose(dW, m & 3);
         // dS = diag(Gc) dS' + Q~^T dO - Wk^T dW
 #pragma unroll
         for (int r = 0; r < KT; ++r) {
@@ -776,14 +839,14 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     }
     __syncthreads();
     // ---- the rows of S and dS' that phase f multiplies: all issued here (and kept here by the scheduling
-    // barrier), so that their latency overlaps phases b to e. Row 16 rt + m, columns 16 sv + 4 qq .. +3: in
-    // their fragment order the four values are consecutive, at ((sv K/16 + rt) 4 + m % 4) 64 + (m / 4) 16 + 4 qq.
+    // barrier), so that their latency overlaps phases b to e. Row 16 rt + m, columns 16 sv + 4 qq .. +3 are
+    // slot l of tile (sv, rt) in the passes' [V/16][K/16][64][4] order.
     f32x4 s4r[NZ][V / 16], d4r[NZ][V / 16];
 #pragma unroll
     for (int z = 0; z < NZ; ++z) {
         const int rt = wv + 4 * z;
         if (rt < KT) {  // wavefront-uniform
-            const int64_t so = ch0 * (int64_t)(K * V) + (rt * 4 + (m & 3)) * 64 + (m >> 2) * 16 + 4 * qq;
+            const int64_t so = ch0 * (int64_t)(K * V) + rt * 256 + 4 * lane;
 #pragma unroll
             for (int sv = 0; sv < V / 16; ++sv) {
                 s4r[z][sv] = *reinterpret_cast<const f32x4 *>(Sbuf + so + sv * (KT * 256));
