@@ -11,8 +11,8 @@ gate, the 16-sequence packed workload (about 130K tokens) and the
 1,048,576-token sequence. The decode half of the metric (N=512 streams, H=96,
 fp32 state of ~3.2 GB updated in place, 100 consecutive steps) is reported
 under "decode". The backward pass (kda_chunk_bwd) on the prefill workload's
-inputs is reported under "backward", against the fp32 vector peak (it runs
-on the vector ALUs).
+inputs is reported under "backward", against the fp32 dense matrix-core peak
+(its products run as fp32 MFMA).
 
 Kernel durations come from HIP events recorded on the stream the kernels run
 on, around each phase of every timed step. Roofline figures use algorithmic
@@ -35,7 +35,7 @@ from kda_gated_delta_chunk_amd.source_hash import csrc_hash
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix, TFLOP/s
-FP32_VECTOR_PEAK_TFS = 157.3    # MI355X fp32 vector, TFLOP/s
+FP32_MFMA_PEAK_TFS = 157.3      # MI355X dense fp32 matrix cores, TFLOP/s
 SIMDS = 256 * 4                 # MI355X: 256 compute units of 4 SIMDs (one matrix core each)
 CLOCK_HZ = 2.4e9                # peak engine clock
 
@@ -614,10 +614,10 @@ def main():
                         "dL/do ~ N(0,1), no dL/dS_final)",
             "ms_per_step": rb["ms"], "tokens_per_s": rb["B"] * rb["T"] / (rb["ms"] * 1e-3),
             "workspace_bytes": rb["ws_bytes"],
-            "roofline": {"bound": "alu", "kernel": "kda_chunk_bwd (chunk factors, state pass, reverse pass, gradients)",
-                         "achieved": tfs, "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": tfs / FP32_VECTOR_PEAK_TFS, "algorithmic_flops_per_call": fl,
-                         "timed": "whole call (5 launches)"}}
+            "roofline": {"bound": "mfma", "kernel": "kda_chunk_bwd (chunk factors, state pass, reverse pass, gradients)",
+                         "achieved": tfs, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_MFMA_PEAK_TFS, "algorithmic_flops_per_call": fl,
+                         "timed": "whole call (6 launches)"}}
         say("backward with the prologue (q/k norm, short convolution with SiLU): warmup 2, steps 5")
         rp = time_backward(w, 5, 2, dev, prologue=True)
         out["backward"]["with_prologue"] = {"ms_per_step": rp["ms"], "workspace_bytes": rp["ws_bytes"],

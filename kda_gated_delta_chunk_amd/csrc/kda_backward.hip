@@ -138,15 +138,16 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
 // The last form of dg_t (the derivative of everything through the decays b_u, u >= t, regrouped) has no
 // cancelling terms: every pair (i, j) of the in-chunk products enters only where it straddles t, weighted
 // by e^{b_i - b_j} summed from the decays between them, instead of as +E at i and -E at j, which in fp32
-// left the rounding of e^{+-b} (|b| up to 80) in dg. The chain runs in four launches:
+// left the rounding of e^{+-b} (|b| up to 80) in dg. After the chunk table, the chain runs in four launches:
 //   kda_cb_factors  (chunk, head): the factors above;
-//   kda_cb_fwd      (sequence, head, 32-column tile): the states S entering every chunk, X and W (and with an
+//   kda_cb_fwd      (sequence, head, 16 NW columns): the states S entering every chunk, X and W (and with an
 //                   output gate the core output, do * sigmoid(z) and dL/dz);
-//   kda_cb_rev      (sequence, head, 32-column tile): dS' leaving every chunk, dW, and dL/dS0;
+//   kda_cb_rev      (sequence, head, 16 NW columns): dS' leaving every chunk, dW, and dL/dS0;
 //   kda_cb_grad     (chunk, head): dq, dk, dv, dg, dbeta from the stored S, dS', X, W, dW.
 // Each column of S and of dS evolves on its own (decay scales rows), so the two sequential passes split V
-// into tiles; their thread (row group, column) holds K/8 rows of one column and sums over key rows go
-// through LDS. All arithmetic is fp32, deterministic (fixed summation orders, no atomics).
+// into tiles: each wavefront keeps a K x 16 slice of the state as matrix-core accumulator tiles. All
+// arithmetic is fp32 (the products as v_mfma_f32_16x16x4f32), deterministic (fixed summation orders, no
+// atomics).
 // Factor block of one (chunk, head), fp32. The sequential passes read their matrix-core operands in
 // fragment order: for v_mfma_f32_16x16x4f32, lane l = m + 16 q supplies row m and k slot q of A, row slot q and
 // column m of B, and receives rows 4 q + i (i = 0..3) of column m of D. A state tile (16 key rows) is then B
@@ -245,8 +246,8 @@ __global__ __launch_bounds__(256) void kda_bwd_chunks(const int64_t *__restrict_
     ctab[c] = e;
 }
 
-// Workgroup barrier over LDS only: each wavefront's LDS operations are complete before it arrives, while
-// its global stores (states, X, W) stay in flight (a __syncthreads would wait for those as well).
+// Workgroup barrier over LDS only: each wavefront's LDS operations are complete before it arrives, while its
+// global loads and stores (prefetches, states, X, W) stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -741,9 +742,9 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
     }
 }
 
-// ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) floats; the
-// four [CB][VM] buffers hold dO, X (then dX), W, dW, and afterwards the per-(token, channel) terms of dg
-// and the factors e^{+-b}.
+// ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) + 4 floats; the
+// four [CB][VM] buffers hold dO, X (then dX), W, dW, then the contractions over V ((dO S^T), (dX S^T),
+// (W dS'^T) in b0..b2), and last the partial sums one half of the per-channel pass hands to the other.
 template <int K, int V>
 __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     const void *__restrict__ q, const void *__restrict__ k, bool qk_bf, const void *__restrict__ g,
