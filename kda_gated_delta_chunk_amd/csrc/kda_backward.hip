@@ -45,7 +45,7 @@ __device__ int64_t bwd_scan(int64_t x, int64_t *sh, bool is_max) {
 
 __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict__ cu, int32_t N, int64_t T_row,
                                                        int64_t total, int64_t *__restrict__ seq_tok,
-                                                       int64_t *__restrict__ seg_off) {
+                                                       int64_t *__restrict__ seg_off, int64_t *__restrict__ half_off) {
     __shared__ int64_t sh[1024];
     const int t = threadIdx.x, nt = blockDim.x;
     const int64_t M = (int64_t)N + 1;
@@ -60,24 +60,30 @@ __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict_
     for (int64_t m = lo; m < hi; ++m) run = start_of(m) > run ? start_of(m) : run;
     const int64_t base = bwd_scan(run, sh, true);
     // prefix maxima of this thread's entries, and the segments of the sequences they start
-    int64_t cur = base, segs = 0;
+    int64_t cur = base, segs = 0, halves = 0;
     for (int64_t m = lo; m < hi; ++m) {
         cur = start_of(m) > cur ? start_of(m) : cur;
         seq_tok[m] = cur;
         if (m < N) {
             const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
-            segs += (nx - cur + CB - 1) / CB;
+            const int64_t nc = (nx - cur + CB - 1) / CB;
+            segs += nc;
+            halves += (nc + 1) / 2;
         }
     }
     const int64_t sbase = bwd_scan(segs, sh, false);
-    int64_t acc = sbase;
+    const int64_t hbase = bwd_scan(halves, sh, false);
+    int64_t acc = sbase, hacc = hbase;
     cur = base;
     for (int64_t m = lo; m < hi; ++m) {
         seg_off[m] = acc;
+        half_off[m] = hacc;
         cur = start_of(m) > cur ? start_of(m) : cur;
         if (m < N) {
             const int64_t nx = start_of(m + 1) > cur ? start_of(m + 1) : cur;
-            acc += (nx - cur + CB - 1) / CB;
+            const int64_t nc = (nx - cur + CB - 1) / CB;
+            acc += nc;
+            hacc += (nc + 1) / 2;
         }
     }
 }
@@ -209,9 +215,18 @@ struct ChunkAt {
     int n, nval;
     int64_t tok0;
 };
-// One entry per chunk: its first token and number of valid tokens (0 past the last chunk).
+// One entry per chunk: its first token and number of valid tokens (0 past the last chunk); the state slot of its
+// pair of chunks (chunks 2p and 2p + 1 of a sequence share slot p: the state entering chunk 2p and the state
+// gradient leaving chunk 2p + 1, or leaving chunk 2p when that is the sequence's last); which of the two the
+// local-gradient kernel rebuilds (SLOT_BOTH: neither, SLOT_REBUILD_DS: dS' leaving this chunk from the next
+// chunk's, SLOT_REBUILD_S: the state entering this chunk from the previous chunk's); the next chunk's valid
+// tokens (for SLOT_REBUILD_DS).
+enum : int32_t { SLOT_REBUILD_DS = 0, SLOT_BOTH = 1, SLOT_REBUILD_S = 2 };
 struct ChunkEnt {
-    int64_t tok0, nval;
+    int64_t tok0;
+    int32_t nval, mode;
+    int64_t slot;
+    int32_t nval_next, pad;
 };
 // chunk c (< chunk_off[N]): its sequence (the largest n < N with chunk_off[n] <= c), first token and
 // number of valid tokens
@@ -233,15 +248,23 @@ __device__ __forceinline__ ChunkAt chunk_at(const int64_t *seq_tok, const int64_
 // The chunk table of the per-(chunk, head) kernels, written once so that each of their workgroups finds its
 // chunk with one load instead of a chain of dependent ones.
 __global__ __launch_bounds__(256) void kda_bwd_chunks(const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off, int32_t N,
+                                                      const int64_t *__restrict__ chunk_off,
+                                                      const int64_t *__restrict__ half_off, int32_t N,
                                                       int64_t n_entries, ChunkEnt *__restrict__ ctab) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= n_entries) return;
-    ChunkEnt e = {0, 0};
+    ChunkEnt e = {0, 0, SLOT_BOTH, 0, 0, 0};
     if (c < chunk_off[N]) {
         const ChunkAt at = chunk_at(seq_tok, chunk_off, N, c);
+        const int64_t ci = c - chunk_off[at.n], nch = chunk_off[at.n + 1] - chunk_off[at.n];
         e.tok0 = at.tok0;
         e.nval = at.nval;
+        e.slot = half_off[at.n] + ci / 2;
+        e.mode = (ci & 1) ? SLOT_REBUILD_S : (ci == nch - 1 ? SLOT_BOTH : SLOT_REBUILD_DS);
+        if (e.mode == SLOT_REBUILD_DS) {
+            const int64_t left = seq_tok[at.n + 1] - (at.tok0 + CB);
+            e.nval_next = (int32_t)(left < CB ? left : CB);
+        }
     }
     ctab[c] = e;
 }
@@ -490,7 +513,8 @@ template <int K, int NW, bool OG, bool VBF, bool IOBF>
 __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v,
                                                       const float *__restrict__ fac, const float *__restrict__ S0,
                                                       const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                      const int64_t *__restrict__ chunk_off,
+                                                      const int64_t *__restrict__ half_off, int32_t H, int32_t V,
                                                       int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
                                                       float *__restrict__ Wbuf, const void *__restrict__ dout,
                                                       const void *__restrict__ zg, float *__restrict__ doe,
@@ -509,7 +533,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     bid /= nvt;
     const int h = (int)(bid % H);
     const int64_t n = bid / H;
-    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
+    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n], p0 = half_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
     const int col = vt * 16 * NW + 16 * w + m;
@@ -570,13 +594,16 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
                 cz[i] = raw_f<IOBF>(st.z[i]);
             }
         }
-        // the state entering the chunk, as [V/16][K/16][64][4] per chunk and head: slot l = m' + 16 q' of tile
-        // (column block, row block) holds row m' of the row block, columns 4 q' .. 4 q' + 3 of the column block
-        // (a quad transpose turns this lane's four rows of one column into one row's four columns); each store
-        // writes a whole 1 KiB tile
-        float *sp = Sbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + 4 * slot;
+        // the state entering the chunk, at even chunks of the sequence only (into the pair's slot), as
+        // [V/16][K/16][64][4] per slot and head: slot l = m' + 16 q' of tile (column block, row block) holds row
+        // m' of the row block, columns 4 q' .. 4 q' + 3 of the column block (a quad transpose turns this lane's
+        // four rows of one column into one row's four columns); each store writes a whole 1 KiB tile
+        if ((ci & 1) == 0) {
+            float *sp = Sbuf + ((p0 + (ci >> 1)) * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) +
+                        4 * slot;
 #pragma unroll
-        for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(sp + r * 256) = quad_transpose(S[r], m & 3);
+            for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(sp + r * 256) = quad_transpose(S[r], m & 3);
+        }
         lds_barrier();
         if (ci + 2 < nch) fetch(st, ci + 2);
         // X = V - K~ S (two independent product chains)
@@ -639,7 +666,8 @@ template <int K, int NW, bool DBF>
 __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ dout,
                                                       const float *__restrict__ fac, const float *__restrict__ dSf,
                                                       const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off, int32_t H, int32_t V,
+                                                      const int64_t *__restrict__ chunk_off,
+                                                      const int64_t *__restrict__ half_off, int32_t H, int32_t V,
                                                       int32_t nvt, float *__restrict__ dSbuf,
                                                       float *__restrict__ dWbuf, float *__restrict__ dS0) {
     using L = FacL<K>;
@@ -655,7 +683,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
     bid /= nvt;
     const int h = (int)(bid % H);
     const int64_t n = bid / H;
-    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n];
+    const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n], p0 = half_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
     const int col = vt * 16 * NW + 16 * w + m;
@@ -699,9 +727,13 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         f32x4 dO;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dO[i] = 4 * qq + i < nval ? raw_f<DBF>(st.d[i]) : 0.f;
-        float *dp = dSbuf + (c * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) + 4 * slot;
+        // dS' leaving the chunk, at odd chunks and the sequence's last (into the pair's slot)
+        if ((ci & 1) || ci == nch - 1) {
+            float *dp = dSbuf + ((p0 + (ci >> 1)) * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) +
+                        4 * slot;
 #pragma unroll
-        for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(dp + r * 256) = quad_transpose(dS[r], m & 3);
+            for (int r = 0; r < KT; ++r) *reinterpret_cast<f32x4 *>(dp + r * 256) = quad_transpose(dS[r], m & 3);
+        }
         lds_barrier();
         if (ci >= 2) fetch(st, ci - 2);
         // dW = P^T dO + Kc dS' (two independent product chains)
@@ -759,7 +791,13 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     constexpr int KT = K / 16, NZ = (KT + 3) / 4;  // 16-row tiles of K; tiles per wavefront in phase f
     constexpr int CPT = K / 16;                  // channels per thread in the per-(token, channel) phase
     __shared__ __align__(16) float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
-    __shared__ __align__(16) float sq[CB * K], sk[CB * K], sg[CB * K];
+    // Until phase f, a neighbour chunk's rows for rebuilding the state or state gradient this chunk does not have
+    // stored (the previous chunk's W in x0, or the next chunk's dO in x0 and dW in x1); from phase g on, q, k and
+    // g (held in registers until then).
+    constexpr int QKG = 3 * CB * K > 2 * CB * VM ? 3 * CB * K : 2 * CB * VM;
+    __shared__ __align__(16) float sqkg[QKG];
+    float *const x0 = sqkg, *const x1 = sqkg + CB * VM;
+    float *const sq = sqkg, *const sk = sqkg + CB * K, *const sg = sqkg + 2 * CB * K;
     __shared__ float sT[CB * CB], sM[CB * CB], sP[CB * CB], sAb[CB * CB], sdT[CB * CB], sdP[CB * CB];
     __shared__ float sY[CB * CB], sdA[CB * CB], sbdA[CB * CB], sb[CB], sdbT[CB], sdGC[K], sGC[K];
     const int tid = threadIdx.x;
@@ -771,13 +809,16 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     at.tok0 = ce.tok0;
     at.nval = (int)ce.nval;
     const int64_t sH = H, sV = V, ch0 = c * sH + h;
+    const bool rebuild_s = ce.mode == SLOT_REBUILD_S, rebuild_ds = ce.mode == SLOT_REBUILD_DS;  // block-uniform
+    const int64_t nb = rebuild_s ? c - 1 : c + 1;  // the neighbour chunk (same sequence) when one is rebuilt
     const float *blk = fac + ch0 * fac_floats(K);
     const int lane = tid & 63, wv = tid >> 6, m = lane & 15, qq = lane >> 4;
     // ---- a. loads, in runs of 4 columns, all issued before any is waited for; rows past the chunk's valid
     // tokens re-read its last valid row, and dO, q, k, g are zeroed there (X, W and dW are zero there already)
+    constexpr int RV = CB * V / 4, NV = (RV + CNT - 1) / CNT, RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
+    uint4 rq[NK], rk[NK], rg[NK];  // q, k, g of this chunk, written to LDS after phase f
     {
-        constexpr int RV = CB * V / 4, NV = (RV + CNT - 1) / CNT, RK = CB * K / 4, NK = (RK + CNT - 1) / CNT;
-        uint4 rdo[NV], rq[NK], rk[NK], rg[NK];
+        uint4 rdo[NV];
         f32x4 rx[NV], rw[NV], rdw[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
@@ -802,6 +843,22 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
                 rg[j] = ld_raw4(g, idx, io_bf);
             }
         }
+        uint4 rxo[NV];  // the next chunk's dO (raw), or unused
+        f32x4 rxw[NV];  // the previous chunk's W, or the next chunk's dW
+        if (ce.mode != SLOT_BOTH) {
+            const float *src = rebuild_s ? Wbuf : dWbuf;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int e = tid + CNT * j, t = e / (V / 4), c4 = e % (V / 4);
+                if (e < RV) {
+                    rxw[j] = *reinterpret_cast<const f32x4 *>(src + ((nb * sH + h) * CB + t) * sV + 4 * c4);
+                    if (rebuild_ds) {
+                        const int tt = t < ce.nval_next ? t : ce.nval_next - 1;
+                        rxo[j] = ld_raw4(dout, ((at.tok0 + CB + tt) * sH + h) * sV + 4 * c4, do_bf);
+                    }
+                }
+            }
+        }
         const float fT = blk[L::TT + tid], fM = blk[L::MM + tid], fP = blk[L::PP + tid], fA = blk[L::AB + tid];
         const float fG = tid < K ? blk[L::GC + tid] : 0.f;
         const uint2 fb = ld_raw1(beta, (at.tok0 + (tid < at.nval ? tid % CB : at.nval - 1)) * sH + h, io_bf);
@@ -817,18 +874,15 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
                 *reinterpret_cast<f32x4 *>(b3 + o) = rdw[j];
             }
         }
+        if (ce.mode != SLOT_BOTH) {
 #pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int e = tid + CNT * j, t = e / (K / 4);
-            if (e < RK) {
-                const bool ok = t < at.nval;
-                const f32x4 gv = raw4_f(rg[j], io_bf);
-                f32x4 ld;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
-                reinterpret_cast<f32x4 *>(sq)[e] = ok ? raw4_f(rq[j], qk_bf) : z;
-                reinterpret_cast<f32x4 *>(sk)[e] = ok ? raw4_f(rk[j], qk_bf) : z;
-                reinterpret_cast<f32x4 *>(sg)[e] = ok ? ld : z;
+            for (int j = 0; j < NV; ++j) {
+                const int e = tid + CNT * j, t = e / (V / 4), c4 = e % (V / 4);
+                if (e < RV) {
+                    const int o = t * VM + 4 * c4;
+                    *reinterpret_cast<f32x4 *>(x0 + o) = rebuild_s ? rxw[j] : (t < ce.nval_next ? raw4_f(rxo[j], do_bf) : z);
+                    if (rebuild_ds) *reinterpret_cast<f32x4 *>(x1 + o) = rxw[j];
+                }
             }
         }
         sT[tid] = fT;
@@ -842,16 +896,25 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     // ---- the rows of S and dS' that phase f multiplies: all issued here (and kept here by the scheduling
     // barrier), so that their latency overlaps phases b to e. Row 16 rt + m, columns 16 sv + 4 qq .. +3 are
     // slot l of tile (sv, rt) in the passes' [V/16][K/16][64][4] order.
-    f32x4 s4r[NZ][V / 16], d4r[NZ][V / 16];
+    // With one of them rebuilt from a neighbour chunk, that chunk's factors come too: Gc of this lane's key row
+    // and the o2-order operand of the rebuild (Kc of the previous chunk, or Q~ and -Wk of the next).
+    f32x4 s4r[NZ][V / 16], d4r[NZ][V / 16], nbB0[NZ], nbB1[NZ];
+    float nbG[NZ];
 #pragma unroll
     for (int z = 0; z < NZ; ++z) {
         const int rt = wv + 4 * z;
         if (rt < KT) {  // wavefront-uniform
-            const int64_t so = ch0 * (int64_t)(K * V) + rt * 256 + 4 * lane;
+            const int64_t so = (ce.slot * sH + h) * (int64_t)(K * V) + rt * 256 + 4 * lane;
 #pragma unroll
             for (int sv = 0; sv < V / 16; ++sv) {
                 s4r[z][sv] = *reinterpret_cast<const f32x4 *>(Sbuf + so + sv * (KT * 256));
                 d4r[z][sv] = *reinterpret_cast<const f32x4 *>(dSbuf + so + sv * (KT * 256));
+            }
+            if (ce.mode != SLOT_BOTH) {
+                const float *nblk = fac + (nb * sH + h) * fac_floats(K);
+                nbG[z] = nblk[L::GC + 16 * rt + m];
+                nbB0[z] = *reinterpret_cast<const f32x4 *>(nblk + (rebuild_s ? L::KC2 : L::QG2) + (rt * 64 + lane) * 4);
+                if (rebuild_ds) nbB1[z] = *reinterpret_cast<const f32x4 *>(nblk + L::NWK2 + (rt * 64 + lane) * 4);
             }
         }
     }
@@ -929,6 +992,40 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         sdA[tid] = a;
         sbdA[tid] = sb[i] * a;
     }
+    // ---- the state or state gradient this chunk does not have stored, rebuilt from its neighbour's, in the
+    // contractions' order. The accumulator of a [16 V][16 K] tile of S^T (or dS'^T) holds rows 16 rt + m of S,
+    // columns 16 sv + 4 qq + i: exactly the order phase f reads. So
+    //   S^T   = S_prev^T diag(Gc_prev) + W_prev^T Kc_prev,
+    //   dS'^T = dS'_next^T diag(Gc_next) + dO_next^T Q~_next + dW_next^T (-Wk_next)
+    // are 16x16x4 products with A = rows 4 qq + j of x0 / x1 at column 16 sv + m and B the o2-order factor.
+    if (ce.mode != SLOT_BOTH) {
+#pragma unroll
+        for (int z = 0; z < NZ; ++z) {
+            const int rt = wv + 4 * z;
+            if (rt < KT) {  // wavefront-uniform
+#pragma unroll
+                for (int sv = 0; sv < V / 16; ++sv) {
+                    float4 a0;
+                    a0.x = x0[(4 * qq + 0) * VM + 16 * sv + m];
+                    a0.y = x0[(4 * qq + 1) * VM + 16 * sv + m];
+                    a0.z = x0[(4 * qq + 2) * VM + 16 * sv + m];
+                    a0.w = x0[(4 * qq + 3) * VM + 16 * sv + m];
+                    if (rebuild_s) {
+                        s4r[z][sv] = mfma_x4(s4r[z][sv] * nbG[z], a0, nbB0[z]);
+                    } else {
+                        float4 a1;
+                        a1.x = x1[(4 * qq + 0) * VM + 16 * sv + m];
+                        a1.y = x1[(4 * qq + 1) * VM + 16 * sv + m];
+                        a1.z = x1[(4 * qq + 2) * VM + 16 * sv + m];
+                        a1.w = x1[(4 * qq + 3) * VM + 16 * sv + m];
+                        d4r[z][sv] = mfma_x4(mfma_x4(d4r[z][sv] * nbG[z], a0, nbB0[z]), a1, nbB1[z]);
+                    }
+                }
+            }
+        }
+        mfma_fence_all(s4r);
+        mfma_fence_all(d4r);
+    }
     // ---- f. contractions over V on the matrix cores: (dO S^T), (dX S^T), (W dS'^T) [CB][K], tile rt of 16 key
     // rows with wavefront rt % 4, and rowsum(S * dS') alongside. Lane l = m + 16 qq: k slot qq of product j
     // stands for column 16 s + 4 qq + j, so one float4 of a row of S or dS' (and of dO, dX, W) serves four
@@ -966,7 +1063,21 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         fsd[z] += __shfl_xor(fsd[z], 16);  // the four lanes of a key row (qq = 0..3)
         fsd[z] += __shfl_xor(fsd[z], 32);
     }
-    __syncthreads();  // every read of b0..b3 is done
+    __syncthreads();  // every read of b0..b3 and x0, x1 is done
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int e = tid + CNT * j, t = e / (K / 4);
+        if (e < RK) {
+            const bool ok = t < at.nval;
+            const f32x4 zz = zero4(), gv = raw4_f(rg[j], io_bf);
+            f32x4 ld;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ld[i] = log_decay_of(gv[i], gate_sig);
+            reinterpret_cast<f32x4 *>(sq)[e] = ok ? raw4_f(rq[j], qk_bf) : zz;
+            reinterpret_cast<f32x4 *>(sk)[e] = ok ? raw4_f(rk[j], qk_bf) : zz;
+            reinterpret_cast<f32x4 *>(sg)[e] = ok ? ld : zz;
+        }
+    }
 #pragma unroll
     for (int z = 0; z < NZ; ++z) {
         const int rt = wv + 4 * z;
@@ -1404,8 +1515,8 @@ __global__ __launch_bounds__(256) void kda_bwd_convw_reduce(const float *__restr
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdWs {
-    int64_t *seq_tok, *seg_off;
-    ChunkEnt *ctab;  // per chunk: first token, valid tokens
+    int64_t *seq_tok, *seg_off, *half_off;
+    ChunkEnt *ctab;  // per chunk: first token, valid tokens, state slot
     // the chunk form: factor blocks per (chunk, head); the state entering and the state gradient leaving every
     // (chunk, head) [K][V]; X, W, dW per (chunk, head) [CB][V]; do * sigmoid(z) per token (output gate)
     float *fac, *Sb, *dSb, *Xb, *Wb, *dWb, *doe;
@@ -1428,10 +1539,13 @@ BwdWs bwd_ptrs(void *ws, int64_t n_tokens, int32_t N, int64_t max_chunks, int32_
     const size_t ch = (size_t)max_chunks * H;
     r.seq_tok = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.seg_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
+    r.half_off = (int64_t *)take(sizeof(int64_t) * ((size_t)N + 1));
     r.ctab = (ChunkEnt *)take(sizeof(ChunkEnt) * (size_t)max_chunks);
+    // state slots: ceil(chunks / 2) per sequence, at most (chunks + sequences) / 2 in all
+    const size_t slots = ((size_t)max_chunks + (size_t)N + 1) / 2 * (size_t)H;
     r.fac = (float *)take(sizeof(float) * ch * (size_t)fac_floats(K));
-    r.Sb = (float *)take(sizeof(float) * ch * K * V);
-    r.dSb = (float *)take(sizeof(float) * ch * K * V);
+    r.Sb = (float *)take(sizeof(float) * slots * K * V);
+    r.dSb = (float *)take(sizeof(float) * slots * K * V);
     r.Xb = (float *)take(sizeof(float) * ch * CB * V);
     r.Wb = (float *)take(sizeof(float) * ch * CB * V);
     r.dWb = (float *)take(sizeof(float) * ch * CB * V);
@@ -1469,7 +1583,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
     if (npass_blocks > 0) {
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
-                               a.S0, w.seq_tok, w.seg_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate, w.doe,
+                               a.S0, w.seq_tok, w.seg_off, w.half_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate, w.doe,
                                a.d_o_gate);
         };
         if (og) {
@@ -1482,7 +1596,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         auto rev = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st,
                                og ? (const void *)w.doe : a.dout, (const float *)w.fac, a.dS_final, w.seq_tok,
-                               w.seg_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
+                               w.seg_off, w.half_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
         };
         (!og && io_bf) ? rev(kda_cb_rev<K, NW, true>) : rev(kda_cb_rev<K, NW, false>);
     }
@@ -1514,10 +1628,10 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
     BwdWs w = bwd_ptrs(a.workspace, n_tok, a.num_seqs, a.max_segs, a.H, K, V, norm, conv);
     const int64_t T_row = a.cu_seqlens ? 0 : a.T;
     hipLaunchKernelGGL(kda_bwd_table, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.num_seqs, T_row, n_tok,
-                       w.seq_tok, w.seg_off);
+                       w.seq_tok, w.seg_off, w.half_off);
     if (a.max_segs > 0)
         hipLaunchKernelGGL(kda_bwd_chunks, dim3(blocks_of(a.max_segs)), dim3(256), 0, st, (const int64_t *)w.seq_tok,
-                           (const int64_t *)w.seg_off, a.num_seqs, a.max_segs, w.ctab);
+                           (const int64_t *)w.seg_off, (const int64_t *)w.half_off, a.num_seqs, a.max_segs, w.ctab);
     if (!norm && !conv) {
         bwd_core<K, V>(a, w, a.q, a.k, a.io_bf16, a.v, a.io_bf16, a.dv, a.dq, a.dk, st);
         return hipGetLastError();
