@@ -394,10 +394,12 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
  *           qk_norm, conv). Per 16-token chunk and head (at most
  *           ceil(T / 16) B chunks, one more per sequence when packed) it holds
- *           the chunk's factors (4 * 16 * K + 4 * 16 * 16 + K floats, rounded
- *           up to 64), the state entering it and the state's gradient leaving
- *           it (K * V floats each) and three 16 * V blocks. It also holds
- *           B * T * H * V floats for dL/do * sigmoid(z) with an output gate.
+ *           the chunk's factors (6 * 16 * K + 7 * 16 * 16 + K floats, rounded
+ *           up to 64) and three 16 * V blocks; per pair of chunks of a
+ *           sequence and head, one state and one state gradient (K * V
+ *           floats each; at most (chunks + num_seqs + 1) / 2 pairs). It also
+ *           holds B * T * H * V floats for dL/do * sigmoid(z) with an output
+ *           gate.
  *           With a prologue it adds the prologue's fp32 outputs and the
  *           recurrence's gradients with respect to them (4 B T H K floats,
  *           plus 2 B T H V with a convolution), 2 B T H norm factors with
@@ -408,6 +410,11 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  * call is needed. All arithmetic is fp32 and the result is deterministic
  * (fixed summation order). Outputs may not alias the inputs or each other.
  * Errors as for kda_chunk_fwd (chunk does not apply).
+ * Long sequences can be taken in segments, with the workspace bounded by the
+ * segment length: the forward over segments 1..i-1 (kda_chunk_fwd's S_final)
+ * gives segment i's S0, and the backward runs the segments last to first,
+ * each one's dS0 passed as the previous segment's dS_final. The chained
+ * gradients equal one call's up to rounding.
  */
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                      kda_qk_norm_t qk_norm, kda_conv_t conv);

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from kda_gated_delta_chunk_amd import _lib, chunk_bwd
+from kda_gated_delta_chunk_amd import _lib, chunk_bwd, chunk_fwd
 from kda_gated_delta_chunk_amd import synth
 from tests.parity import TOL_FP32, err
 
@@ -152,6 +152,34 @@ def test_bwd_mild_decay_long_carry():
     _announce("bwd_mild", T=300, H=2, K=128, V=128, seed=75)
     inp = _inputs(1, 300, 2, 128, 128, "fp32", 75, g_shift=-6.0)
     _compare(_gpu(inp), _oracle(inp))
+
+
+def test_bwd_segments_chained_through_the_states():
+    # A long sequence backpropagated in segments: the forward of the first segment gives the state entering the
+    # second; the second's backward gives dL/d(that state), which is the first segment's dL/dS_final. The
+    # chained gradients equal one call's (to fp32 rounding), with workspace bounded by the segment length.
+    _announce("bwd_segments", T=1000, split=392, H=3, K=128, V=128, seed=77)
+    inp = _inputs(1, 1000, 3, 128, 128, "fp32", 77, g_shift=-6.0)
+    whole = _gpu(inp)
+    T1 = 392
+
+    def part(a, b):
+        seg = {n: inp[n][:, a:b].contiguous() for n in ("q", "k", "v", "g", "beta", "do")}
+        seg["cu_seqlens"] = None
+        return seg
+
+    _, S_mid = chunk_fwd(*(inp[n][:, :T1].contiguous() for n in ("q", "k", "v", "g", "beta")), S0=inp["S0"])
+    second = part(T1, 1000)
+    second["S0"], second["dS_final"] = S_mid, inp["dS_final"]
+    g2 = _gpu(second)
+    first = part(0, T1)
+    first["S0"], first["dS_final"] = inp["S0"], g2["dS0"]
+    g1 = _gpu(first)
+    errs = {n: err(torch.cat([g1[n], g2[n]], dim=1), whole[n]) for n in ("dq", "dk", "dv", "dg", "dbeta")}
+    errs["dS0"] = err(g1["dS0"], whole["dS0"])
+    print("  errors " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL_FP32, (n, e)
 
 
 def test_bwd_is_deterministic():
