@@ -394,7 +394,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
  *           qk_norm, conv). Per 16-token chunk and head (at most
  *           ceil(T / 16) B chunks, one more per sequence when packed) it holds
- *           the chunk's factors (6 * 16 * K + 7 * 16 * 16 + K floats, rounded
+ *           the chunk's factors (4 * 16 * K + 7 * 16 * 16 + K floats, rounded
  *           up to 64) and three 16 * V blocks; per pair of chunks of a
  *           sequence and head, one state and one state gradient (K * V
  *           floats each; at most (chunks + num_seqs + 1) / 2 pairs). It also

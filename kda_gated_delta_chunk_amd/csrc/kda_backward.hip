@@ -146,10 +146,12 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
 // by e^{b_i - b_j} summed from the decays between them, instead of as +E at i and -E at j, which in fp32
 // left the rounding of e^{+-b} (|b| up to 80) in dg. After the chunk table, the chain runs in four launches:
 //   kda_cb_factors  (chunk, head): the factors above;
-//   kda_cb_fwd      (sequence, head, 16 NW columns): the states S entering every chunk, X and W (and with an
-//                   output gate the core output, do * sigmoid(z) and dL/dz);
-//   kda_cb_rev      (sequence, head, 16 NW columns): dS' leaving every chunk, dW, and dL/dS0;
-//   kda_cb_grad     (chunk, head): dq, dk, dv, dg, dbeta from the stored S, dS', X, W, dW.
+//   kda_cb_fwd      (sequence, head, 16 NW columns): X and W of every chunk, the state S entering every even
+//                   chunk of the sequence (and with an output gate the core output, do * sigmoid(z) and dL/dz);
+//   kda_cb_rev      (sequence, head, 16 NW columns): dW of every chunk, dS' leaving every odd chunk and the
+//                   last, and dL/dS0;
+//   kda_cb_grad     (chunk, head): dq, dk, dv, dg, dbeta from the stored S or dS' (rebuilding the other from
+//                   the neighbour chunk's), X, W, dW.
 // Each column of S and of dS evolves on its own (decay scales rows), so the two sequential passes split V
 // into tiles: each wavefront keeps a K x 16 slice of the state as matrix-core accumulator tiles. All
 // arithmetic is fp32 (the products as v_mfma_f32_16x16x4f32), deterministic (fixed summation orders, no
@@ -162,21 +164,29 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
 // X[m][16 r + 4 q + i] (i = 0..3), A for X times a state; "o2" arrays hold X^T the same way, lane l of group r
 // holding X[4 q + i][16 r + m], A for X^T times a [CB][16] tile in accumulator layout; "t" arrays of a
 // [CB][CB] matrix Y are [64][4] with lane l holding Y[m][4 q + i], and "tT" arrays hold Y^T
-// (Y[4 q + i][m]). The row-major T, M, P, Ab and Gc serve the local-gradient kernel.
+// (Y[4 q + i][m]). Kc and Q~ are stored in their o2 order only; a pass that needs their o1 order reads it
+// from LDS. The row-major T, M, P, Ab and Gc serve the local-gradient kernel.
 template <int K> struct FacL {
     static constexpr int NKG1 = 0;                   // -K~, o1: X = V - K~ S
-    static constexpr int QG1 = CB * K;               // Q~, o1: O = Q~ S + P W
-    static constexpr int KC1 = 2 * CB * K;           // Kc, o1: dW = P^T dO + Kc dS'
-    static constexpr int KC2 = 3 * CB * K;           // Kc, o2: S' = diag(Gc) S + Kc^T W
-    static constexpr int QG2 = 4 * CB * K;           // Q~, o2: dS = diag(Gc) dS' + Q~^T dO - Wk^T dW
-    static constexpr int NWK2 = 5 * CB * K;          // -Wk, o2
-    static constexpr int T1 = 6 * CB * K;            // T, t: W = T X
+    static constexpr int KC2 = CB * K;               // Kc, o2: S' = diag(Gc) S + Kc^T W; dW = P^T dO + Kc dS' (o1)
+    static constexpr int QG2 = 2 * CB * K;           // Q~, o2: dS = diag(Gc) dS' + Q~^T dO - Wk^T dW; O = Q~ S + P W (o1)
+    static constexpr int NWK2 = 3 * CB * K;          // -Wk, o2
+    static constexpr int T1 = 4 * CB * K;            // T, t: W = T X
     static constexpr int P1 = T1 + CB * CB;          // P, t
     static constexpr int PT1 = P1 + CB * CB;         // P, tT: P^T dO
     static constexpr int TT = PT1 + CB * CB, PP = TT + CB * CB, MM = PP + CB * CB, AB = MM + CB * CB;
     static constexpr int GC = AB + CB * CB;
 };
-constexpr int64_t fac_floats(int K) { return ((6 * CB * K + 7 * CB * CB + K) + 63) / 64 * 64; }
+constexpr int64_t fac_floats(int K) { return ((4 * CB * K + 7 * CB * CB + K) + 63) / 64 * 64; }
+
+// An o2-order array staged into LDS with one float4 of padding after every 16 (padded_floats(n) floats for n),
+// so that the o1 order of the same matrix (four scalars per lane) reads without bank conflicts.
+constexpr int padded_floats(int n) { return n + n / 16; }
+// the o1 values of lane m + 16 q, group r (X[m][16 r + 4 q + i], i = 0..3) from the padded o2 array
+__device__ __forceinline__ float4 o1_from_padded_o2(const float *base, int r, int m, int q) {
+    const float *p = base + 4 * (68 * r + 17 * (m >> 2) + 4 * q) + (m & 3);
+    return make_float4(p[0], p[4], p[8], p[12]);
+}
 
 // element i of an array of bf16 (bf) or fp32 values
 __device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
@@ -450,8 +460,6 @@ __global__ __launch_bounds__(CNT) void kda_cb_factors(const void *__restrict__ q
         const int o1 = mm * KP + 16 * r + 4 * q4, o2 = 4 * q4 * KP + 16 * r + mm;
         const f32x4 kg = *reinterpret_cast<const f32x4 *>(sKG + o1);
         *reinterpret_cast<f32x4 *>(blk + L::NKG1 + 4 * e4) = -kg;
-        *reinterpret_cast<f32x4 *>(blk + L::QG1 + 4 * e4) = *reinterpret_cast<const f32x4 *>(sQG + o1);
-        *reinterpret_cast<f32x4 *>(blk + L::KC1 + 4 * e4) = *reinterpret_cast<const f32x4 *>(sKc + o1);
         f32x4 kc2, qg2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -503,6 +511,14 @@ struct Stage {
             if (e < NFL / 4) reinterpret_cast<f32x4 *>(dst)[e] = v[j];
         }
     }
+    // into an o2 array's padded LDS layout
+    __device__ __forceinline__ void store_padded(float *dst, int tid) const {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int e = tid + NT * j;
+            if (e < NFL / 4) reinterpret_cast<f32x4 *>(dst)[e + (e >> 4)] = v[j];
+        }
+    }
 };
 
 // ---- forward states: one workgroup of NW wavefronts per (sequence, head, 16 NW columns); wavefront w owns
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
     __shared__ __align__(16) float fKG[FK];
     __shared__ __align__(16) float fKc[FK];
-    __shared__ __align__(16) float fQG[OG ? FK : 4];
+    __shared__ __align__(16) float fQG[OG ? padded_floats(FK) : 4];  // Q~, o2 order padded, read in o1 order
     __shared__ __align__(16) float fT[CB * CB];
     __shared__ __align__(16) float fP[OG ? CB * CB : 4];
     __shared__ __align__(16) float sGC[K];
@@ -558,7 +574,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         const float *blk = fac + (c * sH + h) * fac_floats(K);
         st.KG.load(blk + L::NKG1, tid);
         st.Kc.load(blk + L::KC2, tid);
-        if constexpr (OG) st.QG.load(blk + L::QG1, tid);
+        if constexpr (OG) st.QG.load(blk + L::QG2, tid);
         st.T.load(blk + L::T1, tid);
         if constexpr (OG) st.P.load(blk + L::P1, tid);
         st.GC.load(blk + L::GC, tid);
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         lds_barrier();  // the previous chunk's LDS reads are done
         st.KG.store(fKG, tid);
         st.Kc.store(fKc, tid);
-        if constexpr (OG) st.QG.store(fQG, tid);
+        if constexpr (OG) st.QG.store_padded(fQG, tid);
         st.T.store(fT, tid);
         if constexpr (OG) st.P.store(fP, tid);
         st.GC.store(sGC, tid);
@@ -624,8 +640,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
             f32x4 O0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fP)[lane], W), O1 = zero4();
 #pragma unroll
             for (int r = 0; r < KT; r += 2) {
-                O0 = mfma_x4(O0, reinterpret_cast<const float4 *>(fQG)[r * 64 + lane], S[r]);
-                O1 = mfma_x4(O1, reinterpret_cast<const float4 *>(fQG)[(r + 1) * 64 + lane], S[r + 1]);
+                O0 = mfma_x4(O0, o1_from_padded_o2(fQG, r, m, qq), S[r]);
+                O1 = mfma_x4(O1, o1_from_padded_o2(fQG, r + 1, m, qq), S[r + 1]);
             }
             mfma_fence(O0, O1);
             const f32x4 O = O0 + O1;
@@ -672,7 +688,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
                                                       float *__restrict__ dWbuf, float *__restrict__ dS0) {
     using L = FacL<K>;
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
-    __shared__ __align__(16) float fKc[FK];
+    __shared__ __align__(16) float fKc[padded_floats(FK)];  // Kc, o2 order padded, read in o1 order
     __shared__ __align__(16) float fQG[FK];
     __shared__ __align__(16) float fWk[FK];
     __shared__ __align__(16) float fPT[CB * CB];
@@ -704,7 +720,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         const float *blk = fac + (c * sH + h) * fac_floats(K);
-        st.Kc.load(blk + L::KC1, tid);
+        st.Kc.load(blk + L::KC2, tid);
         st.QG.load(blk + L::QG2, tid);
         st.Wk.load(blk + L::NWK2, tid);
         st.PT.load(blk + L::PT1, tid);
@@ -719,7 +735,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         lds_barrier();
-        st.Kc.store(fKc, tid);
+        st.Kc.store_padded(fKc, tid);
         st.QG.store(fQG, tid);
         st.Wk.store(fWk, tid);
         st.PT.store(fPT, tid);
@@ -740,8 +756,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         f32x4 dW0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fPT)[lane], dO), dW1 = zero4();
 #pragma unroll
         for (int r = 0; r < KT; r += 2) {
-            dW0 = mfma_x4(dW0, reinterpret_cast<const float4 *>(fKc)[r * 64 + lane], dS[r]);
-            dW1 = mfma_x4(dW1, reinterpret_cast<const float4 *>(fKc)[(r + 1) * 64 + lane], dS[r + 1]);
+            dW0 = mfma_x4(dW0, o1_from_padded_o2(fKc, r, m, qq), dS[r]);
+            dW1 = mfma_x4(dW1, o1_from_padded_o2(fKc, r + 1, m, qq), dS[r + 1]);
         }
         mfma_fence(dW0, dW1);
         const f32x4 dW = dW0 + dW1;
@@ -1183,22 +1199,32 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         }
     }
     __syncthreads();
+    // half 0 forms the results in place of half 1's sums (same thread, same addresses); then every thread
+    // stores 16-byte runs of the valid token rows
     if (half == 0) {
         float F = 0.f;
 #pragma unroll
         for (int u = 0; u < CB; ++u) {
             F += aD[u] + b2[u * VM + gch];
-            if (u < at.nval) {
-                const int64_t idx = ((at.tok0 + u) * sH + h) * K + gch;
-                float dgv = bs[u] + F;
-                if (gate_sig) {  // d(-5 sigmoid(x))/dx = -5 s (1 - s) = l (1 + l / 5) with l = -5 s
-                    const float l = sg[u * K + gch];
-                    dgv *= l * (1.f + 0.2f * l);
-                }
-                dq[idx] = aq[u] + b0[u * VM + gch];
-                dk[idx] = ak[u] + b1[u * VM + gch];
-                dg[idx] = dgv;
+            float dgv = bs[u] + F;
+            if (gate_sig) {  // d(-5 sigmoid(x))/dx = -5 s (1 - s) = l (1 + l / 5) with l = -5 s
+                const float l = sg[u * K + gch];
+                dgv *= l * (1.f + 0.2f * l);
             }
+            b0[u * VM + gch] += aq[u];
+            b1[u * VM + gch] += ak[u];
+            b2[u * VM + gch] = dgv;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < CB * K / 4; e += CNT) {
+        const int u = e / (K / 4), c4 = e % (K / 4);
+        if (u < at.nval) {
+            const int64_t idx = ((at.tok0 + u) * sH + h) * K + 4 * c4;
+            const int o = u * VM + 4 * c4;
+            *reinterpret_cast<f32x4 *>(dq + idx) = *reinterpret_cast<const f32x4 *>(b0 + o);
+            *reinterpret_cast<f32x4 *>(dk + idx) = *reinterpret_cast<const f32x4 *>(b1 + o);
+            *reinterpret_cast<f32x4 *>(dg + idx) = *reinterpret_cast<const f32x4 *>(b2 + o);
         }
     }
 }

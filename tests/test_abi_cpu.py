@@ -370,13 +370,13 @@ def test_chunk_bwd_rejects(kw, expect):
 def test_bwd_workspace_bytes():
     lib = _lib.load()
     ws = lib.kda_chunk_bwd_workspace_bytes
-    # per (16-token chunk, head): a factor block (six 16 x K operand arrays, seven 16 x 16 ones and K decays,
+    # per (16-token chunk, head): a factor block (four 16 x K operand arrays, seven 16 x 16 ones and K decays,
     # rounded up to 64 floats) and X, W, dW (16 x V each); per pair of chunks of a sequence and head, one state
     # and one state gradient (K x V each; at most (chunks + sequences + 1) / 2 pairs); per token and head:
     # do * sigmoid(z) (V floats, used with an output gate)
     B, T, H, K, V = 2, 64, 3, 32, 64
     nc = B * (T // 16)
-    fac = -(-(6 * 16 * K + 7 * 16 * 16 + K) // 64) * 64
+    fac = -(-(4 * 16 * K + 7 * 16 * 16 + K) // 64) * 64
     pairs = (nc + B + 1) // 2
     need = nc * H * (fac + 3 * 16 * V) * 4 + pairs * H * 2 * K * V * 4 + B * T * H * V * 4
     assert need <= ws(B, T, H, K, V, B, 0, 0) <= need + 10 * 256
