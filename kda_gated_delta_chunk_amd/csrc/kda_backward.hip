@@ -179,13 +179,14 @@ template <int K> struct FacL {
 };
 constexpr int64_t fac_floats(int K) { return ((4 * CB * K + 7 * CB * CB + K) + 63) / 64 * 64; }
 
-// An o2-order array staged into LDS with one float4 of padding after every 16 (padded_floats(n) floats for n),
-// so that the o1 order of the same matrix (four scalars per lane) reads without bank conflicts.
+// A matrix stored in o2 order, staged into LDS in its o1 order with 4 floats of padding after every 64
+// (padded_floats(n) floats for n): the scattered writes of the conversion and the float4 reads of the o1
+// order both fall in distinct banks.
 constexpr int padded_floats(int n) { return n + n / 16; }
-// the o1 values of lane m + 16 q, group r (X[m][16 r + 4 q + i], i = 0..3) from the padded o2 array
-__device__ __forceinline__ float4 o1_from_padded_o2(const float *base, int r, int m, int q) {
-    const float *p = base + 4 * (68 * r + 17 * (m >> 2) + 4 * q) + (m & 3);
-    return make_float4(p[0], p[4], p[8], p[12]);
+__device__ __forceinline__ int o1_padded(int i) { return i + ((i >> 6) << 2); }
+// the o1 values of lane m + 16 q, group r (X[m][16 r + 4 q + i], i = 0..3)
+__device__ __forceinline__ float4 o1_padded_read(const float *base, int r, int m, int q) {
+    return *reinterpret_cast<const float4 *>(base + 272 * r + 68 * q + 4 * m);
 }
 
 // element i of an array of bf16 (bf) or fp32 values
@@ -511,12 +512,18 @@ struct Stage {
             if (e < NFL / 4) reinterpret_cast<f32x4 *>(dst)[e] = v[j];
         }
     }
-    // into an o2 array's padded LDS layout
-    __device__ __forceinline__ void store_padded(float *dst, int tid) const {
+    // an o2-order array into its o1 order, padded (o1_padded): group e = 64 r + m' + 16 q' of the o2 order holds
+    // X[4 q' + i][16 r + m'] (i = 0..3), which the o1 order keeps at (64 r + 4 q' + i + 16 (m' / 4)) 4 + m' % 4
+    __device__ __forceinline__ void store_o2_as_o1(float *dst, int tid) const {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int e = tid + NT * j;
-            if (e < NFL / 4) reinterpret_cast<f32x4 *>(dst)[e + (e >> 4)] = v[j];
+            if (e < NFL / 4) {
+                const int r = e >> 6, mm = e & 15, q4 = (e >> 4) & 3;
+                const int base = (64 * r + 4 * q4 + 16 * (mm >> 2)) * 4 + (mm & 3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[o1_padded(base + 4 * i)] = v[j][i];
+            }
         }
     }
 };
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
     __shared__ __align__(16) float fKG[FK];
     __shared__ __align__(16) float fKc[FK];
-    __shared__ __align__(16) float fQG[OG ? padded_floats(FK) : 4];  // Q~, o2 order padded, read in o1 order
+    __shared__ __align__(16) float fQG[OG ? padded_floats(FK) : 4];  // Q~ in o1 order, padded
     __shared__ __align__(16) float fT[CB * CB];
     __shared__ __align__(16) float fP[OG ? CB * CB : 4];
     __shared__ __align__(16) float sGC[K];
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         lds_barrier();  // the previous chunk's LDS reads are done
         st.KG.store(fKG, tid);
         st.Kc.store(fKc, tid);
-        if constexpr (OG) st.QG.store_padded(fQG, tid);
+        if constexpr (OG) st.QG.store_o2_as_o1(fQG, tid);
         st.T.store(fT, tid);
         if constexpr (OG) st.P.store(fP, tid);
         st.GC.store(sGC, tid);
@@ -640,8 +647,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
             f32x4 O0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fP)[lane], W), O1 = zero4();
 #pragma unroll
             for (int r = 0; r < KT; r += 2) {
-                O0 = mfma_x4(O0, o1_from_padded_o2(fQG, r, m, qq), S[r]);
-                O1 = mfma_x4(O1, o1_from_padded_o2(fQG, r + 1, m, qq), S[r + 1]);
+                O0 = mfma_x4(O0, o1_padded_read(fQG, r, m, qq), S[r]);
+                O1 = mfma_x4(O1, o1_padded_read(fQG, r + 1, m, qq), S[r + 1]);
             }
             mfma_fence(O0, O1);
             const f32x4 O = O0 + O1;
@@ -688,7 +695,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
                                                       float *__restrict__ dWbuf, float *__restrict__ dS0) {
     using L = FacL<K>;
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
-    __shared__ __align__(16) float fKc[padded_floats(FK)];  // Kc, o2 order padded, read in o1 order
+    __shared__ __align__(16) float fKc[padded_floats(FK)];  // Kc in o1 order, padded
     __shared__ __align__(16) float fQG[FK];
     __shared__ __align__(16) float fWk[FK];
     __shared__ __align__(16) float fPT[CB * CB];
@@ -735,7 +742,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         const int64_t c = c0 + ci, tok0 = t0 + (int64_t)ci * CB;
         const int nval = (int)(t1 - tok0 < CB ? t1 - tok0 : CB);
         lds_barrier();
-        st.Kc.store_padded(fKc, tid);
+        st.Kc.store_o2_as_o1(fKc, tid);
         st.QG.store(fQG, tid);
         st.Wk.store(fWk, tid);
         st.PT.store(fPT, tid);
@@ -756,8 +763,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
         f32x4 dW0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fPT)[lane], dO), dW1 = zero4();
 #pragma unroll
         for (int r = 0; r < KT; r += 2) {
-            dW0 = mfma_x4(dW0, o1_from_padded_o2(fKc, r, m, qq), dS[r]);
-            dW1 = mfma_x4(dW1, o1_from_padded_o2(fKc, r + 1, m, qq), dS[r + 1]);
+            dW0 = mfma_x4(dW0, o1_padded_read(fKc, r, m, qq), dS[r]);
+            dW1 = mfma_x4(dW1, o1_padded_read(fKc, r + 1, m, qq), dS[r + 1]);
         }
         mfma_fence(dW0, dW1);
         const f32x4 dW = dW0 + dW1;
