@@ -88,9 +88,8 @@ __global__ __launch_bounds__(1024) void kda_bwd_table(const int32_t *__restrict_
     }
 }
 
-// ------------------------------------------------------------------ lane sums
-// (every control used here has a source lane for every lane within its quad; bound_ctrl set lets the
-// compiler fold the move into the consuming add)
+// ------------------------------------------------------------------ lane exchanges
+// (every control used here has a source lane for every lane within its quad)
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
@@ -189,10 +188,6 @@ __device__ __forceinline__ float4 o1_padded_read(const float *base, int r, int m
     return *reinterpret_cast<const float4 *>(base + 272 * r + 68 * q + 4 * m);
 }
 
-// element i of an array of bf16 (bf) or fp32 values
-__device__ __forceinline__ float ld_as(const void *p, int64_t i, bool bf) {
-    return bf ? bf2f(reinterpret_cast<const uint16_t *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
-}
 // Four consecutive elements (index i, a multiple of 4) of a bf16 (bf) or fp32 array as raw words, and those
 // words as floats. The split lets a thread issue all its loads before it waits for any of them.
 // Both loads are issued for either type (bf16 reads its 8 bytes twice), so that no branch or select touches
