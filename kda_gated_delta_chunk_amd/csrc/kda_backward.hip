@@ -168,7 +168,7 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
 template <int K> struct FacL {
     static constexpr int NKG1 = 0;                   // -K~, o1: X = V - K~ S
     static constexpr int KC2 = CB * K;               // Kc, o2: S' = diag(Gc) S + Kc^T W; dW = P^T dO + Kc dS' (o1)
-    static constexpr int QG2 = 2 * CB * K;           // Q~, o2: dS = diag(Gc) dS' + Q~^T dO - Wk^T dW; O = Q~ S + P W (o1)
+    static constexpr int QG2 = 2 * CB * K;           // Q~, o2: dS = diag(Gc) dS' + Q~^T dO - Wk^T dW; O (o1)
     static constexpr int NWK2 = 3 * CB * K;          // -Wk, o2
     static constexpr int T1 = 4 * CB * K;            // T, t: W = T X
     static constexpr int P1 = T1 + CB * CB;          // P, t
@@ -807,7 +807,6 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
     using L = FacL<K>;
     constexpr int VM = (K > V ? K : V) + 4;  // row pitch: float4 reads of 16 rows fall in distinct banks
     constexpr int KT = K / 16, NZ = (KT + 3) / 4;  // 16-row tiles of K; tiles per wavefront in phase f
-    constexpr int CPT = K / 16;                  // channels per thread in the per-(token, channel) phase
     __shared__ __align__(16) float b0[CB * VM], b1[CB * VM], b2[CB * VM], b3[CB * VM];
     // Until phase f, a neighbour chunk's rows for rebuilding the state or state gradient this chunk does not have
     // stored (the previous chunk's W in x0, or the next chunk's dO in x0 and dW in x1); from phase g on, q, k and
@@ -898,7 +897,8 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
                 const int e = tid + CNT * j, t = e / (V / 4), c4 = e % (V / 4);
                 if (e < RV) {
                     const int o = t * VM + 4 * c4;
-                    *reinterpret_cast<f32x4 *>(x0 + o) = rebuild_s ? rxw[j] : (t < ce.nval_next ? raw4_f(rxo[j], do_bf) : z);
+                    const f32x4 nx = t < ce.nval_next ? raw4_f(rxo[j], do_bf) : z;
+                    *reinterpret_cast<f32x4 *>(x0 + o) = rebuild_s ? rxw[j] : nx;
                     if (rebuild_ds) *reinterpret_cast<f32x4 *>(x1 + o) = rxw[j];
                 }
             }
@@ -911,9 +911,9 @@ __global__ __launch_bounds__(CNT, 2) void kda_cb_grad(
         if (tid < CB) sb[tid] = tid < at.nval ? raw1_f(fb, io_bf) : 0.f;
     }
     __syncthreads();
-    // ---- the rows of S and dS' that phase f multiplies: all issued here (and kept here by the scheduling
-    // barrier), so that their latency overlaps phases b to e. Row 16 rt + m, columns 16 sv + 4 qq .. +3 are
-    // slot l of tile (sv, rt) in the passes' [V/16][K/16][64][4] order.
+    // ---- the state and state gradient stored in this chunk's pair slot, in the rows phase f multiplies: all
+    // issued here (and kept here by the scheduling barrier), so that their latency overlaps phases b to e. Row
+    // 16 rt + m, columns 16 sv + 4 qq .. +3 are slot l of tile (sv, rt) in the passes' [V/16][K/16][64][4] order.
     // With one of them rebuilt from a neighbour chunk, that chunk's factors come too: Gc of this lane's key row
     // and the o2-order operand of the rebuild (Kc of the previous chunk, or Q~ and -Wk of the next).
     f32x4 s4r[NZ][V / 16], d4r[NZ][V / 16], nbB0[NZ], nbB1[NZ];
@@ -1527,7 +1527,8 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::
     }
     float *dst = dw_part + ((size_t)tile * H + h) * CW * 4 + (size_t)(coff + c0) * 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4 *>(dst + 4 * j) = make_float4(dw[j][0], dw[j][1], dw[j][2], dw[j][3]);
+    for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4 *>(dst + 4 * j) = make_float4(dw[j][0], dw[j][1], dw[j][2], dw[j][3]);
 }
 
 // dL/dw = the tiles' partial sums added in tile order (deterministic); one thread per (head, channel, tap).
@@ -1611,7 +1612,8 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
     if (npass_blocks > 0) {
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
-                               a.S0, w.seq_tok, w.seg_off, w.half_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate, w.doe,
+                               a.S0, w.seq_tok, w.seg_off, w.half_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate,
+                               w.doe,
                                a.d_o_gate);
         };
         if (og) {
