@@ -523,6 +523,14 @@ struct Stage {
     }
 };
 
+// Workgroup -> ((sequence, head) item, column tile) of the two passes: the nvt column tiles of an item, which read
+// the same factor blocks at about the same time, go to workgroups 8 apart, that is to the same XCD (workgroups
+// are dealt to the 8 XCDs in turn), so that the factor blocks come from HBM once per item.
+__device__ __forceinline__ void pass_item(int64_t bid, int nvt, int64_t &item, int &vt) {
+    item = bid / (8 * nvt) * 8 + bid % 8;
+    vt = (int)(bid / 8 % nvt);
+}
+
 // ---- forward states: one workgroup of NW wavefronts per (sequence, head, 16 NW columns); wavefront w owns
 // the 16-column tile 16 w and keeps its K x 16 slice of S as K/16 accumulator tiles. Operands are fetched two
 // chunks ahead into one of two register sets (a fetch takes several microseconds; one chunk's work does not
@@ -532,7 +540,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
                                                       const float *__restrict__ fac, const float *__restrict__ S0,
                                                       const int64_t *__restrict__ seq_tok,
                                                       const int64_t *__restrict__ chunk_off,
-                                                      const int64_t *__restrict__ half_off, int32_t H, int32_t V,
+                                                      const int64_t *__restrict__ half_off, int64_t n_items,
+                                                      int32_t H, int32_t V,
                                                       int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
                                                       float *__restrict__ Wbuf, const void *__restrict__ dout,
                                                       const void *__restrict__ zg, float *__restrict__ doe,
@@ -546,11 +555,12 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     __shared__ __align__(16) float fP[OG ? CB * CB : 4];
     __shared__ __align__(16) float sGC[K];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
-    int64_t bid = blockIdx.x;
-    const int vt = (int)(bid % nvt);
-    bid /= nvt;
-    const int h = (int)(bid % H);
-    const int64_t n = bid / H;
+    int64_t item;
+    int vt;
+    pass_item(blockIdx.x, nvt, item, vt);
+    if (item >= n_items) return;
+    const int h = (int)(item % H);
+    const int64_t n = item / H;
     const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n], p0 = half_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
@@ -685,7 +695,8 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
                                                       const float *__restrict__ fac, const float *__restrict__ dSf,
                                                       const int64_t *__restrict__ seq_tok,
                                                       const int64_t *__restrict__ chunk_off,
-                                                      const int64_t *__restrict__ half_off, int32_t H, int32_t V,
+                                                      const int64_t *__restrict__ half_off, int64_t n_items,
+                                                      int32_t H, int32_t V,
                                                       int32_t nvt, float *__restrict__ dSbuf,
                                                       float *__restrict__ dWbuf, float *__restrict__ dS0) {
     using L = FacL<K>;
@@ -696,11 +707,12 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
     __shared__ __align__(16) float fPT[CB * CB];
     __shared__ __align__(16) float sGC[K];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
-    int64_t bid = blockIdx.x;
-    const int vt = (int)(bid % nvt);
-    bid /= nvt;
-    const int h = (int)(bid % H);
-    const int64_t n = bid / H;
+    int64_t item;
+    int vt;
+    pass_item(blockIdx.x, nvt, item, vt);
+    if (item >= n_items) return;
+    const int h = (int)(item % H);
+    const int64_t n = item / H;
     const int64_t t0 = seq_tok[n], t1 = seq_tok[n + 1], c0 = chunk_off[n], p0 = half_off[n];
     const int nch = (int)((t1 - t0 + CB - 1) / CB);
     const int64_t sH = H, sV = V;
@@ -1605,15 +1617,15 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
     constexpr int NW = V / 16 < 4 ? V / 16 : 4;  // wavefronts (16-column tiles) per workgroup of the two passes
     const int32_t nvt = V / (16 * NW);
     const int64_t nchunk_blocks = a.max_segs * a.H;
-    const int64_t npass_blocks = (int64_t)a.num_seqs * a.H * nvt;
+    const int64_t n_items = (int64_t)a.num_seqs * a.H, npass_blocks = (n_items + 7) / 8 * 8 * nvt;
     if (nchunk_blocks > 0)
         hipLaunchKernelGGL((kda_cb_factors<K>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
                            a.beta, io_bf, a.gate_sigmoid, (const ChunkEnt *)w.ctab, a.H, w.fac);
     if (npass_blocks > 0) {
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
-                               a.S0, w.seq_tok, w.seg_off, w.half_off, a.H, V, nvt, w.Sb, w.Xb, w.Wb, a.dout, a.o_gate,
-                               w.doe,
+                               a.S0, w.seq_tok, w.seg_off, w.half_off, n_items, a.H, V, nvt, w.Sb, w.Xb, w.Wb,
+                               a.dout, a.o_gate, w.doe,
                                a.d_o_gate);
         };
         if (og) {
@@ -1626,7 +1638,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         auto rev = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st,
                                og ? (const void *)w.doe : a.dout, (const float *)w.fac, a.dS_final, w.seq_tok,
-                               w.seg_off, w.half_off, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
+                               w.seg_off, w.half_off, n_items, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
         };
         (!og && io_bf) ? rev(kda_cb_rev<K, NW, true>) : rev(kda_cb_rev<K, NW, false>);
     }
