@@ -261,23 +261,23 @@ __device__ __forceinline__ void load8(const void *base, int64_t idx, float (&x)[
 
 // The short convolution of one 8-channel run in the 16-token prep's lane layout (lane 16 ag + r holds
 // token r of the sub-tile): y_t = w3 x_t + w2 x_{t-1} + w1 x_{t-2} + w0 x_{t-3} with w = taps[c] =
-// (w0, w1, w2, w3), then SiLU when act == 2. x is this lane's raw run; hx, on lanes 13..15, the run of
+// (w0, w1, w2, w3) (the activation is applied by the caller). x is this lane's raw run; hx, on lanes 13..15, the run of
 // token r - 16 (the three rows before the sub-tile; zeros before the sequence start). Token r - d is
 // lane r - d of x or, for r < d, lane r - d + 16 of hx: one rotation of the 16-lane row by d of a
 // source that takes hx on lanes 16 - d .. 15 (the lanes whose values wrap around) and x elsewhere.
 __device__ __forceinline__ void conv_run8(const float (&x)[8], const float (&hx)[8], const float4 *__restrict__ taps,
-                                          int r, int act, float (&y)[8]) {
+                                          int r, float (&y)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float4 w = taps[j];
-        const float p1 = dpp_f<0x121, false>(r >= 15 ? hx[j] : x[j]);  // row_ror:1
-        const float p2 = dpp_f<0x122, false>(r >= 14 ? hx[j] : x[j]);  // row_ror:2
-        const float p3 = dpp_f<0x123, false>(r >= 13 ? hx[j] : x[j]);  // row_ror:3
+        const float p1 = dpp_f<0x121, true>(r >= 15 ? hx[j] : x[j]);  // row_ror:1 (every lane has a source)
+        const float p2 = dpp_f<0x122, true>(r >= 14 ? hx[j] : x[j]);  // row_ror:2
+        const float p3 = dpp_f<0x123, true>(r >= 13 ? hx[j] : x[j]);  // row_ror:3
         float v = w.w * x[j];
         v = __builtin_fmaf(w.z, p1, v);
         v = __builtin_fmaf(w.y, p2, v);
         v = __builtin_fmaf(w.x, p3, v);
-        y[j] = act == 2 ? v * sigmoid_f(v) : v;
+        y[j] = v;
     }
 }
 
@@ -620,6 +620,9 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
         lds_sync();
         const float4 *tq = reinterpret_cast<const float4 *>(kx);
         const float4 *tk = tq + K;
+        // hv on lanes 13..15 is the same for the whole sub-tile: false at the sequence start, true after
+        // (hx on the other lanes is never selected), so the zeros are set under a uniform branch
+        const bool halo = tok0 > tab.tok(n);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int c = 32 * s + 8 * ag;
@@ -627,14 +630,23 @@ __device__ __forceinline__ void prep16_core(const PrepParams &pa, int gc, int n,
             load8<BF>(qp, row * K + c, x);
             load8<BF>(qp, hrow * K + c, hx);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hx[j] = hv ? hx[j] : 0.f;
-            conv_run8(x, hx, tq + c, r, pa.conv, qv[s]);
+            for (int j = 0; j < 8; ++j) hx[j] = halo ? hx[j] : 0.f;
+            conv_run8(x, hx, tq + c, r, qv[s]);
             load8<BF>(kp, row * K + c, x);
             load8<BF>(kp, hrow * K + c, hx);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hx[j] = hv ? hx[j] : 0.f;
-            conv_run8(x, hx, tk + c, r, pa.conv, kv[s]);
+            for (int j = 0; j < 8; ++j) hx[j] = halo ? hx[j] : 0.f;
+            conv_run8(x, hx, tk + c, r, kv[s]);
             load8<BF>(gp, row * K + c, bl[s]);
+        }
+        if (pa.conv == 2) {  // SiLU, wave-uniform
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    qv[s][j] *= sigmoid_f(qv[s][j]);
+                    kv[s][j] *= sigmoid_f(kv[s][j]);
+                }
         }
     } else {
 #pragma unroll
