@@ -172,26 +172,26 @@ __device__ __forceinline__ float row_suffix16(float x) {
     x += dpp_f<0x108, true>(x);  // row_shl:8
     return x;
 }
-__device__ __forceinline__ float row_last(float x) { return dpp_f<0x15f, false>(x); }  // row_newbcast:15
+__device__ __forceinline__ float row_last(float x) { return dpp_f<0x15f, true>(x); }  // row_newbcast:15
 // Lane k of each 16-lane row, broadcast to the row (row_newbcast:k); k must be a compile-time constant.
 __device__ __forceinline__ float row_bcast(float x, int k) {
     switch (k) {
-        case 0: return dpp_f<0x150, false>(x);
-        case 1: return dpp_f<0x151, false>(x);
-        case 2: return dpp_f<0x152, false>(x);
-        case 3: return dpp_f<0x153, false>(x);
-        case 4: return dpp_f<0x154, false>(x);
-        case 5: return dpp_f<0x155, false>(x);
-        case 6: return dpp_f<0x156, false>(x);
-        case 7: return dpp_f<0x157, false>(x);
-        case 8: return dpp_f<0x158, false>(x);
-        case 9: return dpp_f<0x159, false>(x);
-        case 10: return dpp_f<0x15a, false>(x);
-        case 11: return dpp_f<0x15b, false>(x);
-        case 12: return dpp_f<0x15c, false>(x);
-        case 13: return dpp_f<0x15d, false>(x);
-        case 14: return dpp_f<0x15e, false>(x);
-        default: return dpp_f<0x15f, false>(x);
+        case 0: return dpp_f<0x150, true>(x);
+        case 1: return dpp_f<0x151, true>(x);
+        case 2: return dpp_f<0x152, true>(x);
+        case 3: return dpp_f<0x153, true>(x);
+        case 4: return dpp_f<0x154, true>(x);
+        case 5: return dpp_f<0x155, true>(x);
+        case 6: return dpp_f<0x156, true>(x);
+        case 7: return dpp_f<0x157, true>(x);
+        case 8: return dpp_f<0x158, true>(x);
+        case 9: return dpp_f<0x159, true>(x);
+        case 10: return dpp_f<0x15a, true>(x);
+        case 11: return dpp_f<0x15b, true>(x);
+        case 12: return dpp_f<0x15c, true>(x);
+        case 13: return dpp_f<0x15d, true>(x);
+        case 14: return dpp_f<0x15e, true>(x);
+        default: return dpp_f<0x15f, true>(x);
     }
 }
 
