@@ -218,10 +218,11 @@ def backward_flops(T, H, K, V):
     return 24 * K * V * T * H
 
 
-def time_backward(w, steps, warmup, dev, prologue=False):
+def time_backward(w, steps, warmup, dev, prologue=False, segment_tokens=0):
     """kda_chunk_bwd on the prefill workload's inputs, dL/do ~ N(0, 1), no dL/dS_final. prologue: the
     forward normalised q and k and ran the short convolution with SiLU (raw k, taps ~ N(0, 0.5^2)), so the
-    gradients also run back through both and dL/d(taps) is formed."""
+    gradients also run back through both and dL/d(taps) is formed. segment_tokens: a workspace of the size
+    for segments of that many tokens, so the call runs in segments."""
     lib = _lib.load()
     inp = synth.workload_prefill_inputs(w, device=dev, raw_k=prologue)
     B, T, H, K = inp["q"].shape
@@ -236,7 +237,10 @@ def time_backward(w, steps, warmup, dev, prologue=False):
     cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev) if prologue else None
     dcw = torch.empty((H, 2 * K + V, 4), **f32) if prologue else None
     cwp, dcwp = (cw.data_ptr(), dcw.data_ptr()) if prologue else (None, None)
-    wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B, qc, cc)
+    if segment_tokens:
+        wsb = lib.kda_chunk_bwd_segmented_workspace_bytes(B, T, H, K, V, B, qc, cc, segment_tokens)
+    else:
+        wsb = lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, B, qc, cc)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
@@ -622,6 +626,11 @@ def main():
         rp = time_backward(w, 5, 2, dev, prologue=True)
         out["backward"]["with_prologue"] = {"ms_per_step": rp["ms"], "workspace_bytes": rp["ws_bytes"],
                                             "tokens_per_s": rp["B"] * rp["T"] / (rp["ms"] * 1e-3)}
+        say("backward in 1024-token segments (workspace under 1 GB): warmup 2, steps 5")
+        rs = time_backward(w, 5, 2, dev, segment_tokens=1024)
+        out["backward"]["in_segments"] = {"ms_per_step": rs["ms"], "workspace_bytes": rs["ws_bytes"],
+                                          "segment_tokens": 1024,
+                                          "tokens_per_s": rs["B"] * rs["T"] / (rs["ms"] * 1e-3)}
     out["device_errors"] = errors
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle)")

@@ -391,8 +391,8 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  *   d_conv_w [H, K + K + V, 4] fp32: dL/d(conv_w), required with a
  *           convolution (written also when T == 0: zeros), else ignored
  *   dS0     [num_seqs, H, K, V] fp32 output, or NULL to skip
- *   workspace at least kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs,
- *           qk_norm, conv). Per 16-token chunk and head (at most
+ *   workspace kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs, qk_norm,
+ *           conv) for one pass (or less, in segments: below). Per 16-token chunk and head (at most
  *           ceil(T / 16) B chunks, one more per sequence when packed) it holds
  *           the chunk's factors (4 * 16 * K + 7 * 16 * 16 + K floats, rounded
  *           up to 64) and three 16 * V blocks; per pair of chunks of a
@@ -410,14 +410,31 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
  * call is needed. All arithmetic is fp32 and the result is deterministic
  * (fixed summation order). Outputs may not alias the inputs or each other.
  * Errors as for kda_chunk_fwd (chunk does not apply).
- * Long sequences can be taken in segments, with the workspace bounded by the
- * segment length: the forward over segments 1..i-1 (kda_chunk_fwd's S_final)
- * gives segment i's S0, and the backward runs the segments last to first,
- * each one's dS0 passed as the previous segment's dS_final. The chained
- * gradients equal one call's up to rounding.
+ * A smaller workspace (at least kda_chunk_bwd_segmented_workspace_bytes for
+ * 32-token segments; not with a convolution) makes the call take the input in
+ * segments of the longest length L (a multiple of 32 tokens) whose workspace
+ * fits: consecutive sequences of at most L tokens together, and a longer
+ * sequence in segments of L tokens, chained through their states. The
+ * forward states of the segments are recomputed first (fp32, the same chunk
+ * form), then the segments run last to first, each one's dL/dS0 passed on as
+ * the previous one's dL/dS_final; the gradients equal one call's up to
+ * rounding. A long sequence costs about one more forward state pass. With a
+ * packed input the call then reads cu_seqlens back to the host (it waits for
+ * the stream's earlier work), so it cannot be captured into a graph.
+ * The same chaining works across calls: the forward over segments 1..i-1
+ * (kda_chunk_fwd's S_final) gives segment i's S0.
  */
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
                                      kda_qk_norm_t qk_norm, kda_conv_t conv);
+/* Workspace bytes of kda_chunk_bwd taken in segments of segment_tokens tokens
+ * (a multiple of 32): one call's workspace for segment_tokens tokens and up
+ * to segment_tokens / 16 sequences, the states entering the segments of one
+ * sequence (ceil(B T / segment_tokens) - 1 of K * V floats per head), two
+ * state gradients and the calls' sequence starts. 0 if segment_tokens is not
+ * a positive multiple of 32, with a convolution, or for invalid sizes. */
+size_t kda_chunk_bwd_segmented_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                                               int32_t num_seqs, kda_qk_norm_t qk_norm, kda_conv_t conv,
+                                               int64_t segment_tokens);
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
                            const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,

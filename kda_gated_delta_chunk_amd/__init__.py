@@ -84,9 +84,21 @@ def workspace_status(workspace, stream=None) -> int:
     return int(out.value)
 
 
-def bwd_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int) -> int:
-    """Device workspace bytes kda_chunk_bwd needs (0 = unsupported sizes)."""
-    return int(_lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs))
+def bwd_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, qk_norm: bool = False,
+                        conv: str = "none") -> int:
+    """Device workspace bytes kda_chunk_bwd needs in one call (0 = unsupported sizes)."""
+    if conv not in _lib.CONVS:
+        raise ValueError("conv must be one of %s" % sorted(_lib.CONVS))
+    return int(_lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, num_seqs, int(bool(qk_norm)),
+                                                         _lib.CONVS[conv]))
+
+
+def bwd_segmented_workspace_bytes(B: int, T: int, H: int, K: int, V: int, num_seqs: int, segment_tokens: int,
+                                  qk_norm: bool = False) -> int:
+    """Device workspace bytes kda_chunk_bwd needs when it takes the input in segments of segment_tokens
+    tokens (a multiple of 32; no convolution); 0 = unsupported."""
+    return int(_lib.load().kda_chunk_bwd_segmented_workspace_bytes(B, T, H, K, V, num_seqs, int(bool(qk_norm)), 0,
+                                                                   segment_tokens))
 
 
 def _ptr(t):
@@ -295,7 +307,7 @@ def decode_step(q, k, v, g, beta, S, o_dtype=None, out=None, gate: str = "log_de
 
 def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, want_dS0: bool = True,
               workspace=None, gate: str = "log_decay", o_gate=None, qk_norm: bool = False, conv: str = "none",
-              conv_w=None, out=None):
+              conv_w=None, out=None, segment_tokens: int = 0):
     """Gradients of chunk_fwd's (o, S_final) given dL/do and dL/dS_final, with respect to the raw inputs.
     ``gate``, ``qk_norm``, ``conv`` and ``conv_w`` say what the forward did, as for chunk_fwd; dg is the
     gradient with respect to g as given (the log-decay, or the gate pre-activation). With ``o_gate`` (the
@@ -346,9 +358,14 @@ def chunk_bwd(q, k, v, g, beta, do, S0=None, dS_final=None, cu_seqlens=None, wan
             raise ValueError("out[%r]: not a result of this call" % (name,))
         _need(given[name], "out[%r]" % (name,), shapes[name], torch.float32, dev)
     out = {name: given.get(name) if name in given else torch.empty(shp, **f32) for name, shp in shapes.items()}
-    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc))
-    if need == 0:
-        raise KDAError(2, "kda_chunk_bwd_workspace_bytes")
+    if segment_tokens:
+        need = int(lib.kda_chunk_bwd_segmented_workspace_bytes(B, T, H, K, V, N, qc, cc, segment_tokens))
+        if need == 0:
+            raise KDAError(2, "kda_chunk_bwd_segmented_workspace_bytes")
+    else:
+        need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc))
+        if need == 0:
+            raise KDAError(2, "kda_chunk_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o_gate), _ptr(S0), _ptr(cu_seqlens),

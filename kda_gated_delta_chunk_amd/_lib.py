@@ -28,11 +28,12 @@ STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPP
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_min_workspace_bytes",
            "kda_chunk_prep_workspace_bytes",
            "kda_workspace_status", "kda_chunk_fwd", "kda_chunk_prep", "kda_chunk_state", "kda_decode_step",
-           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_chunk_fwd_no_alloc")
+           "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd_segmented_workspace_bytes", "kda_chunk_bwd",
+           "kda_chunk_fwd_no_alloc")
 
 NO_ALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # KDA_NO_ALLOC_SCRATCH_BYTES
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 _lib = None
 
 
@@ -84,6 +85,9 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int]
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd_segmented_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int,
+                                                            i64]
+    lib.kda_chunk_bwd_segmented_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   sz, vp]

@@ -73,7 +73,7 @@ kda_status_t check_device() {
 
 extern "C" {
 
-int kda_abi_version(void) { return 10; }
+int kda_abi_version(void) { return 11; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -344,6 +344,16 @@ size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K,
                                          conv != KDA_CONV_NONE);
 }
 
+size_t kda_chunk_bwd_segmented_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
+                                               int32_t num_seqs, kda_qk_norm_t qk_norm, kda_conv_t conv,
+                                               int64_t segment_tokens) {
+    if (!valid_qk_norm(qk_norm) || !valid_conv(conv) || conv != KDA_CONV_NONE) return 0;
+    const bool packed = (B == 1);
+    if (check_prefill_sizes(B, T, H, K, V, num_seqs, 16, packed) != KDA_SUCCESS) return 0;
+    return kda::backward_segmented_workspace_bytes(B, T, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM,
+                                                   segment_tokens);
+}
+
 kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                            const void *o_gate, const float *S0, const int32_t *cu_seqlens, const void *d_o,
                            const float *dS_final, int64_t B, int64_t T, int32_t H, int32_t K, int32_t V,
@@ -385,7 +395,13 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     if (segs * H >= ((int64_t)1 << 31) || (B * T * H + 15) / 16 >= ((int64_t)1 << 31)) return KDA_ERROR_INVALID_VALUE;
     const size_t need = kda::backward_workspace_bytes(B * T, segs, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM,
                                                       has_conv);
-    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    if (!workspace) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    int64_t seg_tokens = 0;  // a smaller workspace: segments of the longest length that fits
+    if (workspace_bytes < need) {
+        if (has_conv || B * T == 0) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+        seg_tokens = kda::backward_segment_length(B, T, H, K, V, num_seqs, qk_norm == KDA_QK_L2NORM, workspace_bytes);
+        if (seg_tokens == 0) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    }
     st = check_device();
     if (st != KDA_SUCCESS) return st;
     kda::BackwardArgs a;
@@ -402,6 +418,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
     a.workspace = workspace;
     a.max_segs = segs;
+    a.seg_tokens = seg_tokens;
     if (kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return KDA_ERROR_HIP;
     return KDA_SUCCESS;
 }

@@ -18,6 +18,8 @@
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
+#include <vector>
+
 namespace kda {
 namespace {
 
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
                                                       int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
                                                       float *__restrict__ Wbuf, const void *__restrict__ dout,
                                                       const void *__restrict__ zg, float *__restrict__ doe,
-                                                      float *__restrict__ dz) {
+                                                      float *__restrict__ dz, float *__restrict__ S_out) {
     using L = FacL<K>;
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
     __shared__ __align__(16) float fKG[FK];
@@ -685,6 +687,12 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     for (int ci = 0; ci < nch; ci += 2) {
         step(sa, ci);
         if (ci + 1 < nch) step(sb, ci + 1);
+    }
+    if (S_out) {  // the state leaving the sequence, [K][V] per (sequence, head) as S0
+#pragma unroll
+        for (int r = 0; r < KT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S_out[((n * sH + h) * K + 16 * r + 4 * qq + i) * sV + col] = S[r][i];
     }
 }
 
@@ -1613,7 +1621,8 @@ unsigned blocks_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 template <int K, int V>
 void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void *ks, bool qk_bf, const void *vs,
               bool v_bf, float *dv_dst, float *dq_dst, float *dk_dst, hipStream_t st) {
-    const bool io_bf = a.io_bf16, og = a.o_gate != nullptr;
+    // the forward states alone (states_only) need no output gate: it does not act on the state
+    const bool io_bf = a.io_bf16, og = a.o_gate != nullptr && !a.states_only;
     constexpr int NW = V / 16 < 4 ? V / 16 : 4;  // wavefronts (16-column tiles) per workgroup of the two passes
     const int32_t nvt = V / (16 * NW);
     const int64_t nchunk_blocks = a.max_segs * a.H;
@@ -1625,8 +1634,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
                                a.S0, w.seq_tok, w.seg_off, w.half_off, n_items, a.H, V, nvt, w.Sb, w.Xb, w.Wb,
-                               a.dout, a.o_gate, w.doe,
-                               a.d_o_gate);
+                               a.dout, a.o_gate, w.doe, a.d_o_gate, a.S_out);
         };
         if (og) {
             if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
@@ -1634,6 +1642,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         } else {
             v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
         }
+        if (a.states_only) return;
         // with an output gate the reverse reads do * sigmoid(z) (fp32), formed by the forward pass
         auto rev = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st,
@@ -1642,6 +1651,7 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         };
         (!og && io_bf) ? rev(kda_cb_rev<K, NW, true>) : rev(kda_cb_rev<K, NW, false>);
     }
+    if (a.states_only) return;
     if (nchunk_blocks > 0)
         hipLaunchKernelGGL((kda_cb_grad<K, V>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
                            a.beta, io_bf, a.gate_sigmoid, og ? (const void *)w.doe : a.dout, og ? false : io_bf,
@@ -1706,6 +1716,7 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
     // the recurrence's reverse on the prologue's outputs
     if (conv) bwd_core<K, V>(a, w, w.xq, w.xk, false, w.xv, false, w.gv, w.gq, w.gk, st);
     else bwd_core<K, V>(a, w, w.xq, w.xk, false, a.v, a.io_bf16, a.dv, w.gq, w.gk, st);
+    if (a.states_only) return hipGetLastError();
     // prologue, reverse: normalisation (into gq, gk when a convolution follows), then convolution
     if (norm && n_rows > 0) {
         hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xq, w.rq, w.gq,
@@ -1733,6 +1744,153 @@ hipError_t bwd_launch(const BackwardArgs &a, hipStream_t st) {
     }
 }
 
+// ---- the backward in segments (a workspace below the one-call size). Every call below is the one-call
+// backward on a part of the input: consecutive short sequences together, a long sequence in segments of at
+// most L tokens. A long sequence's segments are chained through their states: the forward states alone give
+// the state entering each segment, then the segments run last to first, each one's dL/dS0 passed on as the
+// previous one's dL/dS_final. The chained gradients equal one call's up to rounding (the state crosses a
+// segment boundary in fp32, as it crosses a chunk boundary inside a call).
+
+// The relative starts of sequences n0 .. n0 + count of a packed input, as cu_seqlens for one call: starts
+// clamped to [0, total] and made non-decreasing as one call takes them, minus the first. One thread.
+__global__ __launch_bounds__(64) void kda_bwd_cu_slice(const int32_t *__restrict__ cu, int32_t n0, int32_t count,
+                                                       int64_t base, int64_t total, int32_t *__restrict__ out) {
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    int64_t run = base;
+    out[0] = 0;
+    for (int32_t i = 1; i <= count; ++i) {
+        int64_t x = cu[n0 + i];
+        x = x < 0 ? 0 : (x > total ? total : x);
+        run = x > run ? x : run;
+        out[i] = (int32_t)(run - base);
+    }
+}
+
+int64_t chunks_of(int64_t len) { return (len + CB - 1) / CB; }
+
+// Workspace of the segmented backward with segments of L tokens (a multiple of 2 CB): the calls' starts (cap
+// + 1 int32), the states entering the segments of one long sequence (at most ceil(n_tok / L) - 1), two state
+// gradients passed between segments, and one call's workspace: at most L tokens in L / CB chunks, of at most
+// cap = max(1, L / 64) sequences.
+struct SegWs {
+    size_t cu_rel, bst, gbuf, core, total;
+    int64_t cap;
+};
+SegWs seg_ws(int64_t n_tok, int64_t L, int32_t H, int32_t K, int32_t V, bool norm) {
+    SegWs r;
+    r.cap = L / 64 > 1 ? L / 64 : 1;
+    const int64_t pmax = (n_tok + L - 1) / L;
+    const size_t hkv = (size_t)H * K * V * sizeof(float);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    r.cu_rel = take(sizeof(int32_t) * (size_t)(r.cap + 1));
+    r.bst = take(hkv * (size_t)(pmax > 1 ? pmax - 1 : 0));
+    r.gbuf = take(2 * hkv);
+    size_t core = 0;
+    bwd_ptrs(nullptr, L, (int32_t)r.cap, L / CB, H, K, V, norm, false, &core);
+    r.core = take(core);
+    r.total = off;
+    return r;
+}
+
+hipError_t launch_segmented(const BackwardArgs &a, hipStream_t st) {
+    const int64_t n_tok = a.B * a.T, L = a.seg_tokens;
+    const int32_t N = a.num_seqs;
+    const bool packed = a.cu_seqlens != nullptr;
+    const SegWs lay = seg_ws(n_tok, L, a.H, a.K, a.V, a.qk_l2norm);
+    char *ws = (char *)a.workspace;
+    int32_t *cu_rel = (int32_t *)(ws + lay.cu_rel);
+    float *bst = (float *)(ws + lay.bst), *gbuf = (float *)(ws + lay.gbuf);
+    void *core = ws + lay.core;
+    const int64_t hkv = (int64_t)a.H * a.K * a.V;
+    // the sequences' starts, as one call takes them (read back from the device for a packed input)
+    std::vector<int64_t> start((size_t)N + 1);
+    if (packed) {
+        std::vector<int32_t> cu((size_t)N + 1);
+        hipError_t e = hipMemcpyAsync(cu.data(), a.cu_seqlens, sizeof(int32_t) * ((size_t)N + 1), hipMemcpyDeviceToHost,
+                                      st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return e;
+        int64_t run = 0;
+        for (int32_t m = 0; m <= N; ++m) {
+            const int64_t x = cu[m] < 0 ? 0 : (cu[m] > n_tok ? n_tok : cu[m]);
+            run = x > run ? x : run;
+            start[m] = run;
+        }
+    } else {
+        for (int32_t m = 0; m <= N; ++m) start[m] = (int64_t)m * a.T;
+    }
+    const size_t esz = a.io_bf16 ? 2 : 4;
+    // the one-call arguments for tokens [tok, tok + Bc Tc) holding sequences seq .. seq + Nc - 1 in nch chunks
+    auto part = [&](int64_t tok, int64_t Bc, int64_t Tc, int32_t Nc, const int32_t *cu, int64_t seq, int64_t nch) {
+        BackwardArgs c = a;
+        const int64_t rk = tok * a.H * a.K, rv = tok * a.H * a.V, rh = tok * a.H;
+        auto in = [&](const void *p, int64_t off) { return p ? (const void *)((const char *)p + off * esz) : p; };
+        c.q = in(a.q, rk); c.k = in(a.k, rk); c.g = in(a.g, rk); c.v = in(a.v, rv); c.beta = in(a.beta, rh);
+        c.dout = in(a.dout, rv); c.o_gate = in(a.o_gate, rv);
+        c.dq = a.dq + rk; c.dk = a.dk + rk; c.dg = a.dg + rk; c.dv = a.dv + rv; c.dbeta = a.dbeta + rh;
+        c.d_o_gate = a.d_o_gate ? a.d_o_gate + rv : nullptr;
+        c.S0 = a.S0 ? a.S0 + seq * hkv : nullptr;
+        c.dS_final = a.dS_final ? a.dS_final + seq * hkv : nullptr;
+        c.dS0 = a.dS0 ? a.dS0 + seq * hkv : nullptr;
+        c.B = Bc; c.T = Tc; c.num_seqs = Nc; c.cu_seqlens = cu;
+        c.workspace = core;
+        c.max_segs = nch;
+        c.seg_tokens = 0;
+        return c;
+    };
+    hipError_t e = hipSuccess;
+    int32_t n = 0;
+    while (n < N && e == hipSuccess) {
+        const int64_t len = start[n + 1] - start[n];
+        if (len <= L) {  // consecutive short sequences in one call: at most L tokens, L / CB chunks, cap sequences
+            int32_t n1 = n + 1;
+            int64_t nch = chunks_of(len);
+            while (n1 < N && n1 - n < lay.cap && start[n1 + 1] - start[n] <= L &&
+                   nch + chunks_of(start[n1 + 1] - start[n1]) <= L / CB)
+                nch += chunks_of(start[n1 + 1] - start[n1]), ++n1;
+            const int32_t cnt = n1 - n;
+            if (packed) {
+                hipLaunchKernelGGL(kda_bwd_cu_slice, dim3(1), dim3(64), 0, st, a.cu_seqlens, n, cnt, start[n], n_tok,
+                                   cu_rel);
+                e = launch_backward(part(start[n], 1, start[n1] - start[n], cnt, cu_rel, n, nch), st);
+            } else {
+                e = launch_backward(part(start[n], cnt, a.T, cnt, nullptr, n, nch), st);
+            }
+            n = n1;
+            continue;
+        }
+        // a long sequence in P segments: the forward states first, then the segments last to first
+        const int64_t P = (len + L - 1) / L;
+        auto seg = [&](int64_t j) {
+            const int64_t t0 = start[n] + j * L, tl = (j + 1 < P) ? L : len - j * L;
+            BackwardArgs c = part(t0, 1, tl, 1, nullptr, n, chunks_of(tl));
+            c.S0 = j == 0 ? c.S0 : bst + (j - 1) * hkv;
+            return c;
+        };
+        for (int64_t j = 0; j + 1 < P && e == hipSuccess; ++j) {
+            BackwardArgs c = seg(j);
+            c.states_only = true;
+            c.S_out = bst + j * hkv;  // the state entering segment j + 1
+            e = launch_backward(c, st);
+        }
+        const float *dsf = a.dS_final ? a.dS_final + n * hkv : nullptr;
+        for (int64_t j = P - 1; j >= 0 && e == hipSuccess; --j) {
+            BackwardArgs c = seg(j);
+            c.dS_final = dsf;
+            c.dS0 = j == 0 ? c.dS0 : gbuf + (j & 1) * hkv;
+            e = launch_backward(c, st);
+            dsf = c.dS0;
+        }
+        ++n;
+    }
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
@@ -1744,7 +1902,24 @@ size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, i
 
 int32_t backward_segment_tokens() { return CB; }
 
+size_t backward_segmented_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                          bool qk_norm, int64_t seg_tokens) {
+    (void)num_seqs;
+    if (seg_tokens < 2 * CB || seg_tokens % (2 * CB) != 0) return 0;
+    return seg_ws(B * T, seg_tokens, H, K, V, qk_norm).total;
+}
+
+int64_t backward_segment_length(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                bool qk_norm, size_t ws_bytes) {
+    const int64_t n_tok = B * T;
+    // the longest segment that fits (the states' share shrinks as segments grow, so every length is tried)
+    for (int64_t L = (n_tok + 2 * CB - 1) / (2 * CB) * (2 * CB); L >= 2 * CB; L -= 2 * CB)
+        if (backward_segmented_workspace_bytes(B, T, H, K, V, num_seqs, qk_norm, L) <= ws_bytes) return L;
+    return 0;
+}
+
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
+    if (a.seg_tokens > 0) return launch_segmented(a, st);
     switch (a.K) {
         case 32: return a.io_bf16 ? bwd_launch<true, 32>(a, st) : bwd_launch<false, 32>(a, st);
         case 64: return a.io_bf16 ? bwd_launch<true, 64>(a, st) : bwd_launch<false, 64>(a, st);

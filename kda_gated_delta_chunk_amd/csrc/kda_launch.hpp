@@ -104,12 +104,23 @@ struct BackwardArgs {
     float *d_o_gate;                   // dL/dz [B,T,H,V] fp32 (required with o_gate)
     float *dS0;                        // or null
     void *workspace;
-    int64_t max_segs;                  // upper bound on checkpoint segments over all sequences
+    int64_t max_segs;                  // upper bound on 16-token chunks over all sequences
+    // taken in segments of seg_tokens tokens (a workspace below the one-call size; 0: one call)
+    int64_t seg_tokens = 0;
+    // internal to the segments: the forward states only (no gradients), each sequence's last state into S_out
+    bool states_only = false;
+    float *S_out = nullptr;
 };
-// Tokens per checkpoint segment of the backward pass.
+// Tokens per chunk of the backward's chunk form (the unit of max_segs).
 int32_t backward_segment_tokens();
 size_t backward_workspace_bytes(int64_t n_tokens, int64_t max_segs, int32_t H, int32_t K, int32_t V,
                                 int32_t num_seqs, bool qk_norm, bool conv);
 hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream);
+// Workspace of the backward taken in segments of seg_tokens tokens (a multiple of 32; no convolution), and the
+// longest segment length whose workspace fits in ws_bytes (0 if none does).
+size_t backward_segmented_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                          bool qk_norm, int64_t seg_tokens);
+int64_t backward_segment_length(int64_t B, int64_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs,
+                                bool qk_norm, size_t ws_bytes);
 
 }  // namespace kda

@@ -26,7 +26,7 @@ int main() {
     int ndev = 0;
     const bool device = hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0;
     (void)hipGetLastError();
-    CHECK(kda_abi_version() == 10);
+    CHECK(kda_abi_version() == 11);
     for (int s = -1; s < 8; ++s) CHECK(strlen(kda_status_string((kda_status_t)s)) > 0);
     // workspace queries over a sweep of sizes and options (valid and not)
     const int64_t Ts[] = {0, 1, 15, 16, 17, 4096, (int64_t)1 << 40};
@@ -48,6 +48,12 @@ int main() {
           kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE));
     CHECK(kda_chunk_bwd_workspace_bytes(2, 64, 2, 48, 32, 2, KDA_QK_AS_GIVEN, KDA_CONV_NONE) == 0);
     CHECK(kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, KDA_QK_AS_GIVEN, (kda_conv_t)3) == 0);
+    // the backward in segments: a multiple of 32 tokens, no convolution, below one call's workspace
+    CHECK(kda_chunk_bwd_segmented_workspace_bytes(1, 4096, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE, 256) > 0);
+    CHECK(kda_chunk_bwd_segmented_workspace_bytes(1, 4096, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE, 256) <
+          kda_chunk_bwd_workspace_bytes(1, 4096, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE));
+    CHECK(kda_chunk_bwd_segmented_workspace_bytes(1, 4096, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_NONE, 48) == 0);
+    CHECK(kda_chunk_bwd_segmented_workspace_bytes(1, 4096, 2, 32, 32, 1, KDA_QK_AS_GIVEN, KDA_CONV_SHORT4, 256) == 0);
     // prefill: rejected arguments
     CHECK(fwd(nullptr, A, A, 1 << 30, 64, 32, 16, KDA_DTYPE_BF16, KDA_OPERANDS_BF16, nullptr, 1) == KDA_ERROR_INVALID_VALUE);
     CHECK(fwd(A + 8, A, A, 1 << 30, 64, 32, 16, KDA_DTYPE_BF16, KDA_OPERANDS_BF16, nullptr, 1) == KDA_ERROR_INVALID_VALUE);

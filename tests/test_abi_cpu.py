@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.kda_abi_version() == _lib.ABI_VERSION == 10
+    assert lib.kda_abi_version() == _lib.ABI_VERSION == 11
 
 
 def test_status_strings():
@@ -400,6 +400,40 @@ def test_bwd_workspace_bytes_with_prologue():
         assert extra <= got <= extra + 8 * 256, (qc, cc, got, extra)
 
 
+def test_bwd_segmented_workspace_bytes():
+    # segments of L tokens: one call's workspace for L tokens in L / 16 chunks of at most max(1, L / 64)
+    # sequences, the states entering the segments of one sequence (ceil(T / L) - 1 of K x V per head), two state
+    # gradients and the calls' sequence starts
+    lib = _lib.load()
+    seg, one = lib.kda_chunk_bwd_segmented_workspace_bytes, lib.kda_chunk_bwd_workspace_bytes
+    B, T, H, K, V = 1, 4096, 4, 64, 64
+    hkv = H * K * V * 4
+    fac = -(-(4 * 16 * K + 7 * 16 * 16 + K) // 64) * 64
+    for L in (32, 256, 1024):
+        cap, nc = max(1, L // 64), L // 16
+        core = nc * H * (fac + 3 * 16 * V) * 4 + (nc + cap + 1) // 2 * H * 2 * K * V * 4 + L * H * V * 4
+        extra = (-(-T // L) - 1) * hkv + 2 * hkv
+        slack = 16 * 256 + nc * 32 + 4 * (cap + 1) * 8
+        got = seg(B, T, H, K, V, 1, 0, 0, L)
+        assert core + extra <= got <= core + extra + slack, (L, got, core + extra)
+    assert seg(B, T, H, K, V, 1, 0, 0, 256) < one(B, T, H, K, V, 1, 0, 0) / 4
+    assert seg(B, T, H, K, V, 1, 1, 0, 64) > seg(B, T, H, K, V, 1, 0, 0, 64)  # the normalisation's buffers
+    for L in (0, 16, 48, -32):
+        assert seg(B, T, H, K, V, 1, 0, 0, L) == 0, L                      # not a positive multiple of 32
+    assert seg(B, T, H, K, V, 1, 0, 1, 64) == 0 and seg(B, T, H, K, V, 1, 0, 2, 64) == 0  # no convolution
+    assert seg(B, T, H, 48, V, 1, 0, 0, 64) == 0
+
+
+def test_chunk_bwd_segmented_workspace_limits():
+    lib = _lib.load()
+    # below the least segmented workspace (32-token segments) the call reports a small workspace, and with a
+    # convolution anything below one call's workspace
+    least = min(lib.kda_chunk_bwd_segmented_workspace_bytes(1, 64, 2, 32, 32, 1, 0, 0, L) for L in (32, 64))
+    assert _bwd(wsb=least - 1) == WS_SMALL
+    full_conv = lib.kda_chunk_bwd_workspace_bytes(1, 64, 2, 32, 32, 1, 0, 1)
+    assert _bwd(conv=1, cw=CW, dcw=DCW, wsb=full_conv // 2) == WS_SMALL
+
+
 def _has_gpu():
     try:
         import torch
@@ -417,6 +451,7 @@ def test_valid_arguments_without_a_device_report_no_device():
     assert _state() == NO_DEV
     assert _dec() == NO_DEV
     assert _bwd() == NO_DEV
+    assert _bwd(wsb=_lib.load().kda_chunk_bwd_segmented_workspace_bytes(1, 64, 2, 32, 32, 1, 0, 0, 32)) == NO_DEV
     assert _fwd_no_alloc() == NO_DEV
     assert _fwd_no_alloc(T=1 << 20, H=96, K=128, V=128) == NO_DEV  # fits in the scratch as the fused kernel
     assert _bwd(qk=1, conv=2, cw=CW, dcw=DCW) == NO_DEV

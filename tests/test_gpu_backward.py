@@ -35,9 +35,10 @@ def _nan(shape):
     return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
 
 
-def _gpu(inp, want_dS0=True):
+def _gpu(inp, want_dS0=True, seg=0):
     """The GPU gradients, written over NaN-filled outputs and a NaN-filled workspace (so an element the kernels
-    leave unwritten, or a workspace byte read before it is written, shows up in the comparison)."""
+    leave unwritten, or a workspace byte read before it is written, shows up in the comparison). seg > 0: a
+    workspace of the size for segments of seg tokens, so the call takes the input in segments."""
     B, T, H, K = inp["q"].shape
     V = inp["v"].shape[-1]
     N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
@@ -51,7 +52,11 @@ def _gpu(inp, want_dS0=True):
         out["dconv_w"] = _nan((H, 2 * K + V, 4))
     qc = _lib.KDA_QK_L2NORM if inp.get("qk_norm", False) else _lib.KDA_QK_AS_GIVEN
     cc = _lib.CONVS[inp.get("conv", "none")]
-    wsb = _lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc)
+    if seg:
+        wsb = _lib.load().kda_chunk_bwd_segmented_workspace_bytes(B, T, H, K, V, N, qc, cc, seg)
+        assert 0 < wsb < _lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc)
+    else:
+        wsb = _lib.load().kda_chunk_bwd_workspace_bytes(B, T, H, K, V, N, qc, cc)
     ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN patterns in every fp32 word
     got = chunk_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"], S0=inp["S0"],
                     dS_final=inp["dS_final"], cu_seqlens=inp["cu_seqlens"], want_dS0=want_dS0,
@@ -180,6 +185,60 @@ def test_bwd_segments_chained_through_the_states():
     print("  errors " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= TOL_FP32, (n, e)
+
+
+def _same(got, ref):
+    # In segments the gradients are bitwise one call's: every segment of a sequence holds an even number of
+    # 16-token chunks, so each chunk keeps its place in its pair (which state the gradient kernel stores and
+    # which it rebuilds), and the state crosses a segment boundary in fp32 as it crosses a chunk boundary.
+    errs = {n: err(got[n], ref[n]) for n in ref}
+    print("  against one call " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), (n, errs[n])
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_bwd_in_segments_matches_one_call(io):
+    # a workspace for 128-token segments: the 1000-token sequence runs as 8 segments chained through their
+    # states (mild decay, so the state carries across several segments); the same gradients as one call
+    _announce("bwd_in_segments", io=io, T=1000, H=3, K=64, V=64, seg=128, seed=81)
+    inp = _inputs(1, 1000, 3, 64, 64, io, 81, g_shift=-6.0)
+    got = _gpu(inp, seg=128)
+    _same(got, _gpu(inp))
+    _compare(got, _oracle(inp))
+
+
+def test_bwd_in_segments_varlen_with_the_prologue_and_gates():
+    # packed sequences of 5, 0, 295, 1, 399 and 300 tokens with 64-token segments: the short ones share calls,
+    # the long ones are chained; q/k normalisation, the gate pre-activation and the output gate
+    cu = [0, 5, 5, 300, 301, 700, 1000]
+    _announce("bwd_in_segments_varlen", cu=cu, H=2, K=128, V=64, io="bf16", seg=64, seed=82)
+    inp = _inputs(1, 1000, 2, 128, 64, "bf16", 82, cu=cu, gate_preact=True, with_o_gate=True)
+    inp["gate"] = "scaled_sigmoid"
+    inp["qk_norm"] = True
+    got = _gpu(inp, seg=64)
+    _same(got, _gpu(inp))
+    _compare(got, _oracle(inp))
+
+
+@pytest.mark.parametrize("B,T,seg", [(4, 40, 96), (2, 150, 64)])
+def test_bwd_in_segments_batched_rows(B, T, seg):
+    # batched rows: two 40-token rows per call (B=4, 96-token segments), or each 150-token row in 3 segments
+    _announce("bwd_in_segments_rows", B=B, T=T, H=2, K=32, V=32, seg=seg, seed=83)
+    inp = _inputs(B, T, 2, 32, 32, "fp32", 83)
+    got = _gpu(inp, seg=seg)
+    _same(got, _gpu(inp))
+    _compare(got, _oracle(inp))
+
+
+def test_bwd_4k_workload_in_segments():
+    # the 4096-token, 96-head bf16 workload with a workspace under 1 GB (segments of at most 1024 tokens),
+    # against one call on every head
+    _announce("bwd_4k_in_segments", T=4096, H=96, K=128, V=128, io="bf16", seg=1024, seed=1002)
+    inp = _inputs(1, 4096, 96, 128, 128, "bf16", 1002, with_S0=False)
+    wsb = _lib.load().kda_chunk_bwd_segmented_workspace_bytes(1, 4096, 96, 128, 128, 1, 0, 0, 1024)
+    assert wsb < 1 << 30
+    _same(_gpu(inp, seg=1024), _gpu(inp))
 
 
 def test_bwd_is_deterministic():
