@@ -241,6 +241,18 @@ def test_bwd_4k_workload_in_segments():
     _same(_gpu(inp, seg=1024), _gpu(inp))
 
 
+def test_bwd_1m_tokens_in_segments():
+    # the million-token context: two heads of one 1,048,576-token sequence, in 65,536-token segments (a
+    # workspace of 1.3 GB instead of 18 GB), against one call
+    T, H = 1 << 20, 2
+    _announce("bwd_1m_in_segments", T=T, H=H, K=128, V=128, io="bf16", seg=65536, seed=1003)
+    inp = _inputs(1, T, H, 128, 128, "bf16", 1003)
+    got = _gpu(inp, seg=65536)
+    for n in got:
+        assert torch.isfinite(got[n]).all(), n
+    _same(got, _gpu(inp))
+
+
 def test_bwd_is_deterministic():
     _announce("bwd_determinism", T=200, H=4, K=128, V=128, seed=76)
     inp = _inputs(1, 200, 4, 128, 128, "bf16", 76)
