@@ -1293,15 +1293,27 @@ __device__ __forceinline__ void bwd_st8(float *p, const float (&y)[8]) {
 
 constexpr int CONV_FWD_TILE = 16;  // flat tokens per thread of the convolution's forward
 
+// Sum over the G lanes of an aligned lane group (G a power of two dividing 64; every lane of the group takes
+// part). For G = 16 the same butterfly as sum16.
+template <int G>
+__device__ __forceinline__ float sum_lanes(float x) {
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, G);
+    return x;
+}
+
 // The convolution (and SiLU for act == 2) of one tensor x [tokens][H][D] into out (fp32). One thread per
-// (16-token tile of the flat rows, head, 8-channel run; runs of a row on consecutive lanes): it loads its
-// taps once and walks the tile's tokens with the three previous rows in registers, starting them from zero
-// at each sequence start. Rows of tokens outside every sequence get zeros.
-template <bool BF, int D>
+// (16-token tile of the flat rows, head, 8-channel run; the D / 8 runs of a row on consecutive lanes): it loads
+// its taps once and walks the tile's tokens with the three previous rows in registers, starting them from zero
+// at each sequence start. Rows of tokens outside every sequence get zeros. NORM: each row is also normalised,
+// out = y r with r = 1 / sqrt(|y|^2 + 1e-6) over the row's D channels (a sum over the row's lanes), and r goes
+// to rn [tokens][H].
+template <bool BF, int D, bool NORM = false>
 __global__ __launch_bounds__(256) void kda_bwd_conv_fwd(const typename IO<BF>::T *__restrict__ x,
                                                         const float *__restrict__ taps, int32_t CW, int32_t act,
                                                         int32_t H, int32_t N, const int64_t *__restrict__ seq_tok,
-                                                        int64_t total, int64_t n_items, float *__restrict__ out) {
+                                                        int64_t total, int64_t n_items, float *__restrict__ out,
+                                                        float *__restrict__ rn) {
     constexpr int G = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= n_items) return;
@@ -1335,6 +1347,7 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_fwd(const typename IO<BF>::T
 #pragma unroll
             for (int j = 0; j < 8; ++j) y[j] = 0.f;
             bwd_st8(out + row(t), y);
+            if (NORM && c0 == 0) rn[t * H + h] = rsqrtf(1e-6f);
             continue;
         }
         bool fresh = false;  // t starts a sequence: no history
@@ -1361,6 +1374,15 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_fwd(const typename IO<BF>::T
             p[1][j] = p[0][j];
             p[0][j] = xt[j];
         }
+        if constexpr (NORM) {  // the lanes of a row walk the same tokens, so they reach this together
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(y[j], y[j], ss);
+            const float rr = rsqrtf(sum_lanes<G>(ss) + 1e-6f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] *= rr;
+            if (c0 == 0) rn[t * H + h] = rr;
+        }
         bwd_st8(out + row(t), y);
     }
 }
@@ -1372,12 +1394,14 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
-// The normalisation of every (token, head) row of K channels, in fp32: xn = x r, r = 1 / sqrt(|x|^2 + 1e-6),
-// and r kept for the reverse. x is the I/O-dtype input (FROM_IO) or the fp32 buffer itself (xn, in place).
-// 16 lanes per row, K / 16 consecutive channels each (a row is one coalesced read).
-template <bool BF, int K, bool FROM_IO>
-__global__ __launch_bounds__(256) void kda_bwd_norm_fwd(const typename IO<BF>::T *__restrict__ x, float *xn,
-                                                        float *__restrict__ r, int64_t n_rows) {
+// The normalisation of every (token, head) row of K channels of the I/O-dtype input x, in fp32: xn = x r,
+// r = 1 / sqrt(|x|^2 + 1e-6), and r kept for the reverse (without a convolution; with one, the convolution's
+// forward normalises its rows itself). 16 lanes per row, K / 16 consecutive channels each (a row is one
+// coalesced read).
+template <bool BF, int K>
+__global__ __launch_bounds__(256) void kda_bwd_norm_fwd(const typename IO<BF>::T *__restrict__ x,
+                                                        float *__restrict__ xn, float *__restrict__ r,
+                                                        int64_t n_rows) {
     constexpr int E = K / 16;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t row = gid >> 4;
@@ -1387,7 +1411,7 @@ __global__ __launch_bounds__(256) void kda_bwd_norm_fwd(const typename IO<BF>::T
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < E; ++c) {
-        v[c] = ok ? (FROM_IO ? IO<BF>::ld(x, row * K + c0 + c) : xn[row * K + c0 + c]) : 0.f;
+        v[c] = ok ? IO<BF>::ld(x, row * K + c0 + c) : 0.f;
         ss = __builtin_fmaf(v[c], v[c], ss);
     }
     const float rr = rsqrtf(sum16(ss) + 1e-6f);
@@ -1433,13 +1457,14 @@ constexpr int CONV_TILE = 64;  // flat tokens per thread of the convolution's re
 // zeros before the sequence start) and dL/dy of tokens t-3..t with their sequence ids. It forms
 // dL/dy_t = dz_t act'(y_t), writes dL/dx_{t-3} (rows outside every sequence are not written) and sums the
 // tile's part of dL/dw into dw_part[tile][h][coff + c][4].
-template <bool BF, int D>
+template <bool BF, int D, bool NORM = false>
 __global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::T *__restrict__ x,
                                                          const float *__restrict__ dz, const float *__restrict__ taps,
                                                          int32_t CW, int32_t coff, int32_t act, int32_t H, int32_t N,
                                                          const int64_t *__restrict__ seq_tok, int64_t total,
                                                          int64_t n_items, float *__restrict__ dx,
-                                                         float *__restrict__ dw_part) {
+                                                         float *__restrict__ dw_part, const float *__restrict__ xn,
+                                                         const float *__restrict__ rn) {
     constexpr int G = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= n_items) return;
@@ -1497,6 +1522,16 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_back(const typename IO<BF>::
             float xt[8], g[8];
             bwd_ld8<BF>(x, row(t), xt);
             bwd_ld8<false>(dz, row(t), g);
+            if constexpr (NORM) {  // dz is dL/d(normalised row): through the normalisation, r (dz - (xn . dz) xn)
+                float a[8], dot = 0.f;
+                bwd_ld8<false>(xn, row(t), a);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dot = __builtin_fmaf(a[j], g[j], dot);
+                dot = sum_lanes<G>(dot);  // the lanes of a row walk the same tokens, so they reach this together
+                const float rr = rn[t * H + h];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) g[j] = rr * __builtin_fmaf(-dot, a[j], g[j]);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float y = w[j].w * xt[j];
@@ -1660,16 +1695,21 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
                            dk_dst, dv_dst, a.dg, a.dbeta);
 }
 
+// The convolution's reverse of one tensor; with xn and rn (the normalised rows and their factors) dz is the
+// gradient with respect to the normalised rows and is taken through the normalisation first.
 template <bool BF, int D>
 void conv_back_one(const BackwardArgs &a, const BwdWs &w, const void *x, const float *dz, int coff, float *dx,
-                   hipStream_t st) {
+                   const float *xn, const float *rn, hipStream_t st) {
     using T = typename IO<BF>::T;
     const int64_t total = a.B * a.T;
     const int64_t items = conv_tiles(total) * a.H * (D / 8);
-    if (items > 0)
-        hipLaunchKernelGGL((kda_bwd_conv_back<BF, D>), dim3(blocks_of(items)), dim3(256), 0, st, (const T *)x, dz,
+    if (items <= 0) return;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(blocks_of(items)), dim3(256), 0, st, (const T *)x, dz,
                            a.conv_w + (size_t)coff * 4, 2 * a.K + a.V, coff, a.conv, a.H, a.num_seqs, w.seq_tok,
-                           total, items, dx, w.dw_part);
+                           total, items, dx, w.dw_part, xn, rn);
+    };
+    xn ? go(kda_bwd_conv_back<BF, D, true>) : go(kda_bwd_conv_back<BF, D, false>);
 }
 
 template <bool BF, int K, int V>
@@ -1688,46 +1728,44 @@ hipError_t bwd_launch_kv(const BackwardArgs &a, hipStream_t st) {
         bwd_core<K, V>(a, w, a.q, a.k, a.io_bf16, a.v, a.io_bf16, a.dv, a.dq, a.dk, st);
         return hipGetLastError();
     }
-    // prologue, forward: convolution into xq, xk, xv; normalisation of q and k (in place, or from the input)
+    // prologue, forward: convolution into xq, xk, xv, q and k normalised in the same pass (with both); or the
+    // normalisation alone, from the input
     const int32_t CW = 2 * K + V;
     if (conv && n_tok > 0) {
         const int64_t tiles = (n_tok + CONV_FWD_TILE - 1) / CONV_FWD_TILE;
         const int64_t ik = tiles * a.H * (K / 8), iv = tiles * a.H * (V / 8);
-        hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.q, a.conv_w,
-                           CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, ik, w.xq);
-        hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, K>), dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.k,
-                           a.conv_w + (size_t)K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, ik, w.xk);
+        auto qk = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.q, a.conv_w, CW, a.conv, a.H,
+                               a.num_seqs, w.seq_tok, n_tok, ik, w.xq, w.rq);
+            hipLaunchKernelGGL(kern, dim3(blocks_of(ik)), dim3(256), 0, st, (const T *)a.k, a.conv_w + (size_t)K * 4,
+                               CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, ik, w.xk, w.rk);
+        };
+        norm ? qk(kda_bwd_conv_fwd<BF, K, true>) : qk(kda_bwd_conv_fwd<BF, K, false>);
         hipLaunchKernelGGL((kda_bwd_conv_fwd<BF, V>), dim3(blocks_of(iv)), dim3(256), 0, st, (const T *)a.v,
-                           a.conv_w + (size_t)2 * K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, iv, w.xv);
+                           a.conv_w + (size_t)2 * K * 4, CW, a.conv, a.H, a.num_seqs, w.seq_tok, n_tok, iv, w.xv,
+                           (float *)nullptr);
     }
-    if (norm && n_rows > 0) {
-        if (conv) {
-            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, false>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
-                               (const T *)nullptr, w.xq, w.rq, n_rows);
-            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, false>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
-                               (const T *)nullptr, w.xk, w.rk, n_rows);
-        } else {
-            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, true>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
-                               (const T *)a.q, w.xq, w.rq, n_rows);
-            hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K, true>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
-                               (const T *)a.k, w.xk, w.rk, n_rows);
-        }
+    if (norm && !conv && n_rows > 0) {
+        hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                           (const T *)a.q, w.xq, w.rq, n_rows);
+        hipLaunchKernelGGL((kda_bwd_norm_fwd<BF, K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st,
+                           (const T *)a.k, w.xk, w.rk, n_rows);
     }
     // the recurrence's reverse on the prologue's outputs
     if (conv) bwd_core<K, V>(a, w, w.xq, w.xk, false, w.xv, false, w.gv, w.gq, w.gk, st);
     else bwd_core<K, V>(a, w, w.xq, w.xk, false, a.v, a.io_bf16, a.dv, w.gq, w.gk, st);
     if (a.states_only) return hipGetLastError();
-    // prologue, reverse: normalisation (into gq, gk when a convolution follows), then convolution
-    if (norm && n_rows > 0) {
+    // prologue, reverse: the normalisation, then the convolution (with both, in the convolution's pass)
+    if (norm && !conv && n_rows > 0) {
         hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xq, w.rq, w.gq,
-                           conv ? w.gq : a.dq, n_rows, a.H, a.num_seqs, w.seq_tok);
+                           a.dq, n_rows, a.H, a.num_seqs, w.seq_tok);
         hipLaunchKernelGGL((kda_bwd_norm_back<K>), dim3(blocks_of(16 * n_rows)), dim3(256), 0, st, w.xk, w.rk, w.gk,
-                           conv ? w.gk : a.dk, n_rows, a.H, a.num_seqs, w.seq_tok);
+                           a.dk, n_rows, a.H, a.num_seqs, w.seq_tok);
     }
     if (conv) {
-        conv_back_one<BF, K>(a, w, a.q, w.gq, 0, a.dq, st);
-        conv_back_one<BF, K>(a, w, a.k, w.gk, K, a.dk, st);
-        conv_back_one<BF, V>(a, w, a.v, w.gv, 2 * K, a.dv, st);
+        conv_back_one<BF, K>(a, w, a.q, w.gq, 0, a.dq, norm ? w.xq : nullptr, w.rq, st);
+        conv_back_one<BF, K>(a, w, a.k, w.gk, K, a.dk, norm ? w.xk : nullptr, w.rk, st);
+        conv_back_one<BF, V>(a, w, a.v, w.gv, 2 * K, a.dv, nullptr, nullptr, st);
         const int64_t nel = (int64_t)a.H * CW * 4;
         hipLaunchKernelGGL(kda_bwd_convw_reduce, dim3(blocks_of(nel)), dim3(256), 0, st, w.dw_part,
                            conv_tiles(n_tok), nel, a.d_conv_w);
