@@ -628,7 +628,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         // [V/16][K/16][64][4] per slot and head: slot l = m' + 16 q' of tile (column block, row block) holds row
         // m' of the row block, columns 4 q' .. 4 q' + 3 of the column block (a quad transpose turns this lane's
         // four rows of one column into one row's four columns); each store writes a whole 1 KiB tile
-        if ((ci & 1) == 0) {
+        if ((ci & 1) == 0 && Sbuf) {
             float *sp = Sbuf + ((p0 + (ci >> 1)) * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) +
                         4 * slot;
 #pragma unroll
@@ -648,8 +648,10 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
         f32x4 W = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fT)[lane], X);
         mfma_fence(W);
         const int64_t xo = ((c * sH + h) * CB + 4 * qq + (m & 3)) * sV + col - m + 4 * (m >> 2);  // row-major
-        *reinterpret_cast<f32x4 *>(Xbuf + xo) = quad_transpose(X, m & 3);
-        *reinterpret_cast<f32x4 *>(Wbuf + xo) = quad_transpose(W, m & 3);
+        if (Xbuf) {  // (no X, W or states when only the state leaving the sequence is wanted)
+            *reinterpret_cast<f32x4 *>(Xbuf + xo) = quad_transpose(X, m & 3);
+            *reinterpret_cast<f32x4 *>(Wbuf + xo) = quad_transpose(W, m & 3);
+        }
         if constexpr (OG) {  // core output O = Q~ S + P W; do * sigmoid(z) for the reverse, and dL/dz
             f32x4 O0 = mfma_x4(zero4(), reinterpret_cast<const float4 *>(fP)[lane], W), O1 = zero4();
 #pragma unroll
@@ -1668,8 +1670,9 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
     if (npass_blocks > 0) {
         auto fwd = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
-                               a.S0, w.seq_tok, w.seg_off, w.half_off, n_items, a.H, V, nvt, w.Sb, w.Xb, w.Wb,
-                               a.dout, a.o_gate, w.doe, a.d_o_gate, a.S_out);
+                               a.S0, w.seq_tok, w.seg_off, w.half_off, n_items, a.H, V, nvt,
+                               a.states_only ? nullptr : w.Sb, a.states_only ? nullptr : w.Xb, w.Wb, a.dout,
+                               a.o_gate, w.doe, a.d_o_gate, a.S_out);
         };
         if (og) {
             if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
