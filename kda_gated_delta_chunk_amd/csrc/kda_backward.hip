@@ -537,17 +537,29 @@ __device__ __forceinline__ void pass_item(int64_t bid, int nvt, int64_t &item, i
 // the 16-column tile 16 w and keeps its K x 16 slice of S as K/16 accumulator tiles. Operands are fetched two
 // chunks ahead into one of two register sets (a fetch takes several microseconds; one chunk's work does not
 // cover it). OG: with an output gate.
+struct FwdP {
+    const void *v;
+    const float *fac, *S0;
+    const int64_t *seq_tok, *chunk_off, *half_off;
+    int64_t n_items;
+    int32_t H, V, nvt;
+    float *Sbuf, *Xbuf, *Wbuf;  // or null (only the state leaving the sequence is wanted)
+    const void *dout, *zg;      // with an output gate
+    float *doe, *dz;
+    float *S_out;               // or null
+};
+
 template <int K, int NW, bool OG, bool VBF, bool IOBF>
-__global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v,
-                                                      const float *__restrict__ fac, const float *__restrict__ S0,
-                                                      const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off,
-                                                      const int64_t *__restrict__ half_off, int64_t n_items,
-                                                      int32_t H, int32_t V,
-                                                      int32_t nvt, float *__restrict__ Sbuf, float *__restrict__ Xbuf,
-                                                      float *__restrict__ Wbuf, const void *__restrict__ dout,
-                                                      const void *__restrict__ zg, float *__restrict__ doe,
-                                                      float *__restrict__ dz, float *__restrict__ S_out) {
+__device__ __forceinline__ void cb_fwd_body(int64_t bid, const FwdP &pa) {
+    const void *__restrict__ v = pa.v;
+    const float *__restrict__ fac = pa.fac, *__restrict__ S0 = pa.S0;
+    const int64_t *__restrict__ seq_tok = pa.seq_tok, *__restrict__ chunk_off = pa.chunk_off,
+                  *__restrict__ half_off = pa.half_off;
+    const int64_t n_items = pa.n_items;
+    const int32_t H = pa.H, V = pa.V, nvt = pa.nvt;
+    float *__restrict__ Sbuf = pa.Sbuf, *__restrict__ Xbuf = pa.Xbuf, *__restrict__ Wbuf = pa.Wbuf;
+    const void *__restrict__ dout = pa.dout, *__restrict__ zg = pa.zg;
+    float *__restrict__ doe = pa.doe, *__restrict__ dz = pa.dz, *__restrict__ S_out = pa.S_out;
     using L = FacL<K>;
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
     __shared__ __align__(16) float fKG[FK];
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
     int64_t item;
     int vt;
-    pass_item(blockIdx.x, nvt, item, vt);
+    pass_item(bid, nvt, item, vt);
     if (item >= n_items) return;
     const int h = (int)(item % H);
     const int64_t n = item / H;
@@ -698,17 +710,31 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(const void *__restrict__ v
     }
 }
 
+template <int K, int NW, bool OG, bool VBF, bool IOBF>
+__global__ __launch_bounds__(64 * NW) void kda_cb_fwd(FwdP pa) {
+    cb_fwd_body<K, NW, OG, VBF, IOBF>(blockIdx.x, pa);
+}
+
 // ---- reverse: as the forward pass, chunks last to first, with dS' (the state gradient leaving the chunk) in
 // the accumulator tiles.
+struct RevP {
+    const void *dout;
+    const float *fac, *dSf;
+    const int64_t *seq_tok, *chunk_off, *half_off;
+    int64_t n_items;
+    int32_t H, V, nvt;
+    float *dSbuf, *dWbuf, *dS0;
+};
+
 template <int K, int NW, bool DBF>
-__global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ dout,
-                                                      const float *__restrict__ fac, const float *__restrict__ dSf,
-                                                      const int64_t *__restrict__ seq_tok,
-                                                      const int64_t *__restrict__ chunk_off,
-                                                      const int64_t *__restrict__ half_off, int64_t n_items,
-                                                      int32_t H, int32_t V,
-                                                      int32_t nvt, float *__restrict__ dSbuf,
-                                                      float *__restrict__ dWbuf, float *__restrict__ dS0) {
+__device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
+    const void *__restrict__ dout = pa.dout;
+    const float *__restrict__ fac = pa.fac, *__restrict__ dSf = pa.dSf;
+    const int64_t *__restrict__ seq_tok = pa.seq_tok, *__restrict__ chunk_off = pa.chunk_off,
+                  *__restrict__ half_off = pa.half_off;
+    const int64_t n_items = pa.n_items;
+    const int32_t H = pa.H, V = pa.V, nvt = pa.nvt;
+    float *__restrict__ dSbuf = pa.dSbuf, *__restrict__ dWbuf = pa.dWbuf, *__restrict__ dS0 = pa.dS0;
     using L = FacL<K>;
     constexpr int NT = 64 * NW, KT = K / 16, FK = CB * K;
     __shared__ __align__(16) float fKc[padded_floats(FK)];  // Kc in o1 order, padded
@@ -719,7 +745,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, qq = lane >> 4;
     int64_t item;
     int vt;
-    pass_item(blockIdx.x, nvt, item, vt);
+    pass_item(bid, nvt, item, vt);
     if (item >= n_items) return;
     const int h = (int)(item % H);
     const int64_t n = item / H;
@@ -812,6 +838,21 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_rev(const void *__restrict__ d
 #pragma unroll
             for (int i = 0; i < 4; ++i) dS0[((n * sH + h) * K + 16 * r + 4 * qq + i) * sV + col] = dS[r][i];
     }
+}
+
+template <int K, int NW, bool DBF>
+__global__ __launch_bounds__(64 * NW) void kda_cb_rev(RevP pa) {
+    cb_rev_body<K, NW, DBF>(blockIdx.x, pa);
+}
+
+// ---- both passes in one launch (no output gate: the reverse then reads nothing the forward pass writes):
+// workgroups [0, nfwd) run the forward-state pass, the rest the reverse pass. Each pass leaves a quarter of
+// the CUs idle and is bound by its per-chunk latency, not by throughput, so two resident workgroups per CU
+// (one of each) overlap them.
+template <int K, int NW, bool VBF, bool DBF>
+__global__ __launch_bounds__(64 * NW) void kda_cb_passes(FwdP f, RevP r, int64_t nfwd) {
+    if ((int64_t)blockIdx.x < nfwd) cb_fwd_body<K, NW, false, VBF, false>(blockIdx.x, f);
+    else cb_rev_body<K, NW, DBF>((int64_t)blockIdx.x - nfwd, r);
 }
 
 // ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) + 4 floats; the
@@ -1668,26 +1709,39 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         hipLaunchKernelGGL((kda_cb_factors<K>), dim3((unsigned)nchunk_blocks), dim3(CNT), 0, st, qs, ks, qk_bf, a.g,
                            a.beta, io_bf, a.gate_sigmoid, (const ChunkEnt *)w.ctab, a.H, w.fac);
     if (npass_blocks > 0) {
-        auto fwd = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st, vs, (const float *)w.fac,
-                               a.S0, w.seq_tok, w.seg_off, w.half_off, n_items, a.H, V, nvt,
-                               a.states_only ? nullptr : w.Sb, a.states_only ? nullptr : w.Xb, w.Wb, a.dout,
-                               a.o_gate, w.doe, a.d_o_gate, a.S_out);
-        };
-        if (og) {
-            if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
-            else io_bf ? fwd(kda_cb_fwd<K, NW, true, false, true>) : fwd(kda_cb_fwd<K, NW, true, false, false>);
-        } else {
-            v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
-        }
-        if (a.states_only) return;
+        FwdP f;
+        f.v = vs; f.fac = w.fac; f.S0 = a.S0;
+        f.seq_tok = w.seq_tok; f.chunk_off = w.seg_off; f.half_off = w.half_off;
+        f.n_items = n_items; f.H = a.H; f.V = V; f.nvt = nvt;
+        f.Sbuf = a.states_only ? nullptr : w.Sb;
+        f.Xbuf = a.states_only ? nullptr : w.Xb;
+        f.Wbuf = w.Wb;
+        f.dout = a.dout; f.zg = a.o_gate; f.doe = w.doe; f.dz = a.d_o_gate;
+        f.S_out = a.S_out;
         // with an output gate the reverse reads do * sigmoid(z) (fp32), formed by the forward pass
-        auto rev = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)npass_blocks), dim3(64 * NW), 0, st,
-                               og ? (const void *)w.doe : a.dout, (const float *)w.fac, a.dS_final, w.seq_tok,
-                               w.seg_off, w.half_off, n_items, a.H, V, nvt, w.dSb, w.dWb, a.dS0);
-        };
-        (!og && io_bf) ? rev(kda_cb_rev<K, NW, true>) : rev(kda_cb_rev<K, NW, false>);
+        RevP r;
+        r.dout = og ? (const void *)w.doe : a.dout; r.fac = w.fac; r.dSf = a.dS_final;
+        r.seq_tok = w.seq_tok; r.chunk_off = w.seg_off; r.half_off = w.half_off;
+        r.n_items = n_items; r.H = a.H; r.V = V; r.nvt = nvt;
+        r.dSbuf = w.dSb; r.dWbuf = w.dWb; r.dS0 = a.dS0;
+        const dim3 grid((unsigned)npass_blocks), blk(64 * NW);
+        if (!og && !a.states_only) {  // independent passes: one launch
+            auto both = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3((unsigned)(2 * npass_blocks)), blk, 0, st, f, r, npass_blocks);
+            };
+            if (v_bf) io_bf ? both(kda_cb_passes<K, NW, true, true>) : both(kda_cb_passes<K, NW, true, false>);
+            else io_bf ? both(kda_cb_passes<K, NW, false, true>) : both(kda_cb_passes<K, NW, false, false>);
+        } else {
+            auto fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, blk, 0, st, f); };
+            if (og) {
+                if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
+                else io_bf ? fwd(kda_cb_fwd<K, NW, true, false, true>) : fwd(kda_cb_fwd<K, NW, true, false, false>);
+            } else {
+                v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
+            }
+            if (a.states_only) return;
+            hipLaunchKernelGGL((kda_cb_rev<K, NW, false>), grid, blk, 0, st, r);
+        }
     }
     if (a.states_only) return;
     if (nchunk_blocks > 0)
