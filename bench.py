@@ -218,11 +218,12 @@ def backward_flops(T, H, K, V):
     return 24 * K * V * T * H
 
 
-def time_backward(w, steps, warmup, dev, prologue=False, segment_tokens=0):
+def time_backward(w, steps, warmup, dev, prologue=False, segment_tokens=0, o_gate=False):
     """kda_chunk_bwd on the prefill workload's inputs, dL/do ~ N(0, 1), no dL/dS_final. prologue: the
     forward normalised q and k and ran the short convolution with SiLU (raw k, taps ~ N(0, 0.5^2)), so the
     gradients also run back through both and dL/d(taps) is formed. segment_tokens: a workspace of the size
-    for segments of that many tokens, so the call runs in segments."""
+    for segments of that many tokens, so the call runs in segments. o_gate: the forward gated its output,
+    o = core * sigmoid(z) with z ~ N(0, 1), so dL/dz is formed too."""
     lib = _lib.load()
     inp = synth.workload_prefill_inputs(w, device=dev, raw_k=prologue)
     B, T, H, K = inp["q"].shape
@@ -233,6 +234,9 @@ def time_backward(w, steps, warmup, dev, prologue=False, segment_tokens=0):
                                                                     torch.empty((B, T, H), **f32)]
     dq, dk, dg, dv, db = (t.data_ptr() for t in outs)
     dS0 = torch.empty((B, H, K, V), **f32)
+    z = torch.randn((B, T, H, V), generator=torch.Generator().manual_seed(11)).to(dev, inp["v"].dtype) if o_gate else None
+    dz = torch.empty((B, T, H, V), **f32) if o_gate else None
+    zp, dzp = (z.data_ptr(), dz.data_ptr()) if o_gate else (None, None)
     qc, cc = (_lib.KDA_QK_L2NORM, _lib.CONVS["short4_silu"]) if prologue else (0, 0)
     cw = (0.5 * torch.randn((H, 2 * K + V, 4), generator=torch.Generator().manual_seed(7))).to(dev) if prologue else None
     dcw = torch.empty((H, 2 * K + V, 4), **f32) if prologue else None
@@ -246,8 +250,8 @@ def time_backward(w, steps, warmup, dev, prologue=False, segment_tokens=0):
     p = {n: inp[n].data_ptr() for n in ("q", "k", "v", "g", "beta")}
 
     def bwd():
-        _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], None, None, None, do.data_ptr(),
-                                     None, B, T, H, K, V, B, 1, 0, qc, cc, cwp, dq, dk, dv, dg, db, None, dcwp,
+        _lib.check(lib.kda_chunk_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], zp, None, None, do.data_ptr(),
+                                     None, B, T, H, K, V, B, 1, 0, qc, cc, cwp, dq, dk, dv, dg, db, dzp, dcwp,
                                      dS0.data_ptr(), ws.data_ptr(), wsb, stream.cuda_stream), "kda_chunk_bwd")
 
     for _ in range(warmup):
@@ -626,6 +630,10 @@ def main():
         rp = time_backward(w, 5, 2, dev, prologue=True)
         out["backward"]["with_prologue"] = {"ms_per_step": rp["ms"], "workspace_bytes": rp["ws_bytes"],
                                             "tokens_per_s": rp["B"] * rp["T"] / (rp["ms"] * 1e-3)}
+        say("backward with an output gate: warmup 2, steps 5")
+        rg = time_backward(w, 5, 2, dev, o_gate=True)
+        out["backward"]["with_output_gate"] = {"ms_per_step": rg["ms"], "workspace_bytes": rg["ws_bytes"],
+                                               "tokens_per_s": rg["B"] * rg["T"] / (rg["ms"] * 1e-3)}
         say("backward in 1024-token segments (workspace under 1 GB): warmup 2, steps 5")
         rs = time_backward(w, 5, 2, dev, segment_tokens=1024)
         out["backward"]["in_segments"] = {"ms_per_step": rs["ms"], "workspace_bytes": rs["ws_bytes"],

@@ -145,14 +145,15 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int b) {
 // The last form of dg_t (the derivative of everything through the decays b_u, u >= t, regrouped) has no
 // cancelling terms: every pair (i, j) of the in-chunk products enters only where it straddles t, weighted
 // by e^{b_i - b_j} summed from the decays between them, instead of as +E at i and -E at j, which in fp32
-// left the rounding of e^{+-b} (|b| up to 80) in dg. After the chunk table, the chain runs in four launches:
+// left the rounding of e^{+-b} (|b| up to 80) in dg. After the chunk table, the chain runs in three launches:
 //   kda_cb_factors  (chunk, head): the factors above;
-//   kda_cb_fwd      (sequence, head, 16 NW columns): X and W of every chunk, the state S entering every even
-//                   chunk of the sequence (and with an output gate the core output, do * sigmoid(z) and dL/dz);
-//   kda_cb_rev      (sequence, head, 16 NW columns): dW of every chunk, dS' leaving every odd chunk and the
-//                   last, and dL/dS0;
+//   kda_cb_passes   both sequential passes side by side, each per (sequence, head, 16 NW columns):
+//                   the forward-state pass (X and W of every chunk, the state S entering every even chunk of
+//                   the sequence, and with an output gate the core output, do * sigmoid(z) and dL/dz) and the
+//                   reverse pass (dW of every chunk, dS' leaving every odd chunk and the last, and dL/dS0);
 //   kda_cb_grad     (chunk, head): dq, dk, dv, dg, dbeta from the stored S or dS' (rebuilding the other from
 //                   the neighbour chunk's), X, W, dW.
+// (kda_cb_fwd, the forward-state pass alone, gives the state leaving a segment when a call runs in segments.)
 // Each column of S and of dS evolves on its own (decay scales rows), so the two sequential passes split V
 // into tiles: each wavefront keeps a K x 16 slice of the state as matrix-core accumulator tiles. All
 // arithmetic is fp32 (the products as v_mfma_f32_16x16x4f32), deterministic (fixed summation orders, no
@@ -719,6 +720,7 @@ __global__ __launch_bounds__(64 * NW) void kda_cb_fwd(FwdP pa) {
 // the accumulator tiles.
 struct RevP {
     const void *dout;
+    const void *zg;  // OGZ: the output gate's pre-activation z (dout then dL/d(gated o), dtype as dout)
     const float *fac, *dSf;
     const int64_t *seq_tok, *chunk_off, *half_off;
     int64_t n_items;
@@ -726,9 +728,9 @@ struct RevP {
     float *dSbuf, *dWbuf, *dS0;
 };
 
-template <int K, int NW, bool DBF>
+template <int K, int NW, bool DBF, bool OGZ = false>
 __device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
-    const void *__restrict__ dout = pa.dout;
+    const void *__restrict__ dout = pa.dout, *__restrict__ zg = pa.zg;
     const float *__restrict__ fac = pa.fac, *__restrict__ dSf = pa.dSf;
     const int64_t *__restrict__ seq_tok = pa.seq_tok, *__restrict__ chunk_off = pa.chunk_off,
                   *__restrict__ half_off = pa.half_off;
@@ -764,6 +766,7 @@ __device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
         Stage<CB * CB, NT> PT;
         Stage<K, NT> GC;
         uint32_t d[4];  // raw words of rows 4 qq + i of dO (clamped to the chunk's last valid row)
+        uint32_t z[OGZ ? 4 : 1];
     };
     Set sa, sb;
     auto fetch = [&](Set &st, int ci) {
@@ -779,6 +782,7 @@ __device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * qq + i < nval ? 4 * qq + i : nval - 1;
             st.d[i] = ld_raw<DBF>(dout, ((tok0 + t) * sH + h) * sV + col);
+            if constexpr (OGZ) st.z[i] = ld_raw<DBF>(zg, ((tok0 + t) * sH + h) * sV + col);
         }
     };
     auto step = [&](Set &st, int ci) {
@@ -792,7 +796,10 @@ __device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
         st.GC.store(sGC, tid);
         f32x4 dO;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dO[i] = 4 * qq + i < nval ? raw_f<DBF>(st.d[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) {  // with the gate, do * sigmoid(z) as the forward pass forms it
+            const float d = OGZ ? raw_f<DBF>(st.d[i]) * sigmoid_f(raw_f<DBF>(st.z[OGZ ? i : 0])) : raw_f<DBF>(st.d[i]);
+            dO[i] = 4 * qq + i < nval ? d : 0.f;
+        }
         // dS' leaving the chunk, at odd chunks and the sequence's last (into the pair's slot)
         if ((ci & 1) || ci == nch - 1) {
             float *dp = dSbuf + ((p0 + (ci >> 1)) * sH + h) * (int64_t)(K * V) + (int64_t)(vt * NW + w) * (KT * 256) +
@@ -840,19 +847,15 @@ __device__ __forceinline__ void cb_rev_body(int64_t bid, const RevP &pa) {
     }
 }
 
-template <int K, int NW, bool DBF>
-__global__ __launch_bounds__(64 * NW) void kda_cb_rev(RevP pa) {
-    cb_rev_body<K, NW, DBF>(blockIdx.x, pa);
-}
-
-// ---- both passes in one launch (no output gate: the reverse then reads nothing the forward pass writes):
-// workgroups [0, nfwd) run the forward-state pass, the rest the reverse pass. Each pass leaves a quarter of
-// the CUs idle and is bound by its per-chunk latency, not by throughput, so two resident workgroups per CU
-// (one of each) overlap them.
-template <int K, int NW, bool VBF, bool DBF>
-__global__ __launch_bounds__(64 * NW) void kda_cb_passes(FwdP f, RevP r, int64_t nfwd) {
-    if ((int64_t)blockIdx.x < nfwd) cb_fwd_body<K, NW, false, VBF, false>(blockIdx.x, f);
-    else cb_rev_body<K, NW, DBF>((int64_t)blockIdx.x - nfwd, r);
+// ---- both passes in one launch: workgroups [0, nfwd) run the forward-state pass, the rest the reverse pass,
+// which reads nothing the forward pass writes (with an output gate it forms do * sigmoid(z) itself). Each pass
+// leaves a quarter of the CUs idle and is bound by its per-chunk latency, not by throughput, so two resident
+// workgroups per CU (one of each) overlap them. The output-gate forward pass would take more than half a SIMD's
+// registers; it is held to half (no spills at K = 128), the others fit by themselves.
+template <int K, int NW, bool OG, bool VBF, bool IOBF, bool DBF>
+__global__ __launch_bounds__(64 * NW, (OG && NW == 4) ? 2 : 1) void kda_cb_passes(FwdP f, RevP r, int64_t nfwd) {
+    if ((int64_t)blockIdx.x < nfwd) cb_fwd_body<K, NW, OG, VBF, IOBF>(blockIdx.x, f);
+    else cb_rev_body<K, NW, DBF, OG>((int64_t)blockIdx.x - nfwd, r);
 }
 
 // ---- local gradients: one workgroup per (chunk, head). LDS rows have a pitch of VM = max(K, V) + 4 floats; the
@@ -1718,29 +1721,32 @@ void bwd_core(const BackwardArgs &a, const BwdWs &w, const void *qs, const void 
         f.Wbuf = w.Wb;
         f.dout = a.dout; f.zg = a.o_gate; f.doe = w.doe; f.dz = a.d_o_gate;
         f.S_out = a.S_out;
-        // with an output gate the reverse reads do * sigmoid(z) (fp32), formed by the forward pass
+        // with an output gate the reverse in the same launch forms do * sigmoid(z) from do and z; alone (after the
+        // forward pass) it would read do * sigmoid(z) as the forward pass stored it
         RevP r;
-        r.dout = og ? (const void *)w.doe : a.dout; r.fac = w.fac; r.dSf = a.dS_final;
+        r.dout = a.dout; r.zg = a.o_gate; r.fac = w.fac; r.dSf = a.dS_final;
         r.seq_tok = w.seq_tok; r.chunk_off = w.seg_off; r.half_off = w.half_off;
         r.n_items = n_items; r.H = a.H; r.V = V; r.nvt = nvt;
         r.dSbuf = w.dSb; r.dWbuf = w.dWb; r.dS0 = a.dS0;
         const dim3 grid((unsigned)npass_blocks), blk(64 * NW);
-        if (!og && !a.states_only) {  // independent passes: one launch
-            auto both = [&](auto kern) {
-                hipLaunchKernelGGL(kern, dim3((unsigned)(2 * npass_blocks)), blk, 0, st, f, r, npass_blocks);
-            };
-            if (v_bf) io_bf ? both(kda_cb_passes<K, NW, true, true>) : both(kda_cb_passes<K, NW, true, false>);
-            else io_bf ? both(kda_cb_passes<K, NW, false, true>) : both(kda_cb_passes<K, NW, false, false>);
-        } else {
+        if (a.states_only) {  // the forward states alone (no output gate: states_only clears og)
             auto fwd = [&](auto kern) { hipLaunchKernelGGL(kern, grid, blk, 0, st, f); };
-            if (og) {
-                if (v_bf) io_bf ? fwd(kda_cb_fwd<K, NW, true, true, true>) : fwd(kda_cb_fwd<K, NW, true, true, false>);
-                else io_bf ? fwd(kda_cb_fwd<K, NW, true, false, true>) : fwd(kda_cb_fwd<K, NW, true, false, false>);
-            } else {
-                v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
-            }
-            if (a.states_only) return;
-            hipLaunchKernelGGL((kda_cb_rev<K, NW, false>), grid, blk, 0, st, r);
+            v_bf ? fwd(kda_cb_fwd<K, NW, false, true, false>) : fwd(kda_cb_fwd<K, NW, false, false, false>);
+            return;
+        }
+        auto both = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)(2 * npass_blocks)), blk, 0, st, f, r, npass_blocks);
+        };
+        if (og) {
+            if (v_bf) io_bf ? both(kda_cb_passes<K, NW, true, true, true, true>)
+                            : both(kda_cb_passes<K, NW, true, true, false, false>);
+            else io_bf ? both(kda_cb_passes<K, NW, true, false, true, true>)
+                       : both(kda_cb_passes<K, NW, true, false, false, false>);
+        } else {
+            if (v_bf) io_bf ? both(kda_cb_passes<K, NW, false, true, false, true>)
+                            : both(kda_cb_passes<K, NW, false, true, false, false>);
+            else io_bf ? both(kda_cb_passes<K, NW, false, false, false, true>)
+                       : both(kda_cb_passes<K, NW, false, false, false, false>);
         }
     }
     if (a.states_only) return;
